@@ -1,0 +1,60 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each mutant is a copy of oracle/oracle.c with one plausible mistake (a
+dropped term, a wrong sign, a wrong index, a transposed operand, the wrong
+rounding), compiled on the CPU into a temporary library.  The pin checks of
+test_oracle.py are run against it and at least one of them must fail.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle
+
+MUTANTS = {
+    "drop_last_k_term": ("for (int64_t k = 0; k < K; ++k) sum += arow[k] * brow[k];",
+                         "for (int64_t k = 0; k < K - 1; ++k) sum += arow[k] * brow[k];"),
+    "wrong_sign": ("sum += arow[k] * brow[k];", "sum -= arow[k] * brow[k];"),
+    "reversed_k_index": ("sum += arow[k] * brow[k];", "sum += arow[k] * brow[K - 1 - k];"),
+    "transposed_b": ("const double *brow = Bd + n * K;", "const double *brow = Bd + (n % (K ? K : 1)) * N;"),
+    "round_toward_zero": ("double q = round_half_even(ldexp(a, 10 - E));", "double q = floor(ldexp(a, 10 - E));"),
+    "ties_away_from_zero": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
+    "subnormal_scale": ("mag = ldexp((double)frac, -24);", "mag = ldexp((double)frac, -25);"),
+    "exponent_bias": ("mag = ldexp((double)(1024 + frac), exp - 25);", "mag = ldexp((double)(1024 + frac), exp - 24);"),
+    "gemv_transposed_w": ("sum += xd[k] * oracle_f16_to_f64(W[n * K + k]);",
+                          "sum += xd[k] * oracle_f16_to_f64(W[(k * N + n) % (N * K)]);"),
+    "gemv_drop_first": ("for (int64_t k = 0; k < K; ++k) sum += xd[k]", "for (int64_t k = 1; k < K; ++k) sum += xd[k]"),
+    "overflow_threshold": ("if (a >= 65520.0) return (uint16_t)(sign | 0x7c00);",
+                           "if (a >= 65504.0) return (uint16_t)(sign | 0x7c00);"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_dir):
+    old, new = MUTANTS[name]
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = os.path.join(mutant_dir, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib_path = os.path.join(mutant_dir, f"lib{name}.so")
+    oracle.compile_oracle(source=path, output=lib_path)
+    lib = oracle.load(lib_path)
+    caught = []
+    for check in test_oracle.ALL_CHECKS:
+        try:
+            check(lib)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+    assert caught, f"no pin detects the planted mistake {name}"
