@@ -1,0 +1,245 @@
+"""FP16 GEMM and GEMV for AMD MI355X (gfx950) behind a small C ABI.
+
+    gemm_f16(A, B, D=None)   D = A · Bᵀ   A [M,K], B [N,K], D [M,N]  (fp16, FP32 accumulate)
+    gemv_f16(x, W, y=None)   y = x · Wᵀ   x [K],   W [N,K], y [N]
+
+This module only marshals arguments: it checks tensor dtypes, devices and
+shapes, passes raw device pointers, sizes and the current HIP stream to
+libgemvtile.so (see include/gemvtile.h), and turns a nonzero status into an
+exception.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback path.  If the library has not been built, importing
+works but every call raises ``GemvTileLibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "GemvTileError",
+    "GemvTileLibraryMissing",
+    "LIBRARY_PATH",
+    "EXPORTED_SYMBOLS",
+    "load_library",
+    "gemm_f16",
+    "gemv_f16",
+    "gemm_f16_ptr",
+    "gemv_f16_ptr",
+    "gemm_f16_variant",
+    "gemv_f16_variant",
+    "status_string",
+    "tile_coord",
+    "xcd_logical_id",
+    "gemm_config",
+    "gemm_grid",
+]
+
+LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemvtile.so")
+
+# Every symbol include/gemvtile.h declares.
+EXPORTED_SYMBOLS = (
+    "gemm_f16",
+    "gemv_f16",
+    "gemvtile_status_string",
+    "gemvtile_tile_coord",
+    "gemvtile_gemm_config",
+    "gemvtile_gemm_grid",
+    "gemvtile_gemm_f16_variant",
+    "gemvtile_gemv_f16_variant",
+    "gemvtile_xcd_logical_id",
+)
+
+STATUS_NAMES = {
+    0: "GEMVTILE_OK",
+    1: "GEMVTILE_ERR_INVALID_ARG",
+    2: "GEMVTILE_ERR_UNSUPPORTED",
+    3: "GEMVTILE_ERR_LAUNCH",
+    4: "GEMVTILE_ERR_DEVICE",
+}
+
+
+class GemvTileLibraryMissing(RuntimeError):
+    """libgemvtile.so is not built (run __graft_entry__.build())."""
+
+
+class GemvTileError(RuntimeError):
+    """A library call returned a nonzero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
+    """Load libgemvtile.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None and path == LIBRARY_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise GemvTileLibraryMissing(f"{path} not found; build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    intp = ctypes.POINTER(ctypes.c_int)
+    lib.gemm_f16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.gemm_f16.restype = c_int
+    lib.gemv_f16.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.gemv_f16.restype = c_int
+    lib.gemvtile_gemm_f16_variant.argtypes = [vp, vp, vp, i64, i64, i64, vp, c_int]
+    lib.gemvtile_gemm_f16_variant.restype = c_int
+    lib.gemvtile_gemv_f16_variant.argtypes = [vp, vp, vp, i64, i64, vp, c_int]
+    lib.gemvtile_gemv_f16_variant.restype = c_int
+    lib.gemvtile_status_string.argtypes = [c_int]
+    lib.gemvtile_status_string.restype = ctypes.c_char_p
+    lib.gemvtile_tile_coord.argtypes = [i64, i64, i64, i64, i64p, i64p]
+    lib.gemvtile_tile_coord.restype = c_int
+    lib.gemvtile_xcd_logical_id.argtypes = [i64, i64]
+    lib.gemvtile_xcd_logical_id.restype = i64
+    lib.gemvtile_gemm_config.argtypes = [intp] * 6
+    lib.gemvtile_gemm_config.restype = None
+    lib.gemvtile_gemm_grid.argtypes = [i64, i64, i64]
+    lib.gemvtile_gemm_grid.restype = i64
+    if path == LIBRARY_PATH:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().gemvtile_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise GemvTileError(status, status_string(status))
+
+
+# ---- raw-pointer entry points (same names and arguments as the C ABI) ------
+def gemm_f16_ptr(A: int, B: int, D: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    """Call gemm_f16 with raw device pointers; returns the status code."""
+    return int(load_library().gemm_f16(A, B, D, M, N, K, stream))
+
+
+def gemv_f16_ptr(x: int, W: int, y: int, N: int, K: int, stream: int = 0) -> int:
+    """Call gemv_f16 with raw device pointers; returns the status code."""
+    return int(load_library().gemv_f16(x, W, y, N, K, stream))
+
+
+# ---- tensor entry points ---------------------------------------------------
+def _torch():
+    import torch
+
+    return torch
+
+
+def _require(t, name, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float16:
+        raise TypeError(f"{name} must be float16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+
+
+def _stream_handle(t, stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def gemm_f16(A, B, D=None, stream=None, variant: int = 0):
+    """D = A · Bᵀ on the device.  A [M,K], B [N,K], D [M,N] fp16 contiguous.
+
+    Enqueued on `stream` (default: the current stream) and not synchronised.
+    """
+    torch = _torch()
+    _require(A, "A", 2)
+    _require(B, "B", 2)
+    M, K = A.shape
+    N, K2 = B.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if B.device != A.device:
+        raise ValueError("A and B must be on the same device")
+    if D is None:
+        D = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    else:
+        _require(D, "D", 2)
+        if tuple(D.shape) != (M, N) or D.device != A.device:
+            raise ValueError(f"D must be [{M},{N}] on {A.device}, got {tuple(D.shape)} on {D.device}")
+    s = _stream_handle(A, stream)
+    with torch.cuda.device(A.device):
+        if variant == 0:
+            st = load_library().gemm_f16(A.data_ptr(), B.data_ptr(), D.data_ptr(), M, N, K, s)
+        else:
+            st = load_library().gemvtile_gemm_f16_variant(A.data_ptr(), B.data_ptr(), D.data_ptr(), M, N, K, s, variant)
+    _check(st)
+    return D
+
+
+def gemv_f16(x, W, y=None, stream=None, variant: int = 0):
+    """y = x · Wᵀ on the device.  x [K], W [N,K], y [N] fp16 contiguous."""
+    torch = _torch()
+    _require(x, "x", 1)
+    _require(W, "W", 2)
+    N, K = W.shape
+    if x.shape[0] != K:
+        raise ValueError(f"K mismatch: x is {tuple(x.shape)}, W is {tuple(W.shape)}")
+    if W.device != x.device:
+        raise ValueError("x and W must be on the same device")
+    if y is None:
+        y = torch.empty((N,), dtype=torch.float16, device=x.device)
+    else:
+        _require(y, "y", 1)
+        if y.shape[0] != N or y.device != x.device:
+            raise ValueError(f"y must be [{N}] on {x.device}")
+    s = _stream_handle(x, stream)
+    with torch.cuda.device(x.device):
+        if variant == 0:
+            st = load_library().gemv_f16(x.data_ptr(), W.data_ptr(), y.data_ptr(), N, K, s)
+        else:
+            st = load_library().gemvtile_gemv_f16_variant(x.data_ptr(), W.data_ptr(), y.data_ptr(), N, K, s, variant)
+    _check(st)
+    return y
+
+
+def gemm_f16_variant(A, B, variant: int, D=None, stream=None):
+    """gemm_f16 through an internal kernel variant (measurement only)."""
+    return gemm_f16(A, B, D, stream, variant)
+
+
+def gemv_f16_variant(x, W, variant: int, y=None, stream=None):
+    """gemv_f16 through an internal launch shape (measurement only)."""
+    return gemv_f16(x, W, y, stream, variant)
+
+
+# ---- host-only helpers -----------------------------------------------------
+def tile_coord(t: int, tiles_m: int, tiles_n: int, group_m: int):
+    tm, tn = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().gemvtile_tile_coord(t, tiles_m, tiles_n, group_m, ctypes.byref(tm), ctypes.byref(tn)))
+    return tm.value, tn.value
+
+
+def xcd_logical_id(w: int, grid: int) -> int:
+    return int(load_library().gemvtile_xcd_logical_id(w, grid))
+
+
+def gemm_config() -> dict:
+    vals = [ctypes.c_int() for _ in range(6)]
+    load_library().gemvtile_gemm_config(*[ctypes.byref(v) for v in vals])
+    keys = ("BM", "BN", "BK", "stages", "threads", "group_m")
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+def gemm_grid(M: int, N: int, num_cus: int) -> int:
+    return int(load_library().gemvtile_gemm_grid(M, N, num_cus))

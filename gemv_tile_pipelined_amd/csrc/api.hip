@@ -1,0 +1,171 @@
+// api.hip -- the C ABI of include/gemvtile.h: argument checks, the per-device
+// compute-unit cache, and kernel launches on the caller's stream.
+//
+// Every argument check happens before the first HIP call, so invalid calls are
+// reported the same way on a machine without a GPU.  Nothing here allocates
+// device memory, synchronises, or keeps a pointer past the call.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/gemvtile.h"
+#include "kernels.hpp"
+#include "tile_order.hpp"
+
+namespace {
+
+// Largest M or N: tile origins and row indices are 32-bit in the kernels, and
+// a whole tile past the last row must still be addressable.
+constexpr int64_t kMaxRows = (int64_t{1} << 31) - 512;
+// Largest K of the GEMM: a 256-row panel of A or B (256 * K * 2 bytes) must
+// stay below 2^31 bytes, the range of one buffer descriptor's 32-bit offsets.
+constexpr int64_t kMaxGemmK = 4194296;
+// Largest K of the GEMV (chunk indices are 32-bit).
+constexpr int64_t kMaxGemvK = (int64_t{1} << 31) - 8;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+// Compute units of the current device, cached per device.
+int current_cu_count(int *out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMVTILE_ERR_DEVICE;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *out = cached;
+      return GEMVTILE_OK;
+    }
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return GEMVTILE_ERR_DEVICE;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  *out = cus;
+  return GEMVTILE_OK;
+}
+
+int check_gemm(const void *A, const void *B, const void *D, int64_t M, int64_t N, int64_t K, bool *noop) {
+  *noop = false;
+  if (M < 0 || N < 0 || K < 0) return GEMVTILE_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) {
+    *noop = true;
+    return GEMVTILE_OK;
+  }
+  if (D == nullptr) return GEMVTILE_ERR_INVALID_ARG;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMVTILE_ERR_INVALID_ARG;
+  if (M > kMaxRows || N > kMaxRows) return GEMVTILE_ERR_UNSUPPORTED;
+  if (K % 8 != 0 || K > kMaxGemmK) return GEMVTILE_ERR_UNSUPPORTED;
+  if (misaligned(D, 2)) return GEMVTILE_ERR_UNSUPPORTED;
+  if (K > 0 && (misaligned(A, 16) || misaligned(B, 16))) return GEMVTILE_ERR_UNSUPPORTED;
+  return GEMVTILE_OK;
+}
+
+int check_gemv(const void *x, const void *W, const void *y, int64_t N, int64_t K, bool *noop) {
+  *noop = false;
+  if (N < 0 || K < 0) return GEMVTILE_ERR_INVALID_ARG;
+  if (N == 0) {
+    *noop = true;
+    return GEMVTILE_OK;
+  }
+  if (y == nullptr) return GEMVTILE_ERR_INVALID_ARG;
+  if (K > 0 && (x == nullptr || W == nullptr)) return GEMVTILE_ERR_INVALID_ARG;
+  if (N > kMaxRows) return GEMVTILE_ERR_UNSUPPORTED;
+  if (K % 8 != 0 || K > kMaxGemvK) return GEMVTILE_ERR_UNSUPPORTED;
+  if (misaligned(y, 2)) return GEMVTILE_ERR_UNSUPPORTED;
+  if (K > 0 && (misaligned(x, 16) || misaligned(W, 16))) return GEMVTILE_ERR_UNSUPPORTED;
+  return GEMVTILE_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? GEMVTILE_OK : GEMVTILE_ERR_LAUNCH; }
+
+int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream, int variant) {
+  bool noop = false;
+  int st = check_gemm(A, B, D, M, N, K, &noop);
+  if (st != GEMVTILE_OK || noop) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return to_status(gt::launch_fill_zero_f16(D, M * N, s));
+  int cus = 0;
+  st = current_cu_count(&cus);
+  if (st != GEMVTILE_OK) return st;
+  return to_status(gt::launch_gemm_f16(variant, A, B, D, static_cast<int>(M), static_cast<int>(N),
+                                       static_cast<int>(K), cus, s));
+}
+
+int run_gemv(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream, int variant) {
+  bool noop = false;
+  int st = check_gemv(x, W, y, N, K, &noop);
+  if (st != GEMVTILE_OK || noop) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return to_status(gt::launch_fill_zero_f16(y, N, s));
+  return to_status(gt::launch_gemv_f16(variant, x, W, y, static_cast<int>(N), static_cast<int>(K), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream) {
+  return run_gemm(A, B, D, M, N, K, stream, 0);
+}
+
+int gemv_f16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream) {
+  return run_gemv(x, W, y, N, K, stream, 0);
+}
+
+int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream,
+                              int variant) {
+  if (variant < 0 || variant >= gt::kGemmVariants) return GEMVTILE_ERR_INVALID_ARG;
+  return run_gemm(A, B, D, M, N, K, stream, variant);
+}
+
+int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream,
+                              int variant) {
+  if (variant < 0 || variant >= gt::kGemvVariants) return GEMVTILE_ERR_INVALID_ARG;
+  return run_gemv(x, W, y, N, K, stream, variant);
+}
+
+const char *gemvtile_status_string(int status) {
+  switch (status) {
+    case GEMVTILE_OK: return "ok";
+    case GEMVTILE_ERR_INVALID_ARG: return "invalid argument (NULL pointer with a nonzero extent, or a negative size)";
+    case GEMVTILE_ERR_UNSUPPORTED: return "unsupported (K % 8 != 0, misaligned pointer, or a size beyond the limits)";
+    case GEMVTILE_ERR_LAUNCH: return "kernel launch failed";
+    case GEMVTILE_ERR_DEVICE: return "HIP device query failed";
+    default: return "unknown status";
+  }
+}
+
+int gemvtile_tile_coord(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t group_m, int64_t *tm, int64_t *tn) {
+  if (tm == nullptr || tn == nullptr || tiles_m <= 0 || tiles_n <= 0 || group_m <= 0) return GEMVTILE_ERR_INVALID_ARG;
+  if (t < 0 || t >= tiles_m * tiles_n) return GEMVTILE_ERR_INVALID_ARG;
+  const gt::TileCoord c = gt::grouped_tile(t, tiles_m, tiles_n, group_m);
+  *tm = c.tm;
+  *tn = c.tn;
+  return GEMVTILE_OK;
+}
+
+int64_t gemvtile_xcd_logical_id(int64_t w, int64_t grid) {
+  if (grid <= 0 || w < 0 || w >= grid) return -1;
+  return gt::xcd_logical_id(w, grid);
+}
+
+void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, int *group_m) {
+  if (bm) *bm = gt::kGemmBM;
+  if (bn) *bn = gt::kGemmBN;
+  if (bk) *bk = gt::kGemmBK;
+  if (stages) *stages = gt::kGemmStages;
+  if (threads) *threads = gt::kGemmThreads;
+  if (group_m) *group_m = gt::kGemmGroupM;
+}
+
+int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus) {
+  if (M <= 0 || N <= 0 || num_cus <= 0) return 0;
+  const int64_t tiles = ((M + gt::kGemmBM - 1) / gt::kGemmBM) * ((N + gt::kGemmBN - 1) / gt::kGemmBN);
+  return tiles < num_cus ? tiles : num_cus;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// device_common.hpp -- small gfx950 device primitives shared by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gt {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+
+#define GT_LDS __attribute__((address_space(3)))
+
+// Byte offset of a __shared__ object inside the workgroup's LDS allocation.
+__device__ inline uint32_t lds_addr(const void *p) {
+  // A C-style cast from a generic pointer to address space 3 is an
+  // address-space cast; the result is the 32-bit LDS byte address.
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const GT_LDS char *)p));
+}
+
+// Buffer resource descriptor for raw, byte-addressed loads from
+// [base, base + bytes).  Stride 0, no swizzle; dword 3 = 0x00020000 is the
+// gfx9-family setting (32-bit data format).  A load whose offset is at or
+// beyond `bytes` returns zeros: this is how edge tiles are zero-filled.
+// The descriptor must be wave-uniform, so every field goes through
+// readfirstlane and lives in scalar registers.
+__device__ inline int4_t make_buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  int4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p)));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r.w = 0x00020000;
+  return r;
+}
+
+// An offset no valid buffer in this library reaches (all are < 2^31 bytes):
+// a load from it returns zeros.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+// One wave-wide direct-to-LDS load: lane i fetches 16 bytes from
+// rsrc.base + voffset(i) and the hardware writes them to LDS at
+// lds_base + 16*i (M0 holds lds_base), so one instruction fills 1 KiB of LDS
+// without passing through VGPRs.  Completion is tracked by the wave's vmcnt.
+//
+// Issued as inline asm on purpose: the compiler treats its own LDS-DMA
+// builtins as possibly aliasing every later LDS read and then waits for
+// vmcnt(0) before each one, which would serialise the multi-stage ring.  The
+// ring below does its own vmcnt accounting instead.  The s_nop covers the
+// one wait state required between writing M0 and an LDS-DMA instruction.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void lds_dma_b128(int4_t rsrc, uint32_t voffset, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %2, 0 offen lds"
+      :
+      : "v"(voffset), "s"(lds_base), "s"(rsrc)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until all LDS reads and writes of this wave have completed.
+__device__ inline void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier with no implied memory waits (the callers place the
+// vmcnt / lgkmcnt waits they need right before it).  The "memory" clobber
+// keeps the compiler from moving LDS accesses across it.
+__device__ inline void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+}  // namespace gt

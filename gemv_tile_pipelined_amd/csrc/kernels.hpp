@@ -1,0 +1,27 @@
+// kernels.hpp -- launchers the C ABI layer calls, and the shape of the
+// default GEMM kernel.  All launchers enqueue on `stream` and return the HIP
+// error of the launch; they do no argument checking of their own.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gt {
+
+// Default GEMM kernel: 256x256 output tiles, K tiles of 64, a two-stage LDS
+// ring, 256 threads (4 waves), grouped tile order 8 tile rows high.
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 256;
+constexpr int kGemmBK = 64;
+constexpr int kGemmStages = 2;
+constexpr int kGemmThreads = 256;
+constexpr int kGemmGroupM = 8;
+constexpr int kGemmVariants = 4;
+constexpr int kGemvVariants = 8;
+
+hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
+                           hipStream_t stream);
+hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, hipStream_t stream);
+hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream);
+
+}  // namespace gt

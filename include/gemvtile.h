@@ -1,0 +1,162 @@
+/*
+ * gemvtile.h -- C ABI of the MI355X (gfx950) FP16 GEMM and GEMV library.
+ *
+ * Every entry point takes plain pointers and sizes; no C++ or framework type
+ * crosses this boundary.  All matrices are dense and row-major.  "fp16" means
+ * IEEE 754 binary16.  Device pointers are HIP device (or managed) pointers on
+ * the device that is current for the calling host thread.
+ *
+ * Ownership: the caller allocates and frees every buffer.  The library keeps
+ * no pointer after a call returns and allocates no device memory on these
+ * paths (no hidden workspace).
+ *
+ * Streams: every compute call is stream-ordered and asynchronous.  It
+ * enqueues its kernel on `stream` (a hipStream_t; NULL is the default stream)
+ * and returns at once; the result is ready when that stream reaches the
+ * point of the call.  Errors found before the launch are returned without any
+ * HIP call being made, so they are reported identically on a machine with no
+ * GPU.
+ *
+ * Aliasing: D (or y) must not overlap A, B (or x, W); doing so is undefined.
+ * Thread safety: calls from several host threads are safe; the library's only
+ * mutable state is a per-device cache of the compute-unit count.
+ */
+#ifndef GEMVTILE_H
+#define GEMVTILE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum gemvtile_status {
+    GEMVTILE_OK = 0,
+    GEMVTILE_ERR_INVALID_ARG = 1, /* NULL pointer with a nonzero extent, negative size */
+    GEMVTILE_ERR_UNSUPPORTED = 2, /* K % 8 != 0, misaligned pointer, size beyond the limits below */
+    GEMVTILE_ERR_LAUNCH = 3,      /* the HIP launch failed (no gfx950 device, bad stream, ...) */
+    GEMVTILE_ERR_DEVICE = 4       /* a HIP runtime query failed */
+};
+
+/*
+ * gemm_f16 -- D = A · Bᵀ with FP32 accumulation and one final rounding of each
+ * output to fp16, round-to-nearest, ties to even.
+ *
+ *   D[m,n] = fp16_rne( sum_{k<K} A[m,k] * B[n,k] )   for m < M, n < N
+ *
+ * Defined by "使用 TMA 为 GEMM 建立 Pipeline" (TVM TIRx GEMM chapter), step 4
+ * full kernel: A is (M,K), B is (N,K), D is (M,N), fp16 in and out with the
+ * accumulator in FP32; the same layout is the Croqtile tutorial's ch. 7
+ * pipelined matmul (lhs [M,K], rhs [N,K]) and the SM120 walk-through
+ * "TensorCore_GEMM_with_TMA" §2.2 entrance, whose epilogue rounds with `_rn`.
+ *
+ *   A  device pointer, [M,K] fp16, row-major (leading dimension K), 16-byte aligned
+ *   B  device pointer, [N,K] fp16, row-major (leading dimension K), 16-byte aligned
+ *   D  device pointer, [M,N] fp16, row-major (leading dimension N), 2-byte aligned;
+ *      only the M·N elements are written
+ *   M, N, K  sizes; 0 <= M, N <= 2^31 - 512; 0 <= K <= 4,194,296 and K % 8 == 0
+ *   stream   hipStream_t or NULL
+ *
+ * M == 0 or N == 0: returns GEMVTILE_OK and touches nothing (pointers may be NULL).
+ * K == 0: D is filled with +0 (the empty sum); A and B may be NULL.
+ * M, N need not be multiples of any tile size: edge tiles read zeros beyond
+ * the matrix and write only inside it.  The summation order within FP32 is
+ * unspecified (several results are correct up to rounding).
+ * Returns a gemvtile_status.
+ */
+int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * gemv_f16 -- y = x · Wᵀ (the batch-1 decode product), FP32 accumulation,
+ * one fp16 rounding (nearest, ties to even) per output.
+ *
+ *   y[n] = fp16_rne( sum_{k<K} x[k] * W[n,k] )   for n < N
+ *
+ * Defined by "Learning TileLang with GEMV", §01 GEMV: the matrix is (N,K)
+ * row-major as nn.Linear stores its weight, all kernels accumulate in FP32.
+ *
+ *   x  device pointer, [K] fp16, 16-byte aligned
+ *   W  device pointer, [N,K] fp16, row-major (leading dimension K), 16-byte aligned
+ *   y  device pointer, [N] fp16, 2-byte aligned
+ *   N, K  sizes; 0 <= N <= 2^31 - 1; 0 <= K <= 2^31 - 8 and K % 8 == 0
+ *   stream hipStream_t or NULL
+ *
+ * N == 0: returns GEMVTILE_OK and touches nothing.  K == 0: y is filled with +0.
+ * The row sums are deterministic: no atomics, no split across workgroups.
+ * Returns a gemvtile_status.
+ */
+int gemv_f16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char *gemvtile_status_string(int status);
+
+/*
+ * gemvtile_tile_coord -- the grouped tile order the persistent GEMM walks
+ * (host-callable, no GPU needed).  Tile index t in [0, tiles_m*tiles_n) maps
+ * to the output tile (*tm, *tn); consecutive t run down `group_m` tile rows of
+ * one tile column, then move to the next column; the last group may be
+ * shorter.  This is the threadblock swizzle of "TensorCore_GEMM_with_TMA"
+ * §2.3 kernel (GROUP_M = 8), which the TVM chapter's step 6 persistent
+ * scheduler (l2_group_size = 8) also uses for L2 locality.
+ * Returns GEMVTILE_ERR_INVALID_ARG for t out of range, non-positive sizes or
+ * NULL outputs.
+ */
+int gemvtile_tile_coord(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t group_m, int64_t *tm, int64_t *tn);
+
+/*
+ * gemvtile_gemm_config -- the compile-time shape of the GEMM kernel that
+ * gemm_f16 launches: output tile BM x BN, K tile BK, LDS ring depth, threads
+ * per workgroup and the grouped-order height.  Any output pointer may be NULL.
+ */
+void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, int *group_m);
+
+/*
+ * gemvtile_gemm_grid -- the number of workgroups gemm_f16 launches for an
+ * M x N output on a device with `num_cus` compute units (persistent grid:
+ * min(#tiles, num_cus)).  Host-only arithmetic; returns 0 for empty outputs.
+ */
+int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
+
+/*
+ * gemvtile_gemm_f16_variant -- gemm_f16 with an internal kernel variant, for
+ * ablation measurements only (same contract and results as gemm_f16):
+ *   0  the default kernel (identical to gemm_f16)
+ *   1  no LDS swizzle (plain row-major LDS tiles)
+ *   2  single-stage LDS (load, wait, compute: no overlap)
+ *   3  one workgroup per tile (no persistent loop), no XCD remap
+ * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
+ */
+int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
+                              void *stream, int variant);
+
+/*
+ * gemvtile_gemv_f16_variant -- gemv_f16 with an internal launch shape, for
+ * measurements only (same contract and results as gemv_f16).  A variant fixes
+ * the rows per wave, waves per workgroup, chunk steps in flight per lane and
+ * whether W is read with non-temporal loads:
+ *   0 = 4 rows, 4 waves, 4 steps, non-temporal (the gemv_f16 default)
+ *   1 = as 0 with ordinary loads      2 = 2 rows, 4 waves, 4 steps, nt
+ *   3 = 1 row, 4 waves, 8 steps, nt   4 = 4 rows, 2 waves, 4 steps, nt
+ *   5 = 2 rows, 8 waves, 4 steps, nt  6 = 4 rows, 4 waves, 2 steps, nt
+ *   7 = 8 rows, 4 waves, 2 steps, nt
+ * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
+ */
+int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream,
+                              int variant);
+
+/*
+ * gemvtile_xcd_logical_id -- the logical workgroup id the persistent GEMM
+ * gives hardware workgroup `w` of a `grid`-wide launch.  Workgroups are
+ * dispatched to the 8 XCDs round-robin; when grid % 8 == 0 the renumbering
+ * gives each XCD one contiguous range of ids (so neighbouring tiles in the
+ * grouped order share an L2), otherwise it is the identity.  Host-only;
+ * returns -1 for w outside [0, grid) or grid <= 0.
+ */
+int64_t gemvtile_xcd_logical_id(int64_t w, int64_t grid);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMVTILE_H */

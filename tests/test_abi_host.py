@@ -1,0 +1,192 @@
+"""Host-side checks of the C ABI library: loading, exported symbols, argument
+validation (no GPU needed: every check happens before the first HIP call),
+the tile scheduler's mapping and the measurement formulas."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemv_tile_pipelined_amd as gt
+from gemv_tile_pipelined_amd import metrics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemvtile.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gt.LIBRARY_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return gt.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(gt.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert gt.status_string(code)
+    assert gt.status_string(99) == "unknown status"
+
+
+def _gemm(lib, A, B, D, M, N, K):
+    return lib.gemm_f16(A, B, D, M, N, K, None)
+
+
+def _gemv(lib, x, W, y, N, K):
+    return lib.gemv_f16(x, W, y, N, K, None)
+
+
+FAKE = 0x10000  # a 16-byte aligned address; never dereferenced by these calls
+
+
+def test_gemm_argument_validation(lib):
+    assert _gemm(lib, FAKE, FAKE, FAKE, -1, 4, 8) == INVALID
+    assert _gemm(lib, FAKE, FAKE, FAKE, 4, -1, 8) == INVALID
+    assert _gemm(lib, FAKE, FAKE, FAKE, 4, 4, -8) == INVALID
+    assert _gemm(lib, FAKE, FAKE, None, 4, 4, 8) == INVALID
+    assert _gemm(lib, None, FAKE, FAKE, 4, 4, 8) == INVALID
+    assert _gemm(lib, FAKE, None, FAKE, 4, 4, 8) == INVALID
+    # empty outputs are a no-op, even with NULL pointers
+    assert _gemm(lib, None, None, None, 0, 4, 8) == OK
+    assert _gemm(lib, None, None, None, 4, 0, 8) == OK
+    # K must be a multiple of 8; A/B 16-byte aligned; D 2-byte aligned
+    assert _gemm(lib, FAKE, FAKE, FAKE, 4, 4, 12) == UNSUPPORTED
+    assert _gemm(lib, FAKE + 8, FAKE, FAKE, 4, 4, 8) == UNSUPPORTED
+    assert _gemm(lib, FAKE, FAKE + 2, FAKE, 4, 4, 8) == UNSUPPORTED
+    assert _gemm(lib, FAKE, FAKE, FAKE + 1, 4, 4, 8) == UNSUPPORTED
+    # size limits
+    assert _gemm(lib, FAKE, FAKE, FAKE, 4, 4, 4194304) == UNSUPPORTED
+    assert _gemm(lib, FAKE, FAKE, FAKE, 2**31, 4, 8) == UNSUPPORTED
+    # unknown internal variant
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, 99) == INVALID
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, -1) == INVALID
+
+
+def test_gemv_argument_validation(lib):
+    assert _gemv(lib, FAKE, FAKE, FAKE, -1, 8) == INVALID
+    assert _gemv(lib, FAKE, FAKE, FAKE, 4, -8) == INVALID
+    assert _gemv(lib, FAKE, FAKE, None, 4, 8) == INVALID
+    assert _gemv(lib, None, FAKE, FAKE, 4, 8) == INVALID
+    assert _gemv(lib, FAKE, None, FAKE, 4, 8) == INVALID
+    assert _gemv(lib, None, None, None, 0, 8) == OK
+    assert _gemv(lib, FAKE, FAKE, FAKE, 4, 9) == UNSUPPORTED
+    assert _gemv(lib, FAKE + 4, FAKE, FAKE, 4, 8) == UNSUPPORTED
+    assert _gemv(lib, FAKE, FAKE + 8, FAKE, 4, 8) == UNSUPPORTED
+    assert _gemv(lib, FAKE, FAKE, FAKE + 1, 4, 8) == UNSUPPORTED
+    assert lib.gemvtile_gemv_f16_variant(FAKE, FAKE, FAKE, 4, 8, None, 99) == INVALID
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(gt.GemvTileLibraryMissing):
+        gt.load_library(str(tmp_path / "missing.so"))
+
+
+def _tile_counts():
+    out = {}
+    for line in open(os.path.join(GOLDEN, "tile_counts.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split()
+            out[k] = int(v)
+    return out
+
+
+@pytest.mark.parametrize(
+    "M,N",
+    [(256, 256), (4096, 4096), (4000, 4032), (8192, 8192), (257, 255), (2304, 4096), (100, 9000), (4096, 128)],
+)
+def test_grouped_order_is_a_bijection(lib, M, N):
+    cfg = gt.gemm_config()
+    tiles_m = -(-M // cfg["BM"])
+    tiles_n = -(-N // cfg["BN"])
+    seen = set()
+    for t in range(tiles_m * tiles_n):
+        tm, tn = gt.tile_coord(t, tiles_m, tiles_n, cfg["group_m"])
+        assert 0 <= tm < tiles_m and 0 <= tn < tiles_n
+        seen.add((tm, tn))
+    assert len(seen) == tiles_m * tiles_n
+
+
+def test_grouped_order_shape(lib):
+    # Inside a full group the index runs down group_m tile rows of one column,
+    # then moves to the next column; the last group may be shorter.
+    assert [gt.tile_coord(t, 16, 16, 8) for t in range(10)] == [(r, 0) for r in range(8)] + [(0, 1), (1, 1)]
+    # tiles_m = 10 with group_m = 8: the second group is 2 rows high
+    assert [gt.tile_coord(t, 10, 3, 8) for t in range(24, 30)] == [(8, 0), (9, 0), (8, 1), (9, 1), (8, 2), (9, 2)]
+
+
+def test_tile_coord_rejects_bad_input(lib):
+    tm, tn = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.gemvtile_tile_coord(16, 4, 4, 8, ctypes.byref(tm), ctypes.byref(tn)) == INVALID
+    assert lib.gemvtile_tile_coord(-1, 4, 4, 8, ctypes.byref(tm), ctypes.byref(tn)) == INVALID
+    assert lib.gemvtile_tile_coord(0, 0, 4, 8, ctypes.byref(tm), ctypes.byref(tn)) == INVALID
+    assert lib.gemvtile_tile_coord(0, 4, 4, 0, ctypes.byref(tm), ctypes.byref(tn)) == INVALID
+    assert lib.gemvtile_tile_coord(0, 4, 4, 8, None, ctypes.byref(tn)) == INVALID
+
+
+@pytest.mark.parametrize("grid", [1, 7, 8, 64, 200, 256, 1024])
+def test_xcd_renumbering_is_a_bijection(lib, grid):
+    ids = [gt.xcd_logical_id(w, grid) for w in range(grid)]
+    assert sorted(ids) == list(range(grid))
+    if grid % 8 == 0:
+        # workgroup w runs on XCD w % 8; each XCD owns one contiguous id range
+        per = grid // 8
+        for w in range(grid):
+            assert ids[w] // per == w % 8
+    assert gt.xcd_logical_id(grid, grid) == -1
+
+
+def test_gemm_grid_and_golden_counts(lib):
+    cfg = gt.gemm_config()
+    assert cfg == {"BM": 256, "BN": 256, "BK": 64, "stages": 2, "threads": 256, "group_m": 8}
+    assert gt.gemm_grid(4096, 4096, 256) == 256
+    assert gt.gemm_grid(8192, 8192, 256) == 256
+    assert gt.gemm_grid(256, 256, 256) == 1
+    assert gt.gemm_grid(4000, 4032, 256) == 256
+    assert gt.gemm_grid(0, 4, 256) == 0
+    golden = _tile_counts()
+    # The TVM chapter's counts at its 128x128 tiles and BLK_K = 64: the same
+    # tile-count arithmetic, applied to its parameters.
+    assert -(-4096 // 128) * -(-4096 // 128) == golden["tiles_4096x4096_at_128x128"]
+    assert 4096 // 64 == golden["k_iterations_k4096_bk64"]
+    assert golden["k_iterations_k4096_bk64"] // 2 == golden["uses_per_stage_depth2"]
+    assert 128 * 64 * metrics.FP16_BYTES == golden["tile_bytes_128x64"]
+    assert (128 * 64 + 128 * 64) * metrics.FP16_BYTES == golden["stage_bytes_128x64_pair"]
+    # every output tile visited once: 1024 tiles at 128x128 for 4096^2
+    seen = {gt.tile_coord(t, 32, 32, 8) for t in range(1024)}
+    assert len(seen) == golden["tiles_4096x4096_at_128x128"]
+
+
+def test_measurement_formulas_match_table1():
+    rows = {}
+    for line in open(os.path.join(GOLDEN, "gemv_table1.txt")):
+        if line.strip() and not line.startswith("#"):
+            parts = line.split()
+            rows[parts[0]] = [int(p) for p in parts[1:]]
+    N, K = 4096, 14336
+    el = metrics.gemv_elements(N, K)
+    for name in ("W", "x", "y", "total"):
+        assert el[name] == rows[name][0], name
+        assert el[name] * metrics.FP16_BYTES == rows[name][1], name
+    assert metrics.gemv_bytes(N, K) == rows["total"][1]
+    assert metrics.gemv_flops(N, K) == rows["flops"][0]
+    assert metrics.gemm_flops(4096, 4096, 4096) == 137438953472
