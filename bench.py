@@ -1,15 +1,16 @@
 """Benchmark of the FP16 GEMM / GEMV hot path on one MI355X.
 
-One step = one gemm_f16 at M = N = K = 4096 plus one gemv_f16 at N = 4096,
-K = 14336 (the whole hot path), on seeded synthetic fp16 inputs already
-resident in device memory.  The GEMM rotates over 3 input sets and the GEMV
-over 5 copies of W (587 MB, more than twice the 256 MB MALL) so the GEMV
-streams W from HBM on every step rather than from cache.
+One step = one gemm_f16 at M = N = K = 4096 plus five gemv_f16 at N = 4096,
+K = 14336, one over each of five distinct copies of W (the whole hot path;
+587 MB of W per step, more than twice the 256 MB MALL, so every GEMV streams
+its W from HBM rather than from cache), on seeded synthetic fp16 inputs
+already resident in device memory.  The GEMM rotates over 3 input sets.
 
 Prints ONE JSON line on stdout:
   value        GEMM TFLOP/s (2·M·N·K / mean GEMM kernel time, HIP events)
   roofline     GEMM against the dense fp16 MFMA peak
-  gemv         GEMV GB/s (algorithmic bytes 2·(N·K + K + N) / mean kernel time)
+  gemv         GEMV GB/s (algorithmic bytes 2·(N·K + K + N) / mean kernel time,
+               the five back-to-back launches of a step timed together)
                with its own roofline against the HBM peak
   cpu_baseline the CPU oracle (FP64, OpenMP) on a bounded sample of rows of
                the same GEMM, scaled to TFLOP/s, plus the full GEMV in GB/s
@@ -32,9 +33,27 @@ GEMM_M = GEMM_N = GEMM_K = 4096
 GEMV_N, GEMV_K = 4096, 14336
 GEMM_SETS = 3
 GEMV_COPIES = 5
-# Where a rocprofv3 --pmc run measured the HBM traffic of the current kernels
-# (KiB per dispatch, scaled by the copy-kernel calibration); None until taken.
-MEASURED_TRAFFIC = {"gemm": None, "gemv": None}
+# Beyond-L2 traffic per launch measured with rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch, each scaled by what the same counter reads for
+# a device copy of known size: x2.000 for FETCH_SIZE, x1.000 for WRITE_SIZE),
+# valid only for the kernel sources whose SHA-256 is recorded here; the
+# summary and commands are in profiles/traffic_fetch_write_size.md.
+MEASURED_TRAFFIC = {
+    "sources_sha256": "87c2b2f8fc275207d67e5a17bd0c688fed6562cfe5b779d01c3633e5ee47abb8",
+    "gemm": {"fetch_kib": 98427.5 * 2.0, "write_kib": 32768.0 * 1.0},
+    "gemv": {"fetch_kib": 57476.0 * 2.0, "write_kib": 8.0 * 1.0},
+}
+KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemv.hip", "kernels.hpp", "tile_order.hpp")
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gemv_tile_pipelined_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -61,12 +80,15 @@ def cpu_baseline(target_s: float):
     threads = oracle.max_threads(lib)
     w = datagen.WORKLOADS[1]
     A, B = datagen.gemm_inputs(w)
-    # calibrate on a few rows, then size the sample to about target_s seconds
-    rows = datagen.sample_rows(1, w.M, 16)
+    # calibrate on 64 rows (the fixed cost of decoding B is paid in both
+    # runs), then size the sample to about target_s seconds, at most the
+    # whole GEMM
+    rows = datagen.sample_rows(1, w.M, 64)
+    oracle.gemm(A, B, rows=rows[:8], lib=lib)
     t0 = time.perf_counter()
     oracle.gemm(A, B, rows=rows, lib=lib)
     dt = time.perf_counter() - t0
-    n = int(max(16, min(w.M, 16 * target_s / max(dt, 1e-6))))
+    n = int(max(64, min(w.M, 64 * target_s / max(dt, 1e-6))))
     rows = datagen.sample_rows(1, w.M, n)
     t0 = time.perf_counter()
     oracle.gemm(A, B, rows=rows, lib=lib)
@@ -84,7 +106,7 @@ def cpu_baseline(target_s: float):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"gemm 4096^3 restricted to {len(rows)} seeded output rows x 4096 cols x K 4096 "
+        "sample": f"gemm 4096^3 on {len(rows)} of 4096 seeded output rows x 4096 cols x K 4096 "
         f"({flops / 2:.3g} FP64 FMAs, {dt:.1f} s); FP64 triple loop, OpenMP over rows",
         "seconds": dt,
         "gemv_gbps": metrics.gemv_bytes(wv.N, wv.K) / dtv / 1e9,
@@ -150,13 +172,13 @@ def main():
 
     def step(i, ev=None):
         A, B, D = gemm_sets[i % GEMM_SETS]
-        W, y = gemv_sets[i % GEMV_COPIES]
         if ev:
             ev[0].record(stream)
         st = gt.gemm_f16_ptr(A.data_ptr(), B.data_ptr(), D.data_ptr(), M, N, K, sh)
         if ev:
             ev[1].record(stream)
-        st |= gt.gemv_f16_ptr(x.data_ptr(), W.data_ptr(), y.data_ptr(), wv.N, wv.K, sh)
+        for W, y in gemv_sets:
+            st |= gt.gemv_f16_ptr(x.data_ptr(), W.data_ptr(), y.data_ptr(), wv.N, wv.K, sh)
         if ev:
             ev[2].record(stream)
         if st:
@@ -177,7 +199,7 @@ def main():
     gemm_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     gemv_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     gemm_s = float(gemm_ms.mean()) / 1e3
-    gemv_s = float(gemv_ms.mean()) / 1e3
+    gemv_s = float(gemv_ms.mean()) / 1e3 / GEMV_COPIES
     flops = metrics.gemm_flops(M, N, K)
     gemm_tflops = flops / gemm_s / 1e12
     gemv_bytes = metrics.gemv_bytes(wv.N, wv.K)
@@ -186,7 +208,12 @@ def main():
     cpu = cpu_baseline(args.cpu_seconds)
 
     def traffic(kind):
-        return MEASURED_TRAFFIC[kind]
+        # HBM-side bytes per launch, or None once the kernels have changed
+        # since the counters were taken.
+        if kernel_sources_sha256() != MEASURED_TRAFFIC["sources_sha256"]:
+            return None
+        t = MEASURED_TRAFFIC[kind]
+        return int((t["fetch_kib"] + t["write_kib"]) * 1024)
 
     line = {
         "metric": METRIC,
@@ -202,7 +229,8 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "gemm_f16 D=A·Bᵀ 4096x4096x4096 + gemv_f16 y=x·Wᵀ 4096x14336, fp16 in/out, fp32 accumulate",
+            "workload": "gemm_f16 D=A·Bᵀ 4096x4096x4096 + 5x gemv_f16 y=x·Wᵀ 4096x14336 (5 distinct W), "
+            "fp16 in/out, fp32 accumulate",
             "M": M,
             "N": N,
             "K": K,

@@ -54,14 +54,27 @@ constexpr uint32_t kOobOffset = 0x80000000u;
 // one wait state required between writing M0 and an LDS-DMA instruction.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// POLICY selects the cache-policy modifier of the load: 0 none, 1 sc0,
+// 2 nt, 3 sc0 nt, 4 sc1.
+template <int POLICY = 0>
 __device__ inline void lds_dma_b128(int4_t rsrc, uint32_t voffset, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %2, 0 offen lds"
-      :
-      : "v"(voffset), "s"(lds_base), "s"(rsrc)
-      : "memory", "m0");
+  static_assert(POLICY >= 0 && POLICY <= 4, "cache policy");
+  if constexpr (POLICY == 0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
+  } else if constexpr (POLICY == 1) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen sc0 lds"
+                 : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
+  } else if constexpr (POLICY == 2) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen nt lds"
+                 : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
+  } else if constexpr (POLICY == 3) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen sc0 nt lds"
+                 : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
+  } else {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen sc1 lds"
+                 : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
+  }
 }
 #pragma clang diagnostic pop
 

@@ -24,30 +24,39 @@
 //    behaviour of Croqtile ch. 7 (irregular access), which keeps the MFMA
 //    loop uniform on edge tiles.
 //
-//  * LDS layout -- rows of BK fp16 (128 bytes) in 16-byte chunks; chunk c of
-//    row r is stored at chunk c ^ swz(r).  The loader applies the XOR by
-//    choosing which global chunk each lane fetches (the LDS side of a DMA
-//    instruction is fixed: lane i -> 16*i), and the MFMA operand reads apply
-//    the same XOR, so writer and reader agree (Croqtile ch. 7 swizzle rule;
-//    the 128-byte swizzle of the TVM chapter and of the SM120 page's
-//    ldmatrix addressing play the same role there).
+//  * LDS layout -- rows of BK fp16 in 16-byte chunks; chunk c of row r is
+//    stored at chunk c ^ swz(r).  The loader applies the XOR by choosing which
+//    global chunk each lane fetches (the LDS side of a DMA instruction is
+//    fixed: lane i -> 16*i), and the MFMA operand reads apply the same XOR, so
+//    writer and reader agree (Croqtile ch. 7 swizzle rule; the 128-byte
+//    swizzle of the TVM chapter and of the SM120 page's ldmatrix addressing
+//    play the same role there).
 //
-//  * LDS ring -- STAGES buffers, all filled by the prologue.  In the last
-//    16-wide K step of K tile k, each wave waits (vmcnt) for tile k+1 while
-//    younger tiles stay in flight, finishes its LDS reads of stage k, meets
-//    the other waves at one barrier, refills stage k with tile k + STAGES, and
-//    fetches tile k+1's first MFMA operands while the step's MFMAs run.  The
-//    wait count and the stage index come from the loop counter, so nothing
-//    resets between output tiles (a ragged K = 4104 has 65 K tiles).  TVM chapter step 5 (Pipeline 机制) and the
-//    SM120 page's multistage main loop describe the same ring with mbarriers.
+//  * LDS ring -- STAGES buffers; K tile t lives in stage t % STAGES.  In the
+//    final 16-wide K step of tile k each wave waits (vmcnt) until tile k+1
+//    has landed while younger tiles stay in flight, completes its LDS reads,
+//    and meets the other waves at the one barrier of the K tile; that barrier
+//    frees stage k, whose refill with tile k + STAGES starts at once, the
+//    loads threaded between the MFMAs that follow.  Tile k+1's first
+//    operands are fetched during the same MFMAs.  Stage index and wait count follow from the
+//    loop counter, so nothing resets between output tiles (a ragged K = 4104
+//    has an odd number of K tiles).  TVM chapter step 5 (Pipeline 机制) and
+//    the SM120 page's multistage main loop describe the same ring with
+//    mbarriers.
 //
 //  * MFMA micro-kernel -- v_mfma_f32_32x32x16_f16.  B rows feed the first
 //    operand and A rows the second, so each lane ends up holding four
-//    consecutive output columns of one output row (8-byte stores).
+//    consecutive output columns of one output row (8-byte stores).  Operand
+//    fetches for the next K step are interleaved with the current step's
+//    MFMAs.
 //
 //  * Epilogue -- FP32 -> fp16 with round-to-nearest-even (the `_rn`
-//    conversion of the SM120 page's epilogue), masked to the M x N region.
+//    conversion of the SM120 page's epilogue), staged through LDS so D is
+//    written in whole row segments (the TVM chapter likewise stages D in
+//    shared memory before its bulk store), masked to the M x N region.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -55,7 +64,8 @@
 
 namespace gt {
 
-template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, bool SWIZZLE_, bool PERSISTENT_>
+template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, bool SWIZZLE_, bool PERSISTENT_,
+          int DMA_STRIDE_, int DMA_PHASES_, int K_STAGGER_ = 1, int K_STAGGER_STEP_ = 1, int LOAD_POLICY_ = 0>
 struct GemmShape {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -65,6 +75,20 @@ struct GemmShape {
   static constexpr int WAVES_N = WAVES_N_;
   static constexpr bool SWIZZLE = SWIZZLE_;
   static constexpr bool PERSISTENT = PERSISTENT_;
+  // MFMA slots between two consecutive loads of the ring refill, and the
+  // number of slot phases the waves are spread over (wave w issues its loads
+  // DMA_STRIDE / DMA_PHASES * (w % DMA_PHASES) slots later than wave 0).
+  static constexpr int DMA_STRIDE = DMA_STRIDE_;
+  static constexpr int DMA_PHASES = DMA_PHASES_;
+  static_assert(DMA_STRIDE % DMA_PHASES == 0, "phases divide the stride");
+  // K-loop start stagger: output tile t walks its K tiles starting at tile
+  // (t % K_STAGGER) * K_STAGGER_STEP (mod the K tile count) and wraps around,
+  // so workgroups running side by side read different K columns at any
+  // moment instead of all hitting the same one.
+  static constexpr int K_STAGGER = K_STAGGER_;
+  static constexpr int K_STAGGER_STEP = K_STAGGER_STEP_;
+  // Cache-policy modifier of the tile loads (see lds_dma_b128).
+  static constexpr int LOAD_POLICY = LOAD_POLICY_;
 
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = kWaves * 64;
@@ -73,28 +97,41 @@ struct GemmShape {
   static constexpr int kFragM = kWaveM / 32;   // 32x32 MFMA blocks per wave, M
   static constexpr int kFragN = kWaveN / 32;   // 32x32 MFMA blocks per wave, N
   static constexpr int kRowBytes = BK * 2;
-  static constexpr int kChunks = BK / 8;           // 16-byte chunks per LDS row
+  static constexpr int kChunks = BK / 8;            // 16-byte chunks per LDS row
   static constexpr int kRowsPerDma = 64 / kChunks;  // rows one wave DMA fills
   static constexpr int kDmaA = BM / kRowsPerDma / kWaves;  // per-wave DMA instrs for A
   static constexpr int kDmaB = BN / kRowsPerDma / kWaves;
   static constexpr int kDmaPerStage = kDmaA + kDmaB;
   static constexpr int kStageA = BM * kRowBytes;
   static constexpr int kStageBytes = (BM + BN) * kRowBytes;
-  static constexpr int kLdsBytes = STAGES * kStageBytes;
+  // Epilogue staging: each wave's kWaveM x kWaveN fp16 tile, rows padded by
+  // 16 bytes (keeps 16-byte row alignment for the read-back and spreads the
+  // column-wise writes over the banks).
+  static constexpr int kStagePitch = kWaveN * 2 + 16;
+  static constexpr int kStagingBytes = kWaves * kWaveM * kStagePitch;
+  static constexpr int kRingBytes = STAGES * kStageBytes;
+  static constexpr int kLdsBytes = kRingBytes > kStagingBytes ? kRingBytes : kStagingBytes;
   static constexpr int kKSub = BK / 16;  // MFMA K steps per K tile
 
-  static_assert(BK == 64, "the swizzle and fragment addressing assume 128-byte LDS rows");
+  static_assert(BK == 32 || BK == 64, "LDS rows of 64 or 128 bytes");
   static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
   static_assert(BM % (kRowsPerDma * kWaves) == 0 && BN % (kRowsPerDma * kWaves) == 0, "DMA split");
   static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
   static_assert(STAGES >= 1 && (STAGES - 1) * kDmaPerStage <= 63, "vmcnt range");
 
-  // Physical 16-byte chunk of logical chunk c in LDS row r.  With 8 chunks
-  // per 128-byte row, any 8 consecutive rows read at one logical chunk land
-  // on 8 different chunk positions (conflict-free with 8 lanes per LDS
-  // cycle), and any 16 consecutive rows cover all 16 chunk positions of a
-  // 256-byte bank window (conflict-free with 16 lanes per cycle).
-  __host__ __device__ static constexpr int swz(int row) { return SWIZZLE ? ((row & 7) ^ ((row >> 3) & 1)) : 0; }
+  // Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r);
+  // swz depends only on r & 15.  An operand fetch reads one logical chunk
+  // from 32 consecutive rows.  128-byte rows (8 chunks): any 8 consecutive
+  // rows land on 8 different chunk positions (conflict-free when 8 lanes
+  // share an LDS cycle) and any 16 consecutive rows cover the 16 positions of
+  // a 256-byte bank window (conflict-free with 16 lanes per cycle).  64-byte
+  // rows (4 chunks, two rows per 128 bytes): the same two properties hold
+  // with the XOR taken from rows' bits 1..3.
+  __host__ __device__ static constexpr int swz(int row) {
+    if (!SWIZZLE) return 0;
+    if (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
+    return ((row >> 1) ^ ((row >> 3) & 1)) & 3;
+  }
 };
 
 // Wave-uniform wait until the K tile this wave needs next has landed in LDS,
@@ -117,13 +154,19 @@ __device__ inline void wait_tile_landed(int younger) {
       return;
     }
   }
+  if constexpr (S::STAGES >= 4) {
+    if (younger >= S::STAGES - 3) {
+      wait_vmcnt<(S::STAGES - 3) * S::kDmaPerStage>();
+      return;
+    }
+  }
   wait_vmcnt<0>();
 }
 
 template <class S>
 __global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
-                int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
+                int M, int N, int K, int tiles_m, int tiles_n, int vec16) {
   __shared__ __attribute__((aligned(1024))) char smem[S::kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -138,11 +181,13 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
 
   // ---- loader geometry ----------------------------------------------------
   // DMA instruction i of this wave fills the kRowsPerDma LDS rows starting at
-  // row (i*kWaves + wave)*kRowsPerDma; lane l writes physical chunk l % 8 of
-  // row i*kRowsPerDma*kWaves + ld_row, so it fetches logical chunk
-  // (l % 8) ^ swz(row) of that row.  swz() only sees row & 15, which does not
-  // depend on i, so one offset per lane serves every instruction (instruction
-  // i adds i * kRowsPerDma*kWaves rows).  A and B tiles use the same pattern.
+  // row (i*kWaves + wave)*kRowsPerDma; lane l writes physical chunk
+  // l % kChunks of the row i*kRowsPerDma*kWaves + ld_row, so it fetches the
+  // logical chunk (l % kChunks) ^ swz(row) of that row.  Each instruction
+  // starts at a multiple of 16 rows, so swz(row) does not depend on i: one
+  // offset per lane serves every instruction (instruction i adds
+  // i*kRowsPerDma*kWaves rows).  A and B tiles use the same pattern.
+  static_assert(S::kRowsPerDma * S::kWaves % 16 == 0, "DMA row blocks must keep swz() per-lane");
   const int ld_row = wave * S::kRowsPerDma + lane / S::kChunks;
   const int ld_kcol = ((lane % S::kChunks) ^ S::swz(ld_row)) * 8;
   const uint32_t ld_off = static_cast<uint32_t>(ld_row) * static_cast<uint32_t>(K) * 2u +
@@ -180,31 +225,56 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
     int tile_ld_kcol = ld_kcol;
     asm volatile("" : "+v"(tile_ld_off), "+v"(tile_ld_kcol));
 
-    auto issue_tile = [&](int kt) {
-      const int k0 = kt * S::BK;
+    // Loads [first, last) of the kDmaPerStage per-wave DMA instructions of K
+    // tile kt (A tile first, then B tile).
+    // K tile kt of the loop reads K tile (kt + kofs) mod KT of the matrices.
+    int kofs = 0;
+    if constexpr (S::K_STAGGER > 1) kofs = static_cast<int>((t % S::K_STAGGER) * S::K_STAGGER_STEP) % KT;
+    auto issue_loads = [&](int kt, int first, int last) {
+      int ka = kt + kofs;
+      if (ka >= KT) ka -= KT;
+      const int k0 = ka * S::BK;
       // K chunks at or past K read as zero (the ragged K tail).
       const uint32_t off = (k0 + tile_ld_kcol < K) ? tile_ld_off + static_cast<uint32_t>(k0) * 2u : kOobOffset;
       const uint32_t stage_lds = lds0 + static_cast<uint32_t>((kt % S::STAGES) * S::kStageBytes) +
                                  static_cast<uint32_t>(wave * S::kRowsPerDma * S::kRowBytes);
 #pragma unroll
-      for (int i = 0; i < S::kDmaA; ++i)
-        lds_dma_b128(rsrc_a, off + i * ld_step, __builtin_amdgcn_readfirstlane(stage_lds + i * kLdsStep));
-#pragma unroll
-      for (int i = 0; i < S::kDmaB; ++i)
-        lds_dma_b128(rsrc_b, off + i * ld_step,
-                     __builtin_amdgcn_readfirstlane(stage_lds + S::kStageA + i * kLdsStep));
+      for (int d = 0; d < S::kDmaPerStage; ++d) {
+        if (d < first || d >= last) continue;
+        if (d < S::kDmaA) {
+          lds_dma_b128<S::LOAD_POLICY>(rsrc_a, off + d * ld_step,
+                                       __builtin_amdgcn_readfirstlane(stage_lds + d * kLdsStep));
+        } else {
+          const int i = d - S::kDmaA;
+          lds_dma_b128<S::LOAD_POLICY>(rsrc_b, off + i * ld_step,
+                                       __builtin_amdgcn_readfirstlane(stage_lds + S::kStageA + i * kLdsStep));
+        }
+      }
     };
 
     half8_t fa[2][S::kFragM], fb[2][S::kFragN];
-    auto load_frags = [&](int buf, int kt, int ks) {
+    // Operand read r (of kReads) of K step ks of K tile kt into buffer buf.
+    // Reads go out as fa[0], fb[0..kFragN-1], fa[1..kFragM-1], which is the
+    // order the row-major MFMA sequence below first needs them in.
+    constexpr int kReads = S::kFragM + S::kFragN;
+    constexpr int kMfma = S::kFragM * S::kFragN;
+    static_assert(kMfma >= 2 * kReads - 8 && kMfma >= kReads, "MFMA slots for the operand reads");
+    auto read_frag = [&](int buf, int kt, int ks, int r) {
       const char *stage_ptr = smem + (kt % S::STAGES) * S::kStageBytes;
       const uint32_t chunk = static_cast<uint32_t>(((ks * 2 + frag_half) ^ frag_swz) * 16);
-#pragma unroll
-      for (int i = 0; i < S::kFragM; ++i)
-        fa[buf][i] = *reinterpret_cast<const half8_t *>(stage_ptr + a_row_base + i * 32 * S::kRowBytes + chunk);
-#pragma unroll
-      for (int j = 0; j < S::kFragN; ++j)
+      if (r == 0) {
+        fa[buf][0] = *reinterpret_cast<const half8_t *>(stage_ptr + a_row_base + chunk);
+      } else if (r <= S::kFragN) {
+        const int j = r - 1;
         fb[buf][j] = *reinterpret_cast<const half8_t *>(stage_ptr + b_row_base + j * 32 * S::kRowBytes + chunk);
+      } else {
+        const int i = r - S::kFragN;
+        fa[buf][i] = *reinterpret_cast<const half8_t *>(stage_ptr + a_row_base + i * 32 * S::kRowBytes + chunk);
+      }
+    };
+    auto load_frags = [&](int buf, int kt, int ks) {
+#pragma unroll
+      for (int r = 0; r < kReads; ++r) read_frag(buf, kt, ks, r);
     };
 
     float16_t acc[S::kFragM][S::kFragN];
@@ -215,111 +285,208 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    auto mfma_step = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < S::kFragM; ++i)
-#pragma unroll
-        for (int j = 0; j < S::kFragN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+    auto mfma = [&](int buf, int idx) {
+      const int i = idx / S::kFragN;
+      const int j = idx % S::kFragN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
     };
 
-    // Every wave must be done with the previous output tile's LDS before the
-    // ring is refilled, and the previous tile's stores must have left the
-    // counter so the ring's vmcnt accounting below counts only its own loads.
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
+    // Every wave must be done with the previous output tile's LDS (ring and
+    // epilogue staging) before the ring is refilled.  The previous tile's
+    // stores may still be in flight: they are older than every ring load, so
+    // they can only make the ring's vmcnt waits more conservative.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     workgroup_barrier();
 
     if constexpr (S::STAGES == 1) {
       // No overlap: load, wait, compute -- the serial order the TVM chapter
       // starts from before its step 5 adds a second stage.
       for (int kt = 0; kt < KT; ++kt) {
-        issue_tile(kt);
+        issue_loads(kt, 0, S::kDmaPerStage);
         wait_vmcnt<0>();
         workgroup_barrier();
 #pragma unroll
         for (int ks = 0; ks < S::kKSub; ++ks) {
           load_frags(0, kt, ks);
-          mfma_step(0);
+#pragma unroll
+          for (int idx = 0; idx < kMfma; ++idx) mfma(0, idx);
         }
-        wait_lgkmcnt0();
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         workgroup_barrier();
       }
     } else {
-      // Prologue: every stage of the ring gets a K tile.
+      // One K tile in a fixed instruction order (sched_barrier pins it).
+      // Each MFMA slot of a non-final K step carries one operand read for the
+      // next step; the final K step meets the other waves after its first
+      // kBarrierAt MFMAs and fetches the next K tile's first operands during
+      // the rest.  The barrier frees stage kt, and its refill with K tile
+      // kt + STAGES starts right there.  The refill's loads go out one every
+      // DMA_STRIDE MFMA slots: bunched together, the four waves' loads
+      // saturate the texture path and stall MFMA issue, while spread too
+      // thin the last load lands too close to the barrier that needs it.
+      // Load d of a refill sits at position d*DMA_STRIDE counted in MFMA
+      // slots from the barrier that starts it, and every position is below
+      // the K tile length, so a tile is fully issued one barrier before the
+      // barrier that waits for it.
+      constexpr int kBarrierAt = kMfma - kReads;       // MFMAs before the barrier
+      constexpr int kAfter = kMfma - kBarrierAt;       // slots after the barrier
+      constexpr int kTileSlots = S::kKSub * kMfma;     // MFMA slots per K tile
+      constexpr int kPhaseStep = S::DMA_STRIDE / S::DMA_PHASES;
+      static_assert((S::kDmaPerStage - 1) * S::DMA_STRIDE + (S::DMA_PHASES - 1) * kPhaseStep < kTileSlots,
+                    "refill must finish within a K tile");
+      // Load index issued at slot position `pos` by a wave of slot phase `ph`, or -1.
+      auto dma_at = [&](int pos, int ph) -> int {
+        const int q = pos - ph * kPhaseStep;
+        return (q >= 0 && q % S::DMA_STRIDE == 0 && q / S::DMA_STRIDE < S::kDmaPerStage) ? q / S::DMA_STRIDE : -1;
+      };
+      // This wave's load slot phase (wave-uniform, so the branches below are
+      // scalar branches).
+      const int phase = __builtin_amdgcn_readfirstlane(wave % S::DMA_PHASES);
+      // Issue, at slot position `pos`, the load of K tile `tile` that this
+      // wave's phase places there, if any.
+      auto dma_slot = [&](int tile, int pos) {
 #pragma unroll
-      for (int s = 0; s < S::STAGES; ++s)
-        if (s < KT) issue_tile(s);
-      // Tile 0 is needed; tiles 1 .. min(KT, STAGES) - 1 are younger.
-      wait_tile_landed<S>(min(KT, S::STAGES) - 1);
-      workgroup_barrier();
-      load_frags(0, 0, 0);
-
-      for (int kt = 0; kt < KT; ++kt) {
+        for (int ph = 0; ph < S::DMA_PHASES; ++ph) {
+          const int d = dma_at(pos, ph);
+          if (d >= 0 && (S::DMA_PHASES == 1 || phase == ph)) issue_loads(tile, d, d + 1);
+        }
+      };
+      auto ktile = [&](int kt, auto rest_c, auto early_c, auto next_c) {
+        constexpr bool kRest = decltype(rest_c)::value;      // continue loading K tile kt + STAGES - 1
+        constexpr bool kEarlyOn = decltype(early_c)::value;  // start loading K tile kt + STAGES
+        constexpr bool kNext = decltype(next_c)::value;      // a K tile follows this one
 #pragma unroll
         for (int ks = 0; ks < S::kKSub; ++ks) {
           const int cur = ks & 1;
-          if (ks + 1 < S::kKSub) {
-            load_frags(cur ^ 1, kt, ks + 1);
-          } else if (kt + 1 < KT) {
-            // Last K step of this tile.  Its fragments are already in
-            // registers; once every wave's reads of this stage are complete
-            // and K tile kt+1 has landed, the stage is refilled with tile
-            // kt + STAGES and the first fragments of tile kt+1 are fetched
-            // while this step's MFMAs run.
-            // Issued so far: tiles 0 .. min(KT, kt + STAGES) - 1.
-            wait_tile_landed<S>(min(KT, kt + S::STAGES) - 1 - (kt + 1));
-            wait_lgkmcnt0();
-            workgroup_barrier();
-            if (kt + S::STAGES < KT) issue_tile(kt + S::STAGES);
-            load_frags(cur ^ 1, kt + 1, 0);
-          }
-          mfma_step(cur);
-        }
-      }
-    }
-
-    // ---- epilogue: fp32 -> fp16 (nearest even), masked stores ------------
-    // acc[i][j][4g + e] is D[m][n] with m = m0 + wm*kWaveM + 32i + (lane % 32)
-    // and n = n0 + wn*kWaveN + 32j + 8g + 4*(lane / 32) + e.
+          const bool last = ks == S::kKSub - 1;
 #pragma unroll
-    for (int i = 0; i < S::kFragM; ++i) {
-      const int m = m0 + wm * S::kWaveM + i * 32 + frag_row;
-      const bool row_ok = m < M;
-      _Float16 *drow = D + static_cast<int64_t>(row_ok ? m : 0) * N;
-#pragma unroll
-      for (int j = 0; j < S::kFragN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * S::kWaveN + j * 32 + g * 8 + frag_half * 4;
-          half4_t h;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = static_cast<_Float16>(acc[i][j][4 * g + e]);
-          if (row_ok) {
-            if (vec_store && n + 3 < N) {
-              *reinterpret_cast<half4_t *>(drow + n) = h;
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (n + e < N) drow[n + e] = h[e];
+          for (int idx = 0; idx < kMfma; ++idx) {
+            if (last && kNext && idx == kBarrierAt) {
+              // Tiles 0 .. min(KT, kt + STAGES) - 1 have been issued in full;
+              // tile kt+1 must have landed for every wave, and every wave must
+              // be done reading stage kt before anyone refills it.
+              wait_tile_landed<S>(min(KT, kt + S::STAGES) - (kt + 2));
+              __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+              workgroup_barrier();
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            mfma(cur, idx);
+            __builtin_amdgcn_sched_barrier(0);
+            if (!last) {
+              if (idx < kReads) {
+                read_frag(cur ^ 1, kt, ks + 1, idx);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            } else if (kNext && idx >= kBarrierAt) {
+              read_frag(cur ^ 1, kt + 1, 0, idx - kBarrierAt);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            if (last && idx >= kBarrierAt) {
+              if (kEarlyOn) {
+                dma_slot(kt + S::STAGES, idx - kBarrierAt);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+            } else if (kRest) {
+              dma_slot(kt + S::STAGES - 1, kAfter + ks * kMfma + idx);
+              __builtin_amdgcn_sched_barrier(0);
             }
           }
         }
-        // Keep the scheduler from pulling every accumulator out of the
-        // matrix-core registers at once.
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!kNext) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      };
+
+      // Prologue: K tiles 0 .. STAGES-2 in flight; once tile 0 has landed the
+      // loads of tile STAGES-1 that would follow a barrier go out, the rest
+      // during K tile 0.
+#pragma unroll
+      for (int s = 0; s < S::STAGES - 1; ++s)
+        if (s < KT) issue_loads(s, 0, S::kDmaPerStage);
+      wait_tile_landed<S>(min(KT, S::STAGES - 1) - 1);
+      workgroup_barrier();
+      load_frags(0, 0, 0);
+      if (S::STAGES - 1 < KT) {
+#pragma unroll
+        for (int pos = 0; pos < kAfter; ++pos) dma_slot(S::STAGES - 1, pos);
+      }
+
+      using yes = std::true_type;
+      using no = std::false_type;
+      int kt = 0;
+      for (; kt + S::STAGES < KT; ++kt) ktile(kt, yes{}, yes{}, yes{});  // steady state
+      if (kt + S::STAGES == KT && kt + 1 < KT) {                       // last refill
+        ktile(kt, yes{}, no{}, yes{});
+        ++kt;
+      }
+      for (; kt + 1 < KT; ++kt) ktile(kt, no{}, no{}, yes{});  // the ring drains
+      ktile(kt, no{}, no{}, no{});                             // last K tile
+    }
+
+    // ---- epilogue: fp32 -> fp16 (nearest even), staged through LDS -------
+    // acc[i][j][4g + e] is D[m][n] with m = m0 + wm*kWaveM + 32i + (lane % 32)
+    // and n = n0 + wn*kWaveN + 32j + 8g + 4*(lane / 32) + e: each lane holds
+    // 8-byte pieces of 32 different rows, which written straight to D would
+    // cost one partial cache-line write per row.  The wave instead writes its
+    // tile to LDS and reads it back row by row, so each store instruction
+    // writes whole 16-byte-per-lane row segments (full cache lines).
+    workgroup_barrier();  // every wave is done reading the ring
+    {
+      const uint32_t stage_base = static_cast<uint32_t>(wave * S::kWaveM * S::kStagePitch);
+#pragma unroll
+      for (int i = 0; i < S::kFragM; ++i) {
+#pragma unroll
+        for (int j = 0; j < S::kFragN; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            half4_t h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = static_cast<_Float16>(acc[i][j][4 * g + e]);
+            const uint32_t off = stage_base + static_cast<uint32_t>((i * 32 + frag_row) * S::kStagePitch +
+                                                                    (j * 32 + g * 8 + frag_half * 4) * 2);
+            *reinterpret_cast<half4_t *>(smem + off) = h;
+          }
+        }
+      }
+      constexpr int kRowChunks = S::kWaveN / 8;       // 16-byte chunks per tile row
+      constexpr int kRowsPerPass = 64 / kRowChunks;   // rows one wave instruction covers
+      static_assert(64 % kRowChunks == 0, "lanes per staged row");
+      const int chunk = lane % kRowChunks;
+      const int n = n0 + wn * S::kWaveN + chunk * 8;
+#pragma unroll 4
+      for (int r0 = 0; r0 < S::kWaveM; r0 += kRowsPerPass) {
+        const int r = r0 + lane / kRowChunks;
+        const half8_t v = *reinterpret_cast<const half8_t *>(smem + stage_base + r * S::kStagePitch + chunk * 16);
+        const int m = m0 + wm * S::kWaveM + r;
+        if (m < M) {
+          _Float16 *dst = D + static_cast<int64_t>(m) * N + n;
+          if (vec16 && n + 8 <= N) {
+            *reinterpret_cast<half8_t *>(dst) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < N) dst[e] = v[e];
+          }
+        }
       }
     }
   }
 }
 
 // ---- instantiations ------------------------------------------------------
-// Default: 256x256 output tile, BK = 64, two 64 KiB LDS stages, 2x2 waves of
-// 128x128, swizzled LDS, persistent grouped scheduler.
-using GemmDefault = GemmShape<256, 256, 64, 2, 2, 2, true, true>;
-using GemmNoSwizzle = GemmShape<256, 256, 64, 2, 2, 2, false, true>;
-using GemmOneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true>;
-using GemmNonPersistent = GemmShape<256, 256, 64, 2, 2, 2, true, false>;
+// Default: 256x256 output tile, K tiles of 64 (128-byte LDS rows, so every
+// tile load is a whole 128-byte line), a two-stage 64 KiB-per-stage LDS ring,
+// one refill load every 2 MFMAs, 2x2 waves of 128x128, swizzled LDS,
+// persistent grouped scheduler.  The others exist for ablation measurements.
+using GemmDefault = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1>;
+using GemmNoSwizzle = GemmShape<256, 256, 64, 2, 2, 2, false, true, 2, 1>;
+using GemmOneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true, 1, 1>;
+using GemmNonPersistent = GemmShape<256, 256, 64, 2, 2, 2, true, false, 2, 1>;
+using GemmBk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
+using GemmBk32ThreeStage = GemmShape<256, 256, 32, 3, 2, 2, true, true, 4, 1>;
+using GemmBk32FiveStage = GemmShape<256, 256, 32, 5, 2, 2, true, true, 4, 1>;
+using GemmRefillEveryMfma = GemmShape<256, 256, 64, 2, 2, 2, true, true, 1, 1>;
+using GemmRefillEvery3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 1>;
+using GemmKStagger = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1, 8, 1>;
+using GemmLoadsSc0 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1, 1, 1, 1>;
 
 static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDefault::BK == kGemmBK &&
                   GemmDefault::STAGES == kGemmStages && GemmDefault::kThreads == kGemmThreads,
@@ -332,10 +499,11 @@ static hipError_t launch(const void *A, const void *B, void *D, int M, int N, in
   const int tiles_n = (N + S::BN - 1) / S::BN;
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   const int64_t grid = S::PERSISTENT ? (tiles < num_cus ? tiles : num_cus) : tiles;
-  const int vec_store = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(D) % 8 == 0);
+  // Whole 16-byte row segments of D are 16-byte aligned when N % 8 == 0.
+  const int vec16 = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(D) % 16 == 0);
   hipLaunchKernelGGL(gemm_f16_kernel<S>, dim3(static_cast<unsigned>(grid)), dim3(S::kThreads), 0, stream,
                      static_cast<const _Float16 *>(A), static_cast<const _Float16 *>(B), static_cast<_Float16 *>(D),
-                     M, N, K, tiles_m, tiles_n, vec_store);
+                     M, N, K, tiles_m, tiles_n, vec16);
   return hipGetLastError();
 }
 
@@ -346,6 +514,13 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 1: return launch<GemmNoSwizzle>(A, B, D, M, N, K, num_cus, stream);
     case 2: return launch<GemmOneStage>(A, B, D, M, N, K, num_cus, stream);
     case 3: return launch<GemmNonPersistent>(A, B, D, M, N, K, num_cus, stream);
+    case 4: return launch<GemmBk32FourStage>(A, B, D, M, N, K, num_cus, stream);
+    case 5: return launch<GemmBk32ThreeStage>(A, B, D, M, N, K, num_cus, stream);
+    case 6: return launch<GemmBk32FiveStage>(A, B, D, M, N, K, num_cus, stream);
+    case 7: return launch<GemmRefillEveryMfma>(A, B, D, M, N, K, num_cus, stream);
+    case 8: return launch<GemmRefillEvery3>(A, B, D, M, N, K, num_cus, stream);
+    case 9: return launch<GemmKStagger>(A, B, D, M, N, K, num_cus, stream);
+    case 10: return launch<GemmLoadsSc0>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -109,15 +109,16 @@ static hipError_t launch(const void *x, const void *W, void *y, int N, int K, hi
 }
 
 hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, hipStream_t stream) {
+  // <rows per wave, waves per workgroup, chunk steps in flight, non-temporal W>
   switch (variant) {
-    case 0: return launch<4, 4, 4, true>(x, W, y, N, K, stream);
-    case 1: return launch<4, 4, 4, false>(x, W, y, N, K, stream);
-    case 2: return launch<2, 4, 4, true>(x, W, y, N, K, stream);
-    case 3: return launch<1, 4, 8, true>(x, W, y, N, K, stream);
-    case 4: return launch<4, 2, 4, true>(x, W, y, N, K, stream);
-    case 5: return launch<2, 8, 4, true>(x, W, y, N, K, stream);
-    case 6: return launch<4, 4, 2, true>(x, W, y, N, K, stream);
-    case 7: return launch<8, 4, 2, true>(x, W, y, N, K, stream);
+    case 0: return launch<2, 8, 4, true>(x, W, y, N, K, stream);
+    case 1: return launch<4, 4, 4, true>(x, W, y, N, K, stream);
+    case 2: return launch<2, 8, 8, true>(x, W, y, N, K, stream);
+    case 3: return launch<1, 8, 8, true>(x, W, y, N, K, stream);
+    case 4: return launch<2, 4, 8, true>(x, W, y, N, K, stream);
+    case 5: return launch<1, 16, 4, true>(x, W, y, N, K, stream);
+    case 6: return launch<2, 8, 4, false>(x, W, y, N, K, stream);
+    case 7: return launch<4, 4, 2, true>(x, W, y, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -16,8 +16,13 @@ constexpr int kGemmBK = 64;
 constexpr int kGemmStages = 2;
 constexpr int kGemmThreads = 256;
 constexpr int kGemmGroupM = 8;
-constexpr int kGemmVariants = 4;
+constexpr int kGemmVariants = 11;
 constexpr int kGemvVariants = 8;
+
+// s_waitcnt immediate for "lgkmcnt(0)" alone on gfx9-family targets
+// (vmcnt field [3:0]|[15:14] = 63, expcnt [6:4] = 7, lgkmcnt [11:8] = 0).
+// Issued through the builtin so the compiler knows the LDS reads are done.
+constexpr unsigned kWaitLgkm0 = 0xC07F;
 
 hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                            hipStream_t stream);

@@ -1,0 +1,65 @@
+"""Run one kernel of the library a few times, for hardware-counter profiling.
+
+    python -m gemv_tile_pipelined_amd.profile_driver gemm [--variant V] [--shape M N K] [--iters I]
+    python -m gemv_tile_pipelined_amd.profile_driver gemv [--variant V] [--shape N K] [--iters I]
+    python -m gemv_tile_pipelined_amd.profile_driver copy [--mib S] [--iters I]
+
+Meant to run under `rocprofv3 --pmc ...`: every dispatch of the chosen kernel
+then carries its counters.  `copy` runs a plain device-to-device copy of a
+known size, which calibrates byte counters (FETCH_SIZE, WRITE_SIZE) against
+bytes that are known exactly.  Inputs are seeded synthetic fp16 values; the
+GEMV cycles through 5 copies of W so every dispatch reads W from HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    p.add_argument("kernel", choices=["gemm", "gemv", "copy"])
+    p.add_argument("--variant", type=int, default=0)
+    p.add_argument("--shape", type=int, nargs="+", default=None)
+    p.add_argument("--iters", type=int, default=10)
+    p.add_argument("--mib", type=int, default=512)
+    a = p.parse_args(argv)
+
+    import torch
+
+    import gemv_tile_pipelined_amd as gt
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    if a.kernel == "gemm":
+        M, N, K = a.shape or (4096, 4096, 4096)
+        A = torch.empty((M, K), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)
+        B = torch.empty((N, K), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)
+        D = torch.empty((M, N), dtype=torch.float16, device=dev)
+        for _ in range(a.iters):
+            gt.gemm_f16(A, B, D, variant=a.variant)
+    elif a.kernel == "gemv":
+        N, K = a.shape or (4096, 14336)
+        x = torch.empty((K,), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)
+        Ws = [torch.empty((N, K), dtype=torch.float16, device=dev).uniform_(-0.05, 0.05, generator=g) for _ in range(5)]
+        y = torch.empty((N,), dtype=torch.float16, device=dev)
+        for i in range(a.iters):
+            gt.gemv_f16(x, Ws[i % 5], y, variant=a.variant)
+    else:
+        n = a.mib * 1024 * 1024 // 2
+        src = torch.empty((n,), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)
+        dst = torch.empty_like(src)
+        for _ in range(a.iters):
+            dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(f"profile_driver {a.kernel} done ({a.iters} dispatches)", flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -120,11 +120,17 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
 
 /*
  * gemvtile_gemm_f16_variant -- gemm_f16 with an internal kernel variant, for
- * ablation measurements only (same contract and results as gemm_f16):
- *   0  the default kernel (identical to gemm_f16)
- *   1  no LDS swizzle (plain row-major LDS tiles)
+ * ablation measurements only (same contract and results as gemm_f16).  All
+ * use 256x256 output tiles and 4 waves of 128x128:
+ *   0  the default kernel (identical to gemm_f16): K tiles of 64, a 2-stage
+ *      LDS ring refilled one load every 2 MFMAs, swizzled LDS, persistent
+ *   1  as 0 without the LDS swizzle
  *   2  single-stage LDS (load, wait, compute: no overlap)
- *   3  one workgroup per tile (no persistent loop), no XCD remap
+ *   3  as 0 with one workgroup per tile (no persistent loop, no XCD remap)
+ *   4  K tiles of 32 in a 4-stage ring   5  ... 3-stage   6  ... 5-stage
+ *   7  as 0 with a refill load after every MFMA   8  ... every 3 MFMAs
+ *   9  as 0 with output tile t starting its K loop at K tile t % 8
+ *   10 as 0 with the tile loads' cache-policy modifier sc0
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
@@ -133,13 +139,13 @@ int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, 
 /*
  * gemvtile_gemv_f16_variant -- gemv_f16 with an internal launch shape, for
  * measurements only (same contract and results as gemv_f16).  A variant fixes
- * the rows per wave, waves per workgroup, chunk steps in flight per lane and
- * whether W is read with non-temporal loads:
- *   0 = 4 rows, 4 waves, 4 steps, non-temporal (the gemv_f16 default)
- *   1 = as 0 with ordinary loads      2 = 2 rows, 4 waves, 4 steps, nt
- *   3 = 1 row, 4 waves, 8 steps, nt   4 = 4 rows, 2 waves, 4 steps, nt
- *   5 = 2 rows, 8 waves, 4 steps, nt  6 = 4 rows, 4 waves, 2 steps, nt
- *   7 = 8 rows, 4 waves, 2 steps, nt
+ * the rows per wave, waves per workgroup, 16-byte chunk steps in flight per
+ * lane and whether W is read with non-temporal loads:
+ *   0 = 2 rows, 8 waves, 4 steps, nt (the gemv_f16 default)
+ *   1 = 4 rows, 4 waves, 4 steps, nt   2 = 2 rows, 8 waves, 8 steps, nt
+ *   3 = 1 row, 8 waves, 8 steps, nt    4 = 2 rows, 4 waves, 8 steps, nt
+ *   5 = 1 row, 16 waves, 4 steps, nt   6 = as 0 with ordinary loads
+ *   7 = 4 rows, 4 waves, 2 steps, nt
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream,
