@@ -18,12 +18,16 @@
 //  * the x chunk a lane needs is the same for all ROWS rows, so it is loaded
 //    once and reused from registers;
 //  * UNROLL chunk steps are issued back to back, keeping UNROLL*(ROWS+1)
-//    16-byte loads in flight per lane;
+//    16-byte loads in flight per lane; whole groups of steps run without a
+//    bounds test, and only the ragged end of a row takes a guarded group;
+//  * the waves of a launch start their walk along K at different groups
+//    and wrap around, so at any moment they read different column windows;
 //  * W is read with non-temporal loads (streamed once, no reuse);
 //  * v_dot2_f32_f16 multiplies fp16 pairs and accumulates in FP32;
-//  * the 64 lane partial sums of a row are combined with cross-lane
-//    exchanges inside the wave (no LDS, no atomics, no second kernel), so
-//    each row sum is deterministic.
+//  * the 64 lane partial sums of a row are combined with DPP lane moves
+//    inside the wave (no LDS, no atomics, no second kernel), so each row sum
+//    is deterministic; a wave's rows are reduced together so that the short
+//    dependent chains overlap.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -39,13 +43,44 @@ __device__ inline float dot8_acc(half8_t a, half8_t b, float acc) {
   return acc;
 }
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// One DPP step: v + (v as seen through the lane pattern `ctrl`), restricted
+// to the rows of 16 lanes selected by ROW_MASK (other rows add zero).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ inline float dpp_add(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false);
+  return v + __builtin_bit_cast(float, moved);
 }
 
-template <int ROWS, int WAVES, int UNROLL, bool NONTEMPORAL>
+// Sum of the 64 lane values of a wave, returned to every lane.  The data
+// moves through DPP lane patterns of the VALU (a few cycles each) instead of
+// LDS permutes (a round trip each): swap neighbours, swap pairs, mirror
+// within 8 and within 16 lanes leave the 16-lane sum in every lane of each
+// row; row_bcast:15 then adds row 0 into row 1 and row 2 into row 3, and
+// row_bcast:31 adds lane 31 into rows 2 and 3, so lane 63 holds the total,
+// which v_readlane broadcasts.  Several independent sums interleave well.
+__device__ inline float wave_sum(float v) {
+  v = dpp_add<0xB1>(v);        // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);        // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);       // row_half_mirror
+  v = dpp_add<0x140>(v);       // row_mirror
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Reduce the ROWS partial sums of a wave and store row r's total from lane r.
+template <int ROWS>
+__device__ inline void store_row_sums(const float (&acc)[ROWS], int lane, int64_t row0, int N, _Float16 *y) {
+  float sums[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) sums[r] = wave_sum(acc[r]);
+  float mine = sums[0];
+#pragma unroll
+  for (int r = 1; r < ROWS; ++r) mine = (lane == r) ? sums[r] : mine;
+  if (lane < ROWS && row0 + lane < N) y[row0 + lane] = static_cast<_Float16>(mine);
+}
+
+template <int ROWS, int WAVES, int UNROLL, bool NONTEMPORAL, bool ROTATE = false>
 __global__ void __launch_bounds__(WAVES * 64)
 gemv_f16_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Float16 *__restrict__ y, int N,
                 int K) {
@@ -68,13 +103,17 @@ gemv_f16_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, 
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) acc[r] = 0.0f;
 
-  for (int base = 0; base < chunks; base += 64 * UNROLL) {
+  // One group = UNROLL chunk steps of 64 lanes: every load of a group is
+  // issued before the first product, so a lane has UNROLL*(ROWS+1) 16-byte
+  // loads in flight.  Whole groups need no bounds test; the ragged rest of
+  // the row (fewer than 64*UNROLL chunks) is one guarded group at the end.
+  auto group = [&](int base, bool guarded) {
     half8_t xs[UNROLL];
     half8_t ws[UNROLL][ROWS];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int c = base + u * 64 + lane;
-      if (c < chunks) {
+      if (!guarded || c < chunks) {
         xs[u] = xv[c];
 #pragma unroll
         for (int r = 0; r < ROWS; ++r)
@@ -89,21 +128,28 @@ gemv_f16_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, 
     for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) acc[r] = dot8_acc(xs[u], ws[u][r], acc[r]);
-  }
+  };
 
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r) {
-    const float s = wave_sum(acc[r]);
-    if (lane == r && row0 + r < N) y[row0 + r] = static_cast<_Float16>(s);
+  // With ROTATE, each wave starts its walk over the whole groups at a
+  // different group (and wraps around), so the waves running at one moment
+  // read different column windows of their rows.
+  constexpr int kGroup = 64 * UNROLL;
+  const int full = chunks / kGroup;
+  int g = (ROTATE && full > 0) ? static_cast<int>((row0 / ROWS) % full) : 0;
+  for (int it = 0; it < full; ++it) {
+    group(g * kGroup, false);
+    if (++g == full) g = 0;
   }
+  if (full * kGroup < chunks) group(full * kGroup, true);
+  store_row_sums<ROWS>(acc, lane, row0, N, y);
 }
 
-template <int ROWS, int WAVES, int UNROLL, bool NT>
+template <int ROWS, int WAVES, int UNROLL, bool NT, bool ROT = false>
 static hipError_t launch(const void *x, const void *W, void *y, int N, int K, hipStream_t stream) {
   const int64_t rows_per_block = static_cast<int64_t>(ROWS) * WAVES;
   const int64_t grid = (N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((gemv_f16_kernel<ROWS, WAVES, UNROLL, NT>), dim3(static_cast<unsigned>(grid)), dim3(WAVES * 64),
-                     0, stream, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(W),
+  hipLaunchKernelGGL((gemv_f16_kernel<ROWS, WAVES, UNROLL, NT, ROT>), dim3(static_cast<unsigned>(grid)),
+                     dim3(WAVES * 64), 0, stream, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(W),
                      static_cast<_Float16 *>(y), N, K);
   return hipGetLastError();
 }
@@ -111,14 +157,14 @@ static hipError_t launch(const void *x, const void *W, void *y, int N, int K, hi
 hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, hipStream_t stream) {
   // <rows per wave, waves per workgroup, chunk steps in flight, non-temporal W>
   switch (variant) {
-    case 0: return launch<2, 8, 4, true>(x, W, y, N, K, stream);
+    case 0: return launch<2, 8, 4, true, true>(x, W, y, N, K, stream);
     case 1: return launch<4, 4, 4, true>(x, W, y, N, K, stream);
     case 2: return launch<2, 8, 8, true>(x, W, y, N, K, stream);
     case 3: return launch<1, 8, 8, true>(x, W, y, N, K, stream);
     case 4: return launch<2, 4, 8, true>(x, W, y, N, K, stream);
     case 5: return launch<1, 16, 4, true>(x, W, y, N, K, stream);
     case 6: return launch<2, 8, 4, false>(x, W, y, N, K, stream);
-    case 7: return launch<4, 4, 2, true>(x, W, y, N, K, stream);
+    case 7: return launch<2, 8, 4, true, false>(x, W, y, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }

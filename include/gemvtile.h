@@ -141,11 +141,13 @@ int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, 
  * measurements only (same contract and results as gemv_f16).  A variant fixes
  * the rows per wave, waves per workgroup, 16-byte chunk steps in flight per
  * lane and whether W is read with non-temporal loads:
- *   0 = 2 rows, 8 waves, 4 steps, nt (the gemv_f16 default)
+ *   0 = 2 rows, 8 waves, 4 steps, nt, each wave starting its walk along K at
+ *       a different step group (the gemv_f16 default)
  *   1 = 4 rows, 4 waves, 4 steps, nt   2 = 2 rows, 8 waves, 8 steps, nt
  *   3 = 1 row, 8 waves, 8 steps, nt    4 = 2 rows, 4 waves, 8 steps, nt
  *   5 = 1 row, 16 waves, 4 steps, nt   6 = as 0 with ordinary loads
- *   7 = 4 rows, 4 waves, 2 steps, nt
+ *   7 = as 0 with every wave starting at the row's first column
+ * Variants 1..5 start every wave at the first column.
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream,
