@@ -65,7 +65,8 @@
 namespace gt {
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, bool SWIZZLE_, bool PERSISTENT_,
-          int DMA_STRIDE_, int DMA_PHASES_, int K_STAGGER_ = 1, int K_STAGGER_STEP_ = 1, int LOAD_POLICY_ = 0>
+          int DMA_STRIDE_, int DMA_PHASES_, int K_STAGGER_ = 1, int K_STAGGER_STEP_ = 1, int LOAD_POLICY_ = 0,
+          int MI_ = 32, int READ_STRIDE_ = 1, int DMA_OFFSET_ = 0>
 struct GemmShape {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -89,13 +90,26 @@ struct GemmShape {
   static constexpr int K_STAGGER_STEP = K_STAGGER_STEP_;
   // Cache-policy modifier of the tile loads (see lds_dma_b128).
   static constexpr int LOAD_POLICY = LOAD_POLICY_;
+  // MFMA block edge: 32 (v_mfma_f32_32x32x16_f16) or 16 (v_mfma_f32_16x16x32_f16).
+  static constexpr int MI = MI_;
+  static_assert(MI == 32 || MI == 16, "MFMA shape");
+  static_assert(MI == 32 || STAGES_ >= 2, "16x16x32 blocks need the pipelined (multi-stage) loop");
+  static constexpr int kKStep = MI == 32 ? 16 : 32;  // K consumed by one MFMA
+  static constexpr int kAccRegs = MI * MI / 64;      // FP32 accumulator registers per lane per block
+  // MFMA slots between two operand reads for the next K step (1: one read
+  // per slot from the start of the step), and the slot offset of the refill
+  // loads, which lets them fall between the reads.
+  static constexpr int READ_STRIDE = READ_STRIDE_;
+  static constexpr int DMA_OFFSET = DMA_OFFSET_;
+  static_assert((BK / kKStep) >= 1 && (BM / WAVES_M / MI) * (BN / WAVES_N / MI) % READ_STRIDE == 0,
+                "the read spacing must divide the MFMA slots of a K step");
 
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kWaveM = BM / WAVES_M;  // rows of D per wave
   static constexpr int kWaveN = BN / WAVES_N;  // cols of D per wave
-  static constexpr int kFragM = kWaveM / 32;   // 32x32 MFMA blocks per wave, M
-  static constexpr int kFragN = kWaveN / 32;   // 32x32 MFMA blocks per wave, N
+  static constexpr int kFragM = kWaveM / MI;   // MFMA blocks per wave, M
+  static constexpr int kFragN = kWaveN / MI;   // MFMA blocks per wave, N
   static constexpr int kRowBytes = BK * 2;
   static constexpr int kChunks = BK / 8;            // 16-byte chunks per LDS row
   static constexpr int kRowsPerDma = 64 / kChunks;  // rows one wave DMA fills
@@ -111,10 +125,10 @@ struct GemmShape {
   static constexpr int kStagingBytes = kWaves * kWaveM * kStagePitch;
   static constexpr int kRingBytes = STAGES * kStageBytes;
   static constexpr int kLdsBytes = kRingBytes > kStagingBytes ? kRingBytes : kStagingBytes;
-  static constexpr int kKSub = BK / 16;  // MFMA K steps per K tile
+  static constexpr int kKSub = BK / kKStep;  // MFMA K steps per K tile
 
   static_assert(BK == 32 || BK == 64, "LDS rows of 64 or 128 bytes");
-  static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
+  static_assert(kWaveM % MI == 0 && kWaveN % MI == 0, "wave tile must be whole MFMA blocks");
   static_assert(BM % (kRowsPerDma * kWaves) == 0 && BN % (kRowsPerDma * kWaves) == 0, "DMA split");
   static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
   static_assert(STAGES >= 1 && (STAGES - 1) * kDmaPerStage <= 63, "vmcnt range");
@@ -196,13 +210,15 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
   constexpr uint32_t kLdsStep = S::kRowsPerDma * S::kWaves * S::kRowBytes;
 
   // ---- operand-read geometry ---------------------------------------------
-  // MFMA 32x32x16: lane l supplies row (l % 32) of a 32-row block and 8
-  // consecutive K values starting at 8*(l / 32) of a 16-wide K step.  Both
-  // operands use the same lane -> K mapping, so the products pair up.
-  const int frag_row = lane & 31;
-  const int frag_half = lane >> 5;
-  // Fragment row blocks start at multiples of 32, so swz() of every
-  // fragment row equals swz(lane % 32).
+  // An MFMA with MI x MI blocks takes, from lane l, row (l % MI) of an MI-row
+  // block and the 8 consecutive K values starting at 8*(l / MI) of its K step
+  // (16 wide for MI = 32, 32 wide for MI = 16), i.e. one 16-byte LDS chunk.
+  // Both operands use the same lane -> K mapping, so the products pair up.
+  const int frag_row = lane % S::MI;
+  const int frag_kgrp = lane / S::MI;
+  // Fragment row blocks start at multiples of MI (16 or 32), and swz()
+  // depends only on row & 15, so swz() of every fragment row equals
+  // swz(lane % MI).
   const int frag_swz = S::swz(frag_row);
   const uint32_t a_row_base = static_cast<uint32_t>(wm * S::kWaveM + frag_row) * S::kRowBytes;
   const uint32_t b_row_base = static_cast<uint32_t>(wn * S::kWaveN + frag_row) * S::kRowBytes + S::kStageA;
@@ -258,18 +274,18 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
     // order the row-major MFMA sequence below first needs them in.
     constexpr int kReads = S::kFragM + S::kFragN;
     constexpr int kMfma = S::kFragM * S::kFragN;
-    static_assert(kMfma >= 2 * kReads - 8 && kMfma >= kReads, "MFMA slots for the operand reads");
+    static_assert(kMfma >= kReads * S::READ_STRIDE, "MFMA slots for the operand reads");
     auto read_frag = [&](int buf, int kt, int ks, int r) {
       const char *stage_ptr = smem + (kt % S::STAGES) * S::kStageBytes;
-      const uint32_t chunk = static_cast<uint32_t>(((ks * 2 + frag_half) ^ frag_swz) * 16);
+      const uint32_t chunk = static_cast<uint32_t>(((ks * (S::kKStep / 8) + frag_kgrp) ^ frag_swz) * 16);
       if (r == 0) {
         fa[buf][0] = *reinterpret_cast<const half8_t *>(stage_ptr + a_row_base + chunk);
       } else if (r <= S::kFragN) {
         const int j = r - 1;
-        fb[buf][j] = *reinterpret_cast<const half8_t *>(stage_ptr + b_row_base + j * 32 * S::kRowBytes + chunk);
+        fb[buf][j] = *reinterpret_cast<const half8_t *>(stage_ptr + b_row_base + j * S::MI * S::kRowBytes + chunk);
       } else {
         const int i = r - S::kFragN;
-        fa[buf][i] = *reinterpret_cast<const half8_t *>(stage_ptr + a_row_base + i * 32 * S::kRowBytes + chunk);
+        fa[buf][i] = *reinterpret_cast<const half8_t *>(stage_ptr + a_row_base + i * S::MI * S::kRowBytes + chunk);
       }
     };
     auto load_frags = [&](int buf, int kt, int ks) {
@@ -277,18 +293,53 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
       for (int r = 0; r < kReads; ++r) read_frag(buf, kt, ks, r);
     };
 
-    float16_t acc[S::kFragM][S::kFragN];
+    using AccT = std::conditional_t<S::MI == 32, float16_t, float4_t>;
+    AccT acc[S::kFragM][S::kFragN];
 #pragma unroll
     for (int i = 0; i < S::kFragM; ++i)
 #pragma unroll
       for (int j = 0; j < S::kFragN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        for (int e = 0; e < S::kAccRegs; ++e) acc[i][j][e] = 0.0f;
+    if constexpr (S::MI == 16) {
+      // The zeros above are written by VALU instructions and first read by a
+      // hand-written MFMA, which the compiler's hazard padding does not know
+      // about.  These statements take every accumulator as input and output
+      // and carry wait states: the zeros are materialised before them (and
+      // cannot be re-created after them), so they precede every MFMA by at
+      // least 16 wait states.
+      static_assert(S::kFragN == 8, "accumulator fence covers 8 blocks per row");
+#pragma unroll
+      for (int i = 0; i < S::kFragM; ++i)
+        asm volatile("s_nop 1"
+                     : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                       "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+    }
 
     auto mfma = [&](int buf, int idx) {
       const int i = idx / S::kFragN;
       const int j = idx % S::kFragN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+      if constexpr (S::MI == 32) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+      } else {
+        // Written as inline asm with the accumulator pinned to AGPRs: through
+        // the builtin, the register allocator renames the 64 four-register
+        // accumulators around the K loop and copies them back on every
+        // iteration.  The compiler does not see this as an MFMA, so the read
+        // of the accumulators after the K loop is padded by hand (mfma_drain).
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                     : "+a"(acc[i][j])
+                     : "v"(fb[buf][j]), "v"(fa[buf][i]));
+      }
+    };
+    // Wait states between the last hand-written MFMA and any read of its
+    // result: more than the 16x16x32 MFMA's pass count requires.  The
+    // sched_barrier keeps the accumulator reads after the padding.
+    auto mfma_drain = [&]() {
+      if constexpr (S::MI == 16) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
 
     // Every wave must be done with the previous output tile's LDS (ring and
@@ -316,27 +367,29 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
       }
     } else {
       // One K tile in a fixed instruction order (sched_barrier pins it).
-      // Each MFMA slot of a non-final K step carries one operand read for the
-      // next step; the final K step meets the other waves after its first
-      // kBarrierAt MFMAs and fetches the next K tile's first operands during
-      // the rest.  The barrier frees stage kt, and its refill with K tile
+      // Every READ_STRIDE-th MFMA slot of a non-final K step carries one
+      // operand read for the next step (spread out so that the four waves'
+      // reads do not outrun the LDS); the final K step meets the other waves
+      // after its first kBarrierAt MFMAs and fetches the next K tile's first
+      // operands, at the same spacing, during the rest.  The barrier frees stage kt, and its refill with K tile
       // kt + STAGES starts right there.  The refill's loads go out one every
       // DMA_STRIDE MFMA slots: bunched together, the four waves' loads
       // saturate the texture path and stall MFMA issue, while spread too
       // thin the last load lands too close to the barrier that needs it.
-      // Load d of a refill sits at position d*DMA_STRIDE counted in MFMA
-      // slots from the barrier that starts it, and every position is below
+      // Load d of a refill sits at position DMA_OFFSET + d*DMA_STRIDE
+      // counted in MFMA slots from the barrier that starts it, and every position is below
       // the K tile length, so a tile is fully issued one barrier before the
       // barrier that waits for it.
-      constexpr int kBarrierAt = kMfma - kReads;       // MFMAs before the barrier
+      constexpr int kBarrierAt = kMfma - kReads * S::READ_STRIDE;  // MFMAs before the barrier
       constexpr int kAfter = kMfma - kBarrierAt;       // slots after the barrier
       constexpr int kTileSlots = S::kKSub * kMfma;     // MFMA slots per K tile
       constexpr int kPhaseStep = S::DMA_STRIDE / S::DMA_PHASES;
-      static_assert((S::kDmaPerStage - 1) * S::DMA_STRIDE + (S::DMA_PHASES - 1) * kPhaseStep < kTileSlots,
+      static_assert((S::kDmaPerStage - 1) * S::DMA_STRIDE + (S::DMA_PHASES - 1) * kPhaseStep + S::DMA_OFFSET <
+                        kTileSlots,
                     "refill must finish within a K tile");
       // Load index issued at slot position `pos` by a wave of slot phase `ph`, or -1.
       auto dma_at = [&](int pos, int ph) -> int {
-        const int q = pos - ph * kPhaseStep;
+        const int q = pos - S::DMA_OFFSET - ph * kPhaseStep;
         return (q >= 0 && q % S::DMA_STRIDE == 0 && q / S::DMA_STRIDE < S::kDmaPerStage) ? q / S::DMA_STRIDE : -1;
       };
       // This wave's load slot phase (wave-uniform, so the branches below are
@@ -373,12 +426,12 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
             mfma(cur, idx);
             __builtin_amdgcn_sched_barrier(0);
             if (!last) {
-              if (idx < kReads) {
-                read_frag(cur ^ 1, kt, ks + 1, idx);
+              if (idx % S::READ_STRIDE == 0 && idx / S::READ_STRIDE < kReads) {
+                read_frag(cur ^ 1, kt, ks + 1, idx / S::READ_STRIDE);
                 __builtin_amdgcn_sched_barrier(0);
               }
-            } else if (kNext && idx >= kBarrierAt) {
-              read_frag(cur ^ 1, kt + 1, 0, idx - kBarrierAt);
+            } else if (kNext && idx >= kBarrierAt && (idx - kBarrierAt) % S::READ_STRIDE == 0) {
+              read_frag(cur ^ 1, kt + 1, 0, (idx - kBarrierAt) / S::READ_STRIDE);
               __builtin_amdgcn_sched_barrier(0);
             }
             if (last && idx >= kBarrierAt) {
@@ -422,12 +475,16 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
     }
 
     // ---- epilogue: fp32 -> fp16 (nearest even), staged through LDS -------
-    // acc[i][j][4g + e] is D[m][n] with m = m0 + wm*kWaveM + 32i + (lane % 32)
-    // and n = n0 + wn*kWaveN + 32j + 8g + 4*(lane / 32) + e: each lane holds
-    // 8-byte pieces of 32 different rows, which written straight to D would
-    // cost one partial cache-line write per row.  The wave instead writes its
+    // With MI = 32, acc[i][j][4g + e] is D[m][n] with
+    // m = m0 + wm*kWaveM + 32i + (lane % 32) and
+    // n = n0 + wn*kWaveN + 32j + 8g + 4*(lane / 32) + e; with MI = 16,
+    // acc[i][j][e] is D[m][n] with m = m0 + wm*kWaveM + 16i + (lane % 16) and
+    // n = n0 + wn*kWaveN + 16j + 4*(lane / 16) + e.  Either way each lane
+    // holds 8-byte pieces of many different rows, which written straight to D
+    // would cost one partial cache-line write per row.  The wave instead writes its
     // tile to LDS and reads it back row by row, so each store instruction
     // writes whole 16-byte-per-lane row segments (full cache lines).
+    mfma_drain();
     workgroup_barrier();  // every wave is done reading the ring
     {
       const uint32_t stage_base = static_cast<uint32_t>(wave * S::kWaveM * S::kStagePitch);
@@ -436,12 +493,14 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
 #pragma unroll
         for (int j = 0; j < S::kFragN; ++j) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
+          for (int g = 0; g < S::kAccRegs / 4; ++g) {
             half4_t h;
 #pragma unroll
             for (int e = 0; e < 4; ++e) h[e] = static_cast<_Float16>(acc[i][j][4 * g + e]);
-            const uint32_t off = stage_base + static_cast<uint32_t>((i * 32 + frag_row) * S::kStagePitch +
-                                                                    (j * 32 + g * 8 + frag_half * 4) * 2);
+            // Column of this lane's 4 values inside the wave tile.
+            const int col = S::MI == 32 ? j * 32 + g * 8 + frag_kgrp * 4 : j * 16 + frag_kgrp * 4;
+            const uint32_t off =
+                stage_base + static_cast<uint32_t>((i * S::MI + frag_row) * S::kStagePitch + col * 2);
             *reinterpret_cast<half4_t *>(smem + off) = h;
           }
         }
@@ -474,19 +533,28 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
 // ---- instantiations ------------------------------------------------------
 // Default: 256x256 output tile, K tiles of 64 (128-byte LDS rows, so every
 // tile load is a whole 128-byte line), a two-stage 64 KiB-per-stage LDS ring,
-// one refill load every 2 MFMAs, 2x2 waves of 128x128, swizzled LDS,
-// persistent grouped scheduler.  The others exist for ablation measurements.
-using GemmDefault = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1>;
-using GemmNoSwizzle = GemmShape<256, 256, 64, 2, 2, 2, false, true, 2, 1>;
-using GemmOneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true, 1, 1>;
-using GemmNonPersistent = GemmShape<256, 256, 64, 2, 2, 2, true, false, 2, 1>;
-using GemmBk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
-using GemmBk32ThreeStage = GemmShape<256, 256, 32, 3, 2, 2, true, true, 4, 1>;
-using GemmBk32FiveStage = GemmShape<256, 256, 32, 5, 2, 2, true, true, 4, 1>;
-using GemmRefillEveryMfma = GemmShape<256, 256, 64, 2, 2, 2, true, true, 1, 1>;
-using GemmRefillEvery3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 1>;
-using GemmKStagger = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1, 8, 1>;
-using GemmLoadsSc0 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1, 1, 1, 1>;
+// 2x2 waves of 128x128 made of 16x16x32 MFMA blocks (128 MFMA slots per K
+// tile), the next K step's operand reads one every 2 slots, one refill load
+// every 4 slots (offset by one slot from the reads), swizzled LDS, persistent
+// grouped scheduler.  The 16x16x32 shape moves half the accumulator bytes
+// per flop of 32x32x16 and runs at a measurably higher sustained clock under
+// the power limit.  The others exist for ablation measurements.
+using GemmDefault = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1>;
+using GemmNoSwizzle = GemmShape<256, 256, 64, 2, 2, 2, false, true, 4, 1, 1, 1, 0, 16, 2, 1>;
+using GemmNonPersistent = GemmShape<256, 256, 64, 2, 2, 2, true, false, 4, 1, 1, 1, 0, 16, 2, 1>;
+using GemmReadEverySlot = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 1, 0>;
+using GemmReadEvery4 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 4, 2>;
+using GemmRefillEvery5 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 5, 1, 1, 1, 0, 16, 2, 1>;
+using GemmRefillEvery6 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 6, 1, 1, 1, 0, 16, 2, 1>;
+using GemmKStagger = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 8, 1, 0, 16, 2, 1>;
+using GemmLoadsSc0 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 1, 16, 2, 1>;
+// 32x32x16 MFMA blocks (64 slots per K tile), one operand read per slot, a
+// refill load every 2 slots; the same with a single LDS stage (the
+// hand-written 16x16x32 MFMAs are kept to the pipelined loop, whose
+// accumulators stay in place), and with K tiles of 32 in a 4-stage ring.
+using Gemm32x32 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1>;
+using Gemm32x32OneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true, 1, 1>;
+using Gemm32x32Bk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
 
 static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDefault::BK == kGemmBK &&
                   GemmDefault::STAGES == kGemmStages && GemmDefault::kThreads == kGemmThreads,
@@ -512,15 +580,16 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
   switch (variant) {
     case 0: return launch<GemmDefault>(A, B, D, M, N, K, num_cus, stream);
     case 1: return launch<GemmNoSwizzle>(A, B, D, M, N, K, num_cus, stream);
-    case 2: return launch<GemmOneStage>(A, B, D, M, N, K, num_cus, stream);
+    case 2: return launch<Gemm32x32OneStage>(A, B, D, M, N, K, num_cus, stream);
     case 3: return launch<GemmNonPersistent>(A, B, D, M, N, K, num_cus, stream);
-    case 4: return launch<GemmBk32FourStage>(A, B, D, M, N, K, num_cus, stream);
-    case 5: return launch<GemmBk32ThreeStage>(A, B, D, M, N, K, num_cus, stream);
-    case 6: return launch<GemmBk32FiveStage>(A, B, D, M, N, K, num_cus, stream);
-    case 7: return launch<GemmRefillEveryMfma>(A, B, D, M, N, K, num_cus, stream);
-    case 8: return launch<GemmRefillEvery3>(A, B, D, M, N, K, num_cus, stream);
-    case 9: return launch<GemmKStagger>(A, B, D, M, N, K, num_cus, stream);
-    case 10: return launch<GemmLoadsSc0>(A, B, D, M, N, K, num_cus, stream);
+    case 4: return launch<GemmReadEverySlot>(A, B, D, M, N, K, num_cus, stream);
+    case 5: return launch<GemmReadEvery4>(A, B, D, M, N, K, num_cus, stream);
+    case 6: return launch<GemmRefillEvery5>(A, B, D, M, N, K, num_cus, stream);
+    case 7: return launch<GemmRefillEvery6>(A, B, D, M, N, K, num_cus, stream);
+    case 8: return launch<GemmKStagger>(A, B, D, M, N, K, num_cus, stream);
+    case 9: return launch<GemmLoadsSc0>(A, B, D, M, N, K, num_cus, stream);
+    case 10: return launch<Gemm32x32>(A, B, D, M, N, K, num_cus, stream);
+    case 11: return launch<Gemm32x32Bk32FourStage>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -122,15 +122,20 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  * gemvtile_gemm_f16_variant -- gemm_f16 with an internal kernel variant, for
  * ablation measurements only (same contract and results as gemm_f16).  All
  * use 256x256 output tiles and 4 waves of 128x128:
- *   0  the default kernel (identical to gemm_f16): K tiles of 64, a 2-stage
- *      LDS ring refilled one load every 2 MFMAs, swizzled LDS, persistent
+ *   0  the default kernel (identical to gemm_f16): 16x16x32 MFMA blocks, K
+ *      tiles of 64 in a 2-stage LDS ring, the next K step's operand reads one
+ *      every 2 MFMA slots, a refill load every 4 slots, swizzled LDS,
+ *      persistent
  *   1  as 0 without the LDS swizzle
- *   2  single-stage LDS (load, wait, compute: no overlap)
+ *   2  as 10 with single-stage LDS (load, wait, compute: no overlap)
  *   3  as 0 with one workgroup per tile (no persistent loop, no XCD remap)
- *   4  K tiles of 32 in a 4-stage ring   5  ... 3-stage   6  ... 5-stage
- *   7  as 0 with a refill load after every MFMA   8  ... every 3 MFMAs
- *   9  as 0 with output tile t starting its K loop at K tile t % 8
- *   10 as 0 with the tile loads' cache-policy modifier sc0
+ *   4  as 0 with one operand read per MFMA slot   5  ... every 4 slots
+ *   6  as 0 with a refill load every 5 MFMA slots   7  ... every 6 slots
+ *   8  as 0 with output tile t starting its K loop at K tile t % 8
+ *   9  as 0 with the tile loads' cache-policy modifier sc0
+ *   10 32x32x16 MFMA blocks, one operand read per slot, a refill load every
+ *      2 of its 64 slots per K tile
+ *   11 as 10 with K tiles of 32 in a 4-stage ring
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
