@@ -66,7 +66,7 @@ namespace gt {
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, bool SWIZZLE_, bool PERSISTENT_,
           int DMA_STRIDE_, int DMA_PHASES_, int K_STAGGER_ = 1, int K_STAGGER_STEP_ = 1, int LOAD_POLICY_ = 0,
-          int MI_ = 32, int READ_STRIDE_ = 1, int DMA_OFFSET_ = 0>
+          int MI_ = 32, int READ_STRIDE_ = 1, int DMA_OFFSET_ = 0, bool FUSE_DMA_ = false>
 struct GemmShape {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -101,6 +101,9 @@ struct GemmShape {
   // loads, which lets them fall between the reads.
   static constexpr int READ_STRIDE = READ_STRIDE_;
   static constexpr int DMA_OFFSET = DMA_OFFSET_;
+  // With 16x16x32 MFMAs: issue each tile load in one asm block with the MFMA
+  // of its slot (see mfma_dma in the kernel).
+  static constexpr bool FUSE_DMA = FUSE_DMA_;
   static_assert((BK / kKStep) >= 1 && (BM / WAVES_M / MI) * (BN / WAVES_N / MI) % READ_STRIDE == 0,
                 "the read spacing must divide the MFMA slots of a K step");
 
@@ -216,6 +219,15 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
   // Both operands use the same lane -> K mapping, so the products pair up.
   const int frag_row = lane % S::MI;
   const int frag_kgrp = lane / S::MI;
+  // Which 16-byte chunk of the K step lane group frag_kgrp reads.  The MFMA
+  // only needs A and B to agree, so the order is free.  The LDS serves a
+  // 16-byte-per-lane read in lane groups that pair lane l with lane l + 32;
+  // with 16x16 blocks those lanes read the same rows, and chunks c and c + 2
+  // (an even XOR apart) would land two rows on the same banks under the row
+  // swizzle.  Groups 0..3 therefore read chunks 0, 2, 1, 3 of the step, so
+  // lanes l and l + 32 differ by an odd XOR.  With 32x32 blocks (two groups:
+  // chunks c, c + 1) the plain order already has that property.
+  const int frag_kchunk = S::MI == 16 ? ((frag_kgrp & 1) << 1) | (frag_kgrp >> 1) : frag_kgrp;
   // Fragment row blocks start at multiples of MI (16 or 32), and swz()
   // depends only on row & 15, so swz() of every fragment row equals
   // swz(lane % MI).
@@ -246,7 +258,14 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
     // K tile kt of the loop reads K tile (kt + kofs) mod KT of the matrices.
     int kofs = 0;
     if constexpr (S::K_STAGGER > 1) kofs = static_cast<int>((t % S::K_STAGGER) * S::K_STAGGER_STEP) % KT;
-    auto issue_loads = [&](int kt, int first, int last) {
+    // Operands of load d of K tile kt: buffer descriptor, per-lane byte
+    // offset, and the (wave-uniform) LDS address of its 1 KiB destination.
+    struct DmaArgs {
+      int4_t rsrc;
+      uint32_t voffset;
+      uint32_t lds;
+    };
+    auto dma_args = [&](int kt, int d) -> DmaArgs {
       int ka = kt + kofs;
       if (ka >= KT) ka -= KT;
       const int k0 = ka * S::BK;
@@ -254,17 +273,19 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
       const uint32_t off = (k0 + tile_ld_kcol < K) ? tile_ld_off + static_cast<uint32_t>(k0) * 2u : kOobOffset;
       const uint32_t stage_lds = lds0 + static_cast<uint32_t>((kt % S::STAGES) * S::kStageBytes) +
                                  static_cast<uint32_t>(wave * S::kRowsPerDma * S::kRowBytes);
+      if (d < S::kDmaA)
+        return DmaArgs{rsrc_a, off + d * ld_step,
+                       static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(stage_lds + d * kLdsStep))};
+      const int i = d - S::kDmaA;
+      return DmaArgs{rsrc_b, off + i * ld_step,
+                     static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(stage_lds + S::kStageA + i * kLdsStep))};
+    };
+    auto issue_loads = [&](int kt, int first, int last) {
 #pragma unroll
       for (int d = 0; d < S::kDmaPerStage; ++d) {
         if (d < first || d >= last) continue;
-        if (d < S::kDmaA) {
-          lds_dma_b128<S::LOAD_POLICY>(rsrc_a, off + d * ld_step,
-                                       __builtin_amdgcn_readfirstlane(stage_lds + d * kLdsStep));
-        } else {
-          const int i = d - S::kDmaA;
-          lds_dma_b128<S::LOAD_POLICY>(rsrc_b, off + i * ld_step,
-                                       __builtin_amdgcn_readfirstlane(stage_lds + S::kStageA + i * kLdsStep));
-        }
+        const DmaArgs g = dma_args(kt, d);
+        lds_dma_b128<S::LOAD_POLICY>(g.rsrc, g.voffset, g.lds);
       }
     };
 
@@ -277,7 +298,7 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
     static_assert(kMfma >= kReads * S::READ_STRIDE, "MFMA slots for the operand reads");
     auto read_frag = [&](int buf, int kt, int ks, int r) {
       const char *stage_ptr = smem + (kt % S::STAGES) * S::kStageBytes;
-      const uint32_t chunk = static_cast<uint32_t>(((ks * (S::kKStep / 8) + frag_kgrp) ^ frag_swz) * 16);
+      const uint32_t chunk = static_cast<uint32_t>(((ks * (S::kKStep / 8) + frag_kchunk) ^ frag_swz) * 16);
       if (r == 0) {
         fa[buf][0] = *reinterpret_cast<const half8_t *>(stage_ptr + a_row_base + chunk);
       } else if (r <= S::kFragN) {
@@ -331,6 +352,28 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
                      : "+a"(acc[i][j])
                      : "v"(fb[buf][j]), "v"(fa[buf][i]));
       }
+    };
+    // A 16x16x32 MFMA together with one tile load, in one asm block: M0 (the
+    // load's LDS address) is written before the MFMA, which then serves as the
+    // wait state the load needs after an M0 write.  Issued separately, the M0
+    // write, its s_nop and the load take longer than one 16x16x32 MFMA slot
+    // and delay the next MFMA.  Fusing removes most of that delay (about 7K
+    // cycles per wave at 4096^3), but the chip is power-limited and its clock
+    // drops by more: the default issues the loads separately.
+    constexpr bool kFusedDma = S::FUSE_DMA && S::MI == 16 && S::DMA_PHASES == 1 && S::LOAD_POLICY == 0;
+    auto mfma_dma = [&](int buf, int idx, const DmaArgs &g) {
+      const int i = idx / S::kFragN;
+      const int j = idx % S::kFragN;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile(
+          "s_mov_b32 m0, %3\n\t"
+          "v_mfma_f32_16x16x32_f16 %0, %1, %2, %0\n\t"
+          "buffer_load_dwordx4 %4, %5, 0 offen lds"
+          : "+a"(acc[i][j])
+          : "v"(fb[buf][j]), "v"(fa[buf][i]), "s"(g.lds), "v"(g.voffset), "s"(g.rsrc)
+          : "memory", "m0");
+#pragma clang diagnostic pop
     };
     // Wait states between the last hand-written MFMA and any read of its
     // result: more than the 16x16x32 MFMA's pass count requires.  The
@@ -423,7 +466,22 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
               workgroup_barrier();
               __builtin_amdgcn_sched_barrier(0);
             }
-            mfma(cur, idx);
+            // The tile load (if any) that this slot carries.
+            int dma_tile = -1, dma_d = -1;
+            if (last && idx >= kBarrierAt) {
+              if (kEarlyOn) {
+                dma_tile = kt + S::STAGES;
+                dma_d = dma_at(idx - kBarrierAt, 0);
+              }
+            } else if (kRest) {
+              dma_tile = kt + S::STAGES - 1;
+              dma_d = dma_at(kAfter + ks * kMfma + idx, 0);
+            }
+            if (kFusedDma && dma_d >= 0) {
+              mfma_dma(cur, idx, dma_args(dma_tile, dma_d));
+            } else {
+              mfma(cur, idx);
+            }
             __builtin_amdgcn_sched_barrier(0);
             if (!last) {
               if (idx % S::READ_STRIDE == 0 && idx / S::READ_STRIDE < kReads) {
@@ -434,14 +492,16 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
               read_frag(cur ^ 1, kt + 1, 0, (idx - kBarrierAt) / S::READ_STRIDE);
               __builtin_amdgcn_sched_barrier(0);
             }
-            if (last && idx >= kBarrierAt) {
-              if (kEarlyOn) {
-                dma_slot(kt + S::STAGES, idx - kBarrierAt);
+            if (!kFusedDma) {
+              if (last && idx >= kBarrierAt) {
+                if (kEarlyOn) {
+                  dma_slot(kt + S::STAGES, idx - kBarrierAt);
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+              } else if (kRest) {
+                dma_slot(kt + S::STAGES - 1, kAfter + ks * kMfma + idx);
                 __builtin_amdgcn_sched_barrier(0);
               }
-            } else if (kRest) {
-              dma_slot(kt + S::STAGES - 1, kAfter + ks * kMfma + idx);
-              __builtin_amdgcn_sched_barrier(0);
             }
           }
         }
@@ -552,6 +612,7 @@ using GemmLoadsSc0 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 1,
 // refill load every 2 slots; the same with a single LDS stage (the
 // hand-written 16x16x32 MFMAs are kept to the pipelined loop, whose
 // accumulators stay in place), and with K tiles of 32 in a 4-stage ring.
+using GemmFusedLoads = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, true>;
 using Gemm32x32 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1>;
 using Gemm32x32OneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true, 1, 1>;
 using Gemm32x32Bk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
@@ -590,6 +651,7 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 9: return launch<GemmLoadsSc0>(A, B, D, M, N, K, num_cus, stream);
     case 10: return launch<Gemm32x32>(A, B, D, M, N, K, num_cus, stream);
     case 11: return launch<Gemm32x32Bk32FourStage>(A, B, D, M, N, K, num_cus, stream);
+    case 12: return launch<GemmFusedLoads>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -16,7 +16,7 @@ constexpr int kGemmBK = 64;
 constexpr int kGemmStages = 2;
 constexpr int kGemmThreads = 256;
 constexpr int kGemmGroupM = 8;
-constexpr int kGemmVariants = 12;
+constexpr int kGemmVariants = 13;
 constexpr int kGemvVariants = 8;
 
 // s_waitcnt immediate for "lgkmcnt(0)" alone on gfx9-family targets

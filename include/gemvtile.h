@@ -136,6 +136,9 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *   10 32x32x16 MFMA blocks, one operand read per slot, a refill load every
  *      2 of its 64 slots per K tile
  *   11 as 10 with K tiles of 32 in a 4-stage ring
+ *   12 as 0 with each tile load issued in one block with its slot's MFMA
+ *      (M0 written before the MFMA, which serves as the wait state) rather
+ *      than on its own (M0 write, wait state, load)
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
