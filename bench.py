@@ -32,6 +32,7 @@ METRIC = "fp16 GEMM TFLOP/s @4096³ (% MFMA peak); GEMV GB/s (% HBM peak)"
 GEMM_M = GEMM_N = GEMM_K = 4096
 GEMV_N, GEMV_K = 4096, 14336
 GEMM_SETS = 3
+DECODE_REPS = 20  # event pairs around 5 decode-batch launches, after the timed steps
 GEMV_COPIES = 5
 # Beyond-L2 traffic per launch measured with rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch, each scaled by what the same counter reads for
@@ -43,7 +44,7 @@ MEASURED_TRAFFIC = {
     "gemm": {"fetch_kib": 98437.5 * 2.0, "write_kib": 32768.0 * 1.0},
     "gemv": {"fetch_kib": 57481.0 * 2.0, "write_kib": 8.0 * 1.0},
 }
-KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemv.hip", "kernels.hpp", "tile_order.hpp")
+KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemv.hip", "kernels.hpp", "skinny.hip", "tile_order.hpp")
 
 
 def kernel_sources_sha256() -> str:
@@ -205,6 +206,34 @@ def main():
     gemv_bytes = metrics.gemv_bytes(wv.N, wv.K)
     gemv_gbps = gemv_bytes / gemv_s / 1e9
 
+    # ---- decode batch (8 activation rows against the GEMV's weight shape) --
+    # Timed on its own after the steps: 5 launches per event pair, one per W
+    # copy, so every launch streams its B from HBM.
+    wd = datagen.DECODE_BATCH
+    Ad0, _ = datagen.gemm_inputs(wd)
+    Ad = torch.from_numpy(Ad0).to(dev)
+    Dd = [torch.empty((wd.M, wd.N), dtype=torch.float16, device=dev) for _ in range(GEMV_COPIES)]
+
+    def decode_batch():
+        st = 0
+        for c, (W, _) in enumerate(gemv_sets):
+            st |= gt.gemm_f16_ptr(Ad.data_ptr(), W.data_ptr(), Dd[c].data_ptr(), wd.M, wd.N, wd.K, sh)
+        if st:
+            raise RuntimeError(f"library call failed: {gt.status_string(st)}")
+
+    for _ in range(5):
+        decode_batch()
+    dev_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(DECODE_REPS)]
+    torch.cuda.synchronize(dev)
+    for e in dev_events:
+        e[0].record(stream)
+        decode_batch()
+        e[1].record(stream)
+    torch.cuda.synchronize(dev)
+    decode_s = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_events])) / 1e3 / GEMV_COPIES
+    decode_bytes = metrics.gemm_bytes(wd.M, wd.N, wd.K)
+    decode_gbps = decode_bytes / decode_s / 1e9
+
     cpu = cpu_baseline(args.cpu_seconds)
 
     def traffic(kind):
@@ -260,6 +289,22 @@ def main():
                 "frac": round(gemv_gbps / metrics.PEAK_HBM_GBPS, 4),
                 "traffic": traffic("gemv"),
                 "kernel": "gemv_f16_kernel",
+            },
+        },
+        "decode_batch": {
+            "workload": f"gemm_f16 D=A·Bᵀ {wd.M}x{wd.N}x{wd.K} (5 distinct B), skinny path",
+            "value": round(decode_gbps, 1),
+            "unit": "GB/s",
+            "us_per_launch": round(decode_s * 1e6, 2),
+            "tflops": round(metrics.gemm_flops(wd.M, wd.N, wd.K) / decode_s / 1e12, 2),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(decode_gbps, 1),
+                "peak": metrics.PEAK_HBM_GBPS,
+                "unit": "GB/s",
+                "frac": round(decode_gbps / metrics.PEAK_HBM_GBPS, 4),
+                "traffic": None,
+                "kernel": "gemm_skinny_kernel",
             },
         },
         "cpu_baseline": cpu,

@@ -25,6 +25,7 @@ import numpy as np
 __all__ = [
     "Workload",
     "WORKLOADS",
+    "DECODE_BATCH",
     "rng",
     "uniform_f16",
     "integer_f16",
@@ -59,6 +60,12 @@ WORKLOADS = (
     Workload(3, "gemv_4096x14336", "gemv", 1, 4096, 14336, -1.0, 1.0, -0.05, 0.05),
     Workload(4, "gemm_8192", "gemm", 8192, 8192, 8192, -1.0, 1.0, -1.0, 1.0, sampled_rows=64),
 )
+
+
+# A decode batch: 8 activation rows against the GEMV's weight matrix shape,
+# D = A·Bᵀ with A [8,14336] ~ uniform(-1,1) and B [4096,14336] ~
+# uniform(-0.05,0.05) -- the GEMV workload with a batch of 8 instead of 1.
+DECODE_BATCH = Workload(5, "gemm_decode_8x4096x14336", "gemm", 8, 4096, 14336, -1.0, 1.0, -0.05, 0.05)
 
 
 def rng(cfg_id: int, tensor_id: int) -> np.random.Generator:

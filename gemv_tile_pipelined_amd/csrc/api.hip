@@ -88,6 +88,26 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   if (st != GEMVTILE_OK || noop) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K == 0) return to_status(gt::launch_fill_zero_f16(D, M * N, s));
+  const bool skinny = M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows;
+  // Variant 0 (gemm_f16) sends shapes with at most 16 rows on one side to
+  // the skinny kernel; variants kGemmVariants.. force skinny launch shapes.
+  if (variant >= gt::kGemmVariants) {
+    if (!skinny) return GEMVTILE_ERR_UNSUPPORTED;
+    return to_status(gt::launch_gemm_skinny_f16(variant - gt::kGemmVariants, A, B, D, static_cast<int>(M),
+                                                static_cast<int>(N), static_cast<int>(K), s));
+  }
+  if (variant == 0 && (M == 1 || N == 1)) {
+    // One row on a side is the batch-1 product y = x·Wᵀ: M == 1 is
+    // D[0][n] = A[0]·B[n] (x = A, W = B); N == 1 is D[m][0] = A[m]·B[0]
+    // (x = B, W = A), whose [M,1] output is a contiguous vector.
+    const void *x = M == 1 ? A : B;
+    const void *W = M == 1 ? B : A;
+    const int64_t rows = M == 1 ? N : M;
+    return to_status(gt::launch_gemv_f16(0, x, W, D, static_cast<int>(rows), static_cast<int>(K), s));
+  }
+  if (variant == 0 && skinny)
+    return to_status(gt::launch_gemm_skinny_f16(0, A, B, D, static_cast<int>(M), static_cast<int>(N),
+                                                static_cast<int>(K), s));
   int cus = 0;
   st = current_cu_count(&cus);
   if (st != GEMVTILE_OK) return st;
@@ -118,7 +138,7 @@ int gemv_f16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *
 
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream,
                               int variant) {
-  if (variant < 0 || variant >= gt::kGemmVariants) return GEMVTILE_ERR_INVALID_ARG;
+  if (variant < 0 || variant >= gt::kGemmVariants + gt::kSkinnyVariants) return GEMVTILE_ERR_INVALID_ARG;
   return run_gemm(A, B, D, M, N, K, stream, variant);
 }
 
@@ -164,6 +184,9 @@ void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, 
 
 int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus) {
   if (M <= 0 || N <= 0 || num_cus <= 0) return 0;
+  // Skinny shapes: one workgroup per 16 rows of the larger side.
+  if (M <= gt::kSkinnyMaxRows) return (N + 15) / 16;
+  if (N <= gt::kSkinnyMaxRows) return (M + 15) / 16;
   const int64_t tiles = ((M + gt::kGemmBM - 1) / gt::kGemmBM) * ((N + gt::kGemmBN - 1) / gt::kGemmBN);
   return tiles < num_cus ? tiles : num_cus;
 }

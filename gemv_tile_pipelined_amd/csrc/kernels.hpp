@@ -18,6 +18,10 @@ constexpr int kGemmThreads = 256;
 constexpr int kGemmGroupM = 8;
 constexpr int kGemmVariants = 13;
 constexpr int kGemvVariants = 8;
+// GEMMs with at most this many rows on one side (M or N) take the skinny
+// kernel (skinny.hip); it has kSkinnyVariants launch shapes.
+constexpr int kSkinnyMaxRows = 16;
+constexpr int kSkinnyVariants = 5;
 
 // s_waitcnt immediate for "lgkmcnt(0)" alone on gfx9-family targets
 // (vmcnt field [3:0]|[15:14] = 63, expcnt [6:4] = 7, lgkmcnt [11:8] = 0).
@@ -26,6 +30,8 @@ constexpr unsigned kWaitLgkm0 = 0xC07F;
 
 hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                            hipStream_t stream);
+hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K,
+                                  hipStream_t stream);
 hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, hipStream_t stream);
 hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream);
 

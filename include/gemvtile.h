@@ -63,6 +63,10 @@ enum gemvtile_status {
  * M, N need not be multiples of any tile size: edge tiles read zeros beyond
  * the matrix and write only inside it.  The summation order within FP32 is
  * unspecified (several results are correct up to rounding).
+ * When M <= 16 or N <= 16 (a decode batch against a weight matrix) the call
+ * runs a bandwidth-bound kernel that streams the larger operand once instead
+ * of the 256x256-tiled one, and when M == 1 or N == 1 the GEMV kernel of
+ * gemv_f16; results are deterministic either way.
  * Returns a gemvtile_status.
  */
 int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream);
@@ -113,8 +117,11 @@ void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, 
 
 /*
  * gemvtile_gemm_grid -- the number of workgroups gemm_f16 launches for an
- * M x N output on a device with `num_cus` compute units (persistent grid:
- * min(#tiles, num_cus)).  Host-only arithmetic; returns 0 for empty outputs.
+ * M x N output on a device with `num_cus` compute units: ceil(max(M,N)/16)
+ * when M <= 16 or N <= 16 (the skinny kernel, and the GEMV kernel's 16 rows
+ * per workgroup when M or N is 1), otherwise the persistent grid
+ * min(#tiles, num_cus).  Host-only arithmetic; returns 0 for
+ * empty outputs.
  */
 int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
 
@@ -139,6 +146,12 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *   12 as 0 with each tile load issued in one block with its slot's MFMA
  *      (M0 written before the MFMA, which serves as the wait state) rather
  *      than on its own (M0 write, wait state, load)
+ * Variants 1..12 always run the tiled kernel, whatever the shape; variant
+ * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
+ * <= 16: the skinny kernel).
+ *   13..17 the skinny kernel (only for M <= 16 or N <= 16, else
+ *      GEMVTILE_ERR_UNSUPPORTED) with (waves per workgroup, 32-wide K steps
+ *      in flight per wave) = (8,4) [the default], (8,2), (8,8), (16,4), (4,8)
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,

@@ -80,6 +80,8 @@ def test_gemm_argument_validation(lib):
     # unknown internal variant
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, 99) == INVALID
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, -1) == INVALID
+    # skinny launch shapes only apply when one side has at most 16 rows
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 13) == UNSUPPORTED
 
 
 def test_gemv_argument_validation(lib):
@@ -163,6 +165,11 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(256, 256, 256) == 1
     assert gt.gemm_grid(4000, 4032, 256) == 256
     assert gt.gemm_grid(0, 4, 256) == 0
+    # skinny shapes: one workgroup per 16 rows of the larger side
+    assert gt.gemm_grid(8, 4096, 256) == 256
+    assert gt.gemm_grid(4096, 16, 256) == 256
+    assert gt.gemm_grid(16, 16, 256) == 1
+    assert gt.gemm_grid(17, 4097, 256) == 17
     golden = _tile_counts()
     # The TVM chapter's counts at its 128x128 tiles and BLK_K = 64: the same
     # tile-count arithmetic, applied to its parameters.

@@ -1,0 +1,119 @@
+"""Parity of the skinny GEMM path (M <= 16 or N <= 16) with the CPU oracle.
+
+gemm_f16 sends shapes with at most 16 rows on one side to a bandwidth-bound
+kernel that streams the larger operand once.  The bar is the one of the
+tiled GEMM: |d - ref| <= 1e-2 + 1e-2·|ref| for uniform inputs, bit-for-bit
+for integer inputs (exact FP32 partial sums, so only the final rounding to
+nearest-even decides, and it must agree).  Every shape is compared in full:
+the oracle's cost is M·N·K with one small side.
+"""
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL_ABS = 1e-2
+TOL_REL = 1e-2
+
+SKINNY_VARIANTS = range(13, 18)  # gemvtile_gemm_f16_variant ids of the skinny launch shapes
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    import gemv_tile_pipelined_amd as gt
+
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    gt.load_library()
+    return torch, gt, torch.device("cuda:0")
+
+
+def _gemm(env, A, B, variant=0):
+    torch, gt, dev = env
+    D = gt.gemm_f16(torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev), variant=variant)
+    torch.cuda.synchronize(dev)
+    return D.cpu().numpy()
+
+
+def _violations(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return int((~(np.abs(got - ref) <= TOL_ABS + TOL_REL * np.abs(ref))).sum())
+
+
+# (M, N, K): small M (D = A·Bᵀ with A the batch), small N (the transposed
+# store), both small, ragged row counts and K tails (K not a multiple of 32).
+SHAPES = [
+    (1, 4096, 14336),
+    (2, 520, 1032),
+    (8, 4096, 14336),
+    (16, 1000, 4104),
+    (3, 17, 8),
+    (15, 4097, 520),
+    (16, 16, 64),
+    (4000, 16, 4104),
+    (520, 5, 1032),
+    (33, 1, 72),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_skinny_uniform(env, shape):
+    M, N, K = shape
+    cfg = 3000 + SHAPES.index(shape)
+    A = datagen.uniform_f16(cfg, 0, (M, K), -1.0, 1.0)
+    B = datagen.uniform_f16(cfg, 1, (N, K), -1.0, 1.0)
+    got = _gemm(env, A, B)
+    assert got.shape == (M, N)
+    assert np.isfinite(got).all()
+    assert _violations(got, oracle.gemm(A, B)) == 0
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_skinny_integer_exact(env, shape):
+    M, N, K = shape
+    cfg = 3100 + SHAPES.index(shape)
+    A = datagen.integer_f16(cfg, 0, (M, K))
+    B = datagen.integer_f16(cfg, 1, (N, K))
+    assert np.array_equal(_gemm(env, A, B), oracle.gemm(A, B))
+
+
+@pytest.mark.parametrize("variant", SKINNY_VARIANTS)
+@pytest.mark.parametrize("shape", [(8, 1000, 14344), (1000, 8, 1032)], ids=["small_m", "small_n"])
+def test_skinny_variants_exact(env, shape, variant):
+    M, N, K = shape
+    A = datagen.integer_f16(3200, 0, (M, K))
+    B = datagen.integer_f16(3200, 1, (N, K))
+    assert np.array_equal(_gemm(env, A, B, variant=variant), oracle.gemm(A, B))
+
+
+def test_decode_batch_workload(env):
+    """The 8x4096x14336 decode batch in the launch shape the benchmark times."""
+    w = datagen.DECODE_BATCH
+    A, B = datagen.gemm_inputs(w)
+    got = _gemm(env, A, B)
+    assert _violations(got, oracle.gemm(A, B)) == 0
+
+
+def test_skinny_closed_form_and_guard(env):
+    """Rank-1 inputs give exact products; nothing outside D is written."""
+    torch, gt, dev = env
+    for M, N, K in [(7, 3000, 4104), (3000, 7, 4104)]:
+        u = np.array([0.25, -0.5, 1.0, 2.0, -1.0, 0.5, -2.0], np.float16)
+        v = np.array([0.5, -1.0, 2.0, -0.25], np.float16)
+        a = u[np.arange(M) % 7]
+        b = v[np.arange(N) % 4]
+        A = np.repeat(a[:, None], K, axis=1)
+        B = np.repeat(b[:, None], K, axis=1)
+        guard = 4096
+        buf = torch.full((M * N + guard,), float("nan"), dtype=torch.float16, device=dev)
+        D = buf[: M * N].view(M, N)
+        gt.gemm_f16(torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev), D)
+        torch.cuda.synchronize(dev)
+        expect = (K * a.astype(np.float64)[:, None] * b.astype(np.float64)[None, :]).astype(np.float16)
+        assert np.array_equal(D.cpu().numpy(), expect)
+        assert bool(torch.isnan(buf[M * N :]).all())
