@@ -93,6 +93,8 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   // the skinny kernel; variants kGemmVariants.. force skinny launch shapes.
   if (variant >= gt::kGemmVariants) {
     if (!skinny) return GEMVTILE_ERR_UNSUPPORTED;
+    if (variant - gt::kGemmVariants >= gt::kSkinnyFirstQ8Variant && (M < N ? M : N) > 8)
+      return GEMVTILE_ERR_UNSUPPORTED;
     return to_status(gt::launch_gemm_skinny_f16(variant - gt::kGemmVariants, A, B, D, static_cast<int>(M),
                                                 static_cast<int>(N), static_cast<int>(K), s));
   }

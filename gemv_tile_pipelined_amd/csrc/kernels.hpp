@@ -21,7 +21,9 @@ constexpr int kGemvVariants = 8;
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip); it has kSkinnyVariants launch shapes.
 constexpr int kSkinnyMaxRows = 16;
-constexpr int kSkinnyVariants = 5;
+constexpr int kSkinnyVariants = 12;
+// Skinny launch shapes from this index on stage only 8 rows of the small side.
+constexpr int kSkinnyFirstQ8Variant = 9;
 
 // s_waitcnt immediate for "lgkmcnt(0)" alone on gfx9-family targets
 // (vmcnt field [3:0]|[15:14] = 63, expcnt [6:4] = 7, lgkmcnt [11:8] = 0).

@@ -23,10 +23,16 @@
 //    reads 64 contiguous bytes from each of 16 rows.  Rows of Q past S and
 //    rows of P past R are clamped to the last valid row: they only feed
 //    outputs that are never stored.  K chunks past K read as zero.
-//  * The WAVES waves of a workgroup split the K steps (wave w takes UNROLL
-//    consecutive steps out of every WAVES*UNROLL), each keeping UNROLL pairs
-//    of loads in flight.  Their 16x16 partial sums meet in LDS and are added
-//    in wave order, so every output is deterministic.
+//  * The WAVES waves of a workgroup split the K steps.  Their 16x16 partial
+//    sums meet in LDS and are added in wave order, so every output is
+//    deterministic.
+//  * Two ways to feed the MFMAs: straight into registers (each wave keeps
+//    UNROLL pairs of loads in flight; one load instruction touches 16 rows x
+//    64 bytes), or -- the default -- through an LDS ring filled by
+//    direct-to-LDS loads of whole 1 KiB row segments (gemm_skinny_lds_kernel
+//    below).  On 8x4096x14336 the ring takes 23 us against 30 us, because
+//    the register form re-reads the small operand in 64-byte pieces from
+//    every workgroup.
 //  * Output: D[s*R + r] (D = Q·Pᵀ, the M <= 16 case) or D[r*S + s]
 //    (TRANS, D = P·Qᵀ, the N <= 16 case), rounded to nearest-even fp16.
 #include <hip/hip_runtime.h>
@@ -89,6 +95,144 @@ gemm_skinny_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ 
   }
 }
 
+// Wait until at most `younger` K tiles of PER loads each are still pending
+// (loads complete in issue order); `younger` is in [0, MAXY].
+template <int PER, int MAXY>
+__device__ inline void wait_younger(int younger) {
+  if constexpr (MAXY > 0) {
+    if (younger >= MAXY) {
+      wait_vmcnt<MAXY * PER>();
+      return;
+    }
+    wait_younger<PER, MAXY - 1>(younger);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// LDS-staged variant: both operands go through a STAGES-deep LDS ring of K
+// tiles of BK = 512 (1 KiB per row), filled by direct-to-LDS loads in which
+// one wave instruction moves one whole 1 KiB row segment (the register
+// variant above touches 16 rows x 64 bytes per instruction, and every
+// workgroup re-reads the small operand that way).  A stage holds the 16 rows
+// of P and QROWS rows of Q (rows past R or S and K past K read as zero: the
+// buffer descriptors' ranges and an out-of-range offset).  With QROWS = 8
+// (for S <= 8) the MFMA lanes of Q rows 8..15 re-read rows 0..7, whose
+// products only reach outputs that are never stored, and the smaller stage
+// lets the ring keep more of P in flight.  Each wave issues
+// (16+QROWS)/WAVES row loads per stage and computes BK/32/WAVES of the
+// stage's K steps.  LDS chunk c of row r holds logical chunk c ^ s(r) with
+// s(r) = 2*(r % 8) + (r / 8) (the loader picks the global chunk per lane to
+// make it so), and the four lane groups of a K step read chunks 0, 2, 1, 3
+// of the step: lanes l and l + 32, which the LDS serves together, then read
+// chunks an odd XOR apart and every read is bank-conflict free.
+template <int WAVES, int STAGES, int QROWS, bool TRANS>
+__global__ void __launch_bounds__(WAVES * 64)
+gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ Q, _Float16 *__restrict__ D,
+                       int R, int S, int K) {
+  constexpr int BK = 512;
+  constexpr int kRowBytes = BK * 2;            // 1 KiB: one wave instruction
+  constexpr int kTileBytes = 16 * kRowBytes;                 // the 16 rows of P
+  constexpr int kStageBytes = (16 + QROWS) * kRowBytes;      // P tile, then Q tile
+  constexpr int kDmaPerWave = (16 + QROWS) / WAVES;          // row loads per wave per stage
+  constexpr int kSteps = BK / 32;                            // 32-wide K steps per stage
+  constexpr int kStepsPerWave = kSteps / WAVES;
+  static_assert(QROWS == 8 || QROWS == 16, "Q tile rows");
+  static_assert((16 + QROWS) % WAVES == 0 && kSteps % WAVES == 0, "work split");
+  static_assert(STAGES >= 2 && (STAGES - 1) * kDmaPerWave <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char ring[STAGES * kStageBytes];
+  __shared__ float partial[WAVES][16][17];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r0 = blockIdx.x * 16;
+  const int prows = min(16, R - r0);
+  const int4_t rsrc_p = make_buffer_rsrc(P + static_cast<int64_t>(r0) * K, static_cast<uint32_t>(prows) * K * 2u);
+  const int4_t rsrc_q = make_buffer_rsrc(Q, static_cast<uint32_t>(S) * K * 2u);
+  const uint32_t ring0 = lds_addr(ring);
+  const int KT = (K + BK - 1) / BK;
+  auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+
+  // Row loads of K tile kt: load d of this wave moves tile row
+  // t = d*WAVES + wave (P rows 0..15, then Q rows 0..QROWS-1).
+  auto issue = [&](int kt) {
+    const uint32_t stage = ring0 + static_cast<uint32_t>((kt % STAGES) * kStageBytes);
+#pragma unroll
+    for (int d = 0; d < kDmaPerWave; ++d) {
+      const int t = d * WAVES + wave;
+      const int row = t & 15;
+      const int k = kt * BK + ((lane ^ swz(row)) << 3);  // first K element this lane fetches
+      const uint32_t off = k < K ? static_cast<uint32_t>(row) * K * 2u + static_cast<uint32_t>(k) * 2u : kOobOffset;
+      lds_dma_b128(t < 16 ? rsrc_p : rsrc_q, off,
+                   __builtin_amdgcn_readfirstlane(stage + static_cast<uint32_t>(t * kRowBytes)));
+    }
+  };
+
+  const int frow = lane & 15;
+  const int kgrp = lane >> 4;
+  const int kperm = ((kgrp & 1) << 1) | (kgrp >> 1);
+  const uint32_t frag_off = static_cast<uint32_t>(frow * kRowBytes);
+  const int fswz = swz(frow);
+  const int qrow = frow % QROWS;  // Q row of this lane's fragment
+  const uint32_t qfrag_off = static_cast<uint32_t>(kTileBytes + qrow * kRowBytes);
+  const int qswz = swz(qrow);
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue(s);
+
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int kt = 0; kt < KT; ++kt) {
+    // Tile kt has landed once at most `younger` tiles' loads are pending.
+    // Loads complete in issue order, so waiting until at most
+    // younger*kDmaPerWave are pending leaves only the younger tiles in flight.
+    wait_younger<kDmaPerWave, STAGES - 2>(min(KT, kt + STAGES - 1) - (kt + 1));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    workgroup_barrier();  // tile kt complete for everyone; tile kt-1 no longer read
+    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+    const char *stage = ring + (kt % STAGES) * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < kStepsPerWave; ++j) {
+      const int step = wave * kStepsPerWave + j;
+      const int c = step * 4 + kperm;  // logical chunk
+      const half8_t pf = *reinterpret_cast<const half8_t *>(stage + frag_off + ((c ^ fswz) << 4));
+      const half8_t qf = *reinterpret_cast<const half8_t *>(stage + qfrag_off + ((c ^ qswz) << 4));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, qf, acc, 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int e = 0; e < 4; ++e) partial[wave][frow][4 * kgrp + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int s = threadIdx.x >> 4;
+    const int r = threadIdx.x & 15;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += partial[w][s][r];
+    if (s < S && r0 + r < R) {
+      const int64_t idx = TRANS ? static_cast<int64_t>(r0 + r) * S + s : static_cast<int64_t>(s) * R + r0 + r;
+      D[idx] = static_cast<_Float16>(sum);
+    }
+  }
+}
+
+template <int WAVES, int STAGES, int QROWS>
+static hipError_t launch_lds(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
+                             hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((R + 15) / 16));
+  const auto *p = static_cast<const _Float16 *>(P);
+  const auto *q = static_cast<const _Float16 *>(Q);
+  auto *d = static_cast<_Float16 *>(D);
+  if (trans)
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, true>), grid, dim3(WAVES * 64), 0, stream, p, q,
+                       d, R, S, K);
+  else
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, false>), grid, dim3(WAVES * 64), 0, stream, p,
+                       q, d, R, S, K);
+  return hipGetLastError();
+}
+
 template <int WAVES, int UNROLL>
 static hipError_t launch(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                          hipStream_t stream) {
@@ -115,13 +259,22 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
   const void *Q = small_m ? A : B;
   const int R = small_m ? N : M;
   const int S = small_m ? M : N;
-  // <waves per workgroup, K steps in flight per wave>
   switch (variant) {
-    case 0: return launch<8, 4>(P, Q, D, R, S, K, !small_m, stream);
-    case 1: return launch<8, 2>(P, Q, D, R, S, K, !small_m, stream);
-    case 2: return launch<8, 8>(P, Q, D, R, S, K, !small_m, stream);
-    case 3: return launch<16, 4>(P, Q, D, R, S, K, !small_m, stream);
-    case 4: return launch<4, 8>(P, Q, D, R, S, K, !small_m, stream);
+    // LDS-staged: <waves per workgroup, ring stages, Q rows staged>; 0 is the default
+    case 0: return launch_lds<16, 4, 16>(P, Q, D, R, S, K, !small_m, stream);
+    case 1: return launch_lds<8, 4, 16>(P, Q, D, R, S, K, !small_m, stream);
+    case 2: return launch_lds<8, 3, 16>(P, Q, D, R, S, K, !small_m, stream);
+    case 3: return launch_lds<4, 4, 16>(P, Q, D, R, S, K, !small_m, stream);
+    // operands loaded into registers: <waves per workgroup, K steps in flight per wave>
+    case 4: return launch<8, 4>(P, Q, D, R, S, K, !small_m, stream);
+    case 5: return launch<8, 2>(P, Q, D, R, S, K, !small_m, stream);
+    case 6: return launch<8, 8>(P, Q, D, R, S, K, !small_m, stream);
+    case 7: return launch<16, 4>(P, Q, D, R, S, K, !small_m, stream);
+    case 8: return launch<4, 8>(P, Q, D, R, S, K, !small_m, stream);
+    // Q tile of 8 rows (S <= 8 only): deeper rings
+    case 9: return S <= 8 ? launch_lds<8, 5, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 10: return S <= 8 ? launch_lds<8, 6, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 11: return S <= 8 ? launch_lds<4, 6, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

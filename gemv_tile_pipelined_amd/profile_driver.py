@@ -2,13 +2,15 @@
 
     python -m gemv_tile_pipelined_amd.profile_driver gemm [--variant V] [--shape M N K] [--iters I]
     python -m gemv_tile_pipelined_amd.profile_driver gemv [--variant V] [--shape N K] [--iters I]
+    python -m gemv_tile_pipelined_amd.profile_driver decode [--variant V] [--shape M N K] [--iters I]
     python -m gemv_tile_pipelined_amd.profile_driver copy [--mib S] [--iters I]
 
 Meant to run under `rocprofv3 --pmc ...`: every dispatch of the chosen kernel
 then carries its counters.  `copy` runs a plain device-to-device copy of a
 known size, which calibrates byte counters (FETCH_SIZE, WRITE_SIZE) against
 bytes that are known exactly.  Inputs are seeded synthetic fp16 values; the
-GEMV cycles through 5 copies of W so every dispatch reads W from HBM.
+GEMV and the decode batch (gemm_f16 with few rows of A, default 8x4096x14336)
+cycle through 5 copies of W / B so every dispatch reads it from HBM.
 """
 from __future__ import annotations
 
@@ -23,7 +25,7 @@ if ROOT not in sys.path:
 
 def main(argv=None):
     p = argparse.ArgumentParser()
-    p.add_argument("kernel", choices=["gemm", "gemv", "copy"])
+    p.add_argument("kernel", choices=["gemm", "gemv", "decode", "copy"])
     p.add_argument("--variant", type=int, default=0)
     p.add_argument("--shape", type=int, nargs="+", default=None)
     p.add_argument("--iters", type=int, default=10)
@@ -44,6 +46,13 @@ def main(argv=None):
         D = torch.empty((M, N), dtype=torch.float16, device=dev)
         for _ in range(a.iters):
             gt.gemm_f16(A, B, D, variant=a.variant)
+    elif a.kernel == "decode":
+        M, N, K = a.shape or (8, 4096, 14336)
+        A = torch.empty((M, K), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)
+        Bs = [torch.empty((N, K), dtype=torch.float16, device=dev).uniform_(-0.05, 0.05, generator=g) for _ in range(5)]
+        D = torch.empty((M, N), dtype=torch.float16, device=dev)
+        for i in range(a.iters):
+            gt.gemm_f16(A, Bs[i % 5], D, variant=a.variant)
     elif a.kernel == "gemv":
         N, K = a.shape or (4096, 14336)
         x = torch.empty((K,), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)

@@ -149,9 +149,14 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  * Variants 1..12 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16: the skinny kernel).
- *   13..17 the skinny kernel (only for M <= 16 or N <= 16, else
- *      GEMVTILE_ERR_UNSUPPORTED) with (waves per workgroup, 32-wide K steps
- *      in flight per wave) = (8,4) [the default], (8,2), (8,8), (16,4), (4,8)
+ *   13..24 the skinny kernel (only for M <= 16 or N <= 16, else
+ *      GEMVTILE_ERR_UNSUPPORTED).  13..16: operands staged through an LDS
+ *      ring of 1 KiB row segments, (waves per workgroup, ring stages) =
+ *      (16,4) [the gemm_f16 default], (8,4), (8,3), (4,4).  17..21: operands
+ *      loaded into registers, (waves, 32-wide K steps in flight per wave) =
+ *      (8,4), (8,2), (8,8), (16,4), (4,8).  22..24: as 13.. with only 8 rows
+ *      of the small side staged (min(M,N) <= 8, else
+ *      GEMVTILE_ERR_UNSUPPORTED), (waves, stages) = (8,5), (8,6), (4,6)
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,

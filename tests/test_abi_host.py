@@ -82,6 +82,8 @@ def test_gemm_argument_validation(lib):
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, -1) == INVALID
     # skinny launch shapes only apply when one side has at most 16 rows
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 13) == UNSUPPORTED
+    # the 8-row small-side stagings need min(M, N) <= 8
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 22) == UNSUPPORTED
 
 
 def test_gemv_argument_validation(lib):

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 TOL_ABS = 1e-2
 TOL_REL = 1e-2
 
-SKINNY_VARIANTS = range(13, 18)  # gemvtile_gemm_f16_variant ids of the skinny launch shapes
+SKINNY_VARIANTS = range(13, 25)  # gemvtile_gemm_f16_variant ids of the skinny launch shapes
 
 
 @pytest.fixture(scope="module")
