@@ -29,6 +29,8 @@ __all__ = [
     "rng",
     "uniform_f16",
     "integer_f16",
+    "uniform_bf16",
+    "integer_bf16",
     "sample_rows",
     "gemm_inputs",
     "gemv_inputs",
@@ -83,6 +85,23 @@ def integer_f16(cfg_id: int, tensor_id: int, shape, lo: int = -8, hi: int = 8) -
     """Integers drawn uniformly from [lo, hi], stored as float16 (exact)."""
     g = rng(cfg_id, tensor_id)
     return g.integers(lo, hi + 1, size=shape).astype(np.float16)
+
+
+def uniform_bf16(cfg_id: int, tensor_id: int, shape, lo: float, hi: float) -> np.ndarray:
+    """bf16 values as uint16 bit patterns (numpy has no bfloat16 dtype):
+    uniform(lo, hi) drawn in float64, cast to float32, and the low 16 bits of
+    the float32 pattern dropped (rounding toward zero, so the input draw does
+    not use the method's round-to-nearest)."""
+    g = rng(cfg_id, tensor_id)
+    f = g.uniform(lo, hi, size=shape).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def integer_bf16(cfg_id: int, tensor_id: int, shape, lo: int = -8, hi: int = 8) -> np.ndarray:
+    """Integers drawn uniformly from [lo, hi] as bf16 bit patterns (exact)."""
+    g = rng(cfg_id, tensor_id)
+    f = g.integers(lo, hi + 1, size=shape).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
 
 
 def sample_rows(cfg_id: int, M: int, count: int) -> np.ndarray:

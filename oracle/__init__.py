@@ -57,6 +57,18 @@ def load(path: str = LIBRARY, build_if_missing: bool = True):
     lib.oracle_gemm_f16.restype = ctypes.c_int
     lib.oracle_gemv_f16.argtypes = [u16p, u16p, u16p, i64, i64, ctypes.c_int]
     lib.oracle_gemv_f16.restype = ctypes.c_int
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = ctypes.c_double
+    lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_bf16_to_f64_array.argtypes = [u16p, f64p, i64]
+    lib.oracle_bf16_to_f64_array.restype = None
+    lib.oracle_f64_to_bf16_array.argtypes = [f64p, u16p, i64]
+    lib.oracle_f64_to_bf16_array.restype = None
+    lib.oracle_gemm_bf16.argtypes = [u16p, u16p, u16p, i64, i64, i64, i64p, i64, ctypes.c_int]
+    lib.oracle_gemm_bf16.restype = ctypes.c_int
+    lib.oracle_gemv_bf16.argtypes = [u16p, u16p, u16p, i64, i64, ctypes.c_int]
+    lib.oracle_gemv_bf16.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     if path == LIBRARY:
@@ -132,6 +144,72 @@ def gemv(x: np.ndarray, W: np.ndarray, nthreads: int = 0, lib=None) -> np.ndarra
     rc = lib.oracle_gemv_f16(px, pw, py, N, K, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_gemv_f16 failed ({rc})")
+    return y
+
+
+# ---- bf16: numpy has no bfloat16 dtype, so bf16 arrays are uint16 bit patterns
+def _bf16_bits(a: np.ndarray):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, f"bf16 arrays are passed as uint16 bit patterns, got {a.dtype}"
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16))
+
+
+def bf16_to_f64(bits: np.ndarray, lib=None) -> np.ndarray:
+    """Decode bf16 bit patterns (uint16) to float64."""
+    lib = lib or load()
+    b = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    out = np.empty(b.shape, np.float64)
+    lib.oracle_bf16_to_f64_array(
+        b.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), b.size
+    )
+    return out.reshape(np.shape(bits))
+
+
+def f64_to_bf16(v: np.ndarray, lib=None) -> np.ndarray:
+    """Round float64 values to bf16 (nearest, ties to even); returns uint16 bit patterns."""
+    lib = lib or load()
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    flat = v.ravel()
+    out = np.empty(flat.shape, np.uint16)
+    lib.oracle_f64_to_bf16_array(
+        flat.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), flat.size
+    )
+    return out.reshape(v.shape)
+
+
+def gemm_bf16(A: np.ndarray, B: np.ndarray, rows=None, nthreads: int = 0, lib=None) -> np.ndarray:
+    """D = A·Bᵀ for bf16 bit arrays, in FP64, rounded once to bf16 (bit patterns out)."""
+    lib = lib or load()
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2
+    _, pa = _bf16_bits(A)
+    _, pb = _bf16_bits(B)
+    if rows is None:
+        nrows, prow = M, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows, prow = rows.size, rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    D = np.empty((nrows, N), np.uint16)
+    _, pd = _bf16_bits(D)
+    rc = lib.oracle_gemm_bf16(pa, pb, pd, M, N, K, prow, nrows, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_bf16 failed ({rc})")
+    return D
+
+
+def gemv_bf16(x: np.ndarray, W: np.ndarray, nthreads: int = 0, lib=None) -> np.ndarray:
+    """y = x·Wᵀ for bf16 bit arrays, in FP64, rounded once to bf16 (bit patterns out)."""
+    lib = lib or load()
+    N, K = W.shape
+    assert x.shape == (K,)
+    _, px = _bf16_bits(x)
+    _, pw = _bf16_bits(W)
+    y = np.empty((N,), np.uint16)
+    _, py = _bf16_bits(y)
+    rc = lib.oracle_gemv_bf16(px, pw, py, N, K, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_gemv_bf16 failed ({rc})")
     return y
 
 

@@ -1,5 +1,5 @@
 /*
- * oracle.c -- the plain, slow CPU oracle for the FP16 GEMM and GEMV.
+ * oracle.c -- the plain, slow CPU oracle for the FP16 and BF16 GEMM and GEMV.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
@@ -27,6 +27,14 @@
  * The fp16 <-> fp64 conversions are written here from the IEEE 754 binary16
  * definition (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits;
  * subnormals; overflow to infinity), not taken from any library.
+ *
+ * BF16 (bfloat16: 1 sign bit, 8 exponent bits with bias 127, 7 fraction
+ * bits -- the upper half of an IEEE binary32) is the element type of the
+ * SM120 walk-through's kernel ("TensorCore_GEMM_with_TMA": nv_bfloat16 A, B
+ * and C at §2.2 entrance, FP32 accumulators rounded with
+ * __float22bfloat162_rn in the §2.3 kernel's epilogue).  The bf16 GEMM and
+ * GEMV are the same definitions with bf16 in and out; their conversions are
+ * written here from that format's definition, in the same way.
  *
  * Parallel over output rows with OpenMP; nothing else is reordered, blocked
  * or fused.
@@ -100,6 +108,74 @@ uint16_t oracle_f64_to_f16_rne(double v)
     return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)q - 1024));
 }
 
+/* ---- bf16 decode: bfloat16 bits -> exact double ------------------------ */
+double oracle_bf16_to_f64(uint16_t b)
+{
+    const int sign = (b >> 15) & 1;
+    const int exp = (b >> 7) & 0xff;
+    const int frac = b & 0x7f;
+    double mag;
+    if (exp == 0) {
+        /* zero or subnormal: frac * 2^(1 - 127 - 7) */
+        mag = ldexp((double)frac, -133);
+    } else if (exp == 255) {
+        mag = frac ? NAN : INFINITY;
+    } else {
+        /* normal: (128 + frac) * 2^(exp - 127 - 7) */
+        mag = ldexp((double)(128 + frac), exp - 134);
+    }
+    return sign ? -mag : mag;
+}
+
+/* ---- bf16 encode: double -> bfloat16 bits, round to nearest even ------- */
+uint16_t oracle_f64_to_bf16_rne(double v)
+{
+    if (isnan(v)) return (uint16_t)0x7fc0; /* a quiet NaN */
+    const uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    /* Largest finite bf16 is (2 - 2^-7) * 2^127; halfway to the next grid
+     * point 2^128 is (2 - 2^-8) * 2^127, and that tie rounds to the even
+     * neighbour 2^128, i.e. to infinity. */
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127)) return (uint16_t)(sign | 0x7f80);
+    if (a < ldexp(1.0, -126)) {
+        /* subnormal range: integer multiple of 2^-133; a count of 128 is
+         * the smallest normal, bit pattern 0x0080 */
+        double q = round_half_even(ldexp(a, 133));
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    int e2;
+    (void)frexp(a, &e2); /* a = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;      /* a in [2^E, 2^(E+1)) */
+    double q = round_half_even(ldexp(a, 7 - E)); /* in [128, 256] */
+    if (q >= 256.0) { /* rounding carried into the next binade */
+        q = 128.0;
+        E += 1;
+    }
+    if (E + 127 >= 255) return (uint16_t)(sign | 0x7f80);
+    return (uint16_t)(sign | (uint16_t)((E + 127) << 7) | (uint16_t)((int)q - 128));
+}
+
+void oracle_bf16_to_f64_array(const uint16_t *h, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_to_f64(h[i]);
+}
+
+void oracle_f64_to_bf16_array(const double *v, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_bf16_rne(v[i]);
+}
+
+/* The element formats: 0 = fp16, 1 = bf16. */
+static double decode(int fmt, uint16_t bits)
+{
+    return fmt ? oracle_bf16_to_f64(bits) : oracle_f16_to_f64(bits);
+}
+
+static uint16_t encode(int fmt, double v)
+{
+    return fmt ? oracle_f64_to_bf16_rne(v) : oracle_f64_to_f16_rne(v);
+}
+
 /* Bulk conversions so the Python side can sweep every bit pattern. */
 void oracle_f16_to_f64_array(const uint16_t *h, double *out, int64_t n)
 {
@@ -111,23 +187,23 @@ void oracle_f64_to_f16_array(const double *v, uint16_t *out, int64_t n)
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_f16_rne(v[i]);
 }
 
-static double *decode_matrix(const uint16_t *src, int64_t count)
+static double *decode_matrix(int fmt, const uint16_t *src, int64_t count)
 {
     double *dst = (double *)malloc((size_t)(count > 0 ? count : 1) * sizeof(double));
     if (!dst) return NULL;
-    for (int64_t i = 0; i < count; ++i) dst[i] = oracle_f16_to_f64(src[i]);
+    for (int64_t i = 0; i < count; ++i) dst[i] = decode(fmt, src[i]);
     return dst;
 }
 
 /*
- * GEMM on a chosen set of output rows.
- *   A     [M,K] fp16 bits, row-major
- *   B     [N,K] fp16 bits, row-major
+ * GEMM on a chosen set of output rows, elements in format fmt.
+ *   A     [M,K] bits, row-major
+ *   B     [N,K] bits, row-major
  *   rows  nrows row indices into [0,M); NULL means all rows 0..M-1
- *   D     [nrows, N] fp16 bits, row-major (row r of D is output row rows[r])
+ *   D     [nrows, N] bits, row-major (row r of D is output row rows[r])
  * Returns 0 on success, -1 on a bad argument or out of memory.
  */
-int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
+static int gemm_fmt(int fmt, const uint16_t *A, const uint16_t *B, uint16_t *D,
                     int64_t M, int64_t N, int64_t K,
                     const int64_t *rows, int64_t nrows, int nthreads)
 {
@@ -137,7 +213,7 @@ int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
         if (rows[r] < 0 || rows[r] >= M) return -1;
     if (nrows == 0 || N == 0) return 0;
 
-    double *Bd = decode_matrix(B, N * K);
+    double *Bd = decode_matrix(fmt, B, N * K);
     if (!Bd) return -1;
     int status = 0;
 
@@ -158,12 +234,12 @@ int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
         for (int64_t r = 0; r < nrows; ++r) {
             if (!arow) continue;
             const int64_t m = rows ? rows[r] : r;
-            for (int64_t k = 0; k < K; ++k) arow[k] = oracle_f16_to_f64(A[m * K + k]);
+            for (int64_t k = 0; k < K; ++k) arow[k] = decode(fmt, A[m * K + k]);
             for (int64_t n = 0; n < N; ++n) {
                 const double *brow = Bd + n * K;
                 double sum = 0.0;
                 for (int64_t k = 0; k < K; ++k) sum += arow[k] * brow[k];
-                D[r * N + n] = oracle_f64_to_f16_rne(sum);
+                D[r * N + n] = encode(fmt, sum);
             }
         }
         free(arow);
@@ -172,16 +248,30 @@ int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
     return status;
 }
 
+int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
+                    int64_t M, int64_t N, int64_t K,
+                    const int64_t *rows, int64_t nrows, int nthreads)
+{
+    return gemm_fmt(0, A, B, D, M, N, K, rows, nrows, nthreads);
+}
+
+int oracle_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *D,
+                     int64_t M, int64_t N, int64_t K,
+                     const int64_t *rows, int64_t nrows, int nthreads)
+{
+    return gemm_fmt(1, A, B, D, M, N, K, rows, nrows, nthreads);
+}
+
 /*
- * GEMV y = x . W^T.
- *   x [K], W [N,K] row-major, y [N]; fp16 bits.
+ * GEMV y = x . W^T, elements in format fmt.
+ *   x [K], W [N,K] row-major, y [N]; bits.
  */
-int oracle_gemv_f16(const uint16_t *x, const uint16_t *W, uint16_t *y,
+static int gemv_fmt(int fmt, const uint16_t *x, const uint16_t *W, uint16_t *y,
                     int64_t N, int64_t K, int nthreads)
 {
     if (N < 0 || K < 0) return -1;
     if (N == 0) return 0;
-    double *xd = decode_matrix(x, K);
+    double *xd = decode_matrix(fmt, x, K);
     if (!xd) return -1;
 
 #ifdef _OPENMP
@@ -193,11 +283,23 @@ int oracle_gemv_f16(const uint16_t *x, const uint16_t *W, uint16_t *y,
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         double sum = 0.0;
-        for (int64_t k = 0; k < K; ++k) sum += xd[k] * oracle_f16_to_f64(W[n * K + k]);
-        y[n] = oracle_f64_to_f16_rne(sum);
+        for (int64_t k = 0; k < K; ++k) sum += xd[k] * decode(fmt, W[n * K + k]);
+        y[n] = encode(fmt, sum);
     }
     free(xd);
     return 0;
+}
+
+int oracle_gemv_f16(const uint16_t *x, const uint16_t *W, uint16_t *y,
+                    int64_t N, int64_t K, int nthreads)
+{
+    return gemv_fmt(0, x, W, y, N, K, nthreads);
+}
+
+int oracle_gemv_bf16(const uint16_t *x, const uint16_t *W, uint16_t *y,
+                     int64_t N, int64_t K, int nthreads)
+{
+    return gemv_fmt(1, x, W, y, N, K, nthreads);
 }
 
 /* Threads OpenMP will use by default (for reporting). */

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 import test_oracle
+import test_oracle_bf16
 
 MUTANTS = {
     "drop_last_k_term": ("for (int64_t k = 0; k < K; ++k) sum += arow[k] * brow[k];",
@@ -24,11 +25,22 @@ MUTANTS = {
     "ties_away_from_zero": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
     "subnormal_scale": ("mag = ldexp((double)frac, -24);", "mag = ldexp((double)frac, -25);"),
     "exponent_bias": ("mag = ldexp((double)(1024 + frac), exp - 25);", "mag = ldexp((double)(1024 + frac), exp - 24);"),
-    "gemv_transposed_w": ("sum += xd[k] * oracle_f16_to_f64(W[n * K + k]);",
-                          "sum += xd[k] * oracle_f16_to_f64(W[(k * N + n) % (N * K)]);"),
+    "gemv_transposed_w": ("sum += xd[k] * decode(fmt, W[n * K + k]);",
+                          "sum += xd[k] * decode(fmt, W[(k * N + n) % (N * K)]);"),
     "gemv_drop_first": ("for (int64_t k = 0; k < K; ++k) sum += xd[k]", "for (int64_t k = 1; k < K; ++k) sum += xd[k]"),
     "overflow_threshold": ("if (a >= 65520.0) return (uint16_t)(sign | 0x7c00);",
                            "if (a >= 65504.0) return (uint16_t)(sign | 0x7c00);"),
+    # bf16
+    "bf16_exponent_bias": ("mag = ldexp((double)(128 + frac), exp - 134);", "mag = ldexp((double)(128 + frac), exp - 133);"),
+    "bf16_subnormal_scale": ("mag = ldexp((double)frac, -133);", "mag = ldexp((double)frac, -134);"),
+    "bf16_round_toward_zero": ("double q = round_half_even(ldexp(a, 7 - E));", "double q = floor(ldexp(a, 7 - E));"),
+    "bf16_overflow_threshold": ("if (a >= ldexp(2.0 - ldexp(1.0, -8), 127)) return (uint16_t)(sign | 0x7f80);",
+                                "if (a >= ldexp(2.0 - ldexp(1.0, -7), 127)) return (uint16_t)(sign | 0x7f80);"),
+    "bf16_subnormal_encode": ("double q = round_half_even(ldexp(a, 133));", "double q = round_half_even(ldexp(a, 132));"),
+    "bf16_decoded_as_fp16": ("return fmt ? oracle_bf16_to_f64(bits) : oracle_f16_to_f64(bits);",
+                             "return oracle_f16_to_f64(bits);"),
+    "bf16_encoded_as_fp16": ("return fmt ? oracle_f64_to_bf16_rne(v) : oracle_f64_to_f16_rne(v);",
+                             "return oracle_f64_to_f16_rne(v);"),
 }
 
 
@@ -52,7 +64,7 @@ def test_mutant_is_caught(name, mutant_dir):
     oracle.compile_oracle(source=path, output=lib_path)
     lib = oracle.load(lib_path)
     caught = []
-    for check in test_oracle.ALL_CHECKS:
+    for check in test_oracle.ALL_CHECKS + test_oracle_bf16.ALL_CHECKS:
         try:
             check(lib)
         except (AssertionError, ValueError, IndexError):
