@@ -12,6 +12,9 @@ Prints ONE JSON line on stdout:
   gemv         GEMV GB/s (algorithmic bytes 2·(N·K + K + N) / mean kernel time,
                the five back-to-back launches of a step timed together)
                with its own roofline against the HBM peak
+  decode_batch the 8x4096x14336 GEMM (skinny path) in GB/s, timed on its own
+  bf16         gemm_bf16 at 4096^3 and gemv_bf16 at 4096x14336, bf16 inputs of
+               the same shapes, timed on their own after the decode batch
   cpu_baseline the CPU oracle (FP64, OpenMP) on a bounded sample of rows of
                the same GEMM, scaled to TFLOP/s, plus the full GEMV in GB/s
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 20]
@@ -33,6 +36,7 @@ GEMM_M = GEMM_N = GEMM_K = 4096
 GEMV_N, GEMV_K = 4096, 14336
 GEMM_SETS = 3
 DECODE_REPS = 20  # event pairs around 5 decode-batch launches, after the timed steps
+BF16_REPS = 20  # event triples around one gemm_bf16 and 5 gemv_bf16, after the decode batch
 GEMV_COPIES = 5
 # Beyond-L2 traffic per launch measured with rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch, each scaled by what the same counter reads for
@@ -235,6 +239,44 @@ def main():
     decode_bytes = metrics.gemm_bytes(wd.M, wd.N, wd.K)
     decode_gbps = decode_bytes / decode_s / 1e9
 
+    # ---- bf16: the same GEMM and GEMV shapes on bf16 inputs -----------------
+    # numpy has no bfloat16: datagen returns bf16 bit patterns, viewed as such.
+    def bf16_tensor(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Ab0, Bb0 = datagen.gemm_inputs(wg, bf16=True)
+    Ab, Bb = bf16_tensor(Ab0), bf16_tensor(Bb0)
+    Db = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    xb0, Wb0 = datagen.gemv_inputs(wv, bf16=True)
+    xb, Wb = bf16_tensor(xb0), bf16_tensor(Wb0)
+    gemv_b = [(Wb if c == 0 else Wb.clone(), torch.empty((wv.N,), dtype=torch.bfloat16, device=dev)) for c in range(GEMV_COPIES)]
+
+    def bf16_step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        st = gt.gemm_bf16_ptr(Ab.data_ptr(), Bb.data_ptr(), Db.data_ptr(), M, N, K, sh)
+        if ev:
+            ev[1].record(stream)
+        for W, y in gemv_b:
+            st |= gt.gemv_bf16_ptr(xb.data_ptr(), W.data_ptr(), y.data_ptr(), wv.N, wv.K, sh)
+        if ev:
+            ev[2].record(stream)
+        if st:
+            raise RuntimeError(f"library call failed: {gt.status_string(st)}")
+
+    for _ in range(5):
+        bf16_step()
+    bf_events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(BF16_REPS)]
+    torch.cuda.synchronize(dev)
+    for e in bf_events:
+        bf16_step(e)
+    torch.cuda.synchronize(dev)
+    gemm_bf16_s = float(np.mean([e[0].elapsed_time(e[1]) for e in bf_events])) / 1e3
+    gemv_bf16_s = float(np.mean([e[1].elapsed_time(e[2]) for e in bf_events])) / 1e3 / GEMV_COPIES
+    gemm_bf16_tflops = flops / gemm_bf16_s / 1e12
+    gemv_bf16_gbps = gemv_bytes / gemv_bf16_s / 1e9
+    del gemv_b, Wb, Ab, Bb, Db
+
     cpu = cpu_baseline(args.cpu_seconds)
 
     def traffic(kind):
@@ -275,7 +317,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / metrics.PEAK_FP16_MFMA_TFLOPS, 4),
             "traffic": traffic("gemm"),
-            "kernel": "gemm_f16_kernel",
+            "kernel": "gemm_kernel",
             "us_per_launch": round(gemm_s * 1e6, 2),
         },
         "gemv": {
@@ -289,7 +331,7 @@ def main():
                 "unit": "GB/s",
                 "frac": round(gemv_gbps / metrics.PEAK_HBM_GBPS, 4),
                 "traffic": traffic("gemv"),
-                "kernel": "gemv_f16_kernel",
+                "kernel": "gemv_kernel",
             },
         },
         "decode_batch": {
@@ -307,6 +349,17 @@ def main():
                 "traffic": traffic("decode"),
                 "kernel": "gemm_skinny_lds_kernel",
             },
+        },
+        "bf16": {
+            "workload": f"gemm_bf16 {M}x{N}x{K} and gemv_bf16 {wv.N}x{wv.K} (5 distinct W), "
+            "bf16 in/out, fp32 accumulate",
+            "gemm_tflops": round(gemm_bf16_tflops, 2),
+            "gemm_us_per_launch": round(gemm_bf16_s * 1e6, 2),
+            "gemm_frac": round(gemm_bf16_tflops / metrics.PEAK_BF16_MFMA_TFLOPS, 4),
+            "gemm_peak": metrics.PEAK_BF16_MFMA_TFLOPS,
+            "gemv_gbps": round(gemv_bf16_gbps, 1),
+            "gemv_us_per_launch": round(gemv_bf16_s * 1e6, 2),
+            "gemv_frac": round(gemv_bf16_gbps / metrics.PEAK_HBM_GBPS, 4),
         },
         "cpu_baseline": cpu,
         "context": "pages' figures (other hardware, BF16 GEMM): 36.13 TFLOP/s at 4096^3 on an SM120 GeForce; "

@@ -110,25 +110,28 @@ def sample_rows(cfg_id: int, M: int, count: int) -> np.ndarray:
     return np.sort(g.choice(M, size=min(count, M), replace=False)).astype(np.int64)
 
 
-def gemm_inputs(w: Workload, integer: bool = False):
-    """(A, B) for a GEMM workload, each a C-contiguous float16 array."""
+def gemm_inputs(w: Workload, integer: bool = False, bf16: bool = False):
+    """(A, B) for a GEMM workload, each C-contiguous: float16 arrays, or bf16
+    bit patterns (uint16) when `bf16` is set."""
     assert w.kind == "gemm"
+    uni, intg = (uniform_bf16, integer_bf16) if bf16 else (uniform_f16, integer_f16)
     if integer:
         # Separate tensor ids (10, 11) so the integer draw never aliases the
         # uniform one.
-        return (integer_f16(w.cfg_id, 10, (w.M, w.K)), integer_f16(w.cfg_id, 11, (w.N, w.K)))
+        return (intg(w.cfg_id, 10, (w.M, w.K)), intg(w.cfg_id, 11, (w.N, w.K)))
     return (
-        uniform_f16(w.cfg_id, 0, (w.M, w.K), w.lo_a, w.hi_a),
-        uniform_f16(w.cfg_id, 1, (w.N, w.K), w.lo_b, w.hi_b),
+        uni(w.cfg_id, 0, (w.M, w.K), w.lo_a, w.hi_a),
+        uni(w.cfg_id, 1, (w.N, w.K), w.lo_b, w.hi_b),
     )
 
 
-def gemv_inputs(w: Workload, integer: bool = False):
-    """(x, W) for a GEMV workload."""
+def gemv_inputs(w: Workload, integer: bool = False, bf16: bool = False):
+    """(x, W) for a GEMV workload (float16, or bf16 bit patterns when `bf16`)."""
     assert w.kind == "gemv"
+    uni, intg = (uniform_bf16, integer_bf16) if bf16 else (uniform_f16, integer_f16)
     if integer:
-        return (integer_f16(w.cfg_id, 10, (w.K,)), integer_f16(w.cfg_id, 11, (w.N, w.K)))
+        return (intg(w.cfg_id, 10, (w.K,)), intg(w.cfg_id, 11, (w.N, w.K)))
     return (
-        uniform_f16(w.cfg_id, 0, (w.K,), w.lo_a, w.hi_a),
-        uniform_f16(w.cfg_id, 1, (w.N, w.K), w.lo_b, w.hi_b),
+        uni(w.cfg_id, 0, (w.K,), w.lo_a, w.hi_a),
+        uni(w.cfg_id, 1, (w.N, w.K), w.lo_b, w.hi_b),
     )

@@ -25,6 +25,10 @@ __all__ = [
     "gemv_f16",
     "gemm_f16_ptr",
     "gemv_f16_ptr",
+    "gemm_bf16",
+    "gemv_bf16",
+    "gemm_bf16_ptr",
+    "gemv_bf16_ptr",
     "gemm_f16_variant",
     "gemv_f16_variant",
     "status_string",
@@ -40,6 +44,8 @@ LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemv
 EXPORTED_SYMBOLS = (
     "gemm_f16",
     "gemv_f16",
+    "gemm_bf16",
+    "gemv_bf16",
     "gemvtile_status_string",
     "gemvtile_tile_coord",
     "gemvtile_gemm_config",
@@ -88,6 +94,10 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemm_f16.restype = c_int
     lib.gemv_f16.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.gemv_f16.restype = c_int
+    lib.gemm_bf16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.gemm_bf16.restype = c_int
+    lib.gemv_bf16.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.gemv_bf16.restype = c_int
     lib.gemvtile_gemm_f16_variant.argtypes = [vp, vp, vp, i64, i64, i64, vp, c_int]
     lib.gemvtile_gemm_f16_variant.restype = c_int
     lib.gemvtile_gemv_f16_variant.argtypes = [vp, vp, vp, i64, i64, vp, c_int]
@@ -127,6 +137,16 @@ def gemv_f16_ptr(x: int, W: int, y: int, N: int, K: int, stream: int = 0) -> int
     return int(load_library().gemv_f16(x, W, y, N, K, stream))
 
 
+def gemm_bf16_ptr(A: int, B: int, D: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    """Call gemm_bf16 with raw device pointers; returns the status code."""
+    return int(load_library().gemm_bf16(A, B, D, M, N, K, stream))
+
+
+def gemv_bf16_ptr(x: int, W: int, y: int, N: int, K: int, stream: int = 0) -> int:
+    """Call gemv_bf16 with raw device pointers; returns the status code."""
+    return int(load_library().gemv_bf16(x, W, y, N, K, stream))
+
+
 # ---- tensor entry points ---------------------------------------------------
 def _torch():
     import torch
@@ -134,12 +154,13 @@ def _torch():
     return torch
 
 
-def _require(t, name, ndim):
+def _require(t, name, ndim, dtype=None):
     torch = _torch()
+    dtype = torch.float16 if dtype is None else dtype
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.float16:
-        raise TypeError(f"{name} must be float16, got {t.dtype}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if t.dim() != ndim:
@@ -157,14 +178,10 @@ def _stream_handle(t, stream):
     return stream.cuda_stream
 
 
-def gemm_f16(A, B, D=None, stream=None, variant: int = 0):
-    """D = A · Bᵀ on the device.  A [M,K], B [N,K], D [M,N] fp16 contiguous.
-
-    Enqueued on `stream` (default: the current stream) and not synchronised.
-    """
+def _gemm(A, B, D, stream, dtype, call):
     torch = _torch()
-    _require(A, "A", 2)
-    _require(B, "B", 2)
+    _require(A, "A", 2, dtype)
+    _require(B, "B", 2, dtype)
     M, K = A.shape
     N, K2 = B.shape
     if K != K2:
@@ -172,45 +189,76 @@ def gemm_f16(A, B, D=None, stream=None, variant: int = 0):
     if B.device != A.device:
         raise ValueError("A and B must be on the same device")
     if D is None:
-        D = torch.empty((M, N), dtype=torch.float16, device=A.device)
+        D = torch.empty((M, N), dtype=dtype, device=A.device)
     else:
-        _require(D, "D", 2)
+        _require(D, "D", 2, dtype)
         if tuple(D.shape) != (M, N) or D.device != A.device:
             raise ValueError(f"D must be [{M},{N}] on {A.device}, got {tuple(D.shape)} on {D.device}")
     s = _stream_handle(A, stream)
     with torch.cuda.device(A.device):
-        if variant == 0:
-            st = load_library().gemm_f16(A.data_ptr(), B.data_ptr(), D.data_ptr(), M, N, K, s)
-        else:
-            st = load_library().gemvtile_gemm_f16_variant(A.data_ptr(), B.data_ptr(), D.data_ptr(), M, N, K, s, variant)
+        st = call(A.data_ptr(), B.data_ptr(), D.data_ptr(), M, N, K, s)
     _check(st)
     return D
 
 
-def gemv_f16(x, W, y=None, stream=None, variant: int = 0):
-    """y = x · Wᵀ on the device.  x [K], W [N,K], y [N] fp16 contiguous."""
+def gemm_f16(A, B, D=None, stream=None, variant: int = 0):
+    """D = A · Bᵀ on the device.  A [M,K], B [N,K], D [M,N] fp16 contiguous.
+
+    Enqueued on `stream` (default: the current stream) and not synchronised.
+    """
+    lib = load_library()
+    if variant == 0:
+        call = lib.gemm_f16
+    else:
+        def call(*args):
+            return lib.gemvtile_gemm_f16_variant(*args, variant)
+    return _gemm(A, B, D, stream, _torch().float16, call)
+
+
+def gemm_bf16(A, B, D=None, stream=None):
+    """D = A · Bᵀ on the device.  A [M,K], B [N,K], D [M,N] bfloat16 contiguous.
+
+    Enqueued on `stream` (default: the current stream) and not synchronised.
+    """
+    return _gemm(A, B, D, stream, _torch().bfloat16, load_library().gemm_bf16)
+
+
+def _gemv(x, W, y, stream, dtype, call):
     torch = _torch()
-    _require(x, "x", 1)
-    _require(W, "W", 2)
+    _require(x, "x", 1, dtype)
+    _require(W, "W", 2, dtype)
     N, K = W.shape
     if x.shape[0] != K:
         raise ValueError(f"K mismatch: x is {tuple(x.shape)}, W is {tuple(W.shape)}")
     if W.device != x.device:
         raise ValueError("x and W must be on the same device")
     if y is None:
-        y = torch.empty((N,), dtype=torch.float16, device=x.device)
+        y = torch.empty((N,), dtype=dtype, device=x.device)
     else:
-        _require(y, "y", 1)
+        _require(y, "y", 1, dtype)
         if y.shape[0] != N or y.device != x.device:
             raise ValueError(f"y must be [{N}] on {x.device}")
     s = _stream_handle(x, stream)
     with torch.cuda.device(x.device):
-        if variant == 0:
-            st = load_library().gemv_f16(x.data_ptr(), W.data_ptr(), y.data_ptr(), N, K, s)
-        else:
-            st = load_library().gemvtile_gemv_f16_variant(x.data_ptr(), W.data_ptr(), y.data_ptr(), N, K, s, variant)
+        st = call(x.data_ptr(), W.data_ptr(), y.data_ptr(), N, K, s)
     _check(st)
     return y
+
+
+def gemv_f16(x, W, y=None, stream=None, variant: int = 0):
+    """y = x · Wᵀ on the device.  x [K], W [N,K], y [N] fp16 contiguous."""
+    lib = load_library()
+    if variant == 0:
+        call = lib.gemv_f16
+    else:
+        def call(*args):
+            return lib.gemvtile_gemv_f16_variant(*args, variant)
+    return _gemv(x, W, y, stream, _torch().float16, call)
+
+
+def gemv_bf16(x, W, y=None, stream=None):
+    """y = x · Wᵀ on the device.  x [K], W [N,K], y [N] bfloat16 contiguous."""
+    return _gemv(x, W, y, stream, _torch().bfloat16, load_library().gemv_bf16)
 
 
 def gemm_f16_variant(A, B, variant: int, D=None, stream=None):

@@ -82,12 +82,27 @@ int check_gemv(const void *x, const void *W, const void *y, int64_t N, int64_t K
 
 int to_status(hipError_t e) { return e == hipSuccess ? GEMVTILE_OK : GEMVTILE_ERR_LAUNCH; }
 
-int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream, int variant) {
+// dtype: gt::kF16 or gt::kBF16.  bf16 runs the default kernels only
+// (variant 0).
+int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream, int variant,
+             int dtype = gt::kF16) {
   bool noop = false;
   int st = check_gemm(A, B, D, M, N, K, &noop);
   if (st != GEMVTILE_OK || noop) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // +0 is the all-zero pattern in both formats.
   if (K == 0) return to_status(gt::launch_fill_zero_f16(D, M * N, s));
+  if (dtype == gt::kBF16) {
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    if (M == 1 || N == 1)
+      return to_status(gt::launch_gemv_bf16(M == 1 ? A : B, M == 1 ? B : A, D, M == 1 ? n : m, k, s));
+    if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows)
+      return to_status(gt::launch_gemm_skinny_bf16(A, B, D, m, n, k, s));
+    int cus = 0;
+    st = current_cu_count(&cus);
+    if (st != GEMVTILE_OK) return st;
+    return to_status(gt::launch_gemm_bf16(A, B, D, m, n, k, cus, s));
+  }
   const bool skinny = M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows;
   // Variant 0 (gemm_f16) sends shapes with at most 16 rows on one side to
   // the skinny kernel; variants kGemmVariants.. force skinny launch shapes.
@@ -117,12 +132,14 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
                                        static_cast<int>(K), cus, s));
 }
 
-int run_gemv(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream, int variant) {
+int run_gemv(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream, int variant,
+             int dtype = gt::kF16) {
   bool noop = false;
   int st = check_gemv(x, W, y, N, K, &noop);
   if (st != GEMVTILE_OK || noop) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K == 0) return to_status(gt::launch_fill_zero_f16(y, N, s));
+  if (dtype == gt::kBF16) return to_status(gt::launch_gemv_bf16(x, W, y, static_cast<int>(N), static_cast<int>(K), s));
   return to_status(gt::launch_gemv_f16(variant, x, W, y, static_cast<int>(N), static_cast<int>(K), s));
 }
 
@@ -136,6 +153,14 @@ int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
 
 int gemv_f16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream) {
   return run_gemv(x, W, y, N, K, stream, 0);
+}
+
+int gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream) {
+  return run_gemm(A, B, D, M, N, K, stream, 0, gt::kBF16);
+}
+
+int gemv_bf16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream) {
+  return run_gemv(x, W, y, N, K, stream, 0, gt::kBF16);
 }
 
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream,

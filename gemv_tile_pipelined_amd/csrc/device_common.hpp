@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"
+
 namespace gt {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -12,6 +14,20 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// The kernels move 16-bit patterns and carry them in _Float16 containers
+// whatever the element format (kF16 / kBF16, kernels.hpp); only the
+// arithmetic (MFMA, dot) and the final rounding depend on it.
+
+// FP32 -> the 16-bit output format, round to nearest even (v_cvt_f16_f32 /
+// v_cvt_pk_bf16_f32), returned as a 16-bit pattern in a _Float16 container.
+template <int DT>
+__device__ inline _Float16 round_out(float x) {
+  if constexpr (DT == kF16) return static_cast<_Float16>(x);
+  else return __builtin_bit_cast(_Float16, static_cast<__bf16>(x));
+}
 
 #define GT_LDS __attribute__((address_space(3)))
 

@@ -1,8 +1,10 @@
-// gemm.hip -- persistent, pipelined FP16 GEMM for gfx950: D = A · Bᵀ.
+// gemm.hip -- persistent, pipelined FP16 / BF16 GEMM for gfx950: D = A · Bᵀ.
 //
-//   A [M,K], B [N,K] row-major (K-contiguous) fp16; D [M,N] row-major fp16;
-//   FP32 accumulation in the matrix cores, one round-to-nearest-even per
-//   output.  The operation and layout are those of the TVM TIRx GEMM chapter
+//   A [M,K], B [N,K] row-major (K-contiguous) fp16 or bf16; D [M,N]
+//   row-major in the same format; FP32 accumulation in the matrix cores, one
+//   round-to-nearest-even per output (bf16 in and out is the SM120 page's
+//   own kernel: nv_bfloat16 operands at §2.2 entrance, _rn rounding of the
+//   FP32 accumulators in the §2.3 kernel).  The operation and layout are those of the TVM TIRx GEMM chapter
 //   ("使用 TMA 为 GEMM 建立 Pipeline", step 4 full kernel) and of the SM120
 //   walk-through "TensorCore_GEMM_with_TMA" (§2.2 entrance, §2.3 kernel).
 //
@@ -66,7 +68,7 @@ namespace gt {
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, bool SWIZZLE_, bool PERSISTENT_,
           int DMA_STRIDE_, int DMA_PHASES_, int K_STAGGER_ = 1, int K_STAGGER_STEP_ = 1, int LOAD_POLICY_ = 0,
-          int MI_ = 32, int READ_STRIDE_ = 1, int DMA_OFFSET_ = 0, bool FUSE_DMA_ = false>
+          int MI_ = 32, int READ_STRIDE_ = 1, int DMA_OFFSET_ = 0, bool FUSE_DMA_ = false, int DTYPE_ = kF16>
 struct GemmShape {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -104,6 +106,10 @@ struct GemmShape {
   // With 16x16x32 MFMAs: issue each tile load in one asm block with the MFMA
   // of its slot (see mfma_dma in the kernel).
   static constexpr bool FUSE_DMA = FUSE_DMA_;
+  // Element format of A, B and D (kF16 or kBF16; bf16 only with the
+  // hand-written 16x16x32 MFMAs).
+  static constexpr int DTYPE = DTYPE_;
+  static_assert(DTYPE == kF16 || (DTYPE == kBF16 && MI_ == 16), "bf16 uses the 16x16x32 MFMA path");
   static_assert((BK / kKStep) >= 1 && (BM / WAVES_M / MI) * (BN / WAVES_N / MI) % READ_STRIDE == 0,
                 "the read spacing must divide the MFMA slots of a K step");
 
@@ -182,7 +188,7 @@ __device__ inline void wait_tile_landed(int younger) {
 
 template <class S>
 __global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
+gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
                 int M, int N, int K, int tiles_m, int tiles_n, int vec16) {
   __shared__ __attribute__((aligned(1024))) char smem[S::kLdsBytes];
 
@@ -348,9 +354,14 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
         // accumulators around the K loop and copies them back on every
         // iteration.  The compiler does not see this as an MFMA, so the read
         // of the accumulators after the K loop is padded by hand (mfma_drain).
-        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
-                     : "+a"(acc[i][j])
-                     : "v"(fb[buf][j]), "v"(fa[buf][i]));
+        if constexpr (S::DTYPE == kF16)
+          asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                       : "+a"(acc[i][j])
+                       : "v"(fb[buf][j]), "v"(fa[buf][i]));
+        else
+          asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                       : "+a"(acc[i][j])
+                       : "v"(fb[buf][j]), "v"(fa[buf][i]));
       }
     };
     // A 16x16x32 MFMA together with one tile load, in one asm block: M0 (the
@@ -360,7 +371,8 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
     // and delay the next MFMA.  Fusing removes most of that delay (about 7K
     // cycles per wave at 4096^3), but the chip is power-limited and its clock
     // drops by more: the default issues the loads separately.
-    constexpr bool kFusedDma = S::FUSE_DMA && S::MI == 16 && S::DMA_PHASES == 1 && S::LOAD_POLICY == 0;
+    constexpr bool kFusedDma =
+        S::FUSE_DMA && S::MI == 16 && S::DMA_PHASES == 1 && S::LOAD_POLICY == 0 && S::DTYPE == kF16;
     auto mfma_dma = [&](int buf, int idx, const DmaArgs &g) {
       const int i = idx / S::kFragN;
       const int j = idx % S::kFragN;
@@ -556,7 +568,7 @@ gemm_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, 
           for (int g = 0; g < S::kAccRegs / 4; ++g) {
             half4_t h;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = static_cast<_Float16>(acc[i][j][4 * g + e]);
+            for (int e = 0; e < 4; ++e) h[e] = round_out<S::DTYPE>(acc[i][j][4 * g + e]);
             // Column of this lane's 4 values inside the wave tile.
             const int col = S::MI == 32 ? j * 32 + g * 8 + frag_kgrp * 4 : j * 16 + frag_kgrp * 4;
             const uint32_t off =
@@ -614,6 +626,8 @@ using GemmLoadsSc0 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 1,
 // accumulators stay in place), and with K tiles of 32 in a 4-stage ring.
 using GemmFusedLoads = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, true>;
 using Gemm32x32 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1>;
+// The default shape with bf16 operands and results.
+using GemmBf16 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, kBF16>;
 using Gemm32x32OneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true, 1, 1>;
 using Gemm32x32Bk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
 
@@ -630,7 +644,7 @@ static hipError_t launch(const void *A, const void *B, void *D, int M, int N, in
   const int64_t grid = S::PERSISTENT ? (tiles < num_cus ? tiles : num_cus) : tiles;
   // Whole 16-byte row segments of D are 16-byte aligned when N % 8 == 0.
   const int vec16 = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(D) % 16 == 0);
-  hipLaunchKernelGGL(gemm_f16_kernel<S>, dim3(static_cast<unsigned>(grid)), dim3(S::kThreads), 0, stream,
+  hipLaunchKernelGGL(gemm_kernel<S>, dim3(static_cast<unsigned>(grid)), dim3(S::kThreads), 0, stream,
                      static_cast<const _Float16 *>(A), static_cast<const _Float16 *>(B), static_cast<_Float16 *>(D),
                      M, N, K, tiles_m, tiles_n, vec16);
   return hipGetLastError();
@@ -654,6 +668,11 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 12: return launch<GemmFusedLoads>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
+                            hipStream_t stream) {
+  return launch<GemmBf16>(A, B, D, M, N, K, num_cus, stream);
 }
 
 }  // namespace gt

@@ -1,4 +1,4 @@
-// gemv.hip -- batch-1 FP16 GEMV for gfx950: y = x · Wᵀ.
+// gemv.hip -- batch-1 FP16 / BF16 GEMV for gfx950: y = x · Wᵀ.
 //
 //   x [K], W [N,K] row-major (nn.Linear layout), y [N]; fp16 in and out, FP32
 //   accumulation, one round-to-nearest-even per output ("Learning TileLang
@@ -35,11 +35,23 @@
 
 namespace gt {
 
+// acc + a · b over 8 elements, products and sums in FP32 (v_dot2_f32_f16 or
+// v_dot2_f32_bf16 on pairs).
+template <int DT>
 __device__ inline float dot8_acc(half8_t a, half8_t b, float acc) {
-  acc = __builtin_amdgcn_fdot2(half2_t{a[0], a[1]}, half2_t{b[0], b[1]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(half2_t{a[2], a[3]}, half2_t{b[2], b[3]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(half2_t{a[4], a[5]}, half2_t{b[4], b[5]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(half2_t{a[6], a[7]}, half2_t{b[6], b[7]}, acc, false);
+  if constexpr (DT == kF16) {
+    acc = __builtin_amdgcn_fdot2(half2_t{a[0], a[1]}, half2_t{b[0], b[1]}, acc, false);
+    acc = __builtin_amdgcn_fdot2(half2_t{a[2], a[3]}, half2_t{b[2], b[3]}, acc, false);
+    acc = __builtin_amdgcn_fdot2(half2_t{a[4], a[5]}, half2_t{b[4], b[5]}, acc, false);
+    acc = __builtin_amdgcn_fdot2(half2_t{a[6], a[7]}, half2_t{b[6], b[7]}, acc, false);
+  } else {
+    const bf16x8_t x = __builtin_bit_cast(bf16x8_t, a);
+    const bf16x8_t w = __builtin_bit_cast(bf16x8_t, b);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{x[0], x[1]}, bf16x2_t{w[0], w[1]}, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{x[2], x[3]}, bf16x2_t{w[2], w[3]}, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{x[4], x[5]}, bf16x2_t{w[4], w[5]}, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{x[6], x[7]}, bf16x2_t{w[6], w[7]}, acc, false);
+  }
   return acc;
 }
 
@@ -69,7 +81,7 @@ __device__ inline float wave_sum(float v) {
 }
 
 // Reduce the ROWS partial sums of a wave and store row r's total from lane r.
-template <int ROWS>
+template <int ROWS, int DT>
 __device__ inline void store_row_sums(const float (&acc)[ROWS], int lane, int64_t row0, int N, _Float16 *y) {
   float sums[ROWS];
 #pragma unroll
@@ -77,12 +89,12 @@ __device__ inline void store_row_sums(const float (&acc)[ROWS], int lane, int64_
   float mine = sums[0];
 #pragma unroll
   for (int r = 1; r < ROWS; ++r) mine = (lane == r) ? sums[r] : mine;
-  if (lane < ROWS && row0 + lane < N) y[row0 + lane] = static_cast<_Float16>(mine);
+  if (lane < ROWS && row0 + lane < N) y[row0 + lane] = round_out<DT>(mine);
 }
 
-template <int ROWS, int WAVES, int UNROLL, bool NONTEMPORAL, bool ROTATE = false>
+template <int ROWS, int WAVES, int UNROLL, bool NONTEMPORAL, bool ROTATE = false, int DT = kF16>
 __global__ void __launch_bounds__(WAVES * 64)
-gemv_f16_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Float16 *__restrict__ y, int N,
+gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Float16 *__restrict__ y, int N,
                 int K) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -127,7 +139,7 @@ gemv_f16_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, 
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) acc[r] = dot8_acc(xs[u], ws[u][r], acc[r]);
+      for (int r = 0; r < ROWS; ++r) acc[r] = dot8_acc<DT>(xs[u], ws[u][r], acc[r]);
   };
 
   // With ROTATE, each wave starts its walk over the whole groups at a
@@ -141,14 +153,14 @@ gemv_f16_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, 
     if (++g == full) g = 0;
   }
   if (full * kGroup < chunks) group(full * kGroup, true);
-  store_row_sums<ROWS>(acc, lane, row0, N, y);
+  store_row_sums<ROWS, DT>(acc, lane, row0, N, y);
 }
 
-template <int ROWS, int WAVES, int UNROLL, bool NT, bool ROT = false>
+template <int ROWS, int WAVES, int UNROLL, bool NT, bool ROT = false, int DT = kF16>
 static hipError_t launch(const void *x, const void *W, void *y, int N, int K, hipStream_t stream) {
   const int64_t rows_per_block = static_cast<int64_t>(ROWS) * WAVES;
   const int64_t grid = (N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((gemv_f16_kernel<ROWS, WAVES, UNROLL, NT, ROT>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemv_kernel<ROWS, WAVES, UNROLL, NT, ROT, DT>), dim3(static_cast<unsigned>(grid)),
                      dim3(WAVES * 64), 0, stream, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(W),
                      static_cast<_Float16 *>(y), N, K);
   return hipGetLastError();
@@ -175,6 +187,10 @@ __global__ void fill_zero_f16_kernel(_Float16 *__restrict__ p, int64_t count) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride)
     p[i] = static_cast<_Float16>(0.0f);
+}
+
+hipError_t launch_gemv_bf16(const void *x, const void *W, void *y, int N, int K, hipStream_t stream) {
+  return launch<2, 8, 4, true, true, kBF16>(x, W, y, N, K, stream);
 }
 
 hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream) {

@@ -8,6 +8,10 @@
 
 namespace gt {
 
+// Element formats of operands and results.
+constexpr int kF16 = 0;   // IEEE binary16
+constexpr int kBF16 = 1;  // bfloat16 (1 sign, 8 exponent, 7 fraction bits)
+
 // Default GEMM kernel: 256x256 output tiles, K tiles of 64, a two-stage LDS
 // ring, 256 threads (4 waves), grouped tile order 8 tile rows high.
 constexpr int kGemmBM = 256;
@@ -36,5 +40,10 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
                                   hipStream_t stream);
 hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, hipStream_t stream);
 hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream);
+// bf16 operands and results: the default launch shape of each kernel.
+hipError_t launch_gemm_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
+                            hipStream_t stream);
+hipError_t launch_gemm_skinny_bf16(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t stream);
+hipError_t launch_gemv_bf16(const void *x, const void *W, void *y, int N, int K, hipStream_t stream);
 
 }  // namespace gt

@@ -1,4 +1,4 @@
-// skinny.hip -- FP16 GEMM with one side of at most 16 rows, for gfx950:
+// skinny.hip -- FP16 / BF16 GEMM with one side of at most 16 rows, for gfx950:
 // D = A · Bᵀ when M <= 16 (a decode batch of M activation rows against a
 // weight matrix B [N,K]) or when N <= 16.
 //
@@ -126,7 +126,7 @@ __device__ inline void wait_younger(int younger) {
 // make it so), and the four lane groups of a K step read chunks 0, 2, 1, 3
 // of the step: lanes l and l + 32, which the LDS serves together, then read
 // chunks an odd XOR apart and every read is bank-conflict free.
-template <int WAVES, int STAGES, int QROWS, bool TRANS>
+template <int WAVES, int STAGES, int QROWS, bool TRANS, int DT = kF16>
 __global__ void __launch_bounds__(WAVES * 64)
 gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ Q, _Float16 *__restrict__ D,
                        int R, int S, int K) {
@@ -197,7 +197,11 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
       const int c = step * 4 + kperm;  // logical chunk
       const half8_t pf = *reinterpret_cast<const half8_t *>(stage + frag_off + ((c ^ fswz) << 4));
       const half8_t qf = *reinterpret_cast<const half8_t *>(stage + qfrag_off + ((c ^ qswz) << 4));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, qf, acc, 0, 0, 0);
+      if constexpr (DT == kF16)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, qf, acc, 0, 0, 0);
+      else
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pf), __builtin_bit_cast(bf16x8_t, qf),
+                                                      acc, 0, 0, 0);
     }
   }
 
@@ -212,12 +216,12 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
     for (int w = 0; w < WAVES; ++w) sum += partial[w][s][r];
     if (s < S && r0 + r < R) {
       const int64_t idx = TRANS ? static_cast<int64_t>(r0 + r) * S + s : static_cast<int64_t>(s) * R + r0 + r;
-      D[idx] = static_cast<_Float16>(sum);
+      D[idx] = round_out<DT>(sum);
     }
   }
 }
 
-template <int WAVES, int STAGES, int QROWS>
+template <int WAVES, int STAGES, int QROWS, int DT = kF16>
 static hipError_t launch_lds(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                              hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((R + 15) / 16));
@@ -225,11 +229,11 @@ static hipError_t launch_lds(const void *P, const void *Q, void *D, int R, int S
   const auto *q = static_cast<const _Float16 *>(Q);
   auto *d = static_cast<_Float16 *>(D);
   if (trans)
-    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, true>), grid, dim3(WAVES * 64), 0, stream, p, q,
-                       d, R, S, K);
-  else
-    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, false>), grid, dim3(WAVES * 64), 0, stream, p,
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, true, DT>), grid, dim3(WAVES * 64), 0, stream, p,
                        q, d, R, S, K);
+  else
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, false, DT>), grid, dim3(WAVES * 64), 0, stream,
+                       p, q, d, R, S, K);
   return hipGetLastError();
 }
 
@@ -277,6 +281,13 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
     case 11: return S <= 8 ? launch_lds<4, 6, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_skinny_bf16(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t stream) {
+  const bool small_m = M <= kSkinnyMaxRows;
+  if (!small_m && N > kSkinnyMaxRows) return hipErrorInvalidValue;
+  return launch_lds<16, 4, 16, kBF16>(small_m ? B : A, small_m ? A : B, D, small_m ? N : M, small_m ? M : N, K,
+                                      !small_m, stream);
 }
 
 }  // namespace gt

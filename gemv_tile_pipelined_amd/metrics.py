@@ -12,6 +12,7 @@ FP16_BYTES = 2
 # MI355X published peaks (dense, no sparsity).
 PEAK_HBM_GBPS = 8000.0  # 8 TB/s HBM3E
 PEAK_FP16_MFMA_TFLOPS = 2500.0  # dense fp16 matrix-core peak (about 2.5 PFLOP/s)
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # dense bf16 matrix-core peak (same rate as fp16)
 NUM_CUS = 256
 ENGINE_CLOCK_GHZ = 2.4
 

@@ -1,9 +1,10 @@
 /*
- * gemvtile.h -- C ABI of the MI355X (gfx950) FP16 GEMM and GEMV library.
+ * gemvtile.h -- C ABI of the MI355X (gfx950) FP16 / BF16 GEMM and GEMV library.
  *
  * Every entry point takes plain pointers and sizes; no C++ or framework type
  * crosses this boundary.  All matrices are dense and row-major.  "fp16" means
- * IEEE 754 binary16.  Device pointers are HIP device (or managed) pointers on
+ * IEEE 754 binary16; "bf16" means bfloat16 (1 sign bit, 8 exponent bits with
+ * bias 127, 7 fraction bits: the upper half of a binary32).  Device pointers are HIP device (or managed) pointers on
  * the device that is current for the calling host thread.
  *
  * Ownership: the caller allocates and frees every buffer.  The library keeps
@@ -91,6 +92,24 @@ int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
  * Returns a gemvtile_status.
  */
 int gemv_f16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream);
+
+/*
+ * gemm_bf16 / gemv_bf16 -- gemm_f16 and gemv_f16 with bf16 operands and
+ * results: the same contract (layouts, sizes and their limits, alignment,
+ * degenerate shapes, streams, errors, determinism), FP32 accumulation, and
+ * one rounding of each output to bf16, round-to-nearest, ties to even.
+ *
+ *   D[m,n] = bf16_rne( sum_k A[m,k] * B[n,k] )     y[n] = bf16_rne( sum_k x[k] * W[n,k] )
+ *
+ * bf16 in and out with FP32 accumulators is the element type of the SM120
+ * walk-through "TensorCore_GEMM_with_TMA" (§2.2 entrance: nv_bfloat16 A, B,
+ * C; §2.3 kernel: FP32 accumulators rounded with __float22bfloat162_rn).
+ * Shapes route as for fp16 (M or N == 1: the GEMV kernel; M or N <= 16: the
+ * skinny kernel; otherwise the tiled kernel), each in its default launch
+ * shape.
+ */
+int gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream);
+int gemv_bf16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char *gemvtile_status_string(int status);
