@@ -44,10 +44,12 @@ GEMV_COPIES = 5
 # valid only for the kernel sources whose SHA-256 is recorded here; the
 # summary and commands are in profiles/traffic_fetch_write_size.md.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "8d9d61929c00acb48e1fff4a1164dc3f131713a591fab3c61bf80e8d556c0621",
-    "gemm": {"fetch_kib": 98436.0 * 2.0, "write_kib": 32768.0 * 1.0},
-    "gemv": {"fetch_kib": 57481.0 * 2.0, "write_kib": 8.0 * 1.0},
-    "decode": {"fetch_kib": 58260.5 * 2.0, "write_kib": 64.0 * 1.0},
+    "sources_sha256": "f0cd993b727eb0782c0e7bbc7bcb48ccc13e265bbfc3eabb48c30dcef6e313f8",
+    "gemm": {"fetch_kib": 98437.9 * 2.0, "write_kib": 32768.0 * 1.0},
+    "gemv": {"fetch_kib": 57479.1 * 2.0, "write_kib": 8.0 * 1.0},
+    "decode": {"fetch_kib": 58260.8 * 2.0, "write_kib": 64.0 * 1.0},
+    "gemm_bf16": {"fetch_kib": 98437.2 * 2.0, "write_kib": 32768.0 * 1.0},
+    "gemv_bf16": {"fetch_kib": 57481.2 * 2.0, "write_kib": 8.0 * 1.0},
 }
 KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemv.hip", "kernels.hpp", "skinny.hip", "tile_order.hpp")
 
@@ -360,6 +362,8 @@ def main():
             "gemv_gbps": round(gemv_bf16_gbps, 1),
             "gemv_us_per_launch": round(gemv_bf16_s * 1e6, 2),
             "gemv_frac": round(gemv_bf16_gbps / metrics.PEAK_HBM_GBPS, 4),
+            "gemm_traffic": traffic("gemm_bf16"),
+            "gemv_traffic": traffic("gemv_bf16"),
         },
         "cpu_baseline": cpu,
         "context": "pages' figures (other hardware, BF16 GEMM): 36.13 TFLOP/s at 4096^3 on an SM120 GeForce; "

@@ -5,6 +5,9 @@
     python -m gemv_tile_pipelined_amd.profile_driver decode [--variant V] [--shape M N K] [--iters I]
     python -m gemv_tile_pipelined_amd.profile_driver copy [--mib S] [--iters I]
 
+`--bf16` runs gemm_bf16 / gemv_bf16 on bf16 inputs of the same shapes instead
+(default kernels only).
+
 Meant to run under `rocprofv3 --pmc ...`: every dispatch of the chosen kernel
 then carries its counters.  `copy` runs a plain device-to-device copy of a
 known size, which calibrates byte counters (FETCH_SIZE, WRITE_SIZE) against
@@ -30,6 +33,7 @@ def main(argv=None):
     p.add_argument("--shape", type=int, nargs="+", default=None)
     p.add_argument("--iters", type=int, default=10)
     p.add_argument("--mib", type=int, default=512)
+    p.add_argument("--bf16", action="store_true")
     a = p.parse_args(argv)
 
     import torch
@@ -39,27 +43,43 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(1234)
+    dt = torch.bfloat16 if a.bf16 else torch.float16
+    if a.bf16 and a.variant != 0:
+        p.error("--bf16 runs the default kernels only")
+
+    def gemm(A, B, D):
+        if a.bf16:
+            gt.gemm_bf16(A, B, D)
+        else:
+            gt.gemm_f16(A, B, D, variant=a.variant)
+
+    def gemv(x, W, y):
+        if a.bf16:
+            gt.gemv_bf16(x, W, y)
+        else:
+            gt.gemv_f16(x, W, y, variant=a.variant)
+
     if a.kernel == "gemm":
         M, N, K = a.shape or (4096, 4096, 4096)
-        A = torch.empty((M, K), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)
-        B = torch.empty((N, K), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)
-        D = torch.empty((M, N), dtype=torch.float16, device=dev)
+        A = torch.empty((M, K), dtype=dt, device=dev).uniform_(-1, 1, generator=g)
+        B = torch.empty((N, K), dtype=dt, device=dev).uniform_(-1, 1, generator=g)
+        D = torch.empty((M, N), dtype=dt, device=dev)
         for _ in range(a.iters):
-            gt.gemm_f16(A, B, D, variant=a.variant)
+            gemm(A, B, D)
     elif a.kernel == "decode":
         M, N, K = a.shape or (8, 4096, 14336)
-        A = torch.empty((M, K), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)
-        Bs = [torch.empty((N, K), dtype=torch.float16, device=dev).uniform_(-0.05, 0.05, generator=g) for _ in range(5)]
-        D = torch.empty((M, N), dtype=torch.float16, device=dev)
+        A = torch.empty((M, K), dtype=dt, device=dev).uniform_(-1, 1, generator=g)
+        Bs = [torch.empty((N, K), dtype=dt, device=dev).uniform_(-0.05, 0.05, generator=g) for _ in range(5)]
+        D = torch.empty((M, N), dtype=dt, device=dev)
         for i in range(a.iters):
-            gt.gemm_f16(A, Bs[i % 5], D, variant=a.variant)
+            gemm(A, Bs[i % 5], D)
     elif a.kernel == "gemv":
         N, K = a.shape or (4096, 14336)
-        x = torch.empty((K,), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)
-        Ws = [torch.empty((N, K), dtype=torch.float16, device=dev).uniform_(-0.05, 0.05, generator=g) for _ in range(5)]
-        y = torch.empty((N,), dtype=torch.float16, device=dev)
+        x = torch.empty((K,), dtype=dt, device=dev).uniform_(-1, 1, generator=g)
+        Ws = [torch.empty((N, K), dtype=dt, device=dev).uniform_(-0.05, 0.05, generator=g) for _ in range(5)]
+        y = torch.empty((N,), dtype=dt, device=dev)
         for i in range(a.iters):
-            gt.gemv_f16(x, Ws[i % 5], y, variant=a.variant)
+            gemv(x, Ws[i % 5], y)
     else:
         n = a.mib * 1024 * 1024 // 2
         src = torch.empty((n,), dtype=torch.float16, device=dev).uniform_(-1, 1, generator=g)
