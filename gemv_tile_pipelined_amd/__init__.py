@@ -36,6 +36,7 @@ __all__ = [
     "xcd_logical_id",
     "gemm_config",
     "gemm_grid",
+    "gemv_grid",
 ]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemvtile.so")
@@ -50,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "gemvtile_tile_coord",
     "gemvtile_gemm_config",
     "gemvtile_gemm_grid",
+    "gemvtile_gemv_grid",
     "gemvtile_gemm_f16_variant",
     "gemvtile_gemv_f16_variant",
     "gemvtile_xcd_logical_id",
@@ -112,6 +114,8 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemvtile_gemm_config.restype = None
     lib.gemvtile_gemm_grid.argtypes = [i64, i64, i64]
     lib.gemvtile_gemm_grid.restype = i64
+    lib.gemvtile_gemv_grid.argtypes = [i64, i64]
+    lib.gemvtile_gemv_grid.restype = i64
     if path == LIBRARY_PATH:
         _lib = lib
     return lib
@@ -291,3 +295,7 @@ def gemm_config() -> dict:
 
 def gemm_grid(M: int, N: int, num_cus: int) -> int:
     return int(load_library().gemvtile_gemm_grid(M, N, num_cus))
+
+
+def gemv_grid(N: int, num_cus: int) -> int:
+    return int(load_library().gemvtile_gemv_grid(N, num_cus))

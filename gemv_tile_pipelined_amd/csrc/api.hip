@@ -92,44 +92,34 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   // +0 is the all-zero pattern in both formats.
   if (K == 0) return to_status(gt::launch_fill_zero_f16(D, M * N, s));
-  if (dtype == gt::kBF16) {
-    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    if (M == 1 || N == 1)
-      return to_status(gt::launch_gemv_bf16(M == 1 ? A : B, M == 1 ? B : A, D, M == 1 ? n : m, k, s));
-    if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows)
-      return to_status(gt::launch_gemm_skinny_bf16(A, B, D, m, n, k, s));
-    int cus = 0;
-    st = current_cu_count(&cus);
-    if (st != GEMVTILE_OK) return st;
-    return to_status(gt::launch_gemm_bf16(A, B, D, m, n, k, cus, s));
-  }
   const bool skinny = M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows;
-  // Variant 0 (gemm_f16) sends shapes with at most 16 rows on one side to
-  // the skinny kernel; variants kGemmVariants.. force skinny launch shapes.
   if (variant >= gt::kGemmVariants) {
     if (!skinny) return GEMVTILE_ERR_UNSUPPORTED;
-    if (variant - gt::kGemmVariants >= gt::kSkinnyFirstQ8Variant && (M < N ? M : N) > 8)
-      return GEMVTILE_ERR_UNSUPPORTED;
-    return to_status(gt::launch_gemm_skinny_f16(variant - gt::kGemmVariants, A, B, D, static_cast<int>(M),
-                                                static_cast<int>(N), static_cast<int>(K), s));
+    if (gt::skinny_variant_q8(variant - gt::kGemmVariants) && (M < N ? M : N) > 8) return GEMVTILE_ERR_UNSUPPORTED;
   }
+  int cus = 0;
+  st = current_cu_count(&cus);
+  if (st != GEMVTILE_OK) return st;
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  // Variants kGemmVariants.. force skinny launch shapes (f16 only).
+  if (variant >= gt::kGemmVariants)
+    return to_status(gt::launch_gemm_skinny_f16(variant - gt::kGemmVariants, A, B, D, m, n, k, cus, s));
   if (variant == 0 && (M == 1 || N == 1)) {
     // One row on a side is the batch-1 product y = x·Wᵀ: M == 1 is
     // D[0][n] = A[0]·B[n] (x = A, W = B); N == 1 is D[m][0] = A[m]·B[0]
     // (x = B, W = A), whose [M,1] output is a contiguous vector.
     const void *x = M == 1 ? A : B;
     const void *W = M == 1 ? B : A;
-    const int64_t rows = M == 1 ? N : M;
-    return to_status(gt::launch_gemv_f16(0, x, W, D, static_cast<int>(rows), static_cast<int>(K), s));
+    const int rows = M == 1 ? n : m;
+    return to_status(dtype == gt::kBF16 ? gt::launch_gemv_bf16(x, W, D, rows, k, cus, s)
+                                        : gt::launch_gemv_f16(0, x, W, D, rows, k, cus, s));
   }
+  // Variant 0 sends shapes with at most 16 rows on one side to the skinny kernel.
   if (variant == 0 && skinny)
-    return to_status(gt::launch_gemm_skinny_f16(0, A, B, D, static_cast<int>(M), static_cast<int>(N),
-                                                static_cast<int>(K), s));
-  int cus = 0;
-  st = current_cu_count(&cus);
-  if (st != GEMVTILE_OK) return st;
-  return to_status(gt::launch_gemm_f16(variant, A, B, D, static_cast<int>(M), static_cast<int>(N),
-                                       static_cast<int>(K), cus, s));
+    return to_status(dtype == gt::kBF16 ? gt::launch_gemm_skinny_bf16(A, B, D, m, n, k, cus, s)
+                                        : gt::launch_gemm_skinny_f16(0, A, B, D, m, n, k, cus, s));
+  return to_status(dtype == gt::kBF16 ? gt::launch_gemm_bf16(A, B, D, m, n, k, cus, s)
+                                      : gt::launch_gemm_f16(variant, A, B, D, m, n, k, cus, s));
 }
 
 int run_gemv(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream, int variant,
@@ -139,8 +129,12 @@ int run_gemv(const void *x, const void *W, void *y, int64_t N, int64_t K, void *
   if (st != GEMVTILE_OK || noop) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K == 0) return to_status(gt::launch_fill_zero_f16(y, N, s));
-  if (dtype == gt::kBF16) return to_status(gt::launch_gemv_bf16(x, W, y, static_cast<int>(N), static_cast<int>(K), s));
-  return to_status(gt::launch_gemv_f16(variant, x, W, y, static_cast<int>(N), static_cast<int>(K), s));
+  int cus = 0;
+  st = current_cu_count(&cus);
+  if (st != GEMVTILE_OK) return st;
+  const int n = static_cast<int>(N), k = static_cast<int>(K);
+  if (dtype == gt::kBF16) return to_status(gt::launch_gemv_bf16(x, W, y, n, k, cus, s));
+  return to_status(gt::launch_gemv_f16(variant, x, W, y, n, k, cus, s));
 }
 
 }  // namespace
@@ -209,11 +203,22 @@ void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, 
   if (group_m) *group_m = gt::kGemmGroupM;
 }
 
+int64_t gemvtile_gemv_grid(int64_t N, int64_t num_cus) {
+  if (N <= 0 || num_cus <= 0 || num_cus > (int64_t{1} << 20)) return 0;
+  return gt::gemv_default_grid(N, static_cast<int>(num_cus));
+}
+
 int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus) {
   if (M <= 0 || N <= 0 || num_cus <= 0) return 0;
-  // Skinny shapes: one workgroup per 16 rows of the larger side.
-  if (M <= gt::kSkinnyMaxRows) return (N + 15) / 16;
-  if (N <= gt::kSkinnyMaxRows) return (M + 15) / 16;
+  // One row on a side: the GEMV kernel over the other side's rows.
+  if (M == 1 || N == 1) return gemvtile_gemv_grid(M == 1 ? N : M, num_cus);
+  // Skinny shapes: one workgroup per 16, 8, 4, 2 or 1 rows of the larger side.
+  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows) {
+    if (num_cus > (int64_t{1} << 20)) return 0;
+    const int64_t R = M <= gt::kSkinnyMaxRows ? N : M;
+    const int64_t rows = gt::skinny_default_rows(R, static_cast<int>(num_cus));
+    return (R + rows - 1) / rows;
+  }
   const int64_t tiles = ((M + gt::kGemmBM - 1) / gt::kGemmBM) * ((N + gt::kGemmBN - 1) / gt::kGemmBN);
   return tiles < num_cus ? tiles : num_cus;
 }

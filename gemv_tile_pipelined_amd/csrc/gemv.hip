@@ -27,7 +27,14 @@
 //  * the 64 lane partial sums of a row are combined with DPP lane moves
 //    inside the wave (no LDS, no atomics, no second kernel), so each row sum
 //    is deterministic; a wave's rows are reduced together so that the short
-//    dependent chains overlap.
+//    dependent chains overlap;
+//  * when N is too small to give every CU a workgroup of whole-row waves, the
+//    waves of a workgroup also split K (the page's "enough blocks" lesson,
+//    §5.2 block_split_k, which splits K over blocks and adds the partial sums
+//    with FP32 atomics): KSPLIT waves share each row group, each walks one
+//    slice of K, and the slices' FP32 row sums meet in LDS and are added in
+//    slice order, so the result stays deterministic and no workspace is
+//    needed.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -92,15 +99,31 @@ __device__ inline void store_row_sums(const float (&acc)[ROWS], int lane, int64_
   if (lane < ROWS && row0 + lane < N) y[row0 + lane] = round_out<DT>(mine);
 }
 
-template <int ROWS, int WAVES, int UNROLL, bool NONTEMPORAL, bool ROTATE = false, int DT = kF16>
+template <int ROWS, int WAVES, int UNROLL, bool NONTEMPORAL, bool ROTATE = false, int DT = kF16, int KSPLIT = 1>
 __global__ void __launch_bounds__(WAVES * 64)
 gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Float16 *__restrict__ y, int N,
                 int K) {
+  static_assert(KSPLIT >= 1 && WAVES % KSPLIT == 0, "K slices divide the waves");
+  constexpr int kRowGroups = WAVES / KSPLIT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * WAVES + wave) * ROWS;
-  if (row0 >= N) return;  // wave-uniform
+  const int slice = wave % KSPLIT;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kRowGroups + wave / KSPLIT) * ROWS;
+  if constexpr (KSPLIT == 1) {
+    if (row0 >= N) return;  // wave-uniform
+  }
   const int chunks = K >> 3;
+  // This wave's chunks [c_begin, c_end): all of K, or its slice, cut on
+  // 64-chunk steps (steps * slice / KSPLIT is below steps, so c_begin < chunks).
+  // A row group wholly past N (last workgroup only) walks nothing but still
+  // meets the others at the barrier below.
+  int c_begin = 0, c_end = chunks;
+  if constexpr (KSPLIT > 1) {
+    const int steps = (chunks + 63) >> 6;
+    c_begin = (steps * slice / KSPLIT) * 64;
+    c_end = min(chunks, (steps * (slice + 1) / KSPLIT) * 64);
+    if (row0 >= N) c_end = c_begin;
+  }
   const half8_t *xv = reinterpret_cast<const half8_t *>(x);
   const half8_t *wrow[ROWS];
 #pragma unroll
@@ -125,7 +148,7 @@ gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Flo
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int c = base + u * 64 + lane;
-      if (!guarded || c < chunks) {
+      if (!guarded || c < c_end) {
         xs[u] = xv[c];
 #pragma unroll
         for (int r = 0; r < ROWS; ++r)
@@ -146,30 +169,70 @@ gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Flo
   // different group (and wraps around), so the waves running at one moment
   // read different column windows of their rows.
   constexpr int kGroup = 64 * UNROLL;
-  const int full = chunks / kGroup;
+  const int span = c_end - c_begin;
+  const int full = span / kGroup;
   int g = (ROTATE && full > 0) ? static_cast<int>((row0 / ROWS) % full) : 0;
   for (int it = 0; it < full; ++it) {
-    group(g * kGroup, false);
+    group(c_begin + g * kGroup, false);
     if (++g == full) g = 0;
   }
-  if (full * kGroup < chunks) group(full * kGroup, true);
-  store_row_sums<ROWS, DT>(acc, lane, row0, N, y);
+  if (full * kGroup < span) group(c_begin + full * kGroup, true);
+  if constexpr (KSPLIT == 1) {
+    store_row_sums<ROWS, DT>(acc, lane, row0, N, y);
+  } else {
+    // Each slice's row sums go to LDS; the slice-0 wave of the row group adds
+    // them in slice order and stores the rounded total.
+    __shared__ float part[kRowGroups][ROWS][KSPLIT];
+    float sums[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) sums[r] = wave_sum(acc[r]);
+    const int rg = wave / KSPLIT;
+    if (lane < ROWS) {
+      float mine = sums[0];
+#pragma unroll
+      for (int r = 1; r < ROWS; ++r) mine = (lane == r) ? sums[r] : mine;
+      part[rg][lane][slice] = mine;
+    }
+    __syncthreads();
+    if (slice == 0 && lane < ROWS && row0 + lane < N) {
+      float total = part[rg][lane][0];
+#pragma unroll
+      for (int s2 = 1; s2 < KSPLIT; ++s2) total += part[rg][lane][s2];
+      y[row0 + lane] = round_out<DT>(total);
+    }
+  }
 }
 
-template <int ROWS, int WAVES, int UNROLL, bool NT, bool ROT = false, int DT = kF16>
+template <int ROWS, int WAVES, int UNROLL, bool NT, bool ROT = false, int DT = kF16, int KSPLIT = 1>
 static hipError_t launch(const void *x, const void *W, void *y, int N, int K, hipStream_t stream) {
-  const int64_t rows_per_block = static_cast<int64_t>(ROWS) * WAVES;
+  const int64_t rows_per_block = static_cast<int64_t>(ROWS) * WAVES / KSPLIT;
   const int64_t grid = (N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((gemv_kernel<ROWS, WAVES, UNROLL, NT, ROT, DT>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemv_kernel<ROWS, WAVES, UNROLL, NT, ROT, DT, KSPLIT>), dim3(static_cast<unsigned>(grid)),
                      dim3(WAVES * 64), 0, stream, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(W),
                      static_cast<_Float16 *>(y), N, K);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, hipStream_t stream) {
-  // <rows per wave, waves per workgroup, chunk steps in flight, non-temporal W>
+// The default launch (gemv_default_launch): 16, 8, 4 or 2 rows per workgroup
+// with 1, 2, 4 or 8 K slices, or 1 row in 8 slices.
+template <int DT>
+static hipError_t launch_auto(const void *x, const void *W, void *y, int N, int K, int num_cus, hipStream_t stream) {
+  static_assert(kGemvWaves == 8, "the instantiations below use 8 waves");
+  const GemvLaunch l = gemv_default_launch(N, num_cus);
+  if (l.rows_per_wave == 1) return launch<1, 8, 4, true, true, DT, 8>(x, W, y, N, K, stream);
+  switch (l.ksplit) {
+    case 1: return launch<2, 8, 4, true, true, DT, 1>(x, W, y, N, K, stream);
+    case 2: return launch<2, 8, 4, true, true, DT, 2>(x, W, y, N, K, stream);
+    case 4: return launch<2, 8, 4, true, true, DT, 4>(x, W, y, N, K, stream);
+    default: return launch<2, 8, 4, true, true, DT, 8>(x, W, y, N, K, stream);
+  }
+}
+
+hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, int num_cus,
+                           hipStream_t stream) {
+  // <rows per wave, waves per workgroup, chunk steps in flight, non-temporal W, rotated start, type, K slices>
   switch (variant) {
-    case 0: return launch<2, 8, 4, true, true>(x, W, y, N, K, stream);
+    case 0: return launch_auto<kF16>(x, W, y, N, K, num_cus, stream);
     case 1: return launch<4, 4, 4, true>(x, W, y, N, K, stream);
     case 2: return launch<2, 8, 8, true>(x, W, y, N, K, stream);
     case 3: return launch<1, 8, 8, true>(x, W, y, N, K, stream);
@@ -177,6 +240,11 @@ hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, i
     case 5: return launch<1, 16, 4, true>(x, W, y, N, K, stream);
     case 6: return launch<2, 8, 4, false>(x, W, y, N, K, stream);
     case 7: return launch<2, 8, 4, true, false>(x, W, y, N, K, stream);
+    case 8: return launch<2, 8, 4, true, true, kF16, 1>(x, W, y, N, K, stream);
+    case 9: return launch<2, 8, 4, true, true, kF16, 2>(x, W, y, N, K, stream);
+    case 10: return launch<2, 8, 4, true, true, kF16, 4>(x, W, y, N, K, stream);
+    case 11: return launch<2, 8, 4, true, true, kF16, 8>(x, W, y, N, K, stream);
+    case 12: return launch<1, 8, 4, true, true, kF16, 8>(x, W, y, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -189,8 +257,8 @@ __global__ void fill_zero_f16_kernel(_Float16 *__restrict__ p, int64_t count) {
     p[i] = static_cast<_Float16>(0.0f);
 }
 
-hipError_t launch_gemv_bf16(const void *x, const void *W, void *y, int N, int K, hipStream_t stream) {
-  return launch<2, 8, 4, true, true, kBF16>(x, W, y, N, K, stream);
+hipError_t launch_gemv_bf16(const void *x, const void *W, void *y, int N, int K, int num_cus, hipStream_t stream) {
+  return launch_auto<kBF16>(x, W, y, N, K, num_cus, stream);
 }
 
 hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream) {

@@ -21,13 +21,48 @@ constexpr int kGemmStages = 2;
 constexpr int kGemmThreads = 256;
 constexpr int kGemmGroupM = 8;
 constexpr int kGemmVariants = 13;
-constexpr int kGemvVariants = 8;
+constexpr int kGemvVariants = 13;
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip); it has kSkinnyVariants launch shapes.
 constexpr int kSkinnyMaxRows = 16;
-constexpr int kSkinnyVariants = 12;
-// Skinny launch shapes from this index on stage only 8 rows of the small side.
-constexpr int kSkinnyFirstQ8Variant = 9;
+constexpr int kSkinnyVariants = 40;
+// Skinny launch shapes that stage only 8 rows of the small side (valid for
+// min(M,N) <= 8 only).
+inline bool skinny_variant_q8(int v) {
+  return (v >= 9 && v <= 11) || (v >= 19 && v <= 23) || (v >= 26 && v <= 29) || (v >= 35 && v <= 39);
+}
+
+// The default GEMV launch for N rows on a device with num_cus compute units:
+// 8 waves per workgroup, each wave on `rows_per_wave` rows and one of `ksplit`
+// slices of K.  16 rows per workgroup while that still gives every CU a
+// workgroup; below that the waves split K 2, 4 or 8 ways (8, 4 or 2 rows per
+// workgroup), and below 2 rows per CU a workgroup takes one row in 8 slices.
+struct GemvLaunch {
+  int rows_per_wave;
+  int ksplit;
+};
+constexpr int kGemvWaves = 8;
+inline GemvLaunch gemv_default_launch(int64_t N, int num_cus) {
+  const int64_t c = num_cus;
+  if (N >= 16 * c) return {2, 1};
+  if (N >= 8 * c) return {2, 2};
+  if (N >= 4 * c) return {2, 4};
+  if (N >= 2 * c) return {2, 8};
+  return {1, 8};
+}
+inline int64_t gemv_default_grid(int64_t N, int num_cus) {
+  const GemvLaunch l = gemv_default_launch(N, num_cus);
+  const int64_t rows = static_cast<int64_t>(l.rows_per_wave) * kGemvWaves / l.ksplit;
+  return (N + rows - 1) / rows;
+}
+
+// P rows per workgroup of the default skinny launch for R rows of the large
+// operand: the largest of 16, 8, 4, 2 with R >= rows * num_cus, else 1.
+inline int skinny_default_rows(int64_t R, int num_cus) {
+  for (int rows = 16; rows > 1; rows >>= 1)
+    if (R >= static_cast<int64_t>(rows) * num_cus) return rows;
+  return 1;
+}
 
 // s_waitcnt immediate for "lgkmcnt(0)" alone on gfx9-family targets
 // (vmcnt field [3:0]|[15:14] = 63, expcnt [6:4] = 7, lgkmcnt [11:8] = 0).
@@ -37,13 +72,15 @@ constexpr unsigned kWaitLgkm0 = 0xC07F;
 hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                            hipStream_t stream);
 hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K,
-                                  hipStream_t stream);
-hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, hipStream_t stream);
+                                  int num_cus, hipStream_t stream);
+hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, int num_cus,
+                           hipStream_t stream);
 hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream);
 // bf16 operands and results: the default launch shape of each kernel.
 hipError_t launch_gemm_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                             hipStream_t stream);
-hipError_t launch_gemm_skinny_bf16(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t stream);
-hipError_t launch_gemv_bf16(const void *x, const void *W, void *y, int N, int K, hipStream_t stream);
+hipError_t launch_gemm_skinny_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
+                                   hipStream_t stream);
+hipError_t launch_gemv_bf16(const void *x, const void *W, void *y, int N, int K, int num_cus, hipStream_t stream);
 
 }  // namespace gt

@@ -114,65 +114,85 @@ __device__ inline void wait_younger(int younger) {
 // tiles of BK = 512 (1 KiB per row), filled by direct-to-LDS loads in which
 // one wave instruction moves one whole 1 KiB row segment (the register
 // variant above touches 16 rows x 64 bytes per instruction, and every
-// workgroup re-reads the small operand that way).  A stage holds the 16 rows
-// of P and QROWS rows of Q (rows past R or S and K past K read as zero: the
-// buffer descriptors' ranges and an out-of-range offset).  With QROWS = 8
-// (for S <= 8) the MFMA lanes of Q rows 8..15 re-read rows 0..7, whose
-// products only reach outputs that are never stored, and the smaller stage
-// lets the ring keep more of P in flight.  Each wave issues
-// (16+QROWS)/WAVES row loads per stage and computes BK/32/WAVES of the
-// stage's K steps.  LDS chunk c of row r holds logical chunk c ^ s(r) with
-// s(r) = 2*(r % 8) + (r / 8) (the loader picks the global chunk per lane to
-// make it so), and the four lane groups of a K step read chunks 0, 2, 1, 3
-// of the step: lanes l and l + 32, which the LDS serves together, then read
-// chunks an odd XOR apart and every read is bank-conflict free.
-template <int WAVES, int STAGES, int QROWS, bool TRANS, int DT = kF16>
+// workgroup re-reads the small operand that way).  A workgroup owns PR rows
+// of P (16 by default; 8, 4, 2 or 1 when R is too small to give every CU a
+// workgroup of 16 -- the page's "enough blocks" again, here without splitting
+// K, since every workgroup re-reading the small Q costs only cache traffic).
+// A stage holds the PR rows of P and QROWS rows of Q (rows past R or S and K
+// past K read as zero: the buffer descriptors' ranges and an out-of-range
+// offset).  The MFMA's 16 P lanes read P row (lane % PR) and its 16 Q lanes
+// Q row (lane % QROWS): rows re-read that way only reach outputs that are
+// never stored.  QROWS = 8 (for S <= 8) halves the Q traffic.  The
+// PR + QROWS row loads of a stage are spread over the waves,
+// ceil((PR+QROWS)/WAVES) per wave; spare slots load zeros (out-of-range
+// offset, no memory access) into a junk row so every wave issues the same
+// number of loads and the vmcnt accounting stays uniform.  Each wave computes
+// BK/32/WAVES of the stage's K steps.  LDS chunk c of row r holds logical
+// chunk c ^ s(r) with s(r) = 2*(r % 8) + (r / 8) (the loader picks the global
+// chunk per lane to make it so), and the four lane groups of a K step read
+// chunks 0, 2, 1, 3 of the step: lanes l and l + 32, which the LDS serves
+// together, then read chunks an odd XOR apart and every read is bank-conflict
+// free (lanes that re-read a row read the same address, a broadcast).
+template <int WAVES, int STAGES, int QROWS, bool TRANS, int DT = kF16, int PR = 16, bool KROT = false>
 __global__ void __launch_bounds__(WAVES * 64)
 gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ Q, _Float16 *__restrict__ D,
                        int R, int S, int K) {
   constexpr int BK = 512;
-  constexpr int kRowBytes = BK * 2;            // 1 KiB: one wave instruction
-  constexpr int kTileBytes = 16 * kRowBytes;                 // the 16 rows of P
-  constexpr int kStageBytes = (16 + QROWS) * kRowBytes;      // P tile, then Q tile
-  constexpr int kDmaPerWave = (16 + QROWS) / WAVES;          // row loads per wave per stage
-  constexpr int kSteps = BK / 32;                            // 32-wide K steps per stage
+  constexpr int kRowBytes = BK * 2;                              // 1 KiB: one wave instruction
+  constexpr int kLoads = PR + QROWS;                             // row loads per stage
+  constexpr int kDmaPerWave = (kLoads + WAVES - 1) / WAVES;      // per wave per stage
+  constexpr bool kJunk = kDmaPerWave * WAVES > kLoads;           // spare slots -> junk row kLoads
+  constexpr int kTileBytes = PR * kRowBytes;                     // the P rows, then the Q rows
+  constexpr int kStageBytes = (kLoads + (kJunk ? 1 : 0)) * kRowBytes;
+  constexpr int kSteps = BK / 32;                                // 32-wide K steps per stage
   constexpr int kStepsPerWave = kSteps / WAVES;
   static_assert(QROWS == 8 || QROWS == 16, "Q tile rows");
-  static_assert((16 + QROWS) % WAVES == 0 && kSteps % WAVES == 0, "work split");
+  static_assert(PR == 1 || PR == 2 || PR == 4 || PR == 8 || PR == 16, "P rows per workgroup");
+  static_assert(kSteps % WAVES == 0, "work split");
   static_assert(STAGES >= 2 && (STAGES - 1) * kDmaPerWave <= 63, "vmcnt range");
+  static_assert(STAGES * kStageBytes + WAVES * 16 * 17 * 4 <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * kStageBytes];
   __shared__ float partial[WAVES][16][17];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r0 = blockIdx.x * 16;
-  const int prows = min(16, R - r0);
+  const int r0 = blockIdx.x * PR;
+  const int prows = min(PR, R - r0);
   const int4_t rsrc_p = make_buffer_rsrc(P + static_cast<int64_t>(r0) * K, static_cast<uint32_t>(prows) * K * 2u);
   const int4_t rsrc_q = make_buffer_rsrc(Q, static_cast<uint32_t>(S) * K * 2u);
   const uint32_t ring0 = lds_addr(ring);
   const int KT = (K + BK - 1) / BK;
+  // With KROT, workgroup b walks the K tiles from tile b % KT and wraps, so
+  // the workgroups running at one moment read different parts of Q (which
+  // they all share) instead of the same lines at once.
+  const int kt0 = KROT ? static_cast<int>(blockIdx.x % static_cast<unsigned>(KT)) : 0;
   auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
 
-  // Row loads of K tile kt: load d of this wave moves tile row
-  // t = d*WAVES + wave (P rows 0..15, then Q rows 0..QROWS-1).
+  // Row loads of K tile kt: load d of this wave moves stage row
+  // t = d*WAVES + wave (P rows 0..PR-1, then Q rows 0..QROWS-1; t >= kLoads
+  // loads zeros into the junk row).
   auto issue = [&](int kt) {
     const uint32_t stage = ring0 + static_cast<uint32_t>((kt % STAGES) * kStageBytes);
+    const int ktile = kt + kt0 < KT ? kt + kt0 : kt + kt0 - KT;  // the K tile this ring slot holds
 #pragma unroll
     for (int d = 0; d < kDmaPerWave; ++d) {
       const int t = d * WAVES + wave;
-      const int row = t & 15;
-      const int k = kt * BK + ((lane ^ swz(row)) << 3);  // first K element this lane fetches
-      const uint32_t off = k < K ? static_cast<uint32_t>(row) * K * 2u + static_cast<uint32_t>(k) * 2u : kOobOffset;
-      lds_dma_b128(t < 16 ? rsrc_p : rsrc_q, off,
-                   __builtin_amdgcn_readfirstlane(stage + static_cast<uint32_t>(t * kRowBytes)));
+      const bool junk = kJunk && t >= kLoads;
+      const int row = t < PR ? t : t - PR;  // row within its operand
+      const int k = ktile * BK + ((lane ^ swz(row & 15)) << 3);  // first K element this lane fetches
+      const uint32_t off = (k < K && !junk) ? static_cast<uint32_t>(row) * K * 2u + static_cast<uint32_t>(k) * 2u
+                                            : kOobOffset;
+      lds_dma_b128(t < PR ? rsrc_p : rsrc_q, off,
+                   __builtin_amdgcn_readfirstlane(stage + static_cast<uint32_t>(min(t, kLoads) * kRowBytes)));
     }
   };
 
   const int frow = lane & 15;
   const int kgrp = lane >> 4;
   const int kperm = ((kgrp & 1) << 1) | (kgrp >> 1);
-  const uint32_t frag_off = static_cast<uint32_t>(frow * kRowBytes);
-  const int fswz = swz(frow);
+  const int prow = frow % PR;  // P row of this lane's fragment
+  const uint32_t frag_off = static_cast<uint32_t>(prow * kRowBytes);
+  const int fswz = swz(prow);
   const int qrow = frow % QROWS;  // Q row of this lane's fragment
   const uint32_t qfrag_off = static_cast<uint32_t>(kTileBytes + qrow * kRowBytes);
   const int qswz = swz(qrow);
@@ -208,33 +228,55 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
 #pragma unroll
   for (int e = 0; e < 4; ++e) partial[wave][frow][4 * kgrp + e] = acc[e];
   __syncthreads();
-  if (threadIdx.x < 256) {
-    const int s = threadIdx.x >> 4;
-    const int r = threadIdx.x & 15;
+  // 16 x 16 outputs (Q row s, P row r), each the wave partials in wave order.
+  for (int i = threadIdx.x; i < 256; i += WAVES * 64) {
+    const int s = i >> 4;
+    const int r = i & 15;
     float sum = 0.0f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += partial[w][s][r];
-    if (s < S && r0 + r < R) {
+    if (s < S && r < PR && r0 + r < R) {
       const int64_t idx = TRANS ? static_cast<int64_t>(r0 + r) * S + s : static_cast<int64_t>(s) * R + r0 + r;
       D[idx] = round_out<DT>(sum);
     }
   }
 }
 
-template <int WAVES, int STAGES, int QROWS, int DT = kF16>
+template <int WAVES, int STAGES, int QROWS, int DT = kF16, int PR = 16, bool KROT = false>
 static hipError_t launch_lds(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                              hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((R + 15) / 16));
+  const dim3 grid(static_cast<unsigned>((R + PR - 1) / PR));
   const auto *p = static_cast<const _Float16 *>(P);
   const auto *q = static_cast<const _Float16 *>(Q);
   auto *d = static_cast<_Float16 *>(D);
   if (trans)
-    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, true, DT>), grid, dim3(WAVES * 64), 0, stream, p,
-                       q, d, R, S, K);
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, true, DT, PR, KROT>), grid, dim3(WAVES * 64), 0,
+                       stream, p, q, d, R, S, K);
   else
-    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, false, DT>), grid, dim3(WAVES * 64), 0, stream,
-                       p, q, d, R, S, K);
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, false, DT, PR, KROT>), grid, dim3(WAVES * 64),
+                       0, stream, p, q, d, R, S, K);
   return hipGetLastError();
+}
+
+// The default launch (skinny_default_rows): 16 P rows per workgroup with 16
+// waves, a 4-stage ring and rotated K starts while R gives every CU such a
+// workgroup; else 8, 4, 2 or 1 P rows, staging 8 Q rows when S <= 8.
+template <int DT>
+static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
+                                  int num_cus, hipStream_t stream) {
+  const int pr = skinny_default_rows(R, num_cus);
+  const bool q8 = S <= 8;
+  switch (pr) {
+    case 16: return launch_lds<16, 4, 16, DT, 16, true>(P, Q, D, R, S, K, trans, stream);
+    case 8: return q8 ? launch_lds<8, 4, 8, DT, 8>(P, Q, D, R, S, K, trans, stream)
+                      : launch_lds<8, 4, 16, DT, 8>(P, Q, D, R, S, K, trans, stream);
+    case 4: return q8 ? launch_lds<4, 4, 8, DT, 4>(P, Q, D, R, S, K, trans, stream)
+                      : launch_lds<4, 4, 16, DT, 4>(P, Q, D, R, S, K, trans, stream);
+    case 2: return q8 ? launch_lds<4, 4, 8, DT, 2>(P, Q, D, R, S, K, trans, stream)
+                      : launch_lds<4, 4, 16, DT, 2>(P, Q, D, R, S, K, trans, stream);
+    default: return q8 ? launch_lds<4, 4, 8, DT, 1>(P, Q, D, R, S, K, trans, stream)
+                       : launch_lds<4, 4, 16, DT, 1>(P, Q, D, R, S, K, trans, stream);
+  }
 }
 
 template <int WAVES, int UNROLL>
@@ -254,7 +296,7 @@ static hipError_t launch(const void *P, const void *Q, void *D, int R, int S, in
 }
 
 hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K,
-                                  hipStream_t stream) {
+                                  int num_cus, hipStream_t stream) {
   // The small side is Q.  M <= 16: Q = A, P = B, D = Q·Pᵀ.  Otherwise
   // (N <= 16): Q = B, P = A, D = P·Qᵀ.
   const bool small_m = M <= kSkinnyMaxRows;
@@ -265,7 +307,7 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
   const int S = small_m ? M : N;
   switch (variant) {
     // LDS-staged: <waves per workgroup, ring stages, Q rows staged>; 0 is the default
-    case 0: return launch_lds<16, 4, 16>(P, Q, D, R, S, K, !small_m, stream);
+    case 0: return launch_lds_auto<kF16>(P, Q, D, R, S, K, !small_m, num_cus, stream);
     case 1: return launch_lds<8, 4, 16>(P, Q, D, R, S, K, !small_m, stream);
     case 2: return launch_lds<8, 3, 16>(P, Q, D, R, S, K, !small_m, stream);
     case 3: return launch_lds<4, 4, 16>(P, Q, D, R, S, K, !small_m, stream);
@@ -279,15 +321,47 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
     case 9: return S <= 8 ? launch_lds<8, 5, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
     case 10: return S <= 8 ? launch_lds<8, 6, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
     case 11: return S <= 8 ? launch_lds<4, 6, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    // fewer P rows per workgroup: <waves, stages, Q rows, type, P rows>
+    case 12: return launch_lds<16, 4, 16, kF16, 16>(P, Q, D, R, S, K, !small_m, stream);
+    case 13: return launch_lds<8, 4, 16, kF16, 8>(P, Q, D, R, S, K, !small_m, stream);
+    case 14: return launch_lds<4, 4, 16, kF16, 4>(P, Q, D, R, S, K, !small_m, stream);
+    case 15: return launch_lds<8, 4, 16, kF16, 4>(P, Q, D, R, S, K, !small_m, stream);
+    case 16: return launch_lds<4, 4, 16, kF16, 2>(P, Q, D, R, S, K, !small_m, stream);
+    case 17: return launch_lds<4, 4, 16, kF16, 1>(P, Q, D, R, S, K, !small_m, stream);
+    case 18: return launch_lds<1, 4, 16, kF16, 1>(P, Q, D, R, S, K, !small_m, stream);
+    case 19: return S <= 8 ? launch_lds<8, 4, 8, kF16, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 20: return S <= 8 ? launch_lds<4, 4, 8, kF16, 4>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 21: return S <= 8 ? launch_lds<4, 4, 8, kF16, 2>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 22: return S <= 8 ? launch_lds<4, 4, 8, kF16, 1>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 23: return S <= 8 ? launch_lds<8, 4, 8, kF16, 1>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    // deeper rings for the smaller per-workgroup tiles: <waves, stages, Q rows, type, P rows>
+    case 24: return launch_lds<8, 6, 16, kF16, 8>(P, Q, D, R, S, K, !small_m, stream);
+    case 25: return launch_lds<4, 7, 16, kF16, 4>(P, Q, D, R, S, K, !small_m, stream);
+    case 26: return S <= 8 ? launch_lds<8, 8, 8, kF16, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 27: return S <= 8 ? launch_lds<4, 8, 8, kF16, 4>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 28: return S <= 8 ? launch_lds<4, 12, 8, kF16, 4>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 29: return S <= 8 ? launch_lds<4, 12, 8, kF16, 2>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    // rotated K start per workgroup: <waves, stages, Q rows, type, P rows, rotate>
+    case 30: return launch_lds<16, 4, 16, kF16, 16, true>(P, Q, D, R, S, K, !small_m, stream);
+    case 31: return launch_lds<8, 4, 16, kF16, 8, true>(P, Q, D, R, S, K, !small_m, stream);
+    case 32: return launch_lds<4, 4, 16, kF16, 4, true>(P, Q, D, R, S, K, !small_m, stream);
+    case 33: return launch_lds<4, 4, 16, kF16, 2, true>(P, Q, D, R, S, K, !small_m, stream);
+    case 34: return launch_lds<4, 4, 16, kF16, 1, true>(P, Q, D, R, S, K, !small_m, stream);
+    case 35: return S <= 8 ? launch_lds<8, 4, 8, kF16, 8, true>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 36: return S <= 8 ? launch_lds<4, 4, 8, kF16, 4, true>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 37: return S <= 8 ? launch_lds<4, 4, 8, kF16, 2, true>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 38: return S <= 8 ? launch_lds<4, 4, 8, kF16, 1, true>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
+    case 39: return S <= 8 ? launch_lds<8, 6, 8, kF16, 16, true>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gemm_skinny_bf16(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t stream) {
+hipError_t launch_gemm_skinny_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
+                                   hipStream_t stream) {
   const bool small_m = M <= kSkinnyMaxRows;
   if (!small_m && N > kSkinnyMaxRows) return hipErrorInvalidValue;
-  return launch_lds<16, 4, 16, kBF16>(small_m ? B : A, small_m ? A : B, D, small_m ? N : M, small_m ? M : N, K,
-                                      !small_m, stream);
+  return launch_lds_auto<kBF16>(small_m ? B : A, small_m ? A : B, D, small_m ? N : M, small_m ? M : N, K, !small_m,
+                                num_cus, stream);
 }
 
 }  // namespace gt

@@ -1,0 +1,154 @@
+"""Kernel-trace sweep of the bandwidth-bound paths over shapes.
+
+    rocprofv3 --kernel-trace --output-format csv -d OUT -o sweep -- \\
+        python3 -m gemv_tile_pipelined_amd.shape_sweep [--gemv N:K,...] [--skinny M:N:K,...]
+            [--gemv-variants 0,8] [--skinny-variants 0,25] [--vendor] [--reps 40] > OUT/log.txt
+    python3 -m gemv_tile_pipelined_amd.shape_sweep --parse OUT OUT/log.txt
+
+The first command launches, for every shape, `reps` GEMVs (gemv_f16, one
+line per launch shape in --gemv-variants) or decode-batch GEMMs (gemm_f16,
+one line per gemvtile_gemm_f16_variant id in --skinny-variants)
+over enough distinct copies of W / B (at least 600 MB in all) that each
+launch reads its matrix from HBM rather than the 256 MB MALL; with --vendor
+also torch.mv on the same GEMV inputs.  Segments are delimited in the trace
+by a marker kernel (a bitwise not of one int8), and the last stdout line
+lists the segments.  The second command reads the trace and prints each
+segment's median kernel time and algorithmic bandwidth
+(2·(rows·K + K + rows) bytes for the GEMV, 2·(M·K + N·K + M·N) for the GEMM).
+Inputs are seeded synthetic fp16 values (x, A ~ U(-1,1); W, B ~ U(-0.05,0.05)).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MARKER = "bitwise_not"
+DEFAULT_GEMV = "64:14336,128:14336,256:14336,512:14336,1024:14336,2048:14336,4096:14336,1024:4096,4096:4096,256:65536,1024:65536"
+DEFAULT_SKINNY = "8:256:14336,8:1024:14336,8:4096:14336,8:1024:4096"
+
+
+def _shapes(spec, n):
+    out = []
+    for item in filter(None, spec.split(",")):
+        vals = tuple(int(v) for v in item.split(":"))
+        if len(vals) != n:
+            raise SystemExit(f"shape {item!r}: expected {n} sizes")
+        out.append(vals)
+    return out
+
+
+def run(a):
+    import torch
+
+    import gemv_tile_pipelined_amd as gt
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(4321)
+    marker = torch.zeros((1,), dtype=torch.int8, device=dev)
+    labels = []
+
+    def copies_for(nbytes):
+        return max(2, min(64, int(600e6 // nbytes) + 1))
+
+    def segment(label, fn, copies):
+        try:
+            fn(0)
+        except gt.GemvTileError as e:
+            if e.status != 2:  # only launch shapes that do not apply to this shape are skipped
+                raise
+            return
+        for i in range(1, 3):
+            fn(i % copies)
+        torch.cuda.synchronize(dev)
+        marker.bitwise_not_()
+        for i in range(a.reps):
+            fn(i % copies)
+        marker.bitwise_not_()
+        torch.cuda.synchronize(dev)
+        labels.append(label)
+
+    def uni(shape, lo, hi):
+        return torch.empty(shape, dtype=torch.float16, device=dev).uniform_(lo, hi, generator=g)
+
+    variants = [int(v) for v in a.gemv_variants.split(",")]
+    skinny_variants = [int(v) for v in a.skinny_variants.split(",")]
+    for N, K in _shapes(a.gemv, 2):
+        c = copies_for(2 * N * K)
+        x = uni((K,), -1, 1)
+        Ws = [uni((N, K), -0.05, 0.05) for _ in range(c)]
+        y = torch.empty((N,), dtype=torch.float16, device=dev)
+        nbytes = 2 * (N * K + N + K)
+        for v in variants:
+            segment({"kind": "gemv_f16", "N": N, "K": K, "variant": v, "bytes": nbytes},
+                    lambda i, v=v: gt.gemv_f16(x, Ws[i], y, variant=v), c)
+        if a.vendor:
+            segment({"kind": "torch.mv", "N": N, "K": K, "bytes": nbytes}, lambda i: torch.mv(Ws[i], x, out=y), c)
+        del Ws
+    for M, N, K in _shapes(a.skinny, 3):
+        c = copies_for(2 * N * K)
+        A = uni((M, K), -1, 1)
+        Bs = [uni((N, K), -0.05, 0.05) for _ in range(c)]
+        D = torch.empty((M, N), dtype=torch.float16, device=dev)
+        for v in skinny_variants:
+            segment({"kind": "gemm_f16", "M": M, "N": N, "K": K, "variant": v, "bytes": 2 * (M * K + N * K + M * N)},
+                    lambda i, v=v: gt.gemm_f16(A, Bs[i], D, variant=v), c)
+        if a.vendor:
+            segment({"kind": "torch.matmul", "M": M, "N": N, "K": K, "bytes": 2 * (M * K + N * K + M * N)},
+                    lambda i: torch.matmul(A, Bs[i].t(), out=D), c)
+        del Bs
+    print("SEGMENTS " + json.dumps(labels), flush=True)
+
+
+def parse(trace_dir, log_path):
+    trace = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not trace:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    labels = None
+    for line in open(log_path):
+        if line.startswith("SEGMENTS "):
+            labels = json.loads(line[len("SEGMENTS "):])
+    if labels is None:
+        raise SystemExit(f"no SEGMENTS line in {log_path}")
+    rows = sorted(csv.DictReader(open(trace[0])), key=lambda r: int(r["Start_Timestamp"]))
+    marks = [i for i, r in enumerate(rows) if MARKER in r["Kernel_Name"]]
+    if len(marks) != 2 * len(labels):
+        raise SystemExit(f"{len(marks)} markers for {len(labels)} segments")
+    for lab, (lo, hi) in zip(labels, zip(marks[0::2], marks[1::2])):
+        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[lo + 1 : hi]]
+        names = sorted({r["Kernel_Name"].split("(")[0][:60] for r in rows[lo + 1 : hi]})
+        med = statistics.median(durs) / 1e3
+        gbps = lab["bytes"] / (med * 1e3)
+        shape = "x".join(str(lab[k]) for k in ("M", "N", "K") if k in lab)
+        var = f" v{lab['variant']}" if "variant" in lab else ""
+        print(f"{lab['kind']:13s}{var:4s} {shape:18s} n={len(durs):3d} median {med:8.2f} us "
+              f"{gbps:6.0f} GB/s ({gbps / 80:5.1f} % of 8 TB/s)  {'; '.join(names)}")
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gemv", default=DEFAULT_GEMV, help="N:K,... (empty for none)")
+    p.add_argument("--skinny", default=DEFAULT_SKINNY, help="M:N:K,... (empty for none)")
+    p.add_argument("--gemv-variants", default="0")
+    p.add_argument("--skinny-variants", default="0")
+    p.add_argument("--vendor", action="store_true")
+    p.add_argument("--reps", type=int, default=40)
+    p.add_argument("--parse", nargs=2, metavar=("TRACE_DIR", "LOG"))
+    a = p.parse_args(argv)
+    if a.parse:
+        parse(*a.parse)
+    else:
+        run(a)
+
+
+if __name__ == "__main__":
+    main()

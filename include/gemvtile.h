@@ -66,8 +66,9 @@ enum gemvtile_status {
  * unspecified (several results are correct up to rounding).
  * When M <= 16 or N <= 16 (a decode batch against a weight matrix) the call
  * runs a bandwidth-bound kernel that streams the larger operand once instead
- * of the 256x256-tiled one, and when M == 1 or N == 1 the GEMV kernel of
- * gemv_f16; results are deterministic either way.
+ * of the 256x256-tiled one (with fewer rows of it per workgroup when it has
+ * too few rows to give every compute unit 16), and when M == 1 or N == 1
+ * the GEMV kernel of gemv_f16; results are deterministic either way.
  * Returns a gemvtile_status.
  */
 int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream);
@@ -88,7 +89,11 @@ int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
  *   stream hipStream_t or NULL
  *
  * N == 0: returns GEMVTILE_OK and touches nothing.  K == 0: y is filled with +0.
- * The row sums are deterministic: no atomics, no split across workgroups.
+ * When N is too small to give every compute unit a workgroup of 16 rows, the
+ * waves of a workgroup also split K (§5.2 block_split_k's reason: enough
+ * blocks in flight); the slices' FP32 partial sums are added in LDS in a
+ * fixed order (gemvtile_gemv_grid gives the workgroup count).  The row sums
+ * are deterministic: no atomics, no split across workgroups, no workspace.
  * Returns a gemvtile_status.
  */
 int gemv_f16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream);
@@ -135,12 +140,23 @@ int gemvtile_tile_coord(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t gro
 void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, int *group_m);
 
 /*
+ * gemvtile_gemv_grid -- the number of workgroups gemv_f16 (and gemv_bf16)
+ * launches for N rows on a device with `num_cus` compute units: ceil(N/R)
+ * with R = 16 rows per workgroup when N >= 16*num_cus, else 8, 4 or 2 rows
+ * (K split 2, 4 or 8 ways over the workgroup's 8 waves) while N >=
+ * 8, 4 or 2 times num_cus, else 1 row (K split 8 ways).  Host-only
+ * arithmetic; returns 0 for N <= 0 or num_cus outside [1, 2^20].
+ */
+int64_t gemvtile_gemv_grid(int64_t N, int64_t num_cus);
+
+/*
  * gemvtile_gemm_grid -- the number of workgroups gemm_f16 launches for an
- * M x N output on a device with `num_cus` compute units: ceil(max(M,N)/16)
- * when M <= 16 or N <= 16 (the skinny kernel, and the GEMV kernel's 16 rows
- * per workgroup when M or N is 1), otherwise the persistent grid
- * min(#tiles, num_cus).  Host-only arithmetic; returns 0 for
- * empty outputs.
+ * M x N output on a device with `num_cus` compute units: the GEMV grid of
+ * the other side's rows when M or N is 1; when M <= 16 or N <= 16 (the
+ * skinny kernel) ceil(R/p), R = max(M,N), with p the largest of 16, 8, 4, 2
+ * rows per workgroup such that R >= p*num_cus, else p = 1; otherwise the
+ * persistent grid min(#tiles, num_cus).  Host-only arithmetic; returns 0
+ * for empty outputs.
  */
 int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
 
@@ -168,14 +184,29 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  * Variants 1..12 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16: the skinny kernel).
- *   13..24 the skinny kernel (only for M <= 16 or N <= 16, else
- *      GEMVTILE_ERR_UNSUPPORTED).  13..16: operands staged through an LDS
- *      ring of 1 KiB row segments, (waves per workgroup, ring stages) =
- *      (16,4) [the gemm_f16 default], (8,4), (8,3), (4,4).  17..21: operands
- *      loaded into registers, (waves, 32-wide K steps in flight per wave) =
- *      (8,4), (8,2), (8,8), (16,4), (4,8).  22..24: as 13.. with only 8 rows
- *      of the small side staged (min(M,N) <= 8, else
- *      GEMVTILE_ERR_UNSUPPORTED), (waves, stages) = (8,5), (8,6), (4,6)
+ *   13..52 the skinny kernel (only for M <= 16 or N <= 16, else
+ *      GEMVTILE_ERR_UNSUPPORTED).  13: the gemm_f16 choice (16, 8, 4, 2 or
+ *      1 rows of the large side per workgroup, see gemvtile_gemm_grid; at 16
+ *      rows the rotated launch 43).
+ *      14..16: operands staged through an LDS ring of 1 KiB row segments,
+ *      16 large-side rows per workgroup, (waves per workgroup, ring stages)
+ *      = (8,4), (8,3), (4,4).  17..21: operands loaded into registers,
+ *      (waves, 32-wide K steps in flight per wave) = (8,4), (8,2), (8,8),
+ *      (16,4), (4,8).  22..24: as 14.. with only 8 rows of the small side
+ *      staged (min(M,N) <= 8, else GEMVTILE_ERR_UNSUPPORTED), (waves,
+ *      stages) = (8,5), (8,6), (4,6).  25..31: LDS ring, 4 stages, 16
+ *      small-side rows staged, (waves, large-side rows per workgroup) =
+ *      (16,16), (8,8), (4,4), (8,4), (4,2), (4,1), (1,1).  32..36: the same
+ *      with 8 small-side rows staged (min(M,N) <= 8), (8,8), (4,4), (4,2),
+ *      (4,1), (8,1).  37..42: deeper rings, (waves, stages, small-side rows
+ *      staged, large-side rows per workgroup) = (8,6,16,8), (4,7,16,4),
+ *      (8,8,8,8), (4,8,8,4), (4,12,8,4), (4,12,8,2) (the 8-row stagings need
+ *      min(M,N) <= 8).  43..52: each workgroup starting its K walk at K tile
+ *      (workgroup index mod K tiles), 4 stages, (waves, small-side rows,
+ *      large-side rows) = (16,16,16) [the gemm_f16 choice at 16 rows],
+ *      (8,16,8), (4,16,4), (4,16,2), (4,16,1), (8,8,8), (4,8,4), (4,8,2),
+ *      (4,8,1), and (8,8,16) with 6 stages (the 8-row stagings need
+ *      min(M,N) <= 8)
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
@@ -192,7 +223,11 @@ int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, 
  *   3 = 1 row, 8 waves, 8 steps, nt    4 = 2 rows, 4 waves, 8 steps, nt
  *   5 = 1 row, 16 waves, 4 steps, nt   6 = as 0 with ordinary loads
  *   7 = as 0 with every wave starting at the row's first column
- * Variants 1..5 start every wave at the first column.
+ *   8..11 = 2 rows, 8 waves, 4 steps, nt, rotated start, with K split over
+ *       1, 2, 4, 8 waves per row group (16, 8, 4, 2 rows per workgroup)
+ *   12 = 1 row, 8 waves, 4 steps, nt, rotated start, K split 8 ways
+ * Variant 0 picks one of 8..12 from N and the compute-unit count (see
+ * gemvtile_gemv_grid).  Variants 1..5 start every wave at the first column.
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream,

@@ -84,6 +84,9 @@ def test_gemm_argument_validation(lib):
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 13) == UNSUPPORTED
     # the 8-row small-side stagings need min(M, N) <= 8
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 22) == UNSUPPORTED
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 33) == UNSUPPORTED
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 30) == UNSUPPORTED
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 8, 4096, 8, None, 53) == INVALID
 
 
 def test_gemv_argument_validation(lib):
@@ -167,11 +170,20 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(256, 256, 256) == 1
     assert gt.gemm_grid(4000, 4032, 256) == 256
     assert gt.gemm_grid(0, 4, 256) == 0
-    # skinny shapes: one workgroup per 16 rows of the larger side
+    # skinny shapes: one workgroup per 16 rows of the larger side while that
+    # gives every CU one, else per 8, 4, 2 or 1 rows
     assert gt.gemm_grid(8, 4096, 256) == 256
     assert gt.gemm_grid(4096, 16, 256) == 256
-    assert gt.gemm_grid(16, 16, 256) == 1
+    assert gt.gemm_grid(8, 8192, 256) == 512
+    assert gt.gemm_grid(8, 3000, 256) == 375
+    assert gt.gemm_grid(8, 2000, 256) == 500
+    assert gt.gemm_grid(1000, 9, 256) == 500
+    assert gt.gemm_grid(16, 300, 256) == 300
+    assert gt.gemm_grid(16, 16, 256) == 16
     assert gt.gemm_grid(17, 4097, 256) == 17
+    # one row on a side: the GEMV grid of the other side
+    assert gt.gemm_grid(1, 4096, 256) == gt.gemv_grid(4096, 256) == 256
+    assert gt.gemm_grid(1000, 1, 256) == gt.gemv_grid(1000, 256)
     golden = _tile_counts()
     # The TVM chapter's counts at its 128x128 tiles and BLK_K = 64: the same
     # tile-count arithmetic, applied to its parameters.
@@ -199,3 +211,30 @@ def test_measurement_formulas_match_table1():
     assert metrics.gemv_bytes(N, K) == rows["total"][1]
     assert metrics.gemv_flops(N, K) == rows["flops"][0]
     assert metrics.gemm_flops(4096, 4096, 4096) == 137438953472
+
+
+def test_gemv_grid_gives_every_cu_a_workgroup(lib):
+    """gemv_f16 splits K over the waves of a workgroup when N alone would
+    leave compute units idle: 16, 8, 4, 2 rows per workgroup, then 1."""
+    assert gt.gemv_grid(4096, 256) == 256  # 16 rows per workgroup, no split
+    assert gt.gemv_grid(4097, 256) == 257
+    assert gt.gemv_grid(8192, 256) == 512
+    assert gt.gemv_grid(4095, 256) == 512  # 8 rows per workgroup
+    assert gt.gemv_grid(2048, 256) == 256
+    assert gt.gemv_grid(1024, 256) == 256  # 4 rows
+    assert gt.gemv_grid(1031, 256) == 258
+    assert gt.gemv_grid(512, 256) == 256  # 2 rows
+    assert gt.gemv_grid(511, 256) == 511  # 1 row
+    assert gt.gemv_grid(1, 256) == 1
+    assert gt.gemv_grid(0, 256) == 0
+    assert gt.gemv_grid(5, 0) == 0
+    for N in list(range(1, 70)) + [255, 256, 257, 1000, 3000, 4096, 10000, 14336]:
+        for cus in (1, 8, 80, 256, 304):
+            g = gt.gemv_grid(N, cus)
+            assert g >= 1
+            if N >= 2 * cus:
+                assert g >= cus  # every CU gets a workgroup
+            # the documented rule: the largest of 16, 8, 4, 2 rows per
+            # workgroup with N >= rows * cus, else 1
+            rows = next((r for r in (16, 8, 4, 2) if N >= r * cus), 1)
+            assert g == -(-N // rows)

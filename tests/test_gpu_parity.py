@@ -271,7 +271,7 @@ def test_gemm_variants_bit_identical(env, variant):
     assert np.array_equal(_gemm(env, A, B, variant).cpu().numpy(), base)
 
 
-@pytest.mark.parametrize("variant", list(range(1, 8)))
+@pytest.mark.parametrize("variant", list(range(1, 13)))
 def test_gemv_variants_bit_identical(env, variant):
     N, K = 1031, 14344
     x = datagen.integer_f16(6001, 0, (K,))

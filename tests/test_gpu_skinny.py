@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 TOL_ABS = 1e-2
 TOL_REL = 1e-2
 
-SKINNY_VARIANTS = range(13, 25)  # gemvtile_gemm_f16_variant ids of the skinny launch shapes
+SKINNY_VARIANTS = range(13, 53)  # gemvtile_gemm_f16_variant ids of the skinny launch shapes
 
 
 @pytest.fixture(scope="module")
@@ -58,6 +58,17 @@ SHAPES = [
     (4000, 16, 4104),
     (520, 5, 1032),
     (33, 1, 72),
+    # fewer large-side rows than 16 per CU: 8, 4, 2 or 1 rows per workgroup
+    # (on a 256-CU part), with 8 or 16 small-side rows staged
+    (16, 3000, 1032),
+    (8, 2000, 4104),
+    (9, 1000, 4104),
+    (5, 300, 14336),
+    (16, 100, 65544),
+    (2, 17, 8),
+    (4000, 12, 520),
+    (600, 16, 1032),
+    (300, 3, 4104),
 ]
 
 
@@ -102,7 +113,7 @@ def test_decode_batch_workload(env):
 def test_skinny_closed_form_and_guard(env):
     """Rank-1 inputs give exact products; nothing outside D is written."""
     torch, gt, dev = env
-    for M, N, K in [(7, 3000, 4104), (3000, 7, 4104)]:
+    for M, N, K in [(7, 3000, 4104), (3000, 7, 4104), (7, 500, 4104), (500, 7, 1032)]:
         u = np.array([0.25, -0.5, 1.0, 2.0, -1.0, 0.5, -2.0], np.float16)
         v = np.array([0.5, -1.0, 2.0, -0.25], np.float16)
         a = u[np.arange(M) % 7]
