@@ -93,7 +93,8 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   // +0 is the all-zero pattern in both formats.
   if (K == 0) return to_status(gt::launch_fill_zero_f16(D, M * N, s));
   const bool skinny = M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows;
-  if (variant >= gt::kGemmVariants) {
+  const int ws_first = gt::kGemmVariants + gt::kSkinnyVariants;
+  if (variant >= gt::kGemmVariants && variant < ws_first) {
     if (!skinny) return GEMVTILE_ERR_UNSUPPORTED;
     if (gt::skinny_variant_q8(variant - gt::kGemmVariants) && (M < N ? M : N) > 8) return GEMVTILE_ERR_UNSUPPORTED;
   }
@@ -101,6 +102,8 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   st = current_cu_count(&cus);
   if (st != GEMVTILE_OK) return st;
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  // Variants from ws_first run the wave-specialised kernel, whatever the shape.
+  if (variant >= ws_first) return to_status(gt::launch_gemm_ws_f16(variant - ws_first, A, B, D, m, n, k, cus, s));
   // Variants kGemmVariants.. force skinny launch shapes (f16 only).
   if (variant >= gt::kGemmVariants)
     return to_status(gt::launch_gemm_skinny_f16(variant - gt::kGemmVariants, A, B, D, m, n, k, cus, s));
@@ -159,7 +162,8 @@ int gemv_bf16(const void *x, const void *W, void *y, int64_t N, int64_t K, void 
 
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream,
                               int variant) {
-  if (variant < 0 || variant >= gt::kGemmVariants + gt::kSkinnyVariants) return GEMVTILE_ERR_INVALID_ARG;
+  if (variant < 0 || variant >= gt::kGemmVariants + gt::kSkinnyVariants + gt::kGemmWsVariants)
+    return GEMVTILE_ERR_INVALID_ARG;
   return run_gemm(A, B, D, M, N, K, stream, variant);
 }
 

@@ -101,6 +101,22 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait until at most `younger` K tiles of PER loads each are still pending
+// (loads complete in issue order); `younger` is in [0, MAXY].  vmcnt takes
+// an immediate, hence the unrolled choice.
+template <int PER, int MAXY>
+__device__ inline void wait_younger(int younger) {
+  if constexpr (MAXY > 0) {
+    if (younger >= MAXY) {
+      wait_vmcnt<MAXY * PER>();
+      return;
+    }
+    wait_younger<PER, MAXY - 1>(younger);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 // Wait until all LDS reads and writes of this wave have completed.
 __device__ inline void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 

@@ -26,6 +26,9 @@ constexpr int kGemvVariants = 13;
 // kernel (skinny.hip); it has kSkinnyVariants launch shapes.
 constexpr int kSkinnyMaxRows = 16;
 constexpr int kSkinnyVariants = 40;
+// Wave-specialised (producer / consumer) GEMM launch shapes (gemm_ws.hip),
+// numbered after the skinny ones.
+constexpr int kGemmWsVariants = 2;
 // Skinny launch shapes that stage only 8 rows of the small side (valid for
 // min(M,N) <= 8 only).
 inline bool skinny_variant_q8(int v) {
@@ -75,6 +78,8 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
                                   int num_cus, hipStream_t stream);
 hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, int num_cus,
                            hipStream_t stream);
+hipError_t launch_gemm_ws_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
+                              hipStream_t stream);
 hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream);
 // bf16 operands and results: the default launch shape of each kernel.
 hipError_t launch_gemm_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,

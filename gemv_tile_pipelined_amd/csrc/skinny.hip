@@ -95,21 +95,6 @@ gemm_skinny_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ 
   }
 }
 
-// Wait until at most `younger` K tiles of PER loads each are still pending
-// (loads complete in issue order); `younger` is in [0, MAXY].
-template <int PER, int MAXY>
-__device__ inline void wait_younger(int younger) {
-  if constexpr (MAXY > 0) {
-    if (younger >= MAXY) {
-      wait_vmcnt<MAXY * PER>();
-      return;
-    }
-    wait_younger<PER, MAXY - 1>(younger);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
 // LDS-staged variant: both operands go through a STAGES-deep LDS ring of K
 // tiles of BK = 512 (1 KiB per row), filled by direct-to-LDS loads in which
 // one wave instruction moves one whole 1 KiB row segment (the register

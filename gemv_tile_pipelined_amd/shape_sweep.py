@@ -2,7 +2,8 @@
 
     rocprofv3 --kernel-trace --output-format csv -d OUT -o sweep -- \\
         python3 -m gemv_tile_pipelined_amd.shape_sweep [--gemv N:K,...] [--skinny M:N:K,...]
-            [--gemv-variants 0,8] [--skinny-variants 0,25] [--vendor] [--reps 40] > OUT/log.txt
+            [--gemm M:N:K,...] [--gemv-variants 0,8] [--skinny-variants 0,25]
+            [--gemm-variants 0,53] [--vendor] [--reps 40] > OUT/log.txt
     python3 -m gemv_tile_pipelined_amd.shape_sweep --parse OUT OUT/log.txt
 
 The first command launches, for every shape, `reps` GEMVs (gemv_f16, one
@@ -10,7 +11,9 @@ line per launch shape in --gemv-variants) or decode-batch GEMMs (gemm_f16,
 one line per gemvtile_gemm_f16_variant id in --skinny-variants)
 over enough distinct copies of W / B (at least 600 MB in all) that each
 launch reads its matrix from HBM rather than the 256 MB MALL; with --vendor
-also torch.mv on the same GEMV inputs.  Segments are delimited in the trace
+also torch.mv / torch.matmul on the same inputs.  --gemm shapes run the
+compute-bound GEMM (gemm_f16 through each id in --gemm-variants) over 3
+rotating input sets and report TFLOP/s (2·M·N·K flops).  Segments are delimited in the trace
 by a marker kernel (a bitwise not of one int8), and the last stdout line
 lists the segments.  The second command reads the trace and prints each
 segment's median kernel time and algorithmic bandwidth
@@ -106,6 +109,17 @@ def run(a):
             segment({"kind": "torch.matmul", "M": M, "N": N, "K": K, "bytes": 2 * (M * K + N * K + M * N)},
                     lambda i: torch.matmul(A, Bs[i].t(), out=D), c)
         del Bs
+    gemm_variants = [int(v) for v in a.gemm_variants.split(",")]
+    for M, N, K in _shapes(a.gemm, 3):
+        sets = [(uni((M, K), -1, 1), uni((N, K), -1, 1)) for _ in range(3)]
+        D = torch.empty((M, N), dtype=torch.float16, device=dev)
+        for v in gemm_variants:
+            segment({"kind": "gemm_f16", "M": M, "N": N, "K": K, "variant": v, "flops": 2 * M * N * K},
+                    lambda i, v=v: gt.gemm_f16(sets[i][0], sets[i][1], D, variant=v), 3)
+        if a.vendor:
+            segment({"kind": "torch.matmul", "M": M, "N": N, "K": K, "flops": 2 * M * N * K},
+                    lambda i: torch.matmul(sets[i][0], sets[i][1].t(), out=D), 3)
+        del sets
     print("SEGMENTS " + json.dumps(labels), flush=True)
 
 
@@ -127,11 +141,15 @@ def parse(trace_dir, log_path):
         durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[lo + 1 : hi]]
         names = sorted({r["Kernel_Name"].split("(")[0][:60] for r in rows[lo + 1 : hi]})
         med = statistics.median(durs) / 1e3
-        gbps = lab["bytes"] / (med * 1e3)
         shape = "x".join(str(lab[k]) for k in ("M", "N", "K") if k in lab)
         var = f" v{lab['variant']}" if "variant" in lab else ""
-        print(f"{lab['kind']:13s}{var:4s} {shape:18s} n={len(durs):3d} median {med:8.2f} us "
-              f"{gbps:6.0f} GB/s ({gbps / 80:5.1f} % of 8 TB/s)  {'; '.join(names)}")
+        if "flops" in lab:
+            tf = lab["flops"] / (med * 1e6)
+            rate = f"{tf:6.0f} TFLOP/s ({tf / 25:5.1f} % of 2.5 PFLOP/s)"
+        else:
+            gbps = lab["bytes"] / (med * 1e3)
+            rate = f"{gbps:6.0f} GB/s ({gbps / 80:5.1f} % of 8 TB/s)"
+        print(f"{lab['kind']:13s}{var:4s} {shape:18s} n={len(durs):3d} median {med:8.2f} us {rate}  {'; '.join(names)}")
 
 
 def main(argv=None):
@@ -140,6 +158,8 @@ def main(argv=None):
     p.add_argument("--skinny", default=DEFAULT_SKINNY, help="M:N:K,... (empty for none)")
     p.add_argument("--gemv-variants", default="0")
     p.add_argument("--skinny-variants", default="0")
+    p.add_argument("--gemm", default="", help="M:N:K,... compute-bound GEMM shapes (default none)")
+    p.add_argument("--gemm-variants", default="0")
     p.add_argument("--vendor", action="store_true")
     p.add_argument("--reps", type=int, default=40)
     p.add_argument("--parse", nargs=2, metavar=("TRACE_DIR", "LOG"))

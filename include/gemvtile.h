@@ -207,6 +207,10 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *      (8,16,8), (4,16,4), (4,16,2), (4,16,1), (8,8,8), (4,8,4), (4,8,2),
  *      (4,8,1), and (8,8,16) with 6 stages (the 8-row stagings need
  *      min(M,N) <= 8)
+ *   53, 54 the wave-specialised kernel, whatever the shape: 256x128 output
+ *      tiles, 4 consumer waves (MFMA only, 128x64 each) and 4 loader waves
+ *      (tile loads only) handing K tiles over at one barrier per K tile,
+ *      with a 3-stage (53) or 2-stage (54) LDS ring
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
