@@ -94,14 +94,21 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   if (K == 0) return to_status(gt::launch_fill_zero_f16(D, M * N, s));
   const bool skinny = M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows;
   const int ws_first = gt::kGemmVariants + gt::kSkinnyVariants;
+  const int wp_first = ws_first + gt::kGemmWsVariants;
   if (variant >= gt::kGemmVariants && variant < ws_first) {
     if (!skinny) return GEMVTILE_ERR_UNSUPPORTED;
     if (gt::skinny_variant_q8(variant - gt::kGemmVariants) && (M < N ? M : N) > 8) return GEMVTILE_ERR_UNSUPPORTED;
+  }
+  if (variant >= wp_first) {
+    if (!skinny) return GEMVTILE_ERR_UNSUPPORTED;
+    if (gt::skinny_wp_variant_q8(variant - wp_first) && (M < N ? M : N) > 8) return GEMVTILE_ERR_UNSUPPORTED;
   }
   int cus = 0;
   st = current_cu_count(&cus);
   if (st != GEMVTILE_OK) return st;
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  // Variants from wp_first force wave-private skinny launch shapes (f16 only).
+  if (variant >= wp_first) return to_status(gt::launch_gemm_skinny_wp_f16(variant - wp_first, A, B, D, m, n, k, s));
   // Variants from ws_first run the wave-specialised kernel, whatever the shape.
   if (variant >= ws_first) return to_status(gt::launch_gemm_ws_f16(variant - ws_first, A, B, D, m, n, k, cus, s));
   // Variants kGemmVariants.. force skinny launch shapes (f16 only).
@@ -162,7 +169,8 @@ int gemv_bf16(const void *x, const void *W, void *y, int64_t N, int64_t K, void 
 
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream,
                               int variant) {
-  if (variant < 0 || variant >= gt::kGemmVariants + gt::kSkinnyVariants + gt::kGemmWsVariants)
+  constexpr int kVariants = gt::kGemmVariants + gt::kSkinnyVariants + gt::kGemmWsVariants + gt::kSkinnyWpVariants;
+  if (variant < 0 || variant >= kVariants)
     return GEMVTILE_ERR_INVALID_ARG;
   return run_gemm(A, B, D, M, N, K, stream, variant);
 }

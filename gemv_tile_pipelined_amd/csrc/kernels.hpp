@@ -29,6 +29,10 @@ constexpr int kSkinnyVariants = 40;
 // Wave-specialised (producer / consumer) GEMM launch shapes (gemm_ws.hip),
 // numbered after the skinny ones.
 constexpr int kGemmWsVariants = 2;
+// Wave-private skinny launch shapes (skinny.hip), numbered after those;
+// skinny_wp_variant_q8: the ones that stage 8 small-side rows (min(M,N) <= 8).
+constexpr int kSkinnyWpVariants = 12;
+inline bool skinny_wp_variant_q8(int v) { return (v >= 4 && v <= 6) || v == 9 || v == 10; }
 // Skinny launch shapes that stage only 8 rows of the small side (valid for
 // min(M,N) <= 8 only).
 inline bool skinny_variant_q8(int v) {
@@ -78,6 +82,8 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
                                   int num_cus, hipStream_t stream);
 hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, int num_cus,
                            hipStream_t stream);
+hipError_t launch_gemm_skinny_wp_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K,
+                                     hipStream_t stream);
 hipError_t launch_gemm_ws_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                               hipStream_t stream);
 hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream);

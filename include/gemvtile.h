@@ -187,7 +187,7 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *   13..52 the skinny kernel (only for M <= 16 or N <= 16, else
  *      GEMVTILE_ERR_UNSUPPORTED).  13: the gemm_f16 choice (16, 8, 4, 2 or
  *      1 rows of the large side per workgroup, see gemvtile_gemm_grid; at 16
- *      rows the rotated launch 43).
+ *      rows launch 62).
  *      14..16: operands staged through an LDS ring of 1 KiB row segments,
  *      16 large-side rows per workgroup, (waves per workgroup, ring stages)
  *      = (8,4), (8,3), (4,4).  17..21: operands loaded into registers,
@@ -211,6 +211,18 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *      tiles, 4 consumer waves (MFMA only, 128x64 each) and 4 loader waves
  *      (tile loads only) handing K tiles over at one barrier per K tile,
  *      with a 3-stage (53) or 2-stage (54) LDS ring
+ *   55..66 further skinny launch shapes (only for M <= 16 or N <= 16).
+ *      55..61: wave-private rings, each wave walking its own run of K tiles
+ *      of 64 through its own LDS ring and waiting only for its own loads;
+ *      (waves, stages, large-side rows per workgroup, small-side rows
+ *      staged, rotated runs) = (8,4,16,16,yes), (8,4,16,16,no),
+ *      (4,8,16,16,yes), (8,4,8,16,yes), (8,6,16,8,yes), (8,8,8,8,yes),
+ *      (16,2,16,8,yes).  62..66: the large side loaded non-temporally:
+ *      62 = 43 [the gemm_f16 choice at 16 rows], 63 = 55, 64 = the
+ *      workgroup ring with (waves, stages, small rows, large rows) =
+ *      (8,4,8,8) [the gemm_f16 choice at 8 rows when min(M,N) <= 8],
+ *      65 = (4,4,8,4), 66 = (8,4,16,8).  The 8-row stagings (59..61, 64,
+ *      65) need min(M,N) <= 8
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,

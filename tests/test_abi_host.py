@@ -86,7 +86,9 @@ def test_gemm_argument_validation(lib):
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 22) == UNSUPPORTED
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 33) == UNSUPPORTED
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 30) == UNSUPPORTED
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 8, 4096, 8, None, 55) == INVALID
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 55) == UNSUPPORTED
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 59) == UNSUPPORTED
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 8, 4096, 8, None, 67) == INVALID
 
 
 def test_gemv_argument_validation(lib):

@@ -18,7 +18,9 @@ pytestmark = pytest.mark.gpu
 TOL_ABS = 1e-2
 TOL_REL = 1e-2
 
-SKINNY_VARIANTS = range(13, 53)  # gemvtile_gemm_f16_variant ids of the skinny launch shapes
+# gemvtile_gemm_f16_variant ids of the skinny launch shapes: workgroup-ring
+# kernels 13..52, wave-private kernels 55..61
+SKINNY_VARIANTS = list(range(13, 53)) + list(range(55, 67))
 
 
 @pytest.fixture(scope="module")
@@ -94,7 +96,9 @@ def test_skinny_integer_exact(env, shape):
 
 
 @pytest.mark.parametrize("variant", SKINNY_VARIANTS)
-@pytest.mark.parametrize("shape", [(8, 1000, 14344), (1000, 8, 1032)], ids=["small_m", "small_n"])
+@pytest.mark.parametrize(
+    "shape", [(8, 1000, 14344), (1000, 8, 1032), (5, 300, 72)], ids=["small_m", "small_n", "k_fewer_tiles_than_waves"]
+)
 def test_skinny_variants_exact(env, shape, variant):
     M, N, K = shape
     A = datagen.integer_f16(3200, 0, (M, K))
