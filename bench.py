@@ -44,12 +44,12 @@ GEMV_COPIES = 5
 # valid only for the kernel sources whose SHA-256 is recorded here; the
 # summary and commands are in profiles/traffic_fetch_write_size.md.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "33948a8388ca561df95bdd1915f108fd300fe4c793553be8ae483fc7b12e33ff",
-    "gemm": {"fetch_kib": 98437.5 * 2.0, "write_kib": 32768.0 * 1.0},
-    "gemv": {"fetch_kib": 57481.3 * 2.0, "write_kib": 8.0 * 1.0},
+    "sources_sha256": "630db6f0b509f8397d77b861705a5e100780af60a1fc72ffbfcef69bca20ce04",
+    "gemm": {"fetch_kib": 98437.6 * 2.0, "write_kib": 32768.0 * 1.0},
+    "gemv": {"fetch_kib": 57475.2 * 2.0, "write_kib": 8.0 * 1.0},
     "decode": {"fetch_kib": 58265.3 * 2.0, "write_kib": 64.0 * 1.0},
-    "gemm_bf16": {"fetch_kib": 98437.0 * 2.0, "write_kib": 32768.0 * 1.0},
-    "gemv_bf16": {"fetch_kib": 57481.9 * 2.0, "write_kib": 8.0 * 1.0},
+    "gemm_bf16": {"fetch_kib": 98437.2 * 2.0, "write_kib": 32768.0 * 1.0},
+    "gemv_bf16": {"fetch_kib": 57480.2 * 2.0, "write_kib": 8.0 * 1.0},
 }
 KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemv.hip", "kernels.hpp", "skinny.hip", "tile_order.hpp")
 
@@ -206,6 +206,11 @@ def main():
 
     gemm_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     gemv_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+
+    def us_stats(ms, per=1):
+        us = np.asarray(ms) * 1e3 / per
+        return {"mean": round(float(us.mean()), 2), "median": round(float(np.median(us)), 2),
+                "min": round(float(us.min()), 2), "p90": round(float(np.percentile(us, 90)), 2)}
     gemm_s = float(gemm_ms.mean()) / 1e3
     gemv_s = float(gemv_ms.mean()) / 1e3 / GEMV_COPIES
     flops = metrics.gemm_flops(M, N, K)
@@ -279,6 +284,18 @@ def main():
     gemv_bf16_gbps = gemv_bytes / gemv_bf16_s / 1e9
     del gemv_b, Wb, Ab, Bb, Db
 
+    # The part's own compute peak, for context next to the published one the
+    # rooflines use: dense fp16 MFMA = CUs x 4096 flop per clock at the peak
+    # engine clock (the published 2.5 PFLOP/s is 256 CUs x 4096 x 2.4 GHz).
+    # The memory clock the runtime reports does not give the HBM3E data rate
+    # (2 GHz x 8192 bits x 2 is half of it), so HBM uses the published peak.
+    caps = gt.device_caps()
+    device = {
+        **caps,
+        "fp16_mfma_peak_from_clock_tflops": round(caps["num_cus"] * 4096 * caps["clock_khz"] * 1e3 / 1e12, 1),
+        "peaks_used": "published: 2500 TFLOP/s dense fp16/bf16, 8000 GB/s HBM",
+    }
+
     cpu = cpu_baseline(args.cpu_seconds)
 
     def traffic(kind):
@@ -321,11 +338,13 @@ def main():
             "traffic": traffic("gemm"),
             "kernel": "gemm_kernel",
             "us_per_launch": round(gemm_s * 1e6, 2),
+            "us_stats": us_stats(gemm_ms),
         },
         "gemv": {
             "value": round(gemv_gbps, 1),
             "unit": "GB/s",
             "us_per_launch": round(gemv_s * 1e6, 2),
+            "us_stats": us_stats(gemv_ms, GEMV_COPIES),
             "roofline": {
                 "bound": "hbm",
                 "achieved": round(gemv_gbps, 1),
@@ -365,6 +384,7 @@ def main():
             "gemm_traffic": traffic("gemm_bf16"),
             "gemv_traffic": traffic("gemv_bf16"),
         },
+        "device": device,
         "cpu_baseline": cpu,
         "context": "pages' figures (other hardware, BF16 GEMM): 36.13 TFLOP/s at 4096^3 on an SM120 GeForce; "
         "GEMV 695 GB/s (torch.compile) and 708 GB/s (best TileLang) on an RTX A6000",

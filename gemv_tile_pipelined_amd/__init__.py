@@ -37,6 +37,8 @@ __all__ = [
     "gemm_config",
     "gemm_grid",
     "gemv_grid",
+    "device_caps",
+    "read_stream",
 ]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemvtile.so")
@@ -52,6 +54,8 @@ EXPORTED_SYMBOLS = (
     "gemvtile_gemm_config",
     "gemvtile_gemm_grid",
     "gemvtile_gemv_grid",
+    "gemvtile_device_caps",
+    "gemvtile_read_stream",
     "gemvtile_gemm_f16_variant",
     "gemvtile_gemv_f16_variant",
     "gemvtile_xcd_logical_id",
@@ -116,6 +120,10 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemvtile_gemm_grid.restype = i64
     lib.gemvtile_gemv_grid.argtypes = [i64, i64]
     lib.gemvtile_gemv_grid.restype = i64
+    lib.gemvtile_device_caps.argtypes = [intp] * 4
+    lib.gemvtile_device_caps.restype = c_int
+    lib.gemvtile_read_stream.argtypes = [vp, i64, c_int, c_int, vp, vp]
+    lib.gemvtile_read_stream.restype = c_int
     if path == LIBRARY_PATH:
         _lib = lib
     return lib
@@ -265,6 +273,22 @@ def gemv_bf16(x, W, y=None, stream=None):
     return _gemv(x, W, y, stream, _torch().bfloat16, load_library().gemv_bf16)
 
 
+def read_stream(buf, sink, policy: int = 1, blocks: int = 256, stream=None):
+    """Measurement only: stream all bytes of the device tensor `buf` with the
+    read-only probe kernel (policy 0 none, 1 nt, 2 sc1 nt, 3 sc0 nt); `sink`
+    is a device tensor of at least `blocks` 32-bit words."""
+    torch = _torch()
+    if not (buf.is_cuda and sink.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf and sink must be contiguous device tensors")
+    if sink.numel() * sink.element_size() < 4 * blocks:
+        raise ValueError("sink must hold at least `blocks` 32-bit words")
+    s = _stream_handle(buf, stream)
+    with torch.cuda.device(buf.device):
+        st = load_library().gemvtile_read_stream(buf.data_ptr(), buf.numel() * buf.element_size(), policy, blocks,
+                                                 sink.data_ptr(), s)
+    _check(st)
+
+
 def gemm_f16_variant(A, B, variant: int, D=None, stream=None):
     """gemm_f16 through an internal kernel variant (measurement only)."""
     return gemm_f16(A, B, D, stream, variant)
@@ -299,3 +323,12 @@ def gemm_grid(M: int, N: int, num_cus: int) -> int:
 
 def gemv_grid(N: int, num_cus: int) -> int:
     return int(load_library().gemvtile_gemv_grid(N, num_cus))
+
+
+def device_caps() -> dict:
+    """Compute units, peak engine clock and memory clock (kHz) and memory bus
+    width (bits) of the current device."""
+    vals = [ctypes.c_int() for _ in range(4)]
+    _check(load_library().gemvtile_device_caps(*[ctypes.byref(v) for v in vals]))
+    keys = ("num_cus", "clock_khz", "mem_clock_khz", "mem_bus_bits")
+    return {k: v.value for k, v in zip(keys, vals)}

@@ -215,6 +215,23 @@ void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, 
   if (group_m) *group_m = gt::kGemmGroupM;
 }
 
+int gemvtile_device_caps(int *num_cus, int *clock_khz, int *mem_clock_khz, int *mem_bus_bits) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMVTILE_ERR_DEVICE;
+  const struct {
+    int *out;
+    hipDeviceAttribute_t attr;
+  } q[] = {{num_cus, hipDeviceAttributeMultiprocessorCount},
+           {clock_khz, hipDeviceAttributeClockRate},
+           {mem_clock_khz, hipDeviceAttributeMemoryClockRate},
+           {mem_bus_bits, hipDeviceAttributeMemoryBusWidth}};
+  for (const auto &e : q) {
+    if (e.out == nullptr) continue;
+    if (hipDeviceGetAttribute(e.out, e.attr, dev) != hipSuccess) return GEMVTILE_ERR_DEVICE;
+  }
+  return GEMVTILE_OK;
+}
+
 int64_t gemvtile_gemv_grid(int64_t N, int64_t num_cus) {
   if (N <= 0 || num_cus <= 0 || num_cus > (int64_t{1} << 20)) return 0;
   return gt::gemv_default_grid(N, static_cast<int>(num_cus));

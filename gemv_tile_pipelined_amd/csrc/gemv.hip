@@ -99,7 +99,11 @@ __device__ inline void store_row_sums(const float (&acc)[ROWS], int lane, int64_
   if (lane < ROWS && row0 + lane < N) y[row0 + lane] = round_out<DT>(mine);
 }
 
-template <int ROWS, int WAVES, int UNROLL, bool NONTEMPORAL, bool ROTATE = false, int DT = kF16, int KSPLIT = 1>
+// WPOL >= 0: W is read with buffer loads carrying that cache-policy operand
+// (gfx950: 1 = sc0, 2 = nt, 16 = sc1; one descriptor per row, so the 32-bit
+// offsets cover any K) instead of global loads.
+template <int ROWS, int WAVES, int UNROLL, bool NONTEMPORAL, bool ROTATE = false, int DT = kF16, int KSPLIT = 1,
+          int WPOL = -1>
 __global__ void __launch_bounds__(WAVES * 64)
 gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Float16 *__restrict__ y, int N,
                 int K) {
@@ -126,12 +130,16 @@ gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Flo
   }
   const half8_t *xv = reinterpret_cast<const half8_t *>(x);
   const half8_t *wrow[ROWS];
+  __amdgpu_buffer_rsrc_t wrsrc[ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     // Rows past N re-read the last row (always valid memory); their sums
     // are never stored.
     const int64_t row = (row0 + r < N) ? row0 + r : static_cast<int64_t>(N) - 1;
     wrow[r] = reinterpret_cast<const half8_t *>(W + row * K);
+    if constexpr (WPOL >= 0)
+      wrsrc[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(W + row * K), 0,
+                                                   static_cast<int>(static_cast<uint32_t>(K) * 2u), 0x00020000);
   }
 
   float acc[ROWS];
@@ -151,8 +159,13 @@ gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Flo
       if (!guarded || c < c_end) {
         xs[u] = xv[c];
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r)
-          ws[u][r] = NONTEMPORAL ? __builtin_nontemporal_load(wrow[r] + c) : wrow[r][c];
+        for (int r = 0; r < ROWS; ++r) {
+          if constexpr (WPOL >= 0)
+            ws[u][r] = __builtin_bit_cast(
+                half8_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc[r], static_cast<uint32_t>(c) * 16u, 0, WPOL));
+          else
+            ws[u][r] = NONTEMPORAL ? __builtin_nontemporal_load(wrow[r] + c) : wrow[r][c];
+        }
       } else {
         xs[u] = half8_t{};
 #pragma unroll
@@ -203,11 +216,11 @@ gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Flo
   }
 }
 
-template <int ROWS, int WAVES, int UNROLL, bool NT, bool ROT = false, int DT = kF16, int KSPLIT = 1>
+template <int ROWS, int WAVES, int UNROLL, bool NT, bool ROT = false, int DT = kF16, int KSPLIT = 1, int WPOL = -1>
 static hipError_t launch(const void *x, const void *W, void *y, int N, int K, hipStream_t stream) {
   const int64_t rows_per_block = static_cast<int64_t>(ROWS) * WAVES / KSPLIT;
   const int64_t grid = (N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((gemv_kernel<ROWS, WAVES, UNROLL, NT, ROT, DT, KSPLIT>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemv_kernel<ROWS, WAVES, UNROLL, NT, ROT, DT, KSPLIT, WPOL>), dim3(static_cast<unsigned>(grid)),
                      dim3(WAVES * 64), 0, stream, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(W),
                      static_cast<_Float16 *>(y), N, K);
   return hipGetLastError();
@@ -245,6 +258,12 @@ hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, i
     case 10: return launch<2, 8, 4, true, true, kF16, 4>(x, W, y, N, K, stream);
     case 11: return launch<2, 8, 4, true, true, kF16, 8>(x, W, y, N, K, stream);
     case 12: return launch<1, 8, 4, true, true, kF16, 8>(x, W, y, N, K, stream);
+    // W through buffer loads with an explicit cache policy: nt, sc1 nt, sc0 nt, sc0 sc1 nt
+    case 13: return launch<2, 8, 4, true, true, kF16, 1, 2>(x, W, y, N, K, stream);
+    case 14: return launch<2, 8, 4, true, true, kF16, 1, 18>(x, W, y, N, K, stream);
+    case 15: return launch<2, 8, 4, true, true, kF16, 1, 3>(x, W, y, N, K, stream);
+    case 16: return launch<2, 8, 4, true, true, kF16, 1, 19>(x, W, y, N, K, stream);
+    case 17: return launch<2, 8, 4, true, false, kF16, 1, 18>(x, W, y, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }

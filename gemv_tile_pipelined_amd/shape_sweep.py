@@ -3,7 +3,7 @@
     rocprofv3 --kernel-trace --output-format csv -d OUT -o sweep -- \\
         python3 -m gemv_tile_pipelined_amd.shape_sweep [--gemv N:K,...] [--skinny M:N:K,...]
             [--gemm M:N:K,...] [--gemv-variants 0,8] [--skinny-variants 0,25]
-            [--gemm-variants 0,53] [--vendor] [--reps 40] > OUT/log.txt
+            [--gemm-variants 0,53] [--stream MB --stream-policies 1,2] [--vendor] [--reps 40] > OUT/log.txt
     python3 -m gemv_tile_pipelined_amd.shape_sweep --parse OUT OUT/log.txt
 
 The first command launches, for every shape, `reps` GEMVs (gemv_f16, one
@@ -13,7 +13,10 @@ over enough distinct copies of W / B (at least 600 MB in all) that each
 launch reads its matrix from HBM rather than the 256 MB MALL; with --vendor
 also torch.mv / torch.matmul on the same inputs.  --gemm shapes run the
 compute-bound GEMM (gemm_f16 through each id in --gemm-variants) over 3
-rotating input sets and report TFLOP/s (2·M·N·K flops).  Segments are delimited in the trace
+rotating input sets and report TFLOP/s (2·M·N·K flops).  --stream MB runs
+the read-only probe (gemvtile_read_stream, 256 workgroups) over that many MB
+per launch with each cache policy in --stream-policies: the practical read
+ceiling of the bandwidth-bound kernels.  Segments are delimited in the trace
 by a marker kernel (a bitwise not of one int8), and the last stdout line
 lists the segments.  The second command reads the trace and prints each
 segment's median kernel time and algorithmic bandwidth
@@ -109,6 +112,15 @@ def run(a):
             segment({"kind": "torch.matmul", "M": M, "N": N, "K": K, "bytes": 2 * (M * K + N * K + M * N)},
                     lambda i: torch.matmul(A, Bs[i].t(), out=D), c)
         del Bs
+    if a.stream > 0:
+        nbytes = int(a.stream * 1e6) // 16 * 16
+        c = copies_for(nbytes)
+        bufs = [uni((nbytes // 2,), -1, 1) for _ in range(c)]
+        sink = torch.zeros((256,), dtype=torch.int32, device=dev)
+        for pol in [int(v) for v in a.stream_policies.split(",")]:
+            segment({"kind": "read_stream", "policy": pol, "N": nbytes, "bytes": nbytes},
+                    lambda i, pol=pol: gt.read_stream(bufs[i], sink, pol, 256), c)
+        del bufs
     gemm_variants = [int(v) for v in a.gemm_variants.split(",")]
     for M, N, K in _shapes(a.gemm, 3):
         sets = [(uni((M, K), -1, 1), uni((N, K), -1, 1)) for _ in range(3)]
@@ -142,7 +154,7 @@ def parse(trace_dir, log_path):
         names = sorted({r["Kernel_Name"].split("(")[0][:60] for r in rows[lo + 1 : hi]})
         med = statistics.median(durs) / 1e3
         shape = "x".join(str(lab[k]) for k in ("M", "N", "K") if k in lab)
-        var = f" v{lab['variant']}" if "variant" in lab else ""
+        var = f" v{lab['variant']}" if "variant" in lab else (f" p{lab['policy']}" if "policy" in lab else "")
         if "flops" in lab:
             tf = lab["flops"] / (med * 1e6)
             rate = f"{tf:6.0f} TFLOP/s ({tf / 25:5.1f} % of 2.5 PFLOP/s)"
@@ -160,6 +172,8 @@ def main(argv=None):
     p.add_argument("--skinny-variants", default="0")
     p.add_argument("--gemm", default="", help="M:N:K,... compute-bound GEMM shapes (default none)")
     p.add_argument("--gemm-variants", default="0")
+    p.add_argument("--stream", type=float, default=0.0, help="MB per read-only probe launch (0: none)")
+    p.add_argument("--stream-policies", default="1,2")
     p.add_argument("--vendor", action="store_true")
     p.add_argument("--reps", type=int, default=40)
     p.add_argument("--parse", nargs=2, metavar=("TRACE_DIR", "LOG"))

@@ -140,6 +140,26 @@ int gemvtile_tile_coord(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t gro
 void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, int *group_m);
 
 /*
+ * gemvtile_device_caps -- the current device's compute-unit count, peak
+ * engine clock (kHz), peak memory clock (kHz) and memory bus width (bits),
+ * for recomputing the roofline peaks from the part itself.  Any output
+ * pointer may be NULL.  Returns GEMVTILE_ERR_DEVICE if a HIP query fails.
+ */
+int gemvtile_device_caps(int *num_cus, int *clock_khz, int *mem_clock_khz, int *mem_bus_bits);
+
+/*
+ * gemvtile_read_stream -- measurement only: a read-only kernel that streams
+ * `bytes` (1 .. 2^30) of device memory at p with 16-byte buffer loads
+ * (grid-stride, `blocks` workgroups of 512 threads, 1 .. 4096) and the cache
+ * policy `policy` (0 none, 1 nt, 2 sc1 nt, 3 sc0 nt).  It computes nothing
+ * and writes at most one word per workgroup into `sink` (device memory of at
+ * least `blocks` words), only under an impossible condition.  It gives the
+ * practical HBM read ceiling that the GEMV's roofline fraction is read
+ * against.  Returns GEMVTILE_ERR_INVALID_ARG for arguments out of range.
+ */
+int gemvtile_read_stream(const void *p, int64_t bytes, int policy, int blocks, void *sink, void *stream);
+
+/*
  * gemvtile_gemv_grid -- the number of workgroups gemv_f16 (and gemv_bf16)
  * launches for N rows on a device with `num_cus` compute units: ceil(N/R)
  * with R = 16 rows per workgroup when N >= 16*num_cus, else 8, 4 or 2 rows

@@ -240,3 +240,15 @@ def test_gemv_grid_gives_every_cu_a_workgroup(lib):
             # workgroup with N >= rows * cus, else 1
             rows = next((r for r in (16, 8, 4, 2) if N >= r * cus), 1)
             assert g == -(-N // rows)
+
+
+def test_read_stream_argument_validation(lib):
+    """The measurement-only read probe rejects bad arguments before any HIP call."""
+    rs = lib.gemvtile_read_stream
+    assert rs(None, 1024, 1, 256, FAKE, None) == INVALID
+    assert rs(FAKE, 0, 1, 256, FAKE, None) == INVALID
+    assert rs(FAKE, (1 << 30) + 16, 1, 256, FAKE, None) == INVALID
+    assert rs(FAKE, 1024, 4, 256, FAKE, None) == INVALID
+    assert rs(FAKE, 1024, 1, 0, FAKE, None) == INVALID
+    assert rs(FAKE, 1024, 1, 4097, FAKE, None) == INVALID
+    assert rs(FAKE, 1024, 1, 256, None, None) == INVALID

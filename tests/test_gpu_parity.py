@@ -271,7 +271,7 @@ def test_gemm_variants_bit_identical(env, variant):
     assert np.array_equal(_gemm(env, A, B, variant).cpu().numpy(), base)
 
 
-@pytest.mark.parametrize("variant", list(range(1, 13)))
+@pytest.mark.parametrize("variant", list(range(1, 18)))
 def test_gemv_variants_bit_identical(env, variant):
     N, K = 1031, 14344
     x = datagen.integer_f16(6001, 0, (K,))
@@ -305,3 +305,16 @@ def test_misaligned_pointer_is_rejected(env):
     with pytest.raises(gt.GemvTileError) as e:
         gt.gemm_f16(A, B)
     assert e.value.status == 2
+
+
+def test_read_stream_probe_writes_nothing(env):
+    """The read-ceiling probe only reads: the buffer and the sink are unchanged."""
+    torch, gt, dev = env
+    buf = torch.arange(1 << 20, dtype=torch.int32, device=dev)
+    before = buf.clone()
+    sink = torch.zeros((256,), dtype=torch.int32, device=dev)
+    for policy in range(4):
+        gt.read_stream(buf, sink, policy, 256)
+    torch.cuda.synchronize(dev)
+    assert torch.equal(buf, before)
+    assert bool((sink == 0).all())
