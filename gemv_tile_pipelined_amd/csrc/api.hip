@@ -82,6 +82,23 @@ int check_gemv(const void *x, const void *W, const void *y, int64_t N, int64_t K
 
 int to_status(hipError_t e) { return e == hipSuccess ? GEMVTILE_OK : GEMVTILE_ERR_LAUNCH; }
 
+// The kernel family and index of a gemvtile_gemm_f16_variant number.
+enum class Family { kTiled, kSkinny, kSkinnyExtra, kWs, kInvalid };
+struct VariantRef {
+  Family family;
+  int index;
+};
+VariantRef classify_variant(int variant) {
+  if (variant >= 0 && variant < gt::kGemmVariants) return {Family::kTiled, variant};
+  if (variant >= gt::kSkinnyVariantBase && variant < gt::kSkinnyExtraBase)
+    return {Family::kSkinny, variant - gt::kSkinnyVariantBase};
+  if (variant >= gt::kSkinnyExtraBase && variant < gt::kSkinnyExtraBase + gt::kSkinnyWpVariants)
+    return {Family::kSkinnyExtra, variant - gt::kSkinnyExtraBase};
+  if (variant >= gt::kGemmWsVariantBase && variant < gt::kGemmWsVariantBase + gt::kGemmWsVariants)
+    return {Family::kWs, variant - gt::kGemmWsVariantBase};
+  return {Family::kInvalid, 0};
+}
+
 // dtype: gt::kF16 or gt::kBF16.  bf16 runs the default kernels only
 // (variant 0).
 int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream, int variant,
@@ -93,27 +110,23 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   // +0 is the all-zero pattern in both formats.
   if (K == 0) return to_status(gt::launch_fill_zero_f16(D, M * N, s));
   const bool skinny = M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows;
-  const int ws_first = gt::kGemmVariants + gt::kSkinnyVariants;
-  const int wp_first = ws_first + gt::kGemmWsVariants;
-  if (variant >= gt::kGemmVariants && variant < ws_first) {
+  const VariantRef v = classify_variant(variant);
+  if (v.family == Family::kInvalid) return GEMVTILE_ERR_INVALID_ARG;
+  if (v.family == Family::kSkinny || v.family == Family::kSkinnyExtra) {
     if (!skinny) return GEMVTILE_ERR_UNSUPPORTED;
-    if (gt::skinny_variant_q8(variant - gt::kGemmVariants) && (M < N ? M : N) > 8) return GEMVTILE_ERR_UNSUPPORTED;
-  }
-  if (variant >= wp_first) {
-    if (!skinny) return GEMVTILE_ERR_UNSUPPORTED;
-    if (gt::skinny_wp_variant_q8(variant - wp_first) && (M < N ? M : N) > 8) return GEMVTILE_ERR_UNSUPPORTED;
+    const bool q8 = v.family == Family::kSkinny ? gt::skinny_variant_q8(v.index) : gt::skinny_wp_variant_q8(v.index);
+    if (q8 && (M < N ? M : N) > 8) return GEMVTILE_ERR_UNSUPPORTED;
   }
   int cus = 0;
   st = current_cu_count(&cus);
   if (st != GEMVTILE_OK) return st;
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-  // Variants from wp_first force wave-private skinny launch shapes (f16 only).
-  if (variant >= wp_first) return to_status(gt::launch_gemm_skinny_wp_f16(variant - wp_first, A, B, D, m, n, k, s));
-  // Variants from ws_first run the wave-specialised kernel, whatever the shape.
-  if (variant >= ws_first) return to_status(gt::launch_gemm_ws_f16(variant - ws_first, A, B, D, m, n, k, cus, s));
-  // Variants kGemmVariants.. force skinny launch shapes (f16 only).
-  if (variant >= gt::kGemmVariants)
-    return to_status(gt::launch_gemm_skinny_f16(variant - gt::kGemmVariants, A, B, D, m, n, k, cus, s));
+  // Forced launch shapes of the skinny and wave-specialised families (f16
+  // only); the skinny ones apply to skinny shapes only.
+  if (v.family == Family::kSkinny)
+    return to_status(gt::launch_gemm_skinny_f16(v.index, A, B, D, m, n, k, cus, s));
+  if (v.family == Family::kSkinnyExtra) return to_status(gt::launch_gemm_skinny_wp_f16(v.index, A, B, D, m, n, k, s));
+  if (v.family == Family::kWs) return to_status(gt::launch_gemm_ws_f16(v.index, A, B, D, m, n, k, cus, s));
   if (variant == 0 && (M == 1 || N == 1)) {
     // One row on a side is the batch-1 product y = x·Wᵀ: M == 1 is
     // D[0][n] = A[0]·B[n] (x = A, W = B); N == 1 is D[m][0] = A[m]·B[0]
@@ -169,8 +182,7 @@ int gemv_bf16(const void *x, const void *W, void *y, int64_t N, int64_t K, void 
 
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream,
                               int variant) {
-  constexpr int kVariants = gt::kGemmVariants + gt::kSkinnyVariants + gt::kGemmWsVariants + gt::kSkinnyWpVariants;
-  if (variant < 0 || variant >= kVariants)
+  if (classify_variant(variant).family == Family::kInvalid)
     return GEMVTILE_ERR_INVALID_ARG;
   return run_gemm(A, B, D, M, N, K, stream, variant);
 }

@@ -186,8 +186,10 @@ __device__ inline void wait_tile_landed(int younger) {
   wait_vmcnt<0>();
 }
 
+// One wave per SIMD for 4 waves; with 8 waves two per SIMD, so each is held
+// to half the register file.
 template <class S>
-__global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWaves / 4, S::kWaves / 4)))
 gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
                 int M, int N, int K, int tiles_m, int tiles_n, int vec16) {
   __shared__ __attribute__((aligned(1024))) char smem[S::kLdsBytes];
@@ -335,12 +337,12 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       // and carry wait states: the zeros are materialised before them (and
       // cannot be re-created after them), so they precede every MFMA by at
       // least 16 wait states.
-      static_assert(S::kFragN == 8, "accumulator fence covers 8 blocks per row");
+      static_assert(S::kFragN % 4 == 0, "accumulator fence covers 4 blocks per statement");
 #pragma unroll
       for (int i = 0; i < S::kFragM; ++i)
-        asm volatile("s_nop 1"
-                     : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
-                       "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+#pragma unroll
+        for (int j = 0; j < S::kFragN; j += 4)
+          asm volatile("s_nop 1" : "+a"(acc[i][j]), "+a"(acc[i][j + 1]), "+a"(acc[i][j + 2]), "+a"(acc[i][j + 3]));
     }
 
     auto mfma = [&](int buf, int idx) {
@@ -629,6 +631,11 @@ using Gemm32x32 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1>;
 // The default shape with bf16 operands and results.
 using GemmBf16 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, kBF16>;
 using Gemm32x32OneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true, 1, 1>;
+// Eight waves (2 x 4 of 128x64, two per SIMD): each wave issues half the
+// refill loads, and its SIMD partner can issue MFMAs meanwhile; the price is
+// 1.5x the LDS operand reads per flop.
+using Gemm8Waves = GemmShape<256, 256, 64, 2, 2, 4, true, true, 4, 1, 1, 1, 0, 16, 2, 1>;
+using Gemm8WavesRefill2 = GemmShape<256, 256, 64, 2, 2, 4, true, true, 2, 1, 1, 1, 0, 16, 2, 1>;
 using Gemm32x32Bk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
 
 static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDefault::BK == kGemmBK &&
@@ -666,6 +673,8 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 10: return launch<Gemm32x32>(A, B, D, M, N, K, num_cus, stream);
     case 11: return launch<Gemm32x32Bk32FourStage>(A, B, D, M, N, K, num_cus, stream);
     case 12: return launch<GemmFusedLoads>(A, B, D, M, N, K, num_cus, stream);
+    case 13: return launch<Gemm8Waves>(A, B, D, M, N, K, num_cus, stream);
+    case 14: return launch<Gemm8WavesRefill2>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

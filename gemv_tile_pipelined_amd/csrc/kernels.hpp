@@ -20,18 +20,27 @@ constexpr int kGemmBK = 64;
 constexpr int kGemmStages = 2;
 constexpr int kGemmThreads = 256;
 constexpr int kGemmGroupM = 8;
-constexpr int kGemmVariants = 13;
+constexpr int kGemmVariants = 15;
 constexpr int kGemvVariants = 18;
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip); it has kSkinnyVariants launch shapes.
 constexpr int kSkinnyMaxRows = 16;
 constexpr int kSkinnyVariants = 40;
+// gemvtile_gemm_f16_variant numbers each kernel family from a fixed base so
+// that adding a launch shape to one family renumbers no other: tiled GEMM
+// 0.., skinny kSkinnyVariantBase.. (its kSkinnyVariants shapes, then the
+// kSkinnyWpVariants further ones), wave-specialised kGemmWsVariantBase...
+constexpr int kSkinnyVariantBase = 100;
+constexpr int kGemmWsVariantBase = 200;
 // Wave-specialised (producer / consumer) GEMM launch shapes (gemm_ws.hip),
 // numbered after the skinny ones.
 constexpr int kGemmWsVariants = 2;
 // Wave-private skinny launch shapes (skinny.hip), numbered after those;
 // skinny_wp_variant_q8: the ones that stage 8 small-side rows (min(M,N) <= 8).
 constexpr int kSkinnyWpVariants = 12;
+constexpr int kSkinnyExtraBase = kSkinnyVariantBase + kSkinnyVariants;
+static_assert(kGemmVariants <= kSkinnyVariantBase && kSkinnyExtraBase + kSkinnyWpVariants <= kGemmWsVariantBase,
+              "variant families must not overlap");
 inline bool skinny_wp_variant_q8(int v) { return (v >= 4 && v <= 6) || v == 9 || v == 10; }
 // Skinny launch shapes that stage only 8 rows of the small side (valid for
 // min(M,N) <= 8 only).

@@ -182,8 +182,9 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
 
 /*
  * gemvtile_gemm_f16_variant -- gemm_f16 with an internal kernel variant, for
- * ablation measurements only (same contract and results as gemm_f16).  All
- * use 256x256 output tiles and 4 waves of 128x128:
+ * ablation measurements only (same contract and results as gemm_f16).  The
+ * tiled ones use 256x256 output tiles and (but for 13, 14) 4 waves of
+ * 128x128:
  *   0  the default kernel (identical to gemm_f16): 16x16x32 MFMA blocks, K
  *      tiles of 64 in a 2-stage LDS ring, the next K step's operand reads one
  *      every 2 MFMA slots, a refill load every 4 slots, swizzled LDS,
@@ -201,48 +202,48 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *   12 as 0 with each tile load issued in one block with its slot's MFMA
  *      (M0 written before the MFMA, which serves as the wait state) rather
  *      than on its own (M0 write, wait state, load)
- * Variants 1..12 always run the tiled kernel, whatever the shape; variant
+ *   13 as 0 with 8 waves of 128x64 (2 x 4, two per SIMD, each issuing half
+ *      the refill loads)   14  as 13 with a refill load every 2 slots
+ * Variants 1..14 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
- * <= 16: the skinny kernel).
- *   13..52 the skinny kernel (only for M <= 16 or N <= 16, else
- *      GEMVTILE_ERR_UNSUPPORTED).  13: the gemm_f16 choice (16, 8, 4, 2 or
- *      1 rows of the large side per workgroup, see gemvtile_gemm_grid; at 16
- *      rows launch 62).
- *      14..16: operands staged through an LDS ring of 1 KiB row segments,
+ * <= 16: the skinny kernel).  Each other kernel family has its own range:
+ *   100..151 the skinny kernel (only for M <= 16 or N <= 16, else
+ *      GEMVTILE_ERR_UNSUPPORTED).  100: the gemm_f16 choice (16, 8, 4, 2
+ *      or 1 rows of the large side per workgroup, see gemvtile_gemm_grid; at
+ *      16 rows launch 147).
+ *      101..103: operands staged through an LDS ring of 1 KiB row segments,
  *      16 large-side rows per workgroup, (waves per workgroup, ring stages)
- *      = (8,4), (8,3), (4,4).  17..21: operands loaded into registers,
+ *      = (8,4), (8,3), (4,4).  104..108: operands loaded into registers,
  *      (waves, 32-wide K steps in flight per wave) = (8,4), (8,2), (8,8),
- *      (16,4), (4,8).  22..24: as 14.. with only 8 rows of the small side
+ *      (16,4), (4,8).  109..111: as 101.. with only 8 rows of the small side
  *      staged (min(M,N) <= 8, else GEMVTILE_ERR_UNSUPPORTED), (waves,
- *      stages) = (8,5), (8,6), (4,6).  25..31: LDS ring, 4 stages, 16
+ *      stages) = (8,5), (8,6), (4,6).  112..118: LDS ring, 4 stages, 16
  *      small-side rows staged, (waves, large-side rows per workgroup) =
- *      (16,16), (8,8), (4,4), (8,4), (4,2), (4,1), (1,1).  32..36: the same
- *      with 8 small-side rows staged (min(M,N) <= 8), (8,8), (4,4), (4,2),
- *      (4,1), (8,1).  37..42: deeper rings, (waves, stages, small-side rows
- *      staged, large-side rows per workgroup) = (8,6,16,8), (4,7,16,4),
- *      (8,8,8,8), (4,8,8,4), (4,12,8,4), (4,12,8,2) (the 8-row stagings need
- *      min(M,N) <= 8).  43..52: each workgroup starting its K walk at K tile
- *      (workgroup index mod K tiles), 4 stages, (waves, small-side rows,
- *      large-side rows) = (16,16,16) [the gemm_f16 choice at 16 rows],
- *      (8,16,8), (4,16,4), (4,16,2), (4,16,1), (8,8,8), (4,8,4), (4,8,2),
- *      (4,8,1), and (8,8,16) with 6 stages (the 8-row stagings need
- *      min(M,N) <= 8)
- *   53, 54 the wave-specialised kernel, whatever the shape: 256x128 output
- *      tiles, 4 consumer waves (MFMA only, 128x64 each) and 4 loader waves
- *      (tile loads only) handing K tiles over at one barrier per K tile,
- *      with a 3-stage (53) or 2-stage (54) LDS ring
- *   55..66 further skinny launch shapes (only for M <= 16 or N <= 16).
- *      55..61: wave-private rings, each wave walking its own run of K tiles
- *      of 64 through its own LDS ring and waiting only for its own loads;
- *      (waves, stages, large-side rows per workgroup, small-side rows
+ *      (16,16), (8,8), (4,4), (8,4), (4,2), (4,1), (1,1).  119..123: the
+ *      same with 8 small-side rows staged (min(M,N) <= 8), (8,8), (4,4),
+ *      (4,2), (4,1), (8,1).  124..129: deeper rings, (waves, stages,
+ *      small-side rows staged, large-side rows per workgroup) = (8,6,16,8),
+ *      (4,7,16,4), (8,8,8,8), (4,8,8,4), (4,12,8,4), (4,12,8,2) (the 8-row
+ *      stagings need min(M,N) <= 8).  130..139: each workgroup starting its
+ *      K walk at K tile (workgroup index mod K tiles), 4 stages, (waves,
+ *      small-side rows, large-side rows) = (16,16,16), (8,16,8), (4,16,4),
+ *      (4,16,2), (4,16,1), (8,8,8), (4,8,4), (4,8,2), (4,8,1), and (8,8,16)
+ *      with 6 stages (the 8-row stagings need min(M,N) <= 8).
+ *      140..146: wave-private rings, each wave walking its own run of K
+ *      tiles of 64 through its own LDS ring and waiting only for its own
+ *      loads; (waves, stages, large-side rows per workgroup, small-side rows
  *      staged, rotated runs) = (8,4,16,16,yes), (8,4,16,16,no),
  *      (4,8,16,16,yes), (8,4,8,16,yes), (8,6,16,8,yes), (8,8,8,8,yes),
- *      (16,2,16,8,yes).  62..66: the large side loaded non-temporally:
- *      62 = 43 [the gemm_f16 choice at 16 rows], 63 = 55, 64 = the
- *      workgroup ring with (waves, stages, small rows, large rows) =
- *      (8,4,8,8) [the gemm_f16 choice at 8 rows when min(M,N) <= 8],
- *      65 = (4,4,8,4), 66 = (8,4,16,8).  The 8-row stagings (59..61, 64,
- *      65) need min(M,N) <= 8
+ *      (16,2,16,8,yes).  147..151: the large side loaded non-temporally:
+ *      147 = 130 with nt [the gemm_f16 choice at 16 rows], 148 = 140 with
+ *      nt, 149 = the workgroup ring with (waves, stages, small rows, large
+ *      rows) = (8,4,8,8) [the gemm_f16 choice at 8 rows when min(M,N) <= 8],
+ *      150 = (4,4,8,4), 151 = (8,4,16,8).  The 8-row stagings (144..146,
+ *      149, 150) need min(M,N) <= 8
+ *   200, 201 the wave-specialised kernel, whatever the shape: 256x128
+ *      output tiles, 4 consumer waves (MFMA only, 128x64 each) and 4 loader
+ *      waves (tile loads only) handing K tiles over at one barrier per K
+ *      tile, with a 3-stage (200) or 2-stage (201) LDS ring
  * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,

@@ -77,18 +77,18 @@ def test_gemm_argument_validation(lib):
     # size limits
     assert _gemm(lib, FAKE, FAKE, FAKE, 4, 4, 4194304) == UNSUPPORTED
     assert _gemm(lib, FAKE, FAKE, FAKE, 2**31, 4, 8) == UNSUPPORTED
-    # unknown internal variant
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, 99) == INVALID
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, -1) == INVALID
+    # unknown internal variant: each family has its own id range (tiled 0..,
+    # skinny 100.., wave-specialised 200..); the gaps are invalid
+    for bad in (-1, 15, 99, 152, 199, 202, 1000):
+        assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, bad) == INVALID, bad
     # skinny launch shapes only apply when one side has at most 16 rows
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 13) == UNSUPPORTED
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 100) == UNSUPPORTED
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 117) == UNSUPPORTED
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 140) == UNSUPPORTED
     # the 8-row small-side stagings need min(M, N) <= 8
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 22) == UNSUPPORTED
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 33) == UNSUPPORTED
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 30) == UNSUPPORTED
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 55) == UNSUPPORTED
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 59) == UNSUPPORTED
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 8, 4096, 8, None, 67) == INVALID
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 109) == UNSUPPORTED
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 120) == UNSUPPORTED
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 144) == UNSUPPORTED
 
 
 def test_gemv_argument_validation(lib):

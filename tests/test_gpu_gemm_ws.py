@@ -1,6 +1,6 @@
 """Parity of the wave-specialised (producer / consumer) GEMM with the oracle.
 
-gemvtile_gemm_f16_variant 53 and 54 run gemm_ws.hip whatever the shape:
+gemvtile_gemm_f16_variant 200 and 201 run gemm_ws.hip whatever the shape:
 256x128 output tiles, 4 consumer waves that only read LDS and issue MFMAs, 4
 loader waves that only issue tile loads, one hand-off barrier per K tile, and
 a 3- or 2-stage LDS ring.  Same bar as the default kernel: bit-for-bit on
@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_ABS = 1e-2
 TOL_REL = 1e-2
-WS_VARIANTS = (53, 54)
+WS_VARIANTS = (200, 201)
 
 
 @pytest.fixture(scope="module")
