@@ -92,6 +92,13 @@ __device__ inline void lds_dma_b128(int4_t rsrc, uint32_t voffset, uint32_t lds_
                  : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
   }
 }
+// The same load with M0 already holding lds_base (written by set_m0 at
+// least one instruction earlier): the caller keeps M0 for its loads, so only
+// the load itself takes an issue slot.
+__device__ inline void lds_dma_b128_m0_set(int4_t rsrc, uint32_t voffset) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(rsrc) : "memory");
+}
+__device__ inline void set_m0(uint32_t lds_base) { asm volatile("s_mov_b32 m0, %0" : : "s"(lds_base) : "m0"); }
 #pragma clang diagnostic pop
 
 // Wait until at most N vector-memory operations of this wave are in flight.

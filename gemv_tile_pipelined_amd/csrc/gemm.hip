@@ -68,7 +68,8 @@ namespace gt {
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, bool SWIZZLE_, bool PERSISTENT_,
           int DMA_STRIDE_, int DMA_PHASES_, int K_STAGGER_ = 1, int K_STAGGER_STEP_ = 1, int LOAD_POLICY_ = 0,
-          int MI_ = 32, int READ_STRIDE_ = 1, int DMA_OFFSET_ = 0, bool FUSE_DMA_ = false, int DTYPE_ = kF16>
+          int MI_ = 32, int READ_STRIDE_ = 1, int DMA_OFFSET_ = 0, bool FUSE_DMA_ = false, int DTYPE_ = kF16,
+          bool PRESET_M0_ = false>
 struct GemmShape {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -109,6 +110,12 @@ struct GemmShape {
   // Element format of A, B and D (kF16 or kBF16; bf16 only with the
   // hand-written 16x16x32 MFMAs).
   static constexpr int DTYPE = DTYPE_;
+  // Refill loads of the K loop with M0 written for the next load right after
+  // each load (see dma_slot), instead of M0 write + wait state + load in the
+  // load's own slot.
+  static constexpr bool PRESET_M0 = PRESET_M0_;
+  static_assert(!PRESET_M0 || (DMA_PHASES_ == 1 && !FUSE_DMA_ && LOAD_POLICY_ == 0 && STAGES_ >= 2),
+                "M0 presetting is built for the plain single-phase refill");
   static_assert(DTYPE == kF16 || (DTYPE == kBF16 && MI_ == 16), "bf16 uses the 16x16x32 MFMA path");
   static_assert((BK / kKStep) >= 1 && (BM / WAVES_M / MI) * (BN / WAVES_N / MI) % READ_STRIDE == 0,
                 "the read spacing must divide the MFMA slots of a K step");
@@ -458,7 +465,19 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
 #pragma unroll
         for (int ph = 0; ph < S::DMA_PHASES; ++ph) {
           const int d = dma_at(pos, ph);
-          if (d >= 0 && (S::DMA_PHASES == 1 || phase == ph)) issue_loads(tile, d, d + 1);
+          if (d >= 0 && (S::DMA_PHASES == 1 || phase == ph)) {
+            if constexpr (S::PRESET_M0) {
+              // M0 already holds this load's LDS address.  The refill loads
+              // go out in the order (tile, 0..kDmaPerStage-1), (tile+1, 0),
+              // ..., so point M0 at the next one now; past the last refill
+              // the value is simply never used.
+              const DmaArgs g = dma_args(tile, d);
+              lds_dma_b128_m0_set(g.rsrc, g.voffset);
+              set_m0(d + 1 < S::kDmaPerStage ? dma_args(tile, d + 1).lds : dma_args(tile + 1, 0).lds);
+            } else {
+              issue_loads(tile, d, d + 1);
+            }
+          }
         }
       };
       auto ktile = [&](int kt, auto rest_c, auto early_c, auto next_c) {
@@ -531,6 +550,8 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       wait_tile_landed<S>(min(KT, S::STAGES - 1) - 1);
       workgroup_barrier();
       load_frags(0, 0, 0);
+      // The chain of refill loads starts with load 0 of K tile STAGES-1.
+      if constexpr (S::PRESET_M0) set_m0(dma_args(S::STAGES - 1, 0).lds);
       if (S::STAGES - 1 < KT) {
 #pragma unroll
         for (int pos = 0; pos < kAfter; ++pos) dma_slot(S::STAGES - 1, pos);
@@ -636,6 +657,11 @@ using Gemm32x32OneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true, 1, 1>;
 // 1.5x the LDS operand reads per flop.
 using Gemm8Waves = GemmShape<256, 256, 64, 2, 2, 4, true, true, 4, 1, 1, 1, 0, 16, 2, 1>;
 using Gemm8WavesRefill2 = GemmShape<256, 256, 64, 2, 2, 4, true, true, 2, 1, 1, 1, 0, 16, 2, 1>;
+// The default with M0 set one load ahead, and the same with a refill load
+// every 2 or every 3 slots.
+using GemmPresetM0 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, kF16, true>;
+using GemmPresetM0Refill2 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1, 1, 1, 0, 16, 2, 1, false, kF16, true>;
+using GemmPresetM0Refill3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 1, 1, 1, 0, 16, 2, 1, false, kF16, true>;
 using Gemm32x32Bk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
 
 static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDefault::BK == kGemmBK &&
@@ -675,6 +701,9 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 12: return launch<GemmFusedLoads>(A, B, D, M, N, K, num_cus, stream);
     case 13: return launch<Gemm8Waves>(A, B, D, M, N, K, num_cus, stream);
     case 14: return launch<Gemm8WavesRefill2>(A, B, D, M, N, K, num_cus, stream);
+    case 15: return launch<GemmPresetM0>(A, B, D, M, N, K, num_cus, stream);
+    case 16: return launch<GemmPresetM0Refill2>(A, B, D, M, N, K, num_cus, stream);
+    case 17: return launch<GemmPresetM0Refill3>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }
