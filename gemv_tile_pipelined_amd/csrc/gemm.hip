@@ -662,6 +662,11 @@ using Gemm8WavesRefill2 = GemmShape<256, 256, 64, 2, 2, 4, true, true, 2, 1, 1, 
 using GemmPresetM0 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, kF16, true>;
 using GemmPresetM0Refill2 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1, 1, 1, 0, 16, 2, 1, false, kF16, true>;
 using GemmPresetM0Refill3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 1, 1, 1, 0, 16, 2, 1, false, kF16, true>;
+// The default with a refill load every 3 MFMA slots, so the last one lands
+// further ahead of the barrier that waits for all of them.  (Every 1 or 2
+// slots, the compiler leaves the accumulators too few AGPRs and moves them
+// through scratch around each hand-written MFMA; build.py rejects that.)
+using GemmRefillEvery3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 1, 1, 1, 0, 16, 2, 1>;
 using Gemm32x32Bk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
 
 static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDefault::BK == kGemmBK &&
@@ -704,6 +709,7 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 15: return launch<GemmPresetM0>(A, B, D, M, N, K, num_cus, stream);
     case 16: return launch<GemmPresetM0Refill2>(A, B, D, M, N, K, num_cus, stream);
     case 17: return launch<GemmPresetM0Refill3>(A, B, D, M, N, K, num_cus, stream);
+    case 18: return launch<GemmRefillEvery3>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

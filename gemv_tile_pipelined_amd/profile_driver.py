@@ -6,7 +6,9 @@
     python -m gemv_tile_pipelined_amd.profile_driver copy [--mib S] [--iters I]
 
 `--bf16` runs gemm_bf16 / gemv_bf16 on bf16 inputs of the same shapes instead
-(default kernels only).
+(default kernels only).  For `gemm`, `--data zero|int` replaces the uniform
+operands (zeros, or integers in [-8, 8]: fewer active bits, less power) and
+`--vendor` runs torch.matmul on the same operands instead of the library.
 
 Meant to run under `rocprofv3 --pmc ...`: every dispatch of the chosen kernel
 then carries its counters.  `copy` runs a plain device-to-device copy of a
@@ -34,6 +36,8 @@ def main(argv=None):
     p.add_argument("--iters", type=int, default=10)
     p.add_argument("--mib", type=int, default=512)
     p.add_argument("--bf16", action="store_true")
+    p.add_argument("--data", choices=["uniform", "zero", "int"], default="uniform")
+    p.add_argument("--vendor", action="store_true")
     a = p.parse_args(argv)
 
     import torch
@@ -61,11 +65,21 @@ def main(argv=None):
 
     if a.kernel == "gemm":
         M, N, K = a.shape or (4096, 4096, 4096)
-        A = torch.empty((M, K), dtype=dt, device=dev).uniform_(-1, 1, generator=g)
-        B = torch.empty((N, K), dtype=dt, device=dev).uniform_(-1, 1, generator=g)
+
+        def operand(rows):
+            if a.data == "zero":
+                return torch.zeros((rows, K), dtype=dt, device=dev)
+            if a.data == "int":
+                return torch.randint(-8, 9, (rows, K), device=dev, generator=g).to(dt)
+            return torch.empty((rows, K), dtype=dt, device=dev).uniform_(-1, 1, generator=g)
+
+        A, B = operand(M), operand(N)
         D = torch.empty((M, N), dtype=dt, device=dev)
         for _ in range(a.iters):
-            gemm(A, B, D)
+            if a.vendor:
+                torch.matmul(A, B.t(), out=D)
+            else:
+                gemm(A, B, D)
     elif a.kernel == "decode":
         M, N, K = a.shape or (8, 4096, 14336)
         A = torch.empty((M, K), dtype=dt, device=dev).uniform_(-1, 1, generator=g)

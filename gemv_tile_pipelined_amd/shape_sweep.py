@@ -3,7 +3,8 @@
     rocprofv3 --kernel-trace --output-format csv -d OUT -o sweep -- \\
         python3 -m gemv_tile_pipelined_amd.shape_sweep [--gemv N:K,...] [--skinny M:N:K,...]
             [--gemm M:N:K,...] [--gemv-variants 0,8] [--skinny-variants 0,25]
-            [--gemm-variants 0,53] [--stream MB --stream-policies 1,2] [--vendor] [--reps 40] > OUT/log.txt
+            [--gemm-variants 0,53] [--gemm-data uniform,zero] [--rounds 1] [--warmup-s 1]
+            [--stream MB --stream-policies 1,2] [--vendor] [--reps 40] > OUT/log.txt
     python3 -m gemv_tile_pipelined_amd.shape_sweep --parse OUT OUT/log.txt
 
 The first command launches, for every shape, `reps` GEMVs (gemv_f16, one
@@ -13,7 +14,15 @@ over enough distinct copies of W / B (at least 600 MB in all) that each
 launch reads its matrix from HBM rather than the 256 MB MALL; with --vendor
 also torch.mv / torch.matmul on the same inputs.  --gemm shapes run the
 compute-bound GEMM (gemm_f16 through each id in --gemm-variants) over 3
-rotating input sets and report TFLOP/s (2·M·N·K flops).  --stream MB runs
+rotating input sets and report TFLOP/s (2·M·N·K flops); --gemm-data picks
+their values: uniform (U(-1,1) fp16, the default), m7 (the same with the
+fp16 mantissa cut to its top 7 bits, bf16's precision), int (integers in
+[-8, 8]) or zero, to show how the operands' bit activity moves the
+power-limited clock; --rounds repeats the variant list that many times,
+interleaved, so that a slow drift of the clock does not favour one variant,
+and the parse also prints each variant's median over the rounds.  Before
+the first segment, --warmup-s seconds of untimed 4096^3 GEMMs let the clock
+settle.  --stream MB runs
 the read-only probe (gemvtile_read_stream, 256 workgroups) over that many MB
 per launch with each cache policy in --stream-policies: the practical read
 ceiling of the bandwidth-bound kernels.  Segments are delimited in the trace
@@ -86,6 +95,21 @@ def run(a):
     def uni(shape, lo, hi):
         return torch.empty(shape, dtype=torch.float16, device=dev).uniform_(lo, hi, generator=g)
 
+    if a.warmup_s > 0:
+        # Untimed load before the first marker: the part's clock takes a few
+        # tenths of a second of sustained work to settle, and segments run
+        # before that would read slow for reasons of their position alone.
+        import time
+
+        wa, wb = uni((4096, 4096), -1, 1), uni((4096, 4096), -1, 1)
+        wd = torch.empty((4096, 4096), dtype=torch.float16, device=dev)
+        t_end = time.monotonic() + a.warmup_s
+        while time.monotonic() < t_end:
+            for _ in range(50):
+                gt.gemm_f16(wa, wb, wd)
+            torch.cuda.synchronize(dev)
+        del wa, wb, wd
+
     variants = [int(v) for v in a.gemv_variants.split(",")]
     skinny_variants = [int(v) for v in a.skinny_variants.split(",")]
     for N, K in _shapes(a.gemv, 2):
@@ -121,17 +145,33 @@ def run(a):
             segment({"kind": "read_stream", "policy": pol, "N": nbytes, "bytes": nbytes},
                     lambda i, pol=pol: gt.read_stream(bufs[i], sink, pol, 256), c)
         del bufs
+    def operand(shape, data):
+        if data == "uniform":
+            return uni(shape, -1, 1)
+        if data == "m7":  # keep the top 7 of fp16's 10 mantissa bits
+            t = uni(shape, -1, 1)
+            return (t.view(torch.int16) & ~0x7).view(torch.float16)
+        if data == "int":
+            return torch.randint(-8, 9, shape, device=dev, generator=g).to(torch.float16)
+        if data == "zero":
+            return torch.zeros(shape, dtype=torch.float16, device=dev)
+        raise SystemExit(f"unknown --gemm-data {data!r}")
+
     gemm_variants = [int(v) for v in a.gemm_variants.split(",")]
     for M, N, K in _shapes(a.gemm, 3):
-        sets = [(uni((M, K), -1, 1), uni((N, K), -1, 1)) for _ in range(3)]
-        D = torch.empty((M, N), dtype=torch.float16, device=dev)
-        for v in gemm_variants:
-            segment({"kind": "gemm_f16", "M": M, "N": N, "K": K, "variant": v, "flops": 2 * M * N * K},
-                    lambda i, v=v: gt.gemm_f16(sets[i][0], sets[i][1], D, variant=v), 3)
-        if a.vendor:
-            segment({"kind": "torch.matmul", "M": M, "N": N, "K": K, "flops": 2 * M * N * K},
-                    lambda i: torch.matmul(sets[i][0], sets[i][1].t(), out=D), 3)
-        del sets
+        for data in a.gemm_data.split(","):
+            sets = [(operand((M, K), data), operand((N, K), data)) for _ in range(3)]
+            D = torch.empty((M, N), dtype=torch.float16, device=dev)
+            for rnd in range(a.rounds):
+                for v in gemm_variants:
+                    segment({"kind": "gemm_f16", "M": M, "N": N, "K": K, "variant": v, "data": data,
+                             "round": rnd, "flops": 2 * M * N * K},
+                            lambda i, v=v: gt.gemm_f16(sets[i][0], sets[i][1], D, variant=v), 3)
+                if a.vendor:
+                    segment({"kind": "torch.matmul", "M": M, "N": N, "K": K, "data": data, "round": rnd,
+                             "flops": 2 * M * N * K},
+                            lambda i: torch.matmul(sets[i][0], sets[i][1].t(), out=D), 3)
+            del sets
     print("SEGMENTS " + json.dumps(labels), flush=True)
 
 
@@ -149,12 +189,15 @@ def parse(trace_dir, log_path):
     marks = [i for i, r in enumerate(rows) if MARKER in r["Kernel_Name"]]
     if len(marks) != 2 * len(labels):
         raise SystemExit(f"{len(marks)} markers for {len(labels)} segments")
+    by_label: dict = {}
     for lab, (lo, hi) in zip(labels, zip(marks[0::2], marks[1::2])):
         durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[lo + 1 : hi]]
         names = sorted({r["Kernel_Name"].split("(")[0][:60] for r in rows[lo + 1 : hi]})
         med = statistics.median(durs) / 1e3
         shape = "x".join(str(lab[k]) for k in ("M", "N", "K") if k in lab)
         var = f" v{lab['variant']}" if "variant" in lab else (f" p{lab['policy']}" if "policy" in lab else "")
+        if "data" in lab:
+            shape += f" {lab['data']}"
         if "flops" in lab:
             tf = lab["flops"] / (med * 1e6)
             rate = f"{tf:6.0f} TFLOP/s ({tf / 25:5.1f} % of 2.5 PFLOP/s)"
@@ -162,6 +205,17 @@ def parse(trace_dir, log_path):
             gbps = lab["bytes"] / (med * 1e3)
             rate = f"{gbps:6.0f} GB/s ({gbps / 80:5.1f} % of 8 TB/s)"
         print(f"{lab['kind']:13s}{var:4s} {shape:18s} n={len(durs):3d} median {med:8.2f} us {rate}  {'; '.join(names)}")
+        key = json.dumps({k: v for k, v in lab.items() if k != "round"}, sort_keys=True)
+        by_label.setdefault(key, []).append(med)
+    repeated = {k: v for k, v in by_label.items() if len(v) > 1}
+    if repeated:
+        print("-- over rounds: median of the segment medians (min .. max)")
+        for key, meds in repeated.items():
+            lab = json.loads(key)
+            var = f" v{lab['variant']}" if "variant" in lab else ""
+            shape = "x".join(str(lab[k]) for k in ("M", "N", "K") if k in lab) + f" {lab.get('data', '')}"
+            print(f"{lab['kind']:13s}{var:4s} {shape:18s} rounds={len(meds):2d} {statistics.median(meds):8.2f} us "
+                  f"({min(meds):.2f} .. {max(meds):.2f})")
 
 
 def main(argv=None):
@@ -172,6 +226,9 @@ def main(argv=None):
     p.add_argument("--skinny-variants", default="0")
     p.add_argument("--gemm", default="", help="M:N:K,... compute-bound GEMM shapes (default none)")
     p.add_argument("--gemm-variants", default="0")
+    p.add_argument("--gemm-data", default="uniform", help="uniform,m7,int,zero (comma list)")
+    p.add_argument("--rounds", type=int, default=1, help="times the --gemm-variants list runs, interleaved")
+    p.add_argument("--warmup-s", type=float, default=1.0, help="seconds of untimed GEMMs before the first segment")
     p.add_argument("--stream", type=float, default=0.0, help="MB per read-only probe launch (0: none)")
     p.add_argument("--stream-policies", default="1,2")
     p.add_argument("--vendor", action="store_true")
