@@ -7,19 +7,27 @@ it does not know that feature, which is harmless.
 
 The GEMM kernels issue their 16x16x32 MFMAs as inline asm with the
 accumulators bound to AGPRs.  That is only correct while every accumulator
-stays in an AGPR: if the register allocator gives the kernel fewer AGPRs, it
-moves accumulators through scratch around each asm statement, and those moves
-read an MFMA's result with none of the wait states the compiler inserts for
-MFMAs it knows about (stale values, no error).  The build therefore asks the
-compiler for each kernel's resource usage and fails if such a kernel has
-fewer AGPRs than its accumulators need.
+stays in place: if register pressure makes the allocator move accumulators
+(to scratch, or to other registers), its moves read an MFMA's result with
+none of the wait states the compiler inserts for MFMAs it knows about, and
+the kernel computes stale values with no error.  The build therefore checks
+the code it produced, in two ways, and fails if either finds a problem:
+  * the compiler's resource-usage remarks: every kernel with inline-asm
+    MFMAs has at least as many AGPRs as its accumulators need;
+  * the device assembly of those kernels (kept from the same compilation
+    with -save-temps): no instruction other than an MFMA reads or writes an
+    MFMA's destination registers within MFMA_RESULT_WAIT wait states of it,
+    and no VALU instruction writes an MFMA source register within
+    VALU_TO_MFMA_WAIT wait states before it.
 """
 from __future__ import annotations
 
+import glob
 import os
 import re
 import subprocess
 import sys
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
@@ -51,7 +59,10 @@ def hipcc() -> str:
 
 
 RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
-_REMARK = re.compile(r"remark:\s+(Function Name|AGPRs|VGPRs|ScratchSize \[bytes/lane\]|VGPRs Spill):\s+(\S+)")
+# Either "file:line:col: remark: Key: value" or, when the backend runs as a
+# separate step (-save-temps), "remark: file:line:col: Key: value".
+_REMARK = re.compile(r"remark:\s+(?:\S+:\d+:\d+:\s+)?(Function Name|AGPRs|VGPRs|ScratchSize \[bytes/lane\]|VGPRs Spill):"
+                     r"\s+(\S+)")
 
 
 def parse_resource_usage(text: str) -> dict:
@@ -99,12 +110,110 @@ def check_resource_usage(usage: dict) -> list:
     return bad
 
 
+# Wait states counted by scan_mfma_hazards: each instruction is one, `s_nop N`
+# is N + 1.  The 16x16x32 MFMA's result needs fewer than MFMA_RESULT_WAIT
+# before another instruction may touch it; the kernels pad 24 before reading
+# their accumulators.
+MFMA_RESULT_WAIT = 16
+VALU_TO_MFMA_WAIT = 2
+# Kernels whose MFMAs are inline asm (the compiler pads its own MFMAs).
+INLINE_MFMA_KERNELS = ("gemm_kernel", "gemm_ws_kernel")
+
+_FUNC_START = re.compile(r"^(_Z\S+):\s*(;.*)?$")
+_AREG = re.compile(r"(?<![\w.])a(?:\[(\d+):(\d+)\]|(\d+)(?![\w]))")
+_VREG = re.compile(r"(?<![\w.])v(?:\[(\d+):(\d+)\]|(\d+)(?![\w]))")
+
+
+def _regs(pattern, text: str) -> set:
+    out = set()
+    for m in pattern.finditer(text):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def _functions(asm: str):
+    """(name, [(instruction, from_inline_asm)]) for every function in a device
+    .s file; the compiler brackets inline asm with ;;#ASMSTART / ;;#ASMEND."""
+    name, body, in_asm = None, [], False
+    for line in asm.splitlines():
+        m = _FUNC_START.match(line)
+        if m:
+            name, body, in_asm = m.group(1), [], False
+            continue
+        if name is None:
+            continue
+        if line.startswith(".Lfunc_end"):
+            yield name, body
+            name = None
+            continue
+        stripped = line.strip()
+        if stripped.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif stripped.startswith(";;#ASMEND"):
+            in_asm = False
+        code = line.split(";")[0].strip()
+        if code and not code.startswith(".") and not code.endswith(":"):
+            body.append((code, in_asm))
+
+
+def scan_mfma_hazards(asm: str, kernels=INLINE_MFMA_KERNELS) -> list:
+    """Places in the listed kernels where code touches the result of an
+    inline-asm MFMA, or writes its sources, too soon (see the module
+    docstring).  MFMAs the compiler wrote itself are left to its own hazard
+    padding.  The scan follows the listing's order, i.e. fall-through paths;
+    an inline-asm MFMA is never the last instruction before a branch in
+    these kernels' hot loops, whose bodies are straight-line."""
+    bad = []
+    for name, body in _functions(asm):
+        if not any(k in name for k in kernels):
+            continue
+        pending = []  # [wait states since issue, destination AGPRs, text] of recent inline-asm MFMAs
+        recent_writes = []  # [wait states since issue, written VGPRs/AGPRs, text] of recent VALU ops
+        for ins, from_asm in body:
+            op = ins.split()[0]
+            if op.startswith("v_mfma") and from_asm:
+                ops = [o.strip() for o in ins.split(None, 1)[1].split(",")]
+                dst, srcs = _regs(_AREG, ops[0]), _regs(_VREG, ops[1]) | _regs(_VREG, ops[2])
+                src_c = _regs(_AREG, ops[3]) if len(ops) > 3 else set()
+                for age, regs, text in recent_writes:
+                    if age < VALU_TO_MFMA_WAIT and (regs & srcs or regs & src_c):
+                        bad.append(f"{name}: '{text}' writes a source of '{ins}' {age} wait states before it")
+                step, entry = 1, [0, dst, ins]
+            elif op.startswith("v_mfma"):
+                step, entry = 1, None
+            else:
+                step = int(ins.split()[1], 0) + 1 if op == "s_nop" else 1
+                touched = _regs(_AREG, ins)
+                for age, regs, text in pending:
+                    if age < MFMA_RESULT_WAIT and touched & regs:
+                        bad.append(f"{name}: '{ins}' touches the result of '{text}' {age} wait states after it")
+                entry = None
+                if op.startswith("v_") and len(ins.split()) > 1:
+                    first = ins.split(None, 1)[1].split(",")[0]
+                    written = _regs(_VREG, first) | _regs(_AREG, first)
+                    if written:
+                        recent_writes.append([0, written, ins])
+            for lst in (pending, recent_writes):
+                for e in lst:
+                    e[0] += step
+            pending[:] = [e for e in pending if e[0] < MFMA_RESULT_WAIT]
+            recent_writes[:] = [e for e in recent_writes if e[0] < VALU_TO_MFMA_WAIT]
+            if entry is not None:
+                pending.append(entry)
+    return bad
+
+
 def build_library(output: str = LIBRARY, extra_flags=(), verbose: bool = False) -> str:
     tmp = output + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, RESOURCE_REMARKS, *extra_flags, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    with tempfile.TemporaryDirectory(prefix="gemvtile_build_") as work:
+        cmd = [hipcc(), *HIPCC_FLAGS, RESOURCE_REMARKS, "-save-temps=cwd", *extra_flags, *SOURCES, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True, cwd=work)
+        asm = {os.path.basename(f): open(f).read() for f in glob.glob(os.path.join(work, "*-hip-amdgcn-*.s"))}
     text = res.stdout + res.stderr
     # hipcc's host pass always warns about the device-only feature flag; the
     # resource remarks are parsed below rather than shown.
@@ -125,10 +234,16 @@ def build_library(output: str = LIBRARY, extra_flags=(), verbose: bool = False) 
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     usage = parse_resource_usage(text)
     bad = check_resource_usage(usage)
-    if not usage or bad:
+    if not usage:
+        bad.append("no kernel-resource-usage remarks in the compiler output")
+    if len(asm) != len(SOURCES):
+        bad.append(f"expected {len(SOURCES)} device assembly files from -save-temps, found {sorted(asm)}")
+    for fname, text_s in sorted(asm.items()):
+        bad += scan_mfma_hazards(text_s)
+    if bad:
         os.remove(tmp)
-        raise RuntimeError("inline-asm MFMA accumulators outside AGPRs (results would be wrong):\n"
-                           + ("\n".join(bad) if bad else "no kernel-resource-usage remarks in the compiler output"))
+        raise RuntimeError("inline-asm MFMA accumulators moved or touched too early (results would be wrong):\n"
+                           + "\n".join(bad[:20]) + (f"\n... {len(bad) - 20} more" if len(bad) > 20 else ""))
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, output)

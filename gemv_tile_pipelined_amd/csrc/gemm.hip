@@ -69,7 +69,7 @@ namespace gt {
 template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, bool SWIZZLE_, bool PERSISTENT_,
           int DMA_STRIDE_, int DMA_PHASES_, int K_STAGGER_ = 1, int K_STAGGER_STEP_ = 1, int LOAD_POLICY_ = 0,
           int MI_ = 32, int READ_STRIDE_ = 1, int DMA_OFFSET_ = 0, bool FUSE_DMA_ = false, int DTYPE_ = kF16,
-          bool PRESET_M0_ = false>
+          bool PRESET_M0_ = false, bool PROLOGUE_ALL_ = false>
 struct GemmShape {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -116,6 +116,16 @@ struct GemmShape {
   static constexpr bool PRESET_M0 = PRESET_M0_;
   static_assert(!PRESET_M0 || (DMA_PHASES_ == 1 && !FUSE_DMA_ && LOAD_POLICY_ == 0 && STAGES_ >= 2),
                 "M0 presetting is built for the plain single-phase refill");
+  // Prologue: issue the loads of every ring stage (K tiles 0 .. STAGES-1) at
+  // once, instead of tiles 0 .. STAGES-2 and then the last one spread over
+  // the first K tile.  All stages are free at the start of an output tile.
+  // K tile 0 keeps its usual schedule and so loads the second part of tile
+  // STAGES-1 again: the same bytes into a stage that nobody reads before
+  // the barrier that waits for them.  (Peeling K tile 0 out of the loop
+  // instead raised register pressure until the compiler moved accumulators
+  // around the hand-written MFMAs.)
+  static constexpr bool PROLOGUE_ALL = PROLOGUE_ALL_;
+  static_assert(!PROLOGUE_ALL || (!PRESET_M0_ && STAGES_ >= 2), "whole-ring prologue: pipelined loop, no M0 preset");
   static_assert(DTYPE == kF16 || (DTYPE == kBF16 && MI_ == 16), "bf16 uses the 16x16x32 MFMA path");
   static_assert((BK / kKStep) >= 1 && (BM / WAVES_M / MI) * (BN / WAVES_N / MI) % READ_STRIDE == 0,
                 "the read spacing must divide the MFMA slots of a K step");
@@ -541,18 +551,20 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
         if constexpr (!kNext) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       };
 
-      // Prologue: K tiles 0 .. STAGES-2 in flight; once tile 0 has landed the
+      // Prologue: K tiles 0 .. STAGES-2 in flight (0 .. STAGES-1 with
+      // PROLOGUE_ALL); once tile 0 has landed the
       // loads of tile STAGES-1 that would follow a barrier go out, the rest
       // during K tile 0.
+      constexpr int kPrologueTiles = S::PROLOGUE_ALL ? S::STAGES : S::STAGES - 1;
 #pragma unroll
-      for (int s = 0; s < S::STAGES - 1; ++s)
+      for (int s = 0; s < kPrologueTiles; ++s)
         if (s < KT) issue_loads(s, 0, S::kDmaPerStage);
-      wait_tile_landed<S>(min(KT, S::STAGES - 1) - 1);
+      wait_tile_landed<S>(min(KT, kPrologueTiles) - 1);
       workgroup_barrier();
       load_frags(0, 0, 0);
       // The chain of refill loads starts with load 0 of K tile STAGES-1.
       if constexpr (S::PRESET_M0) set_m0(dma_args(S::STAGES - 1, 0).lds);
-      if (S::STAGES - 1 < KT) {
+      if (!S::PROLOGUE_ALL && S::STAGES - 1 < KT) {
 #pragma unroll
         for (int pos = 0; pos < kAfter; ++pos) dma_slot(S::STAGES - 1, pos);
       }
@@ -667,6 +679,9 @@ using GemmPresetM0Refill3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 1, 1
 // slots, the compiler leaves the accumulators too few AGPRs and moves them
 // through scratch around each hand-written MFMA; build.py rejects that.)
 using GemmRefillEvery3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 1, 1, 1, 0, 16, 2, 1>;
+// The default with both ring stages requested at the start of each output
+// tile, so K tile 1 is in flight while K tile 0 arrives.
+using GemmPrologueAll = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, kF16, false, true>;
 using Gemm32x32Bk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
 
 static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDefault::BK == kGemmBK &&
@@ -710,6 +725,7 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 16: return launch<GemmPresetM0Refill2>(A, B, D, M, N, K, num_cus, stream);
     case 17: return launch<GemmPresetM0Refill3>(A, B, D, M, N, K, num_cus, stream);
     case 18: return launch<GemmRefillEvery3>(A, B, D, M, N, K, num_cus, stream);
+    case 19: return launch<GemmPrologueAll>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

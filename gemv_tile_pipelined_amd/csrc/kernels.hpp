@@ -20,7 +20,7 @@ constexpr int kGemmBK = 64;
 constexpr int kGemmStages = 2;
 constexpr int kGemmThreads = 256;
 constexpr int kGemmGroupM = 8;
-constexpr int kGemmVariants = 19;
+constexpr int kGemmVariants = 20;
 constexpr int kGemvVariants = 18;
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip); it has kSkinnyVariants launch shapes.

@@ -208,7 +208,9 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *      refill load right after each one, so a load's slot holds the load
  *      alone   16  as 15 with a refill load every 2 slots   17  ... every 3
  *   18 as 0 with a refill load every 3 MFMA slots
- * Variants 1..18 always run the tiled kernel, whatever the shape; variant
+ *   19 as 0 with the loads of both ring stages (K tiles 0 and 1) issued
+ *      together at the start of each output tile
+ * Variants 1..19 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16: the skinny kernel).  Each other kernel family has its own range:
  *   100..151 the skinny kernel (only for M <= 16 or N <= 16, else

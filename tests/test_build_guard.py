@@ -1,10 +1,17 @@
-"""The build's check that inline-asm MFMA accumulators stay in AGPRs.
+"""The build's checks that inline-asm MFMA accumulators stay in place.
 
 The remarks below have the form hipcc prints under
 -Rpass-analysis=kernel-resource-usage.  The first kernel is the tiled GEMM
 with a refill load every MFMA slot, as the compiler once allocated it: 32
 AGPRs for 256 accumulator registers and 1552 bytes of scratch per lane.  That
 kernel wrote all-zero outputs, and the check must reject it.
+
+The assembly snippets reproduce, in miniature, what the compiler emitted for
+a GEMM variant that kept all its AGPRs but spilled VGPRs: accumulators copied
+out a few instructions after the MFMA that writes them, and written back one
+instruction before the MFMA that reads them.  That variant gave wrong bits;
+the scan must flag both patterns and accept the padded reads the kernels
+write themselves.
 """
 from gemv_tile_pipelined_amd import build
 
@@ -62,3 +69,68 @@ def test_parse_and_check():
 def test_check_flags_one_agpr_short():
     usage = build.parse_resource_usage(_remarks(EIGHT_WAVES, 127, 232, 0))
     assert len(build.check_resource_usage(usage)) == 1
+
+
+def test_parse_remarks_with_location_after_tag():
+    """With -save-temps the backend prints 'remark: file:line:col: Key: value'."""
+    text = "\n".join([
+        f"remark: /src/gemm.hip:44:0: Function Name: {WS} [-Rpass-analysis=kernel-resource-usage]",
+        "remark: /src/gemm.hip:44:0:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]",
+        "remark: /src/gemm.hip:44:0:     AGPRs: 128 [-Rpass-analysis=kernel-resource-usage]",
+        "remark: /src/gemm.hip:44:0:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]",
+        "remark: /src/gemm.hip:44:0:     VGPRs Spill: 3 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert build.parse_resource_usage(text) == {WS: {"VGPRs": 128, "AGPRs": 128, "ScratchSize": 16, "VGPRs Spill": 3}}
+
+
+def _asm(name, lines):
+    """A device-assembly function in the layout hipcc writes; lines starting
+    with '!' are wrapped in inline-asm markers."""
+    out = [f"{name}:                 ; @{name}", "; %bb.0:"]
+    for ln in lines:
+        if ln.startswith("!"):
+            out += ["\t;;#ASMSTART", "\t" + ln[1:], "\t;;#ASMEND"]
+        else:
+            out.append("\t" + ln)
+    out += [".Lfunc_end0:", f"\t.size\t{name}, .Lfunc_end0-{name}"]
+    return "\n".join(out) + "\n"
+
+
+MFMA = "!v_mfma_f32_16x16x32_f16 a[252:255], v[60:63], v[56:59], a[252:255]"
+
+
+def test_hazard_scan_accepts_padded_reads():
+    # the kernels' own pattern: MFMAs, 24 wait states of padding, then reads
+    ok = _asm(DEFAULT, [MFMA, "!v_mfma_f32_16x16x32_f16 a[248:251], v[4:7], v[56:59], a[248:251]",
+                        "!s_nop 7", "!s_nop 7", "!s_nop 7", "v_accvgpr_read_b32 v0, a252", "v_accvgpr_read_b32 v4, a248"])
+    assert build.scan_mfma_hazards(ok) == []
+
+
+def test_hazard_scan_flags_early_accumulator_read():
+    # as the compiler emitted under register pressure: an accumulator copied
+    # out a few instructions after the MFMA that writes it
+    bad = _asm(DEFAULT, [MFMA, "v_add_u32_e32 v96, s9, v118", "ds_read_b128 v[104:107], v96",
+                         "s_add_i32 s12, s11, 0x8000", "s_mov_b32 m0, s12", "s_nop 0",
+                         "v_accvgpr_read_b32 v0, a252"])
+    found = build.scan_mfma_hazards(bad)
+    assert len(found) == 1 and "v_accvgpr_read_b32 v0, a252" in found[0]
+
+
+def test_hazard_scan_flags_late_accumulator_restore():
+    # an accumulator written back one instruction before the MFMA reads it
+    bad = _asm(DEFAULT, ["v_accvgpr_write_b32 a255, v167", MFMA])
+    found = build.scan_mfma_hazards(bad)
+    assert len(found) == 1 and "writes a source" in found[0]
+    # and an operand register written by a VALU op right before the MFMA
+    bad2 = _asm(DEFAULT, ["v_mov_b32_e32 v58, v200", MFMA])
+    assert len(build.scan_mfma_hazards(bad2)) == 1
+
+
+def test_hazard_scan_skips_compiler_mfmas_and_other_kernels():
+    # an MFMA the compiler wrote (no inline-asm markers) is padded by the
+    # compiler itself; kernels without inline-asm MFMAs are not scanned
+    compiler = _asm(MI32_ONE_STAGE, ["v_mfma_f32_32x32x16_f16 a[64:79], v[32:35], v[24:27], a[64:79]",
+                                     "v_accvgpr_write_b32 a64, 0"])
+    assert build.scan_mfma_hazards(compiler) == []
+    other = _asm(GEMV, [MFMA, "v_accvgpr_read_b32 v0, a252"])
+    assert build.scan_mfma_hazards(other) == []

@@ -259,7 +259,7 @@ def test_output_guard_band(env):
     assert np.array_equal(D.cpu().numpy(), oracle.gemm(A, B))
 
 
-@pytest.mark.parametrize("variant", list(range(1, 19)))
+@pytest.mark.parametrize("variant", list(range(1, 20)))
 def test_gemm_variants_bit_identical(env, variant):
     """The ablation kernels (no swizzle, one stage, non-persistent) give the
     same bits as the default on integer data; a pipeline race would not."""
@@ -269,6 +269,18 @@ def test_gemm_variants_bit_identical(env, variant):
     base = _gemm(env, A, B, 0).cpu().numpy()
     assert np.array_equal(base, oracle.gemm(A, B))
     assert np.array_equal(_gemm(env, A, B, variant).cpu().numpy(), base)
+
+
+@pytest.mark.parametrize("variant", [0, 2, 11, 12, 15, 16, 17, 19])
+@pytest.mark.parametrize("K", [8, 64, 72, 128, 136, 192, 200, 264])
+def test_gemm_variants_few_k_tiles(env, variant, K):
+    """1 to 5 K tiles of 64 (1 to 9 of 32), whole and ragged: the prologue,
+    the last refill and the ring drain take their short-K branches.  Integer
+    data, so every variant must match the oracle bit for bit."""
+    M, N = 300, 260
+    A = datagen.integer_f16(6100 + K, 0, (M, K))
+    B = datagen.integer_f16(6100 + K, 1, (N, K))
+    assert np.array_equal(_gemm(env, A, B, variant).cpu().numpy(), oracle.gemm(A, B))
 
 
 @pytest.mark.parametrize("variant", list(range(1, 18)))
