@@ -36,6 +36,7 @@ __all__ = [
     "xcd_logical_id",
     "gemm_config",
     "gemm_grid",
+    "gemm_tile",
     "gemv_grid",
     "device_caps",
     "read_stream",
@@ -53,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "gemvtile_tile_coord",
     "gemvtile_gemm_config",
     "gemvtile_gemm_grid",
+    "gemvtile_gemm_tile",
     "gemvtile_gemv_grid",
     "gemvtile_device_caps",
     "gemvtile_read_stream",
@@ -118,6 +120,8 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemvtile_gemm_config.restype = None
     lib.gemvtile_gemm_grid.argtypes = [i64, i64, i64]
     lib.gemvtile_gemm_grid.restype = i64
+    lib.gemvtile_gemm_tile.argtypes = [i64, i64, i64, intp, intp, intp]
+    lib.gemvtile_gemm_tile.restype = c_int
     lib.gemvtile_gemv_grid.argtypes = [i64, i64]
     lib.gemvtile_gemv_grid.restype = i64
     lib.gemvtile_device_caps.argtypes = [intp] * 4
@@ -319,6 +323,13 @@ def gemm_config() -> dict:
 
 def gemm_grid(M: int, N: int, num_cus: int) -> int:
     return int(load_library().gemvtile_gemm_grid(M, N, num_cus))
+
+
+def gemm_tile(M: int, N: int, num_cus: int) -> tuple:
+    """(bm, bn, stages) of the tiled GEMM for an M x N output on num_cus CUs."""
+    vals = [ctypes.c_int() for _ in range(3)]
+    _check(load_library().gemvtile_gemm_tile(M, N, num_cus, *[ctypes.byref(v) for v in vals]))
+    return tuple(v.value for v in vals)
 
 
 def gemv_grid(N: int, num_cus: int) -> int:

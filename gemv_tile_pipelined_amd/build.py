@@ -125,12 +125,14 @@ _VREG = re.compile(r"(?<![\w.])v(?:\[(\d+):(\d+)\]|(\d+)(?![\w]))")
 
 
 def _regs(pattern, text: str) -> set:
+    """Registers named in `text`, as (kind, number) with kind "a" or "v"."""
+    kind = "a" if pattern is _AREG else "v"
     out = set()
     for m in pattern.finditer(text):
         if m.group(3) is not None:
-            out.add(int(m.group(3)))
+            out.add((kind, int(m.group(3))))
         else:
-            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+            out.update((kind, r) for r in range(int(m.group(1)), int(m.group(2)) + 1))
     return out
 
 

@@ -260,8 +260,19 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus) {
     const int64_t rows = gt::skinny_default_rows(R, static_cast<int>(num_cus));
     return (R + rows - 1) / rows;
   }
-  const int64_t tiles = ((M + gt::kGemmBM - 1) / gt::kGemmBM) * ((N + gt::kGemmBN - 1) / gt::kGemmBN);
+  if (num_cus > (int64_t{1} << 20)) return 0;
+  const gt::GemmTileShape &t = gt::kGemmTileShapes[gt::gemm_default_tile(M, N, static_cast<int>(num_cus))];
+  const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
   return tiles < num_cus ? tiles : num_cus;
+}
+
+int gemvtile_gemm_tile(int64_t M, int64_t N, int64_t num_cus, int *bm, int *bn, int *stages) {
+  if (M <= 0 || N <= 0 || num_cus <= 0 || num_cus > (int64_t{1} << 20)) return GEMVTILE_ERR_INVALID_ARG;
+  const gt::GemmTileShape &t = gt::kGemmTileShapes[gt::gemm_default_tile(M, N, static_cast<int>(num_cus))];
+  if (bm) *bm = t.bm;
+  if (bn) *bn = t.bn;
+  if (stages) *stages = t.stages;
+  return GEMVTILE_OK;
 }
 
 }  // extern "C"

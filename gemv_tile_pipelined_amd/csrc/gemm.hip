@@ -683,6 +683,18 @@ using GemmRefillEvery3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 1, 1, 1
 // tile, so K tile 1 is in flight while K tile 0 arrives.
 using GemmPrologueAll = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, kF16, false, true>;
 using Gemm32x32Bk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
+// Smaller output tiles, for outputs whose 256x256 tiles would leave CUs
+// idle (gemm_default_tile picks): the default's schedule on 256x128, 128x256
+// and 128x128 tiles (4 waves of 128x64, 64x128 and 64x64; 12, 12 and 8 loads
+// per wave per K tile), with the deeper rings of kGemmTileShapes.  A K tile
+// of these is 1/2 or 1/4 of the 256x256 one in MFMA time, so two stages no
+// longer cover a load's latency.
+template <int DT, int STAGES = 2>
+using GemmTile256x128 = GemmShape<256, 128, 64, STAGES, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, DT>;
+template <int DT, int STAGES = 2>
+using GemmTile128x256 = GemmShape<128, 256, 64, STAGES, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, DT>;
+template <int DT, int STAGES = 2>
+using GemmTile128x128 = GemmShape<128, 128, 64, STAGES, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, DT>;
 
 static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDefault::BK == kGemmBK &&
                   GemmDefault::STAGES == kGemmStages && GemmDefault::kThreads == kGemmThreads,
@@ -703,10 +715,36 @@ static hipError_t launch(const void *A, const void *B, void *D, int M, int N, in
   return hipGetLastError();
 }
 
+// The shape-dependent default: the tile gemm_default_tile picks, with the
+// ring depth of kGemmTileShapes.
+template <int DT>
+static hipError_t launch_default(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
+                                 hipStream_t stream) {
+  using Big = std::conditional_t<DT == kF16, GemmDefault, GemmBf16>;
+  static_assert(Big::BM == kGemmTileShapes[kTile256x256].bm && Big::BN == kGemmTileShapes[kTile256x256].bn &&
+                    Big::STAGES == kGemmTileShapes[kTile256x256].stages &&
+                    GemmTile256x128<DT, kGemmTileShapes[kTile256x128].stages>::BN ==
+                        kGemmTileShapes[kTile256x128].bn &&
+                    GemmTile128x256<DT, kGemmTileShapes[kTile128x256].stages>::BM ==
+                        kGemmTileShapes[kTile128x256].bm &&
+                    GemmTile128x128<DT, kGemmTileShapes[kTile128x128].stages>::BM ==
+                        kGemmTileShapes[kTile128x128].bm,
+                "kGemmTileShapes must describe the kernels launched for each tile");
+  switch (gemm_default_tile(M, N, num_cus)) {
+    case kTile256x128:
+      return launch<GemmTile256x128<DT, kGemmTileShapes[kTile256x128].stages>>(A, B, D, M, N, K, num_cus, stream);
+    case kTile128x256:
+      return launch<GemmTile128x256<DT, kGemmTileShapes[kTile128x256].stages>>(A, B, D, M, N, K, num_cus, stream);
+    case kTile128x128:
+      return launch<GemmTile128x128<DT, kGemmTileShapes[kTile128x128].stages>>(A, B, D, M, N, K, num_cus, stream);
+    default: return launch<Big>(A, B, D, M, N, K, num_cus, stream);
+  }
+}
+
 hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                            hipStream_t stream) {
   switch (variant) {
-    case 0: return launch<GemmDefault>(A, B, D, M, N, K, num_cus, stream);
+    case 0: return launch_default<kF16>(A, B, D, M, N, K, num_cus, stream);
     case 1: return launch<GemmNoSwizzle>(A, B, D, M, N, K, num_cus, stream);
     case 2: return launch<Gemm32x32OneStage>(A, B, D, M, N, K, num_cus, stream);
     case 3: return launch<GemmNonPersistent>(A, B, D, M, N, K, num_cus, stream);
@@ -726,13 +764,21 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 17: return launch<GemmPresetM0Refill3>(A, B, D, M, N, K, num_cus, stream);
     case 18: return launch<GemmRefillEvery3>(A, B, D, M, N, K, num_cus, stream);
     case 19: return launch<GemmPrologueAll>(A, B, D, M, N, K, num_cus, stream);
+    case 20: return launch<GemmDefault>(A, B, D, M, N, K, num_cus, stream);
+    case 21: return launch<GemmTile256x128<kF16, 3>>(A, B, D, M, N, K, num_cus, stream);
+    case 22: return launch<GemmTile128x256<kF16, 3>>(A, B, D, M, N, K, num_cus, stream);
+    case 23: return launch<GemmTile128x128<kF16, 4>>(A, B, D, M, N, K, num_cus, stream);
+    case 24: return launch<GemmTile256x128<kF16, 2>>(A, B, D, M, N, K, num_cus, stream);
+    case 25: return launch<GemmTile128x256<kF16, 2>>(A, B, D, M, N, K, num_cus, stream);
+    case 26: return launch<GemmTile128x128<kF16, 2>>(A, B, D, M, N, K, num_cus, stream);
+    case 27: return launch<GemmTile128x128<kF16, 5>>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gemm_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                             hipStream_t stream) {
-  return launch<GemmBf16>(A, B, D, M, N, K, num_cus, stream);
+  return launch_default<kBF16>(A, B, D, M, N, K, num_cus, stream);
 }
 
 }  // namespace gt

@@ -20,7 +20,42 @@ constexpr int kGemmBK = 64;
 constexpr int kGemmStages = 2;
 constexpr int kGemmThreads = 256;
 constexpr int kGemmGroupM = 8;
-constexpr int kGemmVariants = 20;
+constexpr int kGemmVariants = 28;
+
+// Output tile of the tiled GEMM.  The 256x256 default needs about one tile
+// per CU to fill the chip; outputs that give fewer take smaller tiles, each
+// with a deeper ring so that its shorter K tiles still cover the load
+// latency (2 stages at 256x256, 3 at 256x128 and 128x256, 4 at 128x128).
+enum GemmTile { kTile256x256 = 0, kTile256x128 = 1, kTile128x256 = 2, kTile128x128 = 3 };
+constexpr int kGemmTiles = 4;
+struct GemmTileShape {
+  int bm, bn, stages;
+  // Work rate relative to 256x256 when every CU has tiles to spare, in
+  // percent (measured at 8192^3: 256x128 and 128x256 run at about 0.9 of the
+  // 256x256 rate, 128x128 at about 0.76).
+  int rate_pct;
+};
+constexpr GemmTileShape kGemmTileShapes[kGemmTiles] = {
+    {256, 256, 2, 100}, {256, 128, 3, 90}, {128, 256, 3, 90}, {128, 128, 4, 76}};
+// The tile for an M x N output on num_cus CUs: the one with the least
+// estimated time, i.e. waves of tiles over the CUs times tile area over rate;
+// ties go to the larger tile (the lower enum value).
+inline GemmTile gemm_default_tile(int64_t M, int64_t N, int num_cus) {
+  int best = kTile256x256;
+  int64_t best_cost = -1;
+  for (int t = 0; t < kGemmTiles; ++t) {
+    const GemmTileShape &s = kGemmTileShapes[t];
+    const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
+    const int64_t waves = (tiles + num_cus - 1) / num_cus;
+    // waves * bm * bn / (rate_pct / 100), scaled to stay integral
+    const int64_t cost = waves * s.bm * s.bn * 100 / s.rate_pct;
+    if (best_cost < 0 || cost < best_cost) {
+      best = t;
+      best_cost = cost;
+    }
+  }
+  return static_cast<GemmTile>(best);
+}
 constexpr int kGemvVariants = 18;
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip); it has kSkinnyVariants launch shapes.

@@ -64,11 +64,14 @@ enum gemvtile_status {
  * M, N need not be multiples of any tile size: edge tiles read zeros beyond
  * the matrix and write only inside it.  The summation order within FP32 is
  * unspecified (several results are correct up to rounding).
+ * Otherwise the tiled kernel runs with 256x256 output tiles, or with
+ * 256x128, 128x256 or 128x128 ones when the output has too few 256x256
+ * tiles to keep every compute unit busy (gemvtile_gemm_tile gives the choice).
  * When M <= 16 or N <= 16 (a decode batch against a weight matrix) the call
  * runs a bandwidth-bound kernel that streams the larger operand once instead
- * of the 256x256-tiled one (with fewer rows of it per workgroup when it has
- * too few rows to give every compute unit 16), and when M == 1 or N == 1
- * the GEMV kernel of gemv_f16; results are deterministic either way.
+ * of the tiled one (with fewer rows of it per workgroup when it has too few
+ * rows to give every compute unit 16), and when M == 1 or N == 1 the GEMV
+ * kernel of gemv_f16; results are deterministic either way.
  * Returns a gemvtile_status.
  */
 int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream);
@@ -133,11 +136,28 @@ const char *gemvtile_status_string(int status);
 int gemvtile_tile_coord(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t group_m, int64_t *tm, int64_t *tn);
 
 /*
- * gemvtile_gemm_config -- the compile-time shape of the GEMM kernel that
- * gemm_f16 launches: output tile BM x BN, K tile BK, LDS ring depth, threads
- * per workgroup and the grouped-order height.  Any output pointer may be NULL.
+ * gemvtile_gemm_config -- the compile-time shape of the 256x256 tiled GEMM
+ * kernel that gemm_f16 launches on large outputs: output tile BM x BN, K
+ * tile BK, LDS ring depth, threads per workgroup and the grouped-order
+ * height.  Any output pointer may be NULL.
  */
 void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, int *group_m);
+
+/*
+ * gemvtile_gemm_tile -- the output tile (bm x bn) and LDS ring depth the
+ * tiled GEMM takes for an M x N output on `num_cus` compute units (gemm_f16
+ * and gemm_bf16 when neither side has 16 rows or fewer).  Of 256x256 (2
+ * stages), 256x128 and 128x256 (3 stages) and 128x128 (4 stages), it is the
+ * one with the least ceil(#tiles / num_cus) * bm * bn / rate, where rate is
+ * the tile's measured work rate relative to 256x256 with tiles to spare (1,
+ * 0.9, 0.9, 0.76); ties go to the larger tile.  Smaller tiles fill the CUs
+ * when large ones would leave some idle (an 8192 x 1024 output has 128 tiles
+ * of 256x256, 256 of 256x128); their deeper rings cover the load latency
+ * over their shorter K tiles.  Any output pointer may be NULL.  Host-only
+ * arithmetic; returns GEMVTILE_ERR_INVALID_ARG for M, N or num_cus <= 0 or
+ * num_cus > 2^20.
+ */
+int gemvtile_gemm_tile(int64_t M, int64_t N, int64_t num_cus, int *bm, int *bn, int *stages);
 
 /*
  * gemvtile_device_caps -- the current device's compute-unit count, peak
@@ -175,20 +195,20 @@ int64_t gemvtile_gemv_grid(int64_t N, int64_t num_cus);
  * the other side's rows when M or N is 1; when M <= 16 or N <= 16 (the
  * skinny kernel) ceil(R/p), R = max(M,N), with p the largest of 16, 8, 4, 2
  * rows per workgroup such that R >= p*num_cus, else p = 1; otherwise the
- * persistent grid min(#tiles, num_cus).  Host-only arithmetic; returns 0
- * for empty outputs.
+ * persistent grid min(#tiles, num_cus) over the tiles gemvtile_gemm_tile
+ * picks.  Host-only arithmetic; returns 0 for empty outputs.
  */
 int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
 
 /*
  * gemvtile_gemm_f16_variant -- gemm_f16 with an internal kernel variant, for
  * ablation measurements only (same contract and results as gemm_f16).  The
- * tiled ones use 256x256 output tiles and (but for 13, 14) 4 waves of
+ * tiled ones 1..20 use 256x256 output tiles and (but for 13, 14) 4 waves of
  * 128x128:
- *   0  the default kernel (identical to gemm_f16): 16x16x32 MFMA blocks, K
- *      tiles of 64 in a 2-stage LDS ring, the next K step's operand reads one
- *      every 2 MFMA slots, a refill load every 4 slots, swizzled LDS,
- *      persistent
+ *   0  what gemm_f16 runs: on tiled shapes the tile of gemvtile_gemm_tile;
+ *      with 256x256 tiles, 16x16x32 MFMA blocks, K tiles of 64 in a 2-stage
+ *      LDS ring, the next K step's operand reads one every 2 MFMA slots, a
+ *      refill load every 4 slots, swizzled LDS, persistent
  *   1  as 0 without the LDS swizzle
  *   2  as 10 with single-stage LDS (load, wait, compute: no overlap)
  *   3  as 0 with one workgroup per tile (no persistent loop, no XCD remap)
@@ -210,7 +230,12 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *   18 as 0 with a refill load every 3 MFMA slots
  *   19 as 0 with the loads of both ring stages (K tiles 0 and 1) issued
  *      together at the start of each output tile
- * Variants 1..19 always run the tiled kernel, whatever the shape; variant
+ *   20 the 256x256 tiled kernel of variant 0, whatever the shape
+ *   21, 22, 23 the same schedule on 256x128, 128x256 (3-stage rings) and
+ *      128x128 (4-stage ring) output tiles (4 waves of 128x64, 64x128,
+ *      64x64): the smaller tiles of variant 0, whatever the shape
+ *   24, 25, 26 as 21, 22, 23 with 2-stage rings   27 as 23 with 5 stages
+ * Variants 1..27 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16: the skinny kernel).  Each other kernel family has its own range:
  *   100..151 the skinny kernel (only for M <= 16 or N <= 16, else

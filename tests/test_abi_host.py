@@ -79,7 +79,7 @@ def test_gemm_argument_validation(lib):
     assert _gemm(lib, FAKE, FAKE, FAKE, 2**31, 4, 8) == UNSUPPORTED
     # unknown internal variant: each family has its own id range (tiled 0..,
     # skinny 100.., wave-specialised 200..); the gaps are invalid
-    for bad in (-1, 20, 99, 152, 199, 202, 1000):
+    for bad in (-1, 28, 99, 152, 199, 202, 1000):
         assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, bad) == INVALID, bad
     # skinny launch shapes only apply when one side has at most 16 rows
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 100) == UNSUPPORTED
@@ -169,7 +169,7 @@ def test_gemm_grid_and_golden_counts(lib):
     assert cfg == {"BM": 256, "BN": 256, "BK": 64, "stages": 2, "threads": 256, "group_m": 8}
     assert gt.gemm_grid(4096, 4096, 256) == 256
     assert gt.gemm_grid(8192, 8192, 256) == 256
-    assert gt.gemm_grid(256, 256, 256) == 1
+    assert gt.gemm_grid(256, 256, 256) == 4  # four 128x128 tiles (see the tile rule below)
     assert gt.gemm_grid(4000, 4032, 256) == 256
     assert gt.gemm_grid(0, 4, 256) == 0
     # skinny shapes: one workgroup per 16 rows of the larger side while that
@@ -182,7 +182,7 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(1000, 9, 256) == 500
     assert gt.gemm_grid(16, 300, 256) == 300
     assert gt.gemm_grid(16, 16, 256) == 16
-    assert gt.gemm_grid(17, 4097, 256) == 17
+    assert gt.gemm_grid(17, 4097, 256) == 33  # 1 x 33 tiles of 128x128
     # one row on a side: the GEMV grid of the other side
     assert gt.gemm_grid(1, 4096, 256) == gt.gemv_grid(4096, 256) == 256
     assert gt.gemm_grid(1000, 1, 256) == gt.gemv_grid(1000, 256)
@@ -197,6 +197,44 @@ def test_gemm_grid_and_golden_counts(lib):
     # every output tile visited once: 1024 tiles at 128x128 for 4096^2
     seen = {gt.tile_coord(t, 32, 32, 8) for t in range(1024)}
     assert len(seen) == golden["tiles_4096x4096_at_128x128"]
+
+
+def test_gemm_tile_rule(lib):
+    """The tiled GEMM's tile: 256x256 while it fills the CUs, smaller tiles
+    (with deeper rings) when it would not.  The shapes are those the choice
+    was measured on; the last two differ only in orientation."""
+    want = {
+        (4096, 4096): (256, 256, 2),
+        (8192, 8192): (256, 256, 2),
+        (4000, 4032): (256, 256, 2),
+        (8192, 1024): (256, 128, 3),
+        (4096, 2048): (256, 128, 3),
+        (2048, 2048): (128, 128, 4),
+        (1024, 4096): (128, 128, 4),
+        (512, 4096): (128, 128, 4),
+        (256, 256): (128, 128, 4),
+        (2176, 3840): (128, 256, 3),
+        (3840, 2176): (256, 128, 3),
+    }
+    for (M, N), tile in want.items():
+        assert gt.gemm_tile(M, N, 256) == tile, (M, N)
+        bm, bn, _ = tile
+        assert gt.gemm_grid(M, N, 256) == min(-(-M // bm) * -(-N // bn), 256), (M, N)
+    # the documented cost, ceil(#tiles / CUs) * bm * bn / rate, is least for
+    # the chosen tile, and no larger tile ties it
+    shapes = [(bm, bn, st, rate) for bm, bn, st, rate in
+              ((256, 256, 2, 1.0), (256, 128, 3, 0.9), (128, 256, 3, 0.9), (128, 128, 4, 0.76))]
+    for M in (17, 100, 256, 300, 777, 1024, 2049, 4096, 6000):
+        for N in (17, 129, 512, 1000, 3000, 8192):
+            for cus in (80, 256, 304):
+                cost = [-(-(-(-M // bm) * -(-N // bn)) // cus) * bm * bn / rate for bm, bn, _, rate in shapes]
+                got = gt.gemm_tile(M, N, cus)
+                i = [s[:3] for s in shapes].index(got)
+                assert cost[i] <= min(cost) * (1 + 1e-12), (M, N, cus)
+                assert all(c > cost[i] * (1 + 1e-12) for c in cost[:i]), (M, N, cus)
+    for bad in ((0, 4, 256), (4, 0, 256), (4, 4, 0), (4, 4, 2**21)):
+        with pytest.raises(gt.GemvTileError):
+            gt.gemm_tile(*bad)
 
 
 def test_measurement_formulas_match_table1():

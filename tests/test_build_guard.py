@@ -124,6 +124,9 @@ def test_hazard_scan_flags_late_accumulator_restore():
     # and an operand register written by a VALU op right before the MFMA
     bad2 = _asm(DEFAULT, ["v_mov_b32_e32 v58, v200", MFMA])
     assert len(build.scan_mfma_hazards(bad2)) == 1
+    # a VGPR that shares its number with the MFMA's accumulator is another register
+    ok = _asm(DEFAULT, ["v_add_u32_e32 v253, s55, v94", MFMA])
+    assert build.scan_mfma_hazards(ok) == []
 
 
 def test_hazard_scan_skips_compiler_mfmas_and_other_kernels():

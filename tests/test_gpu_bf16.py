@@ -122,6 +122,24 @@ def test_gemm_bf16_integer_exact(env, shape):
     assert np.array_equal(_bits(_gemm(env, A, B)), oracle.gemm_bf16(A, B))
 
 
+@pytest.mark.parametrize("shape", [(8192, 1000, 264), (2176, 3832, 200)], ids=lambda s: "x".join(map(str, s)))
+def test_gemm_bf16_smaller_tiles(env, shape):
+    """Shapes that take 256x128 and 128x256 tiles: sampled rows, integer data
+    bit-exact and uniform data within the bar."""
+    torch, gt, dev = env
+    M, N, K = shape
+    cfg = 8300 + shape[0] % 97
+    rows = np.sort(datagen.rng(cfg, 2).choice(M, 48, replace=False))
+    Ai = datagen.integer_bf16(cfg, 10, (M, K))
+    Bi = datagen.integer_bf16(cfg, 11, (N, K))
+    got = _bits(_gemm(env, Ai, Bi)[torch.from_numpy(rows).to(dev)])
+    assert np.array_equal(got, oracle.gemm_bf16(Ai, Bi, rows=rows))
+    A = datagen.uniform_bf16(cfg, 0, (M, K), -1.0, 1.0)
+    B = datagen.uniform_bf16(cfg, 1, (N, K), -1.0, 1.0)
+    got = _bits(_gemm(env, A, B)[torch.from_numpy(rows).to(dev)])
+    assert _violations(got, oracle.gemm_bf16(A, B, rows=rows)) == 0
+
+
 def _load_probe():
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "bf16_rne_probe.txt")
     cases = []

@@ -259,7 +259,7 @@ def test_output_guard_band(env):
     assert np.array_equal(D.cpu().numpy(), oracle.gemm(A, B))
 
 
-@pytest.mark.parametrize("variant", list(range(1, 20)))
+@pytest.mark.parametrize("variant", list(range(1, 28)))
 def test_gemm_variants_bit_identical(env, variant):
     """The ablation kernels (no swizzle, one stage, non-persistent) give the
     same bits as the default on integer data; a pipeline race would not."""
@@ -271,7 +271,7 @@ def test_gemm_variants_bit_identical(env, variant):
     assert np.array_equal(_gemm(env, A, B, variant).cpu().numpy(), base)
 
 
-@pytest.mark.parametrize("variant", [0, 2, 11, 12, 15, 16, 17, 19])
+@pytest.mark.parametrize("variant", [0, 2, 11, 12, 15, 16, 17, 19, 20, 21, 22, 23, 24, 25, 26, 27])
 @pytest.mark.parametrize("K", [8, 64, 72, 128, 136, 192, 200, 264])
 def test_gemm_variants_few_k_tiles(env, variant, K):
     """1 to 5 K tiles of 64 (1 to 9 of 32), whole and ragged: the prologue,
@@ -281,6 +281,37 @@ def test_gemm_variants_few_k_tiles(env, variant, K):
     A = datagen.integer_f16(6100 + K, 0, (M, K))
     B = datagen.integer_f16(6100 + K, 1, (N, K))
     assert np.array_equal(_gemm(env, A, B, variant).cpu().numpy(), oracle.gemm(A, B))
+
+
+# Outputs whose 256x256 tiles would leave CUs idle take smaller tiles: these
+# route (with 256 CUs) to 256x128, 128x256 and 128x128 tiles, with ragged M,
+# N and K.  Sampled rows against the oracle; integer data bit-exact.
+TILE_CHOICE_SHAPES = [(8192, 1000, 264, (256, 128)), (2176, 3832, 200, (128, 256)), (1000, 3000, 136, (128, 128))]
+
+
+@pytest.mark.parametrize("case", TILE_CHOICE_SHAPES, ids=lambda c: "x".join(map(str, c[:3])))
+def test_gemm_tile_choice_shapes(env, case):
+    torch, gt, dev = env
+    M, N, K, tile = case
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    print(f"[tile choice] {M}x{N}x{K} on {cus} CUs -> {gt.gemm_tile(M, N, cus)}", flush=True)
+    if cus == 256:
+        assert gt.gemm_tile(M, N, cus)[:2] == tile
+    cfg = 6200 + TILE_CHOICE_SHAPES.index(case)
+    rows = np.sort(datagen.rng(cfg, 2).choice(M, 64, replace=False))
+    A = datagen.uniform_f16(cfg, 0, (M, K), -1.0, 1.0)
+    B = datagen.uniform_f16(cfg, 1, (N, K), -1.0, 1.0)
+    D = _gemm(env, A, B)
+    got = D[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    assert np.isfinite(D.float().cpu().numpy()).all()
+    assert _tol_violations(got, oracle.gemm(A, B, rows=rows)) == 0
+    Ai = datagen.integer_f16(cfg, 10, (M, K))
+    Bi = datagen.integer_f16(cfg, 11, (N, K))
+    Di = _gemm(env, Ai, Bi)
+    assert np.array_equal(Di[torch.from_numpy(rows).to(dev)].cpu().numpy(), oracle.gemm(Ai, Bi, rows=rows))
+    # every element of the last rows (the ragged tile row) as well
+    last = np.arange(M - 40, M)
+    assert np.array_equal(Di[torch.from_numpy(last).to(dev)].cpu().numpy(), oracle.gemm(Ai, Bi, rows=last))
 
 
 @pytest.mark.parametrize("variant", list(range(1, 18)))
