@@ -111,6 +111,15 @@ def cpu_baseline(target_s: float):
     t0 = time.perf_counter()
     oracle.gemv(x, W, lib=lib)
     dtv = time.perf_counter() - t0
+    # one core: the whole 256^3 GEMM and the whole GEMV
+    w0 = datagen.WORKLOADS[0]
+    A0, B0 = datagen.gemm_inputs(w0)
+    t0 = time.perf_counter()
+    oracle.gemm(A0, B0, nthreads=1, lib=lib)
+    dt0 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.gemv(x, W, nthreads=1, lib=lib)
+    dtv1 = time.perf_counter() - t0
     from gemv_tile_pipelined_amd import metrics
 
     return {
@@ -123,6 +132,12 @@ def cpu_baseline(target_s: float):
         "seconds": dt,
         "gemv_gbps": metrics.gemv_bytes(wv.N, wv.K) / dtv / 1e9,
         "gemv_seconds": dtv,
+        "single_core": {
+            "gemm_256cube_gflops": 2.0 * w0.M * w0.N * w0.K / dt0 / 1e9,
+            "gemm_256cube_seconds": dt0,
+            "gemv_gbps": metrics.gemv_bytes(wv.N, wv.K) / dtv1 / 1e9,
+            "gemv_seconds": dtv1,
+        },
         "cpu_model": _cpu_model(),
     }
 
