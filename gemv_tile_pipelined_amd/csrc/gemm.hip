@@ -154,6 +154,12 @@ struct GemmShape {
   static constexpr int kKSub = BK / kKStep;  // MFMA K steps per K tile
 
   static_assert(BK == 32 || BK == 64, "LDS rows of 64 or 128 bytes");
+  // The pipelined loop double-buffers the operand fragments by K-step parity
+  // (step ks of a K tile computes from buffer ks & 1 and fills the other), so
+  // a K tile must hold an even number of K steps for the parity to carry
+  // over to the next tile: K tiles of 64 with 16x16x32 blocks, of 32 or 64
+  // with 32x32x16 blocks.
+  static_assert(STAGES_ == 1 || (BK / kKStep) % 2 == 0, "pipelined loop needs an even number of K steps per K tile");
   static_assert(kWaveM % MI == 0 && kWaveN % MI == 0, "wave tile must be whole MFMA blocks");
   static_assert(BM % (kRowsPerDma * kWaves) == 0 && BN % (kRowsPerDma * kWaves) == 0, "DMA split");
   static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
