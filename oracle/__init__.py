@@ -69,6 +69,10 @@ def load(path: str = LIBRARY, build_if_missing: bool = True):
     lib.oracle_gemm_bf16.restype = ctypes.c_int
     lib.oracle_gemv_bf16.argtypes = [u16p, u16p, u16p, i64, i64, ctypes.c_int]
     lib.oracle_gemv_bf16.restype = ctypes.c_int
+    lib.oracle_gemm_bias_f16.argtypes = [u16p, u16p, u16p, ctypes.c_int, u16p, i64, i64, i64, i64p, i64, ctypes.c_int]
+    lib.oracle_gemm_bias_f16.restype = ctypes.c_int
+    lib.oracle_gemm_bias_bf16.argtypes = [u16p, u16p, u16p, ctypes.c_int, u16p, i64, i64, i64, i64p, i64, ctypes.c_int]
+    lib.oracle_gemm_bias_bf16.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     if path == LIBRARY:
@@ -211,6 +215,46 @@ def gemv_bf16(x: np.ndarray, W: np.ndarray, nthreads: int = 0, lib=None) -> np.n
     if rc != 0:
         raise ValueError(f"oracle_gemv_bf16 failed ({rc})")
     return y
+
+
+ACT_NONE = 0
+ACT_RELU = 1
+
+
+def _gemm_bias(fname, to_bits, dtype, A, B, bias, act, rows, nthreads, lib):
+    lib = lib or load()
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2
+    # keep the (possibly copied) contiguous arrays alive while C reads them
+    a_arr, pa = to_bits(A)
+    b_arr, pb = to_bits(B)
+    bias_arr, pbias = (None, None) if bias is None else to_bits(bias)
+    assert bias is None or np.shape(bias) == (N,)
+    if rows is None:
+        nrows, prow = M, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows, prow = rows.size, rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    D = np.empty((nrows, N), dtype)
+    _, pd = to_bits(D)
+    rc = getattr(lib, fname)(pa, pb, pbias, int(act), pd, M, N, K, prow, nrows, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"{fname} failed ({rc})")
+    return D
+
+
+def gemm_bias(A: np.ndarray, B: np.ndarray, bias=None, act: int = ACT_NONE, rows=None, nthreads: int = 0,
+              lib=None) -> np.ndarray:
+    """D = act(A·Bᵀ + bias) in FP64 (bias [N] added to every row, act
+    ACT_NONE or ACT_RELU), rounded once to fp16."""
+    return _gemm_bias("oracle_gemm_bias_f16", _u16, np.float16, A, B, bias, act, rows, nthreads, lib)
+
+
+def gemm_bias_bf16(A: np.ndarray, B: np.ndarray, bias=None, act: int = ACT_NONE, rows=None, nthreads: int = 0,
+                   lib=None) -> np.ndarray:
+    """gemm_bias for bf16 bit arrays (uint16 in and out)."""
+    return _gemm_bias("oracle_gemm_bias_bf16", _bf16_bits, np.uint16, A, B, bias, act, rows, nthreads, lib)
 
 
 def max_threads(lib=None) -> int:

@@ -36,6 +36,16 @@
  * GEMV are the same definitions with bf16 in and out; their conversions are
  * written here from that format's definition, in the same way.
  *
+ * GEMM with a bias and an activation (not defined on the pages, which end
+ * their epilogue at the rounded store; this is the plain definition of the
+ * usual fused epilogue):
+ *
+ *          D[m,n] = RNE( act( sum_{k<K} A[m,k] * B[n,k] + bias[n] ) )
+ *
+ *          bias [N] in the element format, added to every row; act is the
+ *          identity (0) or ReLU (1): act(v) = +0 for v < 0, else v (a NaN
+ *          stays NaN).  Still one rounding, after the activation.
+ *
  * Parallel over output rows with OpenMP; nothing else is reordered, blocked
  * or fused.
  */
@@ -199,15 +209,17 @@ static double *decode_matrix(int fmt, const uint16_t *src, int64_t count)
  * GEMM on a chosen set of output rows, elements in format fmt.
  *   A     [M,K] bits, row-major
  *   B     [N,K] bits, row-major
+ *   bias  [N] bits added to every output row before the activation, or NULL
+ *   act   0: identity, 1: ReLU
  *   rows  nrows row indices into [0,M); NULL means all rows 0..M-1
  *   D     [nrows, N] bits, row-major (row r of D is output row rows[r])
  * Returns 0 on success, -1 on a bad argument or out of memory.
  */
-static int gemm_fmt(int fmt, const uint16_t *A, const uint16_t *B, uint16_t *D,
+static int gemm_fmt(int fmt, const uint16_t *A, const uint16_t *B, const uint16_t *bias, int act, uint16_t *D,
                     int64_t M, int64_t N, int64_t K,
                     const int64_t *rows, int64_t nrows, int nthreads)
 {
-    if (M < 0 || N < 0 || K < 0 || nrows < 0) return -1;
+    if (M < 0 || N < 0 || K < 0 || nrows < 0 || act < 0 || act > 1) return -1;
     if (!rows) nrows = M;
     for (int64_t r = 0; rows && r < nrows; ++r)
         if (rows[r] < 0 || rows[r] >= M) return -1;
@@ -239,6 +251,8 @@ static int gemm_fmt(int fmt, const uint16_t *A, const uint16_t *B, uint16_t *D,
                 const double *brow = Bd + n * K;
                 double sum = 0.0;
                 for (int64_t k = 0; k < K; ++k) sum += arow[k] * brow[k];
+                if (bias) sum += decode(fmt, bias[n]);
+                if (act == 1 && sum < 0.0) sum = 0.0;
                 D[r * N + n] = encode(fmt, sum);
             }
         }
@@ -252,14 +266,28 @@ int oracle_gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
                     int64_t M, int64_t N, int64_t K,
                     const int64_t *rows, int64_t nrows, int nthreads)
 {
-    return gemm_fmt(0, A, B, D, M, N, K, rows, nrows, nthreads);
+    return gemm_fmt(0, A, B, NULL, 0, D, M, N, K, rows, nrows, nthreads);
 }
 
 int oracle_gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *D,
                      int64_t M, int64_t N, int64_t K,
                      const int64_t *rows, int64_t nrows, int nthreads)
 {
-    return gemm_fmt(1, A, B, D, M, N, K, rows, nrows, nthreads);
+    return gemm_fmt(1, A, B, NULL, 0, D, M, N, K, rows, nrows, nthreads);
+}
+
+int oracle_gemm_bias_f16(const uint16_t *A, const uint16_t *B, const uint16_t *bias, int act, uint16_t *D,
+                         int64_t M, int64_t N, int64_t K,
+                         const int64_t *rows, int64_t nrows, int nthreads)
+{
+    return gemm_fmt(0, A, B, bias, act, D, M, N, K, rows, nrows, nthreads);
+}
+
+int oracle_gemm_bias_bf16(const uint16_t *A, const uint16_t *B, const uint16_t *bias, int act, uint16_t *D,
+                          int64_t M, int64_t N, int64_t K,
+                          const int64_t *rows, int64_t nrows, int nthreads)
+{
+    return gemm_fmt(1, A, B, bias, act, D, M, N, K, rows, nrows, nthreads);
 }
 
 /*

@@ -14,6 +14,7 @@ import pytest
 import oracle
 import test_oracle
 import test_oracle_bf16
+import test_oracle_bias
 
 MUTANTS = {
     "drop_last_k_term": ("for (int64_t k = 0; k < K; ++k) sum += arow[k] * brow[k];",
@@ -41,6 +42,15 @@ MUTANTS = {
                              "return oracle_f16_to_f64(bits);"),
     "bf16_encoded_as_fp16": ("return fmt ? oracle_f64_to_bf16_rne(v) : oracle_f64_to_f16_rne(v);",
                              "return oracle_f64_to_f16_rne(v);"),
+    # bias and activation
+    "bias_dropped": ("if (bias) sum += decode(fmt, bias[n]);", "if (0) sum += decode(fmt, bias[n]);"),
+    "bias_indexed_by_row": ("if (bias) sum += decode(fmt, bias[n]);", "if (bias) sum += decode(fmt, bias[m % N]);"),
+    "bias_subtracted": ("if (bias) sum += decode(fmt, bias[n]);", "if (bias) sum -= decode(fmt, bias[n]);"),
+    "relu_before_bias": ("if (bias) sum += decode(fmt, bias[n]);\n                if (act == 1 && sum < 0.0) sum = 0.0;",
+                         "if (act == 1 && sum < 0.0) sum = 0.0;\n                if (bias) sum += decode(fmt, bias[n]);"),
+    "relu_as_abs": ("if (act == 1 && sum < 0.0) sum = 0.0;", "if (act == 1 && sum < 0.0) sum = -sum;"),
+    "relu_threshold": ("if (act == 1 && sum < 0.0) sum = 0.0;", "if (act == 1 && sum < 1.0) sum = 0.0;"),
+    "relu_negative_zero": ("if (act == 1 && sum < 0.0) sum = 0.0;", "if (act == 1 && sum < 0.0) sum = -0.0;"),
 }
 
 
@@ -64,7 +74,7 @@ def test_mutant_is_caught(name, mutant_dir):
     oracle.compile_oracle(source=path, output=lib_path)
     lib = oracle.load(lib_path)
     caught = []
-    for check in test_oracle.ALL_CHECKS + test_oracle_bf16.ALL_CHECKS:
+    for check in test_oracle.ALL_CHECKS + test_oracle_bf16.ALL_CHECKS + test_oracle_bias.ALL_CHECKS:
         try:
             check(lib)
         except (AssertionError, ValueError, IndexError):
