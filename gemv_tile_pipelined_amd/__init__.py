@@ -29,6 +29,10 @@ __all__ = [
     "gemv_bf16",
     "gemm_bf16_ptr",
     "gemv_bf16_ptr",
+    "gemm_bias_f16",
+    "gemm_bias_bf16",
+    "ACT_NONE",
+    "ACT_RELU",
     "gemm_f16_variant",
     "gemv_f16_variant",
     "status_string",
@@ -50,6 +54,8 @@ EXPORTED_SYMBOLS = (
     "gemv_f16",
     "gemm_bf16",
     "gemv_bf16",
+    "gemm_bias_f16",
+    "gemm_bias_bf16",
     "gemvtile_status_string",
     "gemvtile_tile_coord",
     "gemvtile_gemm_config",
@@ -102,6 +108,10 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemm_f16.restype = c_int
     lib.gemv_f16.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.gemv_f16.restype = c_int
+    lib.gemm_bias_f16.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, vp]
+    lib.gemm_bias_f16.restype = c_int
+    lib.gemm_bias_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, vp]
+    lib.gemm_bias_bf16.restype = c_int
     lib.gemm_bf16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.gemm_bf16.restype = c_int
     lib.gemv_bf16.argtypes = [vp, vp, vp, i64, i64, vp]
@@ -237,6 +247,42 @@ def gemm_bf16(A, B, D=None, stream=None):
     Enqueued on `stream` (default: the current stream) and not synchronised.
     """
     return _gemm(A, B, D, stream, _torch().bfloat16, load_library().gemm_bf16)
+
+
+# Activation codes of gemm_bias_* (gemvtile_act in gemvtile.h).
+ACT_NONE = 0
+ACT_RELU = 1
+
+
+def _gemm_bias(A, B, bias, act, D, stream, dtype, call):
+    torch = _torch()
+    if isinstance(act, str):
+        act = {"none": ACT_NONE, "relu": ACT_RELU}[act]
+    N = B.shape[0] if isinstance(B, torch.Tensor) and B.dim() == 2 else None
+    if bias is not None:
+        _require(bias, "bias", 1, dtype)
+        if N is not None and bias.shape[0] != N:
+            raise ValueError(f"bias must have {N} elements, got {tuple(bias.shape)}")
+        if bias.device != A.device:
+            raise ValueError("bias must be on the device of A")
+    bias_ptr = None if bias is None else bias.data_ptr()
+
+    def with_bias(a, b, d, M, N, K, s):
+        return call(a, b, bias_ptr, d, M, N, K, int(act), s)
+
+    return _gemm(A, B, D, stream, dtype, with_bias)
+
+
+def gemm_bias_f16(A, B, bias=None, act=ACT_NONE, D=None, stream=None):
+    """D = act(A · Bᵀ + bias) on the device, one fp16 rounding.  A [M,K],
+    B [N,K], bias [N] (or None), D [M,N] fp16 contiguous; act "none"/"relu"
+    (or ACT_NONE / ACT_RELU).  Enqueued on `stream`, not synchronised."""
+    return _gemm_bias(A, B, bias, act, D, stream, _torch().float16, load_library().gemm_bias_f16)
+
+
+def gemm_bias_bf16(A, B, bias=None, act=ACT_NONE, D=None, stream=None):
+    """gemm_bias_f16 on bfloat16 tensors."""
+    return _gemm_bias(A, B, bias, act, D, stream, _torch().bfloat16, load_library().gemm_bias_bf16)
 
 
 def _gemv(x, W, y, stream, dtype, call):

@@ -168,6 +168,38 @@ int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   return run_gemm(A, B, D, M, N, K, stream, 0);
 }
 
+}  // extern "C"
+
+namespace {
+// gemm_bias_f16 / gemm_bias_bf16: the GEMM checks, then the activation code
+// and the bias pointer (element aligned, may be NULL), before any HIP call.
+int run_gemm_bias(const void *A, const void *B, const void *bias, void *D, int64_t M, int64_t N, int64_t K, int act,
+                  void *stream, int dtype) {
+  if (act != GEMVTILE_ACT_NONE && act != GEMVTILE_ACT_RELU) return GEMVTILE_ERR_INVALID_ARG;
+  bool noop = false;
+  int st = check_gemm(A, B, D, M, N, K, &noop);
+  if (st != GEMVTILE_OK || noop) return st;
+  if (bias != nullptr && misaligned(bias, 2)) return GEMVTILE_ERR_UNSUPPORTED;
+  int cus = 0;
+  st = current_cu_count(&cus);
+  if (st != GEMVTILE_OK) return st;
+  return to_status(gt::launch_gemm_bias(dtype, A, B, bias, act == GEMVTILE_ACT_RELU ? 1 : 0, D, static_cast<int>(M),
+                                        static_cast<int>(N), static_cast<int>(K), cus, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+int gemm_bias_f16(const void *A, const void *B, const void *bias, void *D, int64_t M, int64_t N, int64_t K, int act,
+                  void *stream) {
+  return run_gemm_bias(A, B, bias, D, M, N, K, act, stream, gt::kF16);
+}
+
+int gemm_bias_bf16(const void *A, const void *B, const void *bias, void *D, int64_t M, int64_t N, int64_t K, int act,
+                   void *stream) {
+  return run_gemm_bias(A, B, bias, D, M, N, K, act, stream, gt::kBF16);
+}
+
 int gemv_f16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream) {
   return run_gemv(x, W, y, N, K, stream, 0);
 }

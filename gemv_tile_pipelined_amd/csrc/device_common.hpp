@@ -29,6 +29,16 @@ __device__ inline _Float16 round_out(float x) {
   else return __builtin_bit_cast(_Float16, static_cast<__bf16>(x));
 }
 
+// A 16-bit pattern of the element format, widened to FP32 (exact).
+template <int DT>
+__device__ inline float widen_in(uint16_t bits) {
+  if constexpr (DT == kF16) return static_cast<float>(__builtin_bit_cast(_Float16, bits));
+  else return __builtin_bit_cast(float, static_cast<uint32_t>(bits) << 16);
+}
+
+// The fused epilogue's activation: +0 for v < 0, else v (a NaN stays NaN).
+__device__ inline float relu_act(float v) { return v < 0.0f ? 0.0f : v; }
+
 #define GT_LDS __attribute__((address_space(3)))
 
 // Byte offset of a __shared__ object inside the workgroup's LDS allocation.

@@ -211,10 +211,14 @@ __device__ inline void wait_tile_landed(int younger) {
 
 // One wave per SIMD for 4 waves; with 8 waves two per SIMD, so each is held
 // to half the register file.
-template <class S>
+// FUSED: the epilogue adds bias[n] and applies ReLU when `relu` is set
+// (gemm_bias_*), before the rounding; the other instantiations ignore `bias`
+// and `relu`.
+template <class S, bool FUSED = false>
 __global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWaves / 4, S::kWaves / 4)))
 gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
-                int M, int N, int K, int tiles_m, int tiles_n, int vec16) {
+                int M, int N, int K, int tiles_m, int tiles_n, int vec16, const uint16_t *__restrict__ bias,
+                int relu) {
   __shared__ __attribute__((aligned(1024))) char smem[S::kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -601,6 +605,25 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
     workgroup_barrier();  // every wave is done reading the ring
     {
       const uint32_t stage_base = static_cast<uint32_t>(wave * S::kWaveM * S::kStagePitch);
+      // Column of this lane's 4 values of group g of block column j inside
+      // the wave tile.
+      auto lane_col = [&](int j, int g) {
+        return S::MI == 32 ? j * 32 + g * 8 + frag_kgrp * 4 : j * 16 + frag_kgrp * 4;
+      };
+      // The bias of every column this lane holds, loaded once per tile
+      // (columns past N read the last bias; their outputs are not stored).
+      float bv[S::kFragN][S::kAccRegs];
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int j = 0; j < S::kFragN; ++j)
+#pragma unroll
+          for (int g = 0; g < S::kAccRegs / 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int n = min(n0 + wn * S::kWaveN + lane_col(j, g) + e, N - 1);
+              bv[j][4 * g + e] = bias ? widen_in<S::DTYPE>(bias[n]) : 0.0f;
+            }
+      }
 #pragma unroll
       for (int i = 0; i < S::kFragM; ++i) {
 #pragma unroll
@@ -609,11 +632,19 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
           for (int g = 0; g < S::kAccRegs / 4; ++g) {
             half4_t h;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = round_out<S::DTYPE>(acc[i][j][4 * g + e]);
-            // Column of this lane's 4 values inside the wave tile.
-            const int col = S::MI == 32 ? j * 32 + g * 8 + frag_kgrp * 4 : j * 16 + frag_kgrp * 4;
+            for (int e = 0; e < 4; ++e) {
+              float v = acc[i][j][4 * g + e];
+              if constexpr (FUSED) {
+                // With no bias this adds +0: every value but -0 stays as it
+                // is, and -0 becomes +0, as the exact sum (which starts at
+                // +0) would be.
+                v += bv[j][4 * g + e];
+                if (relu) v = relu_act(v);
+              }
+              h[e] = round_out<S::DTYPE>(v);
+            }
             const uint32_t off =
-                stage_base + static_cast<uint32_t>((i * S::MI + frag_row) * S::kStagePitch + col * 2);
+                stage_base + static_cast<uint32_t>((i * S::MI + frag_row) * S::kStagePitch + lane_col(j, g) * 2);
             *reinterpret_cast<half4_t *>(smem + off) = h;
           }
         }
@@ -706,26 +737,26 @@ static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDe
                   GemmDefault::STAGES == kGemmStages && GemmDefault::kThreads == kGemmThreads,
               "kernels.hpp constants must describe the default kernel");
 
-template <class S>
+template <class S, bool FUSED = false>
 static hipError_t launch(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
-                         hipStream_t stream) {
+                         hipStream_t stream, const void *bias = nullptr, int relu = 0) {
   const int tiles_m = (M + S::BM - 1) / S::BM;
   const int tiles_n = (N + S::BN - 1) / S::BN;
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   const int64_t grid = S::PERSISTENT ? (tiles < num_cus ? tiles : num_cus) : tiles;
   // Whole 16-byte row segments of D are 16-byte aligned when N % 8 == 0.
   const int vec16 = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(D) % 16 == 0);
-  hipLaunchKernelGGL(gemm_kernel<S>, dim3(static_cast<unsigned>(grid)), dim3(S::kThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_kernel<S, FUSED>), dim3(static_cast<unsigned>(grid)), dim3(S::kThreads), 0, stream,
                      static_cast<const _Float16 *>(A), static_cast<const _Float16 *>(B), static_cast<_Float16 *>(D),
-                     M, N, K, tiles_m, tiles_n, vec16);
+                     M, N, K, tiles_m, tiles_n, vec16, static_cast<const uint16_t *>(bias), relu);
   return hipGetLastError();
 }
 
 // The shape-dependent default: the tile gemm_default_tile picks, with the
 // ring depth of kGemmTileShapes.
-template <int DT>
+template <int DT, bool FUSED = false>
 static hipError_t launch_default(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const void *bias = nullptr, int relu = 0) {
   using Big = std::conditional_t<DT == kF16, GemmDefault, GemmBf16>;
   static_assert(Big::BM == kGemmTileShapes[kTile256x256].bm && Big::BN == kGemmTileShapes[kTile256x256].bn &&
                     Big::STAGES == kGemmTileShapes[kTile256x256].stages &&
@@ -738,12 +769,29 @@ static hipError_t launch_default(const void *A, const void *B, void *D, int M, i
                 "kGemmTileShapes must describe the kernels launched for each tile");
   switch (gemm_default_tile(M, N, num_cus)) {
     case kTile256x128:
-      return launch<GemmTile256x128<DT, kGemmTileShapes[kTile256x128].stages>>(A, B, D, M, N, K, num_cus, stream);
+      return launch<GemmTile256x128<DT, kGemmTileShapes[kTile256x128].stages>, FUSED>(A, B, D, M, N, K, num_cus, stream,
+                                                                                bias, relu);
     case kTile128x256:
-      return launch<GemmTile128x256<DT, kGemmTileShapes[kTile128x256].stages>>(A, B, D, M, N, K, num_cus, stream);
+      return launch<GemmTile128x256<DT, kGemmTileShapes[kTile128x256].stages>, FUSED>(A, B, D, M, N, K, num_cus, stream,
+                                                                                bias, relu);
     case kTile128x128:
-      return launch<GemmTile128x128<DT, kGemmTileShapes[kTile128x128].stages>>(A, B, D, M, N, K, num_cus, stream);
-    default: return launch<Big>(A, B, D, M, N, K, num_cus, stream);
+      return launch<GemmTile128x128<DT, kGemmTileShapes[kTile128x128].stages>, FUSED>(A, B, D, M, N, K, num_cus, stream,
+                                                                                bias, relu);
+    default: return launch<Big, FUSED>(A, B, D, M, N, K, num_cus, stream, bias, relu);
+  }
+}
+
+// D[m,n] = act(bias[n]) (+0 where bias is NULL): the K == 0 case of the
+// fused epilogue, whose sums are empty.  A kernel rather than a memset so
+// the call stays capturable in a HIP graph.
+template <int DT>
+__global__ void fill_bias_kernel(_Float16 *__restrict__ D, const uint16_t *__restrict__ bias, int64_t M, int64_t N,
+                                 int relu) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < M * N; i += stride) {
+    float v = bias ? widen_in<DT>(bias[i % N]) : 0.0f;
+    if (relu) v = relu_act(v);
+    D[i] = round_out<DT>(v);
   }
 }
 
@@ -785,6 +833,24 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
 hipError_t launch_gemm_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                             hipStream_t stream) {
   return launch_default<kBF16>(A, B, D, M, N, K, num_cus, stream);
+}
+
+hipError_t launch_gemm_bias(int dtype, const void *A, const void *B, const void *bias, int relu, void *D, int M, int N,
+                            int K, int num_cus, hipStream_t stream) {
+  if (K == 0) {
+    const int64_t count = static_cast<int64_t>(M) * N;
+    const int64_t threads = 256;
+    int64_t blocks = (count + threads - 1) / threads;
+    if (blocks > 65536) blocks = 65536;
+    if (count <= 0) return hipSuccess;
+    auto kernel = dtype == kBF16 ? fill_bias_kernel<kBF16> : fill_bias_kernel<kF16>;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream,
+                       static_cast<_Float16 *>(D), static_cast<const uint16_t *>(bias), static_cast<int64_t>(M),
+                       static_cast<int64_t>(N), relu);
+    return hipGetLastError();
+  }
+  return dtype == kBF16 ? launch_default<kBF16, true>(A, B, D, M, N, K, num_cus, stream, bias, relu)
+                        : launch_default<kF16, true>(A, B, D, M, N, K, num_cus, stream, bias, relu);
 }
 
 }  // namespace gt

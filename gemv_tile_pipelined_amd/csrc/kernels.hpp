@@ -132,6 +132,11 @@ hipError_t launch_gemm_ws_f16(int variant, const void *A, const void *B, void *D
                               hipStream_t stream);
 hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream);
 // bf16 operands and results: the default launch shape of each kernel.
+// D = act(A·Bᵀ + bias) on the tiled kernel (the tile gemm_default_tile
+// picks, whatever the shape), dtype kF16 or kBF16; bias [N] or NULL, relu 0
+// or 1.  K == 0 fills D with act(bias).
+hipError_t launch_gemm_bias(int dtype, const void *A, const void *B, const void *bias, int relu, void *D, int M, int N,
+                            int K, int num_cus, hipStream_t stream);
 hipError_t launch_gemm_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                             hipStream_t stream);
 hipError_t launch_gemm_skinny_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,

@@ -3,7 +3,7 @@
     rocprofv3 --kernel-trace --output-format csv -d OUT -o sweep -- \\
         python3 -m gemv_tile_pipelined_amd.shape_sweep [--gemv N:K,...] [--skinny M:N:K,...]
             [--gemm M:N:K,...] [--gemv-variants 0,8] [--skinny-variants 0,25]
-            [--gemm-variants 0,53] [--gemm-data uniform,zero] [--rounds 1] [--warmup-s 1]
+            [--gemm-variants 0,53] [--gemm-data uniform,zero] [--rounds 1] [--warmup-s 1] [--gemm-bias]
             [--stream MB --stream-policies 1,2] [--vendor] [--reps 40] > OUT/log.txt
     python3 -m gemv_tile_pipelined_amd.shape_sweep --parse OUT OUT/log.txt
 
@@ -19,7 +19,8 @@ their values: uniform (U(-1,1) fp16, the default), m7 (the same with the
 fp16 mantissa cut to its top 7 bits, bf16's precision), int (integers in
 [-8, 8]) or zero, to show how the operands' bit activity moves the
 power-limited clock; --rounds repeats the variant list that many times,
-interleaved, so that a slow drift of the clock does not favour one variant,
+interleaved, so that a slow drift of the clock does not favour one variant
+(--gemm-bias adds gemm_bias_f16 with a bias and ReLU to each round),
 and the parse also prints each variant's median over the rounds.  Before
 the first segment, --warmup-s seconds of untimed 4096^3 GEMMs let the clock
 settle.  --stream MB runs
@@ -162,11 +163,16 @@ def run(a):
         for data in a.gemm_data.split(","):
             sets = [(operand((M, K), data), operand((N, K), data)) for _ in range(3)]
             D = torch.empty((M, N), dtype=torch.float16, device=dev)
+            bias = uni((N,), -4, 4)
             for rnd in range(a.rounds):
                 for v in gemm_variants:
                     segment({"kind": "gemm_f16", "M": M, "N": N, "K": K, "variant": v, "data": data,
                              "round": rnd, "flops": 2 * M * N * K},
                             lambda i, v=v: gt.gemm_f16(sets[i][0], sets[i][1], D, variant=v), 3)
+                if a.gemm_bias:
+                    segment({"kind": "gemm_bias", "M": M, "N": N, "K": K, "data": data, "round": rnd,
+                             "flops": 2 * M * N * K},
+                            lambda i: gt.gemm_bias_f16(sets[i][0], sets[i][1], bias, gt.ACT_RELU, D), 3)
                 if a.vendor:
                     segment({"kind": "torch.matmul", "M": M, "N": N, "K": K, "data": data, "round": rnd,
                              "flops": 2 * M * N * K},
@@ -228,6 +234,7 @@ def main(argv=None):
     p.add_argument("--gemm-variants", default="0")
     p.add_argument("--gemm-data", default="uniform", help="uniform,m7,int,zero (comma list)")
     p.add_argument("--rounds", type=int, default=1, help="times the --gemm-variants list runs, interleaved")
+    p.add_argument("--gemm-bias", action="store_true", help="also gemm_bias_f16 (bias + ReLU) on each GEMM shape")
     p.add_argument("--warmup-s", type=float, default=1.0, help="seconds of untimed GEMMs before the first segment")
     p.add_argument("--stream", type=float, default=0.0, help="MB per read-only probe launch (0: none)")
     p.add_argument("--stream-policies", default="1,2")

@@ -119,6 +119,43 @@ int gemv_f16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *
 int gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream);
 int gemv_bf16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream);
 
+/* Activation codes of the fused epilogue. */
+enum gemvtile_act {
+    GEMVTILE_ACT_NONE = 0, /* identity */
+    GEMVTILE_ACT_RELU = 1  /* v < 0 -> +0, else v (a NaN stays NaN) */
+};
+
+/*
+ * gemm_bias_f16 / gemm_bias_bf16 -- the GEMM with a fused epilogue: a bias
+ * added to every row and an activation, before the one rounding.
+ *
+ *   D[m,n] = rne( act( sum_{k<K} A[m,k] * B[n,k] + bias[n] ) )
+ *
+ * The pages' kernels end their epilogue at the rounded store and define no
+ * bias or activation; this is the plain definition of the usual fused
+ * epilogue, in the same element format as gemm_f16 (fp16) or gemm_bf16
+ * (bf16).  The sum is accumulated in FP32, bias[n] is added in FP32, the
+ * activation is applied, and the result is rounded once (nearest, ties to
+ * even).
+ *
+ *   A, B, D, M, N, K, stream  as for gemm_f16 / gemm_bf16 (same layouts,
+ *            limits, alignment and degenerate shapes)
+ *   bias   device pointer to N elements of the operand format, 2-byte
+ *          aligned, or NULL for no bias
+ *   act    GEMVTILE_ACT_NONE or GEMVTILE_ACT_RELU
+ *
+ * K == 0: D[m,n] = act(bias[n]) (+0 with no bias).  Every shape runs the
+ * tiled kernel with the tile gemvtile_gemm_tile gives (the skinny and GEMV
+ * kernels have no fused epilogue), so outputs with 16 rows or fewer on a
+ * side are slower here than through gemm_f16.  An unknown act returns
+ * GEMVTILE_ERR_INVALID_ARG, a misaligned bias GEMVTILE_ERR_UNSUPPORTED, both
+ * before any HIP call.  Returns a gemvtile_status.
+ */
+int gemm_bias_f16(const void *A, const void *B, const void *bias, void *D, int64_t M, int64_t N, int64_t K, int act,
+                  void *stream);
+int gemm_bias_bf16(const void *A, const void *B, const void *bias, void *D, int64_t M, int64_t N, int64_t K, int act,
+                   void *stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *gemvtile_status_string(int status);
 

@@ -91,6 +91,27 @@ def test_gemm_argument_validation(lib):
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 144) == UNSUPPORTED
 
 
+def test_gemm_bias_argument_validation(lib):
+    """gemm_bias_f16 / gemm_bias_bf16: the GEMM checks, then the activation
+    code and the bias pointer, all before any HIP call."""
+    for fn in (lib.gemm_bias_f16, lib.gemm_bias_bf16):
+        # act must be NONE (0) or RELU (1), even for an empty output
+        for bad in (-1, 2, 7):
+            assert fn(FAKE, FAKE, FAKE, FAKE, 4, 4, 8, bad, None) == INVALID, bad
+            assert fn(None, None, None, None, 0, 4, 8, bad, None) == INVALID, bad
+        # the GEMM's own checks
+        assert fn(FAKE, FAKE, FAKE, FAKE, -1, 4, 8, 0, None) == INVALID
+        assert fn(FAKE, FAKE, FAKE, None, 4, 4, 8, 0, None) == INVALID
+        assert fn(None, FAKE, FAKE, FAKE, 4, 4, 8, 1, None) == INVALID
+        assert fn(FAKE, FAKE, FAKE, FAKE, 4, 4, 12, 0, None) == UNSUPPORTED
+        assert fn(FAKE + 8, FAKE, FAKE, FAKE, 4, 4, 8, 0, None) == UNSUPPORTED
+        # empty outputs are a no-op, with or without a bias
+        assert fn(None, None, None, None, 0, 4, 8, 1, None) == OK
+        assert fn(None, None, FAKE, None, 4, 0, 8, 0, None) == OK
+        # the bias must be element aligned (NULL is allowed: no bias)
+        assert fn(FAKE, FAKE, FAKE + 1, FAKE, 4, 4, 8, 0, None) == UNSUPPORTED
+
+
 def test_gemv_argument_validation(lib):
     assert _gemv(lib, FAKE, FAKE, FAKE, -1, 8) == INVALID
     assert _gemv(lib, FAKE, FAKE, FAKE, 4, -8) == INVALID

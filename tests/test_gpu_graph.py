@@ -4,8 +4,9 @@ Every call only enqueues kernels on the caller's stream: no allocation, no
 memset (K = 0 writes its zeros with a kernel), no host synchronisation.  A
 graph captured around them must therefore give, on every replay, exactly what
 the eager calls give.  The graph holds the tiled GEMM, the skinny GEMM, the
-K-split GEMV, a bf16 GEMM and a K = 0 fill; it is replayed several times with
-eager work between the replays, and every replay is compared bit for bit.
+K-split GEMV, a bf16 GEMM, a K = 0 fill and a GEMM with the fused bias and
+ReLU; it is replayed several times with eager work between the replays, and
+every replay is compared bit for bit.
 """
 import numpy as np
 import pytest
@@ -37,13 +38,15 @@ def test_graph_replays_match_eager():
     Bb = B.to(torch.bfloat16)
     A0 = torch.empty((33, 0), dtype=torch.float16, device=dev)
     B0 = torch.empty((70, 0), dtype=torch.float16, device=dev)
+    bias = t16(datagen.uniform_f16(9700, 6, (776,), -4.0, 4.0))
 
     D = torch.empty((520, 776), dtype=torch.float16, device=dev)
     Ds = torch.empty((8, 3000), dtype=torch.float16, device=dev)
     y = torch.empty((1000,), dtype=torch.float16, device=dev)
     Db = torch.empty((520, 776), dtype=torch.bfloat16, device=dev)
     D0 = torch.empty((33, 70), dtype=torch.float16, device=dev)
-    outs = (D, Ds, y, Db, D0)
+    Dr = torch.empty((520, 776), dtype=torch.float16, device=dev)
+    outs = (D, Ds, y, Db, D0, Dr)
 
     def work():
         gt.gemm_f16(A, B, D)
@@ -51,6 +54,7 @@ def test_graph_replays_match_eager():
         gt.gemv_f16(x, W, y)
         gt.gemm_bf16(Ab, Bb, Db)
         gt.gemm_f16(A0, B0, D0)
+        gt.gemm_bias_f16(A, B, bias, "relu", Dr)
 
     work()
     torch.cuda.synchronize(dev)
