@@ -8,7 +8,12 @@
 //   ("使用 TMA 为 GEMM 建立 Pipeline", step 4 full kernel) and of the SM120
 //   walk-through "TensorCore_GEMM_with_TMA" (§2.2 entrance, §2.3 kernel).
 //
-// Structure (one workgroup per CU, 4 waves, each wave a 128x128 sub-tile):
+// Structure (one workgroup per CU, 4 waves; with the default 256x256 output
+// tile each wave holds a 128x128 sub-tile):
+//
+//  * Tile shape -- 256x256 output tiles while they give every CU one; an
+//    output with fewer takes 256x128, 128x256 or 128x128 tiles, whose shorter
+//    K tiles get deeper LDS rings (gemm_default_tile, kernels.hpp).
 //
 //  * Tile scheduler -- a persistent grid of min(#tiles, #CUs) workgroups walks
 //    tile indices t = id, id + grid, ... in the grouped order of tile_order.hpp
@@ -35,27 +40,33 @@
 //    play the same role there).
 //
 //  * LDS ring -- STAGES buffers; K tile t lives in stage t % STAGES.  In the
-//    final 16-wide K step of tile k each wave waits (vmcnt) until tile k+1
-//    has landed while younger tiles stay in flight, completes its LDS reads,
-//    and meets the other waves at the one barrier of the K tile; that barrier
-//    frees stage k, whose refill with tile k + STAGES starts at once, the
-//    loads threaded between the MFMAs that follow.  Tile k+1's first
-//    operands are fetched during the same MFMAs.  Stage index and wait count follow from the
-//    loop counter, so nothing resets between output tiles (a ragged K = 4104
-//    has an odd number of K tiles).  TVM chapter step 5 (Pipeline 机制) and
-//    the SM120 page's multistage main loop describe the same ring with
-//    mbarriers.
+//    final K step of tile k each wave waits (vmcnt) until tile k+1 has landed
+//    while younger tiles stay in flight, completes its LDS reads, and meets
+//    the other waves at the one barrier of the K tile; that barrier frees
+//    stage k, whose refill with tile k + STAGES starts at once, the loads
+//    threaded between the MFMAs that follow.  Tile k+1's first operands are
+//    fetched during the same MFMAs.  Stage index and wait count follow from
+//    the loop counter, so nothing resets between output tiles (a ragged
+//    K = 4104 has an odd number of K tiles).  TVM chapter step 5 (Pipeline
+//    机制) and the SM120 page's multistage main loop describe the same ring
+//    with mbarriers.
 //
-//  * MFMA micro-kernel -- v_mfma_f32_32x32x16_f16.  B rows feed the first
-//    operand and A rows the second, so each lane ends up holding four
-//    consecutive output columns of one output row (8-byte stores).  Operand
-//    fetches for the next K step are interleaved with the current step's
-//    MFMAs.
+//  * MFMA micro-kernel -- v_mfma_f32_16x16x32_f16 (or _bf16), written as
+//    inline asm with the accumulators bound to AGPRs (the compiler's builtin
+//    moves them around the loop); the compiler does not see these as MFMAs,
+//    so their hazards are padded by hand, and the build checks the generated
+//    code for accumulator moves near them (build.py).  B rows feed the first
+//    operand and A rows the second, so each lane holds four consecutive
+//    output columns of one output row.  Operand fetches for the next K step
+//    are interleaved with the current step's MFMAs.  A 32x32x16 form through
+//    the compiler's builtin remains for ablation.
 //
-//  * Epilogue -- FP32 -> fp16 with round-to-nearest-even (the `_rn`
+//  * Epilogue -- FP32 -> fp16 or bf16 with round-to-nearest-even (the `_rn`
 //    conversion of the SM120 page's epilogue), staged through LDS so D is
-//    written in whole row segments (the TVM chapter likewise stages D in
-//    shared memory before its bulk store), masked to the M x N region.
+//    written in whole 16-byte row segments (the TVM chapter likewise stages D
+//    in shared memory before its bulk store), masked to the M x N region.
+//    The FUSED instantiations add bias[n] and apply ReLU before the rounding
+//    (gemm_bias_*; not on the pages).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
