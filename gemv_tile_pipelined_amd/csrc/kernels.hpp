@@ -20,7 +20,7 @@ constexpr int kGemmBK = 64;
 constexpr int kGemmStages = 2;
 constexpr int kGemmThreads = 256;
 constexpr int kGemmGroupM = 8;
-constexpr int kGemmVariants = 28;
+constexpr int kGemmVariants = 29;
 
 // Output tile of the tiled GEMM.  The 256x256 default needs about one tile
 // per CU to fill the chip; outputs that give fewer take smaller tiles, each

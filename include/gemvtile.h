@@ -66,7 +66,8 @@ enum gemvtile_status {
  * unspecified (several results are correct up to rounding).
  * Otherwise the tiled kernel runs with 256x256 output tiles, or with
  * 256x128, 128x256 or 128x128 ones when the output has too few 256x256
- * tiles to keep every compute unit busy (gemvtile_gemm_tile gives the choice).
+ * tiles to keep every compute unit busy (gemvtile_gemm_tile gives the choice);
+ * it writes D with non-temporal stores, so D is not left in the caches.
  * When M <= 16 or N <= 16 (a decode batch against a weight matrix) the call
  * runs a bandwidth-bound kernel that streams the larger operand once instead
  * of the tiled one (with fewer rows of it per workgroup when it has too few
@@ -240,7 +241,7 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
 /*
  * gemvtile_gemm_f16_variant -- gemm_f16 with an internal kernel variant, for
  * ablation measurements only (same contract and results as gemm_f16).  The
- * tiled ones 1..20 use 256x256 output tiles and (but for 13, 14) 4 waves of
+ * tiled ones 1..20 and 28 use 256x256 output tiles and (but for 13, 14) 4 waves of
  * 128x128:
  *   0  what gemm_f16 runs: on tiled shapes the tile of gemvtile_gemm_tile;
  *      with 256x256 tiles, 16x16x32 MFMA blocks, K tiles of 64 in a 2-stage
@@ -272,7 +273,9 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *      128x128 (4-stage ring) output tiles (4 waves of 128x64, 64x128,
  *      64x64): the smaller tiles of variant 0, whatever the shape
  *   24, 25, 26 as 21, 22, 23 with 2-stage rings   27 as 23 with 5 stages
- * Variants 1..27 always run the tiled kernel, whatever the shape; variant
+ *   28 as 20 with D written by ordinary (cached) stores instead of
+ *      non-temporal ones
+ * Variants 1..28 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16: the skinny kernel).  Each other kernel family has its own range:
  *   100..151 the skinny kernel (only for M <= 16 or N <= 16, else

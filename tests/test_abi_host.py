@@ -79,7 +79,7 @@ def test_gemm_argument_validation(lib):
     assert _gemm(lib, FAKE, FAKE, FAKE, 2**31, 4, 8) == UNSUPPORTED
     # unknown internal variant: each family has its own id range (tiled 0..,
     # skinny 100.., wave-specialised 200..); the gaps are invalid
-    for bad in (-1, 28, 99, 152, 199, 202, 1000):
+    for bad in (-1, 29, 99, 152, 199, 202, 1000):
         assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, bad) == INVALID, bad
     # skinny launch shapes only apply when one side has at most 16 rows
     assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 100) == UNSUPPORTED
