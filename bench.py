@@ -45,12 +45,12 @@ GEMV_COPIES = 5
 # valid only for the kernel sources whose SHA-256 is recorded here; the
 # summary and commands are in profiles/traffic_fetch_write_size.md.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "c9ab7eb345c799d94f3dc720888c2813072992dedd542bde0364259159cd98eb",
-    "gemm": {"fetch_kib": 98435.5 * 2.0, "write_kib": 32782.5 * 1.0},
+    "sources_sha256": "c518ec08b1c037d2d16d5735a33557d642c20f31d96af3bbed2059d67cf4d5fb",
+    "gemm": {"fetch_kib": 98433.6 * 2.0, "write_kib": 32784.0 * 1.0},
     "gemv": {"fetch_kib": 57475.2 * 2.0, "write_kib": 8.0 * 1.0},
     "decode": {"fetch_kib": 58265.5 * 2.0, "write_kib": 64.0 * 1.0},
-    "gemm_bf16": {"fetch_kib": 98433.7 * 2.0, "write_kib": 32785.1 * 1.0},
-    "gemv_bf16": {"fetch_kib": 57480.2 * 2.0, "write_kib": 8.0 * 1.0},
+    "gemm_bf16": {"fetch_kib": 98435.0 * 2.0, "write_kib": 32788.4 * 1.0},
+    "gemv_bf16": {"fetch_kib": 57480.8 * 2.0, "write_kib": 8.0 * 1.0},
 }
 KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemv.hip", "kernels.hpp", "skinny.hip", "tile_order.hpp")
 

@@ -31,6 +31,10 @@ __all__ = [
     "gemv_bf16_ptr",
     "gemm_bias_f16",
     "gemm_bias_bf16",
+    "gemm_splitk_f16",
+    "gemm_splitk_bf16",
+    "splitk_splits",
+    "splitk_workspace_bytes",
     "ACT_NONE",
     "ACT_RELU",
     "gemm_f16_variant",
@@ -56,6 +60,10 @@ EXPORTED_SYMBOLS = (
     "gemv_bf16",
     "gemm_bias_f16",
     "gemm_bias_bf16",
+    "gemm_splitk_f16",
+    "gemm_splitk_bf16",
+    "gemvtile_gemm_splitk_splits",
+    "gemvtile_gemm_splitk_workspace",
     "gemvtile_status_string",
     "gemvtile_tile_coord",
     "gemvtile_gemm_config",
@@ -112,6 +120,14 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemm_bias_f16.restype = c_int
     lib.gemm_bias_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, c_int, vp]
     lib.gemm_bias_bf16.restype = c_int
+    lib.gemm_splitk_f16.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
+    lib.gemm_splitk_f16.restype = c_int
+    lib.gemm_splitk_bf16.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
+    lib.gemm_splitk_bf16.restype = c_int
+    lib.gemvtile_gemm_splitk_splits.argtypes = [i64, i64, i64, i64]
+    lib.gemvtile_gemm_splitk_splits.restype = c_int
+    lib.gemvtile_gemm_splitk_workspace.argtypes = [i64, i64, i64, i64]
+    lib.gemvtile_gemm_splitk_workspace.restype = i64
     lib.gemm_bf16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.gemm_bf16.restype = c_int
     lib.gemv_bf16.argtypes = [vp, vp, vp, i64, i64, vp]
@@ -283,6 +299,48 @@ def gemm_bias_f16(A, B, bias=None, act=ACT_NONE, D=None, stream=None):
 def gemm_bias_bf16(A, B, bias=None, act=ACT_NONE, D=None, stream=None):
     """gemm_bias_f16 on bfloat16 tensors."""
     return _gemm_bias(A, B, bias, act, D, stream, _torch().bfloat16, load_library().gemm_bias_bf16)
+
+
+def splitk_splits(M: int, N: int, K: int, num_cus: int) -> int:
+    """K slices gemm_splitk_* uses for M x N x K on num_cus CUs (1: no split)."""
+    return int(load_library().gemvtile_gemm_splitk_splits(M, N, K, num_cus))
+
+
+def splitk_workspace_bytes(M: int, N: int, K: int, num_cus: int) -> int:
+    """Workspace bytes gemm_splitk_* needs (0 when it does not split)."""
+    return int(load_library().gemvtile_gemm_splitk_workspace(M, N, K, num_cus))
+
+
+def _gemm_splitk(A, B, D, workspace, stream, dtype, call):
+    torch = _torch()
+    if workspace is None:
+        _require(A, "A", 2, dtype)
+        _require(B, "B", 2, dtype)
+        cus = torch.cuda.get_device_properties(A.device).multi_processor_count
+        need = splitk_workspace_bytes(A.shape[0], B.shape[0], A.shape[1], cus)
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=A.device) if need else None
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or not workspace.is_cuda):
+        raise TypeError("workspace must be a device tensor")
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+    def with_ws(a, b, d, M, N, K, s):
+        return call(a, b, d, M, N, K, ws_ptr, ws_bytes, s)
+
+    return _gemm(A, B, D, stream, dtype, with_ws)
+
+
+def gemm_splitk_f16(A, B, D=None, workspace=None, stream=None):
+    """D = A · Bᵀ with K split across workgroups for small outputs; fp16.
+    `workspace`: a device tensor of at least splitk_workspace_bytes(...)
+    bytes, or None to allocate one here.  Enqueued on `stream`, not
+    synchronised."""
+    return _gemm_splitk(A, B, D, workspace, stream, _torch().float16, load_library().gemm_splitk_f16)
+
+
+def gemm_splitk_bf16(A, B, D=None, workspace=None, stream=None):
+    """gemm_splitk_f16 on bfloat16 tensors."""
+    return _gemm_splitk(A, B, D, workspace, stream, _torch().bfloat16, load_library().gemm_splitk_bf16)
 
 
 def _gemv(x, W, y, stream, dtype, call):

@@ -200,6 +200,57 @@ int gemm_bias_bf16(const void *A, const void *B, const void *bias, void *D, int6
   return run_gemm_bias(A, B, bias, D, M, N, K, act, stream, gt::kBF16);
 }
 
+}  // extern "C"
+
+namespace {
+// Split K applies to shapes of the tiled kernel only (not to the GEMV or the
+// skinny kernel's shapes); elsewhere gemm_splitk_* is the plain GEMM.
+int splitk_splits(int64_t M, int64_t N, int64_t K, int cus) {
+  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows) return 1;
+  return gt::gemm_splitk_splits(M, N, K, cus);
+}
+
+int run_gemm_splitk(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *ws,
+                    int64_t ws_bytes, void *stream, int dtype) {
+  if (ws_bytes < 0) return GEMVTILE_ERR_INVALID_ARG;
+  bool noop = false;
+  int st = check_gemm(A, B, D, M, N, K, &noop);
+  if (st != GEMVTILE_OK || noop) return st;
+  int cus = 0;
+  st = current_cu_count(&cus);
+  if (st != GEMVTILE_OK) return st;
+  const int splits = K == 0 ? 1 : splitk_splits(M, N, K, cus);
+  if (splits == 1) return run_gemm(A, B, D, M, N, K, stream, 0, dtype);
+  if (ws == nullptr || ws_bytes < static_cast<int64_t>(splits) * M * N * 4) return GEMVTILE_ERR_INVALID_ARG;
+  if (misaligned(ws, 16)) return GEMVTILE_ERR_UNSUPPORTED;
+  return to_status(gt::launch_gemm_splitk(dtype, A, B, D, static_cast<int>(M), static_cast<int>(N),
+                                          static_cast<int>(K), ws, splits, cus, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+int gemm_splitk_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *workspace,
+                    int64_t workspace_bytes, void *stream) {
+  return run_gemm_splitk(A, B, D, M, N, K, workspace, workspace_bytes, stream, gt::kF16);
+}
+
+int gemm_splitk_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *workspace,
+                     int64_t workspace_bytes, void *stream) {
+  return run_gemm_splitk(A, B, D, M, N, K, workspace, workspace_bytes, stream, gt::kBF16);
+}
+
+int64_t gemvtile_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int64_t num_cus) {
+  if (M <= 0 || N <= 0 || K <= 0 || num_cus <= 0 || num_cus > (int64_t{1} << 20)) return 0;
+  const int splits = splitk_splits(M, N, K, static_cast<int>(num_cus));
+  return splits > 1 ? static_cast<int64_t>(splits) * M * N * 4 : 0;
+}
+
+int gemvtile_gemm_splitk_splits(int64_t M, int64_t N, int64_t K, int64_t num_cus) {
+  if (M <= 0 || N <= 0 || K <= 0 || num_cus <= 0 || num_cus > (int64_t{1} << 20)) return 1;
+  return splitk_splits(M, N, K, static_cast<int>(num_cus));
+}
+
 int gemv_f16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream) {
   return run_gemv(x, W, y, N, K, stream, 0);
 }

@@ -65,8 +65,10 @@
 //    conversion of the SM120 page's epilogue), staged through LDS so D is
 //    written in whole 16-byte row segments (the TVM chapter likewise stages D
 //    in shared memory before its bulk store), masked to the M x N region.
-//    The FUSED instantiations add bias[n] and apply ReLU before the rounding
-//    (gemm_bias_*; not on the pages).
+//    The fused instantiations add bias[n] and apply ReLU before the rounding
+//    (gemm_bias_*; not on the pages).  With split K (gemm_splitk_*) the units
+//    are (tile, K slice) pairs that store FP32 partial sums to a workspace,
+//    and a second kernel adds the slices in order and rounds.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -229,14 +231,20 @@ __device__ inline void wait_tile_landed(int younger) {
 
 // One wave per SIMD for 4 waves; with 8 waves two per SIMD, so each is held
 // to half the register file.
-// FUSED: the epilogue adds bias[n] and applies ReLU when `relu` is set
-// (gemm_bias_*), before the rounding; the other instantiations ignore `bias`
-// and `relu`.
-template <class S, bool FUSED = false>
+// Epilogue modes.  kEpiPlain: round and store D.  kEpiFused: add bias[n]
+// and apply ReLU when `relu` is set (gemm_bias_*), then round and store D.
+// kEpiPartial (split K, gemm_splitk_*): the grid walks (tile, K slice) units,
+// `splits` slices per tile; each unit sums only its slice of K tiles and
+// stores the FP32 sums, unrounded, to ws[slice][m][n]; splitk_reduce_kernel
+// adds the slices.  Each mode ignores the arguments of the others.
+enum : int { kEpiPlain = 0, kEpiFused = 1, kEpiPartial = 2 };
+
+template <class S, int EPI = kEpiPlain>
 __global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWaves / 4, S::kWaves / 4)))
 gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Float16 *__restrict__ D,
                 int M, int N, int K, int tiles_m, int tiles_n, int vec16, const uint16_t *__restrict__ bias,
-                int relu) {
+                int relu, float *__restrict__ ws, int splits) {
+  static_assert(EPI != kEpiPartial || (S::MI == 16 && S::STAGES >= 2), "split K uses the pipelined 16x16x32 loop");
   __shared__ __attribute__((aligned(1024))) char smem[S::kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -288,8 +296,12 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
   const uint32_t a_row_base = static_cast<uint32_t>(wm * S::kWaveM + frag_row) * S::kRowBytes;
   const uint32_t b_row_base = static_cast<uint32_t>(wn * S::kWaveN + frag_row) * S::kRowBytes + S::kStageA;
 
-  int64_t t = S::PERSISTENT ? xcd_logical_id(blockIdx.x, grid) : static_cast<int64_t>(blockIdx.x);
-  for (; t < num_tiles; t += grid) {
+  // Work units: output tiles, or (tile, K slice) pairs with split K, slice
+  // major, so that units running side by side share K ranges.
+  const int64_t num_units = EPI == kEpiPartial ? num_tiles * splits : num_tiles;
+  int64_t u = S::PERSISTENT ? xcd_logical_id(blockIdx.x, grid) : static_cast<int64_t>(blockIdx.x);
+  for (; u < num_units; u += grid) {
+    const int64_t t = EPI == kEpiPartial ? u % num_tiles : u;
     const TileCoord tc = grouped_tile(t, tiles_m, tiles_n, kGemmGroupM);
     const int m0 = static_cast<int>(tc.tm) * S::BM;
     const int n0 = static_cast<int>(tc.tn) * S::BN;
@@ -308,9 +320,19 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
 
     // Loads [first, last) of the kDmaPerStage per-wave DMA instructions of K
     // tile kt (A tile first, then B tile).
-    // K tile kt of the loop reads K tile (kt + kofs) mod KT of the matrices.
+    // K tile kt of the loop reads K tile (kt + kofs) mod KT of the matrices;
+    // the loop runs over KTu K tiles (all KT of them, or one K slice).
     int kofs = 0;
-    if constexpr (S::K_STAGGER > 1) kofs = static_cast<int>((t % S::K_STAGGER) * S::K_STAGGER_STEP) % KT;
+    int KTu = KT;
+    int slice = 0;
+    if constexpr (EPI == kEpiPartial) {
+      slice = static_cast<int>(u / num_tiles);
+      const int per = (KT + splits - 1) / splits;  // the host keeps every slice non-empty
+      kofs = slice * per;
+      KTu = min(per, KT - kofs);
+    } else if constexpr (S::K_STAGGER > 1) {
+      kofs = static_cast<int>((t % S::K_STAGGER) * S::K_STAGGER_STEP) % KT;
+    }
     // Operands of load d of K tile kt: buffer descriptor, per-lane byte
     // offset, and the (wave-uniform) LDS address of its 1 KiB destination.
     struct DmaArgs {
@@ -454,7 +476,7 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
     if constexpr (S::STAGES == 1) {
       // No overlap: load, wait, compute -- the serial order the TVM chapter
       // starts from before its step 5 adds a second stage.
-      for (int kt = 0; kt < KT; ++kt) {
+      for (int kt = 0; kt < KTu; ++kt) {
         issue_loads(kt, 0, S::kDmaPerStage);
         wait_vmcnt<0>();
         workgroup_barrier();
@@ -529,10 +551,10 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
 #pragma unroll
           for (int idx = 0; idx < kMfma; ++idx) {
             if (last && kNext && idx == kBarrierAt) {
-              // Tiles 0 .. min(KT, kt + STAGES) - 1 have been issued in full;
+              // Tiles 0 .. min(KTu, kt + STAGES) - 1 have been issued in full;
               // tile kt+1 must have landed for every wave, and every wave must
               // be done reading stage kt before anyone refills it.
-              wait_tile_landed<S>(min(KT, kt + S::STAGES) - (kt + 2));
+              wait_tile_landed<S>(min(KTu, kt + S::STAGES) - (kt + 2));
               __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
               workgroup_barrier();
               __builtin_amdgcn_sched_barrier(0);
@@ -586,13 +608,13 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       constexpr int kPrologueTiles = S::PROLOGUE_ALL ? S::STAGES : S::STAGES - 1;
 #pragma unroll
       for (int s = 0; s < kPrologueTiles; ++s)
-        if (s < KT) issue_loads(s, 0, S::kDmaPerStage);
-      wait_tile_landed<S>(min(KT, kPrologueTiles) - 1);
+        if (s < KTu) issue_loads(s, 0, S::kDmaPerStage);
+      wait_tile_landed<S>(min(KTu, kPrologueTiles) - 1);
       workgroup_barrier();
       load_frags(0, 0, 0);
       // The chain of refill loads starts with load 0 of K tile STAGES-1.
       if constexpr (S::PRESET_M0) set_m0(dma_args(S::STAGES - 1, 0).lds);
-      if (!S::PROLOGUE_ALL && S::STAGES - 1 < KT) {
+      if (!S::PROLOGUE_ALL && S::STAGES - 1 < KTu) {
 #pragma unroll
         for (int pos = 0; pos < kAfter; ++pos) dma_slot(S::STAGES - 1, pos);
       }
@@ -600,12 +622,12 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       using yes = std::true_type;
       using no = std::false_type;
       int kt = 0;
-      for (; kt + S::STAGES < KT; ++kt) ktile(kt, yes{}, yes{}, yes{});  // steady state
-      if (kt + S::STAGES == KT && kt + 1 < KT) {                       // last refill
+      for (; kt + S::STAGES < KTu; ++kt) ktile(kt, yes{}, yes{}, yes{});  // steady state
+      if (kt + S::STAGES == KTu && kt + 1 < KTu) {                       // last refill
         ktile(kt, yes{}, no{}, yes{});
         ++kt;
       }
-      for (; kt + 1 < KT; ++kt) ktile(kt, no{}, no{}, yes{});  // the ring drains
+      for (; kt + 1 < KTu; ++kt) ktile(kt, no{}, no{}, yes{});  // the ring drains
       ktile(kt, no{}, no{}, no{});                             // last K tile
     }
 
@@ -621,7 +643,31 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
     // writes whole 16-byte-per-lane row segments (full cache lines).
     mfma_drain();
     workgroup_barrier();  // every wave is done reading the ring
-    {
+    if constexpr (EPI == kEpiPartial) {
+      // FP32 sums of this K slice, unrounded, straight from the accumulators:
+      // lane l holds columns 4*(l/16) .. +3 of row l % 16 of each 16x16
+      // block, a 16-byte piece (ordinary stores: the reduction reads them
+      // next, from the caches).
+      float *wsl = ws + static_cast<int64_t>(slice) * M * N;
+      const bool vec4 = (N % 4) == 0;
+#pragma unroll
+      for (int i = 0; i < S::kFragM; ++i) {
+        const int m = m0 + wm * S::kWaveM + i * 16 + frag_row;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < S::kFragN; ++j) {
+          const int n = n0 + wn * S::kWaveN + j * 16 + frag_kgrp * 4;
+          float *dst = wsl + static_cast<int64_t>(m) * N + n;
+          if (vec4 && n + 4 <= N) {
+            *reinterpret_cast<float4_t *>(dst) = acc[i][j];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) dst[e] = acc[i][j][e];
+          }
+        }
+      }
+    } else {
       const uint32_t stage_base = static_cast<uint32_t>(wave * S::kWaveM * S::kStagePitch);
       // Column of this lane's 4 values of group g of block column j inside
       // the wave tile.
@@ -631,7 +677,7 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       // The bias of every column this lane holds, loaded once per tile
       // (columns past N read the last bias; their outputs are not stored).
       float bv[S::kFragN][S::kAccRegs];
-      if constexpr (FUSED) {
+      if constexpr (EPI == kEpiFused) {
 #pragma unroll
         for (int j = 0; j < S::kFragN; ++j)
 #pragma unroll
@@ -652,7 +698,7 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float v = acc[i][j][4 * g + e];
-              if constexpr (FUSED) {
+              if constexpr (EPI == kEpiFused) {
                 // With no bias this adds +0: every value but -0 stays as it
                 // is, and -0 becomes +0, as the exact sum (which starts at
                 // +0) would be.
@@ -761,26 +807,28 @@ static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDe
                   GemmDefault::STAGES == kGemmStages && GemmDefault::kThreads == kGemmThreads,
               "kernels.hpp constants must describe the default kernel");
 
-template <class S, bool FUSED = false>
+template <class S, int EPI = kEpiPlain>
 static hipError_t launch(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
-                         hipStream_t stream, const void *bias = nullptr, int relu = 0) {
+                         hipStream_t stream, const void *bias = nullptr, int relu = 0, float *ws = nullptr,
+                         int splits = 1) {
   const int tiles_m = (M + S::BM - 1) / S::BM;
   const int tiles_n = (N + S::BN - 1) / S::BN;
-  const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
-  const int64_t grid = S::PERSISTENT ? (tiles < num_cus ? tiles : num_cus) : tiles;
+  const int64_t units = static_cast<int64_t>(tiles_m) * tiles_n * (EPI == kEpiPartial ? splits : 1);
+  const int64_t grid = S::PERSISTENT ? (units < num_cus ? units : num_cus) : units;
   // Whole 16-byte row segments of D are 16-byte aligned when N % 8 == 0.
   const int vec16 = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(D) % 16 == 0);
-  hipLaunchKernelGGL((gemm_kernel<S, FUSED>), dim3(static_cast<unsigned>(grid)), dim3(S::kThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_kernel<S, EPI>), dim3(static_cast<unsigned>(grid)), dim3(S::kThreads), 0, stream,
                      static_cast<const _Float16 *>(A), static_cast<const _Float16 *>(B), static_cast<_Float16 *>(D),
-                     M, N, K, tiles_m, tiles_n, vec16, static_cast<const uint16_t *>(bias), relu);
+                     M, N, K, tiles_m, tiles_n, vec16, static_cast<const uint16_t *>(bias), relu, ws, splits);
   return hipGetLastError();
 }
 
 // The shape-dependent default: the tile gemm_default_tile picks, with the
 // ring depth of kGemmTileShapes.
-template <int DT, bool FUSED = false>
+template <int DT, int EPI = kEpiPlain>
 static hipError_t launch_default(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
-                                 hipStream_t stream, const void *bias = nullptr, int relu = 0) {
+                                 hipStream_t stream, const void *bias = nullptr, int relu = 0, float *ws = nullptr,
+                                 int splits = 1) {
   using Big = std::conditional_t<DT == kF16, GemmDefault, GemmBf16>;
   static_assert(Big::BM == kGemmTileShapes[kTile256x256].bm && Big::BN == kGemmTileShapes[kTile256x256].bn &&
                     Big::STAGES == kGemmTileShapes[kTile256x256].stages &&
@@ -793,15 +841,15 @@ static hipError_t launch_default(const void *A, const void *B, void *D, int M, i
                 "kGemmTileShapes must describe the kernels launched for each tile");
   switch (gemm_default_tile(M, N, num_cus)) {
     case kTile256x128:
-      return launch<GemmTile256x128<DT, kGemmTileShapes[kTile256x128].stages>, FUSED>(A, B, D, M, N, K, num_cus, stream,
-                                                                                bias, relu);
+      return launch<GemmTile256x128<DT, kGemmTileShapes[kTile256x128].stages>, EPI>(A, B, D, M, N, K, num_cus, stream,
+                                                                              bias, relu, ws, splits);
     case kTile128x256:
-      return launch<GemmTile128x256<DT, kGemmTileShapes[kTile128x256].stages>, FUSED>(A, B, D, M, N, K, num_cus, stream,
-                                                                                bias, relu);
+      return launch<GemmTile128x256<DT, kGemmTileShapes[kTile128x256].stages>, EPI>(A, B, D, M, N, K, num_cus, stream,
+                                                                              bias, relu, ws, splits);
     case kTile128x128:
-      return launch<GemmTile128x128<DT, kGemmTileShapes[kTile128x128].stages>, FUSED>(A, B, D, M, N, K, num_cus, stream,
-                                                                                bias, relu);
-    default: return launch<Big, FUSED>(A, B, D, M, N, K, num_cus, stream, bias, relu);
+      return launch<GemmTile128x128<DT, kGemmTileShapes[kTile128x128].stages>, EPI>(A, B, D, M, N, K, num_cus, stream,
+                                                                              bias, relu, ws, splits);
+    default: return launch<Big, EPI>(A, B, D, M, N, K, num_cus, stream, bias, relu, ws, splits);
   }
 }
 
@@ -874,8 +922,81 @@ hipError_t launch_gemm_bias(int dtype, const void *A, const void *B, const void 
                        static_cast<int64_t>(N), relu);
     return hipGetLastError();
   }
-  return dtype == kBF16 ? launch_default<kBF16, true>(A, B, D, M, N, K, num_cus, stream, bias, relu)
-                        : launch_default<kF16, true>(A, B, D, M, N, K, num_cus, stream, bias, relu);
+  return dtype == kBF16 ? launch_default<kBF16, kEpiFused>(A, B, D, M, N, K, num_cus, stream, bias, relu)
+                        : launch_default<kF16, kEpiFused>(A, B, D, M, N, K, num_cus, stream, bias, relu);
+}
+
+// D[i] = rne(ws[0][i] + ws[1][i] + ... + ws[splits-1][i]): the K slices of a
+// split-K GEMM added in slice order, so every output is deterministic.
+template <int DT>
+__global__ void splitk_reduce_kernel(const float *__restrict__ ws, _Float16 *__restrict__ D, int64_t count,
+                                     int splits) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  // Four outputs per thread with 16-byte loads where the layout allows
+  // (count % 4 == 0 keeps every slice's start 16-byte aligned), else one.
+  // The slices' loads go out up to 8 at a time before their sums, which
+  // stay in slice order: one load in flight per thread would leave a small
+  // output's reduction waiting on memory latency once per slice.
+  if (count % 4 == 0) {
+    const int64_t quads = count / 4;
+    for (int64_t q = first; q < quads; q += stride) {
+      const float4_t *src = reinterpret_cast<const float4_t *>(ws) + q;
+      const int64_t step = count / 4;
+      float4_t v = src[0];
+      for (int s = 1; s < splits; s += 8) {
+        float4_t t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (s + j < splits) t[j] = src[(s + j) * step];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (s + j < splits) v += t[j];
+      }
+      half4_t h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = round_out<DT>(v[e]);
+      _Float16 *dst = D + 4 * q;
+      if ((reinterpret_cast<uintptr_t>(dst) & 7) == 0) {
+        *reinterpret_cast<half4_t *>(dst) = h;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = h[e];
+      }
+    }
+    return;
+  }
+  for (int64_t i = first; i < count; i += stride) {
+    float v = ws[i];
+    for (int s = 1; s < splits; s += 8) {
+      float t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s + j < splits) t[j] = ws[(s + j) * count + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s + j < splits) v += t[j];
+    }
+    D[i] = round_out<DT>(v);
+  }
+}
+
+hipError_t launch_gemm_splitk(int dtype, const void *A, const void *B, void *D, int M, int N, int K, void *ws,
+                              int splits, int num_cus, hipStream_t stream) {
+  float *w = static_cast<float *>(ws);
+  const hipError_t e = dtype == kBF16
+                           ? launch_default<kBF16, kEpiPartial>(A, B, D, M, N, K, num_cus, stream, nullptr, 0, w, splits)
+                           : launch_default<kF16, kEpiPartial>(A, B, D, M, N, K, num_cus, stream, nullptr, 0, w, splits);
+  if (e != hipSuccess) return e;
+  const int64_t count = static_cast<int64_t>(M) * N;
+  const int64_t threads = 256;
+  const int64_t items = count % 4 == 0 ? count / 4 : count;  // the reduction's per-thread items
+  int64_t blocks = (items + threads - 1) / threads;
+  if (blocks > 8192) blocks = 8192;
+  auto kernel = dtype == kBF16 ? splitk_reduce_kernel<kBF16> : splitk_reduce_kernel<kF16>;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, w,
+                     static_cast<_Float16 *>(D), count, splits);
+  return hipGetLastError();
 }
 
 }  // namespace gt

@@ -56,6 +56,39 @@ inline GemmTile gemm_default_tile(int64_t M, int64_t N, int num_cus) {
   }
   return static_cast<GemmTile>(best);
 }
+
+// Split K (gemm_splitk_*): when the output's tiles (of the tile
+// gemm_default_tile picks) cannot give every CU one, each tile's K tiles of
+// 64 are cut into `splits` slices, so that tiles x splits units fill the CUs.
+// Every slice keeps at least kSplitKMinTiles K tiles and none is empty.  The
+// split is taken only when the K tiles it takes off the K loop,
+// KT (1 - 1/splits), reach kSplitKMinSaved plus one K tile for every
+// kSplitKOutputsPerTile partial sums it stores and reads back (splits M N):
+// a K tile of the 128x128 tile takes about 0.35 us, a few microseconds go to
+// the reduction's launch and the partial kernel's start, and the partial
+// sums cost about 0.35 us per 2 MB written and read.  The constants come
+// from timing every admissible slice count on outputs of 128..2048 x
+// 128..4096 with K = 1024..14336 on an MI355X: there the rule never chose a
+// split slower than the unsplit GEMM, and its choice was within 2.9 us of
+// the fastest.  Returns 1 (no split) otherwise.
+constexpr int kSplitKMinTiles = 10;
+constexpr int kSplitKMinSaved = 12;
+constexpr int kSplitKOutputsPerTile = 1 << 18;
+inline int gemm_splitk_splits(int64_t M, int64_t N, int64_t K, int num_cus) {
+  const GemmTileShape &s = kGemmTileShapes[gemm_default_tile(M, N, num_cus)];
+  const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
+  const int64_t kt = (K + 63) / 64;
+  if (tiles >= num_cus || kt < 2 * kSplitKMinTiles) return 1;
+  int64_t splits = num_cus / tiles;
+  if (splits > kt / kSplitKMinTiles) splits = kt / kSplitKMinTiles;
+  if (splits < 2) return 1;
+  const int64_t per = (kt + splits - 1) / splits;
+  splits = (kt + per - 1) / per;  // drop slices that would be empty
+  const double saved = static_cast<double>(kt) * static_cast<double>(splits - 1) / static_cast<double>(splits);
+  const double cost = kSplitKMinSaved + static_cast<double>(splits) * static_cast<double>(M) * static_cast<double>(N) /
+                                            static_cast<double>(kSplitKOutputsPerTile);
+  return saved >= cost ? static_cast<int>(splits) : 1;
+}
 constexpr int kGemvVariants = 18;
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip); it has kSkinnyVariants launch shapes.
@@ -137,6 +170,11 @@ hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream);
 // or 1.  K == 0 fills D with act(bias).
 hipError_t launch_gemm_bias(int dtype, const void *A, const void *B, const void *bias, int relu, void *D, int M, int N,
                             int K, int num_cus, hipStream_t stream);
+// Split-K GEMM on the tiled kernel: `splits` K slices write FP32 partial
+// sums to ws [splits][M][N], then a reduction adds them in slice order and
+// rounds into D.  dtype kF16 or kBF16.
+hipError_t launch_gemm_splitk(int dtype, const void *A, const void *B, void *D, int M, int N, int K, void *ws,
+                              int splits, int num_cus, hipStream_t stream);
 hipError_t launch_gemm_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                             hipStream_t stream);
 hipError_t launch_gemm_skinny_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,

@@ -3,7 +3,7 @@
     rocprofv3 --kernel-trace --output-format csv -d OUT -o sweep -- \\
         python3 -m gemv_tile_pipelined_amd.shape_sweep [--gemv N:K,...] [--skinny M:N:K,...]
             [--gemm M:N:K,...] [--gemv-variants 0,8] [--skinny-variants 0,25]
-            [--gemm-variants 0,53] [--gemm-data uniform,zero] [--rounds 1] [--warmup-s 1] [--gemm-bias]
+            [--gemm-variants 0,53] [--gemm-data uniform,zero] [--rounds 1] [--warmup-s 1] [--gemm-bias] [--gemm-splitk]
             [--stream MB --stream-policies 1,2] [--vendor] [--reps 40] > OUT/log.txt
     python3 -m gemv_tile_pipelined_amd.shape_sweep --parse OUT OUT/log.txt
 
@@ -20,7 +20,8 @@ fp16 mantissa cut to its top 7 bits, bf16's precision), int (integers in
 [-8, 8]) or zero, to show how the operands' bit activity moves the
 power-limited clock; --rounds repeats the variant list that many times,
 interleaved, so that a slow drift of the clock does not favour one variant
-(--gemm-bias adds gemm_bias_f16 with a bias and ReLU to each round),
+(--gemm-bias adds gemm_bias_f16 with a bias and ReLU to each round,
+--gemm-splitk gemm_splitk_f16 with a preallocated workspace),
 and the parse also prints each variant's median over the rounds.  Before
 the first segment, --warmup-s seconds of untimed 4096^3 GEMMs let the clock
 settle.  --stream MB runs
@@ -29,8 +30,8 @@ per launch with each cache policy in --stream-policies: the practical read
 ceiling of the bandwidth-bound kernels.  Segments are delimited in the trace
 by a marker kernel (a bitwise not of one int8), and the last stdout line
 lists the segments.  The second command reads the trace and prints each
-segment's median kernel time and algorithmic bandwidth
-(2·(rows·K + K + rows) bytes for the GEMV, 2·(M·K + N·K + M·N) for the GEMM).
+segment's median kernel time (summed over the kernels of one call) and
+algorithmic bandwidth (2·(rows·K + K + rows) bytes for the GEMV, 2·(M·K + N·K + M·N) for the GEMM).
 Inputs are seeded synthetic fp16 values (x, A ~ U(-1,1); W, B ~ U(-0.05,0.05)).
 """
 from __future__ import annotations
@@ -164,11 +165,17 @@ def run(a):
             sets = [(operand((M, K), data), operand((N, K), data)) for _ in range(3)]
             D = torch.empty((M, N), dtype=torch.float16, device=dev)
             bias = uni((N,), -4, 4)
+            cus = torch.cuda.get_device_properties(dev).multi_processor_count
+            ws = torch.empty((max(gt.splitk_workspace_bytes(M, N, K, cus), 16),), dtype=torch.uint8, device=dev)
             for rnd in range(a.rounds):
                 for v in gemm_variants:
                     segment({"kind": "gemm_f16", "M": M, "N": N, "K": K, "variant": v, "data": data,
                              "round": rnd, "flops": 2 * M * N * K},
                             lambda i, v=v: gt.gemm_f16(sets[i][0], sets[i][1], D, variant=v), 3)
+                if a.gemm_splitk:
+                    segment({"kind": "gemm_splitk", "M": M, "N": N, "K": K, "data": data, "round": rnd,
+                             "flops": 2 * M * N * K},
+                            lambda i: gt.gemm_splitk_f16(sets[i][0], sets[i][1], D, workspace=ws), 3)
                 if a.gemm_bias:
                     segment({"kind": "gemm_bias", "M": M, "N": N, "K": K, "data": data, "round": rnd,
                              "flops": 2 * M * N * K},
@@ -197,9 +204,19 @@ def parse(trace_dir, log_path):
         raise SystemExit(f"{len(marks)} markers for {len(labels)} segments")
     by_label: dict = {}
     for lab, (lo, hi) in zip(labels, zip(marks[0::2], marks[1::2])):
-        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[lo + 1 : hi]]
-        names = sorted({r["Kernel_Name"].split("(")[0][:60] for r in rows[lo + 1 : hi]})
-        med = statistics.median(durs) / 1e3
+        # A call may launch several kernels (split K: the partial GEMM, then
+        # the reduction): the segment's time per call is the sum over kernel
+        # names of each one's median duration.
+        per_kernel: dict = {}
+        for r in rows[lo + 1 : hi]:
+            per_kernel.setdefault(r["Kernel_Name"].split("(")[0][:60], []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        names = sorted(per_kernel)
+        durs = per_kernel[names[0]] if names else []
+        kmeds = {n: statistics.median(d) / 1e3 for n, d in per_kernel.items()}
+        med = sum(kmeds.values())
+        if len(kmeds) > 1:
+            names = [f"{n} {kmeds[n]:.2f} us" for n in names]
         shape = "x".join(str(lab[k]) for k in ("M", "N", "K") if k in lab)
         var = f" v{lab['variant']}" if "variant" in lab else (f" p{lab['policy']}" if "policy" in lab else "")
         if "data" in lab:
@@ -235,6 +252,7 @@ def main(argv=None):
     p.add_argument("--gemm-data", default="uniform", help="uniform,m7,int,zero (comma list)")
     p.add_argument("--rounds", type=int, default=1, help="times the --gemm-variants list runs, interleaved")
     p.add_argument("--gemm-bias", action="store_true", help="also gemm_bias_f16 (bias + ReLU) on each GEMM shape")
+    p.add_argument("--gemm-splitk", action="store_true", help="also gemm_splitk_f16 on each GEMM shape")
     p.add_argument("--warmup-s", type=float, default=1.0, help="seconds of untimed GEMMs before the first segment")
     p.add_argument("--stream", type=float, default=0.0, help="MB per read-only probe launch (0: none)")
     p.add_argument("--stream-policies", default="1,2")

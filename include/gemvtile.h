@@ -157,6 +157,56 @@ int gemm_bias_f16(const void *A, const void *B, const void *bias, void *D, int64
 int gemm_bias_bf16(const void *A, const void *B, const void *bias, void *D, int64_t M, int64_t N, int64_t K, int act,
                    void *stream);
 
+/*
+ * gemm_splitk_f16 / gemm_splitk_bf16 -- gemm_f16 / gemm_bf16 with K split
+ * across workgroups, for outputs too small to keep every compute unit busy
+ * even with 128x128 tiles (a 1024x1024 output has 64 of them).  Same
+ * contract and result definition as gemm_f16 / gemm_bf16.
+ *
+ * The pages split K over blocks for the GEMV ("Learning TileLang with GEMV",
+ * §5.2 block_split_k) and add the partial sums with FP32 atomics into a
+ * zeroed output.  Here each (tile, K slice) workgroup unit stores its FP32
+ * partial sums to `workspace`, [splits][M][N] floats, and a second kernel
+ * adds the slices in slice order and rounds once: no atomics, no zeroing,
+ * and every output is deterministic (the summation order depends only on
+ * the shape and the device's compute-unit count).
+ *
+ *   workspace        device memory, 16-byte aligned, owned by the caller; its
+ *                    contents on entry do not matter and are overwritten
+ *   workspace_bytes  its size; at least gemvtile_gemm_splitk_workspace(M, N,
+ *                    K, #CUs) for the current device
+ *
+ * Shapes that do not split (their tiles already fill the CUs, K too short
+ * for the split to pay, or 16 or fewer rows on a side) run exactly as
+ * gemm_f16 / gemm_bf16 and do not touch the workspace, which may then be
+ * NULL.  A workspace that is too small
+ * or NULL when needed returns GEMVTILE_ERR_INVALID_ARG, a misaligned one
+ * GEMVTILE_ERR_UNSUPPORTED; these checks follow the (cached) compute-unit
+ * query and precede any launch.  Calls that share a workspace must be
+ * ordered on one stream.  Returns a gemvtile_status.
+ */
+int gemm_splitk_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *workspace,
+                    int64_t workspace_bytes, void *stream);
+int gemm_splitk_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *workspace,
+                     int64_t workspace_bytes, void *stream);
+
+/*
+ * gemvtile_gemm_splitk_splits / gemvtile_gemm_splitk_workspace -- the number
+ * of K slices gemm_splitk_* uses for an M x N x K product on `num_cus`
+ * compute units, and the workspace bytes it needs (splits * M * N * 4, or 0
+ * when it does not split).  With T tiles of the tile gemvtile_gemm_tile
+ * picks and KT = ceil(K / 64) K tiles: no split when T >= num_cus, when
+ * KT < 20 or when either side has 16 rows or fewer; otherwise
+ * splits = min(floor(num_cus / T), floor(KT / 10)), each slice ceil(KT /
+ * splits) K tiles, minus slices left empty; 1 (0 bytes) below 2, and 1 unless
+ * the K loop gets shorter by KT (splits - 1) / splits >= 12 + splits M N /
+ * 2^18 K tiles (evaluated in double precision): a fixed cost, and one for
+ * the partial sums' traffic.  Host-only arithmetic; 1 and 0 for sizes <= 0
+ * or num_cus out of (0, 2^20].
+ */
+int gemvtile_gemm_splitk_splits(int64_t M, int64_t N, int64_t K, int64_t num_cus);
+int64_t gemvtile_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int64_t num_cus);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *gemvtile_status_string(int status);
 

@@ -57,6 +57,12 @@ def _gemv(lib, x, W, y, N, K):
 
 
 FAKE = 0x10000  # a 16-byte aligned address; never dereferenced by these calls
+# The split-K rule's constants as the header documents them: K tiles of 64
+# per slice at least; K tiles the split must take off the K loop, plus one
+# per SPLITK_OUTPUTS_PER_TILE partial sums.
+SPLITK_MIN_TILES = 10
+SPLITK_MIN_SAVED = 12
+SPLITK_OUTPUTS_PER_TILE = 262144
 
 
 def test_gemm_argument_validation(lib):
@@ -256,6 +262,60 @@ def test_gemm_tile_rule(lib):
     for bad in ((0, 4, 256), (4, 0, 256), (4, 4, 0), (4, 4, 2**21)):
         with pytest.raises(gt.GemvTileError):
             gt.gemm_tile(*bad)
+
+
+def test_gemm_splitk_rule(lib):
+    """K slices of gemm_splitk_*: only when the tiles leave CUs idle, at
+    least 10 K tiles of 64 per slice, no empty slice, never on skinny shapes,
+    and only when the K loop gets at least 12 + splits·M·N / 2^18 K tiles
+    shorter."""
+    want = {
+        (1024, 1024, 4096): 4,     # 64 tiles of 128x128; 16 K tiles per slice
+        (1024, 1024, 14336): 4,
+        (512, 4096, 8192): 2,      # 128 tiles
+        (512, 4096, 4096): 2,      # saves 32 K tiles, costs 12 + 16
+        (1024, 1024, 2048): 1,     # 3 slices would save 21 K tiles, cost 12 + 12
+        (300, 260, 4104): 6,       # 9 tiles; 65 K tiles -> slices of 11
+        (128, 128, 14336): 21,     # one tile; 224 K tiles -> 22 slices of 11 -> 21 non-empty
+        (128, 4096, 14336): 8,     # 32 tiles: 8 slices fill the CUs
+        (2048, 1024, 2048): 1,     # 128 tiles; 2 slices would save 16 K tiles, cost 12 + 16
+        (1024, 1024, 1024): 1,     # 16 K tiles: fewer than 2 x 10
+        (4096, 4096, 4096): 1,     # 256 tiles already
+        (8192, 1024, 8192): 1,     # 256 tiles of 256x128
+        (16, 4096, 4096): 1,       # skinny kernel
+        (4096, 1, 4096): 1,        # GEMV
+    }
+    for (M, N, K), splits in want.items():
+        assert gt.splitk_splits(M, N, K, 256) == splits, (M, N, K)
+        assert gt.splitk_workspace_bytes(M, N, K, 256) == (splits * M * N * 4 if splits > 1 else 0)
+    # the documented formula, evaluated independently
+    for M in (17, 100, 300, 777, 1024, 2049):
+        for N in (17, 129, 1000, 3000):
+            for K in (8, 448, 512, 1032, 1280, 4104, 14336):
+                for cus in (80, 256):
+                    bm, bn, _ = gt.gemm_tile(M, N, cus)
+                    T = -(-M // bm) * -(-N // bn)
+                    kt = -(-K // 64)
+                    s = 1
+                    if T < cus and kt >= 2 * SPLITK_MIN_TILES:
+                        s = min(cus // T, kt // SPLITK_MIN_TILES)
+                        if s >= 2:
+                            per = -(-kt // s)
+                            s = -(-kt // per)
+                            if kt * (s - 1) / s < SPLITK_MIN_SAVED + s * M * N / SPLITK_OUTPUTS_PER_TILE:
+                                s = 1
+                        else:
+                            s = 1
+                    assert gt.splitk_splits(M, N, K, cus) == s, (M, N, K, cus)
+    assert gt.splitk_splits(0, 4, 8, 256) == 1 and gt.splitk_workspace_bytes(4, 4, 0, 256) == 0
+
+
+def test_gemm_splitk_argument_validation(lib):
+    for fn in (lib.gemm_splitk_f16, lib.gemm_splitk_bf16):
+        assert fn(FAKE, FAKE, FAKE, 4, 4, 8, FAKE, -1, None) == INVALID  # negative workspace size
+        assert fn(FAKE, FAKE, FAKE, -1, 4, 8, FAKE, 0, None) == INVALID
+        assert fn(FAKE, FAKE, FAKE, 4, 4, 12, FAKE, 0, None) == UNSUPPORTED
+        assert fn(None, None, None, 0, 4, 8, None, 0, None) == OK
 
 
 def test_measurement_formulas_match_table1():
