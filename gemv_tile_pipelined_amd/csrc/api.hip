@@ -203,10 +203,13 @@ int gemm_bias_bf16(const void *A, const void *B, const void *bias, void *D, int6
 }  // extern "C"
 
 namespace {
-// Split K applies to shapes of the tiled kernel only (not to the GEMV or the
-// skinny kernel's shapes); elsewhere gemm_splitk_* is the plain GEMM.
+// Split K applies to shapes of the tiled kernel and of the skinny kernel
+// (2..16 rows on a side), not to the GEMV's (one row on a side); elsewhere
+// gemm_splitk_* is the plain GEMM.
 int splitk_splits(int64_t M, int64_t N, int64_t K, int cus) {
-  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows) return 1;
+  if (M == 1 || N == 1) return 1;
+  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows)
+    return gt::skinny_splitk_splits(M <= gt::kSkinnyMaxRows ? N : M, K, cus);
   return gt::gemm_splitk_splits(M, N, K, cus);
 }
 
@@ -223,8 +226,11 @@ int run_gemm_splitk(const void *A, const void *B, void *D, int64_t M, int64_t N,
   if (splits == 1) return run_gemm(A, B, D, M, N, K, stream, 0, dtype);
   if (ws == nullptr || ws_bytes < static_cast<int64_t>(splits) * M * N * 4) return GEMVTILE_ERR_INVALID_ARG;
   if (misaligned(ws, 16)) return GEMVTILE_ERR_UNSUPPORTED;
-  return to_status(gt::launch_gemm_splitk(dtype, A, B, D, static_cast<int>(M), static_cast<int>(N),
-                                          static_cast<int>(K), ws, splits, cus, static_cast<hipStream_t>(stream)));
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows)
+    return to_status(gt::launch_gemm_skinny_splitk(dtype, A, B, D, m, n, k, ws, splits, s));
+  return to_status(gt::launch_gemm_splitk(dtype, A, B, D, m, n, k, ws, splits, cus, s));
 }
 }  // namespace
 

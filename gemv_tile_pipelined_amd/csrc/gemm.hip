@@ -981,6 +981,17 @@ __global__ void splitk_reduce_kernel(const float *__restrict__ ws, _Float16 *__r
   }
 }
 
+hipError_t launch_splitk_reduce(int dtype, const float *ws, void *D, int64_t count, int splits, hipStream_t stream) {
+  const int64_t threads = 256;
+  const int64_t items = count % 4 == 0 ? count / 4 : count;  // the reduction's per-thread items
+  int64_t blocks = (items + threads - 1) / threads;
+  if (blocks > 8192) blocks = 8192;
+  auto kernel = dtype == kBF16 ? splitk_reduce_kernel<kBF16> : splitk_reduce_kernel<kF16>;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, ws,
+                     static_cast<_Float16 *>(D), count, splits);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_splitk(int dtype, const void *A, const void *B, void *D, int M, int N, int K, void *ws,
                               int splits, int num_cus, hipStream_t stream) {
   float *w = static_cast<float *>(ws);
@@ -988,15 +999,7 @@ hipError_t launch_gemm_splitk(int dtype, const void *A, const void *B, void *D, 
                            ? launch_default<kBF16, kEpiPartial>(A, B, D, M, N, K, num_cus, stream, nullptr, 0, w, splits)
                            : launch_default<kF16, kEpiPartial>(A, B, D, M, N, K, num_cus, stream, nullptr, 0, w, splits);
   if (e != hipSuccess) return e;
-  const int64_t count = static_cast<int64_t>(M) * N;
-  const int64_t threads = 256;
-  const int64_t items = count % 4 == 0 ? count / 4 : count;  // the reduction's per-thread items
-  int64_t blocks = (items + threads - 1) / threads;
-  if (blocks > 8192) blocks = 8192;
-  auto kernel = dtype == kBF16 ? splitk_reduce_kernel<kBF16> : splitk_reduce_kernel<kF16>;
-  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, w,
-                     static_cast<_Float16 *>(D), count, splits);
-  return hipGetLastError();
+  return launch_splitk_reduce(dtype, w, D, static_cast<int64_t>(M) * N, splits, stream);
 }
 
 }  // namespace gt

@@ -148,6 +148,35 @@ inline int skinny_default_rows(int64_t R, int num_cus) {
   return 1;
 }
 
+// Split K on the skinny kernel (gemm_splitk_*, with R rows on the large side
+// and 2..16 on the small one): while ceil(R / 16) blocks of 16 rows leave
+// CUs idle, each block's K tiles of 512 are cut into `splits` slices of at
+// least kSkinnySplitMinTiles tiles, so that blocks x splits workgroups fill
+// the CUs; every slice is non-empty.  The unsplit kernel instead takes
+// fewer rows per workgroup, which re-reads the small operand from the
+// caches once per workgroup; it is fast at short K, and the split's second
+// launch costs about 2 us, so the split is taken only for KT >=
+// kSkinnySplitBaseTiles + kSkinnySplitFillTiles * blocks / num_cus K tiles
+// (longer K the more CUs the blocks already fill).  The constants come from
+// kernel-trace timings of every admissible slice count on 2, 8 and 16 small
+// rows, 64..3072 large rows and K = 1024..14336 on an MI355X: there the rule
+// was never slower than no split and within 0.1 us of the fastest choice.
+// Returns 1 (no split) otherwise.
+constexpr int kSkinnySplitMinTiles = 2;
+constexpr int kSkinnySplitBaseTiles = 8;
+constexpr int kSkinnySplitFillTiles = 64;
+inline int skinny_splitk_splits(int64_t R, int64_t K, int num_cus) {
+  const int64_t blocks = (R + 15) / 16;
+  const int64_t kt = (K + 511) / 512;
+  if (blocks >= num_cus || kt < 2 * kSkinnySplitMinTiles) return 1;
+  if (kt * num_cus < static_cast<int64_t>(kSkinnySplitBaseTiles) * num_cus + kSkinnySplitFillTiles * blocks) return 1;
+  int64_t splits = num_cus / blocks;
+  if (splits > kt / kSkinnySplitMinTiles) splits = kt / kSkinnySplitMinTiles;
+  if (splits < 2) return 1;
+  const int64_t per = (kt + splits - 1) / splits;
+  return static_cast<int>((kt + per - 1) / per);  // drop slices that would be empty
+}
+
 // s_waitcnt immediate for "lgkmcnt(0)" alone on gfx9-family targets
 // (vmcnt field [3:0]|[15:14] = 63, expcnt [6:4] = 7, lgkmcnt [11:8] = 0).
 // Issued through the builtin so the compiler knows the LDS reads are done.
@@ -175,6 +204,13 @@ hipError_t launch_gemm_bias(int dtype, const void *A, const void *B, const void 
 // rounds into D.  dtype kF16 or kBF16.
 hipError_t launch_gemm_splitk(int dtype, const void *A, const void *B, void *D, int M, int N, int K, void *ws,
                               int splits, int num_cus, hipStream_t stream);
+// The same for shapes with 2..16 rows on one side, on the skinny kernel
+// (16 rows of the large side per workgroup, `splits` workgroups per block
+// of rows).
+hipError_t launch_gemm_skinny_splitk(int dtype, const void *A, const void *B, void *D, int M, int N, int K, void *ws,
+                                     int splits, hipStream_t stream);
+// D[i] = round(ws[0][i] + ... + ws[splits-1][i]) for i < count, in slice order.
+hipError_t launch_splitk_reduce(int dtype, const float *ws, void *D, int64_t count, int splits, hipStream_t stream);
 hipError_t launch_gemm_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                             hipStream_t stream);
 hipError_t launch_gemm_skinny_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,

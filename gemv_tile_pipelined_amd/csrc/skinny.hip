@@ -118,10 +118,20 @@ gemm_skinny_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ 
 // chunks 0, 2, 1, 3 of the step: lanes l and l + 32, which the LDS serves
 // together, then read chunks an odd XOR apart and every read is bank-conflict
 // free (lanes that re-read a row read the same address, a broadcast).
-template <int WAVES, int STAGES, int QROWS, bool TRANS, int DT = kF16, int PR = 16, bool KROT = false, bool NTP = false>
+//
+// With SPLIT, K is split across workgroups as well: the grid holds `splits`
+// workgroups per block of PR rows (row-block major, so that workgroups side
+// by side read different K ranges of Q), workgroup slice j walks only the K
+// tiles [j*per, min(KT, (j+1)*per)) with per = ceil(KT / splits) (the host
+// keeps every slice non-empty), and its sums go unrounded to
+// ws[j][output index] for the ordered reduction kernel.  More workgroups of
+// 16 P rows, instead of fewer P rows per workgroup, keep the number of times
+// Q is read from the caches at ceil(R / 16).
+template <int WAVES, int STAGES, int QROWS, bool TRANS, int DT = kF16, int PR = 16, bool KROT = false, bool NTP = false,
+          bool SPLIT = false>
 __global__ void __launch_bounds__(WAVES * 64)
 gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ Q, _Float16 *__restrict__ D,
-                       int R, int S, int K) {
+                       int R, int S, int K, float *__restrict__ ws, int splits) {
   constexpr int BK = 512;
   constexpr int kRowBytes = BK * 2;                              // 1 KiB: one wave instruction
   constexpr int kLoads = PR + QROWS;                             // row loads per stage
@@ -141,16 +151,25 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r0 = blockIdx.x * PR;
+  const int KT = (K + BK - 1) / BK;
+  // This workgroup's rows and K tiles [kbeg, kbeg + nkt).
+  int rb = static_cast<int>(blockIdx.x), slice = 0, kbeg = 0, nkt = KT;
+  if constexpr (SPLIT) {
+    rb = static_cast<int>(blockIdx.x / static_cast<unsigned>(splits));
+    slice = static_cast<int>(blockIdx.x % static_cast<unsigned>(splits));
+    const int per = (KT + splits - 1) / splits;
+    kbeg = slice * per;
+    nkt = min(per, KT - kbeg);
+  }
+  const int r0 = rb * PR;
   const int prows = min(PR, R - r0);
   const int4_t rsrc_p = make_buffer_rsrc(P + static_cast<int64_t>(r0) * K, static_cast<uint32_t>(prows) * K * 2u);
   const int4_t rsrc_q = make_buffer_rsrc(Q, static_cast<uint32_t>(S) * K * 2u);
   const uint32_t ring0 = lds_addr(ring);
-  const int KT = (K + BK - 1) / BK;
-  // With KROT, workgroup b walks the K tiles from tile b % KT and wraps, so
+  // With KROT, workgroup b walks its K tiles from tile b % nkt and wraps, so
   // the workgroups running at one moment read different parts of Q (which
   // they all share) instead of the same lines at once.
-  const int kt0 = KROT ? static_cast<int>(blockIdx.x % static_cast<unsigned>(KT)) : 0;
+  const int kt0 = KROT ? static_cast<int>(blockIdx.x % static_cast<unsigned>(nkt)) : 0;
   auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
 
   // Row loads of K tile kt: load d of this wave moves stage row
@@ -158,7 +177,7 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   // loads zeros into the junk row).
   auto issue = [&](int kt) {
     const uint32_t stage = ring0 + static_cast<uint32_t>((kt % STAGES) * kStageBytes);
-    const int ktile = kt + kt0 < KT ? kt + kt0 : kt + kt0 - KT;  // the K tile this ring slot holds
+    const int ktile = kbeg + (kt + kt0 < nkt ? kt + kt0 : kt + kt0 - nkt);  // the K tile this ring slot holds
 #pragma unroll
     for (int d = 0; d < kDmaPerWave; ++d) {
       const int t = d * WAVES + wave;
@@ -188,17 +207,17 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s);
+    if (s < nkt) issue(s);
 
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = 0; kt < nkt; ++kt) {
     // Tile kt has landed once at most `younger` tiles' loads are pending.
     // Loads complete in issue order, so waiting until at most
     // younger*kDmaPerWave are pending leaves only the younger tiles in flight.
-    wait_younger<kDmaPerWave, STAGES - 2>(min(KT, kt + STAGES - 1) - (kt + 1));
+    wait_younger<kDmaPerWave, STAGES - 2>(min(nkt, kt + STAGES - 1) - (kt + 1));
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     workgroup_barrier();  // tile kt complete for everyone; tile kt-1 no longer read
-    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+    if (kt + STAGES - 1 < nkt) issue(kt + STAGES - 1);
     const char *stage = ring + (kt % STAGES) * kStageBytes;
 #pragma unroll
     for (int j = 0; j < kStepsPerWave; ++j) {
@@ -226,7 +245,10 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
     for (int w = 0; w < WAVES; ++w) sum += partial[w][s][r];
     if (s < S && r < PR && r0 + r < R) {
       const int64_t idx = TRANS ? static_cast<int64_t>(r0 + r) * S + s : static_cast<int64_t>(s) * R + r0 + r;
-      D[idx] = round_out<DT>(sum);
+      if constexpr (SPLIT)
+        ws[static_cast<int64_t>(slice) * R * S + idx] = sum;
+      else
+        D[idx] = round_out<DT>(sum);
     }
   }
 }
@@ -371,13 +393,50 @@ static hipError_t launch_lds(const void *P, const void *Q, void *D, int R, int S
   const auto *p = static_cast<const _Float16 *>(P);
   const auto *q = static_cast<const _Float16 *>(Q);
   auto *d = static_cast<_Float16 *>(D);
+  float *no_ws = nullptr;
   if (trans)
     hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, true, DT, PR, KROT, NTP>), grid, dim3(WAVES * 64),
-                       0, stream, p, q, d, R, S, K);
+                       0, stream, p, q, d, R, S, K, no_ws, 1);
   else
     hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, false, DT, PR, KROT, NTP>), grid,
-                       dim3(WAVES * 64), 0, stream, p, q, d, R, S, K);
+                       dim3(WAVES * 64), 0, stream, p, q, d, R, S, K, no_ws, 1);
   return hipGetLastError();
+}
+
+// Split-K form: ceil(R / 16) x splits workgroups of 16 P rows write FP32
+// partial sums to ws [splits][M*N]; the ordered reduction then rounds D.
+template <int WAVES, int STAGES, int QROWS, int DT>
+static hipError_t launch_lds_split(const void *P, const void *Q, void *D, int R, int S, int K, bool trans, float *ws,
+                                   int splits, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((R + 15) / 16 * splits));
+  const auto *p = static_cast<const _Float16 *>(P);
+  const auto *q = static_cast<const _Float16 *>(Q);
+  auto *d = static_cast<_Float16 *>(D);
+  if (trans)
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, true, DT, 16, false, true, true>), grid,
+                       dim3(WAVES * 64), 0, stream, p, q, d, R, S, K, ws, splits);
+  else
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, false, DT, 16, false, true, true>), grid,
+                       dim3(WAVES * 64), 0, stream, p, q, d, R, S, K, ws, splits);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce(DT, ws, D, static_cast<int64_t>(R) * S, splits, stream);
+}
+
+hipError_t launch_gemm_skinny_splitk(int dtype, const void *A, const void *B, void *D, int M, int N, int K, void *ws,
+                                     int splits, hipStream_t stream) {
+  const bool small_m = M <= kSkinnyMaxRows;
+  if (!small_m && N > kSkinnyMaxRows) return hipErrorInvalidValue;
+  const void *P = small_m ? B : A;
+  const void *Q = small_m ? A : B;
+  const int R = small_m ? N : M;
+  const int S = small_m ? M : N;
+  float *w = static_cast<float *>(ws);
+  if (dtype == kBF16)
+    return S <= 8 ? launch_lds_split<8, 4, 8, kBF16>(P, Q, D, R, S, K, !small_m, w, splits, stream)
+                  : launch_lds_split<16, 4, 16, kBF16>(P, Q, D, R, S, K, !small_m, w, splits, stream);
+  return S <= 8 ? launch_lds_split<8, 4, 8, kF16>(P, Q, D, R, S, K, !small_m, w, splits, stream)
+                : launch_lds_split<16, 4, 16, kF16>(P, Q, D, R, S, K, !small_m, w, splits, stream);
 }
 
 // The default launch (skinny_default_rows): 16 P rows per workgroup with 16

@@ -21,7 +21,8 @@ fp16 mantissa cut to its top 7 bits, bf16's precision), int (integers in
 power-limited clock; --rounds repeats the variant list that many times,
 interleaved, so that a slow drift of the clock does not favour one variant
 (--gemm-bias adds gemm_bias_f16 with a bias and ReLU to each round,
---gemm-splitk gemm_splitk_f16 with a preallocated workspace),
+--gemm-splitk gemm_splitk_f16 with a preallocated workspace, also to the
+--skinny shapes),
 and the parse also prints each variant's median over the rounds.  Before
 the first segment, --warmup-s seconds of untimed 4096^3 GEMMs let the clock
 settle.  --stream MB runs
@@ -134,6 +135,11 @@ def run(a):
         for v in skinny_variants:
             segment({"kind": "gemm_f16", "M": M, "N": N, "K": K, "variant": v, "bytes": 2 * (M * K + N * K + M * N)},
                     lambda i, v=v: gt.gemm_f16(A, Bs[i], D, variant=v), c)
+        if a.gemm_splitk:
+            cus = torch.cuda.get_device_properties(dev).multi_processor_count
+            ws = torch.empty((max(gt.splitk_workspace_bytes(M, N, K, cus), 16),), dtype=torch.uint8, device=dev)
+            segment({"kind": "gemm_splitk", "M": M, "N": N, "K": K, "bytes": 2 * (M * K + N * K + M * N)},
+                    lambda i: gt.gemm_splitk_f16(A, Bs[i], D, workspace=ws), c)
         if a.vendor:
             segment({"kind": "torch.matmul", "M": M, "N": N, "K": K, "bytes": 2 * (M * K + N * K + M * N)},
                     lambda i: torch.matmul(A, Bs[i].t(), out=D), c)

@@ -160,8 +160,10 @@ int gemm_bias_bf16(const void *A, const void *B, const void *bias, void *D, int6
 /*
  * gemm_splitk_f16 / gemm_splitk_bf16 -- gemm_f16 / gemm_bf16 with K split
  * across workgroups, for outputs too small to keep every compute unit busy
- * even with 128x128 tiles (a 1024x1024 output has 64 of them).  Same
- * contract and result definition as gemm_f16 / gemm_bf16.
+ * even with 128x128 tiles (a 1024x1024 output has 64 of them), and for
+ * decode-batch shapes with 2..16 rows on one side whose other side has too
+ * few blocks of 16 rows (8 x 1024 has 64).  Same contract and result
+ * definition as gemm_f16 / gemm_bf16.
  *
  * The pages split K over blocks for the GEMV ("Learning TileLang with GEMV",
  * §5.2 block_split_k) and add the partial sums with FP32 atomics into a
@@ -176,8 +178,8 @@ int gemm_bias_bf16(const void *A, const void *B, const void *bias, void *D, int6
  *   workspace_bytes  its size; at least gemvtile_gemm_splitk_workspace(M, N,
  *                    K, #CUs) for the current device
  *
- * Shapes that do not split (their tiles already fill the CUs, K too short
- * for the split to pay, or 16 or fewer rows on a side) run exactly as
+ * Shapes that do not split (their tiles or row blocks already fill the CUs,
+ * K too short for the split to pay, or one row on a side) run exactly as
  * gemm_f16 / gemm_bf16 and do not touch the workspace, which may then be
  * NULL.  A workspace that is too small
  * or NULL when needed returns GEMVTILE_ERR_INVALID_ARG, a misaligned one
@@ -195,14 +197,19 @@ int gemm_splitk_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N
  * of K slices gemm_splitk_* uses for an M x N x K product on `num_cus`
  * compute units, and the workspace bytes it needs (splits * M * N * 4, or 0
  * when it does not split).  With T tiles of the tile gemvtile_gemm_tile
- * picks and KT = ceil(K / 64) K tiles: no split when T >= num_cus, when
- * KT < 20 or when either side has 16 rows or fewer; otherwise
+ * picks and KT = ceil(K / 64) K tiles: no split when T >= num_cus or
+ * KT < 20; otherwise
  * splits = min(floor(num_cus / T), floor(KT / 10)), each slice ceil(KT /
  * splits) K tiles, minus slices left empty; 1 (0 bytes) below 2, and 1 unless
  * the K loop gets shorter by KT (splits - 1) / splits >= 12 + splits M N /
  * 2^18 K tiles (evaluated in double precision): a fixed cost, and one for
- * the partial sums' traffic.  Host-only arithmetic; 1 and 0 for sizes <= 0
- * or num_cus out of (0, 2^20].
+ * the partial sums' traffic.  With 2..16 rows on one side (the skinny
+ * kernel), with B = ceil(R / 16) blocks of the other side's R rows and KT =
+ * ceil(K / 512): no split when B >= num_cus, KT < 4 or KT num_cus < 8
+ * num_cus + 64 B; otherwise splits = min(floor(num_cus / B), floor(KT / 2)),
+ * each slice ceil(KT / splits) K tiles, minus slices left empty.  One row
+ * on a side (the GEMV) never splits.  Host-only arithmetic; 1 and 0 for
+ * sizes <= 0 or num_cus out of (0, 2^20].
  */
 int gemvtile_gemm_splitk_splits(int64_t M, int64_t N, int64_t K, int64_t num_cus);
 int64_t gemvtile_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int64_t num_cus);

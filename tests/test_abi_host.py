@@ -310,6 +310,43 @@ def test_gemm_splitk_rule(lib):
     assert gt.splitk_splits(0, 4, 8, 256) == 1 and gt.splitk_workspace_bytes(4, 4, 0, 256) == 0
 
 
+def test_gemm_splitk_skinny_rule(lib):
+    """K slices on the skinny kernel (2..16 rows on a side): K tiles of 512,
+    at least 2 per slice, only while the blocks of 16 large-side rows leave
+    CUs idle and KT >= 8 + 64·blocks/#CUs; one row on a side never splits."""
+    want = {
+        (8, 1024, 14336): 4,     # 64 blocks, 28 K tiles >= 8 + 16
+        (8, 1024, 8192): 1,      # 16 K tiles < 24
+        (8, 256, 14336): 14,     # 16 blocks; 28 K tiles -> 14 slices of 2
+        (16, 64, 8192): 8,       # 4 blocks; 16 K tiles -> 8 slices of 2
+        (8, 64, 4096): 1,        # 8 K tiles < 9
+        (8, 2048, 14336): 1,     # 128 blocks: 28 < 8 + 32
+        (8, 4096, 14336): 1,     # 256 blocks fill the CUs
+        (1000, 5, 14336): 4,     # N <= 16: the same rule on the 1000 rows of A
+        (1, 1024, 14336): 1,     # the GEMV
+        (1024, 1, 14336): 1,
+    }
+    for (M, N, K), splits in want.items():
+        assert gt.splitk_splits(M, N, K, 256) == splits, (M, N, K)
+        assert gt.splitk_workspace_bytes(M, N, K, 256) == (splits * M * N * 4 if splits > 1 else 0)
+    for S in (2, 5, 16):
+        for R in (17, 100, 300, 777, 1024, 2049, 5000):
+            for K in (8, 1032, 2048, 4104, 8192, 14336, 65536):
+                for cus in (80, 256):
+                    blocks = -(-R // 16)
+                    kt = -(-K // 512)
+                    s = 1
+                    if blocks < cus and kt >= 4 and kt * cus >= 8 * cus + 64 * blocks:
+                        s = min(cus // blocks, kt // 2)
+                        if s >= 2:
+                            per = -(-kt // s)
+                            s = -(-kt // per)
+                        else:
+                            s = 1
+                    assert gt.splitk_splits(S, R, K, cus) == s, (S, R, K, cus)
+                    assert gt.splitk_splits(R, S, K, cus) == s, (R, S, K, cus)
+
+
 def test_gemm_splitk_argument_validation(lib):
     for fn in (lib.gemm_splitk_f16, lib.gemm_splitk_bf16):
         assert fn(FAKE, FAKE, FAKE, 4, 4, 8, FAKE, -1, None) == INVALID  # negative workspace size

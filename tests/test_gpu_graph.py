@@ -4,9 +4,11 @@ Every call only enqueues kernels on the caller's stream: no allocation, no
 memset (K = 0 writes its zeros with a kernel), no host synchronisation.  A
 graph captured around them must therefore give, on every replay, exactly what
 the eager calls give.  The graph holds the tiled GEMM, the skinny GEMM, the
-K-split GEMV, a bf16 GEMM, a K = 0 fill and a GEMM with the fused bias and
-ReLU; it is replayed several times with eager work between the replays, and
-every replay is compared bit for bit.
+K-split GEMV, a bf16 GEMM, a K = 0 fill, a GEMM with the fused bias and
+ReLU, and the split-K GEMM on a tiled and on a skinny shape (each with its
+own workspace); it is replayed several times with eager work between the
+replays (which also fills the workspaces with NaN), and every replay is
+compared bit for bit.
 """
 import numpy as np
 import pytest
@@ -46,7 +48,17 @@ def test_graph_replays_match_eager():
     Db = torch.empty((520, 776), dtype=torch.bfloat16, device=dev)
     D0 = torch.empty((33, 70), dtype=torch.float16, device=dev)
     Dr = torch.empty((520, 776), dtype=torch.float16, device=dev)
-    outs = (D, Ds, y, Db, D0, Dr)
+    # split K: a tiled shape (9 tiles, 6 slices) and a skinny one (32 row blocks, 8 slices)
+    Ak = t16(datagen.uniform_f16(9700, 7, (300, 4104), -1.0, 1.0))
+    Bk = t16(datagen.uniform_f16(9700, 8, (260, 4104), -1.0, 1.0))
+    Aq = t16(datagen.uniform_f16(9700, 9, (8, 8192), -1.0, 1.0))
+    Bq = t16(datagen.uniform_f16(9700, 10, (512, 8192), -0.05, 0.05))
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wk = torch.empty((max(gt.splitk_workspace_bytes(300, 260, 4104, cus), 16) // 4,), device=dev)
+    wq = torch.empty((max(gt.splitk_workspace_bytes(8, 512, 8192, cus), 16) // 4,), device=dev)
+    Dk = torch.empty((300, 260), dtype=torch.float16, device=dev)
+    Dq = torch.empty((8, 512), dtype=torch.float16, device=dev)
+    outs = (D, Ds, y, Db, D0, Dr, Dk, Dq)
 
     def work():
         gt.gemm_f16(A, B, D)
@@ -55,6 +67,8 @@ def test_graph_replays_match_eager():
         gt.gemm_bf16(Ab, Bb, Db)
         gt.gemm_f16(A0, B0, D0)
         gt.gemm_bias_f16(A, B, bias, "relu", Dr)
+        gt.gemm_splitk_f16(Ak, Bk, Dk, workspace=wk)
+        gt.gemm_splitk_f16(Aq, Bq, Dq, workspace=wq)
 
     work()
     torch.cuda.synchronize(dev)
@@ -71,7 +85,7 @@ def test_graph_replays_match_eager():
     with torch.cuda.graph(g):
         work()
     for rep in range(4):
-        for o in outs:
+        for o in outs + (wk, wq):
             o.fill_(float("nan"))  # eager work between replays
         torch.cuda.synchronize(dev)
         g.replay()
@@ -80,3 +94,5 @@ def test_graph_replays_match_eager():
             assert torch.equal(got.view(torch.int16), want.view(torch.int16)), rep
     assert bool((D0.view(torch.int16) == 0).all())
     assert np.isfinite(D.float().cpu().numpy()).all()
+    if cus == 256:
+        assert gt.splitk_splits(300, 260, 4104, cus) == 6 and gt.splitk_splits(8, 512, 8192, cus) == 8
