@@ -8,6 +8,8 @@ Inputs are built on the device (a host oracle over gigabytes is not needed):
     one product below 2^6, exact in FP32 in any order, so the bits must match;
     M = 260 adds a ragged second tile row;
   * the skinny path (8 activation rows) at the same K;
+  * gemm_splitk_f16 on both shapes at that K (K split across workgroups:
+    42 and 13 slices on 256 CUs), to the same closed form;
   * gemv_f16 at the largest K (2^31 - 8, one row of W is 4 GiB) with unit
     vectors x = e_j at the start, the middle and the end of the row: y[n] is
     then exactly W[n, j], whatever the summation order.
@@ -51,7 +53,15 @@ def test_gemm_at_largest_k(env, shape):
     want = (K * 2.0**-16 * torch.outer(u, v)).to(torch.float16).to(dev)
     torch.cuda.synchronize(dev)
     assert torch.equal(D.view(torch.int16), want.view(torch.int16))
-    del A, B, D
+    # split K at the same K: FP32 partial sums of each slice, then their ordered sum
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    print(f"[limits] gemm_splitk {M}x{N}x{K}: {gt.splitk_splits(M, N, K, cus)} slices", flush=True)
+    if cus == 256:
+        assert gt.splitk_splits(M, N, K, cus) > 1
+    Ds = gt.gemm_splitk_f16(A, B)
+    torch.cuda.synchronize(dev)
+    assert torch.equal(Ds.view(torch.int16), want.view(torch.int16))
+    del A, B, D, Ds
     torch.cuda.empty_cache()
 
 
