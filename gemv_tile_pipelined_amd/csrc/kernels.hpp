@@ -93,6 +93,11 @@ constexpr int kGemvVariants = 18;
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip); it has kSkinnyVariants launch shapes.
 constexpr int kSkinnyMaxRows = 16;
+// gemm_f16 / gemm_bf16 also send shapes whose smaller side has 17..32 rows
+// to the skinny kernel (two 16-row blocks of the small operand per MFMA
+// step): the tiled kernel's 128-row tiles would leave most of each tile and
+// most CUs idle there.  The forced skinny launch shapes stay at 16 rows.
+constexpr int kSkinnyWideRows = 32;
 constexpr int kSkinnyVariants = 40;
 // gemvtile_gemm_f16_variant numbers each kernel family from a fixed base so
 // that adding a launch shape to one family renumbers no other: tiled GEMM

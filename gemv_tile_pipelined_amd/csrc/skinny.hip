@@ -141,13 +141,14 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   constexpr int kStageBytes = (kLoads + (kJunk ? 1 : 0)) * kRowBytes;
   constexpr int kSteps = BK / 32;                                // 32-wide K steps per stage
   constexpr int kStepsPerWave = kSteps / WAVES;
-  static_assert(QROWS == 8 || QROWS == 16, "Q tile rows");
+  static_assert(QROWS == 8 || QROWS == 16 || QROWS == 32, "Q tile rows");
+  constexpr int QB = QROWS == 32 ? 2 : 1;  // 16-row blocks of Q (each its own MFMA)
   static_assert(PR == 1 || PR == 2 || PR == 4 || PR == 8 || PR == 16, "P rows per workgroup");
   static_assert(kSteps % WAVES == 0, "work split");
   static_assert(STAGES >= 2 && (STAGES - 1) * kDmaPerWave <= 63, "vmcnt range");
-  static_assert(STAGES * kStageBytes + WAVES * 16 * 17 * 4 <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
+  static_assert(STAGES * kStageBytes + WAVES * 16 * QB * 17 * 4 <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * kStageBytes];
-  __shared__ float partial[WAVES][16][17];
+  __shared__ float partial[WAVES][16 * QB][17];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -201,15 +202,17 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   const int prow = frow % PR;  // P row of this lane's fragment
   const uint32_t frag_off = static_cast<uint32_t>(prow * kRowBytes);
   const int fswz = swz(prow);
-  const int qrow = frow % QROWS;  // Q row of this lane's fragment
+  const int qrow = frow % (QROWS < 16 ? QROWS : 16);  // Q row of this lane's fragment in Q block 0
   const uint32_t qfrag_off = static_cast<uint32_t>(kTileBytes + qrow * kRowBytes);
-  const int qswz = swz(qrow);
+  const int qswz = swz(qrow);  // also that of the same row of the other Q block (the swizzle repeats every 16 rows)
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nkt) issue(s);
 
-  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float4_t acc[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) acc[b] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   for (int kt = 0; kt < nkt; ++kt) {
     // Tile kt has landed once at most `younger` tiles' loads are pending.
     // Loads complete in issue order, so waiting until at most
@@ -224,20 +227,26 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
       const int step = wave * kStepsPerWave + j;
       const int c = step * 4 + kperm;  // logical chunk
       const half8_t pf = *reinterpret_cast<const half8_t *>(stage + frag_off + ((c ^ fswz) << 4));
-      const half8_t qf = *reinterpret_cast<const half8_t *>(stage + qfrag_off + ((c ^ qswz) << 4));
-      if constexpr (DT == kF16)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, qf, acc, 0, 0, 0);
-      else
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pf), __builtin_bit_cast(bf16x8_t, qf),
-                                                      acc, 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const half8_t qf =
+            *reinterpret_cast<const half8_t *>(stage + qfrag_off + b * 16 * kRowBytes + ((c ^ qswz) << 4));
+        if constexpr (DT == kF16)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, qf, acc[b], 0, 0, 0);
+        else
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pf),
+                                                           __builtin_bit_cast(bf16x8_t, qf), acc[b], 0, 0, 0);
+      }
     }
   }
 
 #pragma unroll
-  for (int e = 0; e < 4; ++e) partial[wave][frow][4 * kgrp + e] = acc[e];
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) partial[wave][16 * b + frow][4 * kgrp + e] = acc[b][e];
   __syncthreads();
-  // 16 x 16 outputs (Q row s, P row r), each the wave partials in wave order.
-  for (int i = threadIdx.x; i < 256; i += WAVES * 64) {
+  // 16*QB x 16 outputs (Q row s, P row r), each the wave partials in wave order.
+  for (int i = threadIdx.x; i < 256 * QB; i += WAVES * 64) {
     const int s = i >> 4;
     const int r = i & 15;
     float sum = 0.0f;
@@ -448,6 +457,17 @@ template <int DT>
 static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                                   int num_cus, hipStream_t stream) {
   const int pr = skinny_default_rows(R, num_cus);
+  if (S > kSkinnyMaxRows) {
+    // 17..32 small-side rows: 32 staged Q rows, 4 waves, a 3-stage ring of
+    // (PR + 32) KiB stages.
+    switch (pr) {
+      case 16: return launch_lds<4, 3, 32, DT, 16, true, true>(P, Q, D, R, S, K, trans, stream);
+      case 8: return launch_lds<4, 3, 32, DT, 8, false, true>(P, Q, D, R, S, K, trans, stream);
+      case 4: return launch_lds<4, 3, 32, DT, 4>(P, Q, D, R, S, K, trans, stream);
+      case 2: return launch_lds<4, 3, 32, DT, 2>(P, Q, D, R, S, K, trans, stream);
+      default: return launch_lds<4, 3, 32, DT, 1>(P, Q, D, R, S, K, trans, stream);
+    }
+  }
   const bool q8 = S <= 8;
   switch (pr) {
     case 16: return launch_lds<16, 4, 16, DT, 16, true, true>(P, Q, D, R, S, K, trans, stream);
@@ -478,12 +498,28 @@ static hipError_t launch(const void *P, const void *Q, void *D, int R, int S, in
   return hipGetLastError();
 }
 
+// Which operand is the small side Q: A when M <= 16, else B when N <= 16;
+// with `wide` (the default launch only), shapes whose smaller side has
+// 17..32 rows take that side.  Returns false for shapes it does not cover.
+static bool skinny_small_m(int M, int N, bool wide, bool *small_m) {
+  if (M <= kSkinnyMaxRows) {
+    *small_m = true;
+  } else if (N <= kSkinnyMaxRows) {
+    *small_m = false;
+  } else if (wide && (M < N ? M : N) <= kSkinnyWideRows) {
+    *small_m = M <= N;
+  } else {
+    return false;
+  }
+  return true;
+}
+
 hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K,
                                   int num_cus, hipStream_t stream) {
-  // The small side is Q.  M <= 16: Q = A, P = B, D = Q·Pᵀ.  Otherwise
-  // (N <= 16): Q = B, P = A, D = P·Qᵀ.
-  const bool small_m = M <= kSkinnyMaxRows;
-  if (!small_m && N > kSkinnyMaxRows) return hipErrorInvalidValue;
+  // The small side is Q.  Q = A, P = B, D = Q·Pᵀ when the small side is M;
+  // otherwise Q = B, P = A, D = P·Qᵀ.
+  bool small_m = false;
+  if (!skinny_small_m(M, N, variant == 0, &small_m)) return hipErrorInvalidValue;
   const void *P = small_m ? B : A;
   const void *Q = small_m ? A : B;
   const int R = small_m ? N : M;
@@ -570,8 +606,8 @@ hipError_t launch_gemm_skinny_wp_f16(int variant, const void *A, const void *B, 
 
 hipError_t launch_gemm_skinny_bf16(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                                    hipStream_t stream) {
-  const bool small_m = M <= kSkinnyMaxRows;
-  if (!small_m && N > kSkinnyMaxRows) return hipErrorInvalidValue;
+  bool small_m = false;
+  if (!skinny_small_m(M, N, true, &small_m)) return hipErrorInvalidValue;
   return launch_lds_auto<kBF16>(small_m ? B : A, small_m ? A : B, D, small_m ? N : M, small_m ? M : N, K, !small_m,
                                 num_cus, stream);
 }

@@ -209,7 +209,12 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(1000, 9, 256) == 500
     assert gt.gemm_grid(16, 300, 256) == 300
     assert gt.gemm_grid(16, 16, 256) == 16
-    assert gt.gemm_grid(17, 4097, 256) == 33  # 1 x 33 tiles of 128x128
+    # 17..32 rows on the smaller side: the skinny kernel too, over the larger side
+    assert gt.gemm_grid(17, 4097, 256) == 257  # 16 rows per workgroup
+    assert gt.gemm_grid(32, 1000, 256) == 500  # 2 rows per workgroup
+    assert gt.gemm_grid(4000, 30, 256) == 500  # 8 rows per workgroup
+    assert gt.gemm_grid(20, 24, 256) == 24  # the larger side, 1 row per workgroup
+    assert gt.gemm_grid(33, 4097, 256) == 33  # 1 x 33 tiles of 128x128
     # one row on a side: the GEMV grid of the other side
     assert gt.gemm_grid(1, 4096, 256) == gt.gemv_grid(4096, 256) == 256
     assert gt.gemm_grid(1000, 1, 256) == gt.gemv_grid(1000, 256)

@@ -1,7 +1,8 @@
-"""Parity of the skinny GEMM path (M <= 16 or N <= 16) with the CPU oracle.
+"""Parity of the skinny GEMM path with the CPU oracle.
 
-gemm_f16 sends shapes with at most 16 rows on one side to a bandwidth-bound
-kernel that streams the larger operand once.  The bar is the one of the
+gemm_f16 sends shapes with at most 16 rows on one side, or 17..32 rows on
+the smaller side, to a bandwidth-bound kernel that streams the larger
+operand once.  The bar is the one of the
 tiled GEMM: |d - ref| <= 1e-2 + 1e-2·|ref| for uniform inputs, bit-for-bit
 for integer inputs (exact FP32 partial sums, so only the final rounding to
 nearest-even decides, and it must agree).  Every shape is compared in full:
@@ -70,6 +71,17 @@ SHAPES = [
     (4000, 12, 520),
     (600, 16, 1032),
     (300, 3, 4104),
+    # 17..32 rows on the smaller side: two 16-row blocks of the small operand
+    # per MFMA step (the default launch only)
+    (17, 4096, 4104),
+    (32, 4096, 14336),
+    (24, 1000, 1032),
+    (4000, 32, 4104),
+    (1000, 20, 14336),
+    (32, 32, 520),
+    (30, 17, 72),
+    (25, 300, 8200),
+    (17, 129, 8),
 ]
 
 
