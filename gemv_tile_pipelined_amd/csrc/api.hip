@@ -137,9 +137,10 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
     return to_status(dtype == gt::kBF16 ? gt::launch_gemv_bf16(x, W, D, rows, k, cus, s)
                                         : gt::launch_gemv_f16(0, x, W, D, rows, k, cus, s));
   }
-  // Variant 0 sends shapes with at most 16 rows on one side, or 17..32 on
-  // the smaller side, to the skinny kernel.
-  if (variant == 0 && (skinny || (M < N ? M : N) <= gt::kSkinnyWideRows))
+  // Variant 0 sends shapes with at most 16 rows on one side, and those with
+  // 17..64 on the smaller side that the tiled kernel would spread too
+  // thinly (skinny_wide_route), to the skinny kernel.
+  if (variant == 0 && (skinny || gt::skinny_wide_route(M, N, cus)))
     return to_status(dtype == gt::kBF16 ? gt::launch_gemm_skinny_bf16(A, B, D, m, n, k, cus, s)
                                         : gt::launch_gemm_skinny_f16(0, A, B, D, m, n, k, cus, s));
   return to_status(dtype == gt::kBF16 ? gt::launch_gemm_bf16(A, B, D, m, n, k, cus, s)
@@ -343,10 +344,11 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus) {
   if (M <= 0 || N <= 0 || num_cus <= 0) return 0;
   // One row on a side: the GEMV kernel over the other side's rows.
   if (M == 1 || N == 1) return gemvtile_gemv_grid(M == 1 ? N : M, num_cus);
-  // Skinny shapes (at most 16 rows on a side, or 17..32 on the smaller
-  // side): one workgroup per 16, 8, 4, 2 or 1 rows of the other side.
-  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows || (M < N ? M : N) <= gt::kSkinnyWideRows) {
-    if (num_cus > (int64_t{1} << 20)) return 0;
+  // Skinny shapes (at most 16 rows on a side, or 17..64 on the smaller
+  // side as skinny_wide_route decides): one workgroup per 16, 8, 4, 2 or 1
+  // rows of the other side.
+  if (num_cus > (int64_t{1} << 20)) return 0;
+  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows || gt::skinny_wide_route(M, N, static_cast<int>(num_cus))) {
     const int64_t R = M <= gt::kSkinnyMaxRows ? N : N <= gt::kSkinnyMaxRows ? M : (M <= N ? N : M);
     const int64_t rows = gt::skinny_default_rows(R, static_cast<int>(num_cus));
     return (R + rows - 1) / rows;

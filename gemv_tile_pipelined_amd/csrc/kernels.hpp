@@ -93,11 +93,24 @@ constexpr int kGemvVariants = 18;
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip); it has kSkinnyVariants launch shapes.
 constexpr int kSkinnyMaxRows = 16;
-// gemm_f16 / gemm_bf16 also send shapes whose smaller side has 17..32 rows
-// to the skinny kernel (two 16-row blocks of the small operand per MFMA
-// step): the tiled kernel's 128-row tiles would leave most of each tile and
-// most CUs idle there.  The forced skinny launch shapes stay at 16 rows.
-constexpr int kSkinnyWideRows = 32;
+// gemm_f16 / gemm_bf16 also send shapes whose smaller side has 17..64 rows
+// to the skinny kernel (two or four 16-row blocks of the small operand per
+// MFMA step): the tiled kernel's 128-row tiles would leave most of each
+// tile and most CUs idle there.  The forced skinny launch shapes stay at 16
+// rows.
+constexpr int kSkinnyWideRows = 64;
+// The default's choice for such shapes (S = 17..64 rows on the smaller side,
+// R on the larger): the skinny kernel while the tiled kernel's 128x128 tiles
+// along R would leave more than half the CUs idle (S <= 32) or more than
+// three quarters (S > 32: the skinny kernel re-reads twice the small rows
+// per workgroup); measured on MI355X, the tiled kernel was faster past that
+// (64 x 14336 x 4096: 37 against 46 us).
+inline bool skinny_wide_route(int64_t M, int64_t N, int num_cus) {
+  const int64_t S = M < N ? M : N;
+  const int64_t R = M < N ? N : M;
+  if (S <= kSkinnyMaxRows || S > kSkinnyWideRows) return false;
+  return (R + 127) / 128 * (S > 32 ? 4 : 2) <= num_cus;
+}
 constexpr int kSkinnyVariants = 40;
 // gemvtile_gemm_f16_variant numbers each kernel family from a fixed base so
 // that adding a launch shape to one family renumbers no other: tiled GEMM

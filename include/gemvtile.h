@@ -68,8 +68,10 @@ enum gemvtile_status {
  * 256x128, 128x256 or 128x128 ones when the output has too few 256x256
  * tiles to keep every compute unit busy (gemvtile_gemm_tile gives the choice);
  * it writes D with non-temporal stores, so D is not left in the caches.
- * When M <= 16 or N <= 16, or the smaller side has 17..32 rows (a decode
- * batch against a weight matrix), the call runs a bandwidth-bound kernel
+ * When M <= 16 or N <= 16, or the smaller side has 17..64 rows and the
+ * tiled kernel's 128x128 tiles along the larger side would leave more than
+ * half the compute units idle (three quarters above 32 rows) -- a decode
+ * batch against a weight matrix --, the call runs a bandwidth-bound kernel
  * that streams the larger operand once instead of the tiled one (with fewer
  * rows of it per workgroup when it has too few rows to give every compute
  * unit 16), and when M == 1 or N == 1 the GEMV kernel of gemv_f16; results
@@ -115,7 +117,8 @@ int gemv_f16(const void *x, const void *W, void *y, int64_t N, int64_t K, void *
  * walk-through "TensorCore_GEMM_with_TMA" (§2.2 entrance: nv_bfloat16 A, B,
  * C; §2.3 kernel: FP32 accumulators rounded with __float22bfloat162_rn).
  * Shapes route as for fp16 (M or N == 1: the GEMV kernel; M or N <= 16, or
- * 17..32 rows on the smaller side: the skinny kernel; otherwise the tiled
+ * 17..64 rows on the smaller side as gemm_f16 describes: the skinny kernel;
+ * otherwise the tiled
  * kernel), each in its default launch shape.
  */
 int gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream);
@@ -242,7 +245,7 @@ void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, 
 /*
  * gemvtile_gemm_tile -- the output tile (bm x bn) and LDS ring depth the
  * tiled GEMM takes for an M x N output on `num_cus` compute units (gemm_f16
- * and gemm_bf16 when both sides have more than 32 rows).  Of 256x256 (2
+ * and gemm_bf16 when they take the tiled kernel).  Of 256x256 (2
  * stages), 256x128 and 128x256 (3 stages) and 128x128 (4 stages), it is the
  * one with the least ceil(#tiles / num_cus) * bm * bn / rate, where rate is
  * the tile's measured work rate relative to 256x256 with tiles to spare (1,
@@ -289,7 +292,8 @@ int64_t gemvtile_gemv_grid(int64_t N, int64_t num_cus);
  * gemvtile_gemm_grid -- the number of workgroups gemm_f16 launches for an
  * M x N output on a device with `num_cus` compute units: the GEMV grid of
  * the other side's rows when M or N is 1; when M <= 16 or N <= 16, or the
- * smaller side has 17..32 rows (the skinny kernel), ceil(R/p) with R = N if
+ * smaller side has 17..64 rows and gemm_f16 picks the skinny kernel (see
+ * there), ceil(R/p) with R = N if
  * M <= 16, else M if N <= 16, else the larger side, and p the largest of
  * 16, 8, 4, 2 rows per workgroup such that R >= p*num_cus, else p = 1;
  * otherwise the
@@ -337,7 +341,9 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *      non-temporal ones
  * Variants 1..28 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
- * <= 16, or 17..32 rows on the smaller side: the skinny kernel).  Each other kernel family has its own range:
+ * <= 16, and some shapes with 17..64 rows on the smaller side: the skinny
+ * kernel).  Each
+ * other kernel family has its own range:
  *   100..151 the skinny kernel (only for M <= 16 or N <= 16, else
  *      GEMVTILE_ERR_UNSUPPORTED).  100: the gemm_f16 choice (16, 8, 4, 2
  *      or 1 rows of the large side per workgroup, see gemvtile_gemm_grid; at

@@ -209,12 +209,19 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(1000, 9, 256) == 500
     assert gt.gemm_grid(16, 300, 256) == 300
     assert gt.gemm_grid(16, 16, 256) == 16
-    # 17..32 rows on the smaller side: the skinny kernel too, over the larger side
+    # 17..64 rows on the smaller side: the skinny kernel too, over the larger side
     assert gt.gemm_grid(17, 4097, 256) == 257  # 16 rows per workgroup
     assert gt.gemm_grid(32, 1000, 256) == 500  # 2 rows per workgroup
     assert gt.gemm_grid(4000, 30, 256) == 500  # 8 rows per workgroup
     assert gt.gemm_grid(20, 24, 256) == 24  # the larger side, 1 row per workgroup
-    assert gt.gemm_grid(33, 4097, 256) == 33  # 1 x 33 tiles of 128x128
+    assert gt.gemm_grid(64, 4097, 256) == 257
+    assert gt.gemm_grid(65, 4097, 256) == 33  # 1 x 33 tiles of 128x128
+    # ... while the 128x128 tiles along the larger side would leave more than
+    # half (up to 32 rows) or three quarters (33..64) of the CUs idle
+    assert gt.gemm_grid(32, 16384, 256) == 1024  # 128 tiles: skinny, 16 rows per workgroup
+    assert gt.gemm_grid(32, 16385, 256) == 129  # 129 tiles: tiled
+    assert gt.gemm_grid(64, 8192, 256) == 512  # 64 tiles: skinny
+    assert gt.gemm_grid(14336, 64, 256) == 112  # 112 tiles: tiled
     # one row on a side: the GEMV grid of the other side
     assert gt.gemm_grid(1, 4096, 256) == gt.gemv_grid(4096, 256) == 256
     assert gt.gemm_grid(1000, 1, 256) == gt.gemv_grid(1000, 256)

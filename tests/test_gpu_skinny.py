@@ -1,6 +1,6 @@
 """Parity of the skinny GEMM path with the CPU oracle.
 
-gemm_f16 sends shapes with at most 16 rows on one side, or 17..32 rows on
+gemm_f16 sends shapes with at most 16 rows on one side, or 17..64 rows on
 the smaller side, to a bandwidth-bound kernel that streams the larger
 operand once.  The bar is the one of the
 tiled GEMM: |d - ref| <= 1e-2 + 1e-2·|ref| for uniform inputs, bit-for-bit
@@ -82,6 +82,16 @@ SHAPES = [
     (30, 17, 72),
     (25, 300, 8200),
     (17, 129, 8),
+    # 33..64 rows on the smaller side: four 16-row blocks, the partial sums
+    # reusing the LDS ring
+    (33, 4096, 4104),
+    (64, 4096, 14336),
+    (48, 1000, 1032),
+    (4000, 64, 520),
+    (1000, 40, 4104),
+    (64, 64, 72),
+    (50, 300, 8200),
+    (33, 129, 8),
 ]
 
 
