@@ -81,7 +81,9 @@ def _to_bf16_bits(values):
 
 
 # Tiled shapes (one full tile, ragged M/N/K tails, long K), the shapes that
-# route to the GEMV (M or N == 1) and to the skinny kernel (M or N <= 16).
+# route to the GEMV (M or N == 1) and to the skinny kernel (M or N <= 16, and
+# 17..64 rows on the smaller side against few large-side rows: 64x64,
+# 1000x33 and the three after 520x5).
 SHAPES = [
     (256, 256, 256),
     (300, 260, 200),
@@ -98,6 +100,9 @@ SHAPES = [
     (16, 1000, 1032),
     (4000, 16, 520),
     (520, 5, 1032),
+    (32, 4096, 4104),
+    (4000, 48, 520),
+    (24, 300, 8200),
 ]
 
 

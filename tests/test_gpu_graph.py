@@ -5,10 +5,10 @@ memset (K = 0 writes its zeros with a kernel), no host synchronisation.  A
 graph captured around them must therefore give, on every replay, exactly what
 the eager calls give.  The graph holds the tiled GEMM, the skinny GEMM, the
 K-split GEMV, a bf16 GEMM, a K = 0 fill, a GEMM with the fused bias and
-ReLU, and the split-K GEMM on a tiled and on a skinny shape (each with its
-own workspace); it is replayed several times with eager work between the
-replays (which also fills the workspaces with NaN), and every replay is
-compared bit for bit.
+ReLU, the split-K GEMM on a tiled and on a skinny shape (each with its
+own workspace) and a 48-row decode batch; it is replayed several times
+with eager work between the replays (which also fills the workspaces with
+NaN), and every replay is compared bit for bit.
 """
 import numpy as np
 import pytest
@@ -58,7 +58,11 @@ def test_graph_replays_match_eager():
     wq = torch.empty((max(gt.splitk_workspace_bytes(8, 512, 8192, cus), 16) // 4,), device=dev)
     Dk = torch.empty((300, 260), dtype=torch.float16, device=dev)
     Dq = torch.empty((8, 512), dtype=torch.float16, device=dev)
-    outs = (D, Ds, y, Db, D0, Dr, Dk, Dq)
+    # a 48-row decode batch: the skinny kernel with 64 staged rows
+    Aw = t16(datagen.uniform_f16(9700, 11, (48, 1032), -1.0, 1.0))
+    Bw = t16(datagen.uniform_f16(9700, 12, (1000, 1032), -0.05, 0.05))
+    Dw = torch.empty((48, 1000), dtype=torch.float16, device=dev)
+    outs = (D, Ds, y, Db, D0, Dr, Dk, Dq, Dw)
 
     def work():
         gt.gemm_f16(A, B, D)
@@ -69,6 +73,7 @@ def test_graph_replays_match_eager():
         gt.gemm_bias_f16(A, B, bias, "relu", Dr)
         gt.gemm_splitk_f16(Ak, Bk, Dk, workspace=wk)
         gt.gemm_splitk_f16(Aq, Bq, Dq, workspace=wq)
+        gt.gemm_f16(Aw, Bw, Dw)
 
     work()
     torch.cuda.synchronize(dev)
