@@ -467,14 +467,15 @@ static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, 
                                   int num_cus, hipStream_t stream) {
   const int pr = skinny_default_rows(R, num_cus);
   if (S > 32) {
-    // 33..64 small-side rows: 64 staged Q rows, 4 waves, a 2-stage ring of
-    // (PR + 64) KiB stages, the partial sums reusing the ring.
+    // 33..64 small-side rows: 64 staged Q rows, 8 waves (1-4 % ahead of 4,
+    // 16 waves 5-17 % behind), a 2-stage ring of (PR + 64) KiB stages, the
+    // partial sums reusing the ring.
     switch (pr) {
-      case 16: return launch_lds<4, 2, 64, DT, 16, false, true>(P, Q, D, R, S, K, trans, stream);
-      case 8: return launch_lds<4, 2, 64, DT, 8, false, true>(P, Q, D, R, S, K, trans, stream);
-      case 4: return launch_lds<4, 2, 64, DT, 4>(P, Q, D, R, S, K, trans, stream);
-      case 2: return launch_lds<4, 2, 64, DT, 2>(P, Q, D, R, S, K, trans, stream);
-      default: return launch_lds<4, 2, 64, DT, 1>(P, Q, D, R, S, K, trans, stream);
+      case 16: return launch_lds<8, 2, 64, DT, 16, false, true>(P, Q, D, R, S, K, trans, stream);
+      case 8: return launch_lds<8, 2, 64, DT, 8, false, true>(P, Q, D, R, S, K, trans, stream);
+      case 4: return launch_lds<8, 2, 64, DT, 4>(P, Q, D, R, S, K, trans, stream);
+      case 2: return launch_lds<8, 2, 64, DT, 2>(P, Q, D, R, S, K, trans, stream);
+      default: return launch_lds<8, 2, 64, DT, 1>(P, Q, D, R, S, K, trans, stream);
     }
   }
   if (S > kSkinnyMaxRows) {
