@@ -15,6 +15,8 @@ Prints ONE JSON line on stdout:
   decode_batch the 8x4096x14336 GEMM (skinny path) in GB/s, timed on its own
   bf16         gemm_bf16 at 4096^3 and gemv_bf16 at 4096x14336, bf16 inputs of
                the same shapes, timed on their own after the decode batch
+  vendor_same_box  torch.matmul on the same fp16 4096^3 inputs, timed after
+               the rest: where this box's power-limited clock stands
   cpu_baseline the CPU oracle (FP64, OpenMP) on a bounded sample of rows of
                the same GEMM, scaled to TFLOP/s, plus the full GEMV in GB/s
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 2000]
@@ -37,7 +39,8 @@ GEMV_N, GEMV_K = 4096, 14336
 GEMM_SETS = 3
 DECODE_REPS = 20  # event pairs around 5 decode-batch launches, after the timed steps
 BF16_REPS = 50  # event triples around one gemm_bf16 and 5 gemv_bf16, after the decode batch
-SECTION_WARMUP = 200  # untimed repetitions before the decode-batch and bf16 timings
+SECTION_WARMUP = 200  # untimed repetitions before the decode-batch, bf16 and vendor timings
+VENDOR_REPS = 50  # event pairs around one vendor GEMM, the same-box reference
 GEMV_COPIES = 5
 # Beyond-L2 traffic per launch measured with rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch, each scaled by what the same counter reads for
@@ -306,6 +309,23 @@ def main():
     gemv_bf16_gbps = gemv_bytes / gemv_bf16_s / 1e9
     del gemv_b, Wb, Ab, Bb, Db
 
+    # ---- the vendor BLAS on the same inputs, same process (reference) ----
+    # The part's power-limited clock differs from box to box by several per
+    # cent; the vendor GEMM timed here, after the steps, shows where a box
+    # stands.  Not part of the timed region, nor of `value`.
+    vendor_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(VENDOR_REPS)]
+    for i in range(SECTION_WARMUP):
+        A, B, D = gemm_sets[i % GEMM_SETS]
+        torch.matmul(A, B.t(), out=D)
+    torch.cuda.synchronize(dev)
+    for i, e in enumerate(vendor_events):
+        A, B, D = gemm_sets[i % GEMM_SETS]
+        e[0].record(stream)
+        torch.matmul(A, B.t(), out=D)
+        e[1].record(stream)
+    torch.cuda.synchronize(dev)
+    vendor_gemm_s = float(np.mean([e[0].elapsed_time(e[1]) for e in vendor_events])) / 1e3
+
     # The part's own compute peak, for context next to the published one the
     # rooflines use: dense fp16 MFMA = CUs x 4096 flop per clock at the peak
     # engine clock (the published 2.5 PFLOP/s is 256 CUs x 4096 x 2.4 GHz).
@@ -405,6 +425,12 @@ def main():
             "gemv_frac": round(gemv_bf16_gbps / metrics.PEAK_HBM_GBPS, 4),
             "gemm_traffic": traffic("gemm_bf16"),
             "gemv_traffic": traffic("gemv_bf16"),
+        },
+        "vendor_same_box": {
+            "kind": "torch.matmul (vendor BLAS) on the same fp16 4096^3 inputs, timed after the steps",
+            "gemm_us_per_launch": round(vendor_gemm_s * 1e6, 2),
+            "gemm_tflops": round(flops / vendor_gemm_s / 1e12, 2),
+            "ours_over_vendor_time": round(gemm_s / vendor_gemm_s, 4),
         },
         "device": device,
         "cpu_baseline": cpu,
