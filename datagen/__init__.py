@@ -32,6 +32,7 @@ __all__ = [
     "uniform_bf16",
     "integer_bf16",
     "sample_rows",
+    "band_rows",
     "gemm_inputs",
     "gemv_inputs",
 ]
@@ -108,6 +109,15 @@ def sample_rows(cfg_id: int, M: int, count: int) -> np.ndarray:
     """`count` distinct row indices of [0, M), sorted (tensor id 2)."""
     g = rng(cfg_id, 2)
     return np.sort(g.choice(M, size=min(count, M), replace=False)).astype(np.int64)
+
+
+def band_rows(cfg_id: int, M: int, band: int = 256) -> np.ndarray:
+    """One row drawn uniformly from every `band`-row band of [0, M) (tensor
+    id 4), sorted: with band = the output tile height, every tile row of the
+    output holds at least one of them."""
+    g = rng(cfg_id, 4)
+    starts = np.arange(0, M, band)
+    return np.sort(starts + np.floor(g.random(len(starts)) * np.minimum(band, M - starts)).astype(np.int64))
 
 
 def gemm_inputs(w: Workload, integer: bool = False, bf16: bool = False):

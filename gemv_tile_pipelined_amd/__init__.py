@@ -47,7 +47,8 @@ __all__ = [
     "gemm_tile",
     "gemv_grid",
     "device_caps",
-    "read_stream",
+    "ring_trace",
+    "alloc_splitk_workspace",
 ]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemvtile.so")
@@ -71,7 +72,7 @@ EXPORTED_SYMBOLS = (
     "gemvtile_gemm_tile",
     "gemvtile_gemv_grid",
     "gemvtile_device_caps",
-    "gemvtile_read_stream",
+    "gemvtile_ring_trace",
     "gemvtile_gemm_f16_variant",
     "gemvtile_gemv_f16_variant",
     "gemvtile_xcd_logical_id",
@@ -152,8 +153,8 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemvtile_gemv_grid.restype = i64
     lib.gemvtile_device_caps.argtypes = [intp] * 4
     lib.gemvtile_device_caps.restype = c_int
-    lib.gemvtile_read_stream.argtypes = [vp, i64, c_int, c_int, vp, vp]
-    lib.gemvtile_read_stream.restype = c_int
+    lib.gemvtile_ring_trace.argtypes = [c_int, c_int, c_int, i64, ctypes.POINTER(ctypes.c_int32), i64, intp]
+    lib.gemvtile_ring_trace.restype = i64
     if path == LIBRARY_PATH:
         _lib = lib
     return lib
@@ -311,16 +312,24 @@ def splitk_workspace_bytes(M: int, N: int, K: int, num_cus: int) -> int:
     return int(load_library().gemvtile_gemm_splitk_workspace(M, N, K, num_cus))
 
 
+def alloc_splitk_workspace(A, B, dtype=None):
+    """Allocate (on the caller's behalf, explicitly) a device workspace large
+    enough for gemm_splitk_*(A, B): a uint8 tensor of
+    max(splitk_workspace_bytes(M, N, K, #CUs), 16) bytes on A's device.  The
+    split-K calls themselves never allocate: the caller passes this (or any
+    large enough) buffer as `workspace`."""
+    torch = _torch()
+    M, K = A.shape
+    N = B.shape[0]
+    cus = torch.cuda.get_device_properties(A.device).multi_processor_count
+    need = splitk_workspace_bytes(M, N, K, cus)
+    return torch.empty((max(need, 16),), dtype=torch.uint8, device=A.device)
+
+
 def _gemm_splitk(A, B, D, workspace, stream, dtype, call):
     torch = _torch()
-    if workspace is None:
-        _require(A, "A", 2, dtype)
-        _require(B, "B", 2, dtype)
-        cus = torch.cuda.get_device_properties(A.device).multi_processor_count
-        need = splitk_workspace_bytes(A.shape[0], B.shape[0], A.shape[1], cus)
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=A.device) if need else None
     if workspace is not None and (not isinstance(workspace, torch.Tensor) or not workspace.is_cuda):
-        raise TypeError("workspace must be a device tensor")
+        raise TypeError("workspace must be a device tensor (see alloc_splitk_workspace)")
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
 
@@ -333,8 +342,11 @@ def _gemm_splitk(A, B, D, workspace, stream, dtype, call):
 def gemm_splitk_f16(A, B, D=None, workspace=None, stream=None):
     """D = A · Bᵀ with K split across workgroups for small outputs; fp16.
     `workspace`: a device tensor of at least splitk_workspace_bytes(...)
-    bytes, or None to allocate one here.  Enqueued on `stream`, not
-    synchronised."""
+    bytes (alloc_splitk_workspace makes one), owned by the caller.  Shapes
+    that do not split need none; a shape that splits with no workspace, or
+    too small a one, raises GemvTileError (GEMVTILE_ERR_INVALID_ARG).  This
+    call allocates nothing but the output D when D is None.  Enqueued on
+    `stream`, not synchronised."""
     return _gemm_splitk(A, B, D, workspace, stream, _torch().float16, load_library().gemm_splitk_f16)
 
 
@@ -381,22 +393,6 @@ def gemv_bf16(x, W, y=None, stream=None):
     return _gemv(x, W, y, stream, _torch().bfloat16, load_library().gemv_bf16)
 
 
-def read_stream(buf, sink, policy: int = 1, blocks: int = 256, stream=None):
-    """Measurement only: stream all bytes of the device tensor `buf` with the
-    read-only probe kernel (policy 0 none, 1 nt, 2 sc1 nt, 3 sc0 nt); `sink`
-    is a device tensor of at least `blocks` 32-bit words."""
-    torch = _torch()
-    if not (buf.is_cuda and sink.is_cuda and buf.is_contiguous()):
-        raise ValueError("buf and sink must be contiguous device tensors")
-    if sink.numel() * sink.element_size() < 4 * blocks:
-        raise ValueError("sink must hold at least `blocks` 32-bit words")
-    s = _stream_handle(buf, stream)
-    with torch.cuda.device(buf.device):
-        st = load_library().gemvtile_read_stream(buf.data_ptr(), buf.numel() * buf.element_size(), policy, blocks,
-                                                 sink.data_ptr(), s)
-    _check(st)
-
-
 def gemm_f16_variant(A, B, variant: int, D=None, stream=None):
     """gemm_f16 through an internal kernel variant (measurement only)."""
     return gemm_f16(A, B, D, stream, variant)
@@ -438,6 +434,27 @@ def gemm_tile(M: int, N: int, num_cus: int) -> tuple:
 
 def gemv_grid(N: int, num_cus: int) -> int:
     return int(load_library().gemvtile_gemv_grid(N, num_cus))
+
+
+RING_EVENTS = {1: "load", 2: "wait", 3: "lds_wait", 4: "barrier", 5: "read", 6: "mfma"}
+
+
+def ring_trace(bm: int, bn: int, stages: int, ktu: int):
+    """The tiled GEMM kernel's K-loop schedule over ktu K tiles (host-only):
+    (events, info) with events a list of (name, a, b, c, d) tuples as
+    gemvtile_ring_trace describes, info = {"loads_per_tile", "reads_per_step",
+    "ksteps", "mfma_per_step"}."""
+    lib = load_library()
+    info = (ctypes.c_int * 4)()
+    n = int(lib.gemvtile_ring_trace(bm, bn, stages, ktu, None, 0, info))
+    if n < 0:
+        raise GemvTileError(1, f"no tiled kernel with a {bm}x{bn} tile and {stages} stages, or ktu out of range")
+    buf = (ctypes.c_int32 * (5 * max(n, 1)))()
+    n2 = int(lib.gemvtile_ring_trace(bm, bn, stages, ktu, buf, n, info))
+    assert n2 == n
+    events = [(RING_EVENTS[buf[5 * i]], buf[5 * i + 1], buf[5 * i + 2], buf[5 * i + 3], buf[5 * i + 4]) for i in range(n)]
+    keys = ("loads_per_tile", "reads_per_step", "ksteps", "mfma_per_step")
+    return events, dict(zip(keys, list(info)))
 
 
 def device_caps() -> dict:

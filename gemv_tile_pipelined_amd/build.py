@@ -19,6 +19,13 @@ the code it produced, in two ways, and fails if either finds a problem:
     MFMA's destination registers within MFMA_RESULT_WAIT wait states of it,
     and no VALU instruction writes an MFMA source register within
     VALU_TO_MFMA_WAIT wait states before it.
+
+The direct-to-LDS tile loads are inline asm that write M0 (the LDS address)
+and use it in the same statement.  The compiler reserves M0 for its own use
+and does not know these statements change it, so they are only safe while
+the compiler keeps no value in M0 across them.  The build checks that too:
+in every kernel whose inline asm writes M0, no instruction the compiler
+emitted reads or writes M0, explicitly or implicitly (scan_m0_uses).
 """
 from __future__ import annotations
 
@@ -32,7 +39,7 @@ import tempfile
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in ("api.hip", "gemm.hip", "gemm_ws.hip", "gemv.hip", "probe.hip", "skinny.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("api.hip", "gemm.hip", "gemm_ws.hip", "gemv.hip", "skinny.hip")]
 LIBRARY = os.path.join(PKG_DIR, "libgemvtile.so")
 ARCH = "gfx950"
 
@@ -48,6 +55,12 @@ HIPCC_FLAGS = [
     "-target-feature",
     "-Xclang",
     "-packed-fp32-ops",
+    # The pipelined GEMM K loop (ring.hpp) is written as fully unrolled loops
+    # over MFMA slots; its unrolled size exceeds the compiler's default limit
+    # for `#pragma unroll`, and a partly unrolled loop indexes the fragment
+    # arrays at run time, which puts them in scratch memory.
+    "-mllvm",
+    "-pragma-unroll-threshold=200000",
     f"-I{os.path.join(REPO_DIR, 'include')}",
 ]
 
@@ -83,8 +96,8 @@ def required_agprs(kernel: str):
     """AGPRs per lane that the inline-asm MFMA accumulators of a kernel need,
     or None for a kernel without such accumulators.
 
-    gemm_kernel<GemmShape<BM, BN, BK, STAGES, WAVES_M, WAVES_N, ..., MI, ...>>
-    holds a (BM / WAVES_M) x (BN / WAVES_N) FP32 block per wave, one value
+    gemm_kernel<GemmShape<BM, BN, BK, STAGES, WAVES_M, WAVES_N, SWIZZLE,
+    PERSISTENT, DMA_STRIDE, MI, ...>> holds a (BM / WAVES_M) x (BN / WAVES_N) FP32 block per wave, one value
     per lane per 64 outputs; only its MI == 16 form uses inline-asm MFMAs.
     gemm_ws_kernel's consumer waves hold 128 x 64 outputs each."""
     if "gemm_ws_kernel" in kernel:
@@ -93,18 +106,28 @@ def required_agprs(kernel: str):
     if not m:
         return None
     args = [int(a) for a in re.findall(r"L[ib](\d+)E", m.group(1))]
-    bm, bn, waves_m, waves_n, mi = args[0], args[1], args[4], args[5], args[13]
+    bm, bn, waves_m, waves_n, mi = args[0], args[1], args[4], args[5], args[9]
     if mi != 16:
         return None
     return (bm // waves_m) * (bn // waves_n) // 64
 
 
+# Scratch bytes per lane an inline-asm MFMA kernel may use.  A few spilled
+# dwords outside the K loop occur (the fused-bias epilogue spills 28 bytes of
+# addresses); a partly unrolled K loop puts its operand fragment arrays in
+# scratch (hundreds of bytes), which this limit rejects.
+MAX_SCRATCH_BYTES = 64
+
+
 def check_resource_usage(usage: dict) -> list:
-    """Kernels whose inline-asm MFMA accumulators do not all fit in AGPRs."""
+    """Kernels whose inline-asm MFMA accumulators do not all fit in AGPRs, or
+    that keep more than MAX_SCRATCH_BYTES per lane in scratch memory."""
     bad = []
     for name, u in sorted(usage.items()):
         need = required_agprs(name)
-        if need is not None and u.get("AGPRs", 0) < need:
+        if need is None:
+            continue
+        if u.get("AGPRs", 0) < need or u.get("ScratchSize", 0) > MAX_SCRATCH_BYTES:
             bad.append(f"{name}: {u.get('AGPRs', 0)} AGPRs for {need} accumulator registers, "
                        f"scratch {u.get('ScratchSize', 0)} bytes/lane")
     return bad
@@ -208,15 +231,75 @@ def scan_mfma_hazards(asm: str, kernels=INLINE_MFMA_KERNELS) -> list:
     return bad
 
 
+def _compile_one(src: str, work: str, extra_flags, verbose: bool):
+    """Compile one source to an object in its own directory (so -save-temps
+    keeps that source's device assembly apart); returns (object, compiler
+    output, return code, {assembly name: text})."""
+    name = os.path.splitext(os.path.basename(src))[0]
+    wdir = os.path.join(work, name)
+    os.makedirs(wdir, exist_ok=True)
+    obj = os.path.join(wdir, name + ".o")
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    cmd = [hipcc(), *flags, "-c", RESOURCE_REMARKS, "-save-temps=cwd", *extra_flags, src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True, cwd=wdir)
+    asm = {os.path.basename(f): open(f).read() for f in glob.glob(os.path.join(wdir, "*-hip-amdgcn-*.s"))}
+    return obj, res.stdout + res.stderr, res.returncode, asm
+
+
+# Instructions that read M0 without naming it (gfx9 family): indexed register
+# moves, messages, GWS and ordered-count LDS operations, LDS-DMA loads,
+# address-by-lane LDS operations and interpolation.
+_M0_IMPLICIT = re.compile(r"^(s_movrel|v_movrel|s_sendmsg|ds_gws_|ds_ordered_count|ds_append|ds_consume|"
+                          r"ds_read_addtid|ds_write_addtid|v_interp|s_ttracedata|global_load_lds|"
+                          r"scratch_load_lds)")
+_M0_OPERAND = re.compile(r"(?<![\w.])m0(?![\w])")
+
+
+def _uses_m0(ins: str) -> bool:
+    op = ins.split()[0]
+    if _M0_IMPLICIT.match(op):
+        return True
+    if op.startswith("buffer_load") and re.search(r"\blds\b", ins):
+        return True
+    return bool(_M0_OPERAND.search(ins.split(None, 1)[1] if len(ins.split(None, 1)) > 1 else ""))
+
+
+def scan_m0_uses(asm: str) -> list:
+    """Compiler-emitted instructions that read or write M0 in a function whose
+    inline asm writes M0 (see the module docstring)."""
+    bad = []
+    for name, body in _functions(asm):
+        if not any(from_asm and _M0_OPERAND.search(ins) and ins.split()[0].startswith("s_mov") for ins, from_asm in body):
+            continue
+        for ins, from_asm in body:
+            if not from_asm and _uses_m0(ins):
+                bad.append(f"{name}: compiler-emitted '{ins}' uses M0, which inline asm in this kernel writes")
+    return bad
+
+
 def build_library(output: str = LIBRARY, extra_flags=(), verbose: bool = False) -> str:
+    from concurrent.futures import ThreadPoolExecutor
+
     tmp = output + ".tmp"
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with tempfile.TemporaryDirectory(prefix="gemvtile_build_") as work:
-        cmd = [hipcc(), *HIPCC_FLAGS, RESOURCE_REMARKS, "-save-temps=cwd", *extra_flags, *SOURCES, "-o", tmp]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True, cwd=work)
-        asm = {os.path.basename(f): open(f).read() for f in glob.glob(os.path.join(work, "*-hip-amdgcn-*.s"))}
-    text = res.stdout + res.stderr
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            results = list(ex.map(lambda s: _compile_one(s, work, extra_flags, verbose), SOURCES))
+        text = "".join(r[1] for r in results)
+        asm = {}
+        for r in results:
+            asm.update(r[3])
+        failed = [os.path.basename(s) for s, r in zip(SOURCES, results) if r[2] != 0]
+        if not failed:
+            link = [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", *[r[0] for r in results], "-o", tmp]
+            if verbose:
+                print(" ".join(link), flush=True)
+            lres = subprocess.run(link, capture_output=True, text=True, cwd=work)
+            text += lres.stdout + lres.stderr
+            if lres.returncode != 0:
+                failed.append("link")
     # hipcc's host pass always warns about the device-only feature flag; the
     # resource remarks are parsed below rather than shown.
     noise = ("is not a recognized feature for this target", "warning generated", "warnings generated",
@@ -232,8 +315,8 @@ def build_library(output: str = LIBRARY, extra_flags=(), verbose: bool = False) 
         if i > 1 and "remark:" in lines[i - 2] and ln.strip().startswith("|"):
             continue
         msgs.append(ln)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if failed:
+        raise RuntimeError(f"hipcc failed ({', '.join(failed)}):\n" + "\n".join(msgs))
     usage = parse_resource_usage(text)
     bad = check_resource_usage(usage)
     if not usage:
@@ -242,9 +325,10 @@ def build_library(output: str = LIBRARY, extra_flags=(), verbose: bool = False) 
         bad.append(f"expected {len(SOURCES)} device assembly files from -save-temps, found {sorted(asm)}")
     for fname, text_s in sorted(asm.items()):
         bad += scan_mfma_hazards(text_s)
+        bad += scan_m0_uses(text_s)
     if bad:
         os.remove(tmp)
-        raise RuntimeError("inline-asm MFMA accumulators moved or touched too early (results would be wrong):\n"
+        raise RuntimeError("inline-asm MFMA accumulators or M0 not left to the inline asm (results would be wrong):\n"
                            + "\n".join(bad[:20]) + (f"\n... {len(bad) - 20} more" if len(bad) > 20 else ""))
     if verbose and msgs:
         print("\n".join(msgs))

@@ -83,17 +83,15 @@ int check_gemv(const void *x, const void *W, const void *y, int64_t N, int64_t K
 int to_status(hipError_t e) { return e == hipSuccess ? GEMVTILE_OK : GEMVTILE_ERR_LAUNCH; }
 
 // The kernel family and index of a gemvtile_gemm_f16_variant number.
-enum class Family { kTiled, kSkinny, kSkinnyExtra, kWs, kInvalid };
+enum class Family { kTiled, kSkinny, kWs, kInvalid };
 struct VariantRef {
   Family family;
   int index;
 };
 VariantRef classify_variant(int variant) {
-  if (variant >= 0 && variant < gt::kGemmVariants) return {Family::kTiled, variant};
-  if (variant >= gt::kSkinnyVariantBase && variant < gt::kSkinnyExtraBase)
+  if (gt::gemm_variant_exists(variant)) return {Family::kTiled, variant};
+  if (variant >= gt::kSkinnyVariantBase && gt::skinny_variant_exists(variant - gt::kSkinnyVariantBase))
     return {Family::kSkinny, variant - gt::kSkinnyVariantBase};
-  if (variant >= gt::kSkinnyExtraBase && variant < gt::kSkinnyExtraBase + gt::kSkinnyWpVariants)
-    return {Family::kSkinnyExtra, variant - gt::kSkinnyExtraBase};
   if (variant >= gt::kGemmWsVariantBase && variant < gt::kGemmWsVariantBase + gt::kGemmWsVariants)
     return {Family::kWs, variant - gt::kGemmWsVariantBase};
   return {Family::kInvalid, 0};
@@ -112,11 +110,7 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   const bool skinny = M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows;
   const VariantRef v = classify_variant(variant);
   if (v.family == Family::kInvalid) return GEMVTILE_ERR_INVALID_ARG;
-  if (v.family == Family::kSkinny || v.family == Family::kSkinnyExtra) {
-    if (!skinny) return GEMVTILE_ERR_UNSUPPORTED;
-    const bool q8 = v.family == Family::kSkinny ? gt::skinny_variant_q8(v.index) : gt::skinny_wp_variant_q8(v.index);
-    if (q8 && (M < N ? M : N) > 8) return GEMVTILE_ERR_UNSUPPORTED;
-  }
+  if (v.family == Family::kSkinny && !skinny) return GEMVTILE_ERR_UNSUPPORTED;
   int cus = 0;
   st = current_cu_count(&cus);
   if (st != GEMVTILE_OK) return st;
@@ -125,7 +119,6 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   // only); the skinny ones apply to skinny shapes only.
   if (v.family == Family::kSkinny)
     return to_status(gt::launch_gemm_skinny_f16(v.index, A, B, D, m, n, k, cus, s));
-  if (v.family == Family::kSkinnyExtra) return to_status(gt::launch_gemm_skinny_wp_f16(v.index, A, B, D, m, n, k, s));
   if (v.family == Family::kWs) return to_status(gt::launch_gemm_ws_f16(v.index, A, B, D, m, n, k, cus, s));
   if (variant == 0 && (M == 1 || N == 1)) {
     // One row on a side is the batch-1 product y = x·Wᵀ: M == 1 is
@@ -280,7 +273,7 @@ int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, 
 
 int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream,
                               int variant) {
-  if (variant < 0 || variant >= gt::kGemvVariants) return GEMVTILE_ERR_INVALID_ARG;
+  if (!gt::gemv_variant_exists(variant)) return GEMVTILE_ERR_INVALID_ARG;
   return run_gemv(x, W, y, N, K, stream, variant);
 }
 
@@ -302,6 +295,13 @@ int gemvtile_tile_coord(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t gro
   *tm = c.tm;
   *tn = c.tn;
   return GEMVTILE_OK;
+}
+
+int64_t gemvtile_ring_trace(int bm, int bn, int stages, int64_t ktu, int32_t *events, int64_t cap, int *info) {
+  if (ktu < 1 || ktu > (int64_t{1} << 20) || cap < 0 || (events == nullptr && cap > 0)) return -1;
+  int dummy[4];
+  int *o = info != nullptr ? info : dummy;
+  return gt::ring_trace(bm, bn, stages, static_cast<int>(ktu), events, cap, &o[0], &o[1], &o[2], &o[3]);
 }
 
 int64_t gemvtile_xcd_logical_id(int64_t w, int64_t grid) {

@@ -76,39 +76,30 @@ constexpr uint32_t kOobOffset = 0x80000000u;
 // Issued as inline asm on purpose: the compiler treats its own LDS-DMA
 // builtins as possibly aliasing every later LDS read and then waits for
 // vmcnt(0) before each one, which would serialise the multi-stage ring.  The
-// ring below does its own vmcnt accounting instead.  The s_nop covers the
-// one wait state required between writing M0 and an LDS-DMA instruction.
+// ring does its own vmcnt accounting instead.  The s_nop covers the one wait
+// state required between writing M0 and an LDS-DMA instruction.
+//
+// M0 is written and used inside one asm statement, so no value of M0 lives
+// across statements.  The compiler reserves M0 and warns that clobbering it
+// may be unsafe: it would be if compiler-generated code kept a value in M0
+// across one of these statements.  build.py checks the generated code of
+// every kernel that uses this load and fails the build if any instruction
+// outside these statements reads or writes M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// POLICY selects the cache-policy modifier of the load: 0 none, 1 sc0,
-// 2 nt, 3 sc0 nt, 4 sc1.
+// POLICY selects the cache-policy modifier of the load: 0 none, 2 nt
+// (streamed: data read once).
 template <int POLICY = 0>
 __device__ inline void lds_dma_b128(int4_t rsrc, uint32_t voffset, uint32_t lds_base) {
-  static_assert(POLICY >= 0 && POLICY <= 4, "cache policy");
+  static_assert(POLICY == 0 || POLICY == 2, "cache policy");
   if constexpr (POLICY == 0) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                  : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
-  } else if constexpr (POLICY == 1) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen sc0 lds"
-                 : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
-  } else if constexpr (POLICY == 2) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen nt lds"
-                 : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
-  } else if constexpr (POLICY == 3) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen sc0 nt lds"
-                 : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
   } else {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen sc1 lds"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen nt lds"
                  : : "v"(voffset), "s"(lds_base), "s"(rsrc) : "memory", "m0");
   }
 }
-// The same load with M0 already holding lds_base (written by set_m0 at
-// least one instruction earlier): the caller keeps M0 for its loads, so only
-// the load itself takes an issue slot.
-__device__ inline void lds_dma_b128_m0_set(int4_t rsrc, uint32_t voffset) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(rsrc) : "memory");
-}
-__device__ inline void set_m0(uint32_t lds_base) { asm volatile("s_mov_b32 m0, %0" : : "s"(lds_base) : "m0"); }
 #pragma clang diagnostic pop
 
 // Wait until at most N vector-memory operations of this wave are in flight.

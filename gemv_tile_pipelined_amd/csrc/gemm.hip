@@ -75,14 +75,13 @@
 
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "ring.hpp"
 #include "tile_order.hpp"
 
 namespace gt {
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WAVES_M_, int WAVES_N_, bool SWIZZLE_, bool PERSISTENT_,
-          int DMA_STRIDE_, int DMA_PHASES_, int K_STAGGER_ = 1, int K_STAGGER_STEP_ = 1, int LOAD_POLICY_ = 0,
-          int MI_ = 32, int READ_STRIDE_ = 1, int DMA_OFFSET_ = 0, bool FUSE_DMA_ = false, int DTYPE_ = kF16,
-          bool PRESET_M0_ = false, bool PROLOGUE_ALL_ = false, bool NT_STORE_ = true>
+          int DMA_STRIDE_, int MI_ = 32, int READ_STRIDE_ = 1, int DMA_OFFSET_ = 0, int DTYPE_ = kF16>
 struct GemmShape {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -92,20 +91,8 @@ struct GemmShape {
   static constexpr int WAVES_N = WAVES_N_;
   static constexpr bool SWIZZLE = SWIZZLE_;
   static constexpr bool PERSISTENT = PERSISTENT_;
-  // MFMA slots between two consecutive loads of the ring refill, and the
-  // number of slot phases the waves are spread over (wave w issues its loads
-  // DMA_STRIDE / DMA_PHASES * (w % DMA_PHASES) slots later than wave 0).
+  // MFMA slots between two consecutive loads of the ring refill.
   static constexpr int DMA_STRIDE = DMA_STRIDE_;
-  static constexpr int DMA_PHASES = DMA_PHASES_;
-  static_assert(DMA_STRIDE % DMA_PHASES == 0, "phases divide the stride");
-  // K-loop start stagger: output tile t walks its K tiles starting at tile
-  // (t % K_STAGGER) * K_STAGGER_STEP (mod the K tile count) and wraps around,
-  // so workgroups running side by side read different K columns at any
-  // moment instead of all hitting the same one.
-  static constexpr int K_STAGGER = K_STAGGER_;
-  static constexpr int K_STAGGER_STEP = K_STAGGER_STEP_;
-  // Cache-policy modifier of the tile loads (see lds_dma_b128).
-  static constexpr int LOAD_POLICY = LOAD_POLICY_;
   // MFMA block edge: 32 (v_mfma_f32_32x32x16_f16) or 16 (v_mfma_f32_16x16x32_f16).
   static constexpr int MI = MI_;
   static_assert(MI == 32 || MI == 16, "MFMA shape");
@@ -117,35 +104,9 @@ struct GemmShape {
   // loads, which lets them fall between the reads.
   static constexpr int READ_STRIDE = READ_STRIDE_;
   static constexpr int DMA_OFFSET = DMA_OFFSET_;
-  // With 16x16x32 MFMAs: issue each tile load in one asm block with the MFMA
-  // of its slot (see mfma_dma in the kernel).
-  static constexpr bool FUSE_DMA = FUSE_DMA_;
   // Element format of A, B and D (kF16 or kBF16; bf16 only with the
   // hand-written 16x16x32 MFMAs).
   static constexpr int DTYPE = DTYPE_;
-  // Refill loads of the K loop with M0 written for the next load right after
-  // each load (see dma_slot), instead of M0 write + wait state + load in the
-  // load's own slot.
-  static constexpr bool PRESET_M0 = PRESET_M0_;
-  static_assert(!PRESET_M0 || (DMA_PHASES_ == 1 && !FUSE_DMA_ && LOAD_POLICY_ == 0 && STAGES_ >= 2),
-                "M0 presetting is built for the plain single-phase refill");
-  // Prologue: issue the loads of every ring stage (K tiles 0 .. STAGES-1) at
-  // once, instead of tiles 0 .. STAGES-2 and then the last one spread over
-  // the first K tile.  All stages are free at the start of an output tile.
-  // K tile 0 keeps its usual schedule and so loads the second part of tile
-  // STAGES-1 again: the same bytes into a stage that nobody reads before
-  // the barrier that waits for them.  (Peeling K tile 0 out of the loop
-  // instead raised register pressure until the compiler moved accumulators
-  // around the hand-written MFMAs.)
-  static constexpr bool PROLOGUE_ALL = PROLOGUE_ALL_;
-  // Epilogue: D's 16-byte row segments written with non-temporal stores
-  // (streamed to memory, not kept in the caches), or ordinary ones.  With
-  // several tiles per CU, cached D lines would evict the A and B panels the
-  // next tiles read; at 8192^3 the streaming stores are 2 % faster, at
-  // 4096^3 about 1.5 %.  The cost: a kernel that reads D next finds it in
-  // memory rather than in the caches.
-  static constexpr bool NT_STORE = NT_STORE_;
-  static_assert(!PROLOGUE_ALL || (!PRESET_M0_ && STAGES_ >= 2), "whole-ring prologue: pipelined loop, no M0 preset");
   static_assert(DTYPE == kF16 || (DTYPE == kBF16 && MI_ == 16), "bf16 uses the 16x16x32 MFMA path");
   static_assert((BK / kKStep) >= 1 && (BM / WAVES_M / MI) * (BN / WAVES_N / MI) % READ_STRIDE == 0,
                 "the read spacing must divide the MFMA slots of a K step");
@@ -172,6 +133,8 @@ struct GemmShape {
   static constexpr int kRingBytes = STAGES * kStageBytes;
   static constexpr int kLdsBytes = kRingBytes > kStagingBytes ? kRingBytes : kStagingBytes;
   static constexpr int kKSub = BK / kKStep;  // MFMA K steps per K tile
+  static constexpr int kReads = kFragM + kFragN;  // operand reads per wave per K step
+  static constexpr int kMfma = kFragM * kFragN;   // MFMAs per wave per K step
 
   static_assert(BK == 32 || BK == 64, "LDS rows of 64 or 128 bytes");
   // The pipelined loop double-buffers the operand fragments by K-step parity
@@ -200,34 +163,39 @@ struct GemmShape {
   }
 };
 
-// Wave-uniform wait until the K tile this wave needs next has landed in LDS,
-// while `younger` K tiles issued after it may stay in flight.  Loads complete
-// in issue order, so "at most younger*kDmaPerStage outstanding" means every
-// load of the needed tile is done.  vmcnt takes an immediate, so the count is
-// picked from the few values the ring can produce (falling back to a full
-// drain, which is always correct).
-template <class S>
-__device__ inline void wait_tile_landed(int younger) {
-  if constexpr (S::STAGES >= 2) {
-    if (younger >= S::STAGES - 1) {
-      wait_vmcnt<(S::STAGES - 1) * S::kDmaPerStage>();
+// Wait until at most `n` vector-memory operations of this wave are in flight,
+// where n is one of 0, PER, 2*PER, ..., MAXY*PER (the values ring_vmcnt
+// produces for a ring of MAXY+2 stages); vmcnt takes an immediate, so the
+// value is matched against that set, and anything else drains fully (always
+// correct).
+template <int PER, int MAXY>
+__device__ inline void wait_vmcnt_n(int n) {
+  if constexpr (MAXY > 0) {
+    if (n == MAXY * PER) {
+      wait_vmcnt<MAXY * PER>();
       return;
     }
+    wait_vmcnt_n<PER, MAXY - 1>(n);
+  } else {
+    wait_vmcnt<0>();
   }
-  if constexpr (S::STAGES >= 3) {
-    if (younger >= S::STAGES - 2) {
-      wait_vmcnt<(S::STAGES - 2) * S::kDmaPerStage>();
-      return;
-    }
-  }
-  if constexpr (S::STAGES >= 4) {
-    if (younger >= S::STAGES - 3) {
-      wait_vmcnt<(S::STAGES - 3) * S::kDmaPerStage>();
-      return;
-    }
-  }
-  wait_vmcnt<0>();
 }
+
+// The kernel's side of the ring walker (ring.hpp): each event becomes the
+// instruction(s) it stands for.
+template <class S, class Mfma, class Read, class Load>
+struct KernelRingOps {
+  Mfma mfma_fn;
+  Read read_fn;
+  Load load_fn;
+  __device__ __attribute__((always_inline)) void mfma(int buf, int idx) { mfma_fn(buf, idx); }
+  __device__ __attribute__((always_inline)) void read(int buf, int kt, int ks, int r) { read_fn(buf, kt, ks, r); }
+  __device__ __attribute__((always_inline)) void load(int tile, int d) { load_fn(tile, d); }
+  __device__ __attribute__((always_inline)) void wait_tile(int n) { wait_vmcnt_n<S::kDmaPerStage, S::STAGES - 2>(n); }
+  __device__ __attribute__((always_inline)) void wait_lds() { __builtin_amdgcn_s_waitcnt(kWaitLgkm0); }
+  __device__ __attribute__((always_inline)) void barrier() { workgroup_barrier(); }
+  __device__ __attribute__((always_inline)) void fence() { __builtin_amdgcn_sched_barrier(0); }
+};
 
 // One wave per SIMD for 4 waves; with 8 waves two per SIMD, so each is held
 // to half the register file.
@@ -330,8 +298,6 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       const int per = (KT + splits - 1) / splits;  // the host keeps every slice non-empty
       kofs = slice * per;
       KTu = min(per, KT - kofs);
-    } else if constexpr (S::K_STAGGER > 1) {
-      kofs = static_cast<int>((t % S::K_STAGGER) * S::K_STAGGER_STEP) % KT;
     }
     // Operands of load d of K tile kt: buffer descriptor, per-lane byte
     // offset, and the (wave-uniform) LDS address of its 1 KiB destination.
@@ -360,7 +326,7 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       for (int d = 0; d < S::kDmaPerStage; ++d) {
         if (d < first || d >= last) continue;
         const DmaArgs g = dma_args(kt, d);
-        lds_dma_b128<S::LOAD_POLICY>(g.rsrc, g.voffset, g.lds);
+        lds_dma_b128(g.rsrc, g.voffset, g.lds);
       }
     };
 
@@ -368,9 +334,8 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
     // Operand read r (of kReads) of K step ks of K tile kt into buffer buf.
     // Reads go out as fa[0], fb[0..kFragN-1], fa[1..kFragM-1], which is the
     // order the row-major MFMA sequence below first needs them in.
-    constexpr int kReads = S::kFragM + S::kFragN;
-    constexpr int kMfma = S::kFragM * S::kFragN;
-    static_assert(kMfma >= kReads * S::READ_STRIDE, "MFMA slots for the operand reads");
+    constexpr int kReads = S::kReads;
+    constexpr int kMfma = S::kMfma;
     auto read_frag = [&](int buf, int kt, int ks, int r) {
       const char *stage_ptr = smem + (kt % S::STAGES) * S::kStageBytes;
       const uint32_t chunk = static_cast<uint32_t>(((ks * (S::kKStep / 8) + frag_kchunk) ^ frag_swz) * 16);
@@ -433,29 +398,6 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
                        : "v"(fb[buf][j]), "v"(fa[buf][i]));
       }
     };
-    // A 16x16x32 MFMA together with one tile load, in one asm block: M0 (the
-    // load's LDS address) is written before the MFMA, which then serves as the
-    // wait state the load needs after an M0 write.  Issued separately, the M0
-    // write, its s_nop and the load take longer than one 16x16x32 MFMA slot
-    // and delay the next MFMA.  Fusing removes most of that delay (about 7K
-    // cycles per wave at 4096^3), but the chip is power-limited and its clock
-    // drops by more: the default issues the loads separately.
-    constexpr bool kFusedDma =
-        S::FUSE_DMA && S::MI == 16 && S::DMA_PHASES == 1 && S::LOAD_POLICY == 0 && S::DTYPE == kF16;
-    auto mfma_dma = [&](int buf, int idx, const DmaArgs &g) {
-      const int i = idx / S::kFragN;
-      const int j = idx % S::kFragN;
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-      asm volatile(
-          "s_mov_b32 m0, %3\n\t"
-          "v_mfma_f32_16x16x32_f16 %0, %1, %2, %0\n\t"
-          "buffer_load_dwordx4 %4, %5, 0 offen lds"
-          : "+a"(acc[i][j])
-          : "v"(fb[buf][j]), "v"(fa[buf][i]), "s"(g.lds), "v"(g.voffset), "s"(g.rsrc)
-          : "memory", "m0");
-#pragma clang diagnostic pop
-    };
     // Wait states between the last hand-written MFMA and any read of its
     // result: more than the 16x16x32 MFMA's pass count requires.  The
     // sched_barrier keeps the accumulator reads after the padding.
@@ -466,16 +408,12 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       }
     };
 
-    // Every wave must be done with the previous output tile's LDS (ring and
-    // epilogue staging) before the ring is refilled.  The previous tile's
-    // stores may still be in flight: they are older than every ring load, so
-    // they can only make the ring's vmcnt waits more conservative.
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    workgroup_barrier();
-
     if constexpr (S::STAGES == 1) {
       // No overlap: load, wait, compute -- the serial order the TVM chapter
-      // starts from before its step 5 adds a second stage.
+      // starts from before its step 5 adds a second stage.  Every wave must
+      // first be done with the previous output tile's LDS.
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      workgroup_barrier();
       for (int kt = 0; kt < KTu; ++kt) {
         issue_loads(kt, 0, S::kDmaPerStage);
         wait_vmcnt<0>();
@@ -490,145 +428,20 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
         workgroup_barrier();
       }
     } else {
-      // One K tile in a fixed instruction order (sched_barrier pins it).
-      // Every READ_STRIDE-th MFMA slot of a non-final K step carries one
-      // operand read for the next step (spread out so that the four waves'
-      // reads do not outrun the LDS); the final K step meets the other waves
-      // after its first kBarrierAt MFMAs and fetches the next K tile's first
-      // operands, at the same spacing, during the rest.  The barrier frees stage kt, and its refill with K tile
-      // kt + STAGES starts right there.  The refill's loads go out one every
-      // DMA_STRIDE MFMA slots: bunched together, the four waves' loads
-      // saturate the texture path and stall MFMA issue, while spread too
-      // thin the last load lands too close to the barrier that needs it.
-      // Load d of a refill sits at position DMA_OFFSET + d*DMA_STRIDE
-      // counted in MFMA slots from the barrier that starts it, and every position is below
-      // the K tile length, so a tile is fully issued one barrier before the
-      // barrier that waits for it.
-      constexpr int kBarrierAt = kMfma - kReads * S::READ_STRIDE;  // MFMAs before the barrier
-      constexpr int kAfter = kMfma - kBarrierAt;       // slots after the barrier
-      constexpr int kTileSlots = S::kKSub * kMfma;     // MFMA slots per K tile
-      constexpr int kPhaseStep = S::DMA_STRIDE / S::DMA_PHASES;
-      static_assert((S::kDmaPerStage - 1) * S::DMA_STRIDE + (S::DMA_PHASES - 1) * kPhaseStep + S::DMA_OFFSET <
-                        kTileSlots,
-                    "refill must finish within a K tile");
-      // Load index issued at slot position `pos` by a wave of slot phase `ph`, or -1.
-      auto dma_at = [&](int pos, int ph) -> int {
-        const int q = pos - S::DMA_OFFSET - ph * kPhaseStep;
-        return (q >= 0 && q % S::DMA_STRIDE == 0 && q / S::DMA_STRIDE < S::kDmaPerStage) ? q / S::DMA_STRIDE : -1;
-      };
-      // This wave's load slot phase (wave-uniform, so the branches below are
-      // scalar branches).
-      const int phase = __builtin_amdgcn_readfirstlane(wave % S::DMA_PHASES);
-      // Issue, at slot position `pos`, the load of K tile `tile` that this
-      // wave's phase places there, if any.
-      auto dma_slot = [&](int tile, int pos) {
-#pragma unroll
-        for (int ph = 0; ph < S::DMA_PHASES; ++ph) {
-          const int d = dma_at(pos, ph);
-          if (d >= 0 && (S::DMA_PHASES == 1 || phase == ph)) {
-            if constexpr (S::PRESET_M0) {
-              // M0 already holds this load's LDS address.  The refill loads
-              // go out in the order (tile, 0..kDmaPerStage-1), (tile+1, 0),
-              // ..., so point M0 at the next one now; past the last refill
-              // the value is simply never used.
-              const DmaArgs g = dma_args(tile, d);
-              lds_dma_b128_m0_set(g.rsrc, g.voffset);
-              set_m0(d + 1 < S::kDmaPerStage ? dma_args(tile, d + 1).lds : dma_args(tile + 1, 0).lds);
-            } else {
-              issue_loads(tile, d, d + 1);
-            }
-          }
-        }
-      };
-      auto ktile = [&](int kt, auto rest_c, auto early_c, auto next_c) {
-        constexpr bool kRest = decltype(rest_c)::value;      // continue loading K tile kt + STAGES - 1
-        constexpr bool kEarlyOn = decltype(early_c)::value;  // start loading K tile kt + STAGES
-        constexpr bool kNext = decltype(next_c)::value;      // a K tile follows this one
-#pragma unroll
-        for (int ks = 0; ks < S::kKSub; ++ks) {
-          const int cur = ks & 1;
-          const bool last = ks == S::kKSub - 1;
-#pragma unroll
-          for (int idx = 0; idx < kMfma; ++idx) {
-            if (last && kNext && idx == kBarrierAt) {
-              // Tiles 0 .. min(KTu, kt + STAGES) - 1 have been issued in full;
-              // tile kt+1 must have landed for every wave, and every wave must
-              // be done reading stage kt before anyone refills it.
-              wait_tile_landed<S>(min(KTu, kt + S::STAGES) - (kt + 2));
-              __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-              workgroup_barrier();
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            // The tile load (if any) that this slot carries.
-            int dma_tile = -1, dma_d = -1;
-            if (last && idx >= kBarrierAt) {
-              if (kEarlyOn) {
-                dma_tile = kt + S::STAGES;
-                dma_d = dma_at(idx - kBarrierAt, 0);
-              }
-            } else if (kRest) {
-              dma_tile = kt + S::STAGES - 1;
-              dma_d = dma_at(kAfter + ks * kMfma + idx, 0);
-            }
-            if (kFusedDma && dma_d >= 0) {
-              mfma_dma(cur, idx, dma_args(dma_tile, dma_d));
-            } else {
-              mfma(cur, idx);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (!last) {
-              if (idx % S::READ_STRIDE == 0 && idx / S::READ_STRIDE < kReads) {
-                read_frag(cur ^ 1, kt, ks + 1, idx / S::READ_STRIDE);
-                __builtin_amdgcn_sched_barrier(0);
-              }
-            } else if (kNext && idx >= kBarrierAt && (idx - kBarrierAt) % S::READ_STRIDE == 0) {
-              read_frag(cur ^ 1, kt + 1, 0, (idx - kBarrierAt) / S::READ_STRIDE);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            if (!kFusedDma) {
-              if (last && idx >= kBarrierAt) {
-                if (kEarlyOn) {
-                  dma_slot(kt + S::STAGES, idx - kBarrierAt);
-                  __builtin_amdgcn_sched_barrier(0);
-                }
-              } else if (kRest) {
-                dma_slot(kt + S::STAGES - 1, kAfter + ks * kMfma + idx);
-                __builtin_amdgcn_sched_barrier(0);
-              }
-            }
-          }
-        }
-        if constexpr (!kNext) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      };
-
-      // Prologue: K tiles 0 .. STAGES-2 in flight (0 .. STAGES-1 with
-      // PROLOGUE_ALL); once tile 0 has landed the
-      // loads of tile STAGES-1 that would follow a barrier go out, the rest
-      // during K tile 0.
-      constexpr int kPrologueTiles = S::PROLOGUE_ALL ? S::STAGES : S::STAGES - 1;
-#pragma unroll
-      for (int s = 0; s < kPrologueTiles; ++s)
-        if (s < KTu) issue_loads(s, 0, S::kDmaPerStage);
-      wait_tile_landed<S>(min(KTu, kPrologueTiles) - 1);
-      workgroup_barrier();
-      load_frags(0, 0, 0);
-      // The chain of refill loads starts with load 0 of K tile STAGES-1.
-      if constexpr (S::PRESET_M0) set_m0(dma_args(S::STAGES - 1, 0).lds);
-      if (!S::PROLOGUE_ALL && S::STAGES - 1 < KTu) {
-#pragma unroll
-        for (int pos = 0; pos < kAfter; ++pos) dma_slot(S::STAGES - 1, pos);
-      }
-
-      using yes = std::true_type;
-      using no = std::false_type;
-      int kt = 0;
-      for (; kt + S::STAGES < KTu; ++kt) ktile(kt, yes{}, yes{}, yes{});  // steady state
-      if (kt + S::STAGES == KTu && kt + 1 < KTu) {                       // last refill
-        ktile(kt, yes{}, no{}, yes{});
-        ++kt;
-      }
-      for (; kt + 1 < KTu; ++kt) ktile(kt, no{}, no{}, yes{});  // the ring drains
-      ktile(kt, no{}, no{}, no{});                             // last K tile
+      // The pipelined loop: the ring walker of ring.hpp, in a fixed
+      // instruction order (fence() is a sched_barrier).  Every READ_STRIDE-th
+      // MFMA slot of a non-final K step carries one operand read for the next
+      // step, spread out so that the four waves' reads do not outrun the LDS.
+      // The refill's loads go out one every DMA_STRIDE MFMA slots: bunched
+      // together, the four waves' loads saturate the texture path and stall
+      // MFMA issue, while spread too thin the last load lands too close to
+      // the barrier that needs it.  The previous output tile's D stores may
+      // still be in flight when the ring starts: they are older than every
+      // ring load, so they can only make the ring's vmcnt waits more
+      // conservative.
+      auto load_one = [&](int tile, int d) { issue_loads(tile, d, d + 1); };
+      KernelRingOps<S, decltype(mfma), decltype(read_frag), decltype(load_one)> ops{mfma, read_frag, load_one};
+      ring_k_loop<S>(ops, KTu);
     }
 
     // ---- epilogue: fp32 -> fp16 (nearest even), staged through LDS -------
@@ -726,10 +539,11 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
         if (m < M) {
           _Float16 *dst = D + static_cast<int64_t>(m) * N + n;
           if (vec16 && n + 8 <= N) {
-            if constexpr (S::NT_STORE)
-              __builtin_nontemporal_store(v, reinterpret_cast<half8_t *>(dst));
-            else
-              *reinterpret_cast<half8_t *>(dst) = v;
+            // Non-temporal (streamed to memory, not kept in the caches): with
+            // several tiles per CU, cached D lines would evict the A and B
+            // panels the next tiles read (2 % faster at 8192^3, about 1.5 % at
+            // 4096^3).  A kernel that reads D next finds it in memory.
+            __builtin_nontemporal_store(v, reinterpret_cast<half8_t *>(dst));
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -750,58 +564,30 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
 // grouped scheduler.  The 16x16x32 shape moves half the accumulator bytes
 // per flop of 32x32x16 and runs at a measurably higher sustained clock under
 // the power limit.  The others exist for ablation measurements.
-using GemmDefault = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1>;
-using GemmNoSwizzle = GemmShape<256, 256, 64, 2, 2, 2, false, true, 4, 1, 1, 1, 0, 16, 2, 1>;
-using GemmNonPersistent = GemmShape<256, 256, 64, 2, 2, 2, true, false, 4, 1, 1, 1, 0, 16, 2, 1>;
-using GemmReadEverySlot = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 1, 0>;
-using GemmReadEvery4 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 4, 2>;
-using GemmRefillEvery5 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 5, 1, 1, 1, 0, 16, 2, 1>;
-using GemmRefillEvery6 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 6, 1, 1, 1, 0, 16, 2, 1>;
-using GemmKStagger = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 8, 1, 0, 16, 2, 1>;
-using GemmLoadsSc0 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 1, 16, 2, 1>;
-// 32x32x16 MFMA blocks (64 slots per K tile), one operand read per slot, a
-// refill load every 2 slots; the same with a single LDS stage (the
-// hand-written 16x16x32 MFMAs are kept to the pipelined loop, whose
-// accumulators stay in place), and with K tiles of 32 in a 4-stage ring.
-using GemmFusedLoads = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, true>;
-using Gemm32x32 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1>;
+using GemmDefault = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1>;
 // The default shape with bf16 operands and results.
-using GemmBf16 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, kBF16>;
-using Gemm32x32OneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true, 1, 1>;
-// Eight waves (2 x 4 of 128x64, two per SIMD): each wave issues half the
-// refill loads, and its SIMD partner can issue MFMAs meanwhile; the price is
-// 1.5x the LDS operand reads per flop.
-using Gemm8Waves = GemmShape<256, 256, 64, 2, 2, 4, true, true, 4, 1, 1, 1, 0, 16, 2, 1>;
-using Gemm8WavesRefill2 = GemmShape<256, 256, 64, 2, 2, 4, true, true, 2, 1, 1, 1, 0, 16, 2, 1>;
-// The default with M0 set one load ahead, and the same with a refill load
-// every 2 or every 3 slots.
-using GemmPresetM0 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, kF16, true>;
-using GemmPresetM0Refill2 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2, 1, 1, 1, 0, 16, 2, 1, false, kF16, true>;
-using GemmPresetM0Refill3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 1, 1, 1, 0, 16, 2, 1, false, kF16, true>;
-// The default with a refill load every 3 MFMA slots, so the last one lands
-// further ahead of the barrier that waits for all of them.  (Every 1 or 2
-// slots, the compiler leaves the accumulators too few AGPRs and moves them
-// through scratch around each hand-written MFMA; build.py rejects that.)
-using GemmRefillEvery3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 1, 1, 1, 0, 16, 2, 1>;
-// The default with both ring stages requested at the start of each output
-// tile, so K tile 1 is in flight while K tile 0 arrives.
-using GemmPrologueAll = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, kF16, false, true>;
-using Gemm32x32Bk32FourStage = GemmShape<256, 256, 32, 4, 2, 2, true, true, 4, 1>;
+using GemmBf16 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1, kBF16>;
+// Ablations, each the default with one design choice taken back: no LDS
+// swizzle; one workgroup per output tile in launch order (no persistent
+// grouped, XCD-aware schedule); 32x32x16 MFMA blocks through the compiler's
+// builtin (64 slots per K tile, one operand read per slot, a refill load
+// every 2 slots); and the same with a single LDS stage (load, wait, compute).
+using GemmNoSwizzle = GemmShape<256, 256, 64, 2, 2, 2, false, true, 4, 16, 2, 1>;
+using GemmNonPersistent = GemmShape<256, 256, 64, 2, 2, 2, true, false, 4, 16, 2, 1>;
+using Gemm32x32 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2>;
+using Gemm32x32OneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true, 1>;
 // Smaller output tiles, for outputs whose 256x256 tiles would leave CUs
 // idle (gemm_default_tile picks): the default's schedule on 256x128, 128x256
 // and 128x128 tiles (4 waves of 128x64, 64x128 and 64x64; 12, 12 and 8 loads
 // per wave per K tile), with the deeper rings of kGemmTileShapes.  A K tile
 // of these is 1/2 or 1/4 of the 256x256 one in MFMA time, so two stages no
 // longer cover a load's latency.
-// The default with D written by ordinary (cached) stores.
-using GemmCachedStore =
-    GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, kF16, false, false, false>;
 template <int DT, int STAGES = 2>
-using GemmTile256x128 = GemmShape<256, 128, 64, STAGES, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, DT>;
+using GemmTile256x128 = GemmShape<256, 128, 64, STAGES, 2, 2, true, true, 4, 16, 2, 1, DT>;
 template <int DT, int STAGES = 2>
-using GemmTile128x256 = GemmShape<128, 256, 64, STAGES, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, DT>;
+using GemmTile128x256 = GemmShape<128, 256, 64, STAGES, 2, 2, true, true, 4, 16, 2, 1, DT>;
 template <int DT, int STAGES = 2>
-using GemmTile128x128 = GemmShape<128, 128, 64, STAGES, 2, 2, true, true, 4, 1, 1, 1, 0, 16, 2, 1, false, DT>;
+using GemmTile128x128 = GemmShape<128, 128, 64, STAGES, 2, 2, true, true, 4, 16, 2, 1, DT>;
 
 static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDefault::BK == kGemmBK &&
                   GemmDefault::STAGES == kGemmStages && GemmDefault::kThreads == kGemmThreads,
@@ -869,27 +655,14 @@ __global__ void fill_bias_kernel(_Float16 *__restrict__ D, const uint16_t *__res
 
 hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                            hipStream_t stream) {
+  // Numbers of ablations measured and not kept are not reused.
   switch (variant) {
     case 0: return launch_default<kF16>(A, B, D, M, N, K, num_cus, stream);
     case 1: return launch<GemmNoSwizzle>(A, B, D, M, N, K, num_cus, stream);
     case 2: return launch<Gemm32x32OneStage>(A, B, D, M, N, K, num_cus, stream);
     case 3: return launch<GemmNonPersistent>(A, B, D, M, N, K, num_cus, stream);
-    case 4: return launch<GemmReadEverySlot>(A, B, D, M, N, K, num_cus, stream);
-    case 5: return launch<GemmReadEvery4>(A, B, D, M, N, K, num_cus, stream);
-    case 6: return launch<GemmRefillEvery5>(A, B, D, M, N, K, num_cus, stream);
-    case 7: return launch<GemmRefillEvery6>(A, B, D, M, N, K, num_cus, stream);
-    case 8: return launch<GemmKStagger>(A, B, D, M, N, K, num_cus, stream);
-    case 9: return launch<GemmLoadsSc0>(A, B, D, M, N, K, num_cus, stream);
     case 10: return launch<Gemm32x32>(A, B, D, M, N, K, num_cus, stream);
-    case 11: return launch<Gemm32x32Bk32FourStage>(A, B, D, M, N, K, num_cus, stream);
-    case 12: return launch<GemmFusedLoads>(A, B, D, M, N, K, num_cus, stream);
-    case 13: return launch<Gemm8Waves>(A, B, D, M, N, K, num_cus, stream);
-    case 14: return launch<Gemm8WavesRefill2>(A, B, D, M, N, K, num_cus, stream);
-    case 15: return launch<GemmPresetM0>(A, B, D, M, N, K, num_cus, stream);
-    case 16: return launch<GemmPresetM0Refill2>(A, B, D, M, N, K, num_cus, stream);
-    case 17: return launch<GemmPresetM0Refill3>(A, B, D, M, N, K, num_cus, stream);
-    case 18: return launch<GemmRefillEvery3>(A, B, D, M, N, K, num_cus, stream);
-    case 19: return launch<GemmPrologueAll>(A, B, D, M, N, K, num_cus, stream);
+    // Forced output tiles and ring depths (the default picks among them).
     case 20: return launch<GemmDefault>(A, B, D, M, N, K, num_cus, stream);
     case 21: return launch<GemmTile256x128<kF16, 3>>(A, B, D, M, N, K, num_cus, stream);
     case 22: return launch<GemmTile128x256<kF16, 3>>(A, B, D, M, N, K, num_cus, stream);
@@ -898,7 +671,6 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 25: return launch<GemmTile128x256<kF16, 2>>(A, B, D, M, N, K, num_cus, stream);
     case 26: return launch<GemmTile128x128<kF16, 2>>(A, B, D, M, N, K, num_cus, stream);
     case 27: return launch<GemmTile128x128<kF16, 5>>(A, B, D, M, N, K, num_cus, stream);
-    case 28: return launch<GemmCachedStore>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1000,6 +772,64 @@ hipError_t launch_gemm_splitk(int dtype, const void *A, const void *B, void *D, 
                            : launch_default<kF16, kEpiPartial>(A, B, D, M, N, K, num_cus, stream, nullptr, 0, w, splits);
   if (e != hipSuccess) return e;
   return launch_splitk_reduce(dtype, w, D, static_cast<int64_t>(M) * N, splits, stream);
+}
+
+// ---- the ring schedule on the host -------------------------------------
+// The walker gemm_kernel runs (ring.hpp), run on the host with an Ops object
+// that records each event instead of issuing it.
+namespace {
+struct RingRecorder {
+  int stages;
+  int32_t *ev;
+  int64_t cap;
+  int64_t n = 0;
+  void push(int32_t code, int32_t a = 0, int32_t b = 0, int32_t c = 0, int32_t d = 0) {
+    if (ev != nullptr && n < cap) {
+      int32_t *e = ev + 5 * n;
+      e[0] = code;
+      e[1] = a;
+      e[2] = b;
+      e[3] = c;
+      e[4] = d;
+    }
+    ++n;
+  }
+  void mfma(int buf, int idx) { push(kRingMfma, buf, idx); }
+  void read(int buf, int kt, int ks, int r) { push(kRingRead, kt, ks, r, ring_stage(kt, stages)); }
+  void load(int tile, int d) { push(kRingLoad, tile, d, ring_stage(tile, stages)); }
+  void wait_tile(int vmcnt) { push(kRingWaitTile, vmcnt); }
+  void wait_lds() { push(kRingWaitLds); }
+  void barrier() { push(kRingBarrier); }
+  void fence() {}
+};
+
+template <class S>
+int64_t record_ring(int ktu, int32_t *events, int64_t cap) {
+  RingRecorder rec{S::STAGES, events, cap};
+  ring_k_loop<S>(rec, ktu);
+  return rec.n;
+}
+}  // namespace
+
+int64_t ring_trace(int bm, int bn, int stages, int ktu, int32_t *events, int64_t cap, int *loads_per_tile,
+                   int *reads_per_step, int *ksteps, int *mfma_per_step) {
+  auto info = [&](auto shape) {
+    using S = decltype(shape);
+    if (loads_per_tile) *loads_per_tile = S::kDmaPerStage;
+    if (reads_per_step) *reads_per_step = S::kReads;
+    if (ksteps) *ksteps = S::kKSub;
+    if (mfma_per_step) *mfma_per_step = S::kMfma;
+    return record_ring<S>(ktu, events, cap);
+  };
+  if (bm == 256 && bn == 256 && stages == 2) return info(GemmDefault{});
+  if (bm == 256 && bn == 128 && stages == 2) return info(GemmTile256x128<kF16, 2>{});
+  if (bm == 256 && bn == 128 && stages == 3) return info(GemmTile256x128<kF16, 3>{});
+  if (bm == 128 && bn == 256 && stages == 2) return info(GemmTile128x256<kF16, 2>{});
+  if (bm == 128 && bn == 256 && stages == 3) return info(GemmTile128x256<kF16, 3>{});
+  if (bm == 128 && bn == 128 && stages == 2) return info(GemmTile128x128<kF16, 2>{});
+  if (bm == 128 && bn == 128 && stages == 4) return info(GemmTile128x128<kF16, 4>{});
+  if (bm == 128 && bn == 128 && stages == 5) return info(GemmTile128x128<kF16, 5>{});
+  return -1;
 }
 
 }  // namespace gt

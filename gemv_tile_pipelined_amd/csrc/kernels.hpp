@@ -20,7 +20,11 @@ constexpr int kGemmBK = 64;
 constexpr int kGemmStages = 2;
 constexpr int kGemmThreads = 256;
 constexpr int kGemmGroupM = 8;
-constexpr int kGemmVariants = 29;
+// gemvtile_gemm_f16_variant numbers of the tiled kernel: 0 (the default)
+// and the ablations of gemm.hip.  Numbers of ablations that were measured and
+// not kept stay unused.
+constexpr int kGemmVariants = 28;
+inline bool gemm_variant_exists(int v) { return (v >= 0 && v <= 3) || v == 10 || (v >= 20 && v <= 27); }
 
 // Output tile of the tiled GEMM.  The 256x256 default needs about one tile
 // per CU to fill the chip; outputs that give fewer take smaller tiles, each
@@ -89,9 +93,10 @@ inline int gemm_splitk_splits(int64_t M, int64_t N, int64_t K, int num_cus) {
                                             static_cast<double>(kSplitKOutputsPerTile);
   return saved >= cost ? static_cast<int>(splits) : 1;
 }
-constexpr int kGemvVariants = 18;
+// gemvtile_gemv_f16_variant numbers of the GEMV kernel's launch shapes.
+inline bool gemv_variant_exists(int v) { return v == 0 || (v >= 6 && v <= 12); }
 // GEMMs with at most this many rows on one side (M or N) take the skinny
-// kernel (skinny.hip); it has kSkinnyVariants launch shapes.
+// kernel (skinny.hip).
 constexpr int kSkinnyMaxRows = 16;
 // gemm_f16 / gemm_bf16 also send shapes whose smaller side has 17..64 rows
 // to the skinny kernel (two or four 16-row blocks of the small operand per
@@ -111,28 +116,17 @@ inline bool skinny_wide_route(int64_t M, int64_t N, int num_cus) {
   if (S <= kSkinnyMaxRows || S > kSkinnyWideRows) return false;
   return (R + 127) / 128 * (S > 32 ? 4 : 2) <= num_cus;
 }
-constexpr int kSkinnyVariants = 40;
-// gemvtile_gemm_f16_variant numbers each kernel family from a fixed base so
-// that adding a launch shape to one family renumbers no other: tiled GEMM
-// 0.., skinny kSkinnyVariantBase.. (its kSkinnyVariants shapes, then the
-// kSkinnyWpVariants further ones), wave-specialised kGemmWsVariantBase...
+// gemvtile_gemm_f16_variant numbers each kernel family from a fixed base:
+// tiled GEMM 0.., skinny kSkinnyVariantBase + (0, 4, 12, 30, 47),
+// wave-specialised kGemmWsVariantBase...  Numbers of launch shapes measured
+// and not kept stay unused.
 constexpr int kSkinnyVariantBase = 100;
 constexpr int kGemmWsVariantBase = 200;
-// Wave-specialised (producer / consumer) GEMM launch shapes (gemm_ws.hip),
-// numbered after the skinny ones.
+inline bool skinny_variant_exists(int v) { return v == 0 || v == 4 || v == 12 || v == 30 || v == 47; }
+// Wave-specialised (producer / consumer) GEMM launch shapes (gemm_ws.hip).
 constexpr int kGemmWsVariants = 2;
-// Wave-private skinny launch shapes (skinny.hip), numbered after those;
-// skinny_wp_variant_q8: the ones that stage 8 small-side rows (min(M,N) <= 8).
-constexpr int kSkinnyWpVariants = 12;
-constexpr int kSkinnyExtraBase = kSkinnyVariantBase + kSkinnyVariants;
-static_assert(kGemmVariants <= kSkinnyVariantBase && kSkinnyExtraBase + kSkinnyWpVariants <= kGemmWsVariantBase,
+static_assert(kGemmVariants <= kSkinnyVariantBase && kSkinnyVariantBase + 48 <= kGemmWsVariantBase,
               "variant families must not overlap");
-inline bool skinny_wp_variant_q8(int v) { return (v >= 4 && v <= 6) || v == 9 || v == 10; }
-// Skinny launch shapes that stage only 8 rows of the small side (valid for
-// min(M,N) <= 8 only).
-inline bool skinny_variant_q8(int v) {
-  return (v >= 9 && v <= 11) || (v >= 19 && v <= 23) || (v >= 26 && v <= 29) || (v >= 35 && v <= 39);
-}
 
 // The default GEMV launch for N rows on a device with num_cus compute units:
 // 8 waves per workgroup, each wave on `rows_per_wave` rows and one of `ksplit`
@@ -200,14 +194,21 @@ inline int skinny_splitk_splits(int64_t R, int64_t K, int num_cus) {
 // Issued through the builtin so the compiler knows the LDS reads are done.
 constexpr unsigned kWaitLgkm0 = 0xC07F;
 
+// The K-loop schedule of the tiled GEMM kernel with a bm x bn output tile and
+// a ring of `stages` stages over ktu K tiles, as the host-side trace of the
+// ring walker (ring.hpp): up to `cap` events of five int32 each are written
+// to `events` (which may be NULL); returns the number of events, or -1 when
+// the library has no kernel of that shape.  The other outputs (each may be
+// NULL) receive the kernel's loads per wave per K tile, operand reads and
+// MFMAs per wave per K step, and K steps per K tile.
+int64_t ring_trace(int bm, int bn, int stages, int ktu, int32_t *events, int64_t cap, int *loads_per_tile,
+                   int *reads_per_step, int *ksteps, int *mfma_per_step);
 hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                            hipStream_t stream);
 hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K,
                                   int num_cus, hipStream_t stream);
 hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, int num_cus,
                            hipStream_t stream);
-hipError_t launch_gemm_skinny_wp_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K,
-                                     hipStream_t stream);
 hipError_t launch_gemm_ws_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                               hipStream_t stream);
 hipError_t launch_fill_zero_f16(void *p, int64_t count, hipStream_t stream);

@@ -271,139 +271,6 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   }
 }
 
-// Wave-private variant: no workgroup barrier in the main loop.  Each wave
-// walks its own contiguous run of K tiles (TK = 64, so every LDS row is one
-// 128-byte line) through its own STAGES-deep LDS ring, holding the PR rows
-// of P and QROWS rows of Q of one K tile per slot, and waits only for its
-// own loads (vmcnt), like the GEMV's waves; a slow load then stalls one wave
-// rather than the whole workgroup.  The K runs meet once, at the end, in the
-// LDS reduction of the wave partials (wave order, deterministic).  Slot rows
-// use the tiled GEMM's 128-byte-row swizzle (chunk c of row r at c ^ s(r),
-// s(r) = (r % 8) ^ ((r / 8) % 2), taken per operand row) and its K-chunk
-// order 0, 2, 1, 3, which keep the 16-row fragment reads bank-conflict free.
-// With ROT, each workgroup starts its waves' runs at a different tile of the
-// run (and wraps), so workgroups side by side read different parts of Q.
-template <int WAVES, int STAGES, int PR, int QROWS, bool TRANS, int DT, bool ROT, bool NTP = false>
-__global__ void __launch_bounds__(WAVES * 64)
-gemm_skinny_wp_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ Q, _Float16 *__restrict__ D,
-                      int R, int S, int K) {
-  constexpr int TK = 64;
-  constexpr int kRowBytes = TK * 2;                 // 128: one whole line
-  constexpr int kRowsPerDma = 64 * 16 / kRowBytes;  // 8 rows per wave load
-  constexpr int kDmaP = PR / kRowsPerDma;
-  constexpr int kDma = kDmaP + QROWS / kRowsPerDma;  // loads per slot
-  constexpr int kSlotBytes = (PR + QROWS) * kRowBytes;
-  constexpr int kWaveRing = STAGES * kSlotBytes;
-  static_assert(PR == 8 || PR == 16, "P rows per workgroup");
-  static_assert(QROWS == 8 || QROWS == 16, "Q rows staged");
-  static_assert(STAGES >= 2 && (STAGES - 1) * kDma <= 63, "vmcnt range");
-  static_assert(WAVES * kWaveRing + WAVES * 16 * 17 * 4 <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
-  __shared__ __attribute__((aligned(1024))) char ring[WAVES * kWaveRing];
-  __shared__ float partial[WAVES][16][17];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r0 = blockIdx.x * PR;
-  const int prows = min(PR, R - r0);
-  const int4_t rsrc_p = make_buffer_rsrc(P + static_cast<int64_t>(r0) * K, static_cast<uint32_t>(prows) * K * 2u);
-  const int4_t rsrc_q = make_buffer_rsrc(Q, static_cast<uint32_t>(S) * K * 2u);
-  auto swz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
-
-  // This wave's K tiles [t_begin, t_begin + nt); its j-th load of them is
-  // tile t_begin + (j + rot) % nt, into slot j % STAGES.
-  const int KT = (K + TK - 1) / TK;
-  const int t_begin = static_cast<int>(static_cast<int64_t>(KT) * wave / WAVES);
-  const int nt = static_cast<int>(static_cast<int64_t>(KT) * (wave + 1) / WAVES) - t_begin;
-  const int rot = (ROT && nt > 0) ? static_cast<int>(blockIdx.x % static_cast<unsigned>(nt)) : 0;
-  const uint32_t my_ring = lds_addr(ring) + static_cast<uint32_t>(wave * kWaveRing);
-  const int lrow = lane / 8;  // row of a load's 8-row block this lane fills
-  auto issue = [&](int j) {
-    int tt = j + rot;
-    if (tt >= nt) tt -= nt;
-    const int k0 = (t_begin + tt) * TK;
-    const uint32_t slot = my_ring + static_cast<uint32_t>((j % STAGES) * kSlotBytes);
-#pragma unroll
-    for (int d = 0; d < kDma; ++d) {
-      const bool isp = d < kDmaP;
-      const int row = (isp ? d : d - kDmaP) * kRowsPerDma + lrow;  // row within its operand
-      const int k = k0 + (((lane & 7) ^ swz(row)) << 3);           // first K element this lane fetches
-      const uint32_t off = k < K ? static_cast<uint32_t>(row) * K * 2u + static_cast<uint32_t>(k) * 2u : kOobOffset;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(slot + static_cast<uint32_t>(d * kRowsPerDma * kRowBytes));
-      if (NTP && isp)
-        lds_dma_b128<2>(rsrc_p, off, dst);  // rows of P, read once: non-temporal
-      else
-        lds_dma_b128(isp ? rsrc_p : rsrc_q, off, dst);
-    }
-  };
-
-  const int frow = lane & 15;
-  const int kgrp = lane >> 4;
-  const int kchunk = ((kgrp & 1) << 1) | (kgrp >> 1);
-  const int prow = frow % PR;
-  const int qrow = frow % QROWS;
-  const uint32_t p_off = static_cast<uint32_t>(prow * kRowBytes);
-  const uint32_t q_off = static_cast<uint32_t>((PR + qrow) * kRowBytes);
-  const int pswz = swz(prow);
-  const int qswz = swz(qrow);
-  const char *my_ring_ptr = ring + wave * kWaveRing;
-
-#pragma unroll
-  for (int j = 0; j < STAGES - 1; ++j)
-    if (j < nt) issue(j);
-  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < nt; ++j) {
-    // Tile j has landed once at most the younger tiles' loads are pending.
-    wait_younger<kDma, STAGES - 2>(min(nt, j + STAGES - 1) - (j + 1));
-    // Slot (j-1) % STAGES was last read in iteration j-1, whose reads have
-    // completed (lgkmcnt below): refill it with tile j + STAGES - 1.
-    if (j + STAGES - 1 < nt) issue(j + STAGES - 1);
-    const char *slot = my_ring_ptr + (j % STAGES) * kSlotBytes;
-#pragma unroll
-    for (int ks = 0; ks < TK / 32; ++ks) {
-      const int c = ks * 4 + kchunk;
-      const half8_t pf = *reinterpret_cast<const half8_t *>(slot + p_off + ((c ^ pswz) << 4));
-      const half8_t qf = *reinterpret_cast<const half8_t *>(slot + q_off + ((c ^ qswz) << 4));
-      if constexpr (DT == kF16)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, qf, acc, 0, 0, 0);
-      else
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pf), __builtin_bit_cast(bf16x8_t, qf),
-                                                      acc, 0, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  }
-
-#pragma unroll
-  for (int e = 0; e < 4; ++e) partial[wave][frow][4 * kgrp + e] = acc[e];
-  __syncthreads();
-  for (int i = threadIdx.x; i < 256; i += WAVES * 64) {
-    const int s2 = i >> 4;
-    const int r = i & 15;
-    float sum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) sum += partial[w][s2][r];
-    if (s2 < S && r < PR && r0 + r < R) {
-      const int64_t idx = TRANS ? static_cast<int64_t>(r0 + r) * S + s2 : static_cast<int64_t>(s2) * R + r0 + r;
-      D[idx] = round_out<DT>(sum);
-    }
-  }
-}
-
-template <int WAVES, int STAGES, int PR, int QROWS, int DT, bool ROT, bool NTP = false>
-static hipError_t launch_wp(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
-                            hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((R + PR - 1) / PR));
-  const auto *p = static_cast<const _Float16 *>(P);
-  const auto *q = static_cast<const _Float16 *>(Q);
-  auto *d = static_cast<_Float16 *>(D);
-  if (trans)
-    hipLaunchKernelGGL((gemm_skinny_wp_kernel<WAVES, STAGES, PR, QROWS, true, DT, ROT, NTP>), grid, dim3(WAVES * 64),
-                       0, stream, p, q, d, R, S, K);
-  else
-    hipLaunchKernelGGL((gemm_skinny_wp_kernel<WAVES, STAGES, PR, QROWS, false, DT, ROT, NTP>), grid,
-                       dim3(WAVES * 64), 0, stream, p, q, d, R, S, K);
-  return hipGetLastError();
-}
-
 template <int WAVES, int STAGES, int QROWS, int DT = kF16, int PR = 16, bool KROT = false, bool NTP = false>
 static hipError_t launch_lds(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                              hipStream_t stream) {
@@ -546,82 +413,16 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
   const void *Q = small_m ? A : B;
   const int R = small_m ? N : M;
   const int S = small_m ? M : N;
+  // Numbers of launch shapes measured and not kept are not reused.
   switch (variant) {
-    // LDS-staged: <waves per workgroup, ring stages, Q rows staged>; 0 is the default
     case 0: return launch_lds_auto<kF16>(P, Q, D, R, S, K, !small_m, num_cus, stream);
-    case 1: return launch_lds<8, 4, 16>(P, Q, D, R, S, K, !small_m, stream);
-    case 2: return launch_lds<8, 3, 16>(P, Q, D, R, S, K, !small_m, stream);
-    case 3: return launch_lds<4, 4, 16>(P, Q, D, R, S, K, !small_m, stream);
     // operands loaded into registers: <waves per workgroup, K steps in flight per wave>
     case 4: return launch<8, 4>(P, Q, D, R, S, K, !small_m, stream);
-    case 5: return launch<8, 2>(P, Q, D, R, S, K, !small_m, stream);
-    case 6: return launch<8, 8>(P, Q, D, R, S, K, !small_m, stream);
-    case 7: return launch<16, 4>(P, Q, D, R, S, K, !small_m, stream);
-    case 8: return launch<4, 8>(P, Q, D, R, S, K, !small_m, stream);
-    // Q tile of 8 rows (S <= 8 only): deeper rings
-    case 9: return S <= 8 ? launch_lds<8, 5, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 10: return S <= 8 ? launch_lds<8, 6, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 11: return S <= 8 ? launch_lds<4, 6, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    // fewer P rows per workgroup: <waves, stages, Q rows, type, P rows>
+    // LDS ring, 16 P rows per workgroup: <waves, stages, Q rows, type, P rows, rotated K start>
     case 12: return launch_lds<16, 4, 16, kF16, 16>(P, Q, D, R, S, K, !small_m, stream);
-    case 13: return launch_lds<8, 4, 16, kF16, 8>(P, Q, D, R, S, K, !small_m, stream);
-    case 14: return launch_lds<4, 4, 16, kF16, 4>(P, Q, D, R, S, K, !small_m, stream);
-    case 15: return launch_lds<8, 4, 16, kF16, 4>(P, Q, D, R, S, K, !small_m, stream);
-    case 16: return launch_lds<4, 4, 16, kF16, 2>(P, Q, D, R, S, K, !small_m, stream);
-    case 17: return launch_lds<4, 4, 16, kF16, 1>(P, Q, D, R, S, K, !small_m, stream);
-    case 18: return launch_lds<1, 4, 16, kF16, 1>(P, Q, D, R, S, K, !small_m, stream);
-    case 19: return S <= 8 ? launch_lds<8, 4, 8, kF16, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 20: return S <= 8 ? launch_lds<4, 4, 8, kF16, 4>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 21: return S <= 8 ? launch_lds<4, 4, 8, kF16, 2>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 22: return S <= 8 ? launch_lds<4, 4, 8, kF16, 1>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 23: return S <= 8 ? launch_lds<8, 4, 8, kF16, 1>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    // deeper rings for the smaller per-workgroup tiles: <waves, stages, Q rows, type, P rows>
-    case 24: return launch_lds<8, 6, 16, kF16, 8>(P, Q, D, R, S, K, !small_m, stream);
-    case 25: return launch_lds<4, 7, 16, kF16, 4>(P, Q, D, R, S, K, !small_m, stream);
-    case 26: return S <= 8 ? launch_lds<8, 8, 8, kF16, 8>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 27: return S <= 8 ? launch_lds<4, 8, 8, kF16, 4>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 28: return S <= 8 ? launch_lds<4, 12, 8, kF16, 4>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 29: return S <= 8 ? launch_lds<4, 12, 8, kF16, 2>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    // rotated K start per workgroup: <waves, stages, Q rows, type, P rows, rotate>
     case 30: return launch_lds<16, 4, 16, kF16, 16, true>(P, Q, D, R, S, K, !small_m, stream);
-    case 31: return launch_lds<8, 4, 16, kF16, 8, true>(P, Q, D, R, S, K, !small_m, stream);
-    case 32: return launch_lds<4, 4, 16, kF16, 4, true>(P, Q, D, R, S, K, !small_m, stream);
-    case 33: return launch_lds<4, 4, 16, kF16, 2, true>(P, Q, D, R, S, K, !small_m, stream);
-    case 34: return launch_lds<4, 4, 16, kF16, 1, true>(P, Q, D, R, S, K, !small_m, stream);
-    case 35: return S <= 8 ? launch_lds<8, 4, 8, kF16, 8, true>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 36: return S <= 8 ? launch_lds<4, 4, 8, kF16, 4, true>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 37: return S <= 8 ? launch_lds<4, 4, 8, kF16, 2, true>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 38: return S <= 8 ? launch_lds<4, 4, 8, kF16, 1, true>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    case 39: return S <= 8 ? launch_lds<8, 6, 8, kF16, 16, true>(P, Q, D, R, S, K, !small_m, stream) : hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_gemm_skinny_wp_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K,
-                                     hipStream_t stream) {
-  const bool small_m = M <= kSkinnyMaxRows;
-  if (!small_m && N > kSkinnyMaxRows) return hipErrorInvalidValue;
-  const void *P = small_m ? B : A;
-  const void *Q = small_m ? A : B;
-  const int R = small_m ? N : M;
-  const int S = small_m ? M : N;
-  const bool t = !small_m;
-  // <waves, ring stages, P rows per workgroup, Q rows staged, type, rotated K runs>
-  switch (variant) {
-    case 0: return launch_wp<8, 4, 16, 16, kF16, true>(P, Q, D, R, S, K, t, stream);
-    case 1: return launch_wp<8, 4, 16, 16, kF16, false>(P, Q, D, R, S, K, t, stream);
-    case 2: return launch_wp<4, 8, 16, 16, kF16, true>(P, Q, D, R, S, K, t, stream);
-    case 3: return launch_wp<8, 4, 8, 16, kF16, true>(P, Q, D, R, S, K, t, stream);
-    case 4: return S <= 8 ? launch_wp<8, 6, 16, 8, kF16, true>(P, Q, D, R, S, K, t, stream) : hipErrorInvalidValue;
-    case 5: return S <= 8 ? launch_wp<8, 8, 8, 8, kF16, true>(P, Q, D, R, S, K, t, stream) : hipErrorInvalidValue;
-    case 6: return S <= 8 ? launch_wp<16, 2, 16, 8, kF16, true>(P, Q, D, R, S, K, t, stream) : hipErrorInvalidValue;
-    // non-temporal loads of P: the workgroup-ring kernel
-    // <waves, stages, Q rows, type, P rows, rotated, nt> and the wave-private one
-    case 7: return launch_lds<16, 4, 16, kF16, 16, true, true>(P, Q, D, R, S, K, t, stream);
-    case 8: return launch_wp<8, 4, 16, 16, kF16, true, true>(P, Q, D, R, S, K, t, stream);
-    case 9: return S <= 8 ? launch_lds<8, 4, 8, kF16, 8, false, true>(P, Q, D, R, S, K, t, stream) : hipErrorInvalidValue;
-    case 10: return S <= 8 ? launch_lds<4, 4, 8, kF16, 4, false, true>(P, Q, D, R, S, K, t, stream) : hipErrorInvalidValue;
-    case 11: return launch_lds<8, 4, 16, kF16, 8, false, true>(P, Q, D, R, S, K, t, stream);
+    // as 30 with non-temporal loads of P (the default at 16 P rows)
+    case 47: return launch_lds<16, 4, 16, kF16, 16, true, true>(P, Q, D, R, S, K, !small_m, stream);
     default: return hipErrorInvalidValue;
   }
 }

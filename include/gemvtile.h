@@ -267,18 +267,6 @@ int gemvtile_gemm_tile(int64_t M, int64_t N, int64_t num_cus, int *bm, int *bn, 
 int gemvtile_device_caps(int *num_cus, int *clock_khz, int *mem_clock_khz, int *mem_bus_bits);
 
 /*
- * gemvtile_read_stream -- measurement only: a read-only kernel that streams
- * `bytes` (1 .. 2^30) of device memory at p with 16-byte buffer loads
- * (grid-stride, `blocks` workgroups of 512 threads, 1 .. 4096) and the cache
- * policy `policy` (0 none, 1 nt, 2 sc1 nt, 3 sc0 nt).  It computes nothing
- * and writes at most one word per workgroup into `sink` (device memory of at
- * least `blocks` words), only under an impossible condition.  It gives the
- * practical HBM read ceiling that the GEMV's roofline fraction is read
- * against.  Returns GEMVTILE_ERR_INVALID_ARG for arguments out of range.
- */
-int gemvtile_read_stream(const void *p, int64_t bytes, int policy, int blocks, void *sink, void *stream);
-
-/*
  * gemvtile_gemv_grid -- the number of workgroups gemv_f16 (and gemv_bf16)
  * launches for N rows on a device with `num_cus` compute units: ceil(N/R)
  * with R = 16 rows per workgroup when N >= 16*num_cus, else 8, 4 or 2 rows
@@ -304,108 +292,98 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
 
 /*
  * gemvtile_gemm_f16_variant -- gemm_f16 with an internal kernel variant, for
- * ablation measurements only (same contract and results as gemm_f16).  The
- * tiled ones 1..20 and 28 use 256x256 output tiles and (but for 13, 14) 4 waves of
- * 128x128:
+ * ablation measurements only (same contract and results as gemm_f16).
  *   0  what gemm_f16 runs: on tiled shapes the tile of gemvtile_gemm_tile;
- *      with 256x256 tiles, 16x16x32 MFMA blocks, K tiles of 64 in a 2-stage
- *      LDS ring, the next K step's operand reads one every 2 MFMA slots, a
- *      refill load every 4 slots, swizzled LDS, persistent
- *   1  as 0 without the LDS swizzle
+ *      with 256x256 tiles, 4 waves of 128x128, 16x16x32 MFMA blocks, K tiles
+ *      of 64 in a 2-stage LDS ring, the next K step's operand reads one every
+ *      2 MFMA slots, a refill load every 4 slots, swizzled LDS, persistent
+ *      grouped XCD-aware schedule
+ *   1  as 20 without the LDS swizzle
  *   2  as 10 with single-stage LDS (load, wait, compute: no overlap)
- *   3  as 0 with one workgroup per tile (no persistent loop, no XCD remap)
- *   4  as 0 with one operand read per MFMA slot   5  ... every 4 slots
- *   6  as 0 with a refill load every 5 MFMA slots   7  ... every 6 slots
- *   8  as 0 with output tile t starting its K loop at K tile t % 8
- *   9  as 0 with the tile loads' cache-policy modifier sc0
- *   10 32x32x16 MFMA blocks, one operand read per slot, a refill load every
- *      2 of its 64 slots per K tile
- *   11 as 10 with K tiles of 32 in a 4-stage ring
- *   12 as 0 with each tile load issued in one block with its slot's MFMA
- *      (M0 written before the MFMA, which serves as the wait state) rather
- *      than on its own (M0 write, wait state, load)
- *   13 as 0 with 8 waves of 128x64 (2 x 4, two per SIMD, each issuing half
- *      the refill loads)   14  as 13 with a refill load every 2 slots
- *   15 as 0 with M0 (the LDS address of a tile load) written for the next
- *      refill load right after each one, so a load's slot holds the load
- *      alone   16  as 15 with a refill load every 2 slots   17  ... every 3
- *   18 as 0 with a refill load every 3 MFMA slots
- *   19 as 0 with the loads of both ring stages (K tiles 0 and 1) issued
- *      together at the start of each output tile
+ *   3  as 20 with one workgroup per tile (no persistent loop, no XCD remap)
+ *   10 as 20 with 32x32x16 MFMA blocks, one operand read per slot, a refill
+ *      load every 2 of its 64 slots per K tile
  *   20 the 256x256 tiled kernel of variant 0, whatever the shape
  *   21, 22, 23 the same schedule on 256x128, 128x256 (3-stage rings) and
  *      128x128 (4-stage ring) output tiles (4 waves of 128x64, 64x128,
  *      64x64): the smaller tiles of variant 0, whatever the shape
  *   24, 25, 26 as 21, 22, 23 with 2-stage rings   27 as 23 with 5 stages
- *   28 as 20 with D written by ordinary (cached) stores instead of
- *      non-temporal ones
- * Variants 1..28 always run the tiled kernel, whatever the shape; variant
+ * Variants 1..27 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16, and some shapes with 17..64 rows on the smaller side: the skinny
- * kernel).  Each
- * other kernel family has its own range:
- *   100..151 the skinny kernel (only for M <= 16 or N <= 16, else
- *      GEMVTILE_ERR_UNSUPPORTED).  100: the gemm_f16 choice (16, 8, 4, 2
- *      or 1 rows of the large side per workgroup, see gemvtile_gemm_grid; at
- *      16 rows launch 147).
- *      101..103: operands staged through an LDS ring of 1 KiB row segments,
- *      16 large-side rows per workgroup, (waves per workgroup, ring stages)
- *      = (8,4), (8,3), (4,4).  104..108: operands loaded into registers,
- *      (waves, 32-wide K steps in flight per wave) = (8,4), (8,2), (8,8),
- *      (16,4), (4,8).  109..111: as 101.. with only 8 rows of the small side
- *      staged (min(M,N) <= 8, else GEMVTILE_ERR_UNSUPPORTED), (waves,
- *      stages) = (8,5), (8,6), (4,6).  112..118: LDS ring, 4 stages, 16
- *      small-side rows staged, (waves, large-side rows per workgroup) =
- *      (16,16), (8,8), (4,4), (8,4), (4,2), (4,1), (1,1).  119..123: the
- *      same with 8 small-side rows staged (min(M,N) <= 8), (8,8), (4,4),
- *      (4,2), (4,1), (8,1).  124..129: deeper rings, (waves, stages,
- *      small-side rows staged, large-side rows per workgroup) = (8,6,16,8),
- *      (4,7,16,4), (8,8,8,8), (4,8,8,4), (4,12,8,4), (4,12,8,2) (the 8-row
- *      stagings need min(M,N) <= 8).  130..139: each workgroup starting its
- *      K walk at K tile (workgroup index mod K tiles), 4 stages, (waves,
- *      small-side rows, large-side rows) = (16,16,16), (8,16,8), (4,16,4),
- *      (4,16,2), (4,16,1), (8,8,8), (4,8,4), (4,8,2), (4,8,1), and (8,8,16)
- *      with 6 stages (the 8-row stagings need min(M,N) <= 8).
- *      140..146: wave-private rings, each wave walking its own run of K
- *      tiles of 64 through its own LDS ring and waiting only for its own
- *      loads; (waves, stages, large-side rows per workgroup, small-side rows
- *      staged, rotated runs) = (8,4,16,16,yes), (8,4,16,16,no),
- *      (4,8,16,16,yes), (8,4,8,16,yes), (8,6,16,8,yes), (8,8,8,8,yes),
- *      (16,2,16,8,yes).  147..151: the large side loaded non-temporally:
- *      147 = 130 with nt [the gemm_f16 choice at 16 rows], 148 = 140 with
- *      nt, 149 = the workgroup ring with (waves, stages, small rows, large
- *      rows) = (8,4,8,8) [the gemm_f16 choice at 8 rows when min(M,N) <= 8],
- *      150 = (4,4,8,4), 151 = (8,4,16,8).  The 8-row stagings (144..146,
- *      149, 150) need min(M,N) <= 8
- *   200, 201 the wave-specialised kernel, whatever the shape: 256x128
- *      output tiles, 4 consumer waves (MFMA only, 128x64 each) and 4 loader
- *      waves (tile loads only) handing K tiles over at one barrier per K
- *      tile, with a 3-stage (200) or 2-stage (201) LDS ring
- * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
+ * kernel).  The skinny kernel (only for M <= 16 or N <= 16, else
+ * GEMVTILE_ERR_UNSUPPORTED):
+ *   100 the gemm_f16 choice (16, 8, 4, 2 or 1 rows of the large side per
+ *       workgroup, see gemvtile_gemm_grid)
+ *   104 operands loaded straight into registers (8 waves, 4 K steps of 32
+ *       in flight per wave), 16 large-side rows per workgroup
+ *   112 operands staged through a 4-stage LDS ring of 1 KiB row segments,
+ *       16 waves, 16 large-side rows per workgroup
+ *   130 as 112 with each workgroup starting its K walk at a different K tile
+ *   147 as 130 with the large side loaded non-temporally (the gemm_f16
+ *       choice at 16 rows per workgroup)
+ * The wave-specialised kernel, whatever the shape:
+ *   200, 201 256x128 output tiles, 4 consumer waves (MFMA only, 128x64
+ *       each) and 4 loader waves (tile loads only) handing K tiles over at
+ *       one barrier per K tile, with a 3-stage (200) or 2-stage (201) ring
+ * Other numbers (ablations measured and not kept) return
+ * GEMVTILE_ERR_INVALID_ARG.
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
                               void *stream, int variant);
 
 /*
  * gemvtile_gemv_f16_variant -- gemv_f16 with an internal launch shape, for
- * measurements only (same contract and results as gemv_f16).  A variant fixes
- * the rows per wave, waves per workgroup, 16-byte chunk steps in flight per
- * lane and whether W is read with non-temporal loads:
- *   0 = 2 rows, 8 waves, 4 steps, nt, each wave starting its walk along K at
- *       a different step group (the gemv_f16 default)
- *   1 = 4 rows, 4 waves, 4 steps, nt   2 = 2 rows, 8 waves, 8 steps, nt
- *   3 = 1 row, 8 waves, 8 steps, nt    4 = 2 rows, 4 waves, 8 steps, nt
- *   5 = 1 row, 16 waves, 4 steps, nt   6 = as 0 with ordinary loads
- *   7 = as 0 with every wave starting at the row's first column
- *   8..11 = 2 rows, 8 waves, 4 steps, nt, rotated start, with K split over
- *       1, 2, 4, 8 waves per row group (16, 8, 4, 2 rows per workgroup)
- *   12 = 1 row, 8 waves, 4 steps, nt, rotated start, K split 8 ways
- * Variant 0 picks one of 8..12 from N and the compute-unit count (see
- * gemvtile_gemv_grid).  Variants 1..5 start every wave at the first column.
- * Returns GEMVTILE_ERR_INVALID_ARG for an unknown variant.
+ * measurements only (same contract and results as gemv_f16):
+ *   0  the gemv_f16 default (picks one of 8..12 from N and the compute-unit
+ *      count, see gemvtile_gemv_grid)
+ *   6  2 rows per wave, 8 waves, 4 chunk steps in flight, ordinary (cached)
+ *      loads of W, each wave starting its walk along K at a different group
+ *   7  as 6 with non-temporal loads of W and every wave starting at the
+ *      row's first column
+ *   8..11  2 rows per wave, 8 waves, 4 steps, non-temporal W, rotated start,
+ *      K split over 1, 2, 4, 8 waves per row group (16, 8, 4, 2 rows per
+ *      workgroup)
+ *   12 1 row per workgroup, K split 8 ways
+ * Other numbers return GEMVTILE_ERR_INVALID_ARG.
  */
 int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream,
                               int variant);
+
+/*
+ * gemvtile_ring_trace -- the K-loop schedule of the tiled GEMM kernel, for
+ * checking on the CPU (host-only; no GPU needed).  The kernel's K loop is a
+ * walker over K tiles that issues tile loads, operand reads, MFMAs, waits
+ * and barriers; this runs the same walker on the host for the kernel with a
+ * bm x bn output tile and a `stages`-deep LDS ring over `ktu` K tiles (of 64
+ * elements), recording each event instead of issuing it.  The ring follows
+ * "使用 TMA 为 GEMM 建立 Pipeline" (TVM TIRx GEMM chapter), step 5 (Pipeline
+ * 机制): K tile k in stage k % stages, refilled with tile k + stages once
+ * consumed; completion is tracked by in-order vmcnt waits instead of the
+ * chapter's per-stage mbarrier phases.
+ *
+ *   bm, bn, stages  one of the kernel shapes the library has: 256x256 with 2
+ *                   stages; 256x128 and 128x256 with 2 or 3; 128x128 with 2,
+ *                   4 or 5
+ *   ktu     K tiles the loop walks (1 .. 2^20): ceil(K / 64), or one K slice
+ *           of a split-K unit
+ *   events  host memory for `cap` events of five int32 {code, a, b, c, d}:
+ *             1 load      a = K tile, b = load index, c = ring stage
+ *             2 wait      a = vmcnt (vector-memory operations allowed to
+ *                         stay in flight)
+ *             3 LDS wait  (the wave's LDS reads are complete)
+ *             4 barrier   (workgroup barrier)
+ *             5 read      a = K tile, b = K step, c = read index, d = stage
+ *             6 MFMA      a = fragment buffer, b = MFMA index in the K step
+ *           events beyond `cap` are counted but not written; may be NULL
+ *           when cap == 0
+ *   info    if not NULL, 4 ints: loads per wave per K tile, operand reads per
+ *           wave per K step, K steps per K tile, MFMAs per wave per K step
+ * Each wave of the workgroup runs this same sequence.  Returns the number
+ * of events, or -1 for a shape the library has no kernel for or arguments
+ * out of range.
+ */
+int64_t gemvtile_ring_trace(int bm, int bn, int stages, int64_t ktu, int32_t *events, int64_t cap, int *info);
 
 /*
  * gemvtile_xcd_logical_id -- the logical workgroup id the persistent GEMM

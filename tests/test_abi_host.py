@@ -84,17 +84,13 @@ def test_gemm_argument_validation(lib):
     assert _gemm(lib, FAKE, FAKE, FAKE, 4, 4, 4194304) == UNSUPPORTED
     assert _gemm(lib, FAKE, FAKE, FAKE, 2**31, 4, 8) == UNSUPPORTED
     # unknown internal variant: each family has its own id range (tiled 0..,
-    # skinny 100.., wave-specialised 200..); the gaps are invalid
-    for bad in (-1, 29, 99, 152, 199, 202, 1000):
+    # skinny 100.., wave-specialised 200..); the gaps, and the numbers of
+    # ablations measured and not kept, are invalid
+    for bad in (-1, 4, 9, 11, 12, 15, 19, 28, 29, 99, 101, 113, 131, 140, 148, 152, 199, 202, 1000):
         assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, bad) == INVALID, bad
     # skinny launch shapes only apply when one side has at most 16 rows
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 100) == UNSUPPORTED
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 117) == UNSUPPORTED
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, 140) == UNSUPPORTED
-    # the 8-row small-side stagings need min(M, N) <= 8
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 109) == UNSUPPORTED
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 120) == UNSUPPORTED
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 12, 4096, 8, None, 144) == UNSUPPORTED
+    for v in (100, 104, 112, 130, 147):
+        assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, v) == UNSUPPORTED, v
 
 
 def test_gemm_bias_argument_validation(lib):
@@ -129,7 +125,8 @@ def test_gemv_argument_validation(lib):
     assert _gemv(lib, FAKE + 4, FAKE, FAKE, 4, 8) == UNSUPPORTED
     assert _gemv(lib, FAKE, FAKE + 8, FAKE, 4, 8) == UNSUPPORTED
     assert _gemv(lib, FAKE, FAKE, FAKE + 1, 4, 8) == UNSUPPORTED
-    assert lib.gemvtile_gemv_f16_variant(FAKE, FAKE, FAKE, 4, 8, None, 99) == INVALID
+    for bad in (-1, 1, 5, 13, 17, 99):
+        assert lib.gemvtile_gemv_f16_variant(FAKE, FAKE, FAKE, 4, 8, None, bad) == INVALID, bad
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
@@ -408,15 +405,3 @@ def test_gemv_grid_gives_every_cu_a_workgroup(lib):
             # workgroup with N >= rows * cus, else 1
             rows = next((r for r in (16, 8, 4, 2) if N >= r * cus), 1)
             assert g == -(-N // rows)
-
-
-def test_read_stream_argument_validation(lib):
-    """The measurement-only read probe rejects bad arguments before any HIP call."""
-    rs = lib.gemvtile_read_stream
-    assert rs(None, 1024, 1, 256, FAKE, None) == INVALID
-    assert rs(FAKE, 0, 1, 256, FAKE, None) == INVALID
-    assert rs(FAKE, (1 << 30) + 16, 1, 256, FAKE, None) == INVALID
-    assert rs(FAKE, 1024, 4, 256, FAKE, None) == INVALID
-    assert rs(FAKE, 1024, 1, 0, FAKE, None) == INVALID
-    assert rs(FAKE, 1024, 1, 4097, FAKE, None) == INVALID
-    assert rs(FAKE, 1024, 1, 256, None, None) == INVALID

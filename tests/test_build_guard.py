@@ -15,10 +15,12 @@ write themselves.
 """
 from gemv_tile_pipelined_amd import build
 
-SPILLED = "_ZN2gt11gemm_kernelINS_9GemmShapeILi256ELi256ELi64ELi2ELi2ELi2ELb1ELb1ELi1ELi1ELi1ELi1ELi0ELi16ELi2ELi1ELb0ELi0ELb0EEEEEvPKDF16_S4_PDF16_iiiiii"
-DEFAULT = "_ZN2gt11gemm_kernelINS_9GemmShapeILi256ELi256ELi64ELi2ELi2ELi2ELb1ELb1ELi4ELi1ELi1ELi1ELi0ELi16ELi2ELi1ELb0ELi0ELb0EEEEEvPKDF16_S4_PDF16_iiiiii"
-EIGHT_WAVES = "_ZN2gt11gemm_kernelINS_9GemmShapeILi256ELi256ELi64ELi2ELi2ELi4ELb1ELb1ELi4ELi1ELi1ELi1ELi0ELi16ELi2ELi1ELb0ELi0ELb0EEEEEvPKDF16_S4_PDF16_iiiiii"
-MI32_ONE_STAGE = "_ZN2gt11gemm_kernelINS_9GemmShapeILi256ELi256ELi64ELi1ELi2ELi2ELb1ELb1ELi1ELi1ELi1ELi1ELi0ELi32ELi1ELi0ELb0ELi0ELb0EEEEEvPKDF16_S4_PDF16_iiiiii"
+# GemmShape<BM, BN, BK, STAGES, WAVES_M, WAVES_N, SWIZZLE, PERSISTENT,
+# DMA_STRIDE, MI, READ_STRIDE, DMA_OFFSET, DTYPE>
+SPILLED = "_ZN2gt11gemm_kernelINS_9GemmShapeILi256ELi256ELi64ELi2ELi2ELi2ELb1ELb1ELi1ELi16ELi2ELi1ELi0EEELi0EEEvPKDF16_S4_PDF16_iiiiiiPKtiPfi"
+DEFAULT = "_ZN2gt11gemm_kernelINS_9GemmShapeILi256ELi256ELi64ELi2ELi2ELi2ELb1ELb1ELi4ELi16ELi2ELi1ELi0EEELi0EEEvPKDF16_S4_PDF16_iiiiiiPKtiPfi"
+EIGHT_WAVES = "_ZN2gt11gemm_kernelINS_9GemmShapeILi256ELi256ELi64ELi2ELi2ELi4ELb1ELb1ELi4ELi16ELi2ELi1ELi0EEELi0EEEvPKDF16_S4_PDF16_iiiiiiPKtiPfi"
+MI32_ONE_STAGE = "_ZN2gt11gemm_kernelINS_9GemmShapeILi256ELi256ELi64ELi1ELi2ELi2ELb1ELb1ELi1ELi32ELi1ELi0ELi0EEELi0EEEvPKDF16_S4_PDF16_iiiiiiPKtiPfi"
 WS = "_ZN2gt14gemm_ws_kernelILi3ELi0EEEvPKDF16_S2_PDF16_iiiiii"
 GEMV = "_ZN2gt11gemv_kernelILi2ELi8ELi4ELb1ELb1ELi0ELi1ELin1EEEvPKvS2_Pviii"
 
@@ -69,6 +71,14 @@ def test_parse_and_check():
 def test_check_flags_one_agpr_short():
     usage = build.parse_resource_usage(_remarks(EIGHT_WAVES, 127, 232, 0))
     assert len(build.check_resource_usage(usage)) == 1
+
+
+def test_check_flags_spilled_fragments():
+    # all AGPRs in place, but the operand fragments of a partly unrolled K
+    # loop spilled to scratch (as a too-low unroll limit once produced)
+    usage = build.parse_resource_usage(_remarks(DEFAULT, 256, 512, 1040, spill=120))
+    bad = build.check_resource_usage(usage)
+    assert len(bad) == 1 and "scratch 1040" in bad[0]
 
 
 def test_parse_remarks_with_location_after_tag():
@@ -127,6 +137,26 @@ def test_hazard_scan_flags_late_accumulator_restore():
     # a VGPR that shares its number with the MFMA's accumulator is another register
     ok = _asm(DEFAULT, ["v_add_u32_e32 v253, s55, v94", MFMA])
     assert build.scan_mfma_hazards(ok) == []
+
+
+LDS_DMA = "!s_mov_b32 m0, s12\n\ts_nop 0\n\tbuffer_load_dwordx4 v118, s[16:19], 0 offen lds"
+
+
+def test_m0_scan_accepts_inline_only_m0():
+    ok = _asm(DEFAULT, [LDS_DMA, MFMA, "s_add_i32 s12, s12, 0x1000", LDS_DMA, "ds_read_b128 v[4:7], v96"])
+    assert build.scan_m0_uses(ok) == []
+
+
+def test_m0_scan_flags_compiler_m0_use():
+    # the compiler keeps a value in M0 across the inline asm that overwrites it
+    bad = _asm(DEFAULT, ["s_mov_b32 m0, s40", LDS_DMA, "v_movrels_b32_e32 v1, v8"])
+    found = build.scan_m0_uses(bad)
+    assert len(found) == 2 and "s_mov_b32 m0, s40" in found[0] and "v_movrels" in found[1]
+    # a compiler LDS-DMA (reads M0 implicitly) and an explicit read of M0
+    bad2 = _asm(DEFAULT, [LDS_DMA, "buffer_load_dword v1, s[16:19], 0 offen lds", "s_mov_b32 s3, m0"])
+    assert len(build.scan_m0_uses(bad2)) == 2
+    # a kernel without inline M0 writes is not scanned
+    assert build.scan_m0_uses(_asm(GEMV, ["s_mov_b32 m0, s40", "ds_gws_init v0"])) == []
 
 
 def test_hazard_scan_skips_compiler_mfmas_and_other_kernels():

@@ -11,8 +11,8 @@ correctly rounded one); bit-for-bit for integer-valued inputs, whose FP32
 partial sums are exact in any order (|sums| <= K·64 < 2^24), so only the final
 round-to-nearest-even decides.  The tiled path (4096^3, the ragged
 4000x4032x4104), the skinny path (decode batch 8x4096x14336, small N) and the
-GEMV (4096x14336) are all covered, the full sizes on seeded sampled rows plus a
-closed form on every element.
+GEMV (4096x14336) are all covered, the full sizes compared with the oracle on
+every element, plus a closed form on every element.
 """
 import os
 
@@ -103,6 +103,11 @@ SHAPES = [
     (32, 4096, 4104),
     (4000, 48, 520),
     (24, 300, 8200),
+    # 4 large-side rows per workgroup with 32 and 64 staged small-side rows,
+    # and the 64-row staging at 16 large-side rows per workgroup
+    (24, 1500, 4104),
+    (48, 1500, 1032),
+    (48, 4096, 4104),
 ]
 
 
@@ -194,20 +199,23 @@ def test_bf16_rne_probe_subnormal_results(env):
     _probe(env, subnormal_result=True)
 
 
+@pytest.mark.parametrize("integer", [False, True], ids=["uniform", "integer"])
 @pytest.mark.parametrize("cfg_id", [1, 2], ids=["4096cube", "ragged_4000x4032x4104"])
-def test_gemm_bf16_full_size_sampled(env, cfg_id):
+def test_gemm_bf16_full_size_every_element(env, full_size, cfg_id, integer):
+    """4096^3 and 4000x4032x4104 in bf16 against the oracle on every output
+    element: uniform within the tolerance, integer bit for bit."""
     torch, gt, dev = env
     w = datagen.WORKLOADS[cfg_id]
-    print(f"[gemm_bf16 full size] {w.name} M={w.M} N={w.N} K={w.K}", flush=True)
-    A, B = datagen.gemm_inputs(w, bf16=True)
-    rows = datagen.sample_rows(cfg_id, w.M, 64)
+    print(f"[gemm_bf16 full size] {w.name} M={w.M} N={w.N} K={w.K} integer={integer}", flush=True)
+    A, B = full_size.inputs(cfg_id, integer, True)
     D = _gemm(env, A, B)
-    assert bool(torch.isfinite(D).all())
-    got = _bits(D[torch.from_numpy(rows).to(dev)])
-    assert _violations(got, oracle.gemm_bf16(A, B, rows=rows)) == 0
-    Ai, Bi = datagen.gemm_inputs(w, integer=True, bf16=True)
-    Di = _gemm(env, Ai, Bi)
-    assert np.array_equal(_bits(Di[torch.from_numpy(rows).to(dev)]), oracle.gemm_bf16(Ai, Bi, rows=rows))
+    got = _bits(D)
+    ref = full_size.reference(cfg_id, integer, True)
+    if integer:
+        assert np.array_equal(got, ref)
+    else:
+        assert bool(torch.isfinite(D).all())
+        assert _violations(got, ref) == 0
 
 
 @pytest.mark.parametrize("cfg_id", [1, 2], ids=["4096cube", "ragged_4000x4032x4104"])

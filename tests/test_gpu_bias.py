@@ -108,15 +108,20 @@ def test_gemm_bias_null_bias_and_k0(env):
         assert np.array_equal(D.cpu().numpy().view(np.uint16), want.view(np.uint16)), act
 
 
-def test_gemm_bias_full_size_sampled(env):
-    """The 4096^3 workload with a bias and ReLU, on sampled rows."""
+def test_gemm_bias_full_size_every_element(env, full_size):
+    """The 4096^3 workload with a bias and ReLU against the oracle on every
+    output element (uniform inputs), and bit for bit on integer inputs with
+    an integer bias."""
     w = datagen.WORKLOADS[1]
-    A, B = datagen.gemm_inputs(w)
+    print(f"[gemm_bias full size] {w.name} relu", flush=True)
+    A, B = full_size.inputs(1)
     bias = datagen.uniform_f16(1, 3, (w.N,), -4.0, 4.0)
-    rows = datagen.sample_rows(1, w.M, 32)
-    got = _run(env, A, B, bias, RELU, rows)
-    assert _violations(got, oracle.gemm_bias(A, B, bias, RELU, rows=rows)) == 0
+    got = _run(env, A, B, bias, RELU)
+    assert _violations(got, oracle.gemm_bias(A, B, bias, RELU)) == 0
     assert (got == 0).mean() > 0.3  # ReLU did clamp a good part of the outputs
+    Ai, Bi = full_size.inputs(1, True)
+    bias_i = datagen.integer_f16(1, 13, (w.N,), -64, 64)
+    assert np.array_equal(_run(env, Ai, Bi, bias_i, RELU), oracle.gemm_bias(Ai, Bi, bias_i, RELU))
 
 
 @pytest.mark.parametrize("shape", [(300, 260, 200), (8192, 1000, 264), (8, 4100, 520)],

@@ -64,21 +64,18 @@ def test_gemm_ws_small(env, shape, variant):
 
 
 @pytest.mark.parametrize("variant", WS_VARIANTS)
-def test_gemm_ws_full_size(env, variant):
-    """4096^3 (two output tiles per CU in the persistent loop): sampled rows
-    against the oracle, integer inputs bit-exact, and a rank-1 closed form on
-    every element."""
+def test_gemm_ws_full_size(env, full_size, variant):
+    """4096^3 (two output tiles per CU in the persistent loop) against the
+    oracle on every element, uniform inputs within the tolerance and integer
+    inputs bit-exact, and a rank-1 closed form on every element."""
     torch, gt, dev = env
     w = datagen.WORKLOADS[1]
     print(f"[gemm_ws full size] variant {variant} {w.name}", flush=True)
-    rows = datagen.sample_rows(1, w.M, 64)
-    A, B = datagen.gemm_inputs(w)
-    D = _gemm(env, A, B, variant)
-    got = D[torch.from_numpy(rows).to(dev)].cpu().numpy()
-    assert _violations(got, oracle.gemm(A, B, rows=rows)) == 0
-    Ai, Bi = datagen.gemm_inputs(w, integer=True)
-    Di = _gemm(env, Ai, Bi, variant)
-    assert np.array_equal(Di[torch.from_numpy(rows).to(dev)].cpu().numpy(), oracle.gemm(Ai, Bi, rows=rows))
+    A, B = full_size.inputs(1)
+    got = _gemm(env, A, B, variant).cpu().numpy()
+    assert _violations(got, full_size.reference(1)) == 0
+    Ai, Bi = full_size.inputs(1, True)
+    assert np.array_equal(_gemm(env, Ai, Bi, variant).cpu().numpy(), full_size.reference(1, True))
     g = datagen.rng(1, 22)
     choices = np.array([-1.0, -0.5, -0.25, -0.125, 0.125, 0.25, 0.5, 1.0])
     u, v = g.choice(choices, w.M), g.choice(choices, w.N)

@@ -58,7 +58,7 @@ def test_gemm_at_largest_k(env, shape):
     print(f"[limits] gemm_splitk {M}x{N}x{K}: {gt.splitk_splits(M, N, K, cus)} slices", flush=True)
     if cus == 256:
         assert gt.splitk_splits(M, N, K, cus) > 1
-    Ds = gt.gemm_splitk_f16(A, B)
+    Ds = gt.gemm_splitk_f16(A, B, workspace=gt.alloc_splitk_workspace(A, B))
     torch.cuda.synchronize(dev)
     assert torch.equal(Ds.view(torch.int16), want.view(torch.int16))
     del A, B, D, Ds

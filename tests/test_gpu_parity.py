@@ -5,10 +5,12 @@ bit-for-bit (value) equality for integer-valued inputs, whose FP32 partial
 sums are exact in any order (|sums| <= K·64 < 2^24), so only the final
 round-to-nearest-even can differ -- and must not.
 
-Small and ragged shapes are compared in full; the full-size workloads
-(4096^3, 4000x4032x4104, 8192^3, GEMV 4096x14336) run in the launch shape the
-benchmark times and are compared on seeded sampled rows, plus closed forms
-checked on every element.
+Small and ragged shapes are compared in full, and so are the full-size
+workloads 4096^3 (the benchmark's GEMM), 4000x4032x4104 and the GEMV
+4096x14336, in the launch shape the benchmark times.  8192^3 is compared on
+64 seeded rows plus one seeded row from every 256-row band (so every tile row
+of the output is checked against the oracle), and a closed form is checked on
+every element.
 """
 import os
 
@@ -156,23 +158,40 @@ def test_rne_probe_subnormal_inputs(env):
         assert int(y.view(np.uint16)[0]) == want, (av, bv)
 
 
-@pytest.mark.parametrize("cfg_id", [1, 2, 4], ids=["4096cube", "ragged_4000x4032x4104", "8192cube"])
-def test_gemm_full_size_sampled(env, cfg_id):
+@pytest.mark.parametrize("integer", [False, True], ids=["uniform", "integer"])
+@pytest.mark.parametrize("cfg_id", [1, 2], ids=["4096cube", "ragged_4000x4032x4104"])
+def test_gemm_full_size_every_element(env, full_size, cfg_id, integer):
+    """4096^3 and 4000x4032x4104 against the oracle on every output element:
+    uniform inputs within the tolerance, integer inputs bit for bit."""
     torch, gt, dev = env
     w = datagen.WORKLOADS[cfg_id]
+    print(f"[gemm full size] {w.name} M={w.M} N={w.N} K={w.K} integer={integer}", flush=True)
+    A, B = full_size.inputs(cfg_id, integer)
+    got = _gemm(env, A, B).cpu().numpy()
+    ref = full_size.reference(cfg_id, integer)
+    if integer:
+        assert np.array_equal(got, ref)
+    else:
+        assert np.isfinite(got).all()
+        assert _tol_violations(got, ref) == 0
+
+
+def test_gemm_8192_sampled_rows_every_tile_band(env):
+    """8192^3: the 64 seeded rows plus one seeded row of every 256-row tile
+    band, all columns, uniform within the tolerance and integer bit-exact."""
+    torch, gt, dev = env
+    w = datagen.WORKLOADS[4]
     print(f"[gemm full size] {w.name} M={w.M} N={w.N} K={w.K}", flush=True)
+    rows = np.union1d(datagen.sample_rows(4, w.M, 64), datagen.band_rows(4, w.M, 256))
+    assert len(np.unique(rows // 256)) == w.M // 256
+    trows = torch.from_numpy(rows).to(dev)
     A, B = datagen.gemm_inputs(w)
-    rows = datagen.sample_rows(cfg_id, w.M, 64)
     D = _gemm(env, A, B)
     assert bool(torch.isfinite(D).all())
-    got = D[torch.from_numpy(rows).to(dev)].cpu().numpy()
-    ref = oracle.gemm(A, B, rows=rows)
-    assert _tol_violations(got, ref) == 0
-    # integer inputs: bit-exact on the sampled rows
+    assert _tol_violations(D[trows].cpu().numpy(), oracle.gemm(A, B, rows=rows)) == 0
     Ai, Bi = datagen.gemm_inputs(w, integer=True)
     Di = _gemm(env, Ai, Bi)
-    goti = Di[torch.from_numpy(rows).to(dev)].cpu().numpy()
-    assert np.array_equal(goti, oracle.gemm(Ai, Bi, rows=rows))
+    assert np.array_equal(Di[trows].cpu().numpy(), oracle.gemm(Ai, Bi, rows=rows))
 
 
 @pytest.mark.parametrize("cfg_id", [1, 2, 4], ids=["4096cube", "ragged_4000x4032x4104", "8192cube"])
@@ -259,7 +278,10 @@ def test_output_guard_band(env):
     assert np.array_equal(D.cpu().numpy(), oracle.gemm(A, B))
 
 
-@pytest.mark.parametrize("variant", list(range(1, 29)))
+TILED_VARIANTS = [1, 2, 3, 10, 20, 21, 22, 23, 24, 25, 26, 27]
+
+
+@pytest.mark.parametrize("variant", TILED_VARIANTS)
 def test_gemm_variants_bit_identical(env, variant):
     """The ablation kernels (no swizzle, one stage, non-persistent) give the
     same bits as the default on integer data; a pipeline race would not."""
@@ -271,12 +293,13 @@ def test_gemm_variants_bit_identical(env, variant):
     assert np.array_equal(_gemm(env, A, B, variant).cpu().numpy(), base)
 
 
-@pytest.mark.parametrize("variant", [0, 2, 11, 12, 15, 16, 17, 19, 20, 21, 22, 23, 24, 25, 26, 27])
-@pytest.mark.parametrize("K", [8, 64, 72, 128, 136, 192, 200, 264])
+@pytest.mark.parametrize("variant", [0, 2, 10, 20, 21, 22, 23, 24, 25, 26, 27])
+@pytest.mark.parametrize("K", [8, 64, 72, 128, 136, 192, 200, 264, 328])
 def test_gemm_variants_few_k_tiles(env, variant, K):
-    """1 to 5 K tiles of 64 (1 to 9 of 32), whole and ragged: the prologue,
-    the last refill and the ring drain take their short-K branches.  Integer
-    data, so every variant must match the oracle bit for bit."""
+    """1 to 6 K tiles of 64, whole and ragged: the prologue, the last refill
+    and the ring drain take their short-K branches for every ring depth
+    (2 to 5 stages).  Integer data, so every variant must match the oracle
+    bit for bit."""
     M, N = 300, 260
     A = datagen.integer_f16(6100 + K, 0, (M, K))
     B = datagen.integer_f16(6100 + K, 1, (N, K))
@@ -314,7 +337,7 @@ def test_gemm_tile_choice_shapes(env, case):
     assert np.array_equal(Di[torch.from_numpy(last).to(dev)].cpu().numpy(), oracle.gemm(Ai, Bi, rows=last))
 
 
-@pytest.mark.parametrize("variant", list(range(1, 18)))
+@pytest.mark.parametrize("variant", [6, 7, 8, 9, 10, 11, 12])
 def test_gemv_variants_bit_identical(env, variant):
     N, K = 1031, 14344
     x = datagen.integer_f16(6001, 0, (K,))
@@ -348,16 +371,3 @@ def test_misaligned_pointer_is_rejected(env):
     with pytest.raises(gt.GemvTileError) as e:
         gt.gemm_f16(A, B)
     assert e.value.status == 2
-
-
-def test_read_stream_probe_writes_nothing(env):
-    """The read-ceiling probe only reads: the buffer and the sink are unchanged."""
-    torch, gt, dev = env
-    buf = torch.arange(1 << 20, dtype=torch.int32, device=dev)
-    before = buf.clone()
-    sink = torch.zeros((256,), dtype=torch.int32, device=dev)
-    for policy in range(4):
-        gt.read_stream(buf, sink, policy, 256)
-    torch.cuda.synchronize(dev)
-    assert torch.equal(buf, before)
-    assert bool((sink == 0).all())

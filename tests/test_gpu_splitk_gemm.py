@@ -73,7 +73,7 @@ def test_splitk_parity(env, case):
     B = datagen.uniform_f16(cfg, 1, (N, K), -1.0, 1.0)
     tA, tB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
     D1 = gt.gemm_splitk_f16(tA, tB, workspace=ws)
-    D2 = gt.gemm_splitk_f16(tA, tB)  # the binding allocates a workspace
+    D2 = gt.gemm_splitk_f16(tA, tB, workspace=gt.alloc_splitk_workspace(tA, tB))  # a second, fresh workspace
     torch.cuda.synchronize(dev)
     assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))  # deterministic
     assert np.isfinite(D1.float().cpu().numpy()).all()
@@ -90,7 +90,8 @@ def test_splitk_bf16(env):
     def dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    D = gt.gemm_splitk_bf16(dev_bf16(A), dev_bf16(B))
+    tA, tB = dev_bf16(A), dev_bf16(B)
+    D = gt.gemm_splitk_bf16(tA, tB, workspace=gt.alloc_splitk_workspace(tA, tB))
     got = D[torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, oracle.gemm_bf16(A, B, rows=rows))
 
@@ -130,6 +131,10 @@ def test_splitk_workspace_errors(env):
     assert lib.gemm_splitk_f16(*args, ws.data_ptr(), need, s) == 0
     torch.cuda.synchronize(dev)
     assert bool((D == 0).all())
+    # the binding allocates no workspace behind the caller's back
+    with pytest.raises(gt.GemvTileError) as e:
+        gt.gemm_splitk_f16(A, B, D)
+    assert e.value.status == 1
 
 
 # Skinny shapes (2..16 rows on a side): (M, N, K, slices on 256 CUs).  The
@@ -159,7 +164,7 @@ def test_splitk_skinny_parity(env, case):
     B = datagen.uniform_f16(cfg, 1, (N, K), -1.0, 1.0)
     tA, tB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
     D1 = gt.gemm_splitk_f16(tA, tB, workspace=ws)
-    D2 = gt.gemm_splitk_f16(tA, tB)
+    D2 = gt.gemm_splitk_f16(tA, tB, workspace=gt.alloc_splitk_workspace(tA, tB))
     torch.cuda.synchronize(dev)
     assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
     assert np.isfinite(D1.float().cpu().numpy()).all()
@@ -177,6 +182,7 @@ def test_splitk_skinny_bf16(env):
 
         assert gt.splitk_splits(M, N, K, torch.cuda.get_device_properties(dev).multi_processor_count) > 1 or \
             torch.cuda.get_device_properties(dev).multi_processor_count != 256
-        D = gt.gemm_splitk_bf16(dev_bf16(A), dev_bf16(B))
+        tA, tB = dev_bf16(A), dev_bf16(B)
+        D = gt.gemm_splitk_bf16(tA, tB, workspace=gt.alloc_splitk_workspace(tA, tB))
         got = D.view(torch.int16).cpu().numpy().view(np.uint16)
         assert np.array_equal(got, oracle.gemm_bf16(A, B)), (M, N, K)

@@ -1,0 +1,276 @@
+"""The LDS ring of the tiled GEMM's K loop, checked on the CPU.
+
+The kernel's K loop is a walker (ring.hpp) that the library also runs on the
+host, recording every event instead of issuing it (gemvtile_ring_trace).
+These tests replay those traces through an independent model of what the
+events mean on the hardware and check that the schedule is correct:
+
+* loads of one wave complete in issue order, and a wait with count n leaves
+  only the n most recent loads in flight;
+* a tile is visible to every wave once a barrier follows the wait that saw
+  the tile land (each wave runs the same sequence);
+* an operand read of tile t must use stage t % STAGES, see tile t there and
+  find it visible; a stage may only be refilled after every wave has
+  finished reading its previous tile (LDS wait, then a barrier);
+* every K tile is loaded once, completely, into its stage, and read in full,
+  and nothing is in flight when the loop ends.
+
+The stage and prefetch pattern is also compared with the walk-through
+exercise of the TVM chapter ("使用 TMA 为 GEMM 建立 Pipeline", step 5,
+Pipeline 机制: PIPE_DEPTH = 2, K_TILES = 5), and the ragged K = 4104 (65 K
+tiles, an odd count) and split-K slice lengths are covered.
+"""
+import os
+
+import pytest
+
+import gemv_tile_pipelined_amd as gt
+
+# (bm, bn, stages) of every tiled kernel the library instantiates.
+SHAPES = [(256, 256, 2), (256, 128, 2), (256, 128, 3), (128, 256, 2), (128, 256, 3), (128, 128, 2), (128, 128, 4),
+          (128, 128, 5)]
+# 1..9 short loops (every prologue / last-refill / drain branch), 22 and 56
+# (split-K slice lengths: ceil(224 / 4) = 56 for K = 14336 in 4 slices), 64
+# (K = 4096), 65 (K = 4104: the ragged benchmark shape), 128 (K = 8192).
+KTUS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 22, 56, 64, 65, 128]
+
+
+class RingModel:
+    """Replays a trace; raises AssertionError on the first violation."""
+
+    def __init__(self, stages, ktu, info):
+        self.S, self.ktu = stages, ktu
+        self.per = info["loads_per_tile"]
+        self.reads = info["reads_per_step"]
+        self.ksteps = info["ksteps"]
+        self.mfma = info["mfma_per_step"]
+        self.pending = []  # this wave's loads in flight, oldest first: (tile, d)
+        self.landed = {}  # tile -> loads of this wave that have landed
+        self.issued = {}  # tile -> list of load indices issued
+        self.visible = set()  # tiles every wave has landed (a barrier followed)
+        self.landed_before_barrier = set()
+        self.owner = {}  # stage -> tile loaded into it last
+        self.reads_in_flight = set()  # tiles read since the last LDS wait
+        self.reads_done = set()  # tiles whose reads completed since the last barrier
+        self.released = set()  # tiles whose stage every wave has finished reading
+        self.read_log = {}  # tile -> list of (ks, r)
+        self.last_read_tile = -1
+        self.mfmas = 0
+        self.mfma_since_load = {}  # tile -> MFMAs issued since its last load was issued
+        self.overlap = {}  # tile -> MFMAs between its last load and the wait that landed it
+        self.events = []
+
+    def step(self, ev):
+        kind, a, b, c, d = ev
+        self.events.append(ev)
+        getattr(self, "_" + kind)(a, b, c, d)
+
+    def _load(self, tile, d, stage, _):
+        assert 0 <= tile < self.ktu, f"load of K tile {tile} outside 0..{self.ktu - 1}"
+        assert stage == tile % self.S, f"tile {tile} loaded into stage {stage}"
+        got = self.issued.setdefault(tile, [])
+        assert d == len(got), f"tile {tile}: load {d} issued after {got}"
+        if d == 0:
+            prev = self.owner.get(stage)
+            if prev is not None:
+                assert prev == tile - self.S, f"stage {stage} refilled with {tile} over {prev}"
+                assert prev in self.released, f"stage {stage} refilled with tile {tile} before every wave read tile {prev}"
+            self.owner[stage] = tile
+        got.append(d)
+        assert d < self.per
+        self.pending.append((tile, d))
+        if d == self.per - 1:
+            self.mfma_since_load[tile] = 0
+
+    def _wait(self, n, *_):
+        assert 0 <= n <= 63, f"vmcnt {n} outside the counter's range"
+        while len(self.pending) > n:
+            tile, _d = self.pending.pop(0)
+            self.landed[tile] = self.landed.get(tile, 0) + 1
+            if self.landed[tile] == self.per:
+                self.landed_before_barrier.add(tile)
+                self.overlap[tile] = self.mfma_since_load.pop(tile)
+
+    def _lds_wait(self, *_):
+        self.reads_done |= self.reads_in_flight
+        self.reads_in_flight = set()
+
+    def _barrier(self, *_):
+        self.visible |= self.landed_before_barrier
+        self.landed_before_barrier = set()
+        self.released |= self.reads_done
+        self.reads_done = set()
+
+    def _read(self, tile, ks, r, stage):
+        assert stage == tile % self.S, f"tile {tile} read from stage {stage}"
+        assert self.owner.get(stage) == tile, f"tile {tile} read from stage {stage}, which holds {self.owner.get(stage)}"
+        assert tile in self.visible, f"tile {tile} read before every wave's loads of it landed"
+        assert tile not in self.released, f"tile {tile} read after its stage was released"
+        assert tile >= self.last_read_tile, "reads go back to an older K tile"
+        self.last_read_tile = tile
+        self.reads_in_flight.add(tile)
+        self.read_log.setdefault(tile, []).append((ks, r))
+
+    def _mfma(self, *_):
+        self.mfmas += 1
+        for t in self.mfma_since_load:
+            self.mfma_since_load[t] += 1
+
+    def finish(self):
+        assert self.pending == [], f"loads still in flight at the end: {self.pending}"
+        assert self.reads_in_flight == set(), "LDS reads not waited for at the end"
+        for t in range(self.ktu):
+            assert self.issued.get(t) == list(range(self.per)), f"tile {t} loads {self.issued.get(t)}"
+            want = [(ks, r) for ks in range(self.ksteps) for r in range(self.reads)]
+            assert sorted(self.read_log.get(t, [])) == want, f"tile {t} reads"
+        assert self.mfmas == self.ktu * self.ksteps * self.mfma
+
+
+def replay(bm, bn, stages, ktu):
+    events, info = gt.ring_trace(bm, bn, stages, ktu)
+    model = RingModel(stages, ktu, info)
+    for ev in events:
+        model.step(ev)
+    model.finish()
+    return model, events
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}_s{s[2]}")
+@pytest.mark.parametrize("ktu", KTUS)
+def test_ring_schedule_is_correct(shape, ktu):
+    replay(*shape, ktu)
+
+
+# The tiles and ring depths gemm_f16 picks (gemvtile_gemm_tile).
+DEFAULT_SHAPES = [(256, 256, 2), (256, 128, 3), (128, 256, 3), (128, 128, 4)]
+
+
+@pytest.mark.parametrize("shape", DEFAULT_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}_s{s[2]}")
+def test_ring_overlaps_loads_with_mfmas(shape):
+    """In the steady state each K tile's last load is issued at least one
+    whole K step of MFMAs before the wait that needs it: the loads overlap
+    the matrix work (the point of the ring)."""
+    bm, bn, stages = shape
+    model, _ = replay(bm, bn, stages, 16)
+    for t in range(stages, 16):
+        assert model.overlap[t] >= model.mfma, (t, model.overlap[t])
+
+
+def test_two_stage_rings_of_small_tiles_barely_overlap():
+    """The 2-stage ablations of the smaller tiles: a K tile of them is 1/2
+    or 1/4 of the 256x256 one in MFMA slots, so the last load of a refill
+    lands only a few MFMAs before it is needed -- which is why those tiles
+    get 3- and 4-stage rings by default."""
+    for bm, bn in [(256, 128), (128, 256), (128, 128)]:
+        model, _ = replay(bm, bn, 2, 16)
+        assert max(model.overlap[t] for t in range(2, 16)) < model.mfma
+
+
+def test_ring_wait_counts_let_younger_tiles_fly():
+    """With 3 or more stages the steady-state wait leaves the younger tiles'
+    loads in flight (vmcnt = (stages - 2) x loads per tile) rather than
+    draining the ring; with 2 stages nothing younger exists at the wait."""
+    for bm, bn, stages in SHAPES:
+        events, info = gt.ring_trace(bm, bn, stages, 32)
+        waits = [e[1] for e in events if e[0] == "wait"]
+        steady = waits[1:32 - stages]
+        assert set(steady) == {(stages - 2) * info["loads_per_tile"]}, (bm, bn, stages, steady)
+        assert waits[-1] == 0  # the last tile: nothing younger
+
+
+def _load_golden():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "tvm_pipeline_depth2_ktiles5.txt")
+    rows = []
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, stage, ph_tma, ph_mma, pre = [p.strip() for p in line.split("|")]
+            rows.append((int(k), int(stage), int(ph_tma), int(ph_mma), None if pre == "-" else int(pre)))
+    return rows
+
+
+def test_tvm_pipeline_exercise_depth2_ktiles5():
+    """PIPE_DEPTH = 2, K_TILES = 5 (the default 256x256 kernel's 2-stage ring
+    over 5 K tiles): each K tile sits in the chapter's stage, the stage's fill
+    round has the parity of the chapter's phase_tma, and the tile prefetched
+    after each K tile frees its stage is the chapter's (none in the last two).
+    phase_mma has no counterpart here: the MFMA results are ordered by
+    register dependences, not by a barrier."""
+    golden = _load_golden()
+    assert [g[0] for g in golden] == list(range(5))
+    events, info = gt.ring_trace(256, 256, 2, 5)
+    replay(256, 256, 2, 5)
+    # stage of each K tile, from the operand reads
+    stage_of = {}
+    for kind, a, b, c, d in events:
+        if kind == "read":
+            stage_of.setdefault(a, set()).add(d)
+    # the K tile being consumed when each load is issued: the reads seen so
+    # far belong to K tile `cur`; a load issued after the barrier of tile k
+    # (while tile k+1's first operands are read) frees stage k
+    barriers = [i for i, e in enumerate(events) if e[0] == "barrier"]
+    # barrier 0 is the output-tile start, barrier 1 the prologue's; then one
+    # per K tile except the last
+    kbar = barriers[2:]
+    assert len(kbar) == 4
+    prefetch_after = {}
+    for k, bi in enumerate(kbar):
+        end = kbar[k + 1] if k + 1 < len(kbar) else len(events)
+        tiles = {e[1] for e in events[bi:end] if e[0] == "load" and e[2] == 0}
+        prefetch_after[k] = tiles
+    for k, stage, ph_tma, _ph_mma, pre in golden:
+        assert stage_of[k] == {stage}
+        assert (k // 2) % 2 == ph_tma  # the stage's fill round, mod 2
+        got = prefetch_after.get(k, set())
+        assert got == ({pre} if pre is not None else set()), (k, got, pre)
+
+
+def _replay_events(events, stages, ktu, info):
+    model = RingModel(stages, ktu, info)
+    for ev in events:
+        model.step(ev)
+    model.finish()
+
+
+def test_model_rejects_broken_schedules():
+    """The replay model must fail on plausible ring mistakes, each planted in
+    a copy of a real trace: a wait that lets the needed tile stay in flight,
+    a missing barrier, a refill issued before the barrier that frees its
+    stage, a read from the wrong stage, a dropped load."""
+    bm, bn, stages, ktu = 256, 128, 3, 8
+    events, info = gt.ring_trace(bm, bn, stages, ktu)
+    _replay_events(events, stages, ktu, info)  # the real trace passes
+    per = info["loads_per_tile"]
+    waits = [i for i, e in enumerate(events) if e[0] == "wait"]
+    barriers = [i for i, e in enumerate(events) if e[0] == "barrier"]
+    mutants = []
+    # 1. a steady-state wait one tile too lax
+    m = list(events)
+    i = waits[2]
+    m[i] = ("wait", m[i][1] + per, 0, 0, 0)
+    mutants.append(m)
+    # 2. the barrier of K tile 2 dropped
+    m = list(events)
+    del m[barriers[4]]
+    mutants.append(m)
+    # 3. the first load of a refill moved before the barrier that frees its stage
+    m = list(events)
+    j = next(i for i, e in enumerate(m) if e[0] == "load" and e[1] == stages + 1 and e[2] == 0)
+    b = max(i for i in barriers if i < j)
+    ev = m.pop(j)
+    m.insert(b, ev)
+    mutants.append(m)
+    # 4. a read from the wrong stage
+    m = list(events)
+    j = next(i for i, e in enumerate(m) if e[0] == "read" and e[1] == 4)
+    k, ks, r, st = m[j][1:]
+    m[j] = ("read", k, ks, r, (st + 1) % stages)
+    mutants.append(m)
+    # 5. one load of a tile dropped
+    m = list(events)
+    j = next(i for i, e in enumerate(m) if e[0] == "load" and e[1] == 5 and e[2] == 3)
+    del m[j]
+    mutants.append(m)
+    for n, m in enumerate(mutants, 1):
+        with pytest.raises(AssertionError):
+            _replay_events(m, stages, ktu, info)
