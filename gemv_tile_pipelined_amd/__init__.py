@@ -33,6 +33,7 @@ __all__ = [
     "gemm_bias_bf16",
     "gemm_splitk_f16",
     "gemm_splitk_bf16",
+    "gemm_splitk_f16_noalloc",
     "splitk_splits",
     "splitk_workspace_bytes",
     "ACT_NONE",
@@ -63,6 +64,7 @@ EXPORTED_SYMBOLS = (
     "gemm_bias_bf16",
     "gemm_splitk_f16",
     "gemm_splitk_bf16",
+    "gemm_splitk_f16_noalloc",
     "gemvtile_gemm_splitk_splits",
     "gemvtile_gemm_splitk_workspace",
     "gemvtile_status_string",
@@ -84,6 +86,7 @@ STATUS_NAMES = {
     2: "GEMVTILE_ERR_UNSUPPORTED",
     3: "GEMVTILE_ERR_LAUNCH",
     4: "GEMVTILE_ERR_DEVICE",
+    5: "GEMVTILE_ERR_SCRATCH",
 }
 
 
@@ -125,6 +128,8 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemm_splitk_f16.restype = c_int
     lib.gemm_splitk_bf16.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
     lib.gemm_splitk_bf16.restype = c_int
+    lib.gemm_splitk_f16_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.gemm_splitk_f16_noalloc.restype = c_int
     lib.gemvtile_gemm_splitk_splits.argtypes = [i64, i64, i64, i64]
     lib.gemvtile_gemm_splitk_splits.restype = c_int
     lib.gemvtile_gemm_splitk_workspace.argtypes = [i64, i64, i64, i64]
@@ -353,6 +358,17 @@ def gemm_splitk_f16(A, B, D=None, workspace=None, stream=None):
 def gemm_splitk_bf16(A, B, D=None, workspace=None, stream=None):
     """gemm_splitk_f16 on bfloat16 tensors."""
     return _gemm_splitk(A, B, D, workspace, stream, _torch().bfloat16, load_library().gemm_splitk_bf16)
+
+
+def gemm_splitk_f16_noalloc(A, B, D, stream=None):
+    """gemm_splitk_f16 without a workspace: the partial sums go to the
+    library's static 16 MiB scratch on the device (GemvTileError with
+    GEMVTILE_ERR_SCRATCH when a shape needs more).  D must be given: this
+    call allocates nothing.  Calls overlapping on one GPU race; order them
+    on one stream.  Enqueued on `stream`, not synchronised."""
+    if D is None:
+        raise ValueError("gemm_splitk_f16_noalloc allocates nothing: pass the output D")
+    return _gemm(A, B, D, stream, _torch().float16, load_library().gemm_splitk_f16_noalloc)
 
 
 def _gemv(x, W, y, stream, dtype, call):

@@ -208,9 +208,12 @@ int splitk_splits(int64_t M, int64_t N, int64_t K, int cus) {
   return gt::gemm_splitk_splits(M, N, K, cus);
 }
 
+// ws == nullptr with ws_bytes == -1: use the static scratch of
+// gemm_splitk_f16_noalloc instead of a caller's workspace.
 int run_gemm_splitk(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *ws,
                     int64_t ws_bytes, void *stream, int dtype) {
-  if (ws_bytes < 0) return GEMVTILE_ERR_INVALID_ARG;
+  const bool use_static = ws == nullptr && ws_bytes == -1;
+  if (ws_bytes < 0 && !use_static) return GEMVTILE_ERR_INVALID_ARG;
   bool noop = false;
   int st = check_gemm(A, B, D, M, N, K, &noop);
   if (st != GEMVTILE_OK || noop) return st;
@@ -219,8 +222,14 @@ int run_gemm_splitk(const void *A, const void *B, void *D, int64_t M, int64_t N,
   if (st != GEMVTILE_OK) return st;
   const int splits = K == 0 ? 1 : splitk_splits(M, N, K, cus);
   if (splits == 1) return run_gemm(A, B, D, M, N, K, stream, 0, dtype);
-  if (ws == nullptr || ws_bytes < static_cast<int64_t>(splits) * M * N * 4) return GEMVTILE_ERR_INVALID_ARG;
-  if (misaligned(ws, 16)) return GEMVTILE_ERR_UNSUPPORTED;
+  const int64_t need = static_cast<int64_t>(splits) * M * N * 4;
+  if (use_static) {
+    if (need > gt::kNoAllocScratchBytes) return GEMVTILE_ERR_SCRATCH;
+    if (gt::noalloc_scratch(&ws) != hipSuccess) return GEMVTILE_ERR_DEVICE;
+  } else {
+    if (ws == nullptr || ws_bytes < need) return GEMVTILE_ERR_INVALID_ARG;
+    if (misaligned(ws, 16)) return GEMVTILE_ERR_UNSUPPORTED;
+  }
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows)
@@ -239,6 +248,10 @@ int gemm_splitk_f16(const void *A, const void *B, void *D, int64_t M, int64_t N,
 int gemm_splitk_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *workspace,
                      int64_t workspace_bytes, void *stream) {
   return run_gemm_splitk(A, B, D, M, N, K, workspace, workspace_bytes, stream, gt::kBF16);
+}
+
+int gemm_splitk_f16_noalloc(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream) {
+  return run_gemm_splitk(A, B, D, M, N, K, nullptr, -1, stream, gt::kF16);
 }
 
 int64_t gemvtile_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int64_t num_cus) {
@@ -284,6 +297,9 @@ const char *gemvtile_status_string(int status) {
     case GEMVTILE_ERR_UNSUPPORTED: return "unsupported (K % 8 != 0, misaligned pointer, or a size beyond the limits)";
     case GEMVTILE_ERR_LAUNCH: return "kernel launch failed";
     case GEMVTILE_ERR_DEVICE: return "HIP device query failed";
+    case GEMVTILE_ERR_SCRATCH:
+      return "gemm_splitk_f16_noalloc: the split-K partial sums of this shape exceed its static scratch (16 MiB); "
+             "use gemm_splitk_f16 with a workspace";
     default: return "unknown status";
   }
 }

@@ -71,6 +71,7 @@
 //    and a second kernel adds the slices in order and rounds.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -772,6 +773,35 @@ hipError_t launch_gemm_splitk(int dtype, const void *A, const void *B, void *D, 
                            : launch_default<kF16, kEpiPartial>(A, B, D, M, N, K, num_cus, stream, nullptr, 0, w, splits);
   if (e != hipSuccess) return e;
   return launch_splitk_reduce(dtype, w, D, static_cast<int64_t>(M) * N, splits, stream);
+}
+
+// ---- static scratch of the non-allocating split-K entry point ------------
+// gemm_splitk_f16_noalloc keeps its FP32 partial sums here instead of in a
+// caller's workspace.  Each device the library runs on holds one copy of the
+// array, at its own address, until the process ends.  In host code the name
+// `scratch` is a host-side stand-in, not a device address: the kernels only
+// ever receive the address hipGetSymbolAddress returns for the current
+// device (noalloc_scratch below).
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> per_device[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = per_device[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // Once per device, with that device current (two threads racing here
+    // both obtain the same address).
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    per_device[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 // ---- the ring schedule on the host -------------------------------------

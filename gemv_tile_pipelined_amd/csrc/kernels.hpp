@@ -189,6 +189,11 @@ inline int skinny_splitk_splits(int64_t R, int64_t K, int num_cus) {
   return static_cast<int>((kt + per - 1) / per);  // drop slices that would be empty
 }
 
+// The static scratch of gemm_splitk_f16_noalloc (FP32 partial sums,
+// [splits][M][N]) and the device address of the current device's copy of it.
+constexpr int64_t kNoAllocScratchBytes = int64_t{16} << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 // s_waitcnt immediate for "lgkmcnt(0)" alone on gfx9-family targets
 // (vmcnt field [3:0]|[15:14] = 63, expcnt [6:4] = 7, lgkmcnt [11:8] = 0).
 // Issued through the builtin so the compiler knows the LDS reads are done.

@@ -37,7 +37,8 @@ enum gemvtile_status {
     GEMVTILE_ERR_INVALID_ARG = 1, /* NULL pointer with a nonzero extent, negative size */
     GEMVTILE_ERR_UNSUPPORTED = 2, /* K % 8 != 0, misaligned pointer, size beyond the limits below */
     GEMVTILE_ERR_LAUNCH = 3,      /* the HIP launch failed (no gfx950 device, bad stream, ...) */
-    GEMVTILE_ERR_DEVICE = 4       /* a HIP runtime query failed */
+    GEMVTILE_ERR_DEVICE = 4,      /* a HIP runtime query failed */
+    GEMVTILE_ERR_SCRATCH = 5      /* gemm_splitk_f16_noalloc: partial sums beyond its static scratch */
 };
 
 /*
@@ -195,6 +196,30 @@ int gemm_splitk_f16(const void *A, const void *B, void *D, int64_t M, int64_t N,
                     int64_t workspace_bytes, void *stream);
 int gemm_splitk_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *workspace,
                      int64_t workspace_bytes, void *stream);
+
+/*
+ * gemm_splitk_f16_noalloc -- gemm_splitk_f16 for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument, and no
+ * allocation of any kind on the call path.  Same result, rounding and
+ * determinism as gemm_splitk_f16 (the same kernels, in the same order).
+ *
+ * The FP32 partial sums go to a static device array of 16 MiB
+ * (splits * M * N * 4 bytes are needed, see gemvtile_gemm_splitk_workspace)
+ * that the library holds on each device it runs on until the process ends.
+ * Shapes split only while their tiles (128x128 whenever they split) leave
+ * compute units idle, and tiles * splits <= #CUs, so on parts with up to
+ * 256 compute units every shape fits; a shape that needs more (on a larger
+ * part) returns GEMVTILE_ERR_SCRATCH before any launch (use
+ * gemm_splitk_f16 with a workspace then).  Shapes that do not split run
+ * exactly as gemm_f16 and need none.  Every partial sum the reduction reads
+ * is written by the same call, so the array needs no clearing; it keeps the
+ * last call's contents.  All calls on one device share its one array:
+ * calls that overlap on one GPU (on different streams, or from different
+ * host threads without ordering) race and give undefined results; order
+ * them on one stream.  Returns a gemvtile_status.
+ */
+int gemm_splitk_f16_noalloc(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
  * gemvtile_gemm_splitk_splits / gemvtile_gemm_splitk_workspace -- the number

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert gt.status_string(code)
     assert gt.status_string(99) == "unknown status"
 
@@ -362,6 +362,36 @@ def test_gemm_splitk_argument_validation(lib):
         assert fn(FAKE, FAKE, FAKE, -1, 4, 8, FAKE, 0, None) == INVALID
         assert fn(FAKE, FAKE, FAKE, 4, 4, 12, FAKE, 0, None) == UNSUPPORTED
         assert fn(None, None, None, 0, 4, 8, None, 0, None) == OK
+
+
+def test_gemm_splitk_noalloc_argument_validation(lib):
+    """The non-allocating split-K entry point checks its arguments like
+    gemm_splitk_f16, before any HIP call."""
+    fn = lib.gemm_splitk_f16_noalloc
+    assert fn(FAKE, FAKE, FAKE, -1, 4, 8, None) == INVALID
+    assert fn(FAKE, FAKE, None, 4, 4, 8, None) == INVALID
+    assert fn(FAKE, FAKE, FAKE, 4, 4, 12, None) == UNSUPPORTED
+    assert fn(FAKE + 8, FAKE, FAKE, 4, 4, 8, None) == UNSUPPORTED
+    assert fn(None, None, None, 0, 4, 8, None) == OK
+    assert "16 MiB" in gt.status_string(5)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def test_noalloc_scratch_covers_every_split_on_256_cus():
+    """Split-K shapes take 128x128 tiles and tiles x splits <= #CUs, so on
+    256 compute units no shape needs more than the 16 MiB static scratch of
+    gemm_splitk_f16_noalloc; a larger part can (hence its size check)."""
+    sizes = [1, 2, 15, 16, 17, 33, 64, 100, 128, 129, 255, 256, 300, 384, 512, 640, 768, 1000, 1024, 1280, 1536,
+             2000, 2048, 3000, 4096, 8192]
+    worst = 0
+    for M in sizes:
+        for N in sizes:
+            for K in (1024, 4104, 14336, 65536, 1 << 20):
+                worst = max(worst, gt.splitk_workspace_bytes(M, N, K, 256))
+    assert 0 < worst <= NOALLOC_SCRATCH_BYTES
+    assert gt.splitk_workspace_bytes(1024, 1024, 14336, 512) > NOALLOC_SCRATCH_BYTES
 
 
 def test_measurement_formulas_match_table1():
