@@ -26,15 +26,22 @@ Prints ONE JSON line on stdout:
                steps, so both see one clock state
   decode_batch the 8x4096x14336 GEMM (skinny path) in GB/s, timed on its own
   bf16         gemm_bf16 at 4096^3 and gemv_bf16 at 4096x14336
+  clock        the engine clock and socket power sampled (amdsmi, read-only)
+               while back-to-back gemm_f16 4096^3 launches run on the uniform
+               inputs and then on all-zero inputs of the same shape: the
+               part's power limit sets the clock the MFMAs run at
   cpu_baseline the CPU oracle (FP64, OpenMP) on a bounded sample of the same
                workloads: the 4096^3 GEMM (rows sized to the time budget), the
                ragged GEMM in full, the 8192^3 GEMM on its 64 seeded rows and
                the GEMV in full
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 2000] [--settle-s 0.5]
-                       [--only gemm|gemv|decode|bf16|configs|vendor]
---only runs the steps (or, for decode/bf16/configs/vendor, that section
-alone after the same settle phase) and prints the line without the other
-sections; it exists so that profiler runs time one kernel family at a time.
+                       [--only gemm|gemv|decode|bf16|configs|vendor|clock|copy]
+--only runs the steps (or, for decode/bf16/configs/vendor/clock, that
+section alone after the same settle phase) and prints the line without the
+other sections; it exists so that profiler runs time one kernel family at a
+time.  --only copy runs nothing of the library: 20 device-to-device copies of
+a 256 MiB buffer, the known-size reference that hardware traffic counters
+are calibrated against.
 """
 from __future__ import annotations
 
@@ -64,8 +71,8 @@ CONFIG_REPS = {0: 200, 2: 50, 4: 10}  # timed launches per extra workload
 MEASURED_TRAFFIC = {
     "sources_sha256": None,
 }
-KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemv.hip", "kernels.hpp", "ring.hpp", "skinny.hip",
-                  "tile_order.hpp")
+KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemm_kernel.hpp", "gemm_plain.hip", "gemv.hip", "kernels.hpp",
+                  "ring.hpp", "skinny.hip", "tile_order.hpp")
 
 
 def kernel_sources_sha256() -> str:
@@ -89,7 +96,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--settle-s", type=float, default=0.5, help="seconds of untimed steps before the warm-up steps")
     p.add_argument("--cpu-seconds", type=float, default=8.0, help="target CPU time of the 4096^3 oracle sample")
-    p.add_argument("--only", choices=("gemm", "gemv", "decode", "bf16", "configs", "vendor"), default=None)
+    p.add_argument("--only", choices=("gemm", "gemv", "decode", "bf16", "configs", "vendor", "clock", "copy"),
+                   default=None)
+    p.add_argument("--clock-s", type=float, default=1.0, help="seconds of sampled load per data set in the clock section")
     return p.parse_args()
 
 
@@ -180,6 +189,93 @@ def _cpu_model():
     return None
 
 
+class ClockSampler:
+    """Samples the GPU's engine clocks and socket power through amdsmi (the
+    ROCm system-management library; read-only queries) in a background
+    thread."""
+
+    def __init__(self, device_index=0, period_s=0.005):
+        import threading
+
+        import amdsmi
+
+        self.amdsmi = amdsmi
+        amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+        self.handle = amdsmi.amdsmi_get_processor_handles()[device_index]
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        one = m.get("current_gfxclk")
+        if not clks and isinstance(one, (int, float)) and 0 < one < 10000:
+            clks = [one]
+        power = m.get("current_socket_power")
+        if not isinstance(power, (int, float)) or power <= 0 or power > 100000:
+            power = m.get("average_socket_power")
+        return {"clks": clks, "power": power if isinstance(power, (int, float)) and 0 < power < 100000 else None}
+
+    def _run(self):
+        import time as _t
+
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self.read())
+            except Exception as e:  # a failing query ends the sampling, not the bench
+                self.samples.append({"error": repr(e)})
+                return
+            _t.sleep(self.period)
+
+    def start(self):
+        self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join()
+        return self.samples
+
+    def power_cap_w(self):
+        try:
+            info = self.amdsmi.amdsmi_get_power_cap_info(self.handle)
+            cap = info.get("power_cap")
+            return cap / 1e6 if isinstance(cap, (int, float)) and cap > 1e5 else cap
+        except Exception:
+            return None
+
+    def close(self):
+        try:
+            self.amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
+def summarize_clock(samples):
+    import numpy as np
+
+    good = [x for x in samples if "clks" in x and x["clks"]]
+    if not good:
+        return {"samples": len(samples), "error": next((x["error"] for x in samples if "error" in x), "no clock data")}
+    # drop the first tenth (the load ramping up)
+    good = good[len(good) // 10:]
+    per_xcd = np.array([x["clks"] for x in good if len(x["clks"]) == len(good[0]["clks"])], dtype=float)
+    mean_clk = per_xcd.mean(axis=1)
+    pw = np.array([x["power"] for x in good if x["power"] is not None], dtype=float)
+    out = {
+        "samples": len(good),
+        "gfxclk_mhz_mean": round(float(mean_clk.mean()), 1),
+        "gfxclk_mhz_min": round(float(mean_clk.min()), 1),
+        "gfxclk_mhz_max": round(float(mean_clk.max()), 1),
+        "per_xcd_mhz_mean": [round(float(v), 1) for v in per_xcd.mean(axis=0)],
+    }
+    if pw.size:
+        out["socket_power_w_mean"] = round(float(pw.mean()), 1)
+        out["socket_power_w_max"] = round(float(pw.max()), 1)
+    return out
+
+
 def us_stats(ms, per=1):
     import numpy as np
 
@@ -219,6 +315,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     only = args.only
+    if only == "copy":
+        nbytes = 256 << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"metric": METRIC, "value": None, "only": "copy", "copy_bytes": nbytes, "copies": 20}))
+        return
     want = (lambda s: only is None or only == s)
 
     # ---- inputs, resident in HBM before timing --------------------------
@@ -495,6 +600,57 @@ def main():
             "gemv_traffic": traffic("gemv_bf16"),
         }
         del gemv_b, Wb, Ab, Bb, Db
+
+    # ---- the engine clock under sustained GEMM load ---------------------
+    if want("clock"):
+        clock = {"method": "amdsmi gpu metrics (current per-XCD gfx clock, socket power) sampled every 5 ms in a "
+                           "thread while gemm_f16 4096^3 runs back to back; the first tenth of the samples dropped"}
+        try:
+            zero_A = torch.zeros((M, K), dtype=torch.float16, device=dev)
+            zero_B = torch.zeros((N, K), dtype=torch.float16, device=dev)
+            zero_D = torch.empty((M, N), dtype=torch.float16, device=dev)
+            for name, operands in (("uniform", [(A_, B_, D_) for A_, B_, D_ in gemm_sets]),
+                                   ("zero", [(zero_A, zero_B, zero_D)])):
+                def one(i, operands=operands):
+                    A_, B_, D_ = operands[i % len(operands)]
+                    check(gt.gemm_f16_ptr(A_.data_ptr(), B_.data_ptr(), D_.data_ptr(), M, N, K, sh))
+
+                for i in range(SECTION_WARMUP):
+                    one(i)
+                torch.cuda.synchronize(dev)
+                sampler = ClockSampler()
+                sampler.start()
+                t_end = time.perf_counter() + args.clock_s
+                n = 0
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                while time.perf_counter() < t_end:
+                    for _ in range(50):
+                        one(n)
+                        n += 1
+                    torch.cuda.synchronize(dev)
+                e1.record(stream)
+                torch.cuda.synchronize(dev)
+                samples = sampler.stop()
+                cap = sampler.power_cap_w()
+                sampler.close()
+                us = e0.elapsed_time(e1) * 1e3 / n
+                clock[name] = {**summarize_clock(samples), "launches": n, "us_per_launch": round(us, 2),
+                               "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
+                if cap is not None:
+                    clock["power_cap_w"] = cap
+            del zero_A, zero_B, zero_D
+            # MFMA-only clock ceiling: at f MHz the dense fp16 peak is
+            # CUs x 4096 flop x f
+            cus = gt.device_caps()["num_cus"]
+            for name in ("uniform", "zero"):
+                c = clock.get(name, {})
+                if "gfxclk_mhz_mean" in c:
+                    c["mfma_peak_at_this_clock_tflops"] = round(cus * 4096 * c["gfxclk_mhz_mean"] * 1e6 / 1e12, 1)
+                    c["frac_of_peak_at_this_clock"] = round(c["tflops"] / c["mfma_peak_at_this_clock_tflops"], 4)
+        except Exception as e:  # the clock evidence is optional; the bench line is not
+            clock["error"] = repr(e)
+        line["clock"] = clock
 
     # The part's own compute peak, for context next to the published one the
     # rooflines use: dense fp16 MFMA = CUs x 4096 flop per clock at the peak

@@ -158,7 +158,7 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemvtile_gemv_grid.restype = i64
     lib.gemvtile_device_caps.argtypes = [intp] * 4
     lib.gemvtile_device_caps.restype = c_int
-    lib.gemvtile_ring_trace.argtypes = [c_int, c_int, c_int, i64, ctypes.POINTER(ctypes.c_int32), i64, intp]
+    lib.gemvtile_ring_trace.argtypes = [c_int, i64, ctypes.POINTER(ctypes.c_int32), i64, intp]
     lib.gemvtile_ring_trace.restype = i64
     if path == LIBRARY_PATH:
         _lib = lib
@@ -455,21 +455,22 @@ def gemv_grid(N: int, num_cus: int) -> int:
 RING_EVENTS = {1: "load", 2: "wait", 3: "lds_wait", 4: "barrier", 5: "read", 6: "mfma"}
 
 
-def ring_trace(bm: int, bn: int, stages: int, ktu: int):
-    """The tiled GEMM kernel's K-loop schedule over ktu K tiles (host-only):
-    (events, info) with events a list of (name, a, b, c, d) tuples as
-    gemvtile_ring_trace describes, info = {"loads_per_tile", "reads_per_step",
-    "ksteps", "mfma_per_step"}."""
+def ring_trace(variant: int, ktu: int):
+    """The K-loop schedule of tiled GEMM variant `variant` over ktu K tiles
+    (host-only): (events, info) with events a list of (name, a, b, c, d)
+    tuples as gemvtile_ring_trace describes, info = {"loads_per_tile",
+    "reads_per_step", "ksteps", "mfma_per_step", "stages", "bm", "bn",
+    "early_free"}."""
     lib = load_library()
-    info = (ctypes.c_int * 4)()
-    n = int(lib.gemvtile_ring_trace(bm, bn, stages, ktu, None, 0, info))
+    info = (ctypes.c_int * 8)()
+    n = int(lib.gemvtile_ring_trace(variant, ktu, None, 0, info))
     if n < 0:
-        raise GemvTileError(1, f"no tiled kernel with a {bm}x{bn} tile and {stages} stages, or ktu out of range")
+        raise GemvTileError(1, f"tiled variant {variant} has no multi-stage ring, or ktu is out of range")
     buf = (ctypes.c_int32 * (5 * max(n, 1)))()
-    n2 = int(lib.gemvtile_ring_trace(bm, bn, stages, ktu, buf, n, info))
+    n2 = int(lib.gemvtile_ring_trace(variant, ktu, buf, n, info))
     assert n2 == n
     events = [(RING_EVENTS[buf[5 * i]], buf[5 * i + 1], buf[5 * i + 2], buf[5 * i + 3], buf[5 * i + 4]) for i in range(n)]
-    keys = ("loads_per_tile", "reads_per_step", "ksteps", "mfma_per_step")
+    keys = ("loads_per_tile", "reads_per_step", "ksteps", "mfma_per_step", "stages", "bm", "bn", "early_free")
     return events, dict(zip(keys, list(info)))
 
 

@@ -39,7 +39,7 @@ import tempfile
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in ("api.hip", "gemm.hip", "gemm_ws.hip", "gemv.hip", "skinny.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("api.hip", "gemm.hip", "gemm_plain.hip", "gemm_ws.hip", "gemv.hip", "skinny.hip")]
 LIBRARY = os.path.join(PKG_DIR, "libgemvtile.so")
 ARCH = "gfx950"
 

@@ -313,11 +313,10 @@ int gemvtile_tile_coord(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t gro
   return GEMVTILE_OK;
 }
 
-int64_t gemvtile_ring_trace(int bm, int bn, int stages, int64_t ktu, int32_t *events, int64_t cap, int *info) {
+int64_t gemvtile_ring_trace(int variant, int64_t ktu, int32_t *events, int64_t cap, int *info) {
   if (ktu < 1 || ktu > (int64_t{1} << 20) || cap < 0 || (events == nullptr && cap > 0)) return -1;
-  int dummy[4];
-  int *o = info != nullptr ? info : dummy;
-  return gt::ring_trace(bm, bn, stages, static_cast<int>(ktu), events, cap, &o[0], &o[1], &o[2], &o[3]);
+  int dummy[8];
+  return gt::ring_trace(variant, static_cast<int>(ktu), events, cap, info != nullptr ? info : dummy);
 }
 
 int64_t gemvtile_xcd_logical_id(int64_t w, int64_t grid) {

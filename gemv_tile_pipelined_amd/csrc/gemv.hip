@@ -87,36 +87,49 @@ __device__ inline float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-// Reduce the ROWS partial sums of a wave and store row r's total from lane r.
-template <int ROWS, int DT>
-__device__ inline void store_row_sums(const float (&acc)[ROWS], int lane, int64_t row0, int N, _Float16 *y) {
-  float sums[ROWS];
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r) sums[r] = wave_sum(acc[r]);
-  float mine = sums[0];
-#pragma unroll
-  for (int r = 1; r < ROWS; ++r) mine = (lane == r) ? sums[r] : mine;
-  if (lane < ROWS && row0 + lane < N) y[row0 + lane] = round_out<DT>(mine);
+// Rows of W a wave works on.  ROWMAP 0: workgroup b owns the kRows
+// consecutive rows starting at b * kRows, and its row group g (of ROWS rows)
+// the ROWS consecutive rows g * ROWS .. of those.  ROWMAP 1 (grid-strided):
+// workgroup b owns rows b, b + G, b + 2G, ... (G = the grid size), so the
+// workgroups running side by side read adjacent rows -- one contiguous
+// front through W, as a plain read stream would -- instead of regions
+// kRows rows apart.
+template <int ROWMAP, int ROWS>
+__device__ inline int64_t wave_row(int group, int r, int rows_per_wg) {
+  const int local = group * ROWS + r;
+  if constexpr (ROWMAP == 0) return static_cast<int64_t>(blockIdx.x) * rows_per_wg + local;
+  else return static_cast<int64_t>(local) * gridDim.x + blockIdx.x;
 }
 
-// WPOL >= 0: W is read with buffer loads carrying that cache-policy operand
-// (gfx950: 1 = sc0, 2 = nt, 16 = sc1; one descriptor per row, so the 32-bit
-// offsets cover any K) instead of global loads.
+// XLDS: x is staged in LDS once per workgroup (K <= kGemvXldsMaxK) and each
+// wave reads its chunks from there, instead of every wave loading x from the
+// caches alongside its rows of W.
+constexpr int kGemvXldsMaxK = 16384;
+
 template <int ROWS, int WAVES, int UNROLL, bool NONTEMPORAL, bool ROTATE = false, int DT = kF16, int KSPLIT = 1,
-          int WPOL = -1>
+          int ROWMAP = 0, bool XLDS = false>
 __global__ void __launch_bounds__(WAVES * 64)
 gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Float16 *__restrict__ y, int N,
                 int K) {
   static_assert(KSPLIT >= 1 && WAVES % KSPLIT == 0, "K slices divide the waves");
   constexpr int kRowGroups = WAVES / KSPLIT;
+  constexpr int kRows = kRowGroups * ROWS;  // rows per workgroup
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slice = wave % KSPLIT;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * kRowGroups + wave / KSPLIT) * ROWS;
-  if constexpr (KSPLIT == 1) {
-    if (row0 >= N) return;  // wave-uniform
-  }
+  const int group = wave / KSPLIT;
   const int chunks = K >> 3;
+  const half8_t *xv = reinterpret_cast<const half8_t *>(x);
+  __shared__ half8_t x_lds[XLDS ? kGemvXldsMaxK / 8 : 1];
+  if constexpr (XLDS) {
+    // every wave takes part, before any wave may leave
+    for (int c = threadIdx.x; c < chunks; c += WAVES * 64) x_lds[c] = xv[c];
+    __syncthreads();
+  }
+  const int64_t first_row = wave_row<ROWMAP, ROWS>(group, 0, kRows);
+  if constexpr (KSPLIT == 1) {
+    if (first_row >= N) return;  // wave-uniform; later rows of the wave are past N too
+  }
   // This wave's chunks [c_begin, c_end): all of K, or its slice, cut on
   // 64-chunk steps (steps * slice / KSPLIT is below steps, so c_begin < chunks).
   // A row group wholly past N (last workgroup only) walks nothing but still
@@ -126,20 +139,16 @@ gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Flo
     const int steps = (chunks + 63) >> 6;
     c_begin = (steps * slice / KSPLIT) * 64;
     c_end = min(chunks, (steps * (slice + 1) / KSPLIT) * 64);
-    if (row0 >= N) c_end = c_begin;
+    if (first_row >= N) c_end = c_begin;
   }
-  const half8_t *xv = reinterpret_cast<const half8_t *>(x);
   const half8_t *wrow[ROWS];
-  __amdgpu_buffer_rsrc_t wrsrc[ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     // Rows past N re-read the last row (always valid memory); their sums
     // are never stored.
-    const int64_t row = (row0 + r < N) ? row0 + r : static_cast<int64_t>(N) - 1;
+    int64_t row = wave_row<ROWMAP, ROWS>(group, r, kRows);
+    if (row >= N) row = static_cast<int64_t>(N) - 1;
     wrow[r] = reinterpret_cast<const half8_t *>(W + row * K);
-    if constexpr (WPOL >= 0)
-      wrsrc[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16 *>(W + row * K), 0,
-                                                   static_cast<int>(static_cast<uint32_t>(K) * 2u), 0x00020000);
   }
 
   float acc[ROWS];
@@ -150,22 +159,17 @@ gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Flo
   // issued before the first product, so a lane has UNROLL*(ROWS+1) 16-byte
   // loads in flight.  Whole groups need no bounds test; the ragged rest of
   // the row (fewer than 64*UNROLL chunks) is one guarded group at the end.
-  auto group = [&](int base, bool guarded) {
+  auto group_step = [&](int base, bool guarded) {
     half8_t xs[UNROLL];
     half8_t ws[UNROLL][ROWS];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int c = base + u * 64 + lane;
       if (!guarded || c < c_end) {
-        xs[u] = xv[c];
+        if constexpr (XLDS) xs[u] = x_lds[c];
+        else xs[u] = xv[c];
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          if constexpr (WPOL >= 0)
-            ws[u][r] = __builtin_bit_cast(
-                half8_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc[r], static_cast<uint32_t>(c) * 16u, 0, WPOL));
-          else
-            ws[u][r] = NONTEMPORAL ? __builtin_nontemporal_load(wrow[r] + c) : wrow[r][c];
-        }
+        for (int r = 0; r < ROWS; ++r) ws[u][r] = NONTEMPORAL ? __builtin_nontemporal_load(wrow[r] + c) : wrow[r][c];
       } else {
         xs[u] = half8_t{};
 #pragma unroll
@@ -184,45 +188,48 @@ gemv_kernel(const _Float16 *__restrict__ x, const _Float16 *__restrict__ W, _Flo
   constexpr int kGroup = 64 * UNROLL;
   const int span = c_end - c_begin;
   const int full = span / kGroup;
-  int g = (ROTATE && full > 0) ? static_cast<int>((row0 / ROWS) % full) : 0;
+  const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * kRowGroups + group;
+  int g = (ROTATE && full > 0) ? static_cast<int>(wave_id % full) : 0;
   for (int it = 0; it < full; ++it) {
-    group(c_begin + g * kGroup, false);
+    group_step(c_begin + g * kGroup, false);
     if (++g == full) g = 0;
   }
-  if (full * kGroup < span) group(c_begin + full * kGroup, true);
+  if (full * kGroup < span) group_step(c_begin + full * kGroup, true);
+
+  // Row sums: DPP reductions inside the wave; lane r < ROWS holds row r's.
+  float sums[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) sums[r] = wave_sum(acc[r]);
+  float mine = sums[0];
+#pragma unroll
+  for (int r = 1; r < ROWS; ++r) mine = (lane == r) ? sums[r] : mine;
+  const int64_t my_row = wave_row<ROWMAP, ROWS>(group, lane < ROWS ? lane : 0, kRows);
   if constexpr (KSPLIT == 1) {
-    store_row_sums<ROWS, DT>(acc, lane, row0, N, y);
+    if (lane < ROWS && my_row < N) y[my_row] = round_out<DT>(mine);
   } else {
     // Each slice's row sums go to LDS; the slice-0 wave of the row group adds
     // them in slice order and stores the rounded total.
     __shared__ float part[kRowGroups][ROWS][KSPLIT];
-    float sums[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) sums[r] = wave_sum(acc[r]);
-    const int rg = wave / KSPLIT;
-    if (lane < ROWS) {
-      float mine = sums[0];
-#pragma unroll
-      for (int r = 1; r < ROWS; ++r) mine = (lane == r) ? sums[r] : mine;
-      part[rg][lane][slice] = mine;
-    }
+    if (lane < ROWS) part[group][lane][slice] = mine;
     __syncthreads();
-    if (slice == 0 && lane < ROWS && row0 + lane < N) {
-      float total = part[rg][lane][0];
+    if (slice == 0 && lane < ROWS && my_row < N) {
+      float total = part[group][lane][0];
 #pragma unroll
-      for (int s2 = 1; s2 < KSPLIT; ++s2) total += part[rg][lane][s2];
-      y[row0 + lane] = round_out<DT>(total);
+      for (int s2 = 1; s2 < KSPLIT; ++s2) total += part[group][lane][s2];
+      y[my_row] = round_out<DT>(total);
     }
   }
 }
 
-template <int ROWS, int WAVES, int UNROLL, bool NT, bool ROT = false, int DT = kF16, int KSPLIT = 1, int WPOL = -1>
+template <int ROWS, int WAVES, int UNROLL, bool NT, bool ROT = false, int DT = kF16, int KSPLIT = 1, int ROWMAP = 0,
+          bool XLDS = false>
 static hipError_t launch(const void *x, const void *W, void *y, int N, int K, hipStream_t stream) {
+  if (XLDS && K > kGemvXldsMaxK) return hipErrorInvalidValue;
   const int64_t rows_per_block = static_cast<int64_t>(ROWS) * WAVES / KSPLIT;
   const int64_t grid = (N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((gemv_kernel<ROWS, WAVES, UNROLL, NT, ROT, DT, KSPLIT, WPOL>), dim3(static_cast<unsigned>(grid)),
-                     dim3(WAVES * 64), 0, stream, static_cast<const _Float16 *>(x), static_cast<const _Float16 *>(W),
-                     static_cast<_Float16 *>(y), N, K);
+  hipLaunchKernelGGL((gemv_kernel<ROWS, WAVES, UNROLL, NT, ROT, DT, KSPLIT, ROWMAP, XLDS>),
+                     dim3(static_cast<unsigned>(grid)), dim3(WAVES * 64), 0, stream, static_cast<const _Float16 *>(x),
+                     static_cast<const _Float16 *>(W), static_cast<_Float16 *>(y), N, K);
   return hipGetLastError();
 }
 
@@ -254,6 +261,25 @@ hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, i
     case 10: return launch<2, 8, 4, true, true, kF16, 4>(x, W, y, N, K, stream);
     case 11: return launch<2, 8, 4, true, true, kF16, 8>(x, W, y, N, K, stream);
     case 12: return launch<1, 8, 4, true, true, kF16, 8>(x, W, y, N, K, stream);
+    // grid-strided rows; x staged in LDS; deeper unroll; other wave shapes
+    case 20: return launch<2, 8, 4, true, true, kF16, 1, 1>(x, W, y, N, K, stream);
+    case 21: return launch<2, 8, 4, true, true, kF16, 1, 0, true>(x, W, y, N, K, stream);
+    case 22: return launch<2, 8, 4, true, true, kF16, 1, 1, true>(x, W, y, N, K, stream);
+    case 23: return launch<2, 8, 8, true, true, kF16, 1, 1>(x, W, y, N, K, stream);
+    case 24: return launch<4, 4, 4, true, true, kF16, 1, 1>(x, W, y, N, K, stream);
+    case 25: return launch<1, 16, 4, true, true, kF16, 1, 1>(x, W, y, N, K, stream);
+    case 26: return launch<4, 4, 4, true, true, kF16, 1, 1, true>(x, W, y, N, K, stream);
+    case 27: return launch<2, 8, 4, true, false, kF16, 1, 1>(x, W, y, N, K, stream);
+    // no rotated start: deeper / shallower unroll, other wave shapes, K splits
+    case 28: return launch<2, 8, 8, true, false>(x, W, y, N, K, stream);
+    case 29: return launch<4, 4, 4, true, false>(x, W, y, N, K, stream);
+    case 30: return launch<2, 8, 2, true, false>(x, W, y, N, K, stream);
+    case 31: return launch<1, 8, 4, true, false>(x, W, y, N, K, stream);
+    case 32: return launch<2, 8, 4, true, false, kF16, 2>(x, W, y, N, K, stream);
+    case 33: return launch<2, 8, 4, true, false, kF16, 4>(x, W, y, N, K, stream);
+    case 34: return launch<2, 8, 4, true, false, kF16, 8>(x, W, y, N, K, stream);
+    case 35: return launch<1, 8, 4, true, false, kF16, 8>(x, W, y, N, K, stream);
+    case 36: return launch<4, 8, 4, true, false>(x, W, y, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }

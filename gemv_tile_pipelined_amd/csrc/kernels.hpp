@@ -23,8 +23,8 @@ constexpr int kGemmGroupM = 8;
 // gemvtile_gemm_f16_variant numbers of the tiled kernel: 0 (the default)
 // and the ablations of gemm.hip.  Numbers of ablations that were measured and
 // not kept stay unused.
-constexpr int kGemmVariants = 28;
-inline bool gemm_variant_exists(int v) { return (v >= 0 && v <= 3) || v == 10 || (v >= 20 && v <= 27); }
+constexpr int kGemmVariants = 37;
+inline bool gemm_variant_exists(int v) { return (v >= 0 && v <= 3) || v == 10 || (v >= 20 && v <= 27) || (v >= 30 && v <= 36); }
 
 // Output tile of the tiled GEMM.  The 256x256 default needs about one tile
 // per CU to fill the chip; outputs that give fewer take smaller tiles, each
@@ -94,7 +94,7 @@ inline int gemm_splitk_splits(int64_t M, int64_t N, int64_t K, int num_cus) {
   return saved >= cost ? static_cast<int>(splits) : 1;
 }
 // gemvtile_gemv_f16_variant numbers of the GEMV kernel's launch shapes.
-inline bool gemv_variant_exists(int v) { return v == 0 || (v >= 6 && v <= 12); }
+inline bool gemv_variant_exists(int v) { return v == 0 || (v >= 6 && v <= 12) || (v >= 20 && v <= 36); }
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip).
 constexpr int kSkinnyMaxRows = 16;
@@ -122,10 +122,10 @@ inline bool skinny_wide_route(int64_t M, int64_t N, int num_cus) {
 // and not kept stay unused.
 constexpr int kSkinnyVariantBase = 100;
 constexpr int kGemmWsVariantBase = 200;
-inline bool skinny_variant_exists(int v) { return v == 0 || v == 4 || v == 12 || v == 30 || v == 47; }
+inline bool skinny_variant_exists(int v) { return v == 0 || v == 4 || v == 12 || v == 30 || v == 47 || v == 48; }
 // Wave-specialised (producer / consumer) GEMM launch shapes (gemm_ws.hip).
 constexpr int kGemmWsVariants = 2;
-static_assert(kGemmVariants <= kSkinnyVariantBase && kSkinnyVariantBase + 48 <= kGemmWsVariantBase,
+static_assert(kGemmVariants <= kSkinnyVariantBase && kSkinnyVariantBase + 49 <= kGemmWsVariantBase,
               "variant families must not overlap");
 
 // The default GEMV launch for N rows on a device with num_cus compute units:
@@ -199,15 +199,15 @@ hipError_t noalloc_scratch(void **ptr);
 // Issued through the builtin so the compiler knows the LDS reads are done.
 constexpr unsigned kWaitLgkm0 = 0xC07F;
 
-// The K-loop schedule of the tiled GEMM kernel with a bm x bn output tile and
-// a ring of `stages` stages over ktu K tiles, as the host-side trace of the
-// ring walker (ring.hpp): up to `cap` events of five int32 each are written
-// to `events` (which may be NULL); returns the number of events, or -1 when
-// the library has no kernel of that shape.  The other outputs (each may be
-// NULL) receive the kernel's loads per wave per K tile, operand reads and
-// MFMAs per wave per K step, and K steps per K tile.
-int64_t ring_trace(int bm, int bn, int stages, int ktu, int32_t *events, int64_t cap, int *loads_per_tile,
-                   int *reads_per_step, int *ksteps, int *mfma_per_step);
+// The K-loop schedule of tiled GEMM variant `variant` (a
+// gemvtile_gemm_f16_variant number whose kernel has a multi-stage ring) over
+// ktu K tiles, as the host-side trace of the ring walker (ring.hpp): up to
+// `cap` events of five int32 each are written to `events` (which may be
+// NULL); returns the number of events, or -1 for a variant without a ring.
+// info[0..7] receive the kernel's loads per wave per K tile, operand reads
+// and MFMAs per wave per K step, K steps per K tile, ring stages, bm, bn and
+// whether it runs the early-free schedule (1) or not (0).
+int64_t ring_trace(int variant, int ktu, int32_t *events, int64_t cap, int *info);
 hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                            hipStream_t stream);
 hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K,

@@ -187,6 +187,115 @@ GT_RING_INLINE void ring_k_loop(Ops &ops, int ktu) {
   ring_ktile<S, false, false, false>(ops, kt, ktu);                                  // last K tile
 }
 
+// ---- the early-free schedule -------------------------------------------
+// The loop above has one barrier per K tile, which does two jobs at once:
+// every wave is done reading stage kt (so it may be refilled) and tile kt+1
+// has landed (so it may be read).  With two stages the refill of stage kt
+// then has one K tile of MFMA slots, minus its own issue span, before the
+// barrier that needs it.  The early-free schedule (S::EARLY_FREE) splits the
+// two jobs: a "free" barrier in K step 0 of tile kt, at slot S::WAR_AT, once
+// the wave has read all of stage kt (K step 1's operands are read during K
+// step 0), starts the refill of stage kt with tile kt + STAGES there; the
+// "landed" barrier stays where it was, in the last K step.  The refill
+// starts about half a K tile earlier and the wait for a tile leaves the
+// next tile's loads in flight, at the price of a second barrier per K tile.
+// The prologue issues tiles 0 .. STAGES-1 at once (every stage is free at
+// the start of an output tile).
+template <class S>
+struct RingEarly {
+  static constexpr int kBarrierAt = S::kMfma - S::kReads * S::READ_STRIDE;  // landed barrier, last K step
+  static constexpr int kRawPos = (S::kKSub - 1) * S::kMfma + kBarrierAt;    // ... counted from the tile start
+  static constexpr int kTileSlots = S::kKSub * S::kMfma;
+  static constexpr int kLastLoad = S::WAR_AT + S::DMA_OFFSET + (S::kDmaPerStage - 1) * S::DMA_STRIDE;
+  // refill loads issued before the landed barrier of the same K tile
+  static constexpr int loads_before_raw() {
+    int n = 0;
+    for (int d = 0; d < S::kDmaPerStage; ++d)
+      if (S::WAR_AT + S::DMA_OFFSET + d * S::DMA_STRIDE < kRawPos) ++n;
+    return n;
+  }
+  static constexpr int kLoadsBeforeRaw = loads_before_raw();
+  // the vmcnt of the landed wait in the steady state: the STAGES-2 whole
+  // tiles after the needed one, and the part of the newest refill issued
+  static constexpr int kSteadyVmcnt = (S::STAGES - 2) * S::kDmaPerStage + kLoadsBeforeRaw;
+  static_assert(S::STAGES >= 2 && S::kKSub == 2, "early free: two K steps per K tile");
+  static_assert(S::WAR_AT >= S::kReads * S::READ_STRIDE && S::WAR_AT < S::kMfma,
+                "the free barrier follows the last operand read of K step 0, within K step 0");
+  static_assert(S::DMA_OFFSET + (S::kDmaPerStage - 1) * S::DMA_STRIDE < kTileSlots,
+                "a refill is issued in full before the next one starts");
+  static_assert(kLastLoad < kTileSlots + kRawPos, "a refill is issued in full before the barrier that needs it");
+  static_assert(S::STAGES * S::kDmaPerStage <= 63 && kSteadyVmcnt <= 63, "vmcnt range");
+};
+
+// vmcnt of the landed wait in K tile kt: loads of whole tiles issued after
+// tile kt+1, and the newest refill's loads issued so far.
+template <class S, bool kEarly>
+GT_HD constexpr int ring_ef_vmcnt(int kt, int ktu) {
+  return kEarly ? RingEarly<S>::kSteadyVmcnt
+                : ring_max(0, ring_min(ktu, kt + S::STAGES) - (kt + 2)) * S::kDmaPerStage;
+}
+
+template <class S, bool kEarly, bool kNext, class Ops>
+GT_RING_INLINE void ring_ktile_ef(Ops &ops, int kt, int ktu) {
+  using R = RingEarly<S>;
+#pragma unroll
+  for (int ks = 0; ks < S::kKSub; ++ks) {
+    const int cur = ks & 1;
+    const bool last = ks == S::kKSub - 1;
+#pragma unroll
+    for (int idx = 0; idx < S::kMfma; ++idx) {
+      if (kEarly && !last && idx == S::WAR_AT) {
+        ops.wait_lds();
+        ops.barrier();
+        ops.fence();
+      }
+      if (last && kNext && idx == R::kBarrierAt) {
+        ops.wait_tile(ring_ef_vmcnt<S, kEarly>(kt, ktu));
+        ops.barrier();
+        ops.fence();
+      }
+      ops.mfma(cur, idx);
+      ops.fence();
+      if (!last) {
+        if (idx % S::READ_STRIDE == 0 && idx / S::READ_STRIDE < S::kReads) {
+          ops.read(cur ^ 1, kt, ks + 1, idx / S::READ_STRIDE);
+          ops.fence();
+        }
+      } else if (kNext && idx >= R::kBarrierAt && (idx - R::kBarrierAt) % S::READ_STRIDE == 0) {
+        ops.read(cur ^ 1, kt + 1, 0, (idx - R::kBarrierAt) / S::READ_STRIDE);
+        ops.fence();
+      }
+      const int pos = ks * S::kMfma + idx;
+      if (kEarly && pos >= S::WAR_AT) {
+        const int d = ring_slot_load<S>(pos - S::WAR_AT);
+        if (d >= 0) ops.load(kt + S::STAGES, d);
+        ops.fence();
+      }
+    }
+  }
+  if (!kNext) ops.wait_lds();
+}
+
+template <class S, class Ops>
+GT_RING_INLINE void ring_k_loop_ef(Ops &ops, int ktu) {
+  // Every wave must be done with the previous output tile's LDS first.
+  ops.wait_lds();
+  ops.barrier();
+#pragma unroll
+  for (int s = 0; s < S::STAGES; ++s)
+    if (s < ktu)
+#pragma unroll
+      for (int d = 0; d < S::kDmaPerStage; ++d) ops.load(s, d);
+  ops.wait_tile(ring_min(ktu, S::STAGES) * S::kDmaPerStage - S::kDmaPerStage);
+  ops.barrier();
+#pragma unroll
+  for (int r = 0; r < S::kReads; ++r) ops.read(0, 0, 0, r);
+  int kt = 0;
+  for (; ring_early(kt, ktu, S::STAGES); ++kt) ring_ktile_ef<S, true, true>(ops, kt, ktu);  // steady state
+  for (; ring_next(kt, ktu); ++kt) ring_ktile_ef<S, false, true>(ops, kt, ktu);          // the ring drains
+  ring_ktile_ef<S, false, false>(ops, kt, ktu);                                          // last K tile
+}
+
 // Event codes of the host-side trace (gemvtile_ring_trace): each event is
 // five int32 values {code, a, b, c, d}.
 enum RingEvent : int32_t {

@@ -423,6 +423,8 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
     case 30: return launch_lds<16, 4, 16, kF16, 16, true>(P, Q, D, R, S, K, !small_m, stream);
     // as 30 with non-temporal loads of P (the default at 16 P rows)
     case 47: return launch_lds<16, 4, 16, kF16, 16, true, true>(P, Q, D, R, S, K, !small_m, stream);
+    // as 47 without the rotated K start
+    case 48: return launch_lds<16, 4, 16, kF16, 16, false, true>(P, Q, D, R, S, K, !small_m, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -333,7 +333,10 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *      128x128 (4-stage ring) output tiles (4 waves of 128x64, 64x128,
  *      64x64): the smaller tiles of variant 0, whatever the shape
  *   24, 25, 26 as 21, 22, 23 with 2-stage rings   27 as 23 with 5 stages
- * Variants 1..27 always run the tiled kernel, whatever the shape; variant
+ *   30, 31 as 20 with the early-free K loop: a second barrier per K tile,
+ *      in K step 0 at MFMA slot 32 (30) or 40 (31), after which the wave's
+ *      stage is refilled, half a K tile earlier than in 20
+ * Variants 1..31 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16, and some shapes with 17..64 rows on the smaller side: the skinny
  * kernel).  The skinny kernel (only for M <= 16 or N <= 16, else
@@ -379,17 +382,15 @@ int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, 
  * gemvtile_ring_trace -- the K-loop schedule of the tiled GEMM kernel, for
  * checking on the CPU (host-only; no GPU needed).  The kernel's K loop is a
  * walker over K tiles that issues tile loads, operand reads, MFMAs, waits
- * and barriers; this runs the same walker on the host for the kernel with a
- * bm x bn output tile and a `stages`-deep LDS ring over `ktu` K tiles (of 64
- * elements), recording each event instead of issuing it.  The ring follows
- * "使用 TMA 为 GEMM 建立 Pipeline" (TVM TIRx GEMM chapter), step 5 (Pipeline
- * 机制): K tile k in stage k % stages, refilled with tile k + stages once
- * consumed; completion is tracked by in-order vmcnt waits instead of the
- * chapter's per-stage mbarrier phases.
+ * and barriers; this runs the same walker on the host for the kernel of
+ * tiled variant `variant` (a gemvtile_gemm_f16_variant number: 0 = 20, the
+ * 256x256 default; 1 and 3 share its ring; 10 and 20..27, 30, 31) over `ktu`
+ * K tiles (of 64 elements), recording each event instead of issuing it.
+ * The ring follows "使用 TMA 为 GEMM 建立 Pipeline" (TVM TIRx GEMM chapter),
+ * step 5 (Pipeline 机制): K tile k in stage k % stages, refilled with tile
+ * k + stages once consumed; completion is tracked by in-order vmcnt waits
+ * instead of the chapter's per-stage mbarrier phases.
  *
- *   bm, bn, stages  one of the kernel shapes the library has: 256x256 with 2
- *                   stages; 256x128 and 128x256 with 2 or 3; 128x128 with 2,
- *                   4 or 5
  *   ktu     K tiles the loop walks (1 .. 2^20): ceil(K / 64), or one K slice
  *           of a split-K unit
  *   events  host memory for `cap` events of five int32 {code, a, b, c, d}:
@@ -402,13 +403,15 @@ int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, 
  *             6 MFMA      a = fragment buffer, b = MFMA index in the K step
  *           events beyond `cap` are counted but not written; may be NULL
  *           when cap == 0
- *   info    if not NULL, 4 ints: loads per wave per K tile, operand reads per
- *           wave per K step, K steps per K tile, MFMAs per wave per K step
+ *   info    if not NULL, 8 ints: loads per wave per K tile, operand reads
+ *           per wave per K step, K steps per K tile, MFMAs per wave per K
+ *           step, ring stages, output tile rows and columns, and 1 for the
+ *           early-free schedule (two barriers per K tile) or 0
  * Each wave of the workgroup runs this same sequence.  Returns the number
- * of events, or -1 for a shape the library has no kernel for or arguments
+ * of events, or -1 for a variant without a multi-stage ring or arguments
  * out of range.
  */
-int64_t gemvtile_ring_trace(int bm, int bn, int stages, int64_t ktu, int32_t *events, int64_t cap, int *info);
+int64_t gemvtile_ring_trace(int variant, int64_t ktu, int32_t *events, int64_t cap, int *info);
 
 /*
  * gemvtile_xcd_logical_id -- the logical workgroup id the persistent GEMM

@@ -278,7 +278,7 @@ def test_output_guard_band(env):
     assert np.array_equal(D.cpu().numpy(), oracle.gemm(A, B))
 
 
-TILED_VARIANTS = [1, 2, 3, 10, 20, 21, 22, 23, 24, 25, 26, 27]
+TILED_VARIANTS = [1, 2, 3, 10, 20, 21, 22, 23, 24, 25, 26, 27, 30, 31, 32, 33, 34, 35, 36]
 
 
 @pytest.mark.parametrize("variant", TILED_VARIANTS)
@@ -293,7 +293,7 @@ def test_gemm_variants_bit_identical(env, variant):
     assert np.array_equal(_gemm(env, A, B, variant).cpu().numpy(), base)
 
 
-@pytest.mark.parametrize("variant", [0, 2, 10, 20, 21, 22, 23, 24, 25, 26, 27])
+@pytest.mark.parametrize("variant", [0, 2, 10, 20, 21, 22, 23, 24, 25, 26, 27, 30, 31, 32, 33, 34, 35, 36])
 @pytest.mark.parametrize("K", [8, 64, 72, 128, 136, 192, 200, 264, 328])
 def test_gemm_variants_few_k_tiles(env, variant, K):
     """1 to 6 K tiles of 64, whole and ragged: the prologue, the last refill
@@ -337,7 +337,7 @@ def test_gemm_tile_choice_shapes(env, case):
     assert np.array_equal(Di[torch.from_numpy(last).to(dev)].cpu().numpy(), oracle.gemm(Ai, Bi, rows=last))
 
 
-@pytest.mark.parametrize("variant", [6, 7, 8, 9, 10, 11, 12])
+@pytest.mark.parametrize("variant", [6, 7, 8, 9, 10, 11, 12] + list(range(20, 37)))
 def test_gemv_variants_bit_identical(env, variant):
     N, K = 1031, 14344
     x = datagen.integer_f16(6001, 0, (K,))

@@ -26,9 +26,10 @@ import pytest
 
 import gemv_tile_pipelined_amd as gt
 
-# (bm, bn, stages) of every tiled kernel the library instantiates.
-SHAPES = [(256, 256, 2), (256, 128, 2), (256, 128, 3), (128, 256, 2), (128, 256, 3), (128, 128, 2), (128, 128, 4),
-          (128, 128, 5)]
+# Tiled variants with a multi-stage ring (gemvtile_gemm_f16_variant numbers):
+# 20 the 256x256 default, 10 its 32x32x16 form, 21..27 the smaller tiles with
+# 2..5 stages, 30 and 31 the early-free schedule.
+VARIANTS = [20, 10, 21, 22, 23, 24, 25, 26, 27, 30, 31, 32, 33, 34, 35, 36]
 # 1..9 short loops (every prologue / last-refill / drain branch), 22 and 56
 # (split-K slice lengths: ceil(224 / 4) = 56 for K = 14336 in 4 slices), 64
 # (K = 4096), 65 (K = 4104: the ragged benchmark shape), 128 (K = 8192).
@@ -38,8 +39,8 @@ KTUS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 22, 56, 64, 65, 128]
 class RingModel:
     """Replays a trace; raises AssertionError on the first violation."""
 
-    def __init__(self, stages, ktu, info):
-        self.S, self.ktu = stages, ktu
+    def __init__(self, ktu, info):
+        self.S, self.ktu = info["stages"], ktu
         self.per = info["loads_per_tile"]
         self.reads = info["reads_per_step"]
         self.ksteps = info["ksteps"]
@@ -126,34 +127,59 @@ class RingModel:
         assert self.mfmas == self.ktu * self.ksteps * self.mfma
 
 
-def replay(bm, bn, stages, ktu):
-    events, info = gt.ring_trace(bm, bn, stages, ktu)
-    model = RingModel(stages, ktu, info)
+def replay(variant, ktu):
+    events, info = gt.ring_trace(variant, ktu)
+    model = RingModel(ktu, info)
     for ev in events:
         model.step(ev)
     model.finish()
     return model, events
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}_s{s[2]}")
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("ktu", KTUS)
-def test_ring_schedule_is_correct(shape, ktu):
-    replay(*shape, ktu)
+def test_ring_schedule_is_correct(variant, ktu):
+    replay(variant, ktu)
 
 
-# The tiles and ring depths gemm_f16 picks (gemvtile_gemm_tile).
-DEFAULT_SHAPES = [(256, 256, 2), (256, 128, 3), (128, 256, 3), (128, 128, 4)]
+def test_trace_info_describes_the_kernels():
+    want = {20: (256, 256, 2, 16, 0), 10: (256, 256, 2, 16, 0), 21: (256, 128, 3, 12, 0), 22: (128, 256, 3, 12, 0),
+            23: (128, 128, 4, 8, 0), 24: (256, 128, 2, 12, 0), 25: (128, 256, 2, 12, 0), 26: (128, 128, 2, 8, 0),
+            27: (128, 128, 5, 8, 0), 30: (256, 256, 2, 16, 1), 31: (256, 256, 2, 16, 1)}
+    for v, (bm, bn, stages, per, ef) in want.items():
+        _, info = gt.ring_trace(v, 4)
+        assert (info["bm"], info["bn"], info["stages"], info["loads_per_tile"], info["early_free"]) == \
+            (bm, bn, stages, per, ef), v
+    for v in (0, 1, 3):  # the default's ring
+        assert gt.ring_trace(v, 7)[0] == gt.ring_trace(20, 7)[0]
+    with pytest.raises(gt.GemvTileError):
+        gt.ring_trace(2, 4)  # the one-stage ablation has no ring
 
 
-@pytest.mark.parametrize("shape", DEFAULT_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}_s{s[2]}")
-def test_ring_overlaps_loads_with_mfmas(shape):
+# The tiles and ring depths gemm_f16 picks (gemvtile_gemm_tile), and the
+# early-free schedule.
+OVERLAPPED = [20, 21, 22, 23, 30, 31, 32, 33, 34, 35, 36]
+
+
+@pytest.mark.parametrize("variant", OVERLAPPED)
+def test_ring_overlaps_loads_with_mfmas(variant):
     """In the steady state each K tile's last load is issued at least one
     whole K step of MFMAs before the wait that needs it: the loads overlap
     the matrix work (the point of the ring)."""
-    bm, bn, stages = shape
-    model, _ = replay(bm, bn, stages, 16)
-    for t in range(stages, 16):
+    model, _ = replay(variant, 16)
+    for t in range(model.S, 16):
         assert model.overlap[t] >= model.mfma, (t, model.overlap[t])
+
+
+def test_early_free_doubles_the_refill_slack():
+    """The early-free schedule starts each refill about half a K tile sooner
+    than the one-barrier ring, so a tile's last load has roughly twice the
+    MFMA slots to land before the barrier that needs it."""
+    base, _ = replay(20, 16)
+    for v in (30, 31):
+        ef, _ = replay(v, 16)
+        for t in range(2, 16):
+            assert ef.overlap[t] >= base.overlap[t] + 40, (v, t, ef.overlap[t], base.overlap[t])
 
 
 def test_two_stage_rings_of_small_tiles_barely_overlap():
@@ -161,20 +187,28 @@ def test_two_stage_rings_of_small_tiles_barely_overlap():
     or 1/4 of the 256x256 one in MFMA slots, so the last load of a refill
     lands only a few MFMAs before it is needed -- which is why those tiles
     get 3- and 4-stage rings by default."""
-    for bm, bn in [(256, 128), (128, 256), (128, 128)]:
-        model, _ = replay(bm, bn, 2, 16)
+    for v in (24, 25, 26):
+        model, _ = replay(v, 16)
         assert max(model.overlap[t] for t in range(2, 16)) < model.mfma
 
 
 def test_ring_wait_counts_let_younger_tiles_fly():
     """With 3 or more stages the steady-state wait leaves the younger tiles'
     loads in flight (vmcnt = (stages - 2) x loads per tile) rather than
-    draining the ring; with 2 stages nothing younger exists at the wait."""
-    for bm, bn, stages in SHAPES:
-        events, info = gt.ring_trace(bm, bn, stages, 32)
+    draining the ring; with 2 stages nothing younger exists at the wait --
+    except in the early-free schedule, whose next refill is already issued
+    there (vmcnt = loads per tile)."""
+    for v in VARIANTS:
+        events, info = gt.ring_trace(v, 32)
+        stages, per = info["stages"], info["loads_per_tile"]
         waits = [e[1] for e in events if e[0] == "wait"]
         steady = waits[1:32 - stages]
-        assert set(steady) == {(stages - 2) * info["loads_per_tile"]}, (bm, bn, stages, steady)
+        assert len(set(steady)) == 1, (v, steady)
+        younger = steady[0] - (stages - 2) * per
+        if info["early_free"]:
+            assert 0 < younger <= per, (v, steady)  # part of the next refill
+        else:
+            assert younger == 0, (v, steady)
         assert waits[-1] == 0  # the last tile: nothing younger
 
 
@@ -198,8 +232,8 @@ def test_tvm_pipeline_exercise_depth2_ktiles5():
     register dependences, not by a barrier."""
     golden = _load_golden()
     assert [g[0] for g in golden] == list(range(5))
-    events, info = gt.ring_trace(256, 256, 2, 5)
-    replay(256, 256, 2, 5)
+    events, info = gt.ring_trace(20, 5)
+    replay(20, 5)
     # stage of each K tile, from the operand reads
     stage_of = {}
     for kind, a, b, c, d in events:
@@ -225,8 +259,8 @@ def test_tvm_pipeline_exercise_depth2_ktiles5():
         assert got == ({pre} if pre is not None else set()), (k, got, pre)
 
 
-def _replay_events(events, stages, ktu, info):
-    model = RingModel(stages, ktu, info)
+def _replay_events(events, ktu, info):
+    model = RingModel(ktu, info)
     for ev in events:
         model.step(ev)
     model.finish()
@@ -237,9 +271,10 @@ def test_model_rejects_broken_schedules():
     a copy of a real trace: a wait that lets the needed tile stay in flight,
     a missing barrier, a refill issued before the barrier that frees its
     stage, a read from the wrong stage, a dropped load."""
-    bm, bn, stages, ktu = 256, 128, 3, 8
-    events, info = gt.ring_trace(bm, bn, stages, ktu)
-    _replay_events(events, stages, ktu, info)  # the real trace passes
+    ktu = 8
+    events, info = gt.ring_trace(21, ktu)  # 256x128, 3 stages
+    stages = info["stages"]
+    _replay_events(events, ktu, info)  # the real trace passes
     per = info["loads_per_tile"]
     waits = [i for i, e in enumerate(events) if e[0] == "wait"]
     barriers = [i for i, e in enumerate(events) if e[0] == "barrier"]
@@ -273,4 +308,4 @@ def test_model_rejects_broken_schedules():
     mutants.append(m)
     for n, m in enumerate(mutants, 1):
         with pytest.raises(AssertionError):
-            _replay_events(m, stages, ktu, info)
+            _replay_events(m, ktu, info)
