@@ -26,22 +26,28 @@ Prints ONE JSON line on stdout:
                steps, so both see one clock state
   decode_batch the 8x4096x14336 GEMM (skinny path) in GB/s, timed on its own
   bf16         gemm_bf16 at 4096^3 and gemv_bf16 at 4096x14336
-  clock        the engine clock and socket power sampled (amdsmi, read-only)
-               while back-to-back gemm_f16 4096^3 launches run on the uniform
-               inputs and then on all-zero inputs of the same shape: the
-               part's power limit sets the clock the MFMAs run at
+  clock        the clock the MFMAs run at, from per-workgroup timestamps of the
+               GEMM kernel (gemvtile_gemm_f16_timed) while 4096^3 launches run
+               back to back on the uniform inputs and then on all-zero inputs,
+               with the time split into prologue + K loop, epilogue and the
+               spread of workgroup end times, and socket power (amdsmi,
+               read-only) alongside: the part's power limit sets the clock
   cpu_baseline the CPU oracle (FP64, OpenMP) on a bounded sample of the same
                workloads: the 4096^3 GEMM (rows sized to the time budget), the
                ragged GEMM in full, the 8192^3 GEMM on its 64 seeded rows and
                the GEMV in full
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 2000] [--settle-s 0.5]
-                       [--only gemm|gemv|decode|bf16|configs|vendor|clock|copy]
+                       [--only gemm|gemv|decode|bf16|configs|vendor|clock|copy|gemm_variants|gemv_variants]
 --only runs the steps (or, for decode/bf16/configs/vendor/clock, that
 section alone after the same settle phase) and prints the line without the
 other sections; it exists so that profiler runs time one kernel family at a
 time.  --only copy runs nothing of the library: 20 device-to-device copies of
 a 256 MiB buffer, the known-size reference that hardware traffic counters
-are calibrated against.
+are calibrated against.  --only gemm_variants / gemv_variants time the
+internal ablation variants (gemvtile_gemm_f16_variant / _gemv_f16_variant)
+against each other, one launch (GEMM) or five launches over five copies of
+W (GEMV) per variant in turn, each bracketed by events, after 1 s of the
+same rotation untimed, and print one line per variant and shape.
 """
 from __future__ import annotations
 
@@ -96,9 +102,15 @@ def parse():
     p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--settle-s", type=float, default=0.5, help="seconds of untimed steps before the warm-up steps")
     p.add_argument("--cpu-seconds", type=float, default=8.0, help="target CPU time of the 4096^3 oracle sample")
-    p.add_argument("--only", choices=("gemm", "gemv", "decode", "bf16", "configs", "vendor", "clock", "copy"),
-                   default=None)
-    p.add_argument("--clock-s", type=float, default=1.0, help="seconds of sampled load per data set in the clock section")
+    p.add_argument("--only", choices=("gemm", "gemv", "decode", "bf16", "configs", "vendor", "clock", "copy",
+                                      "gemm_variants", "gemv_variants"), default=None)
+    p.add_argument("--variants", default="0", help="--only gemm_variants / gemv_variants: variant numbers, "
+                   "comma-separated (gemm: -1 = the vendor GEMM, torch.matmul)")
+    p.add_argument("--shapes", default="4096x4096x4096", help="--only gemm_variants: MxNxK list; gemv_variants: NxK "
+                   "list, or RxNxK for gemm_f16 variants on an R-row activation batch against W [N,K]")
+    p.add_argument("--data", choices=("uniform", "zero"), default="uniform", help="--only gemm_variants inputs")
+    p.add_argument("--reps", type=int, default=24, help="--only gemm_variants / gemv_variants timed rounds")
+    p.add_argument("--clock-s", type=float, default=2.0, help="seconds of sampled load per data set in the clock section")
     return p.parse_args()
 
 
@@ -293,6 +305,88 @@ def roofline(bound, achieved, peak, unit, traffic=None, kernel=None, **extra):
     return r
 
 
+def variant_sweep(args, torch, np, gt, datagen, dev):
+    """Interleaved timing of ablation variants (see the module doc)."""
+    lib = gt.load_library()
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    variants = [int(v) for v in args.variants.split(",")]
+    out = {"only": args.only, "data": args.data, "results": []}
+
+    def interleaved(run, n_per):
+        t_end = time.perf_counter() + 1.0
+        i = 0
+        while time.perf_counter() < t_end:
+            for v in variants:
+                run(v, i)
+            i += 1
+            torch.cuda.synchronize(dev)
+        ev = {v: [] for v in variants}
+        for r in range(args.reps):
+            for v in variants:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run(v, r)
+                e1.record(stream)
+                ev[v].append((e0, e1))
+        torch.cuda.synchronize(dev)
+        return {v: np.array([a.elapsed_time(b) for a, b in ev[v]]) * 1e3 / n_per for v in variants}
+
+    for shape in args.shapes.split(","):
+        dims = [int(t) for t in shape.split("x")]
+        if args.only == "gemm_variants":
+            M, N, K = dims
+            sets = []
+            for i in range(3 if M * N * K <= 4096 ** 3 else 1):
+                if args.data == "zero":
+                    A = torch.zeros((M, K), dtype=torch.float16, device=dev)
+                    B = torch.zeros((N, K), dtype=torch.float16, device=dev)
+                else:
+                    A = torch.from_numpy(datagen.uniform_f16(50 + i, 0, (M, K), -1.0, 1.0)).to(dev)
+                    B = torch.from_numpy(datagen.uniform_f16(50 + i, 1, (N, K), -1.0, 1.0)).to(dev)
+                sets.append((A, B, torch.empty((M, N), dtype=torch.float16, device=dev)))
+
+            def run(v, i):
+                A, B, D = sets[i % len(sets)]
+                if v < 0:
+                    torch.matmul(A, B.t(), out=D)
+                else:
+                    st = lib.gemvtile_gemm_f16_variant(A.data_ptr(), B.data_ptr(), D.data_ptr(), M, N, K, sh, v)
+                    if st:
+                        raise RuntimeError(f"variant {v}: {gt.status_string(st)}")
+
+            us = interleaved(run, 1)
+            work, unit = 2.0 * M * N * K, "TFLOP/s"
+        else:
+            rows = dims[0] if len(dims) == 3 else 0
+            N, K = dims[-2], dims[-1]
+            x = torch.from_numpy(datagen.uniform_f16(3, 0, (max(rows, 1), K) if rows else (K,), -1.0, 1.0)).to(dev)
+            W0 = torch.from_numpy(datagen.uniform_f16(3, 1, (N, K), -0.05, 0.05)).to(dev)
+            Ws = [W0] + [W0.clone() for _ in range(GEMV_COPIES - 1)]
+            ys = [torch.empty((rows, N) if rows else (N,), dtype=torch.float16, device=dev) for _ in Ws]
+
+            def run(v, i):
+                for W, y in zip(Ws, ys):
+                    if rows:
+                        st = lib.gemvtile_gemm_f16_variant(x.data_ptr(), W.data_ptr(), y.data_ptr(), rows, N, K, sh, v)
+                    else:
+                        st = lib.gemvtile_gemv_f16_variant(x.data_ptr(), W.data_ptr(), y.data_ptr(), N, K, sh, v)
+                    if st:
+                        raise RuntimeError(f"variant {v}: {gt.status_string(st)}")
+
+            us = interleaved(run, GEMV_COPIES)
+            work, unit = 2.0 * (N * K + max(rows, 1) * (K + N)), "GB/s"
+        for v in variants:
+            u = us[v]
+            rate = work / (u.mean() * 1e-6) / (1e12 if unit == "TFLOP/s" else 1e9)
+            print(f"{shape} variant {v}: mean {u.mean():.2f} median {np.median(u):.2f} min {u.min():.2f} us, "
+                  f"{rate:.0f} {unit}", file=sys.stderr, flush=True)
+            out["results"].append({"shape": shape, "variant": v, "us_mean": round(float(u.mean()), 2),
+                                   "us_median": round(float(np.median(u)), 2), "us_min": round(float(u.min()), 2),
+                                   "rate": round(rate, 1), "unit": unit})
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -315,6 +409,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     only = args.only
+    if only in ("gemm_variants", "gemv_variants"):
+        variant_sweep(args, torch, np, gt, datagen, dev)
+        return
     if only == "copy":
         nbytes = 256 << 20
         src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
@@ -603,51 +700,86 @@ def main():
 
     # ---- the engine clock under sustained GEMM load ---------------------
     if want("clock"):
-        clock = {"method": "amdsmi gpu metrics (current per-XCD gfx clock, socket power) sampled every 5 ms in a "
-                           "thread while gemm_f16 4096^3 runs back to back; the first tenth of the samples dropped"}
+        clock = {"method": "gemvtile_gemm_f16_timed (the default 256x256 kernel with per-workgroup start / "
+                           "K-loop end / end stamps of the 100 MHz real-time and the shader-cycle counters) run "
+                           "back to back; the last 20 launches analysed. Socket power and the SMU's clock "
+                           "reading sampled alongside with amdsmi (read-only; its readings refresh slowly)."}
         try:
+            lib = gt.load_library()
             zero_A = torch.zeros((M, K), dtype=torch.float16, device=dev)
             zero_B = torch.zeros((N, K), dtype=torch.float16, device=dev)
             zero_D = torch.empty((M, N), dtype=torch.float16, device=dev)
+            grid = gt.gemm_grid(M, N, gt.device_caps()["num_cus"])
+            n_keep = 20
+            stamps = torch.zeros((n_keep, grid * 8), dtype=torch.int64, device=dev)
+            # MFMA cycles per wave of one 256x256 tile: (128/16)^2 blocks x K/32 steps x 16 cycles
+            mfma_cycles = (128 // 16) * (128 // 16) * (K // 32) * 16
             for name, operands in (("uniform", [(A_, B_, D_) for A_, B_, D_ in gemm_sets]),
                                    ("zero", [(zero_A, zero_B, zero_D)])):
                 def one(i, operands=operands):
                     A_, B_, D_ = operands[i % len(operands)]
-                    check(gt.gemm_f16_ptr(A_.data_ptr(), B_.data_ptr(), D_.data_ptr(), M, N, K, sh))
+                    check(lib.gemvtile_gemm_f16_timed(A_.data_ptr(), B_.data_ptr(), D_.data_ptr(), M, N, K, sh,
+                                                      stamps[i % n_keep].data_ptr(), grid * 8))
 
                 for i in range(SECTION_WARMUP):
                     one(i)
                 torch.cuda.synchronize(dev)
-                sampler = ClockSampler()
-                sampler.start()
+                sampler = None
+                try:
+                    sampler = ClockSampler()
+                    sampler.start()
+                except Exception as e:
+                    clock.setdefault("amdsmi_error", repr(e))
                 t_end = time.perf_counter() + args.clock_s
                 n = 0
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                while time.perf_counter() < t_end:
+                while time.perf_counter() < t_end or n < n_keep:
                     for _ in range(50):
                         one(n)
                         n += 1
                     torch.cuda.synchronize(dev)
                 e1.record(stream)
                 torch.cuda.synchronize(dev)
-                samples = sampler.stop()
-                cap = sampler.power_cap_w()
-                sampler.close()
                 us = e0.elapsed_time(e1) * 1e3 / n
-                clock[name] = {**summarize_clock(samples), "launches": n, "us_per_launch": round(us, 2),
-                               "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
-                if cap is not None:
-                    clock["power_cap_w"] = cap
-            del zero_A, zero_B, zero_D
-            # MFMA-only clock ceiling: at f MHz the dense fp16 peak is
-            # CUs x 4096 flop x f
-            cus = gt.device_caps()["num_cus"]
-            for name in ("uniform", "zero"):
-                c = clock.get(name, {})
-                if "gfxclk_mhz_mean" in c:
-                    c["mfma_peak_at_this_clock_tflops"] = round(cus * 4096 * c["gfxclk_mhz_mean"] * 1e6 / 1e12, 1)
-                    c["frac_of_peak_at_this_clock"] = round(c["tflops"] / c["mfma_peak_at_this_clock_tflops"], 4)
+                entry = {"launches": n, "us_per_launch": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
+                if sampler is not None:
+                    samples = sampler.stop()
+                    entry["amdsmi"] = summarize_clock(samples)
+                    cap = sampler.power_cap_w()
+                    if cap is not None:
+                        clock["power_cap_w"] = cap
+                    sampler.close()
+                st = stamps.cpu().numpy().reshape(n_keep, grid, 8).astype(np.float64)
+                r0, c0, r1, c1, r2, c2 = (st[..., k] for k in range(6))
+                xcc = (st[..., 7].astype(np.int64) & 0xF)
+                clk_mhz = (c2 - c0) / (r2 - r0) * 100.0  # per workgroup and launch
+                span_us = (r2.max(axis=1) - r0.min(axis=1)) / 100.0  # per launch
+                loop_us = (r1 - r0) / 100.0
+                epi_us = (r2 - r1) / 100.0
+                end_spread_us = (r2.max(axis=1) - np.median(r2, axis=1)) / 100.0
+                start_spread_us = (r0.max(axis=1) - r0.min(axis=1)) / 100.0
+                loop_cycles = c1 - c0
+                entry["timed"] = {
+                    "clock_mhz_median": round(float(np.median(clk_mhz)), 1),
+                    "clock_mhz_p10_p90": [round(float(np.percentile(clk_mhz, 10)), 1),
+                                          round(float(np.percentile(clk_mhz, 90)), 1)],
+                    "clock_mhz_per_xcd": [round(float(np.median(clk_mhz[xcc == x])), 1) for x in range(8)
+                                          if (xcc == x).any()],
+                    "launch_span_us_median": round(float(np.median(span_us)), 2),
+                    "start_spread_us_median": round(float(np.median(start_spread_us)), 2),
+                    "prologue_and_k_loop_us_median": round(float(np.median(loop_us)), 2),
+                    "epilogue_us_median": round(float(np.median(epi_us)), 2),
+                    "end_spread_us_median": round(float(np.median(end_spread_us)), 2),
+                    "k_loop_cycles_median": round(float(np.median(loop_cycles))),
+                    "mfma_cycles_per_wave": mfma_cycles,
+                    "mfma_busy_in_k_loop": round(mfma_cycles / float(np.median(loop_cycles)), 4),
+                }
+                mhz = entry["timed"]["clock_mhz_median"]
+                entry["mfma_peak_at_this_clock_tflops"] = round(gt.device_caps()["num_cus"] * 4096 * mhz * 1e6 / 1e12, 1)
+                entry["frac_of_peak_at_this_clock"] = round(entry["tflops"] / entry["mfma_peak_at_this_clock_tflops"], 4)
+                clock[name] = entry
+            del zero_A, zero_B, zero_D, stamps
         except Exception as e:  # the clock evidence is optional; the bench line is not
             clock["error"] = repr(e)
         line["clock"] = clock

@@ -76,6 +76,7 @@ EXPORTED_SYMBOLS = (
     "gemvtile_device_caps",
     "gemvtile_ring_trace",
     "gemvtile_gemm_f16_variant",
+    "gemvtile_gemm_f16_timed",
     "gemvtile_gemv_f16_variant",
     "gemvtile_xcd_logical_id",
 )
@@ -128,6 +129,8 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemm_splitk_f16.restype = c_int
     lib.gemm_splitk_bf16.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
     lib.gemm_splitk_bf16.restype = c_int
+    lib.gemvtile_gemm_f16_timed.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64]
+    lib.gemvtile_gemm_f16_timed.restype = c_int
     lib.gemm_splitk_f16_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.gemm_splitk_f16_noalloc.restype = c_int
     lib.gemvtile_gemm_splitk_splits.argtypes = [i64, i64, i64, i64]

@@ -284,6 +284,22 @@ int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, 
   return run_gemm(A, B, D, M, N, K, stream, variant);
 }
 
+int gemvtile_gemm_f16_timed(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream,
+                            uint64_t *stamps, int64_t stamps_len) {
+  bool noop = false;
+  int st = check_gemm(A, B, D, M, N, K, &noop);
+  if (st != GEMVTILE_OK) return st;
+  if (noop || K == 0 || M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows) return GEMVTILE_ERR_UNSUPPORTED;
+  int cus = 0;
+  st = current_cu_count(&cus);
+  if (st != GEMVTILE_OK) return st;
+  const int64_t tiles = ((M + gt::kGemmBM - 1) / gt::kGemmBM) * ((N + gt::kGemmBN - 1) / gt::kGemmBN);
+  const int64_t grid = tiles < cus ? tiles : cus;
+  if (stamps == nullptr || stamps_len < 8 * grid || misaligned(stamps, 8)) return GEMVTILE_ERR_INVALID_ARG;
+  return to_status(gt::launch_gemm_f16_timed(A, B, D, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), cus,
+                                             stamps, static_cast<hipStream_t>(stream)));
+}
+
 int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream,
                               int variant) {
   if (!gt::gemv_variant_exists(variant)) return GEMVTILE_ERR_INVALID_ARG;

@@ -287,13 +287,7 @@ int64_t ring_trace(int variant, int ktu, int32_t *events, int64_t cap, int *info
     case 25: return run(GemmTile128x256<kF16, 2>{});
     case 26: return run(GemmTile128x128<kF16, 2>{});
     case 27: return run(GemmTile128x128<kF16, 5>{});
-    case 30: return run(GemmEarlyFree32{});
-    case 31: return run(GemmEarlyFree40{});
-    case 32: return run(GemmEarlyFree48{});
-    case 33: return run(GemmEarlyFree56{});
-    case 34: return run(GemmEarlyFree40s3{});
-    case 35: return run(GemmEarlyFree40s5{});
-    case 36: return run(GemmEarlyFree44{});
+    case 30: return run(GemmOneBarrier{});
     default: return -1;
   }
 }

@@ -148,15 +148,19 @@ struct KernelRingOps {
   __device__ __attribute__((always_inline)) void fence() { __builtin_amdgcn_sched_barrier(0); }
 };
 
-// One wave per SIMD for 4 waves; with 8 waves two per SIMD, so each is held
-// to half the register file.
 // Epilogue modes.  kEpiPlain: round and store D.  kEpiFused: add bias[n]
 // and apply ReLU when `relu` is set (gemm_bias_*), then round and store D.
 // kEpiPartial (split K, gemm_splitk_*): the grid walks (tile, K slice) units,
 // `splits` slices per tile; each unit sums only its slice of K tiles and
 // stores the FP32 sums, unrounded, to ws[slice][m][n]; splitk_reduce_kernel
-// adds the slices.  Each mode ignores the arguments of the others.
-enum : int { kEpiPlain = 0, kEpiFused = 1, kEpiPartial = 2 };
+// adds the slices.  kEpiTimed: as kEpiPlain, and thread 0 of each workgroup
+// records when it started, when the K loop of its first output tile ended
+// and when it finished (its stores complete), in the constant 100 MHz
+// real-time counter and the shader-cycle counter, with its XCC and hardware
+// ids, into 8 uint64 at ws + 16 * blockIdx.x bytes (a measurement of the
+// clock the MFMAs run at and of where the time goes; gemvtile_gemm_f16_timed).
+// Each mode ignores the arguments of the others.
+enum : int { kEpiPlain = 0, kEpiFused = 1, kEpiPartial = 2, kEpiTimed = 3 };
 
 template <class S, int EPI = kEpiPlain>
 __global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWaves / 4, S::kWaves / 4)))
@@ -168,6 +172,12 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  uint64_t t_start_r = 0, t_start_c = 0, t_loop_r = 0, t_loop_c = 0;
+  bool first_tile = true;
+  if constexpr (EPI == kEpiTimed) {
+    t_start_r = __builtin_amdgcn_s_memrealtime();
+    t_start_c = __builtin_amdgcn_s_memtime();
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / S::WAVES_N;
   const int wn = wave % S::WAVES_N;
@@ -397,6 +407,13 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       else
         ring_k_loop<S>(ops, KTu);
     }
+    if constexpr (EPI == kEpiTimed) {
+      if (first_tile) {
+        t_loop_r = __builtin_amdgcn_s_memrealtime();
+        t_loop_c = __builtin_amdgcn_s_memtime();
+        first_tile = false;
+      }
+    }
 
     // ---- epilogue: fp32 -> fp16 (nearest even), staged through LDS -------
     // With MI = 32, acc[i][j][4g + e] is D[m][n] with
@@ -507,6 +524,23 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       }
     }
   }
+  if constexpr (EPI == kEpiTimed) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+    workgroup_barrier();            // ... and every other wave's
+    if (tid == 0) {
+      const uint64_t t_end_r = __builtin_amdgcn_s_memrealtime();
+      const uint64_t t_end_c = __builtin_amdgcn_s_memtime();
+      uint64_t *st = reinterpret_cast<uint64_t *>(ws) + static_cast<int64_t>(blockIdx.x) * 8;
+      st[0] = t_start_r;
+      st[1] = t_start_c;
+      st[2] = t_loop_r;
+      st[3] = t_loop_c;
+      st[4] = t_end_r;
+      st[5] = t_end_c;
+      st[6] = static_cast<uint32_t>(__builtin_amdgcn_s_getreg((31 << 11) | 4));   // HW_ID
+      st[7] = static_cast<uint32_t>(__builtin_amdgcn_s_getreg((31 << 11) | 20));  // XCC_ID
+    }
+  }
 }
 
 // ---- instantiations ------------------------------------------------------
@@ -514,39 +548,34 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
 // tile load is a whole 128-byte line), a two-stage 64 KiB-per-stage LDS ring,
 // 2x2 waves of 128x128 made of 16x16x32 MFMA blocks (128 MFMA slots per K
 // tile), the next K step's operand reads one every 2 slots, one refill load
-// every 4 slots (offset by one slot from the reads), swizzled LDS, persistent
-// grouped scheduler.  The 16x16x32 shape moves half the accumulator bytes
-// per flop of 32x32x16 and runs at a measurably higher sustained clock under
-// the power limit.  The others exist for ablation measurements.
-using GemmDefault = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1>;
+// every 4 slots, swizzled LDS, persistent grouped scheduler, and the
+// early-free K loop with its free barrier at slot 48 of K step 0 (ring.hpp:
+// measured 1.5-3 % faster than one barrier per K tile at 4096^3 and 8192^3,
+// 4 % at the maximum clock; the slot, 32..56, and the refill spacing, 3..5,
+// made no difference beyond noise).  The 16x16x32 shape moves half the
+// accumulator bytes per flop of 32x32x16 and runs at a measurably higher
+// sustained clock under the power limit.
+using GemmDefault = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1, kF16, true, 48>;
 // The default shape with bf16 operands and results.
-using GemmBf16 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1, kBF16>;
+using GemmBf16 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1, kBF16, true, 48>;
 // Ablations, each the default with one design choice taken back: no LDS
 // swizzle; one workgroup per output tile in launch order (no persistent
-// grouped, XCD-aware schedule); 32x32x16 MFMA blocks through the compiler's
-// builtin (64 slots per K tile, one operand read per slot, a refill load
-// every 2 slots); and the same with a single LDS stage (load, wait, compute).
-using GemmNoSwizzle = GemmShape<256, 256, 64, 2, 2, 2, false, true, 4, 16, 2, 1>;
-using GemmNonPersistent = GemmShape<256, 256, 64, 2, 2, 2, true, false, 4, 16, 2, 1>;
+// grouped, XCD-aware schedule); one barrier per K tile (the ring without the
+// early free); 32x32x16 MFMA blocks through the compiler's builtin (64 slots
+// per K tile, one operand read per slot, a refill load every 2 slots; four K
+// steps per K tile, so the one-barrier ring); and that with a single LDS
+// stage (load, wait, compute).
+using GemmNoSwizzle = GemmShape<256, 256, 64, 2, 2, 2, false, true, 4, 16, 2, 1, kF16, true, 48>;
+using GemmNonPersistent = GemmShape<256, 256, 64, 2, 2, 2, true, false, 4, 16, 2, 1, kF16, true, 48>;
+using GemmOneBarrier = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1>;
 using Gemm32x32 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 2>;
 using Gemm32x32OneStage = GemmShape<256, 256, 64, 1, 2, 2, true, true, 1>;
 // Smaller output tiles, for outputs whose 256x256 tiles would leave CUs
-// idle (gemm_default_tile picks): the default's schedule on 256x128, 128x256
-// and 128x128 tiles (4 waves of 128x64, 64x128 and 64x64; 12, 12 and 8 loads
-// per wave per K tile), with the deeper rings of kGemmTileShapes.  A K tile
-// of these is 1/2 or 1/4 of the 256x256 one in MFMA time, so two stages no
-// longer cover a load's latency.
-// The default with the early-free K loop (ring.hpp): the free barrier at
-// slot 32 (right after K step 0's last operand read) or 40 of K step 0.
-using GemmEarlyFree32 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1, kF16, true, 32>;
-using GemmEarlyFree40 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1, kF16, true, 40>;
-// <free barrier slot, refill load spacing, offset>: (48, 4, 1), (56, 4, 1),
-// (40, 3, 1), (40, 5, 1), (44, 4, 1)
-using GemmEarlyFree48 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1, kF16, true, 48>;
-using GemmEarlyFree56 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1, kF16, true, 56>;
-using GemmEarlyFree40s3 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 3, 16, 2, 1, kF16, true, 40>;
-using GemmEarlyFree40s5 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 5, 16, 2, 1, kF16, true, 40>;
-using GemmEarlyFree44 = GemmShape<256, 256, 64, 2, 2, 2, true, true, 4, 16, 2, 1, kF16, true, 44>;
+// idle (gemm_default_tile picks): the one-barrier schedule on 256x128,
+// 128x256 and 128x128 tiles (4 waves of 128x64, 64x128 and 64x64; 12, 12 and
+// 8 loads per wave per K tile), with the deeper rings of kGemmTileShapes.  A
+// K tile of these is 1/2 or 1/4 of the 256x256 one in MFMA time, so two
+// stages no longer cover a load's latency.
 template <int DT, int STAGES = 2>
 using GemmTile256x128 = GemmShape<256, 128, 64, STAGES, 2, 2, true, true, 4, 16, 2, 1, DT>;
 template <int DT, int STAGES = 2>

@@ -23,13 +23,7 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 25: return launch<GemmTile128x256<kF16, 2>>(A, B, D, M, N, K, num_cus, stream);
     case 26: return launch<GemmTile128x128<kF16, 2>>(A, B, D, M, N, K, num_cus, stream);
     case 27: return launch<GemmTile128x128<kF16, 5>>(A, B, D, M, N, K, num_cus, stream);
-    case 30: return launch<GemmEarlyFree32>(A, B, D, M, N, K, num_cus, stream);
-    case 31: return launch<GemmEarlyFree40>(A, B, D, M, N, K, num_cus, stream);
-    case 32: return launch<GemmEarlyFree48>(A, B, D, M, N, K, num_cus, stream);
-    case 33: return launch<GemmEarlyFree56>(A, B, D, M, N, K, num_cus, stream);
-    case 34: return launch<GemmEarlyFree40s3>(A, B, D, M, N, K, num_cus, stream);
-    case 35: return launch<GemmEarlyFree40s5>(A, B, D, M, N, K, num_cus, stream);
-    case 36: return launch<GemmEarlyFree44>(A, B, D, M, N, K, num_cus, stream);
+    case 30: return launch<GemmOneBarrier>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -39,5 +33,11 @@ hipError_t launch_gemm_bf16(const void *A, const void *B, void *D, int M, int N,
   return launch_default<kBF16>(A, B, D, M, N, K, num_cus, stream);
 }
 
+
+hipError_t launch_gemm_f16_timed(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
+                                 uint64_t *stamps, hipStream_t stream) {
+  return launch<GemmDefault, kEpiTimed>(A, B, D, M, N, K, num_cus, stream, nullptr, 0,
+                                        reinterpret_cast<float *>(stamps), 1);
+}
 
 }  // namespace gt

@@ -23,8 +23,8 @@ constexpr int kGemmGroupM = 8;
 // gemvtile_gemm_f16_variant numbers of the tiled kernel: 0 (the default)
 // and the ablations of gemm.hip.  Numbers of ablations that were measured and
 // not kept stay unused.
-constexpr int kGemmVariants = 37;
-inline bool gemm_variant_exists(int v) { return (v >= 0 && v <= 3) || v == 10 || (v >= 20 && v <= 27) || (v >= 30 && v <= 36); }
+constexpr int kGemmVariants = 31;
+inline bool gemm_variant_exists(int v) { return (v >= 0 && v <= 3) || v == 10 || (v >= 20 && v <= 27) || v == 30; }
 
 // Output tile of the tiled GEMM.  The 256x256 default needs about one tile
 // per CU to fill the chip; outputs that give fewer take smaller tiles, each
@@ -208,6 +208,10 @@ constexpr unsigned kWaitLgkm0 = 0xC07F;
 // and MFMAs per wave per K step, K steps per K tile, ring stages, bm, bn and
 // whether it runs the early-free schedule (1) or not (0).
 int64_t ring_trace(int variant, int ktu, int32_t *events, int64_t cap, int *info);
+// The 256x256 tiled kernel of gemm_f16 with per-workgroup timestamps
+// (kEpiTimed in gemm_kernel.hpp) written to stamps[8 * workgroup ...].
+hipError_t launch_gemm_f16_timed(const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
+                                 uint64_t *stamps, hipStream_t stream);
 hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K, int num_cus,
                            hipStream_t stream);
 hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, void *D, int M, int N, int K,

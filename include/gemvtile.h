@@ -322,21 +322,21 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *      with 256x256 tiles, 4 waves of 128x128, 16x16x32 MFMA blocks, K tiles
  *      of 64 in a 2-stage LDS ring, the next K step's operand reads one every
  *      2 MFMA slots, a refill load every 4 slots, swizzled LDS, persistent
- *      grouped XCD-aware schedule
+ *      grouped XCD-aware schedule, and the early-free K loop (a second
+ *      barrier per K tile, at MFMA slot 48 of K step 0, after which the
+ *      wave's stage is refilled, half a K tile sooner than with one barrier)
  *   1  as 20 without the LDS swizzle
  *   2  as 10 with single-stage LDS (load, wait, compute: no overlap)
  *   3  as 20 with one workgroup per tile (no persistent loop, no XCD remap)
- *   10 as 20 with 32x32x16 MFMA blocks, one operand read per slot, a refill
+ *   10 as 30 with 32x32x16 MFMA blocks, one operand read per slot, a refill
  *      load every 2 of its 64 slots per K tile
  *   20 the 256x256 tiled kernel of variant 0, whatever the shape
  *   21, 22, 23 the same schedule on 256x128, 128x256 (3-stage rings) and
  *      128x128 (4-stage ring) output tiles (4 waves of 128x64, 64x128,
  *      64x64): the smaller tiles of variant 0, whatever the shape
  *   24, 25, 26 as 21, 22, 23 with 2-stage rings   27 as 23 with 5 stages
- *   30, 31 as 20 with the early-free K loop: a second barrier per K tile,
- *      in K step 0 at MFMA slot 32 (30) or 40 (31), after which the wave's
- *      stage is refilled, half a K tile earlier than in 20
- * Variants 1..31 always run the tiled kernel, whatever the shape; variant
+ *   30 as 20 with one barrier per K tile (the ring without the early free)
+ * Variants 1..30 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16, and some shapes with 17..64 rows on the smaller side: the skinny
  * kernel).  The skinny kernel (only for M <= 16 or N <= 16, else
@@ -359,6 +359,26 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  */
 int gemvtile_gemm_f16_variant(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
                               void *stream, int variant);
+
+/*
+ * gemvtile_gemm_f16_timed -- measurement only: the 256x256 tiled kernel of
+ * gemm_f16 (variant 20) on an M x N x K product (M, N > 16, K > 0; same
+ * result as gemm_f16), with one record of 8 uint64 per workgroup written to
+ * `stamps` (host-visible or device memory of `stamps_len` uint64, at least
+ * 8 * min(#256x256 tiles, #CUs), 8-byte aligned) by its first thread:
+ *   [0], [1]  the constant 100 MHz real-time counter and the shader-cycle
+ *             counter when the workgroup started
+ *   [2], [3]  the same when the K loop of its first output tile ended
+ *   [4], [5]  the same when it finished, after every store of every wave
+ *             completed
+ *   [6], [7]  the HW_ID and XCC_ID hardware registers (XCD in bits 0..3 of
+ *             the latter)
+ * Cycle deltas over real-time deltas give the clock each workgroup ran at.
+ * Returns GEMVTILE_ERR_UNSUPPORTED for shapes gemm_f16 would not run on the
+ * tiled kernel, GEMVTILE_ERR_INVALID_ARG for too small a buffer.
+ */
+int gemvtile_gemm_f16_timed(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream,
+                            uint64_t *stamps, int64_t stamps_len);
 
 /*
  * gemvtile_gemv_f16_variant -- gemv_f16 with an internal launch shape, for
@@ -384,7 +404,7 @@ int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, 
  * walker over K tiles that issues tile loads, operand reads, MFMAs, waits
  * and barriers; this runs the same walker on the host for the kernel of
  * tiled variant `variant` (a gemvtile_gemm_f16_variant number: 0 = 20, the
- * 256x256 default; 1 and 3 share its ring; 10 and 20..27, 30, 31) over `ktu`
+ * 256x256 default; 1 and 3 share its ring; 10, 20..27 and 30) over `ktu`
  * K tiles (of 64 elements), recording each event instead of issuing it.
  * The ring follows "使用 TMA 为 GEMM 建立 Pipeline" (TVM TIRx GEMM chapter),
  * step 5 (Pipeline 机制): K tile k in stage k % stages, refilled with tile

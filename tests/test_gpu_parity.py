@@ -278,7 +278,7 @@ def test_output_guard_band(env):
     assert np.array_equal(D.cpu().numpy(), oracle.gemm(A, B))
 
 
-TILED_VARIANTS = [1, 2, 3, 10, 20, 21, 22, 23, 24, 25, 26, 27, 30, 31, 32, 33, 34, 35, 36]
+TILED_VARIANTS = [1, 2, 3, 10, 20, 21, 22, 23, 24, 25, 26, 27, 30]
 
 
 @pytest.mark.parametrize("variant", TILED_VARIANTS)
@@ -293,7 +293,7 @@ def test_gemm_variants_bit_identical(env, variant):
     assert np.array_equal(_gemm(env, A, B, variant).cpu().numpy(), base)
 
 
-@pytest.mark.parametrize("variant", [0, 2, 10, 20, 21, 22, 23, 24, 25, 26, 27, 30, 31, 32, 33, 34, 35, 36])
+@pytest.mark.parametrize("variant", [0, 2, 10, 20, 21, 22, 23, 24, 25, 26, 27, 30])
 @pytest.mark.parametrize("K", [8, 64, 72, 128, 136, 192, 200, 264, 328])
 def test_gemm_variants_few_k_tiles(env, variant, K):
     """1 to 6 K tiles of 64, whole and ragged: the prologue, the last refill
@@ -371,3 +371,31 @@ def test_misaligned_pointer_is_rejected(env):
     with pytest.raises(gt.GemvTileError) as e:
         gt.gemm_f16(A, B)
     assert e.value.status == 2
+
+
+def test_timed_gemm_matches_and_stamps_are_sane(env):
+    """gemvtile_gemm_f16_timed computes what the 256x256 kernel computes, and
+    each workgroup's stamps are ordered and give a plausible clock."""
+    torch, gt, dev = env
+    lib = gt.load_library()
+    M, N, K = 1000, 1300, 1032
+    Ai = datagen.integer_f16(6300, 10, (M, K))
+    Bi = datagen.integer_f16(6300, 11, (N, K))
+    tA, tB = torch.from_numpy(Ai).to(dev), torch.from_numpy(Bi).to(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    grid = min(((M + 255) // 256) * ((N + 255) // 256), cus)
+    stamps = torch.zeros((grid * 8,), dtype=torch.int64, device=dev)
+    D = torch.empty((M, N), dtype=torch.float16, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    assert lib.gemvtile_gemm_f16_timed(tA.data_ptr(), tB.data_ptr(), D.data_ptr(), M, N, K, s, stamps.data_ptr(),
+                                       grid * 8 - 1) == 1  # too small a buffer
+    assert lib.gemvtile_gemm_f16_timed(tA.data_ptr(), tB.data_ptr(), D.data_ptr(), M, N, K, s, stamps.data_ptr(),
+                                       grid * 8) == 0
+    torch.cuda.synchronize(dev)
+    assert np.array_equal(D.cpu().numpy(), oracle.gemm(Ai, Bi))
+    st = stamps.cpu().numpy().reshape(grid, 8).astype(np.int64)
+    assert (st[:, 0] > 0).all() and (st[:, 0] <= st[:, 2]).all() and (st[:, 2] <= st[:, 4]).all()
+    assert (st[:, 1] <= st[:, 3]).all() and (st[:, 3] <= st[:, 5]).all()
+    mhz = (st[:, 5] - st[:, 1]) / np.maximum(st[:, 4] - st[:, 0], 1) * 100.0
+    assert ((mhz > 300) & (mhz < 3500)).all(), mhz
+    assert set((st[:, 7] & 0xF).tolist()) <= set(range(8))
