@@ -45,9 +45,13 @@ time.  --only copy runs nothing of the library: 20 device-to-device copies of
 a 256 MiB buffer, the known-size reference that hardware traffic counters
 are calibrated against.  --only gemm_variants / gemv_variants time the
 internal ablation variants (gemvtile_gemm_f16_variant / _gemv_f16_variant)
-against each other, one launch (GEMM) or five launches over five copies of
-W (GEMV) per variant in turn, each bracketed by events, after 1 s of the
-same rotation untimed, and print one line per variant and shape.
+against each other after 1 s of the same rotation untimed: in each round,
+each variant in turn runs one untimed launch (which absorbs the switch from
+the previous variant) and then a timed block between two events, of four
+launches (GEMM) or of five launches over five copies of W (GEMV); one line
+per variant and shape.  Before each GEMV block a 512 MiB buffer is read
+(untimed), so no variant finds copies of W left in the 256 MB last-level
+cache.
 """
 from __future__ import annotations
 
@@ -75,7 +79,12 @@ CONFIG_REPS = {0: 200, 2: 50, 4: 10}  # timed launches per extra workload
 # valid only for the kernel sources whose SHA-256 is recorded here; the
 # summary and commands are in profiles/traffic_fetch_write_size.md.
 MEASURED_TRAFFIC = {
-    "sources_sha256": None,
+    "sources_sha256": "0a3e218016ec32d903f566a98214448fd7eed78a5a414666a8fb66ab3f1b147e",
+    "gemm": {"fetch_kib": 98429.5 * 2.0, "write_kib": 32791.0 * 1.0},
+    "gemv": {"fetch_kib": 57481.1 * 2.0, "write_kib": 8.0 * 1.0},
+    "decode": {"fetch_kib": 58264.5 * 2.0, "write_kib": 64.0 * 1.0},
+    "gemm_bf16": {"fetch_kib": 98421.0 * 2.0, "write_kib": 32780.3 * 1.0},
+    "gemv_bf16": {"fetch_kib": 57481.0 * 2.0, "write_kib": 8.0 * 1.0},
 }
 KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemm_kernel.hpp", "gemm_plain.hip", "gemv.hip", "kernels.hpp",
                   "ring.hpp", "skinny.hip", "tile_order.hpp")
@@ -105,7 +114,8 @@ def parse():
     p.add_argument("--only", choices=("gemm", "gemv", "decode", "bf16", "configs", "vendor", "clock", "copy",
                                       "gemm_variants", "gemv_variants"), default=None)
     p.add_argument("--variants", default="0", help="--only gemm_variants / gemv_variants: variant numbers, "
-                   "comma-separated (gemm: -1 = the vendor GEMM, torch.matmul)")
+                   "comma-separated (gemm: -1 = the vendor GEMM, torch.matmul; -2 = gemm_splitk_f16 with a workspace; "
+                   "-3 = gemm_bias_f16 with a bias and ReLU; -4 = gemm_bf16 on the same shapes)")
     p.add_argument("--shapes", default="4096x4096x4096", help="--only gemm_variants: MxNxK list; gemv_variants: NxK "
                    "list, or RxNxK for gemm_f16 variants on an R-row activation batch against W [N,K]")
     p.add_argument("--data", choices=("uniform", "zero"), default="uniform", help="--only gemm_variants inputs")
@@ -313,6 +323,11 @@ def variant_sweep(args, torch, np, gt, datagen, dev):
     variants = [int(v) for v in args.variants.split(",")]
     out = {"only": args.only, "data": args.data, "results": []}
 
+    # a 512 MiB buffer read (not written: no write-backs left behind) before
+    # each GEMV variant's block, so none finds W left in the last-level cache
+    flush = torch.ones((128 << 20,), dtype=torch.int32, device=dev) if args.only == "gemv_variants" else None
+    block = 4 if args.only == "gemm_variants" else 1
+
     def interleaved(run, n_per):
         t_end = time.perf_counter() + 1.0
         i = 0
@@ -324,13 +339,17 @@ def variant_sweep(args, torch, np, gt, datagen, dev):
         ev = {v: [] for v in variants}
         for r in range(args.reps):
             for v in variants:
+                if flush is not None:
+                    flush.max()
+                run(v, r)  # untimed: absorbs the switch from the previous variant
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                run(v, r)
+                for b in range(block):
+                    run(v, r + 1 + b)
                 e1.record(stream)
                 ev[v].append((e0, e1))
         torch.cuda.synchronize(dev)
-        return {v: np.array([a.elapsed_time(b) for a, b in ev[v]]) * 1e3 / n_per for v in variants}
+        return {v: np.array([a.elapsed_time(b) for a, b in ev[v]]) * 1e3 / (n_per * block) for v in variants}
 
     for shape in args.shapes.split(","):
         dims = [int(t) for t in shape.split("x")]
@@ -345,11 +364,25 @@ def variant_sweep(args, torch, np, gt, datagen, dev):
                     A = torch.from_numpy(datagen.uniform_f16(50 + i, 0, (M, K), -1.0, 1.0)).to(dev)
                     B = torch.from_numpy(datagen.uniform_f16(50 + i, 1, (N, K), -1.0, 1.0)).to(dev)
                 sets.append((A, B, torch.empty((M, N), dtype=torch.float16, device=dev)))
+            if -2 in variants:
+                ws = gt.alloc_splitk_workspace(sets[0][0], sets[0][1])
+            if -3 in variants:
+                bias = torch.from_numpy(datagen.uniform_f16(1, 3, (N,), -4.0, 4.0)).to(dev)
+            if -4 in variants:
+                bsets = [(A.to(torch.bfloat16), B.to(torch.bfloat16), torch.empty((M, N), dtype=torch.bfloat16,
+                                                                                   device=dev)) for A, B, _ in sets]
 
             def run(v, i):
                 A, B, D = sets[i % len(sets)]
-                if v < 0:
+                if v == -1:
                     torch.matmul(A, B.t(), out=D)
+                elif v == -2:
+                    gt.gemm_splitk_f16(A, B, D, workspace=ws)
+                elif v == -3:
+                    gt.gemm_bias_f16(A, B, bias, gt.ACT_RELU, D)
+                elif v == -4:
+                    Ab, Bb, Db = bsets[i % len(bsets)]
+                    gt.gemm_bf16(Ab, Bb, Db)
                 else:
                     st = lib.gemvtile_gemm_f16_variant(A.data_ptr(), B.data_ptr(), D.data_ptr(), M, N, K, sh, v)
                     if st:
