@@ -118,7 +118,9 @@ def parse():
                    "-3 = gemm_bias_f16 with a bias and ReLU; -4 = gemm_bf16 on the same shapes)")
     p.add_argument("--shapes", default="4096x4096x4096", help="--only gemm_variants: MxNxK list; gemv_variants: NxK "
                    "list, or RxNxK for gemm_f16 variants on an R-row activation batch against W [N,K]")
-    p.add_argument("--data", choices=("uniform", "zero"), default="uniform", help="--only gemm_variants inputs")
+    p.add_argument("--data", choices=("uniform", "zero", "mant7"), default="uniform",
+                   help="--only gemm_variants inputs: seeded U(-1,1) fp16, all zeros, or the same U(-1,1) fp16 values "
+                   "with the low 3 of their 10 mantissa bits cleared (the mantissa width of bf16)")
     p.add_argument("--reps", type=int, default=24, help="--only gemm_variants / gemv_variants timed rounds")
     p.add_argument("--clock-s", type=float, default=2.0, help="seconds of sampled load per data set in the clock section")
     return p.parse_args()
@@ -363,6 +365,9 @@ def variant_sweep(args, torch, np, gt, datagen, dev):
                 else:
                     A = torch.from_numpy(datagen.uniform_f16(50 + i, 0, (M, K), -1.0, 1.0)).to(dev)
                     B = torch.from_numpy(datagen.uniform_f16(50 + i, 1, (N, K), -1.0, 1.0)).to(dev)
+                    if args.data == "mant7":
+                        A.view(torch.int16).bitwise_and_(-8)
+                        B.view(torch.int16).bitwise_and_(-8)
                 sets.append((A, B, torch.empty((M, N), dtype=torch.float16, device=dev)))
             if -2 in variants:
                 ws = gt.alloc_splitk_workspace(sets[0][0], sets[0][1])

@@ -460,17 +460,29 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       };
       // The bias of every column this lane holds, loaded once per tile
       // (columns past N read the last bias; their outputs are not stored).
+      // The null test is made once, outside the loads: inside them it put
+      // every load under its own branch, each waited for before the next.
       float bv[S::kFragN][S::kAccRegs];
       if constexpr (EPI == kEpiFused) {
+        if (bias != nullptr) {
+          uint16_t raw[S::kFragN][S::kAccRegs];
 #pragma unroll
-        for (int j = 0; j < S::kFragN; ++j)
+          for (int j = 0; j < S::kFragN; ++j)
 #pragma unroll
-          for (int g = 0; g < S::kAccRegs / 4; ++g)
+            for (int g = 0; g < S::kAccRegs / 4; ++g)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int n = min(n0 + wn * S::kWaveN + lane_col(j, g) + e, N - 1);
-              bv[j][4 * g + e] = bias ? widen_in<S::DTYPE>(bias[n]) : 0.0f;
-            }
+              for (int e = 0; e < 4; ++e)
+                raw[j][4 * g + e] = bias[min(n0 + wn * S::kWaveN + lane_col(j, g) + e, N - 1)];
+#pragma unroll
+          for (int j = 0; j < S::kFragN; ++j)
+#pragma unroll
+            for (int r = 0; r < S::kAccRegs; ++r) bv[j][r] = widen_in<S::DTYPE>(raw[j][r]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < S::kFragN; ++j)
+#pragma unroll
+            for (int r = 0; r < S::kAccRegs; ++r) bv[j][r] = 0.0f;
+        }
       }
 #pragma unroll
       for (int i = 0; i < S::kFragM; ++i) {

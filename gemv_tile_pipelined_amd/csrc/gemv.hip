@@ -261,25 +261,12 @@ hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, i
     case 10: return launch<2, 8, 4, true, true, kF16, 4>(x, W, y, N, K, stream);
     case 11: return launch<2, 8, 4, true, true, kF16, 8>(x, W, y, N, K, stream);
     case 12: return launch<1, 8, 4, true, true, kF16, 8>(x, W, y, N, K, stream);
-    // grid-strided rows; x staged in LDS; deeper unroll; other wave shapes
+    // grid-strided rows; x staged in LDS once per workgroup
     case 20: return launch<2, 8, 4, true, true, kF16, 1, 1>(x, W, y, N, K, stream);
     case 21: return launch<2, 8, 4, true, true, kF16, 1, 0, true>(x, W, y, N, K, stream);
-    case 22: return launch<2, 8, 4, true, true, kF16, 1, 1, true>(x, W, y, N, K, stream);
-    case 23: return launch<2, 8, 8, true, true, kF16, 1, 1>(x, W, y, N, K, stream);
-    case 24: return launch<4, 4, 4, true, true, kF16, 1, 1>(x, W, y, N, K, stream);
-    case 25: return launch<1, 16, 4, true, true, kF16, 1, 1>(x, W, y, N, K, stream);
-    case 26: return launch<4, 4, 4, true, true, kF16, 1, 1, true>(x, W, y, N, K, stream);
-    case 27: return launch<2, 8, 4, true, false, kF16, 1, 1>(x, W, y, N, K, stream);
-    // no rotated start: deeper / shallower unroll, other wave shapes, K splits
+    // no rotated start: 8 chunk steps in flight; 4 rows per wave, 4 waves
     case 28: return launch<2, 8, 8, true, false>(x, W, y, N, K, stream);
     case 29: return launch<4, 4, 4, true, false>(x, W, y, N, K, stream);
-    case 30: return launch<2, 8, 2, true, false>(x, W, y, N, K, stream);
-    case 31: return launch<1, 8, 4, true, false>(x, W, y, N, K, stream);
-    case 32: return launch<2, 8, 4, true, false, kF16, 2>(x, W, y, N, K, stream);
-    case 33: return launch<2, 8, 4, true, false, kF16, 4>(x, W, y, N, K, stream);
-    case 34: return launch<2, 8, 4, true, false, kF16, 8>(x, W, y, N, K, stream);
-    case 35: return launch<1, 8, 4, true, false, kF16, 8>(x, W, y, N, K, stream);
-    case 36: return launch<4, 8, 4, true, false>(x, W, y, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -94,7 +94,7 @@ inline int gemm_splitk_splits(int64_t M, int64_t N, int64_t K, int num_cus) {
   return saved >= cost ? static_cast<int>(splits) : 1;
 }
 // gemvtile_gemv_f16_variant numbers of the GEMV kernel's launch shapes.
-inline bool gemv_variant_exists(int v) { return v == 0 || (v >= 6 && v <= 12) || (v >= 20 && v <= 36); }
+inline bool gemv_variant_exists(int v) { return v == 0 || (v >= 6 && v <= 12) || v == 20 || v == 21 || v == 28 || v == 29; }
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip).
 constexpr int kSkinnyMaxRows = 16;

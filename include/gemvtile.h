@@ -350,6 +350,7 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
  *   130 as 112 with each workgroup starting its K walk at a different K tile
  *   147 as 130 with the large side loaded non-temporally (the gemm_f16
  *       choice at 16 rows per workgroup)
+ *   148 as 147 with every workgroup starting its K walk at K tile 0
  * The wave-specialised kernel, whatever the shape:
  *   200, 201 256x128 output tiles, 4 consumer waves (MFMA only, 128x64
  *       each) and 4 loader waves (tile loads only) handing K tiles over at
@@ -393,6 +394,13 @@ int gemvtile_gemm_f16_timed(const void *A, const void *B, void *D, int64_t M, in
  *      K split over 1, 2, 4, 8 waves per row group (16, 8, 4, 2 rows per
  *      workgroup)
  *   12 1 row per workgroup, K split 8 ways
+ *   20 as 8 with grid-strided rows: local row r (0..15) of workgroup b is
+ *      row r*G + b (G = the grid size), so workgroups running side by side
+ *      read adjacent rows, instead of 16 consecutive rows per workgroup
+ *   21 as 8 with x staged in LDS once per workgroup (K <= 16384, else
+ *      GEMVTILE_ERR_INVALID_ARG) instead of loaded by every wave
+ *   28 as 7 with 8 chunk steps in flight
+ *   29 as 7 with 4 rows per wave and 4 waves
  * Other numbers return GEMVTILE_ERR_INVALID_ARG.
  */
 int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream,
