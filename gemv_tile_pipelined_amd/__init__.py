@@ -153,11 +153,11 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.gemvtile_xcd_logical_id.restype = i64
     lib.gemvtile_gemm_config.argtypes = [intp] * 6
     lib.gemvtile_gemm_config.restype = None
-    lib.gemvtile_gemm_grid.argtypes = [i64, i64, i64]
+    lib.gemvtile_gemm_grid.argtypes = [i64, i64, i64, i64]
     lib.gemvtile_gemm_grid.restype = i64
     lib.gemvtile_gemm_tile.argtypes = [i64, i64, i64, intp, intp, intp]
     lib.gemvtile_gemm_tile.restype = c_int
-    lib.gemvtile_gemv_grid.argtypes = [i64, i64]
+    lib.gemvtile_gemv_grid.argtypes = [i64, i64, i64]
     lib.gemvtile_gemv_grid.restype = i64
     lib.gemvtile_device_caps.argtypes = [intp] * 4
     lib.gemvtile_device_caps.restype = c_int
@@ -440,8 +440,8 @@ def gemm_config() -> dict:
     return {k: v.value for k, v in zip(keys, vals)}
 
 
-def gemm_grid(M: int, N: int, num_cus: int) -> int:
-    return int(load_library().gemvtile_gemm_grid(M, N, num_cus))
+def gemm_grid(M: int, N: int, K: int, num_cus: int) -> int:
+    return int(load_library().gemvtile_gemm_grid(M, N, K, num_cus))
 
 
 def gemm_tile(M: int, N: int, num_cus: int) -> tuple:
@@ -451,8 +451,8 @@ def gemm_tile(M: int, N: int, num_cus: int) -> tuple:
     return tuple(v.value for v in vals)
 
 
-def gemv_grid(N: int, num_cus: int) -> int:
-    return int(load_library().gemvtile_gemv_grid(N, num_cus))
+def gemv_grid(N: int, K: int, num_cus: int) -> int:
+    return int(load_library().gemvtile_gemv_grid(N, K, num_cus))
 
 
 RING_EVENTS = {1: "load", 2: "wait", 3: "lds_wait", 4: "barrier", 5: "read", 6: "mfma"}

@@ -366,15 +366,15 @@ int gemvtile_device_caps(int *num_cus, int *clock_khz, int *mem_clock_khz, int *
   return GEMVTILE_OK;
 }
 
-int64_t gemvtile_gemv_grid(int64_t N, int64_t num_cus) {
-  if (N <= 0 || num_cus <= 0 || num_cus > (int64_t{1} << 20)) return 0;
-  return gt::gemv_default_grid(N, static_cast<int>(num_cus));
+int64_t gemvtile_gemv_grid(int64_t N, int64_t K, int64_t num_cus) {
+  if (N <= 0 || K < 0 || num_cus <= 0 || num_cus > (int64_t{1} << 20)) return 0;
+  return gt::gemv_default_grid(N, K, static_cast<int>(num_cus));
 }
 
-int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus) {
-  if (M <= 0 || N <= 0 || num_cus <= 0) return 0;
+int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus) {
+  if (M <= 0 || N <= 0 || K < 0 || num_cus <= 0) return 0;
   // One row on a side: the GEMV kernel over the other side's rows.
-  if (M == 1 || N == 1) return gemvtile_gemv_grid(M == 1 ? N : M, num_cus);
+  if (M == 1 || N == 1) return gemvtile_gemv_grid(M == 1 ? N : M, K, num_cus);
   // Skinny shapes (at most 16 rows on a side, or 17..64 on the smaller
   // side as skinny_wide_route decides): one workgroup per 16, 8, 4, 2 or 1
   // rows of the other side.

@@ -234,11 +234,11 @@ static hipError_t launch(const void *x, const void *W, void *y, int N, int K, hi
 }
 
 // The default launch (gemv_default_launch): 16, 8, 4 or 2 rows per workgroup
-// with 1, 2, 4 or 8 K slices, or 1 row in 8 slices.
+// with 1, 2, 4 or 8 K slices, or 1 row in 8 slices, from N, K and the CU count.
 template <int DT>
 static hipError_t launch_auto(const void *x, const void *W, void *y, int N, int K, int num_cus, hipStream_t stream) {
   static_assert(kGemvWaves == 8, "the instantiations below use 8 waves");
-  const GemvLaunch l = gemv_default_launch(N, num_cus);
+  const GemvLaunch l = gemv_default_launch(N, K, num_cus);
   if (l.rows_per_wave == 1) return launch<1, 8, 4, true, true, DT, 8>(x, W, y, N, K, stream);
   switch (l.ksplit) {
     case 1: return launch<2, 8, 4, true, true, DT, 1>(x, W, y, N, K, stream);

@@ -97,10 +97,11 @@ int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
  *   stream hipStream_t or NULL
  *
  * N == 0: returns GEMVTILE_OK and touches nothing.  K == 0: y is filled with +0.
- * When N is too small to give every compute unit a workgroup of 16 rows, the
- * waves of a workgroup also split K (§5.2 block_split_k's reason: enough
- * blocks in flight); the slices' FP32 partial sums are added in LDS in a
- * fixed order (gemvtile_gemv_grid gives the workgroup count).  The row sums
+ * When N is too small to give every compute unit a workgroup of 16 rows, or
+ * when K >= 8192, the waves of a workgroup also split K (§5.2
+ * block_split_k's reason: enough blocks in flight); the slices' FP32 partial
+ * sums are added in LDS in a fixed order (gemvtile_gemv_grid gives the
+ * workgroup count).  The row sums
  * are deterministic: no atomics, no split across workgroups, no workspace.
  * Returns a gemvtile_status.
  */
@@ -293,18 +294,20 @@ int gemvtile_device_caps(int *num_cus, int *clock_khz, int *mem_clock_khz, int *
 
 /*
  * gemvtile_gemv_grid -- the number of workgroups gemv_f16 (and gemv_bf16)
- * launches for N rows on a device with `num_cus` compute units: ceil(N/R)
- * with R = 16 rows per workgroup when N >= 16*num_cus, else 8, 4 or 2 rows
- * (K split 2, 4 or 8 ways over the workgroup's 8 waves) while N >=
- * 8, 4 or 2 times num_cus, else 1 row (K split 8 ways).  Host-only
- * arithmetic; returns 0 for N <= 0 or num_cus outside [1, 2^20].
+ * launches for an N x K matrix on a device with `num_cus` compute units:
+ * ceil(N/R) with R = 2 rows per workgroup (K split 8 ways over the
+ * workgroup's 8 waves) when K >= 8192 and N >= 2*num_cus; otherwise R = 16
+ * rows per workgroup when N >= 16*num_cus, else 8, 4 or 2 rows (K split 2,
+ * 4 or 8 ways) while N >= 8, 4 or 2 times num_cus; else 1 row (K split 8
+ * ways).  Host-only arithmetic; returns 0 for N <= 0, K < 0 or num_cus
+ * outside [1, 2^20].
  */
-int64_t gemvtile_gemv_grid(int64_t N, int64_t num_cus);
+int64_t gemvtile_gemv_grid(int64_t N, int64_t K, int64_t num_cus);
 
 /*
  * gemvtile_gemm_grid -- the number of workgroups gemm_f16 launches for an
- * M x N output on a device with `num_cus` compute units: the GEMV grid of
- * the other side's rows when M or N is 1; when M <= 16 or N <= 16, or the
+ * M x N x K product on a device with `num_cus` compute units: the GEMV grid
+ * of the other side's rows when M or N is 1; when M <= 16 or N <= 16, or the
  * smaller side has 17..64 rows and gemm_f16 picks the skinny kernel (see
  * there), ceil(R/p) with R = N if
  * M <= 16, else M if N <= 16, else the larger side, and p the largest of
@@ -313,7 +316,7 @@ int64_t gemvtile_gemv_grid(int64_t N, int64_t num_cus);
  * persistent grid min(#tiles, num_cus) over the tiles gemvtile_gemm_tile
  * picks.  Host-only arithmetic; returns 0 for empty outputs.
  */
-int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t num_cus);
+int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
 
 /*
  * gemvtile_gemm_f16_variant -- gemm_f16 with an internal kernel variant, for
@@ -384,8 +387,8 @@ int gemvtile_gemm_f16_timed(const void *A, const void *B, void *D, int64_t M, in
 /*
  * gemvtile_gemv_f16_variant -- gemv_f16 with an internal launch shape, for
  * measurements only (same contract and results as gemv_f16):
- *   0  the gemv_f16 default (picks one of 8..12 from N and the compute-unit
- *      count, see gemvtile_gemv_grid)
+ *   0  the gemv_f16 default (picks one of 8..12 from N, K and the
+ *      compute-unit count, see gemvtile_gemv_grid)
  *   6  2 rows per wave, 8 waves, 4 chunk steps in flight, ordinary (cached)
  *      loads of W, each wave starting its walk along K at a different group
  *   7  as 6 with non-temporal loads of W and every wave starting at the

@@ -191,37 +191,38 @@ def test_xcd_renumbering_is_a_bijection(lib, grid):
 def test_gemm_grid_and_golden_counts(lib):
     cfg = gt.gemm_config()
     assert cfg == {"BM": 256, "BN": 256, "BK": 64, "stages": 2, "threads": 256, "group_m": 8}
-    assert gt.gemm_grid(4096, 4096, 256) == 256
-    assert gt.gemm_grid(8192, 8192, 256) == 256
-    assert gt.gemm_grid(256, 256, 256) == 4  # four 128x128 tiles (see the tile rule below)
-    assert gt.gemm_grid(4000, 4032, 256) == 256
-    assert gt.gemm_grid(0, 4, 256) == 0
+    assert gt.gemm_grid(4096, 4096, 4096, 256) == 256
+    assert gt.gemm_grid(8192, 8192, 4096, 256) == 256
+    assert gt.gemm_grid(256, 256, 4096, 256) == 4  # four 128x128 tiles (see the tile rule below)
+    assert gt.gemm_grid(4000, 4032, 4096, 256) == 256
+    assert gt.gemm_grid(0, 4, 4096, 256) == 0
     # skinny shapes: one workgroup per 16 rows of the larger side while that
     # gives every CU one, else per 8, 4, 2 or 1 rows
-    assert gt.gemm_grid(8, 4096, 256) == 256
-    assert gt.gemm_grid(4096, 16, 256) == 256
-    assert gt.gemm_grid(8, 8192, 256) == 512
-    assert gt.gemm_grid(8, 3000, 256) == 375
-    assert gt.gemm_grid(8, 2000, 256) == 500
-    assert gt.gemm_grid(1000, 9, 256) == 500
-    assert gt.gemm_grid(16, 300, 256) == 300
-    assert gt.gemm_grid(16, 16, 256) == 16
+    assert gt.gemm_grid(8, 4096, 4096, 256) == 256
+    assert gt.gemm_grid(4096, 16, 4096, 256) == 256
+    assert gt.gemm_grid(8, 8192, 4096, 256) == 512
+    assert gt.gemm_grid(8, 3000, 4096, 256) == 375
+    assert gt.gemm_grid(8, 2000, 4096, 256) == 500
+    assert gt.gemm_grid(1000, 9, 4096, 256) == 500
+    assert gt.gemm_grid(16, 300, 4096, 256) == 300
+    assert gt.gemm_grid(16, 16, 4096, 256) == 16
     # 17..64 rows on the smaller side: the skinny kernel too, over the larger side
-    assert gt.gemm_grid(17, 4097, 256) == 257  # 16 rows per workgroup
-    assert gt.gemm_grid(32, 1000, 256) == 500  # 2 rows per workgroup
-    assert gt.gemm_grid(4000, 30, 256) == 500  # 8 rows per workgroup
-    assert gt.gemm_grid(20, 24, 256) == 24  # the larger side, 1 row per workgroup
-    assert gt.gemm_grid(64, 4097, 256) == 257
-    assert gt.gemm_grid(65, 4097, 256) == 33  # 1 x 33 tiles of 128x128
+    assert gt.gemm_grid(17, 4097, 4096, 256) == 257  # 16 rows per workgroup
+    assert gt.gemm_grid(32, 1000, 4096, 256) == 500  # 2 rows per workgroup
+    assert gt.gemm_grid(4000, 30, 4096, 256) == 500  # 8 rows per workgroup
+    assert gt.gemm_grid(20, 24, 4096, 256) == 24  # the larger side, 1 row per workgroup
+    assert gt.gemm_grid(64, 4097, 4096, 256) == 257
+    assert gt.gemm_grid(65, 4097, 4096, 256) == 33  # 1 x 33 tiles of 128x128
     # ... while the 128x128 tiles along the larger side would leave more than
     # half (up to 32 rows) or three quarters (33..64) of the CUs idle
-    assert gt.gemm_grid(32, 16384, 256) == 1024  # 128 tiles: skinny, 16 rows per workgroup
-    assert gt.gemm_grid(32, 16385, 256) == 129  # 129 tiles: tiled
-    assert gt.gemm_grid(64, 8192, 256) == 512  # 64 tiles: skinny
-    assert gt.gemm_grid(14336, 64, 256) == 112  # 112 tiles: tiled
+    assert gt.gemm_grid(32, 16384, 4096, 256) == 1024  # 128 tiles: skinny, 16 rows per workgroup
+    assert gt.gemm_grid(32, 16385, 4096, 256) == 129  # 129 tiles: tiled
+    assert gt.gemm_grid(64, 8192, 4096, 256) == 512  # 64 tiles: skinny
+    assert gt.gemm_grid(14336, 64, 4096, 256) == 112  # 112 tiles: tiled
     # one row on a side: the GEMV grid of the other side
-    assert gt.gemm_grid(1, 4096, 256) == gt.gemv_grid(4096, 256) == 256
-    assert gt.gemm_grid(1000, 1, 256) == gt.gemv_grid(1000, 256)
+    assert gt.gemm_grid(1, 4096, 4096, 256) == gt.gemv_grid(4096, 4096, 256) == 256
+    assert gt.gemm_grid(1000, 1, 4096, 256) == gt.gemv_grid(1000, 4096, 256)
+    assert gt.gemm_grid(1, 4096, 14336, 256) == gt.gemv_grid(4096, 14336, 256) == 2048
     golden = _tile_counts()
     # The TVM chapter's counts at its 128x128 tiles and BLK_K = 64: the same
     # tile-count arithmetic, applied to its parameters.
@@ -255,7 +256,7 @@ def test_gemm_tile_rule(lib):
     for (M, N), tile in want.items():
         assert gt.gemm_tile(M, N, 256) == tile, (M, N)
         bm, bn, _ = tile
-        assert gt.gemm_grid(M, N, 256) == min(-(-M // bm) * -(-N // bn), 256), (M, N)
+        assert gt.gemm_grid(M, N, 4096, 256) == min(-(-M // bm) * -(-N // bn), 256), (M, N)
     # the documented cost, ceil(#tiles / CUs) * bm * bn / rate, is least for
     # the chosen tile, and no larger tile ties it
     shapes = [(bm, bn, st, rate) for bm, bn, st, rate in
@@ -412,26 +413,41 @@ def test_measurement_formulas_match_table1():
 
 def test_gemv_grid_gives_every_cu_a_workgroup(lib):
     """gemv_f16 splits K over the waves of a workgroup when N alone would
-    leave compute units idle: 16, 8, 4, 2 rows per workgroup, then 1."""
-    assert gt.gemv_grid(4096, 256) == 256  # 16 rows per workgroup, no split
-    assert gt.gemv_grid(4097, 256) == 257
-    assert gt.gemv_grid(8192, 256) == 512
-    assert gt.gemv_grid(4095, 256) == 512  # 8 rows per workgroup
-    assert gt.gemv_grid(2048, 256) == 256
-    assert gt.gemv_grid(1024, 256) == 256  # 4 rows
-    assert gt.gemv_grid(1031, 256) == 258
-    assert gt.gemv_grid(512, 256) == 256  # 2 rows
-    assert gt.gemv_grid(511, 256) == 511  # 1 row
-    assert gt.gemv_grid(1, 256) == 1
-    assert gt.gemv_grid(0, 256) == 0
-    assert gt.gemv_grid(5, 0) == 0
-    for N in list(range(1, 70)) + [255, 256, 257, 1000, 3000, 4096, 10000, 14336]:
-        for cus in (1, 8, 80, 256, 304):
-            g = gt.gemv_grid(N, cus)
-            assert g >= 1
-            if N >= 2 * cus:
-                assert g >= cus  # every CU gets a workgroup
-            # the documented rule: the largest of 16, 8, 4, 2 rows per
-            # workgroup with N >= rows * cus, else 1
-            rows = next((r for r in (16, 8, 4, 2) if N >= r * cus), 1)
-            assert g == -(-N // rows)
+    leave compute units idle (16, 8, 4, 2 rows per workgroup, then 1), and
+    always takes 2 rows per workgroup (K split 8 ways) for K >= 8192 while
+    that gives every CU a workgroup."""
+    K = 4096
+    assert gt.gemv_grid(4096, K, 256) == 256  # 16 rows per workgroup, no split
+    assert gt.gemv_grid(4097, K, 256) == 257
+    assert gt.gemv_grid(8192, K, 256) == 512
+    assert gt.gemv_grid(4095, K, 256) == 512  # 8 rows per workgroup
+    assert gt.gemv_grid(2048, K, 256) == 256
+    assert gt.gemv_grid(1024, K, 256) == 256  # 4 rows
+    assert gt.gemv_grid(1031, K, 256) == 258
+    assert gt.gemv_grid(512, K, 256) == 256  # 2 rows
+    assert gt.gemv_grid(511, K, 256) == 511  # 1 row
+    assert gt.gemv_grid(1, K, 256) == 1
+    assert gt.gemv_grid(0, K, 256) == 0
+    assert gt.gemv_grid(5, K, 0) == 0
+    assert gt.gemv_grid(5, -8, 256) == 0
+    # long rows: 2 rows per workgroup from N = 2 * CUs up
+    assert gt.gemv_grid(4096, 8184, 256) == 256
+    assert gt.gemv_grid(4096, 8192, 256) == 2048
+    assert gt.gemv_grid(4096, 14336, 256) == 2048
+    assert gt.gemv_grid(512, 14336, 256) == 256
+    assert gt.gemv_grid(511, 14336, 256) == 511
+    for K in (0, 8, 4096, 8184, 8192, 14336, 65536):
+        for N in list(range(1, 70)) + [255, 256, 257, 1000, 3000, 4096, 10000, 14336]:
+            for cus in (1, 8, 80, 256, 304):
+                g = gt.gemv_grid(N, K, cus)
+                assert g >= 1
+                if N >= 2 * cus:
+                    assert g >= cus  # every CU gets a workgroup
+                # the documented rule: 2 rows per workgroup when K >= 8192
+                # and N >= 2 * cus; else the largest of 16, 8, 4, 2 rows per
+                # workgroup with N >= rows * cus, else 1
+                if K >= 8192 and N >= 2 * cus:
+                    rows = 2
+                else:
+                    rows = next((r for r in (16, 8, 4, 2) if N >= r * cus), 1)
+                assert g == -(-N // rows)

@@ -3,10 +3,12 @@
 For N below 16 rows per compute unit, gemv_f16 splits K over the waves of a
 workgroup (2, 4 or 8 slices, or one row per workgroup in 8 slices) and adds
 the slices' FP32 row sums in LDS in slice order ("Learning TileLang with
-GEMV", §5.2 block_split_k: split K when N alone gives too few blocks).  Each
-level is exercised at sizes around its thresholds (on a 256-CU part: N >= 4096,
-2048, 1024, 512, else 1 row), with K tails that leave slices partly or wholly
-empty (K = 8 is one 16-byte chunk, so only the last slice has work).
+GEMV", §5.2 block_split_k: split K when N alone gives too few blocks); for
+K >= 8192 it takes 2 rows per workgroup in 8 slices whatever N.  Each level
+is exercised at sizes around its thresholds (on a 256-CU part: N >= 4096,
+2048, 1024, 512, else 1 row; K >= 8192), with K tails that leave slices
+partly or wholly empty (K = 8 is one 16-byte chunk, so only the last slice
+has work).
 
 Bar as elsewhere: |d - ref| <= 1e-2 + 1e-2·|ref| for uniform inputs,
 bit-for-bit for integer inputs (exact FP32 partial sums in any order).
@@ -52,11 +54,15 @@ def _violations(got, ref):
 # (K/8 not a multiple of 64), and K shorter than one step per slice.
 SHAPES = [
     (4095, 4104),  # 8 rows per workgroup (2 slices)
-    (2048, 14336),
+    (2048, 4096),
     (2047, 520),  # 4 rows (4 slices)
-    (1024, 14344),
+    (1024, 4104),
     (1031, 72),
     (1000, 4096),  # 2 rows (8 slices)
+    (4097, 8192),  # K >= 8192: 2 rows (8 slices) whatever N
+    (4096, 8184),  # just below: 16 rows, no split
+    (2048, 14336),
+    (1024, 14344),
     (512, 16392),
     (511, 14336),  # 1 row (8 slices)
     (257, 8),
