@@ -122,10 +122,10 @@ inline bool skinny_wide_route(int64_t M, int64_t N, int num_cus) {
 // and not kept stay unused.
 constexpr int kSkinnyVariantBase = 100;
 constexpr int kGemmWsVariantBase = 200;
-inline bool skinny_variant_exists(int v) { return v == 0 || v == 4 || v == 12 || v == 30 || v == 47 || v == 48; }
+inline bool skinny_variant_exists(int v) { return v == 0 || v == 4 || v == 12 || v == 30 || v == 47 || v == 52; }
 // Wave-specialised (producer / consumer) GEMM launch shapes (gemm_ws.hip).
 constexpr int kGemmWsVariants = 2;
-static_assert(kGemmVariants <= kSkinnyVariantBase && kSkinnyVariantBase + 49 <= kGemmWsVariantBase,
+static_assert(kGemmVariants <= kSkinnyVariantBase && kSkinnyVariantBase + 53 <= kGemmWsVariantBase,
               "variant families must not overlap");
 
 // The default GEMV launch for an N x K matrix on a device with num_cus

@@ -424,7 +424,7 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
     // as 30 with non-temporal loads of P (the default at 16 P rows)
     case 47: return launch_lds<16, 4, 16, kF16, 16, true, true>(P, Q, D, R, S, K, !small_m, stream);
     // as 47 without the rotated K start
-    case 48: return launch_lds<16, 4, 16, kF16, 16, false, true>(P, Q, D, R, S, K, !small_m, stream);
+    case 52: return launch_lds<16, 4, 16, kF16, 16, false, true>(P, Q, D, R, S, K, !small_m, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -353,7 +353,7 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
  *   130 as 112 with each workgroup starting its K walk at a different K tile
  *   147 as 130 with the large side loaded non-temporally (the gemm_f16
  *       choice at 16 rows per workgroup)
- *   148 as 147 with every workgroup starting its K walk at K tile 0
+ *   152 as 147 with every workgroup starting its K walk at K tile 0
  * The wave-specialised kernel, whatever the shape:
  *   200, 201 256x128 output tiles, 4 consumer waves (MFMA only, 128x64
  *       each) and 4 loader waves (tile loads only) handing K tiles over at

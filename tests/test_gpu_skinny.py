@@ -20,7 +20,7 @@ TOL_ABS = 1e-2
 TOL_REL = 1e-2
 
 # gemvtile_gemm_f16_variant ids of the skinny launch shapes
-SKINNY_VARIANTS = [100, 104, 112, 130, 147, 148]
+SKINNY_VARIANTS = [100, 104, 112, 130, 147, 152]
 
 
 @pytest.fixture(scope="module")
