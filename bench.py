@@ -13,7 +13,8 @@ a clock that the kernels never see in steady use.  Both phases are untimed.
 
 Prints ONE JSON line on stdout:
   value        GEMM TFLOP/s (2·M·N·K / mean GEMM kernel time, HIP events on
-               the stream the kernels run on)
+               the stream the kernels run on, created without the
+               system-scope fence: see TimingEvent)
   roofline     GEMM against the dense fp16 MFMA peak
   gemv         GEMV GB/s (algorithmic bytes 2·(N·K + K + N) / mean kernel time,
                the five back-to-back launches of a step timed together)
@@ -79,12 +80,12 @@ CONFIG_REPS = {0: 200, 2: 50, 4: 10}  # timed launches per extra workload
 # valid only for the kernel sources whose SHA-256 is recorded here; the
 # summary and commands are in profiles/traffic_fetch_write_size.md.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "0a3e218016ec32d903f566a98214448fd7eed78a5a414666a8fb66ab3f1b147e",
-    "gemm": {"fetch_kib": 98429.5 * 2.0, "write_kib": 32791.0 * 1.0},
-    "gemv": {"fetch_kib": 57481.1 * 2.0, "write_kib": 8.0 * 1.0},
+    "sources_sha256": "ab81cae90ac6f20e8710fc86667c202f2763a41ec506a07e936252e040b81689",
+    "gemm": {"fetch_kib": 98428.0 * 2.0, "write_kib": 32782.7 * 1.0},
+    "gemv": {"fetch_kib": 57482.6 * 2.0, "write_kib": 64.0 * 1.0},
     "decode": {"fetch_kib": 58264.5 * 2.0, "write_kib": 64.0 * 1.0},
-    "gemm_bf16": {"fetch_kib": 98421.0 * 2.0, "write_kib": 32780.3 * 1.0},
-    "gemv_bf16": {"fetch_kib": 57481.0 * 2.0, "write_kib": 8.0 * 1.0},
+    "gemm_bf16": {"fetch_kib": 98421.0 * 2.0, "write_kib": 32786.4 * 1.0},
+    "gemv_bf16": {"fetch_kib": 57482.5 * 2.0, "write_kib": 64.0 * 1.0},
 }
 KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemm_kernel.hpp", "gemm_plain.hip", "gemv.hip", "kernels.hpp",
                   "ring.hpp", "skinny.hip", "tile_order.hpp")
@@ -102,6 +103,58 @@ def kernel_sources_sha256() -> str:
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+_HIP = None
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class TimingEvent:
+    """A HIP event for timing only (record on a stream, elapsed time between
+    two), created with hipEventDisableSystemFence.  A default event makes a
+    system-scope release when it is recorded: an L2 write-back and invalidate
+    that lands inside the timed interval and leaves the next kernel to start
+    on an invalidated L2.  Timing events need neither (the elapsed time is
+    read after a device synchronisation), and without them a per-launch
+    event pair measures the kernel rather than the fence.  Same interface as
+    TimingEvent() for record() and elapsed_time();
+    the HIP runtime is the one torch has loaded."""
+
+    def __init__(self):
+        import ctypes
+
+        global _HIP
+        if _HIP is None:
+            path = next((ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln), None)
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded (torch.cuda must be initialised first)")
+            _HIP = ctypes.CDLL(path)
+            _HIP.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            _HIP.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            _HIP.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            _HIP.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        st = _HIP.hipEventCreateWithFlags(ctypes.byref(self.ev), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if st:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self, stream):
+        st = _HIP.hipEventRecord(self.ev, self._ct.c_void_p(stream.cuda_stream))
+        if st:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both must have completed)."""
+        ms = self._ct.c_float()
+        st = _HIP.hipEventElapsedTime(self._ct.byref(ms), self.ev, end.ev)
+        if st:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def __del__(self):
+        if _HIP is not None and self.ev:
+            _HIP.hipEventDestroy(self.ev)
 
 
 def parse():
@@ -349,7 +402,7 @@ def variant_sweep(args, torch, np, gt, datagen, dev):
                 if flush is not None:
                     flush.max()
                 run(v, r)  # untimed: absorbs the switch from the previous variant
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0, e1 = TimingEvent(), TimingEvent()
                 e0.record(stream)
                 for b in range(block):
                     run(v, r + 1 + b)
@@ -537,7 +590,7 @@ def main():
                                                           gemm_sets[i % GEMM_SETS][2].data_ptr(), M, N, K, sh)))
     torch.cuda.synchronize(dev)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     if main_steps:
@@ -603,7 +656,7 @@ def main():
     def timed(fn, reps, warm=SECTION_WARMUP):
         for i in range(warm):
             fn(i)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        evs = [[TimingEvent() for _ in range(2)] for _ in range(reps)]
         torch.cuda.synchronize(dev)
         for i, e in enumerate(evs):
             e[0].record(stream)
@@ -654,7 +707,7 @@ def main():
 
         for i in range(SECTION_WARMUP):
             pair(i)
-        vev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(VENDOR_REPS)]
+        vev = [[TimingEvent() for _ in range(3)] for _ in range(VENDOR_REPS)]
         torch.cuda.synchronize(dev)
         for i, e in enumerate(vev):
             pair(i, e)
@@ -719,7 +772,7 @@ def main():
 
         for _ in range(SECTION_WARMUP):
             bf16_step()
-        bf_events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(BF16_REPS)]
+        bf_events = [[TimingEvent() for _ in range(3)] for _ in range(BF16_REPS)]
         torch.cuda.synchronize(dev)
         for e in bf_events:
             bf16_step(e)
@@ -775,7 +828,7 @@ def main():
                     clock.setdefault("amdsmi_error", repr(e))
                 t_end = time.perf_counter() + args.clock_s
                 n = 0
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0, e1 = TimingEvent(), TimingEvent()
                 e0.record(stream)
                 while time.perf_counter() < t_end or n < n_keep:
                     for _ in range(50):
