@@ -109,6 +109,19 @@ _HIP = None
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
 
+_FENCED_EVENTS = False
+
+
+def new_event():
+    """A timing event: fence-free (TimingEvent), or torch's default one with
+    --fenced-events."""
+    if _FENCED_EVENTS:
+        import torch
+
+        return torch.cuda.Event(enable_timing=True)
+    return TimingEvent()
+
+
 class TimingEvent:
     """A HIP event for timing only (record on a stream, elapsed time between
     two), created with hipEventDisableSystemFence.  A default event makes a
@@ -117,7 +130,7 @@ class TimingEvent:
     on an invalidated L2.  Timing events need neither (the elapsed time is
     read after a device synchronisation), and without them a per-launch
     event pair measures the kernel rather than the fence.  Same interface as
-    TimingEvent() for record() and elapsed_time();
+    torch.cuda.Event(enable_timing=True) for record() and elapsed_time();
     the HIP runtime is the one torch has loaded."""
 
     def __init__(self):
@@ -176,6 +189,8 @@ def parse():
                    "with the low 3 of their 10 mantissa bits cleared (the mantissa width of bf16)")
     p.add_argument("--reps", type=int, default=24, help="--only gemm_variants / gemv_variants timed rounds")
     p.add_argument("--clock-s", type=float, default=2.0, help="seconds of sampled load per data set in the clock section")
+    p.add_argument("--fenced-events", action="store_true", help="time with default HIP events (torch.cuda.Event), "
+                   "which make a system-scope release when recorded, instead of fence-free ones (for comparison)")
     return p.parse_args()
 
 
@@ -402,7 +417,7 @@ def variant_sweep(args, torch, np, gt, datagen, dev):
                 if flush is not None:
                     flush.max()
                 run(v, r)  # untimed: absorbs the switch from the previous variant
-                e0, e1 = TimingEvent(), TimingEvent()
+                e0, e1 = new_event(), new_event()
                 e0.record(stream)
                 for b in range(block):
                     run(v, r + 1 + b)
@@ -484,7 +499,9 @@ def variant_sweep(args, torch, np, gt, datagen, dev):
 
 
 def main():
+    global _FENCED_EVENTS
     args = parse()
+    _FENCED_EVENTS = args.fenced_events
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(
@@ -590,7 +607,7 @@ def main():
                                                           gemm_sets[i % GEMM_SETS][2].data_ptr(), M, N, K, sh)))
     torch.cuda.synchronize(dev)
 
-    events = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
+    events = [[new_event() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     if main_steps:
@@ -616,6 +633,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
+        "timing_events": "default (system-scope fence)" if _FENCED_EVENTS else "fence-free (hipEventDisableSystemFence)",
         "config": {
             "workload": "gemm_f16 D=A·Bᵀ 4096x4096x4096 + 5x gemv_f16 y=x·Wᵀ 4096x14336 (5 distinct W), "
             "fp16 in/out, fp32 accumulate",
@@ -656,7 +674,7 @@ def main():
     def timed(fn, reps, warm=SECTION_WARMUP):
         for i in range(warm):
             fn(i)
-        evs = [[TimingEvent() for _ in range(2)] for _ in range(reps)]
+        evs = [[new_event() for _ in range(2)] for _ in range(reps)]
         torch.cuda.synchronize(dev)
         for i, e in enumerate(evs):
             e[0].record(stream)
@@ -707,7 +725,7 @@ def main():
 
         for i in range(SECTION_WARMUP):
             pair(i)
-        vev = [[TimingEvent() for _ in range(3)] for _ in range(VENDOR_REPS)]
+        vev = [[new_event() for _ in range(3)] for _ in range(VENDOR_REPS)]
         torch.cuda.synchronize(dev)
         for i, e in enumerate(vev):
             pair(i, e)
@@ -772,7 +790,7 @@ def main():
 
         for _ in range(SECTION_WARMUP):
             bf16_step()
-        bf_events = [[TimingEvent() for _ in range(3)] for _ in range(BF16_REPS)]
+        bf_events = [[new_event() for _ in range(3)] for _ in range(BF16_REPS)]
         torch.cuda.synchronize(dev)
         for e in bf_events:
             bf16_step(e)
@@ -828,7 +846,7 @@ def main():
                     clock.setdefault("amdsmi_error", repr(e))
                 t_end = time.perf_counter() + args.clock_s
                 n = 0
-                e0, e1 = TimingEvent(), TimingEvent()
+                e0, e1 = new_event(), new_event()
                 e0.record(stream)
                 while time.perf_counter() < t_end or n < n_keep:
                     for _ in range(50):
