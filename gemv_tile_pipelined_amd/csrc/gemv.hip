@@ -234,18 +234,26 @@ static hipError_t launch(const void *x, const void *W, void *y, int N, int K, hi
 }
 
 // The default launch (gemv_default_launch): 16, 8, 4 or 2 rows per workgroup
-// with 1, 2, 4 or 8 K slices, or 1 row in 8 slices, from N, K and the CU count.
+// with 1, 2, 4 or 8 K slices, or 1 row in 8 slices, from N, K and the CU
+// count, with non-temporal or cached loads of W by its size.
+template <int DT, bool NT>
+static hipError_t launch_auto_nt(const GemvLaunch &l, const void *x, const void *W, void *y, int N, int K,
+                                 hipStream_t stream) {
+  static_assert(kGemvWaves == 8, "the instantiations below use 8 waves");
+  if (l.rows_per_wave == 1) return launch<1, 8, 4, NT, true, DT, 8>(x, W, y, N, K, stream);
+  switch (l.ksplit) {
+    case 1: return launch<2, 8, 4, NT, true, DT, 1>(x, W, y, N, K, stream);
+    case 2: return launch<2, 8, 4, NT, true, DT, 2>(x, W, y, N, K, stream);
+    case 4: return launch<2, 8, 4, NT, true, DT, 4>(x, W, y, N, K, stream);
+    default: return launch<2, 8, 4, NT, true, DT, 8>(x, W, y, N, K, stream);
+  }
+}
+
 template <int DT>
 static hipError_t launch_auto(const void *x, const void *W, void *y, int N, int K, int num_cus, hipStream_t stream) {
-  static_assert(kGemvWaves == 8, "the instantiations below use 8 waves");
   const GemvLaunch l = gemv_default_launch(N, K, num_cus);
-  if (l.rows_per_wave == 1) return launch<1, 8, 4, true, true, DT, 8>(x, W, y, N, K, stream);
-  switch (l.ksplit) {
-    case 1: return launch<2, 8, 4, true, true, DT, 1>(x, W, y, N, K, stream);
-    case 2: return launch<2, 8, 4, true, true, DT, 2>(x, W, y, N, K, stream);
-    case 4: return launch<2, 8, 4, true, true, DT, 4>(x, W, y, N, K, stream);
-    default: return launch<2, 8, 4, true, true, DT, 8>(x, W, y, N, K, stream);
-  }
+  return l.nontemporal ? launch_auto_nt<DT, true>(l, x, W, y, N, K, stream)
+                       : launch_auto_nt<DT, false>(l, x, W, y, N, K, stream);
 }
 
 hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, int N, int K, int num_cus,
@@ -267,6 +275,12 @@ hipError_t launch_gemv_f16(int variant, const void *x, const void *W, void *y, i
     // no rotated start: 8 chunk steps in flight; 4 rows per wave, 4 waves
     case 28: return launch<2, 8, 8, true, false>(x, W, y, N, K, stream);
     case 29: return launch<4, 4, 4, true, false>(x, W, y, N, K, stream);
+    // as 8..12 with cached (not non-temporal) loads of W
+    case 37: return launch<2, 8, 4, false, true, kF16, 1>(x, W, y, N, K, stream);
+    case 38: return launch<2, 8, 4, false, true, kF16, 2>(x, W, y, N, K, stream);
+    case 39: return launch<2, 8, 4, false, true, kF16, 4>(x, W, y, N, K, stream);
+    case 40: return launch<2, 8, 4, false, true, kF16, 8>(x, W, y, N, K, stream);
+    case 41: return launch<1, 8, 4, false, true, kF16, 8>(x, W, y, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -94,7 +94,9 @@ inline int gemm_splitk_splits(int64_t M, int64_t N, int64_t K, int num_cus) {
   return saved >= cost ? static_cast<int>(splits) : 1;
 }
 // gemvtile_gemv_f16_variant numbers of the GEMV kernel's launch shapes.
-inline bool gemv_variant_exists(int v) { return v == 0 || (v >= 6 && v <= 12) || v == 20 || v == 21 || v == 28 || v == 29; }
+inline bool gemv_variant_exists(int v) {
+  return v == 0 || (v >= 6 && v <= 12) || v == 20 || v == 21 || v == 28 || v == 29 || (v >= 37 && v <= 41);
+}
 // GEMMs with at most this many rows on one side (M or N) take the skinny
 // kernel (skinny.hip).
 constexpr int kSkinnyMaxRows = 16;
@@ -138,26 +140,42 @@ static_assert(kGemmVariants <= kSkinnyVariantBase && kSkinnyVariantBase + 53 <= 
 // every CU a workgroup; below that the waves split K 2, 4 or 8 ways (8, 4 or
 // 2 rows per workgroup).  Below 2 rows per CU a workgroup takes one row in 8
 // slices.
+//
+// W is read with non-temporal loads when it holds kGemvStreamMinElems
+// elements or more (64 MiB of fp16), with cached loads below that: with cold
+// W every launch measured faster that way below 64 MiB (4096x4096: 7.2 ->
+// 6.7 us; 2048x8192: 7.3 -> 6.8 us; 512x4096: 3.5 -> 3.0 us), and slower
+// from 64 MiB up (8192x4096: 11.9 -> 12.8 us; 4096x14336: 19.6 -> 21.5 us).
 struct GemvLaunch {
   int rows_per_wave;
   int ksplit;
+  bool nontemporal;
 };
 constexpr int kGemvWaves = 8;
 constexpr int64_t kGemvSplitMinK = 8192;
+constexpr int64_t kGemvStreamMinElems = int64_t{1} << 25;
 inline GemvLaunch gemv_default_launch(int64_t N, int64_t K, int num_cus) {
   const int64_t c = num_cus;
-  if (K >= kGemvSplitMinK && N >= 2 * c) return {2, 8};
-  if (N >= 16 * c) return {2, 1};
-  if (N >= 8 * c) return {2, 2};
-  if (N >= 4 * c) return {2, 4};
-  if (N >= 2 * c) return {2, 8};
-  return {1, 8};
+  const bool nt = N * K >= kGemvStreamMinElems;
+  if (K >= kGemvSplitMinK && N >= 2 * c) return {2, 8, nt};
+  if (N >= 16 * c) return {2, 1, nt};
+  if (N >= 8 * c) return {2, 2, nt};
+  if (N >= 4 * c) return {2, 4, nt};
+  if (N >= 2 * c) return {2, 8, nt};
+  return {1, 8, nt};
 }
 inline int64_t gemv_default_grid(int64_t N, int64_t K, int num_cus) {
   const GemvLaunch l = gemv_default_launch(N, K, num_cus);
   const int64_t rows = static_cast<int64_t>(l.rows_per_wave) * kGemvWaves / l.ksplit;
   return (N + rows - 1) / rows;
 }
+
+// At 16 P rows per workgroup the default skinny launch streams P with
+// non-temporal loads and rotated K starts only for K of at least this many
+// elements; below it cached loads from K tile 0 measured faster (8x4096x4096:
+// 8.8 -> 7.4 us; 8x4096x6144: 10.5 -> 9.4 us), above it slower (8x4096x14336:
+// 20.3 -> 24.0 us).
+constexpr int kSkinnyStreamMinK = 8192;
 
 // P rows per workgroup of the default skinny launch for R rows of the large
 // operand: the largest of 16, 8, 4, 2 with R >= rows * num_cus, else 1.

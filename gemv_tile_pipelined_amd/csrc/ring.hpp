@@ -221,8 +221,11 @@ struct RingEarly {
   static_assert(S::STAGES >= 2 && S::kKSub == 2, "early free: two K steps per K tile");
   static_assert(S::WAR_AT >= S::kReads * S::READ_STRIDE && S::WAR_AT < S::kMfma,
                 "the free barrier follows the last operand read of K step 0, within K step 0");
-  static_assert(S::DMA_OFFSET + (S::kDmaPerStage - 1) * S::DMA_STRIDE < kTileSlots,
-                "a refill is issued in full before the next one starts");
+  // The walker issues a refill only within the K tile whose free barrier
+  // starts it: a load placed past that tile's last MFMA slot would never be
+  // issued.
+  static_assert(S::WAR_AT + S::DMA_OFFSET + (S::kDmaPerStage - 1) * S::DMA_STRIDE < kTileSlots,
+                "a refill is issued in full within the K tile that starts it");
   static_assert(kLastLoad < kTileSlots + kRawPos, "a refill is issued in full before the barrier that needs it");
   static_assert(S::STAGES * S::kDmaPerStage <= 63 && kSteadyVmcnt <= 63, "vmcnt range");
 };

@@ -325,10 +325,11 @@ hipError_t launch_gemm_skinny_splitk(int dtype, const void *A, const void *B, vo
 }
 
 // The default launch (skinny_default_rows): 16 P rows per workgroup with 16
-// waves, a 4-stage ring, rotated K starts and non-temporal P loads while R
-// gives every CU such a workgroup; else 8, 4, 2 or 1 P rows, staging 8 Q
-// rows when S <= 8 (and loading P non-temporally at 8 rows with 8 Q rows;
-// at fewer rows that measured slower).
+// waves and a 4-stage ring while R gives every CU such a workgroup, with
+// rotated K starts and non-temporal P loads from K = kSkinnyStreamMinK up
+// and cached loads from K tile 0 below it; else 8, 4, 2 or 1 P rows,
+// staging 8 Q rows when S <= 8 (and loading P non-temporally at 8 rows with
+// 8 Q rows; at fewer rows that measured slower).
 template <int DT>
 static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                                   int num_cus, hipStream_t stream) {
@@ -359,7 +360,9 @@ static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, 
   }
   const bool q8 = S <= 8;
   switch (pr) {
-    case 16: return launch_lds<16, 4, 16, DT, 16, true, true>(P, Q, D, R, S, K, trans, stream);
+    case 16:
+      if (K < kSkinnyStreamMinK) return launch_lds<16, 4, 16, DT, 16>(P, Q, D, R, S, K, trans, stream);
+      return launch_lds<16, 4, 16, DT, 16, true, true>(P, Q, D, R, S, K, trans, stream);
     case 8: return q8 ? launch_lds<8, 4, 8, DT, 8, false, true>(P, Q, D, R, S, K, trans, stream)
                       : launch_lds<8, 4, 16, DT, 8>(P, Q, D, R, S, K, trans, stream);
     case 4: return q8 ? launch_lds<4, 4, 8, DT, 4>(P, Q, D, R, S, K, trans, stream)

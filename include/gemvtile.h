@@ -388,7 +388,8 @@ int gemvtile_gemm_f16_timed(const void *A, const void *B, void *D, int64_t M, in
  * gemvtile_gemv_f16_variant -- gemv_f16 with an internal launch shape, for
  * measurements only (same contract and results as gemv_f16):
  *   0  the gemv_f16 default (picks one of 8..12 from N, K and the
- *      compute-unit count, see gemvtile_gemv_grid)
+ *      compute-unit count, see gemvtile_gemv_grid, or its cached twin
+ *      37..41 when W holds fewer than 2^25 elements)
  *   6  2 rows per wave, 8 waves, 4 chunk steps in flight, ordinary (cached)
  *      loads of W, each wave starting its walk along K at a different group
  *   7  as 6 with non-temporal loads of W and every wave starting at the
@@ -404,6 +405,7 @@ int gemvtile_gemm_f16_timed(const void *A, const void *B, void *D, int64_t M, in
  *      GEMVTILE_ERR_INVALID_ARG) instead of loaded by every wave
  *   28 as 7 with 8 chunk steps in flight
  *   29 as 7 with 4 rows per wave and 4 waves
+ *   37..41 as 8..12 with cached (not non-temporal) loads of W
  * Other numbers return GEMVTILE_ERR_INVALID_ARG.
  */
 int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, int64_t K, void *stream,

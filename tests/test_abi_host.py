@@ -125,7 +125,7 @@ def test_gemv_argument_validation(lib):
     assert _gemv(lib, FAKE + 4, FAKE, FAKE, 4, 8) == UNSUPPORTED
     assert _gemv(lib, FAKE, FAKE + 8, FAKE, 4, 8) == UNSUPPORTED
     assert _gemv(lib, FAKE, FAKE, FAKE + 1, 4, 8) == UNSUPPORTED
-    for bad in (-1, 1, 5, 13, 17, 19, 22, 27, 30, 36, 99):
+    for bad in (-1, 1, 5, 13, 17, 19, 22, 27, 30, 36, 42, 99):
         assert lib.gemvtile_gemv_f16_variant(FAKE, FAKE, FAKE, 4, 8, None, bad) == INVALID, bad
 
 

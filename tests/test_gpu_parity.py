@@ -337,7 +337,7 @@ def test_gemm_tile_choice_shapes(env, case):
     assert np.array_equal(Di[torch.from_numpy(last).to(dev)].cpu().numpy(), oracle.gemm(Ai, Bi, rows=last))
 
 
-@pytest.mark.parametrize("variant", [6, 7, 8, 9, 10, 11, 12, 20, 21, 28, 29])
+@pytest.mark.parametrize("variant", [6, 7, 8, 9, 10, 11, 12, 20, 21, 28, 29, 37, 38, 39, 40, 41])
 def test_gemv_variants_bit_identical(env, variant):
     N, K = 1031, 14344
     x = datagen.integer_f16(6001, 0, (K,))

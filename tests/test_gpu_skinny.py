@@ -53,6 +53,11 @@ SHAPES = [
     (1, 4096, 14336),
     (2, 520, 1032),
     (8, 4096, 14336),
+    # 16 large-side rows per workgroup: cached loads below K = 8192,
+    # non-temporal loads with rotated K starts from K = 8192 up
+    (8, 4096, 8184),
+    (8, 4096, 8192),
+    (16, 4096, 4096),
     (16, 1000, 4104),
     (3, 17, 8),
     (15, 4097, 520),
