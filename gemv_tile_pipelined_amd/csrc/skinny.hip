@@ -326,8 +326,8 @@ hipError_t launch_gemm_skinny_splitk(int dtype, const void *A, const void *B, vo
 
 // The default launch (skinny_default_rows): 16 P rows per workgroup with 16
 // waves and a 4-stage ring while R gives every CU such a workgroup, with
-// rotated K starts and non-temporal P loads from K = kSkinnyStreamMinK up
-// and cached loads from K tile 0 below it; else 8, 4, 2 or 1 P rows,
+// non-temporal P loads from K = kSkinnyStreamMinK up (cached below), and
+// rotated K starts from K = kSkinnyRotateMinK up (K tile 0 below); else 8, 4, 2 or 1 P rows,
 // staging 8 Q rows when S <= 8 (and loading P non-temporally at 8 rows with
 // 8 Q rows; at fewer rows that measured slower).
 template <int DT>
@@ -362,6 +362,7 @@ static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, 
   switch (pr) {
     case 16:
       if (K < kSkinnyStreamMinK) return launch_lds<16, 4, 16, DT, 16>(P, Q, D, R, S, K, trans, stream);
+      if (K < kSkinnyRotateMinK) return launch_lds<16, 4, 16, DT, 16, false, true>(P, Q, D, R, S, K, trans, stream);
       return launch_lds<16, 4, 16, DT, 16, true, true>(P, Q, D, R, S, K, trans, stream);
     case 8: return q8 ? launch_lds<8, 4, 8, DT, 8, false, true>(P, Q, D, R, S, K, trans, stream)
                       : launch_lds<8, 4, 16, DT, 8>(P, Q, D, R, S, K, trans, stream);

@@ -54,9 +54,11 @@ SHAPES = [
     (2, 520, 1032),
     (8, 4096, 14336),
     # 16 large-side rows per workgroup: cached loads below K = 8192,
-    # non-temporal loads with rotated K starts from K = 8192 up
+    # non-temporal loads from there up, rotated K starts from K = 10240 up
     (8, 4096, 8184),
     (8, 4096, 8192),
+    (8, 4096, 10232),
+    (8, 4096, 10240),
     (16, 4096, 4096),
     (16, 1000, 4104),
     (3, 17, 8),
