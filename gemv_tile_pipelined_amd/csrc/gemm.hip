@@ -278,7 +278,8 @@ int64_t ring_trace(int variant, int ktu, int32_t *events, int64_t cap, int *info
     case 0:
     case 1:
     case 3:
-    case 20: return run(GemmDefault{});
+    case 20:
+    case 28: return run(GemmDefault{});
     case 10: return run(Gemm32x32{});
     case 21: return run(GemmTile256x128<kF16, 3>{});
     case 22: return run(GemmTile128x256<kF16, 3>{});

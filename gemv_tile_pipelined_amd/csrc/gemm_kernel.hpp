@@ -159,8 +159,10 @@ struct KernelRingOps {
 // real-time counter and the shader-cycle counter, with its XCC and hardware
 // ids, into 8 uint64 at ws + 16 * blockIdx.x bytes (a measurement of the
 // clock the MFMAs run at and of where the time goes; gemvtile_gemm_f16_timed).
-// Each mode ignores the arguments of the others.
-enum : int { kEpiPlain = 0, kEpiFused = 1, kEpiPartial = 2, kEpiTimed = 3 };
+// kEpiCachedStores: as kEpiPlain with ordinary (cached) stores of D instead
+// of non-temporal ones (an ablation).  Each mode ignores the arguments of the
+// others.
+enum : int { kEpiPlain = 0, kEpiFused = 1, kEpiPartial = 2, kEpiTimed = 3, kEpiCachedStores = 4 };
 
 template <class S, int EPI = kEpiPlain>
 __global__ void __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(S::kWaves / 4, S::kWaves / 4)))
@@ -526,7 +528,10 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
             // several tiles per CU, cached D lines would evict the A and B
             // panels the next tiles read (2 % faster at 8192^3, about 1.5 % at
             // 4096^3).  A kernel that reads D next finds it in memory.
-            __builtin_nontemporal_store(v, reinterpret_cast<half8_t *>(dst));
+            if constexpr (EPI == kEpiCachedStores)
+              *reinterpret_cast<half8_t *>(dst) = v;
+            else
+              __builtin_nontemporal_store(v, reinterpret_cast<half8_t *>(dst));
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)

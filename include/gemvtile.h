@@ -338,6 +338,8 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
  *      128x128 (4-stage ring) output tiles (4 waves of 128x64, 64x128,
  *      64x64): the smaller tiles of variant 0, whatever the shape
  *   24, 25, 26 as 21, 22, 23 with 2-stage rings   27 as 23 with 5 stages
+ *   28 as 20 with D written by ordinary (cached) stores instead of
+ *      non-temporal ones
  *   30 as 20 with one barrier per K tile (the ring without the early free)
  * Variants 1..30 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N

@@ -150,7 +150,7 @@ def test_trace_info_describes_the_kernels():
         _, info = gt.ring_trace(v, 4)
         assert (info["bm"], info["bn"], info["stages"], info["loads_per_tile"], info["early_free"]) == \
             (bm, bn, stages, per, ef), v
-    for v in (0, 1, 3):  # the default's ring
+    for v in (0, 1, 3, 28):  # the default's ring
         assert gt.ring_trace(v, 7)[0] == gt.ring_trace(20, 7)[0]
     with pytest.raises(gt.GemvTileError):
         gt.ring_trace(2, 4)  # the one-stage ablation has no ring
