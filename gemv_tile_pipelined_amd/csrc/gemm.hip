@@ -244,6 +244,10 @@ struct RingRecorder {
   void mfma(int buf, int idx) { push(kRingMfma, buf, idx); }
   void read(int buf, int kt, int ks, int r) { push(kRingRead, kt, ks, r, ring_stage(kt, stages)); }
   void load(int tile, int d) { push(kRingLoad, tile, d, ring_stage(tile, stages)); }
+  void mfma_load(int buf, int idx, int tile, int d) {
+    mfma(buf, idx);
+    load(tile, d);
+  }
   void wait_tile(int vmcnt) { push(kRingWaitTile, vmcnt); }
   void wait_lds() { push(kRingWaitLds); }
   void barrier() { push(kRingBarrier); }

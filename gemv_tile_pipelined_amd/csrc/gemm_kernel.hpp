@@ -123,14 +123,18 @@ __device__ inline void wait_vmcnt_n(int n) {
 
 // The kernel's side of the ring walker (ring.hpp): each event becomes the
 // instruction(s) it stands for.
-template <class S, class Mfma, class Read, class Load>
+template <class S, class Mfma, class Read, class Load, class MfmaLoad>
 struct KernelRingOps {
   Mfma mfma_fn;
   Read read_fn;
   Load load_fn;
+  MfmaLoad mfma_load_fn;
   __device__ __attribute__((always_inline)) void mfma(int buf, int idx) { mfma_fn(buf, idx); }
   __device__ __attribute__((always_inline)) void read(int buf, int kt, int ks, int r) { read_fn(buf, kt, ks, r); }
   __device__ __attribute__((always_inline)) void load(int tile, int d) { load_fn(tile, d); }
+  __device__ __attribute__((always_inline)) void mfma_load(int buf, int idx, int tile, int d) {
+    mfma_load_fn(buf, idx, tile, d);
+  }
   __device__ __attribute__((always_inline)) void wait_tile(int n) {
     if constexpr (S::EARLY_FREE) {
       constexpr int kSteady = RingEarly<S>::kSteadyVmcnt;
@@ -403,7 +407,40 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       // ring load, so they can only make the ring's vmcnt waits more
       // conservative.
       auto load_one = [&](int tile, int d) { issue_loads(tile, d, d + 1); };
-      KernelRingOps<S, decltype(mfma), decltype(read_frag), decltype(load_one)> ops{mfma, read_frag, load_one};
+      // A slot's MFMA and its refill load in one asm statement: M0 (the
+      // load's LDS address) is written before the MFMA, which then serves as
+      // the wait state an LDS DMA needs after an M0 write, instead of an
+      // s_nop of its own.  0.8-1.7 % faster at 4096^3 and 8192^3 than the
+      // load issued on its own after the MFMA, on uniform data and on zeros.
+      // As in lds_dma_b128, M0 is written and used inside the one statement
+      // (build.py rejects compiler-emitted M0 uses in such kernels).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      auto mfma_load = [&](int buf, int idx, int tile, int d) {
+        if constexpr (S::MI == 16) {
+          const int i = idx / S::kFragN;
+          const int j = idx % S::kFragN;
+          const DmaArgs g = dma_args(tile, d);
+          if constexpr (S::DTYPE == kF16)
+            asm volatile(
+                "s_mov_b32 m0, %3\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0\n\tbuffer_load_dwordx4 %4, %5, 0 offen lds"
+                : "+a"(acc[i][j])
+                : "v"(fb[buf][j]), "v"(fa[buf][i]), "s"(g.lds), "v"(g.voffset), "s"(g.rsrc)
+                : "memory", "m0");
+          else
+            asm volatile(
+                "s_mov_b32 m0, %3\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\tbuffer_load_dwordx4 %4, %5, 0 offen lds"
+                : "+a"(acc[i][j])
+                : "v"(fb[buf][j]), "v"(fa[buf][i]), "s"(g.lds), "v"(g.voffset), "s"(g.rsrc)
+                : "memory", "m0");
+        } else {
+          mfma(buf, idx);
+          load_one(tile, d);
+        }
+      };
+#pragma clang diagnostic pop
+      KernelRingOps<S, decltype(mfma), decltype(read_frag), decltype(load_one), decltype(mfma_load)> ops{
+          mfma, read_frag, load_one, mfma_load};
       if constexpr (S::EARLY_FREE)
         ring_k_loop_ef<S>(ops, KTu);
       else

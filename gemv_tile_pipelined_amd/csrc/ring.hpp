@@ -106,7 +106,9 @@ struct RingSlots {
 
 // One K tile of the loop (see the file comment).  Ops provides
 //   mfma(buf, idx), read(buf, kt, ks, r), load(tile, d), wait_tile(vmcnt),
-//   wait_lds(), barrier(), fence()
+//   wait_lds(), barrier(), fence(), and (used by the early-free loop)
+//   mfma_load(buf, idx, tile, d): mfma(buf, idx) then load(tile, d) as one
+//   instruction group
 // where fence() keeps the instruction order (a scheduling barrier).
 template <class S, bool kRest, bool kEarly, bool kNext, class Ops>
 GT_RING_INLINE void ring_ktile(Ops &ops, int kt, int ktu) {
@@ -257,7 +259,15 @@ GT_RING_INLINE void ring_ktile_ef(Ops &ops, int kt, int ktu) {
         ops.barrier();
         ops.fence();
       }
-      ops.mfma(cur, idx);
+      // A slot that carries a refill load issues it together with the
+      // slot's MFMA (mfma_load: one instruction group, the load after the
+      // MFMA).
+      const int pos = ks * S::kMfma + idx;
+      const int d = (kEarly && pos >= S::WAR_AT) ? ring_slot_load<S>(pos - S::WAR_AT) : -1;
+      if (d >= 0)
+        ops.mfma_load(cur, idx, kt + S::STAGES, d);
+      else
+        ops.mfma(cur, idx);
       ops.fence();
       if (!last) {
         if (idx % S::READ_STRIDE == 0 && idx / S::READ_STRIDE < S::kReads) {
@@ -266,12 +276,6 @@ GT_RING_INLINE void ring_ktile_ef(Ops &ops, int kt, int ktu) {
         }
       } else if (kNext && idx >= R::kBarrierAt && (idx - R::kBarrierAt) % S::READ_STRIDE == 0) {
         ops.read(cur ^ 1, kt + 1, 0, (idx - R::kBarrierAt) / S::READ_STRIDE);
-        ops.fence();
-      }
-      const int pos = ks * S::kMfma + idx;
-      if (kEarly && pos >= S::WAR_AT) {
-        const int d = ring_slot_load<S>(pos - S::WAR_AT);
-        if (d >= 0) ops.load(kt + S::STAGES, d);
         ops.fence();
       }
     }
