@@ -6,9 +6,10 @@ the slices' FP32 row sums in LDS in slice order ("Learning TileLang with
 GEMV", §5.2 block_split_k: split K when N alone gives too few blocks); for
 K >= 8192 it takes 2 rows per workgroup in 8 slices whatever N.  Each level
 is exercised at sizes around its thresholds (on a 256-CU part: N >= 4096,
-2048, 1024, 512, else 1 row; K >= 8192), with K tails that leave slices
-partly or wholly empty (K = 8 is one 16-byte chunk, so only the last slice
-has work).
+2048, 1024, 512, else 1 row; K >= 8192), on both sides of the size from
+which W is read with non-temporal loads (2^25 elements), with K tails that
+leave slices partly or wholly empty (K = 8 is one 16-byte chunk, so only the
+last slice has work).
 
 Bar as elsewhere: |d - ref| <= 1e-2 + 1e-2·|ref| for uniform inputs,
 bit-for-bit for integer inputs (exact FP32 partial sums in any order).
@@ -61,6 +62,8 @@ SHAPES = [
     (1000, 4096),  # 2 rows (8 slices)
     (4097, 8192),  # K >= 8192: 2 rows (8 slices) whatever N
     (4096, 8184),  # just below: 16 rows, no split
+    (8192, 4096),  # W of 2^25 elements: non-temporal loads
+    (8192, 4088),  # just below: cached loads
     (2048, 14336),
     (1024, 14344),
     (512, 16392),
