@@ -71,7 +71,7 @@ GEMM_SETS = 3
 GEMV_COPIES = 5
 DECODE_REPS = 20  # event pairs around 5 decode-batch launches
 BF16_REPS = 50  # event triples around one gemm_bf16 and 5 gemv_bf16
-SECTION_WARMUP = 200  # untimed repetitions before each section after the steps
+SECTION_SETTLE_S = 0.25  # seconds of untimed calls before each section after the steps
 VENDOR_REPS = 50  # interleaved pairs (ours, vendor) of timed 4096^3 GEMMs
 CONFIG_REPS = {0: 200, 2: 50, 4: 10}  # timed launches per extra workload
 # Beyond-L2 traffic per launch measured with rocprofv3 --pmc FETCH_SIZE and
@@ -555,6 +555,32 @@ def main():
     gemv_sets = [(Wt if c == 0 else Wt.clone(), torch.empty((wv.N,), dtype=torch.float16, device=dev))
                  for c in range(GEMV_COPIES)]
     M, N, K = wg.M, wg.N, wg.K
+    # The later sections' inputs too, so that no host work (uploads) idles
+    # the GPU between sections.
+    cfg_inputs = {}
+    if want("configs"):
+        for cid in (0, 2, 4):
+            w = datagen.WORKLOADS[cid]
+            Ah, Bh = datagen.gemm_inputs(w)
+            cfg_inputs[cid] = (torch.from_numpy(Ah).to(dev), torch.from_numpy(Bh).to(dev),
+                               torch.empty((w.M, w.N), dtype=torch.float16, device=dev))
+            del Ah, Bh
+    wd = datagen.DECODE_BATCH
+    if want("decode"):
+        Ad = torch.from_numpy(datagen.gemm_inputs(wd)[0]).to(dev)
+        Dd = [torch.empty((wd.M, wd.N), dtype=torch.float16, device=dev) for _ in range(GEMV_COPIES)]
+    if want("bf16"):
+        def bf16_tensor(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        Ab0, Bb0 = datagen.gemm_inputs(wg, bf16=True)
+        Ab, Bb = bf16_tensor(Ab0), bf16_tensor(Bb0)
+        Db = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        xb0, Wb0 = datagen.gemv_inputs(wv, bf16=True)
+        xb, Wb = bf16_tensor(xb0), bf16_tensor(Wb0)
+        gemv_b = [(Wb if c == 0 else Wb.clone(), torch.empty((wv.N,), dtype=torch.bfloat16, device=dev))
+                  for c in range(GEMV_COPIES)]
+        del Ab0, Bb0, xb0, Wb0
     torch.cuda.synchronize(dev)
 
     stream = torch.cuda.current_stream(dev)
@@ -671,9 +697,21 @@ def main():
         if only == "gemv":
             line["value"] = None
 
-    def timed(fn, reps, warm=SECTION_WARMUP):
-        for i in range(warm):
-            fn(i)
+    def section_settle(fn):
+        # untimed calls for SECTION_SETTLE_S seconds before a section's timed
+        # calls: a section that changes the load (its own shape, or the
+        # vendor's kernel) moves the power-managed clock, which takes a few
+        # tenths of a second to settle again
+        t_end = time.perf_counter() + SECTION_SETTLE_S
+        i = 0
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize(dev)
+
+    def timed(fn, reps):
+        section_settle(fn)
         evs = [[new_event() for _ in range(2)] for _ in range(reps)]
         torch.cuda.synchronize(dev)
         for i, e in enumerate(evs):
@@ -688,16 +726,13 @@ def main():
         cfg_out = {}
         for cid in (0, 2, 4):
             w = datagen.WORKLOADS[cid]
-            Ah, Bh = datagen.gemm_inputs(w)
-            Ac, Bc = torch.from_numpy(Ah).to(dev), torch.from_numpy(Bh).to(dev)
-            Dc = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
-            del Ah, Bh
+            Ac, Bc, Dc = cfg_inputs[cid]
 
             def one(i, Ac=Ac, Bc=Bc, Dc=Dc, w=w):
                 check(gt.gemm_f16_ptr(Ac.data_ptr(), Bc.data_ptr(), Dc.data_ptr(), w.M, w.N, w.K, sh))
 
             reps = CONFIG_REPS[cid]
-            ms = timed(one, reps, warm=max(10, reps))
+            ms = timed(one, reps)
             s = float(ms.mean()) / 1e3
             tf = metrics.gemm_flops(w.M, w.N, w.K) / s / 1e12
             bound = "latency" if cid == 0 else "mfma"
@@ -708,6 +743,7 @@ def main():
                                      regime=bound),
             }
             del Ac, Bc, Dc
+        cfg_inputs.clear()
         line["configs"] = cfg_out
 
     # ---- our GEMM and the vendor's, interleaved on the same inputs -------
@@ -723,8 +759,7 @@ def main():
             if ev:
                 ev[2].record(stream)
 
-        for i in range(SECTION_WARMUP):
-            pair(i)
+        section_settle(pair)
         vev = [[new_event() for _ in range(3)] for _ in range(VENDOR_REPS)]
         torch.cuda.synchronize(dev)
         for i, e in enumerate(vev):
@@ -744,11 +779,6 @@ def main():
 
     # ---- decode batch (8 activation rows against the GEMV's weight shape) --
     if want("decode"):
-        wd = datagen.DECODE_BATCH
-        Ad0, _ = datagen.gemm_inputs(wd)
-        Ad = torch.from_numpy(Ad0).to(dev)
-        Dd = [torch.empty((wd.M, wd.N), dtype=torch.float16, device=dev) for _ in range(GEMV_COPIES)]
-
         def decode_batch(i):
             for c, (W, _) in enumerate(gemv_sets):
                 check(gt.gemm_f16_ptr(Ad.data_ptr(), W.data_ptr(), Dd[c].data_ptr(), wd.M, wd.N, wd.K, sh))
@@ -766,17 +796,6 @@ def main():
 
     # ---- bf16: the same GEMM and GEMV shapes on bf16 inputs ---------------
     if want("bf16"):
-        def bf16_tensor(bits):
-            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-        Ab0, Bb0 = datagen.gemm_inputs(wg, bf16=True)
-        Ab, Bb = bf16_tensor(Ab0), bf16_tensor(Bb0)
-        Db = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        xb0, Wb0 = datagen.gemv_inputs(wv, bf16=True)
-        xb, Wb = bf16_tensor(xb0), bf16_tensor(Wb0)
-        gemv_b = [(Wb if c == 0 else Wb.clone(), torch.empty((wv.N,), dtype=torch.bfloat16, device=dev))
-                  for c in range(GEMV_COPIES)]
-
         def bf16_step(ev=None):
             if ev:
                 ev[0].record(stream)
@@ -788,8 +807,7 @@ def main():
             if ev:
                 ev[2].record(stream)
 
-        for _ in range(SECTION_WARMUP):
-            bf16_step()
+        section_settle(lambda i: bf16_step())
         bf_events = [[new_event() for _ in range(3)] for _ in range(BF16_REPS)]
         torch.cuda.synchronize(dev)
         for e in bf_events:
@@ -835,9 +853,7 @@ def main():
                     check(lib.gemvtile_gemm_f16_timed(A_.data_ptr(), B_.data_ptr(), D_.data_ptr(), M, N, K, sh,
                                                       stamps[i % n_keep].data_ptr(), grid * 8))
 
-                for i in range(SECTION_WARMUP):
-                    one(i)
-                torch.cuda.synchronize(dev)
+                section_settle(one)
                 sampler = None
                 try:
                     sampler = ClockSampler()
