@@ -248,6 +248,7 @@ struct RingRecorder {
     mfma(buf, idx);
     load(tile, d);
   }
+  void prep(int tile, int part) { push(kRingPrep, tile, part); }
   void wait_tile(int vmcnt) { push(kRingWaitTile, vmcnt); }
   void wait_lds() { push(kRingWaitLds); }
   void barrier() { push(kRingBarrier); }

@@ -123,18 +123,20 @@ __device__ inline void wait_vmcnt_n(int n) {
 
 // The kernel's side of the ring walker (ring.hpp): each event becomes the
 // instruction(s) it stands for.
-template <class S, class Mfma, class Read, class Load, class MfmaLoad>
+template <class S, class Mfma, class Read, class Load, class MfmaLoad, class Prep>
 struct KernelRingOps {
   Mfma mfma_fn;
   Read read_fn;
   Load load_fn;
   MfmaLoad mfma_load_fn;
+  Prep prep_fn;
   __device__ __attribute__((always_inline)) void mfma(int buf, int idx) { mfma_fn(buf, idx); }
   __device__ __attribute__((always_inline)) void read(int buf, int kt, int ks, int r) { read_fn(buf, kt, ks, r); }
   __device__ __attribute__((always_inline)) void load(int tile, int d) { load_fn(tile, d); }
   __device__ __attribute__((always_inline)) void mfma_load(int buf, int idx, int tile, int d) {
     mfma_load_fn(buf, idx, tile, d);
   }
+  __device__ __attribute__((always_inline)) void prep(int tile, int part) { prep_fn(tile, part); }
   __device__ __attribute__((always_inline)) void wait_tile(int n) {
     if constexpr (S::EARLY_FREE) {
       constexpr int kSteady = RingEarly<S>::kSteadyVmcnt;
@@ -255,8 +257,9 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
 
     // Loads [first, last) of the kDmaPerStage per-wave DMA instructions of K
     // tile kt (A tile first, then B tile).
-    // K tile kt of the loop reads K tile (kt + kofs) mod KT of the matrices;
-    // the loop runs over KTu K tiles (all KT of them, or one K slice).
+    // K tile kt of the loop reads K tile kt + kofs of the matrices; the loop
+    // runs over KTu K tiles (all KT of them, or one K slice), and kofs + KTu
+    // <= KT.
     int kofs = 0;
     int KTu = KT;
     int slice = 0;
@@ -274,9 +277,7 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       uint32_t lds;
     };
     auto dma_args = [&](int kt, int d) -> DmaArgs {
-      int ka = kt + kofs;
-      if (ka >= KT) ka -= KT;
-      const int k0 = ka * S::BK;
+      const int k0 = (kt + kofs) * S::BK;
       // K chunks at or past K read as zero (the ragged K tail).
       const uint32_t off = (k0 + tile_ld_kcol < K) ? tile_ld_off + static_cast<uint32_t>(k0) * 2u : kOobOffset;
       const uint32_t stage_lds = lds0 + static_cast<uint32_t>((kt % S::STAGES) * S::kStageBytes) +
@@ -407,6 +408,41 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       // ring load, so they can only make the ring's vmcnt waits more
       // conservative.
       auto load_one = [&](int tile, int d) { issue_loads(tile, d, d + 1); };
+      // The refill's addresses, worked out by prep() in the otherwise empty
+      // MFMA slots before the free barrier (computed all at once after the
+      // barrier, they held up the next MFMA by about 8 instruction issues):
+      // rf_off is this lane's byte offset for the refill's load 0 (each
+      // further row block adds ld_step; the A and B tiles share it), or
+      // kOobOffset past K; rf_lds is the LDS address of load 0 (this wave's
+      // rows of the stage).  The empty asm statements pin each part where
+      // the walker puts it.  A lane's chunk lies past K when
+      // rf_k0 + tile_ld_kcol >= K, i.e. when rf_lim - rf_k0 is negative; its
+      // sign bit then moves rf_off past every buffer's range (as kOobOffset
+      // does), without a compare and a select.
+      static_assert(kOobOffset == 0x80000000u, "the sign bit is the out-of-range offset");
+      const int rf_lim = K - 1 - tile_ld_kcol;
+      uint32_t rf_off = 0, rf_lds = 0, rf_past = 0;
+      int rf_k0 = 0;
+      auto prep = [&](int tile, int part) {
+        if (part == 0) {
+          rf_k0 = (tile + kofs) * S::BK;
+          asm volatile("" : "+s"(rf_k0));
+        } else if (part == 1) {
+          rf_lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+              lds0 + static_cast<uint32_t>((tile % S::STAGES) * S::kStageBytes) +
+              static_cast<uint32_t>(wave * S::kRowsPerDma * S::kRowBytes)));
+          asm volatile("" : "+s"(rf_lds));
+        } else if (part == 2) {
+          rf_off = tile_ld_off + static_cast<uint32_t>(rf_k0) * 2u;
+          asm volatile("" : "+v"(rf_off));
+        } else if (part == 3) {
+          rf_past = static_cast<uint32_t>(rf_lim - rf_k0);
+          asm volatile("" : "+v"(rf_past));
+        } else {
+          rf_off |= rf_past & kOobOffset;
+          asm volatile("" : "+v"(rf_off));
+        }
+      };
       // A slot's MFMA and its refill load in one asm statement: M0 (the
       // load's LDS address) is written before the MFMA, which then serves as
       // the wait state an LDS DMA needs after an M0 write, instead of an
@@ -420,7 +456,11 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
         if constexpr (S::MI == 16) {
           const int i = idx / S::kFragN;
           const int j = idx % S::kFragN;
-          const DmaArgs g = dma_args(tile, d);
+          (void)tile;  // prep() has worked out this refill's addresses
+          const bool is_a = d < S::kDmaA;
+          const uint32_t row_block = static_cast<uint32_t>(is_a ? d : d - S::kDmaA);
+          const DmaArgs g{is_a ? rsrc_a : rsrc_b, rf_off + row_block * ld_step,
+                          rf_lds + (is_a ? 0u : static_cast<uint32_t>(S::kStageA)) + row_block * kLdsStep};
           if constexpr (S::DTYPE == kF16)
             asm volatile(
                 "s_mov_b32 m0, %3\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0\n\tbuffer_load_dwordx4 %4, %5, 0 offen lds"
@@ -439,8 +479,8 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
         }
       };
 #pragma clang diagnostic pop
-      KernelRingOps<S, decltype(mfma), decltype(read_frag), decltype(load_one), decltype(mfma_load)> ops{
-          mfma, read_frag, load_one, mfma_load};
+      KernelRingOps<S, decltype(mfma), decltype(read_frag), decltype(load_one), decltype(mfma_load), decltype(prep)>
+          ops{mfma, read_frag, load_one, mfma_load, prep};
       if constexpr (S::EARLY_FREE)
         ring_k_loop_ef<S>(ops, KTu);
       else

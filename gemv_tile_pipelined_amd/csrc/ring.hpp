@@ -108,7 +108,9 @@ struct RingSlots {
 //   mfma(buf, idx), read(buf, kt, ks, r), load(tile, d), wait_tile(vmcnt),
 //   wait_lds(), barrier(), fence(), and (used by the early-free loop)
 //   mfma_load(buf, idx, tile, d): mfma(buf, idx) then load(tile, d) as one
-//   instruction group
+//   instruction group, and prep(tile, part): work out, in part `part` of
+//   RingEarly::kPrepParts, the addresses of the refill of K tile `tile`
+//   that the following mfma_load calls issue
 // where fence() keeps the instruction order (a scheduling barrier).
 template <class S, bool kRest, bool kEarly, bool kNext, class Ops>
 GT_RING_INLINE void ring_ktile(Ops &ops, int kt, int ktu) {
@@ -217,6 +219,16 @@ struct RingEarly {
     return n;
   }
   static constexpr int kLoadsBeforeRaw = loads_before_raw();
+  // The refill's addresses are worked out ahead of its free barrier, in
+  // kPrepParts pieces one MFMA slot apart (every other slot from kPrepAt),
+  // in the slots after K step 0's last operand read, which carry nothing
+  // else.  A wave issues one instruction every 4 cycles at most, so a slot
+  // (16 cycles of one MFMA) has room for 3 more before the next MFMA waits.
+  static constexpr int kPrepParts = 5;
+  static constexpr int kPrepAt = S::kReads * S::READ_STRIDE + 1;
+  static constexpr bool is_prep_slot(int idx) {
+    return idx >= kPrepAt && (idx - kPrepAt) % 2 == 0 && (idx - kPrepAt) / 2 < kPrepParts;
+  }
   // the vmcnt of the landed wait in the steady state: the STAGES-2 whole
   // tiles after the needed one, and the part of the newest refill issued
   static constexpr int kSteadyVmcnt = (S::STAGES - 2) * S::kDmaPerStage + kLoadsBeforeRaw;
@@ -230,6 +242,7 @@ struct RingEarly {
                 "a refill is issued in full within the K tile that starts it");
   static_assert(kLastLoad < kTileSlots + kRawPos, "a refill is issued in full before the barrier that needs it");
   static_assert(S::STAGES * S::kDmaPerStage <= 63 && kSteadyVmcnt <= 63, "vmcnt range");
+  static_assert(kPrepAt + 2 * (kPrepParts - 1) < S::WAR_AT, "the refill's addresses are ready before its free barrier");
 };
 
 // vmcnt of the landed wait in K tile kt: loads of whole tiles issued after
@@ -274,6 +287,10 @@ GT_RING_INLINE void ring_ktile_ef(Ops &ops, int kt, int ktu) {
           ops.read(cur ^ 1, kt, ks + 1, idx / S::READ_STRIDE);
           ops.fence();
         }
+        if (kEarly && R::is_prep_slot(idx)) {
+          ops.prep(kt + S::STAGES, (idx - R::kPrepAt) / 2);
+          ops.fence();
+        }
       } else if (kNext && idx >= R::kBarrierAt && (idx - R::kBarrierAt) % S::READ_STRIDE == 0) {
         ops.read(cur ^ 1, kt + 1, 0, (idx - R::kBarrierAt) / S::READ_STRIDE);
         ops.fence();
@@ -298,7 +315,14 @@ GT_RING_INLINE void ring_k_loop_ef(Ops &ops, int ktu) {
 #pragma unroll
   for (int r = 0; r < S::kReads; ++r) ops.read(0, 0, 0, r);
   int kt = 0;
-  for (; ring_early(kt, ktu, S::STAGES); ++kt) ring_ktile_ef<S, true, true>(ops, kt, ktu);  // steady state
+  // The steady state, two K tiles per iteration: the stage of each is then
+  // known when the code is generated, and the loop's own bookkeeping comes
+  // once per two K tiles.
+  for (; ring_early(kt + 1, ktu, S::STAGES); kt += 2) {
+    ring_ktile_ef<S, true, true>(ops, kt, ktu);
+    ring_ktile_ef<S, true, true>(ops, kt + 1, ktu);
+  }
+  if (ring_early(kt, ktu, S::STAGES)) ring_ktile_ef<S, true, true>(ops, kt++, ktu);
   for (; ring_next(kt, ktu); ++kt) ring_ktile_ef<S, false, true>(ops, kt, ktu);          // the ring drains
   ring_ktile_ef<S, false, false>(ops, kt, ktu);                                          // last K tile
 }
@@ -312,6 +336,7 @@ enum RingEvent : int32_t {
   kRingBarrier = 4,   // workgroup barrier
   kRingRead = 5,      // a = K tile, b = K step, c = read index r, d = stage
   kRingMfma = 6,      // a = fragment buffer, b = MFMA index within the K step
+  kRingPrep = 7,      // a = K tile whose refill addresses are prepared, b = part
 };
 
 }  // namespace gt

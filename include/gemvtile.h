@@ -436,6 +436,9 @@ int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, 
  *             4 barrier   (workgroup barrier)
  *             5 read      a = K tile, b = K step, c = read index, d = stage
  *             6 MFMA      a = fragment buffer, b = MFMA index in the K step
+ *             7 prep      a = K tile, b = part: part b of working out the
+ *                         addresses of that K tile's refill loads (the
+ *                         early-free schedule), ahead of those loads
  *           events beyond `cap` are counted but not written; may be NULL
  *           when cap == 0
  *   info    if not NULL, 8 ints: loads per wave per K tile, operand reads

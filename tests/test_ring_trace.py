@@ -57,6 +57,10 @@ class RingModel:
         self.read_log = {}  # tile -> list of (ks, r)
         self.last_read_tile = -1
         self.mfmas = 0
+        self.early_free = info["early_free"]
+        self.prepared = {}  # tile -> parts of its refill addresses worked out (early-free schedule)
+        self.prep_tile = None  # the tile whose refill addresses the kernel holds
+        self.prep_parts = None  # parts per refill (the first refill's count; every refill must match)
         self.mfma_since_load = {}  # tile -> MFMAs issued since its last load was issued
         self.overlap = {}  # tile -> MFMAs between its last load and the wait that landed it
         self.events = []
@@ -71,6 +75,14 @@ class RingModel:
         assert stage == tile % self.S, f"tile {tile} loaded into stage {stage}"
         got = self.issued.setdefault(tile, [])
         assert d == len(got), f"tile {tile}: load {d} issued after {got}"
+        if self.early_free and tile >= self.S:
+            # a refill (not the prologue): its addresses were worked out in
+            # full beforehand and are still the ones the kernel holds
+            assert self.prep_tile == tile, f"refill of tile {tile} issued with the addresses of {self.prep_tile}"
+            parts = self.prepared.get(tile, [])
+            if self.prep_parts is None:
+                self.prep_parts = len(parts)
+            assert parts and parts == list(range(self.prep_parts)), f"refill of tile {tile} issued after prep parts {parts}"
         if d == 0:
             prev = self.owner.get(stage)
             if prev is not None:
@@ -112,6 +124,24 @@ class RingModel:
         self.reads_in_flight.add(tile)
         self.read_log.setdefault(tile, []).append((ks, r))
 
+    def _prep(self, tile, part, *_):
+        assert self.early_free, "address preparation outside the early-free schedule"
+        assert self.S <= tile < self.ktu, f"prep for K tile {tile}, which no refill loads"
+        if part == 0:
+            # the kernel holds one set of refill addresses: the previous
+            # refill must have been issued in full before they are replaced
+            if self.prep_tile is not None:
+                assert len(self.issued.get(self.prep_tile, [])) == self.per, \
+                    f"addresses of tile {tile} prepared before tile {self.prep_tile}'s refill was issued"
+            assert tile not in self.prepared, f"tile {tile} prepared twice"
+            self.prep_tile = tile
+        else:
+            assert self.prep_tile == tile, f"prep part {part} of tile {tile} during tile {self.prep_tile}'s"
+        parts = self.prepared.setdefault(tile, [])
+        assert part == len(parts), f"prep part {part} of tile {tile} after {parts}"
+        assert not self.issued.get(tile), f"prep part {part} of tile {tile} after its loads began"
+        parts.append(part)
+
     def _mfma(self, *_):
         self.mfmas += 1
         for t in self.mfma_since_load:
@@ -125,6 +155,8 @@ class RingModel:
             want = [(ks, r) for ks in range(self.ksteps) for r in range(self.reads)]
             assert sorted(self.read_log.get(t, [])) == want, f"tile {t} reads"
         assert self.mfmas == self.ktu * self.ksteps * self.mfma
+        if self.early_free:
+            assert sorted(self.prepared) == list(range(self.S, self.ktu)), f"refills prepared: {sorted(self.prepared)}"
 
 
 def replay(variant, ktu):
