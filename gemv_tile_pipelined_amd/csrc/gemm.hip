@@ -225,6 +225,7 @@ hipError_t noalloc_scratch(void **ptr) {
 // The walker gemm_kernel runs (ring.hpp), run on the host with an Ops object
 // that records each event instead of issuing it.
 namespace {
+template <class S>
 struct RingRecorder {
   int stages;
   int32_t *ev;
@@ -241,7 +242,7 @@ struct RingRecorder {
     }
     ++n;
   }
-  void mfma(int buf, int idx) { push(kRingMfma, buf, idx); }
+  void mfma(int buf, int idx) { push(kRingMfma, buf, idx, S::mfma_i(idx), S::mfma_j(idx)); }
   void read(int buf, int kt, int ks, int r) { push(kRingRead, kt, ks, r, ring_stage(kt, stages)); }
   void load(int tile, int d) { push(kRingLoad, tile, d, ring_stage(tile, stages)); }
   void mfma_load(int buf, int idx, int tile, int d) {
@@ -257,7 +258,7 @@ struct RingRecorder {
 
 template <class S>
 int64_t record_ring(int ktu, int32_t *events, int64_t cap) {
-  RingRecorder rec{S::STAGES, events, cap};
+  RingRecorder<S> rec{S::STAGES, events, cap};
   if constexpr (S::EARLY_FREE)
     ring_k_loop_ef<S>(rec, ktu);
   else
@@ -294,6 +295,7 @@ int64_t ring_trace(int variant, int ktu, int32_t *events, int64_t cap, int *info
     case 26: return run(GemmTile128x128<kF16, 2>{});
     case 27: return run(GemmTile128x128<kF16, 5>{});
     case 30: return run(GemmOneBarrier{});
+    case 31: return run(GemmRowMajorMfma{});
     default: return -1;
   }
 }

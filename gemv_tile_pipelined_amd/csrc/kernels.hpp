@@ -23,8 +23,8 @@ constexpr int kGemmGroupM = 8;
 // gemvtile_gemm_f16_variant numbers of the tiled kernel: 0 (the default)
 // and the ablations of gemm.hip.  Numbers of ablations that were measured and
 // not kept stay unused.
-constexpr int kGemmVariants = 31;
-inline bool gemm_variant_exists(int v) { return (v >= 0 && v <= 3) || v == 10 || (v >= 20 && v <= 28) || v == 30; }
+constexpr int kGemmVariants = 32;
+inline bool gemm_variant_exists(int v) { return (v >= 0 && v <= 3) || v == 10 || (v >= 20 && v <= 28) || v == 30 || v == 31; }
 
 // Output tile of the tiled GEMM.  The 256x256 default needs about one tile
 // per CU to fill the chip; outputs that give fewer take smaller tiles, each

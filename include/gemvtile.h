@@ -327,7 +327,8 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
  *      2 MFMA slots, a refill load every 4 slots, swizzled LDS, persistent
  *      grouped XCD-aware schedule, and the early-free K loop (a second
  *      barrier per K tile, at MFMA slot 48 of K step 0, after which the
- *      wave's stage is refilled, half a K tile sooner than with one barrier)
+ *      wave's stage is refilled, half a K tile sooner than with one barrier);
+ *      each K step's MFMAs in serpentine order over the wave's 16x16 blocks
  *   1  as 20 without the LDS swizzle
  *   2  as 10 with single-stage LDS (load, wait, compute: no overlap)
  *   3  as 20 with one workgroup per tile (no persistent loop, no XCD remap)
@@ -341,7 +342,8 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
  *   28 as 20 with D written by ordinary (cached) stores instead of
  *      non-temporal ones
  *   30 as 20 with one barrier per K tile (the ring without the early free)
- * Variants 1..30 always run the tiled kernel, whatever the shape; variant
+ *   31 as 20 with the MFMAs of a K step in row-major order over the blocks
+ * Variants 1..31 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16, and some shapes with 17..64 rows on the smaller side: the skinny
  * kernel).  The skinny kernel (only for M <= 16 or N <= 16, else
@@ -419,7 +421,7 @@ int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, 
  * walker over K tiles that issues tile loads, operand reads, MFMAs, waits
  * and barriers; this runs the same walker on the host for the kernel of
  * tiled variant `variant` (a gemvtile_gemm_f16_variant number: 0 = 20, the
- * 256x256 default; 1 and 3 share its ring; 10, 20..27 and 30) over `ktu`
+ * 256x256 default; 1 and 3 share its ring; 10, 20..27, 30 and 31) over `ktu`
  * K tiles (of 64 elements), recording each event instead of issuing it.
  * The ring follows "使用 TMA 为 GEMM 建立 Pipeline" (TVM TIRx GEMM chapter),
  * step 5 (Pipeline 机制): K tile k in stage k % stages, refilled with tile
@@ -434,8 +436,13 @@ int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, 
  *                         stay in flight)
  *             3 LDS wait  (the wave's LDS reads are complete)
  *             4 barrier   (workgroup barrier)
- *             5 read      a = K tile, b = K step, c = read index, d = stage
- *             6 MFMA      a = fragment buffer, b = MFMA index in the K step
+ *             5 read      a = K tile, b = K step, c = read index, d = stage;
+ *                         with nA x nB MFMA blocks per wave, read index 0
+ *                         fetches A block 0, 1..nB the B blocks 0..nB-1,
+ *                         and nB+1.. the A blocks 1..nA-1
+ *             6 MFMA      a = fragment buffer, b = MFMA index in the K step,
+ *                         c = its block row (A block), d = its block
+ *                         column (B block)
  *             7 prep      a = K tile, b = part: part b of working out the
  *                         addresses of that K tile's refill loads (the
  *                         early-free schedule), ahead of those loads

@@ -278,7 +278,7 @@ def test_output_guard_band(env):
     assert np.array_equal(D.cpu().numpy(), oracle.gemm(A, B))
 
 
-TILED_VARIANTS = [1, 2, 3, 10, 20, 21, 22, 23, 24, 25, 26, 27, 28, 30]
+TILED_VARIANTS = [1, 2, 3, 10, 20, 21, 22, 23, 24, 25, 26, 27, 28, 30, 31]
 
 
 @pytest.mark.parametrize("variant", TILED_VARIANTS)

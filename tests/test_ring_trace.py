@@ -27,9 +27,10 @@ import pytest
 import gemv_tile_pipelined_amd as gt
 
 # Tiled variants with a multi-stage ring (gemvtile_gemm_f16_variant numbers):
-# 20 the 256x256 default, 10 its 32x32x16 form, 21..27 the smaller tiles with
-# 2..5 stages, 30 and 31 the early-free schedule.
-VARIANTS = [20, 10, 21, 22, 23, 24, 25, 26, 27, 30]
+# 20 the 256x256 default (early-free schedule), 10 its 32x32x16 form, 21..27
+# the smaller tiles with 2..5 stages, 30 the one-barrier ring, 31 the default
+# with row-major MFMA order.
+VARIANTS = [20, 10, 21, 22, 23, 24, 25, 26, 27, 30, 31]
 # 1..9 short loops (every prologue / last-refill / drain branch), 22 and 56
 # (split-K slice lengths: ceil(224 / 4) = 56 for K = 14336 in 4 slices), 64
 # (K = 4096), 65 (K = 4104: the ragged benchmark shape), 128 (K = 8192).
@@ -63,6 +64,14 @@ class RingModel:
         self.prep_parts = None  # parts per refill (the first refill's count; every refill must match)
         self.mfma_since_load = {}  # tile -> MFMAs issued since its last load was issued
         self.overlap = {}  # tile -> MFMAs between its last load and the wait that landed it
+        # MFMA blocks per wave: 16x16 blocks with 2 K steps per 64-wide K
+        # tile, 32x32 blocks with 4; 2x2 waves per output tile.
+        mi = 16 if self.ksteps == 2 else 32
+        self.n_a, self.n_b = info["bm"] // 2 // mi, info["bn"] // 2 // mi
+        assert self.n_a + self.n_b == self.reads and self.n_a * self.n_b == self.mfma
+        self.frag = ({}, {})  # fragment buffer -> {("A" | "B", block): (K tile, K step) it holds}
+        self.blocks = set()  # (A block, B block) pairs of the current K step's MFMAs
+        self.order = []  # (A block, B block) of the MFMAs of K step 0 of K tile 0
         self.events = []
 
     def step(self, ev):
@@ -123,6 +132,10 @@ class RingModel:
         self.last_read_tile = tile
         self.reads_in_flight.add(tile)
         self.read_log.setdefault(tile, []).append((ks, r))
+        # read index -> fragment: A block 0, the B blocks, the other A blocks;
+        # a K step's operands go to fragment buffer (K step parity)
+        frag = ("A", 0) if r == 0 else ("B", r - 1) if r <= self.n_b else ("A", r - self.n_b)
+        self.frag[ks & 1][frag] = (tile, ks)
 
     def _prep(self, tile, part, *_):
         assert self.early_free, "address preparation outside the early-free schedule"
@@ -142,7 +155,22 @@ class RingModel:
         assert not self.issued.get(tile), f"prep part {part} of tile {tile} after its loads began"
         parts.append(part)
 
-    def _mfma(self, *_):
+    def _mfma(self, buf, idx, i, j):
+        step = self.mfmas // self.mfma
+        tile, ks = divmod(step, self.ksteps)
+        assert idx == self.mfmas % self.mfma, f"MFMA index {idx} out of order"
+        assert buf == ks & 1, f"K step {ks} computes from fragment buffer {buf}"
+        assert 0 <= i < self.n_a and 0 <= j < self.n_b, f"MFMA block ({i}, {j})"
+        assert self.frag[buf].get(("A", i)) == (tile, ks), \
+            f"MFMA ({i}, {j}) of K tile {tile} step {ks}: A fragment holds {self.frag[buf].get(('A', i))}"
+        assert self.frag[buf].get(("B", j)) == (tile, ks), \
+            f"MFMA ({i}, {j}) of K tile {tile} step {ks}: B fragment holds {self.frag[buf].get(('B', j))}"
+        assert (i, j) not in self.blocks, f"block ({i}, {j}) computed twice in K tile {tile} step {ks}"
+        self.blocks.add((i, j))
+        if step == 0:
+            self.order.append((i, j))
+        if len(self.blocks) == self.mfma:
+            self.blocks = set()
         self.mfmas += 1
         for t in self.mfma_since_load:
             self.mfma_since_load[t] += 1
@@ -155,6 +183,7 @@ class RingModel:
             want = [(ks, r) for ks in range(self.ksteps) for r in range(self.reads)]
             assert sorted(self.read_log.get(t, [])) == want, f"tile {t} reads"
         assert self.mfmas == self.ktu * self.ksteps * self.mfma
+        assert self.blocks == set(), "a K step ended without all its blocks"
         if self.early_free:
             assert sorted(self.prepared) == list(range(self.S, self.ktu)), f"refills prepared: {sorted(self.prepared)}"
 
@@ -174,10 +203,60 @@ def test_ring_schedule_is_correct(variant, ktu):
     replay(variant, ktu)
 
 
+# Variants whose MFMAs go in serpentine order over the wave's blocks (each
+# shares an operand with the one before it), and those in row-major order.
+SERPENTINE = [20, 21, 22, 23, 24, 25, 26, 27, 30]
+ROW_MAJOR = [10, 31]
+
+
+@pytest.mark.parametrize("variant", SERPENTINE + ROW_MAJOR)
+def test_mfma_order(variant):
+    model, _ = replay(variant, 3)
+    n_b = model.n_b
+    if variant in ROW_MAJOR:
+        assert model.order == [(k // n_b, k % n_b) for k in range(model.mfma)]
+    else:
+        want = [(k // n_b, k % n_b if (k // n_b) % 2 == 0 else n_b - 1 - k % n_b) for k in range(model.mfma)]
+        assert model.order == want
+        for (i0, j0), (i1, j1) in zip(model.order, model.order[1:]):
+            assert i0 == i1 or j0 == j1, "consecutive MFMAs share an operand"
+
+
+def _rejects(events, info, ktu):
+    model = RingModel(ktu, info)
+    try:
+        for ev in events:
+            model.step(ev)
+        model.finish()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_model_rejects_wrong_mfma_operands():
+    """Traces with an MFMA on a transposed block (i, j) -> (j, i), on the
+    other fragment buffer, or before its operand was read for its K step
+    fail the model."""
+    events, info = gt.ring_trace(20, 3)
+    assert not _rejects(events, info, 3)
+    mfmas = [n for n, e in enumerate(events) if e[0] == "mfma"]
+    k = next(n for n in mfmas if events[n][3] != events[n][4])
+    name, a, b, c, d = events[k]
+    assert _rejects(events[:k] + [(name, a, b, d, c)] + events[k + 1:], info, 3)
+    assert _rejects(events[:k] + [(name, a ^ 1, b, c, d)] + events[k + 1:], info, 3)
+    # the read of A block 1 for K step 1 of K tile 1, moved after the first
+    # MFMA of that step that uses it
+    r = next(n for n, e in enumerate(events) if e == ("read", 1, 1, info["bn"] // 32 + 1, 1))
+    per_step = info["mfma_per_step"]
+    first = next(n for n in mfmas[3 * per_step:4 * per_step] if events[n][3] == 1)
+    moved = events[:r] + events[r + 1:first] + [events[first], events[r]] + events[first + 1:]
+    assert _rejects(moved, info, 3)
+
+
 def test_trace_info_describes_the_kernels():
     want = {20: (256, 256, 2, 16, 1), 10: (256, 256, 2, 16, 0), 21: (256, 128, 3, 12, 0), 22: (128, 256, 3, 12, 0),
             23: (128, 128, 4, 8, 0), 24: (256, 128, 2, 12, 0), 25: (128, 256, 2, 12, 0), 26: (128, 128, 2, 8, 0),
-            27: (128, 128, 5, 8, 0), 30: (256, 256, 2, 16, 0)}
+            27: (128, 128, 5, 8, 0), 30: (256, 256, 2, 16, 0), 31: (256, 256, 2, 16, 1)}
     for v, (bm, bn, stages, per, ef) in want.items():
         _, info = gt.ring_trace(v, 4)
         assert (info["bm"], info["bn"], info["stages"], info["loads_per_tile"], info["early_free"]) == \
