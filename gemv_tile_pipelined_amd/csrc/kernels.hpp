@@ -171,15 +171,14 @@ inline int64_t gemv_default_grid(int64_t N, int64_t K, int num_cus) {
 }
 
 // At 16 P rows per workgroup the default skinny launch streams P with
-// non-temporal loads only for K of at least kSkinnyStreamMinK elements, and
-// rotates the workgroups' K starts only from kSkinnyRotateMinK: below 8192
-// cached loads from K tile 0 measured faster (8x4096x4096: 8.8 -> 7.4 us;
-// 8x4096x6144: 10.5 -> 9.4 us); at 8192 the rotated starts cost a third
-// (22.7 against 16.9 us unrotated, non-temporal); from 10240 up the rotated
-// non-temporal form is the fastest (8x4096x14336: 20.0 us against 23.2 us
-// cached and unrotated; 8x4096x28672: 36.5 against 42.0 us).
+// non-temporal loads only for K of at least kSkinnyStreamMinK elements:
+// below 8192 cached loads measured faster (8x4096x4096: 8.8 -> 7.4 us;
+// 8x4096x6144: 10.5 -> 9.4 us); from 8192 up the non-temporal form is the
+// faster (8x4096x14336: 20.0 us against 23.2 us cached; 8x4096x28672: 36.5
+// against 42.0 us).  Launches of 16 or 8 P rows per workgroup start each
+// workgroup's K walk at kSkinnyRotateXcd's K tile (skinny.hip).
 constexpr int kSkinnyStreamMinK = 8192;
-constexpr int kSkinnyRotateMinK = 10240;
+constexpr int kSkinnyRotateXcd = 2;
 
 // P rows per workgroup of the default skinny launch for R rows of the large
 // operand: the largest of 16, 8, 4, 2 with R >= rows * num_cus, else 1.

@@ -127,7 +127,7 @@ gemm_skinny_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ 
 // ws[j][output index] for the ordered reduction kernel.  More workgroups of
 // 16 P rows, instead of fewer P rows per workgroup, keep the number of times
 // Q is read from the caches at ceil(R / 16).
-template <int WAVES, int STAGES, int QROWS, bool TRANS, int DT = kF16, int PR = 16, bool KROT = false, bool NTP = false,
+template <int WAVES, int STAGES, int QROWS, bool TRANS, int DT = kF16, int PR = 16, int KROT = 0, bool NTP = false,
           bool SPLIT = false>
 __global__ void __launch_bounds__(WAVES * 64)
 gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ Q, _Float16 *__restrict__ D,
@@ -173,10 +173,16 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   const int4_t rsrc_p = make_buffer_rsrc(P + static_cast<int64_t>(r0) * K, static_cast<uint32_t>(prows) * K * 2u);
   const int4_t rsrc_q = make_buffer_rsrc(Q, static_cast<uint32_t>(S) * K * 2u);
   const uint32_t ring0 = lds_addr(ring);
-  // With KROT, workgroup b walks its K tiles from tile b % nkt and wraps, so
-  // the workgroups running at one moment read different parts of Q (which
-  // they all share) instead of the same lines at once.
-  const int kt0 = KROT ? static_cast<int>(blockIdx.x % static_cast<unsigned>(nkt)) : 0;
+  // With KROT, workgroup b walks its K tiles from tile j % nkt and wraps, so
+  // the workgroups running at one moment read different K ranges: j = b
+  // (KROT 1), or j = b / 8, its index within its XCD (KROT 2; workgroups are
+  // dispatched to the 8 XCDs in turn), so the workgroups sharing one L2 all
+  // start at different K tiles (with j = b they take only two starts per XCD
+  // when there are 16 K tiles).
+  const int kt0 = KROT == 1   ? static_cast<int>(blockIdx.x % static_cast<unsigned>(nkt))
+                  : KROT == 2 ? static_cast<int>((blockIdx.x >> 3) % static_cast<unsigned>(nkt))
+                              : 0;
+  static_assert(KROT >= 0 && KROT <= 2, "K start rotation mode");
   auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
 
   // Row loads of K tile kt: load d of this wave moves stage row
@@ -271,7 +277,7 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   }
 }
 
-template <int WAVES, int STAGES, int QROWS, int DT = kF16, int PR = 16, bool KROT = false, bool NTP = false>
+template <int WAVES, int STAGES, int QROWS, int DT = kF16, int PR = 16, int KROT = 0, bool NTP = false>
 static hipError_t launch_lds(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                              hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((R + PR - 1) / PR));
@@ -326,10 +332,16 @@ hipError_t launch_gemm_skinny_splitk(int dtype, const void *A, const void *B, vo
 
 // The default launch (skinny_default_rows): 16 P rows per workgroup with 16
 // waves and a 4-stage ring while R gives every CU such a workgroup, with
-// non-temporal P loads from K = kSkinnyStreamMinK up (cached below), and
-// rotated K starts from K = kSkinnyRotateMinK up (K tile 0 below); else 8, 4, 2 or 1 P rows,
-// staging 8 Q rows when S <= 8 (and loading P non-temporally at 8 rows with
-// 8 Q rows; at fewer rows that measured slower).
+// non-temporal P loads from K = kSkinnyStreamMinK up (cached below); else 8,
+// 4, 2 or 1 P rows, staging 8 Q rows when S <= 8 (and loading P
+// non-temporally at 8 rows with 8 Q rows; at fewer rows that measured
+// slower).  Launches of 16 or 8 P rows start each workgroup's K walk at its
+// index within its XCD (KROT 2, kSkinnyRotateXcd): without it, rows whose
+// length is a multiple of 8 KiB (K % 4096 == 0) read 17-22 % slower, as
+// every workgroup sharing an L2 then reads the same offset of its rows at
+// once.  With 17..32 staged Q rows the rotation is taken only for such rows
+// (elsewhere it measured 5 % slower); with 4 or fewer P rows never (4-10 %
+// slower: every workgroup re-reads the same Q lines, best all at once).
 template <int DT>
 static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                                   int num_cus, hipStream_t stream) {
@@ -339,8 +351,8 @@ static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, 
     // 16 waves 5-17 % behind), a 2-stage ring of (PR + 64) KiB stages, the
     // partial sums reusing the ring.
     switch (pr) {
-      case 16: return launch_lds<8, 2, 64, DT, 16, false, true>(P, Q, D, R, S, K, trans, stream);
-      case 8: return launch_lds<8, 2, 64, DT, 8, false, true>(P, Q, D, R, S, K, trans, stream);
+      case 16: return launch_lds<8, 2, 64, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream);
+      case 8: return launch_lds<8, 2, 64, DT, 8, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream);
       case 4: return launch_lds<8, 2, 64, DT, 4>(P, Q, D, R, S, K, trans, stream);
       case 2: return launch_lds<8, 2, 64, DT, 2>(P, Q, D, R, S, K, trans, stream);
       default: return launch_lds<8, 2, 64, DT, 1>(P, Q, D, R, S, K, trans, stream);
@@ -348,11 +360,13 @@ static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, 
   }
   if (S > kSkinnyMaxRows) {
     // 17..32 small-side rows: 32 staged Q rows, 4 waves, a 3-stage ring of
-    // (PR + 32) KiB stages (rotated K starts measured no better here: equal
-    // or up to 4 % slower).
+    // (PR + 32) KiB stages.
+    const bool rot = K % 4096 == 0;
     switch (pr) {
-      case 16: return launch_lds<4, 3, 32, DT, 16, false, true>(P, Q, D, R, S, K, trans, stream);
-      case 8: return launch_lds<4, 3, 32, DT, 8, false, true>(P, Q, D, R, S, K, trans, stream);
+      case 16: return rot ? launch_lds<4, 3, 32, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
+                          : launch_lds<4, 3, 32, DT, 16, 0, true>(P, Q, D, R, S, K, trans, stream);
+      case 8: return rot ? launch_lds<4, 3, 32, DT, 8, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
+                         : launch_lds<4, 3, 32, DT, 8, 0, true>(P, Q, D, R, S, K, trans, stream);
       case 4: return launch_lds<4, 3, 32, DT, 4>(P, Q, D, R, S, K, trans, stream);
       case 2: return launch_lds<4, 3, 32, DT, 2>(P, Q, D, R, S, K, trans, stream);
       default: return launch_lds<4, 3, 32, DT, 1>(P, Q, D, R, S, K, trans, stream);
@@ -361,11 +375,10 @@ static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, 
   const bool q8 = S <= 8;
   switch (pr) {
     case 16:
-      if (K < kSkinnyStreamMinK) return launch_lds<16, 4, 16, DT, 16>(P, Q, D, R, S, K, trans, stream);
-      if (K < kSkinnyRotateMinK) return launch_lds<16, 4, 16, DT, 16, false, true>(P, Q, D, R, S, K, trans, stream);
-      return launch_lds<16, 4, 16, DT, 16, true, true>(P, Q, D, R, S, K, trans, stream);
-    case 8: return q8 ? launch_lds<8, 4, 8, DT, 8, false, true>(P, Q, D, R, S, K, trans, stream)
-                      : launch_lds<8, 4, 16, DT, 8>(P, Q, D, R, S, K, trans, stream);
+      if (K < kSkinnyStreamMinK) return launch_lds<16, 4, 16, DT, 16, kSkinnyRotateXcd>(P, Q, D, R, S, K, trans, stream);
+      return launch_lds<16, 4, 16, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream);
+    case 8: return q8 ? launch_lds<8, 4, 8, DT, 8, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
+                      : launch_lds<8, 4, 16, DT, 8, kSkinnyRotateXcd>(P, Q, D, R, S, K, trans, stream);
     case 4: return q8 ? launch_lds<4, 4, 8, DT, 4>(P, Q, D, R, S, K, trans, stream)
                       : launch_lds<4, 4, 16, DT, 4>(P, Q, D, R, S, K, trans, stream);
     case 2: return q8 ? launch_lds<4, 4, 8, DT, 2>(P, Q, D, R, S, K, trans, stream)
@@ -422,7 +435,8 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
     case 0: return launch_lds_auto<kF16>(P, Q, D, R, S, K, !small_m, num_cus, stream);
     // operands loaded into registers: <waves per workgroup, K steps in flight per wave>
     case 4: return launch<8, 4>(P, Q, D, R, S, K, !small_m, stream);
-    // LDS ring, 16 P rows per workgroup: <waves, stages, Q rows, type, P rows, rotated K start>
+    // LDS ring, 16 P rows per workgroup: <waves, stages, Q rows, type, P rows, K start rotation (1: by
+    // workgroup index)>
     case 12: return launch_lds<16, 4, 16, kF16, 16>(P, Q, D, R, S, K, !small_m, stream);
     case 30: return launch_lds<16, 4, 16, kF16, 16, true>(P, Q, D, R, S, K, !small_m, stream);
     // as 30 with non-temporal loads of P (the default at 16 P rows)

@@ -354,10 +354,13 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
  *       in flight per wave), 16 large-side rows per workgroup
  *   112 operands staged through a 4-stage LDS ring of 1 KiB row segments,
  *       16 waves, 16 large-side rows per workgroup
- *   130 as 112 with each workgroup starting its K walk at a different K tile
- *   147 as 130 with the large side loaded non-temporally (the gemm_f16
- *       choice at 16 rows per workgroup)
+ *   130 as 112 with workgroup b starting its K walk at K tile b (mod the
+ *       number of K tiles)
+ *   147 as 130 with the large side loaded non-temporally
  *   152 as 147 with every workgroup starting its K walk at K tile 0
+ * (gemm_f16's choice at 16 rows per workgroup starts workgroup b at K tile
+ * b / 8, its index within its XCD, and loads the large side non-temporally
+ * from K = 8192 up.)
  * The wave-specialised kernel, whatever the shape:
  *   200, 201 256x128 output tiles, 4 consumer waves (MFMA only, 128x64
  *       each) and 4 loader waves (tile loads only) handing K tiles over at

@@ -54,11 +54,17 @@ SHAPES = [
     (2, 520, 1032),
     (8, 4096, 14336),
     # 16 large-side rows per workgroup: cached loads below K = 8192,
-    # non-temporal loads from there up, rotated K starts from K = 10240 up
+    # non-temporal loads from there up; K starts rotated by the workgroup's
+    # index within its XCD (8 K tiles at 4096, 16 at 8192, 32 at 16384)
     (8, 4096, 8184),
     (8, 4096, 8192),
     (8, 4096, 10232),
     (8, 4096, 10240),
+    (8, 4096, 16384),
+    (12, 4096, 4096),
+    # 8 large-side rows per workgroup, rotated K starts
+    (8, 2048, 8192),
+    (13, 3000, 4104),
     (16, 4096, 4096),
     (16, 1000, 4104),
     (3, 17, 8),
@@ -104,6 +110,11 @@ SHAPES = [
     (24, 1500, 4104),
     (1500, 48, 1032),
     (40, 1100, 8200),
+    # 17..32 staged rows with rotated K starts (K % 4096 == 0), at 16 and 8
+    # large-side rows per workgroup; 33..64 at 8 rows per workgroup
+    (24, 4096, 8192),
+    (2500, 20, 4096),
+    (48, 2600, 4104),
 ]
 
 
