@@ -455,7 +455,7 @@ def gemv_grid(N: int, K: int, num_cus: int) -> int:
     return int(load_library().gemvtile_gemv_grid(N, K, num_cus))
 
 
-RING_EVENTS = {1: "load", 2: "wait", 3: "lds_wait", 4: "barrier", 5: "read", 6: "mfma", 7: "prep"}
+RING_EVENTS = {1: "load", 2: "wait", 3: "lds_wait", 4: "barrier", 5: "read", 6: "mfma", 7: "prep", 8: "init"}
 
 
 def ring_trace(variant: int, ktu: int):

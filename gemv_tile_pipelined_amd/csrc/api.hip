@@ -323,7 +323,7 @@ const char *gemvtile_status_string(int status) {
 int gemvtile_tile_coord(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t group_m, int64_t *tm, int64_t *tn) {
   if (tm == nullptr || tn == nullptr || tiles_m <= 0 || tiles_n <= 0 || group_m <= 0) return GEMVTILE_ERR_INVALID_ARG;
   if (t < 0 || t >= tiles_m * tiles_n) return GEMVTILE_ERR_INVALID_ARG;
-  const gt::TileCoord c = gt::grouped_tile(t, tiles_m, tiles_n, group_m);
+  const gt::TileCoord c = gt::tile_of(t, tiles_m, tiles_n, group_m);
   *tm = c.tm;
   *tn = c.tn;
   return GEMVTILE_OK;

@@ -250,6 +250,7 @@ struct RingRecorder {
     load(tile, d);
   }
   void prep(int tile, int part) { push(kRingPrep, tile, part); }
+  void init_acc() { push(kRingInit); }
   void wait_tile(int vmcnt) { push(kRingWaitTile, vmcnt); }
   void wait_lds() { push(kRingWaitLds); }
   void barrier() { push(kRingBarrier); }

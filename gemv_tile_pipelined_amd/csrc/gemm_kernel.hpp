@@ -132,13 +132,14 @@ __device__ inline void wait_vmcnt_n(int n) {
 
 // The kernel's side of the ring walker (ring.hpp): each event becomes the
 // instruction(s) it stands for.
-template <class S, class Mfma, class Read, class Load, class MfmaLoad, class Prep>
+template <class S, class Mfma, class Read, class Load, class MfmaLoad, class Prep, class InitAcc>
 struct KernelRingOps {
   Mfma mfma_fn;
   Read read_fn;
   Load load_fn;
   MfmaLoad mfma_load_fn;
   Prep prep_fn;
+  InitAcc init_acc_fn;
   __device__ __attribute__((always_inline)) void mfma(int buf, int idx) { mfma_fn(buf, idx); }
   __device__ __attribute__((always_inline)) void read(int buf, int kt, int ks, int r) { read_fn(buf, kt, ks, r); }
   __device__ __attribute__((always_inline)) void load(int tile, int d) { load_fn(tile, d); }
@@ -146,6 +147,7 @@ struct KernelRingOps {
     mfma_load_fn(buf, idx, tile, d);
   }
   __device__ __attribute__((always_inline)) void prep(int tile, int part) { prep_fn(tile, part); }
+  __device__ __attribute__((always_inline)) void init_acc() { init_acc_fn(); }
   __device__ __attribute__((always_inline)) void wait_tile(int n) {
     if constexpr (S::EARLY_FREE) {
       constexpr int kSteady = RingEarly<S>::kSteadyVmcnt;
@@ -255,7 +257,7 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
   int64_t u = S::PERSISTENT ? xcd_logical_id(blockIdx.x, grid) : static_cast<int64_t>(blockIdx.x);
   for (; u < num_units; u += grid) {
     const int64_t t = EPI == kEpiPartial ? u % num_tiles : u;
-    const TileCoord tc = grouped_tile(t, tiles_m, tiles_n, kGemmGroupM);
+    const TileCoord tc = tile_of(t, tiles_m, tiles_n, kGemmGroupM);
     const int m0 = static_cast<int>(tc.tm) * S::BM;
     const int n0 = static_cast<int>(tc.tn) * S::BN;
     const int rows_a = min(S::BM, M - m0);
@@ -341,26 +343,31 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
 
     using AccT = std::conditional_t<S::MI == 32, float16_t, float4_t>;
     AccT acc[S::kFragM][S::kFragN];
-#pragma unroll
-    for (int i = 0; i < S::kFragM; ++i)
-#pragma unroll
-      for (int j = 0; j < S::kFragN; ++j)
-#pragma unroll
-        for (int e = 0; e < S::kAccRegs; ++e) acc[i][j][e] = 0.0f;
-    if constexpr (S::MI == 16) {
-      // The zeros above are written by VALU instructions and first read by a
-      // hand-written MFMA, which the compiler's hazard padding does not know
-      // about.  These statements take every accumulator as input and output
-      // and carry wait states: the zeros are materialised before them (and
-      // cannot be re-created after them), so they precede every MFMA by at
-      // least 16 wait states.
-      static_assert(S::kFragN % 4 == 0, "accumulator fence covers 4 blocks per statement");
+    // Zero the accumulators.  The pipelined loop does this after issuing its
+    // first tile loads (ring.hpp calls init_acc), so the 256 register writes
+    // overlap the loads' latency instead of delaying their issue.
+    auto init_acc = [&]() {
 #pragma unroll
       for (int i = 0; i < S::kFragM; ++i)
 #pragma unroll
-        for (int j = 0; j < S::kFragN; j += 4)
-          asm volatile("s_nop 1" : "+a"(acc[i][j]), "+a"(acc[i][j + 1]), "+a"(acc[i][j + 2]), "+a"(acc[i][j + 3]));
-    }
+        for (int j = 0; j < S::kFragN; ++j)
+#pragma unroll
+          for (int e = 0; e < S::kAccRegs; ++e) acc[i][j][e] = 0.0f;
+      if constexpr (S::MI == 16) {
+        // The zeros above are written by VALU instructions and first read by
+        // a hand-written MFMA, which the compiler's hazard padding does not
+        // know about.  These statements take every accumulator as input and
+        // output and carry wait states: the zeros are materialised before
+        // them (and cannot be re-created after them), so they precede every
+        // MFMA by at least 16 wait states.
+        static_assert(S::kFragN % 4 == 0, "accumulator fence covers 4 blocks per statement");
+#pragma unroll
+        for (int i = 0; i < S::kFragM; ++i)
+#pragma unroll
+          for (int j = 0; j < S::kFragN; j += 4)
+            asm volatile("s_nop 1" : "+a"(acc[i][j]), "+a"(acc[i][j + 1]), "+a"(acc[i][j + 2]), "+a"(acc[i][j + 3]));
+      }
+    };
 
     auto mfma = [&](int buf, int idx) {
       const int i = S::mfma_i(idx);
@@ -397,6 +404,7 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
       // No overlap: load, wait, compute -- the serial order the TVM chapter
       // starts from before its step 5 adds a second stage.  Every wave must
       // first be done with the previous output tile's LDS.
+      init_acc();
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       workgroup_barrier();
       for (int kt = 0; kt < KTu; ++kt) {
@@ -496,8 +504,9 @@ gemm_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, _Flo
         }
       };
 #pragma clang diagnostic pop
-      KernelRingOps<S, decltype(mfma), decltype(read_frag), decltype(load_one), decltype(mfma_load), decltype(prep)>
-          ops{mfma, read_frag, load_one, mfma_load, prep};
+      KernelRingOps<S, decltype(mfma), decltype(read_frag), decltype(load_one), decltype(mfma_load), decltype(prep),
+                    decltype(init_acc)>
+          ops{mfma, read_frag, load_one, mfma_load, prep, init_acc};
       if constexpr (S::EARLY_FREE)
         ring_k_loop_ef<S>(ops, KTu);
       else

@@ -106,7 +106,9 @@ struct RingSlots {
 
 // One K tile of the loop (see the file comment).  Ops provides
 //   mfma(buf, idx), read(buf, kt, ks, r), load(tile, d), wait_tile(vmcnt),
-//   wait_lds(), barrier(), fence(), and (used by the early-free loop)
+//   wait_lds(), barrier(), fence(), init_acc() (zero the accumulators: the
+//   walker calls it once, between the prologue's loads and its first wait),
+//   and (used by the early-free loop)
 //   mfma_load(buf, idx, tile, d): mfma(buf, idx) then load(tile, d) as one
 //   instruction group, and prep(tile, part): work out, in part `part` of
 //   RingEarly::kPrepParts, the addresses of the refill of K tile `tile`
@@ -170,6 +172,10 @@ GT_RING_INLINE void ring_k_loop(Ops &ops, int ktu) {
     if (s < ktu)
 #pragma unroll
       for (int d = 0; d < S::kDmaPerStage; ++d) ops.load(s, d);
+  // The accumulators are zeroed while the first tiles are in flight.
+  ops.fence();
+  ops.init_acc();
+  ops.fence();
   ops.wait_tile(ring_vmcnt(ring_younger_at_prologue(ktu, S::STAGES), S::STAGES, S::kDmaPerStage));
   ops.barrier();
 #pragma unroll
@@ -310,6 +316,10 @@ GT_RING_INLINE void ring_k_loop_ef(Ops &ops, int ktu) {
     if (s < ktu)
 #pragma unroll
       for (int d = 0; d < S::kDmaPerStage; ++d) ops.load(s, d);
+  // The accumulators are zeroed while the first tiles are in flight.
+  ops.fence();
+  ops.init_acc();
+  ops.fence();
   ops.wait_tile(ring_min(ktu, S::STAGES) * S::kDmaPerStage - S::kDmaPerStage);
   ops.barrier();
 #pragma unroll
@@ -337,6 +347,7 @@ enum RingEvent : int32_t {
   kRingRead = 5,      // a = K tile, b = K step, c = read index r, d = stage
   kRingMfma = 6,      // a = fragment buffer, b = MFMA index within the K step
   kRingPrep = 7,      // a = K tile whose refill addresses are prepared, b = part
+  kRingInit = 8,      // the accumulators are zeroed
 };
 
 }  // namespace gt

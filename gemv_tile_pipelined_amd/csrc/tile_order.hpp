@@ -47,6 +47,31 @@ GT_HD inline TileCoord grouped_tile(int64_t t, int64_t tiles_m, int64_t tiles_n,
   return c;
 }
 
+// The same mapping in 32-bit arithmetic, for grids of fewer than 2^31 tiles
+// (a 64-bit division is a long instruction sequence on the GPU).
+GT_HD inline TileCoord grouped_tile32(uint32_t t, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m) {
+  const uint32_t per_group = group_m * tiles_n;
+  const uint32_t group = t / per_group;
+  const uint32_t first_m = group * group_m;
+  const uint32_t rows_here = (tiles_m - first_m < group_m) ? (tiles_m - first_m) : group_m;
+  const uint32_t within = t - group * per_group;
+  const uint32_t tn = within / rows_here;
+  TileCoord c;
+  c.tm = first_m + (within - tn * rows_here);
+  c.tn = tn;
+  return c;
+}
+
+// The grouped mapping as the kernel computes it: in 32-bit arithmetic when
+// every intermediate fits (fewer than 2^30 tiles and group_m * tiles_n below
+// 2^31), else in 64-bit.
+GT_HD inline TileCoord tile_of(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t group_m) {
+  if (tiles_m * tiles_n < (int64_t{1} << 30) && group_m * tiles_n < (int64_t{1} << 31))
+    return grouped_tile32(static_cast<uint32_t>(t), static_cast<uint32_t>(tiles_m), static_cast<uint32_t>(tiles_n),
+                          static_cast<uint32_t>(group_m));
+  return grouped_tile(t, tiles_m, tiles_n, group_m);
+}
+
 // Logical id of hardware workgroup `w` in a grid of `grid` workgroups.  The
 // renumbering is a bijection on [0, grid) when grid % kNumXcd == 0, and the
 // identity otherwise.

@@ -449,6 +449,8 @@ int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, 
  *             7 prep      a = K tile, b = part: part b of working out the
  *                         addresses of that K tile's refill loads (the
  *                         early-free schedule), ahead of those loads
+ *             8 init      the accumulators are zeroed (once, after the
+ *                         prologue's loads are issued)
  *           events beyond `cap` are counted but not written; may be NULL
  *           when cap == 0
  *   info    if not NULL, 8 ints: loads per wave per K tile, operand reads

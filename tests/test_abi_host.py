@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import gemv_tile_pipelined_amd as gt
@@ -165,6 +166,22 @@ def test_grouped_order_shape(lib):
     assert [gt.tile_coord(t, 16, 16, 8) for t in range(10)] == [(r, 0) for r in range(8)] + [(0, 1), (1, 1)]
     # tiles_m = 10 with group_m = 8: the second group is 2 rows high
     assert [gt.tile_coord(t, 10, 3, 8) for t in range(24, 30)] == [(8, 0), (9, 0), (8, 1), (9, 1), (8, 2), (9, 2)]
+
+
+def test_tile_coord_large_grids():
+    """Grids of 2^30 tiles or more take the 64-bit form of the mapping; near
+    that size both forms must stay in range and one-to-one (sampled), and
+    the first group runs down its 8 tile rows."""
+    rng = np.random.default_rng(7)
+    for tiles_m, tiles_n in ((1 << 15, (1 << 15) - 1), (1 << 15, (1 << 15) + 3), (8, 1 << 27), (3, 1 << 23)):
+        total = tiles_m * tiles_n
+        ts = np.unique(np.concatenate([rng.integers(0, total, 2000), [0, 1, total - 2, total - 1]]))
+        coords = [gt.tile_coord(int(t), tiles_m, tiles_n, 8) for t in ts]
+        assert all(0 <= tm < tiles_m and 0 <= tn < tiles_n for tm, tn in coords)
+        assert len(set(coords)) == len(coords)
+        rows = min(8, tiles_m)
+        assert [gt.tile_coord(t, tiles_m, tiles_n, 8) for t in range(rows + 1)] == \
+            [(r, 0) for r in range(rows)] + [(0, 1)]
 
 
 def test_tile_coord_rejects_bad_input(lib):

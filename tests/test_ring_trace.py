@@ -72,6 +72,7 @@ class RingModel:
         self.frag = ({}, {})  # fragment buffer -> {("A" | "B", block): (K tile, K step) it holds}
         self.blocks = set()  # (A block, B block) pairs of the current K step's MFMAs
         self.order = []  # (A block, B block) of the MFMAs of K step 0 of K tile 0
+        self.inits = 0  # accumulator zeroings
         self.events = []
 
     def step(self, ev):
@@ -155,7 +156,18 @@ class RingModel:
         assert not self.issued.get(tile), f"prep part {part} of tile {tile} after its loads began"
         parts.append(part)
 
+    def _init(self, *_):
+        # once, after the prologue has issued every load it issues (those of
+        # the first min(ktu, S) tiles, or S-1 for the one-barrier ring) and
+        # before any wait or MFMA
+        assert self.inits == 0 and self.mfmas == 0, "accumulators zeroed twice or after an MFMA"
+        before = [e[0] for e in self.events[:-1]]
+        assert before and before[-1] == "load", "accumulators zeroed before the prologue's loads were issued"
+        assert not {"wait", "read", "mfma"} & set(before), "accumulators zeroed after a wait or read"
+        self.inits += 1
+
     def _mfma(self, buf, idx, i, j):
+        assert self.inits == 1, "MFMA before the accumulators were zeroed"
         step = self.mfmas // self.mfma
         tile, ks = divmod(step, self.ksteps)
         assert idx == self.mfmas % self.mfma, f"MFMA index {idx} out of order"
@@ -184,6 +196,7 @@ class RingModel:
             assert sorted(self.read_log.get(t, [])) == want, f"tile {t} reads"
         assert self.mfmas == self.ktu * self.ksteps * self.mfma
         assert self.blocks == set(), "a K step ended without all its blocks"
+        assert self.inits == 1, "accumulators never zeroed"
         if self.early_free:
             assert sorted(self.prepared) == list(range(self.S, self.ktu)), f"refills prepared: {sorted(self.prepared)}"
 
@@ -251,6 +264,18 @@ def test_model_rejects_wrong_mfma_operands():
     first = next(n for n in mfmas[3 * per_step:4 * per_step] if events[n][3] == 1)
     moved = events[:r] + events[r + 1:first] + [events[first], events[r]] + events[first + 1:]
     assert _rejects(moved, info, 3)
+
+
+def test_model_rejects_misplaced_accumulator_zeroing():
+    """The accumulators are zeroed once, between the prologue's loads and its
+    first wait: a trace that zeroes them after the first MFMA, or twice,
+    fails the model."""
+    events, info = gt.ring_trace(20, 3)
+    k = events.index(("init", 0, 0, 0, 0))
+    first = next(n for n, e in enumerate(events) if e[0] == "mfma")
+    late = events[:k] + events[k + 1:first + 1] + [events[k]] + events[first + 1:]
+    assert _rejects(late, info, 3)
+    assert _rejects(events[:k + 1] + [events[k]] + events[k + 1:], info, 3)
 
 
 def test_trace_info_describes_the_kernels():
