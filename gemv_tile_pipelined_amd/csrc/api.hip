@@ -381,7 +381,8 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus) {
   if (num_cus > (int64_t{1} << 20)) return 0;
   if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows || gt::skinny_wide_route(M, N, static_cast<int>(num_cus))) {
     const int64_t R = M <= gt::kSkinnyMaxRows ? N : N <= gt::kSkinnyMaxRows ? M : (M <= N ? N : M);
-    const int64_t rows = gt::skinny_default_rows(R, static_cast<int>(num_cus));
+    const int64_t S = M <= gt::kSkinnyMaxRows ? M : N <= gt::kSkinnyMaxRows ? N : (M <= N ? M : N);
+    const int64_t rows = gt::skinny_launch_rows(R, S, static_cast<int>(num_cus));
     return (R + rows - 1) / rows;
   }
   if (num_cus > (int64_t{1} << 20)) return 0;

@@ -187,6 +187,21 @@ inline int skinny_default_rows(int64_t R, int num_cus) {
     if (R >= static_cast<int64_t>(rows) * num_cus) return rows;
   return 1;
 }
+// ... and with S rows on the small side: 17..32 small-side rows take 32 P
+// rows per workgroup (each workgroup stages the small side once per 32 P
+// rows instead of 16, halving its reads from the caches) when R gives every
+// CU that many and no CU gets more rows than with 16 per workgroup (whole
+// waves of workgroups: 12288 rows on 256 CUs make 1.5 waves of 32-row
+// workgroups, 3 of 16-row ones, and the 16-row form was faster there).
+inline int skinny_launch_rows(int64_t R, int64_t S, int num_cus) {
+  if (S > kSkinnyMaxRows && S <= 32 && R >= int64_t{32} * num_cus) {
+    const int64_t c = num_cus;
+    const int64_t rows32 = ((R + 31) / 32 + c - 1) / c * 32;  // P rows per CU, 32-row workgroups
+    const int64_t rows16 = ((R + 15) / 16 + c - 1) / c * 16;  // ... and 16-row ones
+    if (rows32 <= rows16) return 32;
+  }
+  return skinny_default_rows(R, num_cus);
+}
 
 // Split K on the skinny kernel (gemm_splitk_*, with R rows on the large side
 // and 2..16 on the small one): while ceil(R / 16) blocks of 16 rows leave

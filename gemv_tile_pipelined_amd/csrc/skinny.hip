@@ -143,18 +143,21 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   constexpr int kStepsPerWave = kSteps / WAVES;
   static_assert(QROWS == 8 || QROWS == 16 || QROWS == 32 || QROWS == 64, "Q tile rows");
   constexpr int QB = QROWS >= 32 ? QROWS / 16 : 1;  // 16-row blocks of Q (each its own MFMA)
+  constexpr int PB = PR > 16 ? PR / 16 : 1;         // 16-row blocks of P
+  constexpr int kPRows = 16 * PB;                   // P rows of the partial sums
   // With 64 Q rows the ring takes (nearly) all of the LDS: the wave partial
   // sums then reuse the ring once the K loop is done with it.
   constexpr bool kAliasPartial = QROWS == 64;
-  constexpr int kPartialBytes = WAVES * 16 * QB * 17 * 4;
-  static_assert(PR == 1 || PR == 2 || PR == 4 || PR == 8 || PR == 16, "P rows per workgroup");
+  constexpr int kPartialBytes = WAVES * 16 * QB * (kPRows + 1) * 4;
+  static_assert(PR == 1 || PR == 2 || PR == 4 || PR == 8 || PR == 16 || PR == 32, "P rows per workgroup");
   static_assert(kSteps % WAVES == 0, "work split");
   static_assert(STAGES >= 2 && (STAGES - 1) * kDmaPerWave <= 63, "vmcnt range");
   static_assert(STAGES * kStageBytes + (kAliasPartial ? 0 : kPartialBytes) <= 160 * 1024,
                 "gfx950 has 160 KiB of LDS per CU");
   static_assert(!kAliasPartial || kPartialBytes <= STAGES * kStageBytes, "partial sums fit the ring");
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * kStageBytes + (kAliasPartial ? 0 : kPartialBytes)];
-  auto partial = reinterpret_cast<float (*)[16 * QB][17]>(ring + (kAliasPartial ? 0 : STAGES * kStageBytes));
+  auto partial =
+      reinterpret_cast<float (*)[16 * QB][kPRows + 1]>(ring + (kAliasPartial ? 0 : STAGES * kStageBytes));
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -211,7 +214,7 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   const int frow = lane & 15;
   const int kgrp = lane >> 4;
   const int kperm = ((kgrp & 1) << 1) | (kgrp >> 1);
-  const int prow = frow % PR;  // P row of this lane's fragment
+  const int prow = frow % (PR < 16 ? PR : 16);  // P row of this lane's fragment in P block 0
   const uint32_t frag_off = static_cast<uint32_t>(prow * kRowBytes);
   const int fswz = swz(prow);
   const int qrow = frow % (QROWS < 16 ? QROWS : 16);  // Q row of this lane's fragment in Q block 0
@@ -222,9 +225,11 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nkt) issue(s);
 
-  float4_t acc[QB];
+  float4_t acc[PB][QB];
 #pragma unroll
-  for (int b = 0; b < QB; ++b) acc[b] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int a = 0; a < PB; ++a)
+#pragma unroll
+    for (int b = 0; b < QB; ++b) acc[a][b] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   for (int kt = 0; kt < nkt; ++kt) {
     // Tile kt has landed once at most `younger` tiles' loads are pending.
     // Loads complete in issue order, so waiting until at most
@@ -238,16 +243,22 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
     for (int j = 0; j < kStepsPerWave; ++j) {
       const int step = wave * kStepsPerWave + j;
       const int c = step * 4 + kperm;  // logical chunk
-      const half8_t pf = *reinterpret_cast<const half8_t *>(stage + frag_off + ((c ^ fswz) << 4));
+      half8_t pf[PB];
+#pragma unroll
+      for (int a = 0; a < PB; ++a)
+        pf[a] = *reinterpret_cast<const half8_t *>(stage + frag_off + a * 16 * kRowBytes + ((c ^ fswz) << 4));
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
         const half8_t qf =
             *reinterpret_cast<const half8_t *>(stage + qfrag_off + b * 16 * kRowBytes + ((c ^ qswz) << 4));
-        if constexpr (DT == kF16)
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, qf, acc[b], 0, 0, 0);
-        else
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pf),
-                                                           __builtin_bit_cast(bf16x8_t, qf), acc[b], 0, 0, 0);
+#pragma unroll
+        for (int a = 0; a < PB; ++a) {
+          if constexpr (DT == kF16)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[a], qf, acc[a][b], 0, 0, 0);
+          else
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, pf[a]), __builtin_bit_cast(bf16x8_t, qf), acc[a][b], 0, 0, 0);
+        }
       }
     }
   }
@@ -256,14 +267,16 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   // flight: the last tile was waited for) before the partials overwrite it.
   if constexpr (kAliasPartial) __syncthreads();
 #pragma unroll
-  for (int b = 0; b < QB; ++b)
+  for (int a = 0; a < PB; ++a)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) partial[wave][16 * b + frow][4 * kgrp + e] = acc[b][e];
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) partial[wave][16 * b + frow][16 * a + 4 * kgrp + e] = acc[a][b][e];
   __syncthreads();
-  // 16*QB x 16 outputs (Q row s, P row r), each the wave partials in wave order.
-  for (int i = threadIdx.x; i < 256 * QB; i += WAVES * 64) {
-    const int s = i >> 4;
-    const int r = i & 15;
+  // 16*QB x kPRows outputs (Q row s, P row r), each the wave partials in wave order.
+  for (int i = threadIdx.x; i < 16 * QB * kPRows; i += WAVES * 64) {
+    const int s = i / kPRows;
+    const int r = i % kPRows;
     float sum = 0.0f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += partial[w][s][r];
@@ -345,7 +358,7 @@ hipError_t launch_gemm_skinny_splitk(int dtype, const void *A, const void *B, vo
 template <int DT>
 static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                                   int num_cus, hipStream_t stream) {
-  const int pr = skinny_default_rows(R, num_cus);
+  const int pr = skinny_launch_rows(R, S, num_cus);
   if (S > 32) {
     // 33..64 small-side rows: 64 staged Q rows, 8 waves (1-4 % ahead of 4,
     // 16 waves 5-17 % behind), a 2-stage ring of (PR + 64) KiB stages, the
@@ -363,6 +376,10 @@ static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, 
     // (PR + 32) KiB stages.
     const bool rot = K % 4096 == 0;
     switch (pr) {
+      case 32:
+        // two 16-row P blocks: (32 + 32) KiB stages, so a 2-stage ring
+        return rot ? launch_lds<4, 2, 32, DT, 32, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
+                   : launch_lds<4, 2, 32, DT, 32, 0, true>(P, Q, D, R, S, K, trans, stream);
       case 16: return rot ? launch_lds<4, 3, 32, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
                           : launch_lds<4, 3, 32, DT, 16, 0, true>(P, Q, D, R, S, K, trans, stream);
       case 8: return rot ? launch_lds<4, 3, 32, DT, 8, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)

@@ -75,7 +75,8 @@ enum gemvtile_status {
  * batch against a weight matrix --, the call runs a bandwidth-bound kernel
  * that streams the larger operand once instead of the tiled one (with fewer
  * rows of it per workgroup when it has too few rows to give every compute
- * unit 16), and when M == 1 or N == 1 the GEMV kernel of gemv_f16; results
+ * unit 16, and 32 when the smaller side has 17..32 rows and the larger one
+ * enough to give every compute unit 32 in whole waves), and when M == 1 or N == 1 the GEMV kernel of gemv_f16; results
  * are deterministic either way.
  * Returns a gemvtile_status.
  */
@@ -312,7 +313,9 @@ int64_t gemvtile_gemv_grid(int64_t N, int64_t K, int64_t num_cus);
  * there), ceil(R/p) with R = N if
  * M <= 16, else M if N <= 16, else the larger side, and p the largest of
  * 16, 8, 4, 2 rows per workgroup such that R >= p*num_cus, else p = 1;
- * otherwise the
+ * except that p = 32 when the smaller side S has 17..32 rows, R >= 32*num_cus
+ * and ceil(ceil(R/32)/num_cus)*32 <= ceil(ceil(R/16)/num_cus)*16 (no compute
+ * unit gets more rows than with p = 16); otherwise the
  * persistent grid min(#tiles, num_cus) over the tiles gemvtile_gemm_tile
  * picks.  Host-only arithmetic; returns 0 for empty outputs.
  */

@@ -232,7 +232,17 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(65, 4097, 4096, 256) == 33  # 1 x 33 tiles of 128x128
     # ... while the 128x128 tiles along the larger side would leave more than
     # half (up to 32 rows) or three quarters (33..64) of the CUs idle
-    assert gt.gemm_grid(32, 16384, 4096, 256) == 1024  # 128 tiles: skinny, 16 rows per workgroup
+    assert gt.gemm_grid(32, 16384, 4096, 256) == 512  # 128 tiles: skinny, 32 rows per workgroup
+    # 17..32 small-side rows take 32 large-side rows per workgroup from
+    # 32 * CUs rows up while no CU gets more rows than with 16 per
+    # workgroup; 64 small-side rows stay at 16
+    assert gt.gemm_grid(24, 8192, 4096, 256) == 256
+    assert gt.gemm_grid(24, 16384, 4096, 256) == 512
+    assert gt.gemm_grid(20, 12288, 4096, 256) == 768  # 1.5 waves of 32-row workgroups: 16 rows
+    assert gt.gemm_grid(20, 12289, 4096, 256) == 385  # 49 rows per CU either way: 32 rows
+    assert gt.gemm_grid(8191, 17, 4096, 256) == 512
+    assert gt.gemm_grid(33, 8192, 4096, 256) == 512
+    assert gt.gemm_grid(16, 8192, 4096, 256) == 512
     assert gt.gemm_grid(32, 16385, 4096, 256) == 129  # 129 tiles: tiled
     assert gt.gemm_grid(64, 8192, 4096, 256) == 512  # 64 tiles: skinny
     assert gt.gemm_grid(14336, 64, 4096, 256) == 112  # 112 tiles: tiled

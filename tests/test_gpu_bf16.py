@@ -108,6 +108,8 @@ SHAPES = [
     (24, 1500, 4104),
     (48, 1500, 1032),
     (48, 4096, 4104),
+    # 32 large-side rows per workgroup
+    (20, 8192, 4096),
 ]
 
 

@@ -115,6 +115,15 @@ SHAPES = [
     (24, 4096, 8192),
     (2500, 20, 4096),
     (48, 2600, 4104),
+    # 17..32 staged rows with 32 large-side rows per workgroup (two 16-row
+    # MFMA blocks of the large side), from 32 rows per CU up: rotated and
+    # unrotated K starts, ragged large side and K, the transposed store;
+    # and past 32 rows per CU where 16-row workgroups fill whole waves
+    (24, 8192, 4096),
+    (32, 12300, 4104),
+    (12300, 17, 1032),
+    (8210, 17, 1032),
+    (20, 12288, 4096),
 ]
 
 
