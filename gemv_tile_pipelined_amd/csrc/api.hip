@@ -110,7 +110,9 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   const bool skinny = M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows;
   const VariantRef v = classify_variant(variant);
   if (v.family == Family::kInvalid) return GEMVTILE_ERR_INVALID_ARG;
-  if (v.family == Family::kSkinny && !skinny) return GEMVTILE_ERR_UNSUPPORTED;
+  // the small-side split (skinny 60) also takes 17..64 rows on the smaller side
+  const bool skinny_wide = (M < N ? M : N) <= gt::kSkinnyWideRows;
+  if (v.family == Family::kSkinny && !skinny && !(v.index == 60 && skinny_wide)) return GEMVTILE_ERR_UNSUPPORTED;
   int cus = 0;
   st = current_cu_count(&cus);
   if (st != GEMVTILE_OK) return st;
@@ -376,17 +378,22 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus) {
   // One row on a side: the GEMV kernel over the other side's rows.
   if (M == 1 || N == 1) return gemvtile_gemv_grid(M == 1 ? N : M, K, num_cus);
   // Skinny shapes (at most 16 rows on a side, or 17..64 on the smaller
-  // side as skinny_wide_route decides): one workgroup per 16, 8, 4, 2 or 1
-  // rows of the other side.
+  // side as skinny_wide_route decides): one workgroup per 32, 16, 8, 4, 2 or
+  // 1 rows of the other side, times the small side's 16-row blocks when it
+  // is split.
   if (num_cus > (int64_t{1} << 20)) return 0;
-  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows || gt::skinny_wide_route(M, N, static_cast<int>(num_cus))) {
+  const int cus = static_cast<int>(num_cus);
+  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows || gt::skinny_wide_route(M, N, cus)) {
     const int64_t R = M <= gt::kSkinnyMaxRows ? N : N <= gt::kSkinnyMaxRows ? M : (M <= N ? N : M);
     const int64_t S = M <= gt::kSkinnyMaxRows ? M : N <= gt::kSkinnyMaxRows ? N : (M <= N ? M : N);
-    const int64_t rows = gt::skinny_launch_rows(R, S, static_cast<int>(num_cus));
+    if (gt::skinny_qsplit(R, S, cus)) {
+      const int64_t rows = gt::skinny_qsplit_rows(R, S, cus);
+      return (R + rows - 1) / rows * ((S + 15) / 16);
+    }
+    const int64_t rows = gt::skinny_launch_rows(R, S, cus);
     return (R + rows - 1) / rows;
   }
-  if (num_cus > (int64_t{1} << 20)) return 0;
-  const gt::GemmTileShape &t = gt::kGemmTileShapes[gt::gemm_default_tile(M, N, static_cast<int>(num_cus))];
+  const gt::GemmTileShape &t = gt::kGemmTileShapes[gt::gemm_default_tile(M, N, cus)];
   const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
   return tiles < num_cus ? tiles : num_cus;
 }

@@ -124,10 +124,12 @@ inline bool skinny_wide_route(int64_t M, int64_t N, int num_cus) {
 // and not kept stay unused.
 constexpr int kSkinnyVariantBase = 100;
 constexpr int kGemmWsVariantBase = 200;
-inline bool skinny_variant_exists(int v) { return v == 0 || v == 4 || v == 12 || v == 30 || v == 47 || v == 52; }
+inline bool skinny_variant_exists(int v) {
+  return v == 0 || v == 4 || v == 12 || v == 30 || v == 47 || v == 52 || v == 60;
+}
 // Wave-specialised (producer / consumer) GEMM launch shapes (gemm_ws.hip).
 constexpr int kGemmWsVariants = 2;
-static_assert(kGemmVariants <= kSkinnyVariantBase && kSkinnyVariantBase + 53 <= kGemmWsVariantBase,
+static_assert(kGemmVariants <= kSkinnyVariantBase && kSkinnyVariantBase + 61 <= kGemmWsVariantBase,
               "variant families must not overlap");
 
 // The default GEMV launch for an N x K matrix on a device with num_cus
@@ -201,6 +203,29 @@ inline int skinny_launch_rows(int64_t R, int64_t S, int num_cus) {
     if (rows32 <= rows16) return 32;
   }
   return skinny_default_rows(R, num_cus);
+}
+// 17..64 small-side rows against few large-side rows: the small side is
+// split into ceil(S / 16) blocks of 16 rows along the grid's y dimension,
+// each workgroup staging one block (the launches of the S <= 16 case), when
+// the staged form above would take fewer than 8 P rows per workgroup, or 8
+// with at most 32 small-side rows.  Each workgroup then re-reads 16 Q rows
+// per P row block instead of all S, and P is read ceil(S / 16) times, from
+// the caches after the first (64x1024x14336 31.0 -> 17.5 us, 48x1500x4104
+// 20.1 -> 11.6 us, 20x2048x4096 7.8 -> 6.2 us; at 16 P rows per workgroup,
+// or 8 with 64 small-side rows, it measured 13-125 % slower).
+inline bool skinny_qsplit(int64_t R, int64_t S, int num_cus) {
+  if (S <= kSkinnyMaxRows || S > kSkinnyWideRows) return false;
+  const int pr = skinny_launch_rows(R, S, num_cus);
+  return pr < 8 || (pr == 8 && S <= 32);
+}
+// P rows per workgroup of the split launch: the most of 16, 8, 4, 2 that
+// still gives every CU a workgroup (counting the ceil(S / 16) small-side
+// blocks), else 1.
+inline int skinny_qsplit_rows(int64_t R, int64_t S, int num_cus) {
+  const int64_t qb = (S + 15) / 16;
+  for (int rows = 16; rows > 1; rows >>= 1)
+    if ((R + rows - 1) / rows * qb >= num_cus) return rows;
+  return 1;
 }
 
 // Split K on the skinny kernel (gemm_splitk_*, with R rows on the large side

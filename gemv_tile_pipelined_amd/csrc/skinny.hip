@@ -173,8 +173,12 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   }
   const int r0 = rb * PR;
   const int prows = min(PR, R - r0);
+  // With the small side split over the grid's y dimension, this workgroup
+  // stages Q rows [q0, q0 + QROWS) (q0 = 0 with one Q block).
+  const int q0 = static_cast<int>(blockIdx.y) * QROWS;
   const int4_t rsrc_p = make_buffer_rsrc(P + static_cast<int64_t>(r0) * K, static_cast<uint32_t>(prows) * K * 2u);
-  const int4_t rsrc_q = make_buffer_rsrc(Q, static_cast<uint32_t>(S) * K * 2u);
+  const int4_t rsrc_q =
+      make_buffer_rsrc(Q + static_cast<int64_t>(q0) * K, static_cast<uint32_t>(S - q0) * K * 2u);
   const uint32_t ring0 = lds_addr(ring);
   // With KROT, workgroup b walks its K tiles from tile j % nkt and wraps, so
   // the workgroups running at one moment read different K ranges: j = b
@@ -280,8 +284,9 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
     float sum = 0.0f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += partial[w][s][r];
-    if (s < S && r < PR && r0 + r < R) {
-      const int64_t idx = TRANS ? static_cast<int64_t>(r0 + r) * S + s : static_cast<int64_t>(s) * R + r0 + r;
+    const int sg = q0 + s;  // row of Q (column of D when TRANS)
+    if (s < QROWS && sg < S && r < PR && r0 + r < R) {
+      const int64_t idx = TRANS ? static_cast<int64_t>(r0 + r) * S + sg : static_cast<int64_t>(sg) * R + r0 + r;
       if constexpr (SPLIT)
         ws[static_cast<int64_t>(slice) * R * S + idx] = sum;
       else
@@ -290,10 +295,12 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   }
 }
 
+// ceil(R / PR) workgroups along x; with qblocks > 1 the small side is split
+// into blocks of QROWS rows along y.
 template <int WAVES, int STAGES, int QROWS, int DT = kF16, int PR = 16, int KROT = 0, bool NTP = false>
 static hipError_t launch_lds(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
-                             hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((R + PR - 1) / PR));
+                             hipStream_t stream, int qblocks = 1) {
+  const dim3 grid(static_cast<unsigned>((R + PR - 1) / PR), static_cast<unsigned>(qblocks));
   const auto *p = static_cast<const _Float16 *>(P);
   const auto *q = static_cast<const _Float16 *>(Q);
   auto *d = static_cast<_Float16 *>(D);
@@ -343,6 +350,25 @@ hipError_t launch_gemm_skinny_splitk(int dtype, const void *A, const void *B, vo
                 : launch_lds_split<16, 4, 16, kF16>(P, Q, D, R, S, K, !small_m, w, splits, stream);
 }
 
+// The small side in ceil(S / 16) blocks of 16 rows along the grid's y
+// dimension, each workgroup staging one block against PR rows of P (the
+// launches of the S <= 16 case), PR from skinny_qsplit_rows.
+template <int DT>
+static hipError_t launch_lds_qsplit(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
+                                    int num_cus, hipStream_t stream) {
+  const int qb = (S + 15) / 16;
+  switch (skinny_qsplit_rows(R, S, num_cus)) {
+    case 16:
+      if (K < kSkinnyStreamMinK)
+        return launch_lds<16, 4, 16, DT, 16, kSkinnyRotateXcd>(P, Q, D, R, S, K, trans, stream, qb);
+      return launch_lds<16, 4, 16, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream, qb);
+    case 8: return launch_lds<8, 4, 16, DT, 8, kSkinnyRotateXcd>(P, Q, D, R, S, K, trans, stream, qb);
+    case 4: return launch_lds<4, 4, 16, DT, 4>(P, Q, D, R, S, K, trans, stream, qb);
+    case 2: return launch_lds<4, 4, 16, DT, 2>(P, Q, D, R, S, K, trans, stream, qb);
+    default: return launch_lds<4, 4, 16, DT, 1>(P, Q, D, R, S, K, trans, stream, qb);
+  }
+}
+
 // The default launch (skinny_default_rows): 16 P rows per workgroup with 16
 // waves and a 4-stage ring while R gives every CU such a workgroup, with
 // non-temporal P loads from K = kSkinnyStreamMinK up (cached below); else 8,
@@ -355,39 +381,32 @@ hipError_t launch_gemm_skinny_splitk(int dtype, const void *A, const void *B, vo
 // once.  With 17..32 staged Q rows the rotation is taken only for such rows
 // (elsewhere it measured 5 % slower); with 4 or fewer P rows never (4-10 %
 // slower: every workgroup re-reads the same Q lines, best all at once).
+// 17..64 small-side rows against few P rows take the small-side split
+// (skinny_qsplit).
 template <int DT>
 static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                                   int num_cus, hipStream_t stream) {
+  if (skinny_qsplit(R, S, num_cus)) return launch_lds_qsplit<DT>(P, Q, D, R, S, K, trans, num_cus, stream);
   const int pr = skinny_launch_rows(R, S, num_cus);
   if (S > 32) {
-    // 33..64 small-side rows: 64 staged Q rows, 8 waves (1-4 % ahead of 4,
-    // 16 waves 5-17 % behind), a 2-stage ring of (PR + 64) KiB stages, the
-    // partial sums reusing the ring.
-    switch (pr) {
-      case 16: return launch_lds<8, 2, 64, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream);
-      case 8: return launch_lds<8, 2, 64, DT, 8, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream);
-      case 4: return launch_lds<8, 2, 64, DT, 4>(P, Q, D, R, S, K, trans, stream);
-      case 2: return launch_lds<8, 2, 64, DT, 2>(P, Q, D, R, S, K, trans, stream);
-      default: return launch_lds<8, 2, 64, DT, 1>(P, Q, D, R, S, K, trans, stream);
-    }
+    // 33..64 small-side rows at 16 or 8 P rows per workgroup (fewer take the
+    // split): 64 staged Q rows, 8 waves (1-4 % ahead of 4, 16 waves 5-17 %
+    // behind), a 2-stage ring of (PR + 64) KiB stages, the partial sums
+    // reusing the ring.
+    return pr == 16 ? launch_lds<8, 2, 64, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
+                    : launch_lds<8, 2, 64, DT, 8, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream);
   }
   if (S > kSkinnyMaxRows) {
-    // 17..32 small-side rows: 32 staged Q rows, 4 waves, a 3-stage ring of
-    // (PR + 32) KiB stages.
+    // 17..32 small-side rows at 32 or 16 P rows per workgroup (fewer take
+    // the split): 32 staged Q rows, 4 waves; two 16-row P blocks with
+    // (32 + 32) KiB stages in a 2-stage ring, or one in a 3-stage ring of
+    // (16 + 32) KiB stages.
     const bool rot = K % 4096 == 0;
-    switch (pr) {
-      case 32:
-        // two 16-row P blocks: (32 + 32) KiB stages, so a 2-stage ring
-        return rot ? launch_lds<4, 2, 32, DT, 32, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
-                   : launch_lds<4, 2, 32, DT, 32, 0, true>(P, Q, D, R, S, K, trans, stream);
-      case 16: return rot ? launch_lds<4, 3, 32, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
-                          : launch_lds<4, 3, 32, DT, 16, 0, true>(P, Q, D, R, S, K, trans, stream);
-      case 8: return rot ? launch_lds<4, 3, 32, DT, 8, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
-                         : launch_lds<4, 3, 32, DT, 8, 0, true>(P, Q, D, R, S, K, trans, stream);
-      case 4: return launch_lds<4, 3, 32, DT, 4>(P, Q, D, R, S, K, trans, stream);
-      case 2: return launch_lds<4, 3, 32, DT, 2>(P, Q, D, R, S, K, trans, stream);
-      default: return launch_lds<4, 3, 32, DT, 1>(P, Q, D, R, S, K, trans, stream);
-    }
+    if (pr == 32)
+      return rot ? launch_lds<4, 2, 32, DT, 32, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
+                 : launch_lds<4, 2, 32, DT, 32, 0, true>(P, Q, D, R, S, K, trans, stream);
+    return rot ? launch_lds<4, 3, 32, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
+               : launch_lds<4, 3, 32, DT, 16, 0, true>(P, Q, D, R, S, K, trans, stream);
   }
   const bool q8 = S <= 8;
   switch (pr) {
@@ -442,7 +461,7 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
   // The small side is Q.  Q = A, P = B, D = Q·Pᵀ when the small side is M;
   // otherwise Q = B, P = A, D = P·Qᵀ.
   bool small_m = false;
-  if (!skinny_small_m(M, N, variant == 0, &small_m)) return hipErrorInvalidValue;
+  if (!skinny_small_m(M, N, variant == 0 || variant == 60, &small_m)) return hipErrorInvalidValue;
   const void *P = small_m ? B : A;
   const void *Q = small_m ? A : B;
   const int R = small_m ? N : M;
@@ -460,6 +479,8 @@ hipError_t launch_gemm_skinny_f16(int variant, const void *A, const void *B, voi
     case 47: return launch_lds<16, 4, 16, kF16, 16, true, true>(P, Q, D, R, S, K, !small_m, stream);
     // as 47 without the rotated K start
     case 52: return launch_lds<16, 4, 16, kF16, 16, false, true>(P, Q, D, R, S, K, !small_m, stream);
+    // the small side in 16-row blocks along the grid's y dimension, whatever the shape
+    case 60: return launch_lds_qsplit<kF16>(P, Q, D, R, S, K, !small_m, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

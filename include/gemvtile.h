@@ -76,7 +76,9 @@ enum gemvtile_status {
  * that streams the larger operand once instead of the tiled one (with fewer
  * rows of it per workgroup when it has too few rows to give every compute
  * unit 16, and 32 when the smaller side has 17..32 rows and the larger one
- * enough to give every compute unit 32 in whole waves), and when M == 1 or N == 1 the GEMV kernel of gemv_f16; results
+ * enough to give every compute unit 32 in whole waves; with 17..64 rows on
+ * the smaller side and few on the larger, the smaller side is split into
+ * 16-row blocks over the workgroups instead), and when M == 1 or N == 1 the GEMV kernel of gemv_f16; results
  * are deterministic either way.
  * Returns a gemvtile_status.
  */
@@ -315,7 +317,10 @@ int64_t gemvtile_gemv_grid(int64_t N, int64_t K, int64_t num_cus);
  * 16, 8, 4, 2 rows per workgroup such that R >= p*num_cus, else p = 1;
  * except that p = 32 when the smaller side S has 17..32 rows, R >= 32*num_cus
  * and ceil(ceil(R/32)/num_cus)*32 <= ceil(ceil(R/16)/num_cus)*16 (no compute
- * unit gets more rows than with p = 16); otherwise the
+ * unit gets more rows than with p = 16); and, when S has 17..64 rows and
+ * that p is below 8 (or 8 with S <= 32), ceil(S/16)*ceil(R/q) with q the
+ * largest of 16, 8, 4, 2 such that ceil(S/16)*ceil(R/q) >= num_cus, else
+ * q = 1 (the smaller side split into 16-row blocks); otherwise the
  * persistent grid min(#tiles, num_cus) over the tiles gemvtile_gemm_tile
  * picks.  Host-only arithmetic; returns 0 for empty outputs.
  */
@@ -349,8 +354,8 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
  * Variants 1..31 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16, and some shapes with 17..64 rows on the smaller side: the skinny
- * kernel).  The skinny kernel (only for M <= 16 or N <= 16, else
- * GEMVTILE_ERR_UNSUPPORTED):
+ * kernel).  The skinny kernel (only for M <= 16 or N <= 16, and 160 also
+ * for 17..64 rows on the smaller side, else GEMVTILE_ERR_UNSUPPORTED):
  *   100 the gemm_f16 choice (16, 8, 4, 2 or 1 rows of the large side per
  *       workgroup, see gemvtile_gemm_grid)
  *   104 operands loaded straight into registers (8 waves, 4 K steps of 32
@@ -361,6 +366,10 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
  *       number of K tiles)
  *   147 as 130 with the large side loaded non-temporally
  *   152 as 147 with every workgroup starting its K walk at K tile 0
+ *   160 the small side split into blocks of 16 rows along the grid's y
+ *       dimension, each workgroup staging one block against 16, 8, 4, 2 or
+ *       1 rows of the large side (the most that still give every compute
+ *       unit a workgroup); also for 17..64 rows on the smaller side
  * (gemm_f16's choice at 16 rows per workgroup starts workgroup b at K tile
  * b / 8, its index within its XCD, and loads the large side non-temporally
  * from K = 8192 up.)

@@ -89,9 +89,11 @@ def test_gemm_argument_validation(lib):
     # ablations measured and not kept, are invalid
     for bad in (-1, 4, 9, 11, 12, 15, 19, 29, 32, 36, 99, 101, 113, 131, 140, 148, 149, 153, 199, 202, 1000):
         assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, bad) == INVALID, bad
-    # skinny launch shapes only apply when one side has at most 16 rows
+    # skinny launch shapes only apply when one side has at most 16 rows (at
+    # most 64 for the small-side split, 160)
     for v in (100, 104, 112, 130, 147, 152):
         assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, v) == UNSUPPORTED, v
+    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 65, 65, 8, None, 160) == UNSUPPORTED
 
 
 def test_gemm_bias_argument_validation(lib):
@@ -225,9 +227,17 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(16, 16, 4096, 256) == 16
     # 17..64 rows on the smaller side: the skinny kernel too, over the larger side
     assert gt.gemm_grid(17, 4097, 4096, 256) == 257  # 16 rows per workgroup
-    assert gt.gemm_grid(32, 1000, 4096, 256) == 500  # 2 rows per workgroup
-    assert gt.gemm_grid(4000, 30, 4096, 256) == 500  # 8 rows per workgroup
-    assert gt.gemm_grid(20, 24, 4096, 256) == 24  # the larger side, 1 row per workgroup
+    # ... with the small side split into 16-row blocks (grid y) where the
+    # staged launch would take fewer than 8 rows per workgroup, or 8 with at
+    # most 32 small-side rows: blocks x workgroups of the most of 16, 8, 4, 2
+    # rows that still give every CU one
+    assert gt.gemm_grid(32, 1000, 4096, 256) == 2 * 250  # 4 rows per workgroup
+    assert gt.gemm_grid(4000, 30, 4096, 256) == 2 * 250  # 16 rows per workgroup
+    assert gt.gemm_grid(20, 24, 4096, 256) == 2 * 24  # 1 row per workgroup
+    assert gt.gemm_grid(64, 1024, 14336, 256) == 4 * 64
+    assert gt.gemm_grid(1500, 48, 4104, 256) == 3 * 94
+    assert gt.gemm_grid(30, 2100, 4096, 256) == 2 * 132  # staged: 8 rows, at most 32 small-side rows
+    assert gt.gemm_grid(50, 2100, 4096, 256) == 263  # staged, 8 rows per workgroup
     assert gt.gemm_grid(64, 4097, 4096, 256) == 257
     assert gt.gemm_grid(65, 4097, 4096, 256) == 33  # 1 x 33 tiles of 128x128
     # ... while the 128x128 tiles along the larger side would leave more than

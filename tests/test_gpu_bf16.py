@@ -107,6 +107,7 @@ SHAPES = [
     # and the 64-row staging at 16 large-side rows per workgroup
     (24, 1500, 4104),
     (48, 1500, 1032),
+    (1000, 50, 2056),
     (48, 4096, 4104),
     # 32 large-side rows per workgroup
     (20, 8192, 4096),

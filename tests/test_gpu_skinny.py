@@ -105,11 +105,17 @@ SHAPES = [
     (64, 64, 72),
     (50, 300, 8200),
     (33, 129, 8),
-    # 1024 <= large side < 2048: 4 large-side rows per workgroup on a 256-CU
-    # part, with 32 and 64 staged small-side rows (and ragged K)
+    # few large-side rows: the small side split into 16-row blocks along the
+    # grid's y dimension, 4 large-side rows per workgroup on a 256-CU part
+    # (and ragged K), a ragged last block of 2 rows with the transposed
+    # store, 16 large-side rows at 8 staged-launch rows with <= 32 small-side
+    # rows, and 4 blocks at the 64-row limit
     (24, 1500, 4104),
     (1500, 48, 1032),
     (40, 1100, 8200),
+    (1000, 50, 2056),
+    (20, 2048, 4096),
+    (64, 1024, 14336),
     # 17..32 staged rows with rotated K starts (K % 4096 == 0), at 16 and 8
     # large-side rows per workgroup; 33..64 at 8 rows per workgroup
     (24, 4096, 8192),
