@@ -110,9 +110,11 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
   const bool skinny = M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows;
   const VariantRef v = classify_variant(variant);
   if (v.family == Family::kInvalid) return GEMVTILE_ERR_INVALID_ARG;
-  // the small-side split (skinny 60) also takes 17..64 rows on the smaller side
+  // the skinny kernel as gemm_f16 launches it (skinny 0) and the small-side
+  // split (skinny 60) also take 17..64 rows on the smaller side
   const bool skinny_wide = (M < N ? M : N) <= gt::kSkinnyWideRows;
-  if (v.family == Family::kSkinny && !skinny && !(v.index == 60 && skinny_wide)) return GEMVTILE_ERR_UNSUPPORTED;
+  if (v.family == Family::kSkinny && !skinny && !((v.index == 0 || v.index == 60) && skinny_wide))
+    return GEMVTILE_ERR_UNSUPPORTED;
   int cus = 0;
   st = current_cu_count(&cus);
   if (st != GEMVTILE_OK) return st;
@@ -133,9 +135,8 @@ int run_gemm(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
                                         : gt::launch_gemv_f16(0, x, W, D, rows, k, cus, s));
   }
   // Variant 0 sends shapes with at most 16 rows on one side, and those with
-  // 17..64 on the smaller side that the tiled kernel would spread too
-  // thinly (skinny_wide_route), to the skinny kernel.
-  if (variant == 0 && (skinny || gt::skinny_wide_route(M, N, cus)))
+  // 17..64 on the smaller side (skinny_wide_route), to the skinny kernel.
+  if (variant == 0 && (skinny || gt::skinny_wide_route(M, N)))
     return to_status(dtype == gt::kBF16 ? gt::launch_gemm_skinny_bf16(A, B, D, m, n, k, cus, s)
                                         : gt::launch_gemm_skinny_f16(0, A, B, D, m, n, k, cus, s));
   return to_status(dtype == gt::kBF16 ? gt::launch_gemm_bf16(A, B, D, m, n, k, cus, s)
@@ -378,19 +379,19 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus) {
   // One row on a side: the GEMV kernel over the other side's rows.
   if (M == 1 || N == 1) return gemvtile_gemv_grid(M == 1 ? N : M, K, num_cus);
   // Skinny shapes (at most 16 rows on a side, or 17..64 on the smaller
-  // side as skinny_wide_route decides): one workgroup per 32, 16, 8, 4, 2 or
+  // side, skinny_wide_route): one workgroup per 32, 16, 8, 4, 2 or
   // 1 rows of the other side, times the small side's 16-row blocks when it
   // is split.
   if (num_cus > (int64_t{1} << 20)) return 0;
   const int cus = static_cast<int>(num_cus);
-  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows || gt::skinny_wide_route(M, N, cus)) {
+  if (M <= gt::kSkinnyMaxRows || N <= gt::kSkinnyMaxRows || gt::skinny_wide_route(M, N)) {
     const int64_t R = M <= gt::kSkinnyMaxRows ? N : N <= gt::kSkinnyMaxRows ? M : (M <= N ? N : M);
     const int64_t S = M <= gt::kSkinnyMaxRows ? M : N <= gt::kSkinnyMaxRows ? N : (M <= N ? M : N);
     if (gt::skinny_qsplit(R, S, cus)) {
       const int64_t rows = gt::skinny_qsplit_rows(R, S, cus);
       return (R + rows - 1) / rows * ((S + 15) / 16);
     }
-    const int64_t rows = gt::skinny_launch_rows(R, S, cus);
+    const int64_t rows = gt::skinny_default_rows(R, cus);
     return (R + rows - 1) / rows;
   }
   const gt::GemmTileShape &t = gt::kGemmTileShapes[gt::gemm_default_tile(M, N, cus)];

@@ -102,21 +102,18 @@ inline bool gemv_variant_exists(int v) {
 constexpr int kSkinnyMaxRows = 16;
 // gemm_f16 / gemm_bf16 also send shapes whose smaller side has 17..64 rows
 // to the skinny kernel (two or four 16-row blocks of the small operand per
-// MFMA step): the tiled kernel's 128-row tiles would leave most of each
-// tile and most CUs idle there.  The forced skinny launch shapes stay at 16
-// rows.
+// MFMA step, or the small side split into 16-row blocks over the grid): the
+// tiled kernel's 128-row tiles would leave most of each tile idle there.
 constexpr int kSkinnyWideRows = 64;
 // The default's choice for such shapes (S = 17..64 rows on the smaller side,
-// R on the larger): the skinny kernel while the tiled kernel's 128x128 tiles
-// along R would leave more than half the CUs idle (S <= 32) or more than
-// three quarters (S > 32: the skinny kernel re-reads twice the small rows
-// per workgroup); measured on MI355X, the tiled kernel was faster past that
-// (64 x 14336 x 4096: 37 against 46 us).
-inline bool skinny_wide_route(int64_t M, int64_t N, int num_cus) {
+// R on the larger): the skinny kernel whatever R.  Measured on MI355X
+// against the tiled kernel past the R where 128x128 tiles fill the CUs, it
+// was 5-27 % faster (64x16384x4096 39.9 -> 29.7 us, 24x24576x4096 47.0 ->
+// 34.2 us, 64x12288x14336 123.8 -> 93.0 us, 64x65536x4096 122.7 -> 116.4
+// us), with 32 large-side rows per workgroup in K tiles of 256.
+inline bool skinny_wide_route(int64_t M, int64_t N) {
   const int64_t S = M < N ? M : N;
-  const int64_t R = M < N ? N : M;
-  if (S <= kSkinnyMaxRows || S > kSkinnyWideRows) return false;
-  return (R + 127) / 128 * (S > 32 ? 4 : 2) <= num_cus;
+  return S > kSkinnyMaxRows && S <= kSkinnyWideRows;
 }
 // gemvtile_gemm_f16_variant numbers each kernel family from a fixed base:
 // tiled GEMM 0.., skinny kSkinnyVariantBase + (0, 4, 12, 30, 47),
@@ -183,26 +180,16 @@ constexpr int kSkinnyStreamMinK = 8192;
 constexpr int kSkinnyRotateXcd = 2;
 
 // P rows per workgroup of the default skinny launch for R rows of the large
-// operand: the largest of 16, 8, 4, 2 with R >= rows * num_cus, else 1.
+// operand: the largest of 32, 16, 8, 4, 2 with R >= rows * num_cus, else 1.
+// 32 rows go in K tiles of 256 (so that a ring of 3 or 4 stages still fits
+// the LDS), and each workgroup then stages the small side once per 32 P
+// rows instead of 16: 64x8192x8192 40.4 -> 28.6 us, 24x8192x4096 16.0 ->
+// 12.5 us, 16x8192x8192 24.4 -> 21.6 us, also at 1.5 waves of workgroups
+// (20x12288x8192 43.3 -> 38.1 us).
 inline int skinny_default_rows(int64_t R, int num_cus) {
-  for (int rows = 16; rows > 1; rows >>= 1)
+  for (int rows = 32; rows > 1; rows >>= 1)
     if (R >= static_cast<int64_t>(rows) * num_cus) return rows;
   return 1;
-}
-// ... and with S rows on the small side: 17..32 small-side rows take 32 P
-// rows per workgroup (each workgroup stages the small side once per 32 P
-// rows instead of 16, halving its reads from the caches) when R gives every
-// CU that many and no CU gets more rows than with 16 per workgroup (whole
-// waves of workgroups: 12288 rows on 256 CUs make 1.5 waves of 32-row
-// workgroups, 3 of 16-row ones, and the 16-row form was faster there).
-inline int skinny_launch_rows(int64_t R, int64_t S, int num_cus) {
-  if (S > kSkinnyMaxRows && S <= 32 && R >= int64_t{32} * num_cus) {
-    const int64_t c = num_cus;
-    const int64_t rows32 = ((R + 31) / 32 + c - 1) / c * 32;  // P rows per CU, 32-row workgroups
-    const int64_t rows16 = ((R + 15) / 16 + c - 1) / c * 16;  // ... and 16-row ones
-    if (rows32 <= rows16) return 32;
-  }
-  return skinny_default_rows(R, num_cus);
 }
 // 17..64 small-side rows against few large-side rows: the small side is
 // split into ceil(S / 16) blocks of 16 rows along the grid's y dimension,
@@ -215,7 +202,7 @@ inline int skinny_launch_rows(int64_t R, int64_t S, int num_cus) {
 // or 8 with 64 small-side rows, it measured 13-125 % slower).
 inline bool skinny_qsplit(int64_t R, int64_t S, int num_cus) {
   if (S <= kSkinnyMaxRows || S > kSkinnyWideRows) return false;
-  const int pr = skinny_launch_rows(R, S, num_cus);
+  const int pr = skinny_default_rows(R, num_cus);
   return pr < 8 || (pr == 8 && S <= 32);
 }
 // P rows per workgroup of the split launch: the most of 16, 8, 4, 2 that

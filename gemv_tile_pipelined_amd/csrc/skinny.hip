@@ -96,28 +96,33 @@ gemm_skinny_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ 
 }
 
 // LDS-staged variant: both operands go through a STAGES-deep LDS ring of K
-// tiles of BK = 512 (1 KiB per row), filled by direct-to-LDS loads in which
-// one wave instruction moves one whole 1 KiB row segment (the register
-// variant above touches 16 rows x 64 bytes per instruction, and every
-// workgroup re-reads the small operand that way).  A workgroup owns PR rows
-// of P (16 by default; 8, 4, 2 or 1 when R is too small to give every CU a
-// workgroup of 16 -- the page's "enough blocks" again, here without splitting
-// K, since every workgroup re-reading the small Q costs only cache traffic).
+// tiles of BK = 512 (1 KiB per row) or 256 (512 bytes per row), filled by
+// direct-to-LDS loads in which one wave instruction moves 1 KiB: one row
+// segment, or two at BK = 256 (the register variant above touches 16 rows x
+// 64 bytes per instruction, and every workgroup re-reads the small operand
+// that way).  A workgroup owns PR rows of P (32 at BK = 256 or 16 by default;
+// 8, 4, 2 or 1 when R is too small to give every CU a workgroup of 16 -- the
+// page's "enough blocks" again, here without splitting K, since every
+// workgroup re-reading the small Q costs only cache traffic).
 // A stage holds the PR rows of P and QROWS rows of Q (rows past R or S and K
 // past K read as zero: the buffer descriptors' ranges and an out-of-range
 // offset).  The MFMA's 16 P lanes read P row (lane % PR) and its 16 Q lanes
 // Q row (lane % QROWS): rows re-read that way only reach outputs that are
-// never stored.  QROWS = 8 (for S <= 8) halves the Q traffic.  The
-// PR + QROWS row loads of a stage are spread over the waves,
-// ceil((PR+QROWS)/WAVES) per wave; spare slots load zeros (out-of-range
-// offset, no memory access) into a junk row so every wave issues the same
-// number of loads and the vmcnt accounting stays uniform.  Each wave computes
+// never stored.  QROWS = 8 (for S <= 8) halves the Q traffic.  The load
+// instructions of a stage's PR + QROWS rows are spread over the waves;
+// spare slots load zeros (out-of-range offset, no memory access) into a
+// junk KiB so every wave issues the same number of loads and the vmcnt
+// accounting stays uniform.  With PR = 32 the P rows form two 16-row MFMA
+// blocks.  Each wave computes
 // BK/32/WAVES of the stage's K steps.  LDS chunk c of row r holds logical
 // chunk c ^ s(r) with s(r) = 2*(r % 8) + (r / 8) (the loader picks the global
 // chunk per lane to make it so), and the four lane groups of a K step read
 // chunks 0, 2, 1, 3 of the step: lanes l and l + 32, which the LDS serves
 // together, then read chunks an odd XOR apart and every read is bank-conflict
-// free (lanes that re-read a row read the same address, a broadcast).
+// free (lanes that re-read a row read the same address, a broadcast; rows
+// of 512 bytes or 1 KiB both start at bank 0, so the argument holds for
+// either K tile).  With the grid's y dimension above 1, workgroup (x, y)
+// stages Q rows [16y, 16y + 16) (the small-side split).
 //
 // With SPLIT, K is split across workgroups as well: the grid holds `splits`
 // workgroups per block of PR rows (row-block major, so that workgroups side
@@ -128,17 +133,21 @@ gemm_skinny_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ 
 // 16 P rows, instead of fewer P rows per workgroup, keep the number of times
 // Q is read from the caches at ceil(R / 16).
 template <int WAVES, int STAGES, int QROWS, bool TRANS, int DT = kF16, int PR = 16, int KROT = 0, bool NTP = false,
-          bool SPLIT = false>
+          bool SPLIT = false, int BK = 512>
 __global__ void __launch_bounds__(WAVES * 64)
 gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ Q, _Float16 *__restrict__ D,
                        int R, int S, int K, float *__restrict__ ws, int splits) {
-  constexpr int BK = 512;
-  constexpr int kRowBytes = BK * 2;                              // 1 KiB: one wave instruction
-  constexpr int kLoads = PR + QROWS;                             // row loads per stage
-  constexpr int kDmaPerWave = (kLoads + WAVES - 1) / WAVES;      // per wave per stage
-  constexpr bool kJunk = kDmaPerWave * WAVES > kLoads;           // spare slots -> junk row kLoads
+  static_assert(BK == 512 || BK == 256, "K tile");
+  constexpr int kRowBytes = BK * 2;                              // one row of a stage
+  constexpr int kChunks = BK / 8;                                // 16-byte chunks per row
+  constexpr int kRowsPerLoad = 1024 / kRowBytes;                 // rows per 1 KiB wave instruction
+  constexpr int kLoads = PR + QROWS;                             // rows per stage
+  constexpr int kInstr = (kLoads + kRowsPerLoad - 1) / kRowsPerLoad;  // wave instructions per stage
+  constexpr int kDmaPerWave = (kInstr + WAVES - 1) / WAVES;      // per wave per stage
+  constexpr bool kJunk = kDmaPerWave * WAVES > kInstr;           // spare slots -> junk KiB kInstr
   constexpr int kTileBytes = PR * kRowBytes;                     // the P rows, then the Q rows
-  constexpr int kStageBytes = (kLoads + (kJunk ? 1 : 0)) * kRowBytes;
+  constexpr int kStageBytes = (kInstr + (kJunk ? 1 : 0)) * 1024;
+  static_assert(PR % kRowsPerLoad == 0, "an instruction's rows belong to one operand");
   constexpr int kSteps = BK / 32;                                // 32-wide K steps per stage
   constexpr int kStepsPerWave = kSteps / WAVES;
   static_assert(QROWS == 8 || QROWS == 16 || QROWS == 32 || QROWS == 64, "Q tile rows");
@@ -192,26 +201,31 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   static_assert(KROT >= 0 && KROT <= 2, "K start rotation mode");
   auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
 
-  // Row loads of K tile kt: load d of this wave moves stage row
-  // t = d*WAVES + wave (P rows 0..PR-1, then Q rows 0..QROWS-1; t >= kLoads
-  // loads zeros into the junk row).
+  // Row loads of K tile kt: load d of this wave is the stage's 1 KiB
+  // instruction t = d*WAVES + wave, which moves stage rows
+  // t*kRowsPerLoad .. +kRowsPerLoad-1 (P rows 0..PR-1, then Q rows
+  // 0..QROWS-1; rows past kLoads, and instructions t >= kInstr into the junk
+  // KiB, load zeros).
   auto issue = [&](int kt) {
     const uint32_t stage = ring0 + static_cast<uint32_t>((kt % STAGES) * kStageBytes);
     const int ktile = kbeg + (kt + kt0 < nkt ? kt + kt0 : kt + kt0 - nkt);  // the K tile this ring slot holds
 #pragma unroll
     for (int d = 0; d < kDmaPerWave; ++d) {
       const int t = d * WAVES + wave;
-      const bool junk = kJunk && t >= kLoads;
-      const int row = t < PR ? t : t - PR;  // row within its operand
-      const int k = ktile * BK + ((lane ^ swz(row & 15)) << 3);  // first K element this lane fetches
-      const uint32_t off = (k < K && !junk) ? static_cast<uint32_t>(row) * K * 2u + static_cast<uint32_t>(k) * 2u
-                                            : kOobOffset;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + static_cast<uint32_t>(min(t, kLoads) * kRowBytes));
+      const bool junk = kJunk && t >= kInstr;
+      const int t0 = t * kRowsPerLoad;                        // the instruction's first stage row
+      const int tr = t0 + (kRowsPerLoad > 1 ? lane / kChunks : 0);  // this lane's stage row
+      const int row = tr < PR ? tr : tr - PR;                 // row within its operand
+      const int k = ktile * BK + (((lane % kChunks) ^ swz(row & 15)) << 3);  // first K element this lane fetches
+      const uint32_t off = (k < K && !junk && tr < kLoads)
+                               ? static_cast<uint32_t>(row) * K * 2u + static_cast<uint32_t>(k) * 2u
+                               : kOobOffset;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + static_cast<uint32_t>(min(t, kInstr) * 1024));
       // With NTP the rows of P, read once, are loaded non-temporally.
-      if (NTP && t < PR)
+      if (NTP && t0 < PR)
         lds_dma_b128<2>(rsrc_p, off, dst);
       else
-        lds_dma_b128(t < PR ? rsrc_p : rsrc_q, off, dst);
+        lds_dma_b128(t0 < PR ? rsrc_p : rsrc_q, off, dst);
     }
   };
 
@@ -297,7 +311,8 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
 
 // ceil(R / PR) workgroups along x; with qblocks > 1 the small side is split
 // into blocks of QROWS rows along y.
-template <int WAVES, int STAGES, int QROWS, int DT = kF16, int PR = 16, int KROT = 0, bool NTP = false>
+template <int WAVES, int STAGES, int QROWS, int DT = kF16, int PR = 16, int KROT = 0, bool NTP = false,
+          int BK = 512>
 static hipError_t launch_lds(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                              hipStream_t stream, int qblocks = 1) {
   const dim3 grid(static_cast<unsigned>((R + PR - 1) / PR), static_cast<unsigned>(qblocks));
@@ -306,10 +321,10 @@ static hipError_t launch_lds(const void *P, const void *Q, void *D, int R, int S
   auto *d = static_cast<_Float16 *>(D);
   float *no_ws = nullptr;
   if (trans)
-    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, true, DT, PR, KROT, NTP>), grid, dim3(WAVES * 64),
-                       0, stream, p, q, d, R, S, K, no_ws, 1);
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, true, DT, PR, KROT, NTP, false, BK>), grid,
+                       dim3(WAVES * 64), 0, stream, p, q, d, R, S, K, no_ws, 1);
   else
-    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, false, DT, PR, KROT, NTP>), grid,
+    hipLaunchKernelGGL((gemm_skinny_lds_kernel<WAVES, STAGES, QROWS, false, DT, PR, KROT, NTP, false, BK>), grid,
                        dim3(WAVES * 64), 0, stream, p, q, d, R, S, K, no_ws, 1);
   return hipGetLastError();
 }
@@ -369,25 +384,35 @@ static hipError_t launch_lds_qsplit(const void *P, const void *Q, void *D, int R
   }
 }
 
-// The default launch (skinny_default_rows): 16 P rows per workgroup with 16
-// waves and a 4-stage ring while R gives every CU such a workgroup, with
-// non-temporal P loads from K = kSkinnyStreamMinK up (cached below); else 8,
-// 4, 2 or 1 P rows, staging 8 Q rows when S <= 8 (and loading P
-// non-temporally at 8 rows with 8 Q rows; at fewer rows that measured
-// slower).  Launches of 16 or 8 P rows start each workgroup's K walk at its
-// index within its XCD (KROT 2, kSkinnyRotateXcd): without it, rows whose
-// length is a multiple of 8 KiB (K % 4096 == 0) read 17-22 % slower, as
-// every workgroup sharing an L2 then reads the same offset of its rows at
-// once.  With 17..32 staged Q rows the rotation is taken only for such rows
-// (elsewhere it measured 5 % slower); with 4 or fewer P rows never (4-10 %
-// slower: every workgroup re-reads the same Q lines, best all at once).
-// 17..64 small-side rows against few P rows take the small-side split
-// (skinny_qsplit).
+// The default launch (skinny_default_rows): 32 P rows per workgroup in K
+// tiles of 256 while R gives every CU 32 rows; else 16 P rows with 16 waves
+// and a 4-stage ring, with non-temporal P loads from K = kSkinnyStreamMinK
+// up (cached below); else 8, 4, 2 or 1 P rows, staging 8 Q rows when S <= 8
+// (and loading P non-temporally at 8 rows with 8 Q rows; at fewer rows that
+// measured slower).  Launches of 32, 16 or 8 P rows start each workgroup's
+// K walk at its index within its XCD (KROT 2, kSkinnyRotateXcd): without
+// it, rows whose length is a multiple of 8 KiB (K % 4096 == 0) read 17-22 %
+// slower, as every workgroup sharing an L2 then reads the same offset of
+// its rows at once.  With 17..32 staged Q rows at 16 P rows the rotation is
+// taken only for such rows (elsewhere it measured 5 % slower); with 4 or
+// fewer P rows never (4-10 % slower: every workgroup re-reads the same Q
+// lines, best all at once).  17..64 small-side rows against few P rows take
+// the small-side split (skinny_qsplit).
 template <int DT>
 static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, int S, int K, bool trans,
                                   int num_cus, hipStream_t stream) {
   if (skinny_qsplit(R, S, num_cus)) return launch_lds_qsplit<DT>(P, Q, D, R, S, K, trans, num_cus, stream);
-  const int pr = skinny_launch_rows(R, S, num_cus);
+  const int pr = skinny_default_rows(R, num_cus);
+  if (pr == 32) {
+    // 32 P rows per workgroup (two 16-row MFMA blocks) in K tiles of 256
+    // (512-byte rows, two to a load instruction), so the ring holds 3 or 4
+    // stages of (32 + Q rows) x 512 bytes: each workgroup reads the staged
+    // Q rows once per 32 P rows.
+    if (S > 32) return launch_lds<8, 3, 64, DT, 32, kSkinnyRotateXcd, true, 256>(P, Q, D, R, S, K, trans, stream);
+    if (S > kSkinnyMaxRows)
+      return launch_lds<4, 4, 32, DT, 32, kSkinnyRotateXcd, true, 256>(P, Q, D, R, S, K, trans, stream);
+    return launch_lds<8, 4, 16, DT, 32, kSkinnyRotateXcd, true, 256>(P, Q, D, R, S, K, trans, stream);
+  }
   if (S > 32) {
     // 33..64 small-side rows at 16 or 8 P rows per workgroup (fewer take the
     // split): 64 staged Q rows, 8 waves (1-4 % ahead of 4, 16 waves 5-17 %
@@ -397,14 +422,10 @@ static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, 
                     : launch_lds<8, 2, 64, DT, 8, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream);
   }
   if (S > kSkinnyMaxRows) {
-    // 17..32 small-side rows at 32 or 16 P rows per workgroup (fewer take
-    // the split): 32 staged Q rows, 4 waves; two 16-row P blocks with
-    // (32 + 32) KiB stages in a 2-stage ring, or one in a 3-stage ring of
-    // (16 + 32) KiB stages.
+    // 17..32 small-side rows at 16 P rows per workgroup (fewer take the
+    // split): 32 staged Q rows, 4 waves, a 3-stage ring of (16 + 32) KiB
+    // stages.
     const bool rot = K % 4096 == 0;
-    if (pr == 32)
-      return rot ? launch_lds<4, 2, 32, DT, 32, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
-                 : launch_lds<4, 2, 32, DT, 32, 0, true>(P, Q, D, R, S, K, trans, stream);
     return rot ? launch_lds<4, 3, 32, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
                : launch_lds<4, 3, 32, DT, 16, 0, true>(P, Q, D, R, S, K, trans, stream);
   }

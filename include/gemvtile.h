@@ -69,17 +69,14 @@ enum gemvtile_status {
  * 256x128, 128x256 or 128x128 ones when the output has too few 256x256
  * tiles to keep every compute unit busy (gemvtile_gemm_tile gives the choice);
  * it writes D with non-temporal stores, so D is not left in the caches.
- * When M <= 16 or N <= 16, or the smaller side has 17..64 rows and the
- * tiled kernel's 128x128 tiles along the larger side would leave more than
- * half the compute units idle (three quarters above 32 rows) -- a decode
- * batch against a weight matrix --, the call runs a bandwidth-bound kernel
- * that streams the larger operand once instead of the tiled one (with fewer
- * rows of it per workgroup when it has too few rows to give every compute
- * unit 16, and 32 when the smaller side has 17..32 rows and the larger one
- * enough to give every compute unit 32 in whole waves; with 17..64 rows on
- * the smaller side and few on the larger, the smaller side is split into
- * 16-row blocks over the workgroups instead), and when M == 1 or N == 1 the GEMV kernel of gemv_f16; results
- * are deterministic either way.
+ * When the smaller side has at most 64 rows -- a decode batch against a
+ * weight matrix --, the call runs a bandwidth-bound kernel that streams the
+ * larger operand once instead of the tiled one (32 rows of it per
+ * workgroup when it gives every compute unit 32, else 16, 8, 4, 2 or 1;
+ * with 17..64 rows on the smaller side and few on the larger, the smaller
+ * side is split into 16-row blocks over the workgroups instead), and when
+ * M == 1 or N == 1 the GEMV kernel of gemv_f16; results are deterministic
+ * either way.
  * Returns a gemvtile_status.
  */
 int gemm_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, void *stream);
@@ -310,19 +307,16 @@ int64_t gemvtile_gemv_grid(int64_t N, int64_t K, int64_t num_cus);
 /*
  * gemvtile_gemm_grid -- the number of workgroups gemm_f16 launches for an
  * M x N x K product on a device with `num_cus` compute units: the GEMV grid
- * of the other side's rows when M or N is 1; when M <= 16 or N <= 16, or the
- * smaller side has 17..64 rows and gemm_f16 picks the skinny kernel (see
- * there), ceil(R/p) with R = N if
- * M <= 16, else M if N <= 16, else the larger side, and p the largest of
- * 16, 8, 4, 2 rows per workgroup such that R >= p*num_cus, else p = 1;
- * except that p = 32 when the smaller side S has 17..32 rows, R >= 32*num_cus
- * and ceil(ceil(R/32)/num_cus)*32 <= ceil(ceil(R/16)/num_cus)*16 (no compute
- * unit gets more rows than with p = 16); and, when S has 17..64 rows and
- * that p is below 8 (or 8 with S <= 32), ceil(S/16)*ceil(R/q) with q the
- * largest of 16, 8, 4, 2 such that ceil(S/16)*ceil(R/q) >= num_cus, else
- * q = 1 (the smaller side split into 16-row blocks); otherwise the
- * persistent grid min(#tiles, num_cus) over the tiles gemvtile_gemm_tile
- * picks.  Host-only arithmetic; returns 0 for empty outputs.
+ * of the other side's rows when M or N is 1; when the smaller side has at
+ * most 64 rows (the skinny kernel), ceil(R/p) with R = N if M <= 16, else M
+ * if N <= 16, else the larger side, and p the largest of 32, 16, 8, 4, 2
+ * rows per workgroup such that R >= p*num_cus, else p = 1; except that,
+ * when the smaller side S has 17..64 rows and that p is below 8 (or 8 with
+ * S <= 32), ceil(S/16)*ceil(R/q) with q the largest of 16, 8, 4, 2 such
+ * that ceil(S/16)*ceil(R/q) >= num_cus, else q = 1 (the smaller side split
+ * into 16-row blocks); otherwise the persistent grid min(#tiles, num_cus)
+ * over the tiles gemvtile_gemm_tile picks.  Host-only arithmetic; returns 0
+ * for empty outputs.
  */
 int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
 

@@ -90,10 +90,12 @@ def test_gemm_argument_validation(lib):
     for bad in (-1, 4, 9, 11, 12, 15, 19, 29, 32, 36, 99, 101, 113, 131, 140, 148, 149, 153, 199, 202, 1000):
         assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, bad) == INVALID, bad
     # skinny launch shapes only apply when one side has at most 16 rows (at
-    # most 64 for the small-side split, 160)
-    for v in (100, 104, 112, 130, 147, 152):
+    # most 64 for gemm_f16's own skinny launch, 100, and the small-side
+    # split, 160)
+    for v in (104, 112, 130, 147, 152):
         assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 32, 32, 8, None, v) == UNSUPPORTED, v
-    assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 65, 65, 8, None, 160) == UNSUPPORTED
+    for v in (100, 160):
+        assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 65, 65, 8, None, v) == UNSUPPORTED, v
 
 
 def test_gemm_bias_argument_validation(lib):
@@ -215,11 +217,12 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(256, 256, 4096, 256) == 4  # four 128x128 tiles (see the tile rule below)
     assert gt.gemm_grid(4000, 4032, 4096, 256) == 256
     assert gt.gemm_grid(0, 4, 4096, 256) == 0
-    # skinny shapes: one workgroup per 16 rows of the larger side while that
-    # gives every CU one, else per 8, 4, 2 or 1 rows
+    # skinny shapes: one workgroup per 32 rows of the larger side while that
+    # gives every CU one, else per 16, 8, 4, 2 or 1 rows
     assert gt.gemm_grid(8, 4096, 4096, 256) == 256
     assert gt.gemm_grid(4096, 16, 4096, 256) == 256
-    assert gt.gemm_grid(8, 8192, 4096, 256) == 512
+    assert gt.gemm_grid(8, 8192, 4096, 256) == 256  # 32 rows per workgroup
+    assert gt.gemm_grid(8, 8191, 4096, 256) == 512  # 16 rows per workgroup
     assert gt.gemm_grid(8, 3000, 4096, 256) == 375
     assert gt.gemm_grid(8, 2000, 4096, 256) == 500
     assert gt.gemm_grid(1000, 9, 4096, 256) == 500
@@ -240,22 +243,20 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(50, 2100, 4096, 256) == 263  # staged, 8 rows per workgroup
     assert gt.gemm_grid(64, 4097, 4096, 256) == 257
     assert gt.gemm_grid(65, 4097, 4096, 256) == 33  # 1 x 33 tiles of 128x128
-    # ... while the 128x128 tiles along the larger side would leave more than
-    # half (up to 32 rows) or three quarters (33..64) of the CUs idle
-    assert gt.gemm_grid(32, 16384, 4096, 256) == 512  # 128 tiles: skinny, 32 rows per workgroup
-    # 17..32 small-side rows take 32 large-side rows per workgroup from
-    # 32 * CUs rows up while no CU gets more rows than with 16 per
-    # workgroup; 64 small-side rows stay at 16
+    # ... whatever the larger side
+    assert gt.gemm_grid(32, 16384, 4096, 256) == 512  # 32 rows per workgroup
     assert gt.gemm_grid(24, 8192, 4096, 256) == 256
     assert gt.gemm_grid(24, 16384, 4096, 256) == 512
-    assert gt.gemm_grid(20, 12288, 4096, 256) == 768  # 1.5 waves of 32-row workgroups: 16 rows
-    assert gt.gemm_grid(20, 12289, 4096, 256) == 385  # 49 rows per CU either way: 32 rows
+    assert gt.gemm_grid(20, 12288, 4096, 256) == 384  # 1.5 waves of 32-row workgroups
+    assert gt.gemm_grid(20, 12289, 4096, 256) == 385
     assert gt.gemm_grid(8191, 17, 4096, 256) == 512
-    assert gt.gemm_grid(33, 8192, 4096, 256) == 512
-    assert gt.gemm_grid(16, 8192, 4096, 256) == 512
-    assert gt.gemm_grid(32, 16385, 4096, 256) == 129  # 129 tiles: tiled
-    assert gt.gemm_grid(64, 8192, 4096, 256) == 512  # 64 tiles: skinny
-    assert gt.gemm_grid(14336, 64, 4096, 256) == 112  # 112 tiles: tiled
+    assert gt.gemm_grid(33, 8192, 4096, 256) == 256
+    assert gt.gemm_grid(16, 8192, 4096, 256) == 256
+    assert gt.gemm_grid(32, 16385, 4096, 256) == 513
+    assert gt.gemm_grid(64, 8192, 4096, 256) == 256
+    assert gt.gemm_grid(14336, 64, 4096, 256) == 448
+    assert gt.gemm_grid(65536, 64, 4096, 256) == 2048
+    assert gt.gemm_grid(65536, 65, 4096, 256) == 256  # tiled
     # one row on a side: the GEMV grid of the other side
     assert gt.gemm_grid(1, 4096, 4096, 256) == gt.gemv_grid(4096, 4096, 256) == 256
     assert gt.gemm_grid(1000, 1, 4096, 256) == gt.gemv_grid(1000, 4096, 256)

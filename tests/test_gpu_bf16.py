@@ -108,6 +108,8 @@ SHAPES = [
     (24, 1500, 4104),
     (48, 1500, 1032),
     (1000, 50, 2056),
+    (8200, 40, 1032),
+    (16, 8192, 2056),
     (48, 4096, 4104),
     # 32 large-side rows per workgroup
     (20, 8192, 4096),

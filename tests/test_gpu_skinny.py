@@ -121,15 +121,25 @@ SHAPES = [
     (24, 4096, 8192),
     (2500, 20, 4096),
     (48, 2600, 4104),
-    # 17..32 staged rows with 32 large-side rows per workgroup (two 16-row
-    # MFMA blocks of the large side), from 32 rows per CU up: rotated and
-    # unrotated K starts, ragged large side and K, the transposed store;
-    # and past 32 rows per CU where 16-row workgroups fill whole waves
+    # 32 large-side rows per workgroup (two 16-row MFMA blocks) in K tiles
+    # of 256, from 32 rows per CU up: 16, 32 and 64 staged small-side rows,
+    # ragged large side, ragged K (a last K tile of 8 or 16 elements, or one
+    # tile and a tail), the transposed store, 1.5 waves of workgroups
     (24, 8192, 4096),
     (32, 12300, 4104),
     (12300, 17, 1032),
     (8210, 17, 1032),
     (20, 12288, 4096),
+    (8, 8200, 4104),
+    (8210, 12, 1032),
+    (3, 8192, 264),
+    (64, 8200, 2056),
+    (8300, 40, 1032),
+    (33, 8192, 4096),
+    # 17..64 small-side rows against more large-side rows than 128x128
+    # tiles would need to fill the CUs (the skinny kernel whatever R)
+    (24, 16500, 1032),
+    (20000, 40, 520),
 ]
 
 
