@@ -180,14 +180,29 @@ constexpr int kSkinnyStreamMinK = 8192;
 constexpr int kSkinnyRotateXcd = 2;
 
 // P rows per workgroup of the default skinny launch for R rows of the large
-// operand: the largest of 32, 16, 8, 4, 2 with R >= rows * num_cus, else 1.
-// 32 rows go in K tiles of 256 (so that a ring of 3 or 4 stages still fits
-// the LDS), and each workgroup then stages the small side once per 32 P
-// rows instead of 16: 64x8192x8192 40.4 -> 28.6 us, 24x8192x4096 16.0 ->
-// 12.5 us, 16x8192x8192 24.4 -> 21.6 us, also at 1.5 waves of workgroups
-// (20x12288x8192 43.3 -> 38.1 us).
+// operand.  From 32 rows per CU up: 32, 48 or 64, whichever gives a CU the
+// fewest rows over whole rounds of workgroups (ties to the larger: fewer
+// re-reads of the small side), in K tiles of 256 (32 rows) or 128 (48, 64)
+// so that a ring of 3 or 4 stages still fits the LDS; each workgroup then
+// stages the small side once per 32-64 P rows instead of 16 (64x8192x8192
+// 40.4 -> 27.7 us, 24x8192x4096 16.0 -> 12.4 us, 16x8192x8192 24.4 -> 21.8
+// us; 64x12288x14336 at 48 rows 98.3 -> 71.9 us, 64x16384x4096 at 64 rows
+// 30.0 -> 25.9 us).  Below that, the largest of 16, 8, 4, 2 with
+// R >= rows * num_cus, else 1.
 inline int skinny_default_rows(int64_t R, int num_cus) {
-  for (int rows = 32; rows > 1; rows >>= 1)
+  if (R >= int64_t{32} * num_cus) {
+    int best = 32;
+    int64_t best_rows = ((R + 31) / 32 + num_cus - 1) / num_cus * 32;
+    for (int rows = 48; rows <= 64; rows += 16) {
+      const int64_t per_cu = ((R + rows - 1) / rows + num_cus - 1) / num_cus * rows;
+      if (per_cu <= best_rows) {
+        best = rows;
+        best_rows = per_cu;
+      }
+    }
+    return best;
+  }
+  for (int rows = 16; rows > 1; rows >>= 1)
     if (R >= static_cast<int64_t>(rows) * num_cus) return rows;
   return 1;
 }

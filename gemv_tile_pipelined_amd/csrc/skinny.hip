@@ -96,11 +96,12 @@ gemm_skinny_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ 
 }
 
 // LDS-staged variant: both operands go through a STAGES-deep LDS ring of K
-// tiles of BK = 512 (1 KiB per row) or 256 (512 bytes per row), filled by
-// direct-to-LDS loads in which one wave instruction moves 1 KiB: one row
-// segment, or two at BK = 256 (the register variant above touches 16 rows x
+// tiles of BK = 512 (1 KiB per row), 256 or 128, filled by direct-to-LDS
+// loads in which one wave instruction moves 1 KiB: one row segment, or two
+// at BK = 256 (the register variant above touches 16 rows x
 // 64 bytes per instruction, and every workgroup re-reads the small operand
-// that way).  A workgroup owns PR rows of P (32 at BK = 256 or 16 by default;
+// that way), or four at BK = 128.  A workgroup owns PR rows of P (48 or 64
+// at BK = 128, 32 at BK = 256 or 16 by default;
 // 8, 4, 2 or 1 when R is too small to give every CU a workgroup of 16 -- the
 // page's "enough blocks" again, here without splitting K, since every
 // workgroup re-reading the small Q costs only cache traffic).
@@ -112,8 +113,8 @@ gemm_skinny_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ 
 // instructions of a stage's PR + QROWS rows are spread over the waves;
 // spare slots load zeros (out-of-range offset, no memory access) into a
 // junk KiB so every wave issues the same number of loads and the vmcnt
-// accounting stays uniform.  With PR = 32 the P rows form two 16-row MFMA
-// blocks.  Each wave computes
+// accounting stays uniform.  With PR = 32, 48 or 64 the P rows form two,
+// three or four 16-row MFMA blocks.  Each wave computes
 // BK/32/WAVES of the stage's K steps.  LDS chunk c of row r holds logical
 // chunk c ^ s(r) with s(r) = 2*(r % 8) + (r / 8) (the loader picks the global
 // chunk per lane to make it so), and the four lane groups of a K step read
@@ -137,7 +138,7 @@ template <int WAVES, int STAGES, int QROWS, bool TRANS, int DT = kF16, int PR = 
 __global__ void __launch_bounds__(WAVES * 64)
 gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restrict__ Q, _Float16 *__restrict__ D,
                        int R, int S, int K, float *__restrict__ ws, int splits) {
-  static_assert(BK == 512 || BK == 256, "K tile");
+  static_assert(BK == 512 || BK == 256 || BK == 128, "K tile");
   constexpr int kRowBytes = BK * 2;                              // one row of a stage
   constexpr int kChunks = BK / 8;                                // 16-byte chunks per row
   constexpr int kRowsPerLoad = 1024 / kRowBytes;                 // rows per 1 KiB wave instruction
@@ -158,7 +159,8 @@ gemm_skinny_lds_kernel(const _Float16 *__restrict__ P, const _Float16 *__restric
   // sums then reuse the ring once the K loop is done with it.
   constexpr bool kAliasPartial = QROWS == 64;
   constexpr int kPartialBytes = WAVES * 16 * QB * (kPRows + 1) * 4;
-  static_assert(PR == 1 || PR == 2 || PR == 4 || PR == 8 || PR == 16 || PR == 32, "P rows per workgroup");
+  static_assert(PR == 1 || PR == 2 || PR == 4 || PR == 8 || PR == 16 || PR == 32 || PR == 48 || PR == 64,
+                "P rows per workgroup");
   static_assert(kSteps % WAVES == 0, "work split");
   static_assert(STAGES >= 2 && (STAGES - 1) * kDmaPerWave <= 63, "vmcnt range");
   static_assert(STAGES * kStageBytes + (kAliasPartial ? 0 : kPartialBytes) <= 160 * 1024,
@@ -384,8 +386,9 @@ static hipError_t launch_lds_qsplit(const void *P, const void *Q, void *D, int R
   }
 }
 
-// The default launch (skinny_default_rows): 32 P rows per workgroup in K
-// tiles of 256 while R gives every CU 32 rows; else 16 P rows with 16 waves
+// The default launch (skinny_default_rows): 32, 48 or 64 P rows per
+// workgroup, in K tiles of 256 or 128, while R gives every CU 32 rows; else
+// 16 P rows with 16 waves
 // and a 4-stage ring, with non-temporal P loads from K = kSkinnyStreamMinK
 // up (cached below); else 8, 4, 2 or 1 P rows, staging 8 Q rows when S <= 8
 // (and loading P non-temporally at 8 rows with 8 Q rows; at fewer rows that
@@ -403,6 +406,19 @@ static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, 
                                   int num_cus, hipStream_t stream) {
   if (skinny_qsplit(R, S, num_cus)) return launch_lds_qsplit<DT>(P, Q, D, R, S, K, trans, num_cus, stream);
   const int pr = skinny_default_rows(R, num_cus);
+  if (pr > 32) {
+    // 48 or 64 P rows (three or four 16-row MFMA blocks) in K tiles of 128
+    // (256-byte rows, four to a load instruction), 4 waves, a 4-stage ring of
+    // (PR + Q rows) x 256 bytes.
+    if (S > 32)
+      return pr == 48 ? launch_lds<4, 4, 64, DT, 48, kSkinnyRotateXcd, true, 128>(P, Q, D, R, S, K, trans, stream)
+                      : launch_lds<4, 4, 64, DT, 64, kSkinnyRotateXcd, true, 128>(P, Q, D, R, S, K, trans, stream);
+    if (S > kSkinnyMaxRows)
+      return pr == 48 ? launch_lds<4, 4, 32, DT, 48, kSkinnyRotateXcd, true, 128>(P, Q, D, R, S, K, trans, stream)
+                      : launch_lds<4, 4, 32, DT, 64, kSkinnyRotateXcd, true, 128>(P, Q, D, R, S, K, trans, stream);
+    return pr == 48 ? launch_lds<4, 4, 16, DT, 48, kSkinnyRotateXcd, true, 128>(P, Q, D, R, S, K, trans, stream)
+                    : launch_lds<4, 4, 16, DT, 64, kSkinnyRotateXcd, true, 128>(P, Q, D, R, S, K, trans, stream);
+  }
   if (pr == 32) {
     // 32 P rows per workgroup (two 16-row MFMA blocks) in K tiles of 256
     // (512-byte rows, two to a load instruction), so the ring holds 3 or 4

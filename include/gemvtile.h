@@ -71,7 +71,7 @@ enum gemvtile_status {
  * it writes D with non-temporal stores, so D is not left in the caches.
  * When the smaller side has at most 64 rows -- a decode batch against a
  * weight matrix --, the call runs a bandwidth-bound kernel that streams the
- * larger operand once instead of the tiled one (32 rows of it per
+ * larger operand once instead of the tiled one (32, 48 or 64 rows of it per
  * workgroup when it gives every compute unit 32, else 16, 8, 4, 2 or 1;
  * with 17..64 rows on the smaller side and few on the larger, the smaller
  * side is split into 16-row blocks over the workgroups instead), and when
@@ -309,8 +309,10 @@ int64_t gemvtile_gemv_grid(int64_t N, int64_t K, int64_t num_cus);
  * M x N x K product on a device with `num_cus` compute units: the GEMV grid
  * of the other side's rows when M or N is 1; when the smaller side has at
  * most 64 rows (the skinny kernel), ceil(R/p) with R = N if M <= 16, else M
- * if N <= 16, else the larger side, and p the largest of 32, 16, 8, 4, 2
- * rows per workgroup such that R >= p*num_cus, else p = 1; except that,
+ * if N <= 16, else the larger side, and p rows per workgroup: when
+ * R >= 32*num_cus, the one of 32, 48, 64 with the least
+ * ceil(ceil(R/p)/num_cus)*p (ties to the larger), else the largest of 16,
+ * 8, 4, 2 such that R >= p*num_cus, else 1; except that,
  * when the smaller side S has 17..64 rows and that p is below 8 (or 8 with
  * S <= 32), ceil(S/16)*ceil(R/q) with q the largest of 16, 8, 4, 2 such
  * that ceil(S/16)*ceil(R/q) >= num_cus, else q = 1 (the smaller side split

@@ -217,12 +217,16 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(256, 256, 4096, 256) == 4  # four 128x128 tiles (see the tile rule below)
     assert gt.gemm_grid(4000, 4032, 4096, 256) == 256
     assert gt.gemm_grid(0, 4, 4096, 256) == 0
-    # skinny shapes: one workgroup per 32 rows of the larger side while that
-    # gives every CU one, else per 16, 8, 4, 2 or 1 rows
+    # skinny shapes: from 32 rows of the larger side per CU, one workgroup
+    # per 32, 48 or 64 rows (the fewest rows per CU over whole rounds of
+    # workgroups, ties to the larger), else per 16, 8, 4, 2 or 1 rows
     assert gt.gemm_grid(8, 4096, 4096, 256) == 256
     assert gt.gemm_grid(4096, 16, 4096, 256) == 256
     assert gt.gemm_grid(8, 8192, 4096, 256) == 256  # 32 rows per workgroup
     assert gt.gemm_grid(8, 8191, 4096, 256) == 512  # 16 rows per workgroup
+    assert gt.gemm_grid(8, 10300, 4096, 256) == 215  # 48 rows: one round
+    assert gt.gemm_grid(64, 14400, 4096, 256) == 225  # 64 rows: one round
+    assert gt.gemm_grid(16400, 40, 4096, 256) == 342  # 48 rows: 96 per CU, as with 32
     assert gt.gemm_grid(8, 3000, 4096, 256) == 375
     assert gt.gemm_grid(8, 2000, 4096, 256) == 500
     assert gt.gemm_grid(1000, 9, 4096, 256) == 500
@@ -244,18 +248,18 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(64, 4097, 4096, 256) == 257
     assert gt.gemm_grid(65, 4097, 4096, 256) == 33  # 1 x 33 tiles of 128x128
     # ... whatever the larger side
-    assert gt.gemm_grid(32, 16384, 4096, 256) == 512  # 32 rows per workgroup
+    assert gt.gemm_grid(32, 16384, 4096, 256) == 256  # 64 rows per workgroup
     assert gt.gemm_grid(24, 8192, 4096, 256) == 256
-    assert gt.gemm_grid(24, 16384, 4096, 256) == 512
-    assert gt.gemm_grid(20, 12288, 4096, 256) == 384  # 1.5 waves of 32-row workgroups
-    assert gt.gemm_grid(20, 12289, 4096, 256) == 385
+    assert gt.gemm_grid(24, 16384, 4096, 256) == 256
+    assert gt.gemm_grid(20, 12288, 4096, 256) == 256  # 48 rows per workgroup
+    assert gt.gemm_grid(20, 12289, 4096, 256) == 193  # 64 rows: 64 per CU, as with 32
     assert gt.gemm_grid(8191, 17, 4096, 256) == 512
     assert gt.gemm_grid(33, 8192, 4096, 256) == 256
     assert gt.gemm_grid(16, 8192, 4096, 256) == 256
-    assert gt.gemm_grid(32, 16385, 4096, 256) == 513
+    assert gt.gemm_grid(32, 16385, 4096, 256) == 342
     assert gt.gemm_grid(64, 8192, 4096, 256) == 256
-    assert gt.gemm_grid(14336, 64, 4096, 256) == 448
-    assert gt.gemm_grid(65536, 64, 4096, 256) == 2048
+    assert gt.gemm_grid(14336, 64, 4096, 256) == 224
+    assert gt.gemm_grid(65536, 64, 4096, 256) == 1024
     assert gt.gemm_grid(65536, 65, 4096, 256) == 256  # tiled
     # one row on a side: the GEMV grid of the other side
     assert gt.gemm_grid(1, 4096, 4096, 256) == gt.gemv_grid(4096, 4096, 256) == 256

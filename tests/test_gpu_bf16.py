@@ -110,6 +110,8 @@ SHAPES = [
     (1000, 50, 2056),
     (8200, 40, 1032),
     (16, 8192, 2056),
+    (10300, 40, 1032),
+    (64, 16384, 264),
     (48, 4096, 4104),
     # 32 large-side rows per workgroup
     (20, 8192, 4096),

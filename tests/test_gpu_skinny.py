@@ -136,6 +136,15 @@ SHAPES = [
     (64, 8200, 2056),
     (8300, 40, 1032),
     (33, 8192, 4096),
+    # 48 and 64 large-side rows per workgroup (three or four MFMA blocks) in
+    # K tiles of 128, with 16, 32 and 64 staged rows, ragged large side and
+    # K, the transposed store
+    (8, 10300, 1032),
+    (10300, 20, 2056),
+    (64, 14400, 520),
+    (16400, 40, 1032),
+    (16384, 30, 136),
+    (12, 16390, 4104),
     # 17..64 small-side rows against more large-side rows than 128x128
     # tiles would need to fill the CUs (the skinny kernel whatever R)
     (24, 16500, 1032),
