@@ -463,9 +463,9 @@ def ring_trace(variant: int, ktu: int):
     (host-only): (events, info) with events a list of (name, a, b, c, d)
     tuples as gemvtile_ring_trace describes, info = {"loads_per_tile",
     "reads_per_step", "ksteps", "mfma_per_step", "stages", "bm", "bn",
-    "early_free"}."""
+    "early_free", "waves_m", "waves_n"}."""
     lib = load_library()
-    info = (ctypes.c_int * 8)()
+    info = (ctypes.c_int * 10)()
     n = int(lib.gemvtile_ring_trace(variant, ktu, None, 0, info))
     if n < 0:
         raise GemvTileError(1, f"tiled variant {variant} has no multi-stage ring, or ktu is out of range")
@@ -473,7 +473,8 @@ def ring_trace(variant: int, ktu: int):
     n2 = int(lib.gemvtile_ring_trace(variant, ktu, buf, n, info))
     assert n2 == n
     events = [(RING_EVENTS[buf[5 * i]], buf[5 * i + 1], buf[5 * i + 2], buf[5 * i + 3], buf[5 * i + 4]) for i in range(n)]
-    keys = ("loads_per_tile", "reads_per_step", "ksteps", "mfma_per_step", "stages", "bm", "bn", "early_free")
+    keys = ("loads_per_tile", "reads_per_step", "ksteps", "mfma_per_step", "stages", "bm", "bn", "early_free",
+            "waves_m", "waves_n")
     return events, dict(zip(keys, list(info)))
 
 

@@ -279,6 +279,8 @@ int64_t ring_trace(int variant, int ktu, int32_t *events, int64_t cap, int *info
     info[5] = S::BM;
     info[6] = S::BN;
     info[7] = S::EARLY_FREE ? 1 : 0;
+    info[8] = S::WAVES_M;
+    info[9] = S::WAVES_N;
     return record_ring<S>(ktu, events, cap);
   };
   switch (variant) {
@@ -297,6 +299,7 @@ int64_t ring_trace(int variant, int ktu, int32_t *events, int64_t cap, int *info
     case 27: return run(GemmTile128x128<kF16, 5>{});
     case 30: return run(GemmOneBarrier{});
     case 31: return run(GemmRowMajorMfma{});
+    case 32: return run(GemmTile128x64<kF16, 4>{});
     default: return -1;
   }
 }

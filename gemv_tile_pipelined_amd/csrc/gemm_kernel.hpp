@@ -706,6 +706,10 @@ template <int DT, int STAGES = 2>
 using GemmTile128x256 = GemmShape<128, 256, 64, STAGES, 2, 2, true, true, 4, 16, 2, 1, DT, false, 0, true>;
 template <int DT, int STAGES = 2>
 using GemmTile128x128 = GemmShape<128, 128, 64, STAGES, 2, 2, true, true, 4, 16, 2, 1, DT, false, 0, true>;
+// A smaller tile, four waves stacked along M (32 rows by 64 columns each):
+// 8 MFMAs per K step, so an operand read in every slot.
+template <int DT, int STAGES = 4, int DMA_STRIDE = 2>
+using GemmTile128x64 = GemmShape<128, 64, 64, STAGES, 4, 1, true, true, DMA_STRIDE, 16, 1, 1, DT, false, 0, true>;
 
 static_assert(GemmDefault::BM == kGemmBM && GemmDefault::BN == kGemmBN && GemmDefault::BK == kGemmBK &&
                   GemmDefault::STAGES == kGemmStages && GemmDefault::kThreads == kGemmThreads,
@@ -741,9 +745,11 @@ static hipError_t launch_default(const void *A, const void *B, void *D, int M, i
                     GemmTile128x256<DT, kGemmTileShapes[kTile128x256].stages>::BM ==
                         kGemmTileShapes[kTile128x256].bm &&
                     GemmTile128x128<DT, kGemmTileShapes[kTile128x128].stages>::BM ==
-                        kGemmTileShapes[kTile128x128].bm,
+                        kGemmTileShapes[kTile128x128].bm &&
+                    GemmTile128x64<DT, kGemmTileShapes[kTile128x64].stages>::BN ==
+                        kGemmTileShapes[kTile128x64].bn,
                 "kGemmTileShapes must describe the kernels launched for each tile");
-  switch (gemm_default_tile(M, N, num_cus)) {
+  switch (gemm_default_tile(M, N, num_cus, EPI == kEpiPartial ? kGemmSplitKTiles : kGemmTiles)) {
     case kTile256x128:
       return launch<GemmTile256x128<DT, kGemmTileShapes[kTile256x128].stages>, EPI>(A, B, D, M, N, K, num_cus, stream,
                                                                               bias, relu, ws, splits);
@@ -753,6 +759,11 @@ static hipError_t launch_default(const void *A, const void *B, void *D, int M, i
     case kTile128x128:
       return launch<GemmTile128x128<DT, kGemmTileShapes[kTile128x128].stages>, EPI>(A, B, D, M, N, K, num_cus, stream,
                                                                               bias, relu, ws, splits);
+    case kTile128x64:
+      if constexpr (EPI != kEpiPartial)
+        return launch<GemmTile128x64<DT, kGemmTileShapes[kTile128x64].stages>, EPI>(A, B, D, M, N, K, num_cus, stream,
+                                                                               bias, relu, ws, splits);
+      return hipErrorInvalidValue;  // split K keeps to the first kGemmSplitKTiles tiles
     default: return launch<Big, EPI>(A, B, D, M, N, K, num_cus, stream, bias, relu, ws, splits);
   }
 }

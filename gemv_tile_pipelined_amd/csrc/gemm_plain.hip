@@ -26,6 +26,7 @@ hipError_t launch_gemm_f16(int variant, const void *A, const void *B, void *D, i
     case 28: return launch<GemmDefault, kEpiCachedStores>(A, B, D, M, N, K, num_cus, stream);
     case 30: return launch<GemmOneBarrier>(A, B, D, M, N, K, num_cus, stream);
     case 31: return launch<GemmRowMajorMfma>(A, B, D, M, N, K, num_cus, stream);
+    case 32: return launch<GemmTile128x64<kF16, 4>>(A, B, D, M, N, K, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

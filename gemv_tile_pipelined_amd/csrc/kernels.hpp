@@ -23,31 +23,37 @@ constexpr int kGemmGroupM = 8;
 // gemvtile_gemm_f16_variant numbers of the tiled kernel: 0 (the default)
 // and the ablations of gemm.hip.  Numbers of ablations that were measured and
 // not kept stay unused.
-constexpr int kGemmVariants = 32;
-inline bool gemm_variant_exists(int v) { return (v >= 0 && v <= 3) || v == 10 || (v >= 20 && v <= 28) || v == 30 || v == 31; }
+constexpr int kGemmVariants = 33;
+inline bool gemm_variant_exists(int v) { return (v >= 0 && v <= 3) || v == 10 || (v >= 20 && v <= 28) || v == 30 || v == 31 || v == 32; }
 
 // Output tile of the tiled GEMM.  The 256x256 default needs about one tile
 // per CU to fill the chip; outputs that give fewer take smaller tiles, each
 // with a deeper ring so that its shorter K tiles still cover the load
-// latency (2 stages at 256x256, 3 at 256x128 and 128x256, 4 at 128x128).
-enum GemmTile { kTile256x256 = 0, kTile256x128 = 1, kTile128x256 = 2, kTile128x128 = 3 };
-constexpr int kGemmTiles = 4;
+// latency (2 stages at 256x256, 3 at 256x128 and 128x256, 4 at 128x128 and
+// 128x64).
+enum GemmTile { kTile256x256 = 0, kTile256x128 = 1, kTile128x256 = 2, kTile128x128 = 3, kTile128x64 = 4 };
+constexpr int kGemmTiles = 5;
 struct GemmTileShape {
   int bm, bn, stages;
   // Work rate relative to 256x256 when every CU has tiles to spare, in
   // percent (measured at 8192^3: 256x128 and 128x256 run at about 0.9 of the
-  // 256x256 rate, 128x128 at about 0.76).
+  // 256x256 rate, 128x128 at about 0.76; 128x64 at 0.69-0.79 of the 128x128
+  // rate at 1024-4096 x 1024 x 4096-14336).
   int rate_pct;
 };
 constexpr GemmTileShape kGemmTileShapes[kGemmTiles] = {
-    {256, 256, 2, 100}, {256, 128, 3, 90}, {128, 256, 3, 90}, {128, 128, 4, 76}};
+    {256, 256, 2, 100}, {256, 128, 3, 90}, {128, 256, 3, 90}, {128, 128, 4, 76}, {128, 64, 4, 55}};
+// Split K (below) picks among the first kGemmSplitKTiles tiles only: its
+// constants were measured with them.
+constexpr int kGemmSplitKTiles = 4;
 // The tile for an M x N output on num_cus CUs: the one with the least
 // estimated time, i.e. waves of tiles over the CUs times tile area over rate;
-// ties go to the larger tile (the lower enum value).
-inline GemmTile gemm_default_tile(int64_t M, int64_t N, int num_cus) {
+// ties go to the larger tile (the lower enum value).  `tiles` limits the
+// choice to the first entries of kGemmTileShapes.
+inline GemmTile gemm_default_tile(int64_t M, int64_t N, int num_cus, int tiles = kGemmTiles) {
   int best = kTile256x256;
   int64_t best_cost = -1;
-  for (int t = 0; t < kGemmTiles; ++t) {
+  for (int t = 0; t < tiles; ++t) {
     const GemmTileShape &s = kGemmTileShapes[t];
     const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
     const int64_t waves = (tiles + num_cus - 1) / num_cus;
@@ -79,7 +85,7 @@ constexpr int kSplitKMinTiles = 10;
 constexpr int kSplitKMinSaved = 12;
 constexpr int kSplitKOutputsPerTile = 1 << 18;
 inline int gemm_splitk_splits(int64_t M, int64_t N, int64_t K, int num_cus) {
-  const GemmTileShape &s = kGemmTileShapes[gemm_default_tile(M, N, num_cus)];
+  const GemmTileShape &s = kGemmTileShapes[gemm_default_tile(M, N, num_cus, kGemmSplitKTiles)];
   const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
   const int64_t kt = (K + 63) / 64;
   if (tiles >= num_cus || kt < 2 * kSplitKMinTiles) return 1;

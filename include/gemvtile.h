@@ -66,7 +66,7 @@ enum gemvtile_status {
  * the matrix and write only inside it.  The summation order within FP32 is
  * unspecified (several results are correct up to rounding).
  * Otherwise the tiled kernel runs with 256x256 output tiles, or with
- * 256x128, 128x256 or 128x128 ones when the output has too few 256x256
+ * 256x128, 128x256, 128x128 or 128x64 ones when the output has too few 256x256
  * tiles to keep every compute unit busy (gemvtile_gemm_tile gives the choice);
  * it writes D with non-temporal stores, so D is not left in the caches.
  * When the smaller side has at most 64 rows -- a decode batch against a
@@ -272,10 +272,11 @@ void gemvtile_gemm_config(int *bm, int *bn, int *bk, int *stages, int *threads, 
  * gemvtile_gemm_tile -- the output tile (bm x bn) and LDS ring depth the
  * tiled GEMM takes for an M x N output on `num_cus` compute units (gemm_f16
  * and gemm_bf16 when they take the tiled kernel).  Of 256x256 (2
- * stages), 256x128 and 128x256 (3 stages) and 128x128 (4 stages), it is the
- * one with the least ceil(#tiles / num_cus) * bm * bn / rate, where rate is
- * the tile's measured work rate relative to 256x256 with tiles to spare (1,
- * 0.9, 0.9, 0.76); ties go to the larger tile.  Smaller tiles fill the CUs
+ * stages), 256x128 and 128x256 (3 stages), 128x128 and 128x64 (4 stages),
+ * it is the one with the least ceil(#tiles / num_cus) * bm * bn / rate,
+ * where rate is the tile's measured work rate relative to 256x256 with
+ * tiles to spare (1, 0.9, 0.9, 0.76, 0.55); ties go to the larger tile.
+ * The split-K entry points choose the same way among the first four.  Smaller tiles fill the CUs
  * when large ones would leave some idle (an 8192 x 1024 output has 128 tiles
  * of 256x256, 256 of 256x128); their deeper rings cover the load latency
  * over their shorter K tiles.  Any output pointer may be NULL.  Host-only
@@ -343,11 +344,13 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
  *      128x128 (4-stage ring) output tiles (4 waves of 128x64, 64x128,
  *      64x64): the smaller tiles of variant 0, whatever the shape
  *   24, 25, 26 as 21, 22, 23 with 2-stage rings   27 as 23 with 5 stages
+ *   32 the 128x64 tile of variant 0 (4-stage ring, 4 waves of 32x64),
+ *      whatever the shape
  *   28 as 20 with D written by ordinary (cached) stores instead of
  *      non-temporal ones
  *   30 as 20 with one barrier per K tile (the ring without the early free)
  *   31 as 20 with the MFMAs of a K step in row-major order over the blocks
- * Variants 1..31 always run the tiled kernel, whatever the shape; variant
+ * Variants 1..32 always run the tiled kernel, whatever the shape; variant
  * 0 routes shapes as gemm_f16 does (M or N == 1: the GEMV kernel; M or N
  * <= 16, and some shapes with 17..64 rows on the smaller side: the skinny
  * kernel).  The skinny kernel (only for M <= 16 or N <= 16, and 160 also
@@ -461,10 +464,11 @@ int gemvtile_gemv_f16_variant(const void *x, const void *W, void *y, int64_t N, 
  *                         prologue's loads are issued)
  *           events beyond `cap` are counted but not written; may be NULL
  *           when cap == 0
- *   info    if not NULL, 8 ints: loads per wave per K tile, operand reads
+ *   info    if not NULL, 10 ints: loads per wave per K tile, operand reads
  *           per wave per K step, K steps per K tile, MFMAs per wave per K
- *           step, ring stages, output tile rows and columns, and 1 for the
- *           early-free schedule (two barriers per K tile) or 0
+ *           step, ring stages, output tile rows and columns, 1 for the
+ *           early-free schedule (two barriers per K tile) or 0, and the
+ *           waves along the tile's rows and along its columns
  * Each wave of the workgroup runs this same sequence.  Returns the number
  * of events, or -1 for a variant without a multi-stage ring or arguments
  * out of range.

@@ -87,7 +87,7 @@ def test_gemm_argument_validation(lib):
     # unknown internal variant: each family has its own id range (tiled 0..,
     # skinny 100.., wave-specialised 200..); the gaps, and the numbers of
     # ablations measured and not kept, are invalid
-    for bad in (-1, 4, 9, 11, 12, 15, 19, 29, 32, 36, 99, 101, 113, 131, 140, 148, 149, 153, 199, 202, 1000):
+    for bad in (-1, 4, 9, 11, 12, 15, 19, 29, 33, 36, 99, 101, 113, 131, 140, 148, 149, 153, 199, 202, 1000):
         assert lib.gemvtile_gemm_f16_variant(FAKE, FAKE, FAKE, 4, 4, 8, None, bad) == INVALID, bad
     # skinny launch shapes only apply when one side has at most 16 rows (at
     # most 64 for gemm_f16's own skinny launch, 100, and the small-side
@@ -214,7 +214,7 @@ def test_gemm_grid_and_golden_counts(lib):
     assert cfg == {"BM": 256, "BN": 256, "BK": 64, "stages": 2, "threads": 256, "group_m": 8}
     assert gt.gemm_grid(4096, 4096, 4096, 256) == 256
     assert gt.gemm_grid(8192, 8192, 4096, 256) == 256
-    assert gt.gemm_grid(256, 256, 4096, 256) == 4  # four 128x128 tiles (see the tile rule below)
+    assert gt.gemm_grid(256, 256, 4096, 256) == 8  # eight 128x64 tiles (see the tile rule below)
     assert gt.gemm_grid(4000, 4032, 4096, 256) == 256
     assert gt.gemm_grid(0, 4, 4096, 256) == 0
     # skinny shapes: from 32 rows of the larger side per CU, one workgroup
@@ -246,7 +246,7 @@ def test_gemm_grid_and_golden_counts(lib):
     assert gt.gemm_grid(30, 2100, 4096, 256) == 2 * 132  # staged: 8 rows, at most 32 small-side rows
     assert gt.gemm_grid(50, 2100, 4096, 256) == 263  # staged, 8 rows per workgroup
     assert gt.gemm_grid(64, 4097, 4096, 256) == 257
-    assert gt.gemm_grid(65, 4097, 4096, 256) == 33  # 1 x 33 tiles of 128x128
+    assert gt.gemm_grid(65, 4097, 4096, 256) == 65  # 1 x 65 tiles of 128x64
     # ... whatever the larger side
     assert gt.gemm_grid(32, 16384, 4096, 256) == 256  # 64 rows per workgroup
     assert gt.gemm_grid(24, 8192, 4096, 256) == 256
@@ -290,8 +290,10 @@ def test_gemm_tile_rule(lib):
         (4096, 2048): (256, 128, 3),
         (2048, 2048): (128, 128, 4),
         (1024, 4096): (128, 128, 4),
-        (512, 4096): (128, 128, 4),
-        (256, 256): (128, 128, 4),
+        (512, 4096): (128, 64, 4),
+        (256, 256): (128, 64, 4),
+        (1024, 1024): (128, 64, 4),
+        (1536, 1024): (128, 64, 4),
         (2176, 3840): (128, 256, 3),
         (3840, 2176): (256, 128, 3),
     }
@@ -302,7 +304,8 @@ def test_gemm_tile_rule(lib):
     # the documented cost, ceil(#tiles / CUs) * bm * bn / rate, is least for
     # the chosen tile, and no larger tile ties it
     shapes = [(bm, bn, st, rate) for bm, bn, st, rate in
-              ((256, 256, 2, 1.0), (256, 128, 3, 0.9), (128, 256, 3, 0.9), (128, 128, 4, 0.76))]
+              ((256, 256, 2, 1.0), (256, 128, 3, 0.9), (128, 256, 3, 0.9), (128, 128, 4, 0.76),
+               (128, 64, 4, 0.55))]
     for M in (17, 100, 256, 300, 777, 1024, 2049, 4096, 6000):
         for N in (17, 129, 512, 1000, 3000, 8192):
             for cus in (80, 256, 304):
@@ -314,6 +317,15 @@ def test_gemm_tile_rule(lib):
     for bad in ((0, 4, 256), (4, 0, 256), (4, 4, 0), (4, 4, 2**21)):
         with pytest.raises(gt.GemvTileError):
             gt.gemm_tile(*bad)
+
+
+def _splitk_tile(M, N, cus):
+    # split K picks by the same cost as gemm_tile among the first four
+    # tiles (256x256, 256x128, 128x256, 128x128), ties to the larger
+    shapes = ((256, 256, 1.0), (256, 128, 0.9), (128, 256, 0.9), (128, 128, 0.76))
+    cost = [-(-(-(-M // bm) * -(-N // bn)) // cus) * bm * bn / rate for bm, bn, rate in shapes]
+    i = next(j for j in range(len(shapes)) if cost[j] <= min(cost) * (1 + 1e-12))
+    return shapes[i][:2]
 
 
 def test_gemm_splitk_rule(lib):
@@ -345,7 +357,7 @@ def test_gemm_splitk_rule(lib):
         for N in (17, 129, 1000, 3000):
             for K in (8, 448, 512, 1032, 1280, 4104, 14336):
                 for cus in (80, 256):
-                    bm, bn, _ = gt.gemm_tile(M, N, cus)
+                    bm, bn = _splitk_tile(M, N, cus)
                     T = -(-M // bm) * -(-N // bn)
                     kt = -(-K // 64)
                     s = 1

@@ -278,7 +278,7 @@ def test_output_guard_band(env):
     assert np.array_equal(D.cpu().numpy(), oracle.gemm(A, B))
 
 
-TILED_VARIANTS = [1, 2, 3, 10, 20, 21, 22, 23, 24, 25, 26, 27, 28, 30, 31]
+TILED_VARIANTS = [1, 2, 3, 10, 20, 21, 22, 23, 24, 25, 26, 27, 28, 30, 31, 32]
 
 
 @pytest.mark.parametrize("variant", TILED_VARIANTS)
@@ -307,9 +307,10 @@ def test_gemm_variants_few_k_tiles(env, variant, K):
 
 
 # Outputs whose 256x256 tiles would leave CUs idle take smaller tiles: these
-# route (with 256 CUs) to 256x128, 128x256 and 128x128 tiles, with ragged M,
+# route (with 256 CUs) to 256x128, 128x256, 128x128 and 128x64 tiles, with ragged M,
 # N and K.  Sampled rows against the oracle; integer data bit-exact.
-TILE_CHOICE_SHAPES = [(8192, 1000, 264, (256, 128)), (2176, 3832, 200, (128, 256)), (1000, 3000, 136, (128, 128))]
+TILE_CHOICE_SHAPES = [(8192, 1000, 264, (256, 128)), (2176, 3832, 200, (128, 256)), (1000, 3000, 136, (128, 128)),
+                      (1000, 1000, 264, (128, 64))]
 
 
 @pytest.mark.parametrize("case", TILE_CHOICE_SHAPES, ids=lambda c: "x".join(map(str, c[:3])))

@@ -30,7 +30,7 @@ import gemv_tile_pipelined_amd as gt
 # 20 the 256x256 default (early-free schedule), 10 its 32x32x16 form, 21..27
 # the smaller tiles with 2..5 stages, 30 the one-barrier ring, 31 the default
 # with row-major MFMA order.
-VARIANTS = [20, 10, 21, 22, 23, 24, 25, 26, 27, 30, 31]
+VARIANTS = [20, 10, 21, 22, 23, 24, 25, 26, 27, 30, 31, 32]
 # 1..9 short loops (every prologue / last-refill / drain branch), 22 and 56
 # (split-K slice lengths: ceil(224 / 4) = 56 for K = 14336 in 4 slices), 64
 # (K = 4096), 65 (K = 4104: the ragged benchmark shape), 128 (K = 8192).
@@ -65,9 +65,9 @@ class RingModel:
         self.mfma_since_load = {}  # tile -> MFMAs issued since its last load was issued
         self.overlap = {}  # tile -> MFMAs between its last load and the wait that landed it
         # MFMA blocks per wave: 16x16 blocks with 2 K steps per 64-wide K
-        # tile, 32x32 blocks with 4; 2x2 waves per output tile.
+        # tile, 32x32 blocks with 4; waves_m x waves_n waves per output tile.
         mi = 16 if self.ksteps == 2 else 32
-        self.n_a, self.n_b = info["bm"] // 2 // mi, info["bn"] // 2 // mi
+        self.n_a, self.n_b = info["bm"] // info["waves_m"] // mi, info["bn"] // info["waves_n"] // mi
         assert self.n_a + self.n_b == self.reads and self.n_a * self.n_b == self.mfma
         self.frag = ({}, {})  # fragment buffer -> {("A" | "B", block): (K tile, K step) it holds}
         self.blocks = set()  # (A block, B block) pairs of the current K step's MFMAs
@@ -281,7 +281,7 @@ def test_model_rejects_misplaced_accumulator_zeroing():
 def test_trace_info_describes_the_kernels():
     want = {20: (256, 256, 2, 16, 1), 10: (256, 256, 2, 16, 0), 21: (256, 128, 3, 12, 0), 22: (128, 256, 3, 12, 0),
             23: (128, 128, 4, 8, 0), 24: (256, 128, 2, 12, 0), 25: (128, 256, 2, 12, 0), 26: (128, 128, 2, 8, 0),
-            27: (128, 128, 5, 8, 0), 30: (256, 256, 2, 16, 0), 31: (256, 256, 2, 16, 1)}
+            27: (128, 128, 5, 8, 0), 30: (256, 256, 2, 16, 0), 31: (256, 256, 2, 16, 1), 32: (128, 64, 4, 6, 0)}
     for v, (bm, bn, stages, per, ef) in want.items():
         _, info = gt.ring_trace(v, 4)
         assert (info["bm"], info["bn"], info["stages"], info["loads_per_tile"], info["early_free"]) == \
