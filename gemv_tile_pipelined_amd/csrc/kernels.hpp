@@ -176,7 +176,8 @@ inline int64_t gemv_default_grid(int64_t N, int64_t K, int num_cus) {
 }
 
 // At 16 P rows per workgroup the default skinny launch streams P with
-// non-temporal loads only for K of at least kSkinnyStreamMinK elements:
+// non-temporal loads (and K tiles of 256 in a 6-stage ring) only for K of
+// at least kSkinnyStreamMinK elements:
 // below 8192 cached loads measured faster (8x4096x4096: 8.8 -> 7.4 us;
 // 8x4096x6144: 10.5 -> 9.4 us); from 8192 up the non-temporal form is the
 // faster (8x4096x14336: 20.0 us against 23.2 us cached; 8x4096x28672: 36.5

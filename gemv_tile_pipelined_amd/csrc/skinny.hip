@@ -388,9 +388,10 @@ static hipError_t launch_lds_qsplit(const void *P, const void *Q, void *D, int R
 
 // The default launch (skinny_default_rows): 32, 48 or 64 P rows per
 // workgroup, in K tiles of 256 or 128, while R gives every CU 32 rows; else
-// 16 P rows with 16 waves
-// and a 4-stage ring, with non-temporal P loads from K = kSkinnyStreamMinK
-// up (cached below); else 8, 4, 2 or 1 P rows, staging 8 Q rows when S <= 8
+// 16 P rows: with 16 waves, a 4-stage ring of K tiles of 512 and cached P
+// loads below K = kSkinnyStreamMinK, and with 8 waves, a 6-stage ring of K
+// tiles of 256 and non-temporal P loads from there up; else 8, 4, 2 or 1 P
+// rows, staging 8 Q rows when S <= 8
 // (and loading P non-temporally at 8 rows with 8 Q rows; at fewer rows that
 // measured slower).  Launches of 32, 16 or 8 P rows start each workgroup's
 // K walk at its index within its XCD (KROT 2, kSkinnyRotateXcd): without
@@ -449,7 +450,10 @@ static hipError_t launch_lds_auto(const void *P, const void *Q, void *D, int R, 
   switch (pr) {
     case 16:
       if (K < kSkinnyStreamMinK) return launch_lds<16, 4, 16, DT, 16, kSkinnyRotateXcd>(P, Q, D, R, S, K, trans, stream);
-      return launch_lds<16, 4, 16, DT, 16, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream);
+      // from K = 8192: K tiles of 256, 8 waves, a 6-stage ring of 16 KiB
+      // (8x4096x14336 19.27 -> 18.93 us, 8x4096x8192 12.39 -> 11.65 us
+      // against 16 waves and 4 stages of 512)
+      return launch_lds<8, 6, 16, DT, 16, kSkinnyRotateXcd, true, 256>(P, Q, D, R, S, K, trans, stream);
     case 8: return q8 ? launch_lds<8, 4, 8, DT, 8, kSkinnyRotateXcd, true>(P, Q, D, R, S, K, trans, stream)
                       : launch_lds<8, 4, 16, DT, 8, kSkinnyRotateXcd>(P, Q, D, R, S, K, trans, stream);
     case 4: return q8 ? launch_lds<4, 4, 8, DT, 4>(P, Q, D, R, S, K, trans, stream)
