@@ -80,11 +80,11 @@ CONFIG_REPS = {0: 200, 2: 50, 4: 10}  # timed launches per extra workload
 # valid only for the kernel sources whose SHA-256 is recorded here; the
 # summary and commands are in profiles/traffic_fetch_write_size.md.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "3302b52412ea78984ca35753a1da9d4db3062c97c34789a90112789459ccf034",
-    "gemm": {"fetch_kib": 98442.9 * 2.0, "write_kib": 32794.6 * 1.0},
+    "sources_sha256": "7ad5b1342ccb7e4ffd74183bf3e069855fa50d3069fc765de71172d24c3f256a",
+    "gemm": {"fetch_kib": 98443.0 * 2.0, "write_kib": 32791.6 * 1.0},
     "gemv": {"fetch_kib": 57482.6 * 2.0, "write_kib": 64.0 * 1.0},
     "decode": {"fetch_kib": 58267.0 * 2.0, "write_kib": 64.0 * 1.0},
-    "gemm_bf16": {"fetch_kib": 98442.0 * 2.0, "write_kib": 32796.5 * 1.0},
+    "gemm_bf16": {"fetch_kib": 98442.0 * 2.0, "write_kib": 32793.2 * 1.0},
     "gemv_bf16": {"fetch_kib": 57482.5 * 2.0, "write_kib": 64.0 * 1.0},
 }
 KERNEL_SOURCES = ("device_common.hpp", "gemm.hip", "gemm_kernel.hpp", "gemm_plain.hip", "gemv.hip", "kernels.hpp",

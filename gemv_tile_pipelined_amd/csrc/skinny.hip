@@ -29,8 +29,8 @@
 //  * Two ways to feed the MFMAs: straight into registers (each wave keeps
 //    UNROLL pairs of loads in flight; one load instruction touches 16 rows x
 //    64 bytes), or -- the default -- through an LDS ring filled by
-//    direct-to-LDS loads of whole 1 KiB row segments (gemm_skinny_lds_kernel
-//    below).  On 8x4096x14336 the ring takes 23 us against 30 us, because
+//    direct-to-LDS loads of 1 KiB each, one to four whole row segments
+//    (gemm_skinny_lds_kernel below).  On 8x4096x14336 the ring takes 23 us against 30 us, because
 //    the register form re-reads the small operand in 64-byte pieces from
 //    every workgroup.
 //  * Output: D[s*R + r] (D = Q·Pᵀ, the M <= 16 case) or D[r*S + s]

@@ -355,8 +355,8 @@ int64_t gemvtile_gemm_grid(int64_t M, int64_t N, int64_t K, int64_t num_cus);
  * <= 16, and some shapes with 17..64 rows on the smaller side: the skinny
  * kernel).  The skinny kernel (only for M <= 16 or N <= 16, and 160 also
  * for 17..64 rows on the smaller side, else GEMVTILE_ERR_UNSUPPORTED):
- *   100 the gemm_f16 choice (16, 8, 4, 2 or 1 rows of the large side per
- *       workgroup, see gemvtile_gemm_grid)
+ *   100 the gemm_f16 choice (32, 48, 64, 16, 8, 4, 2 or 1 rows of the
+ *       large side per workgroup, see gemvtile_gemm_grid)
  *   104 operands loaded straight into registers (8 waves, 4 K steps of 32
  *       in flight per wave), 16 large-side rows per workgroup
  *   112 operands staged through a 4-stage LDS ring of 1 KiB row segments,
