@@ -116,8 +116,10 @@ SHAPES = [
     (1000, 50, 2056),
     (20, 2048, 4096),
     (64, 1024, 14336),
-    # 17..32 staged rows with rotated K starts (K % 4096 == 0), at 16 and 8
-    # large-side rows per workgroup; 33..64 at 8 rows per workgroup
+    # 17..32 staged rows with rotated K starts (K % 4096 == 0) at 16
+    # large-side rows per workgroup, the small-side split at 8 staged-launch
+    # rows with at most 32 small-side rows, and 33..64 staged rows at 8 rows
+    # per workgroup
     (24, 4096, 8192),
     (2500, 20, 4096),
     (48, 2600, 4104),
